@@ -1,0 +1,167 @@
+"""Oracle for the gated delta rule: plain float64 CPU implementations.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import this package.  Nothing here is shared with the HIP library, and nothing here imports it.
+
+* :func:`recurrent` -- the definition, token by token, in C (``gdn_oracle.c``), float64, OpenMP
+  over independent (batch, value-head) chains.  This is the oracle every GPU result is compared to.
+* :func:`decode` -- the same recurrence applied once per call over a sequence of decode steps.
+* :func:`brute_force` -- the recurrence with every transition matrix written out densely
+  (numpy), for tiny inputs; an independent code path used to pin :func:`recurrent`.
+* :func:`chunked` -- the chunkwise (WY / UT-transform) refactoring of the same recurrence in
+  numpy float64, used to pin the chunk algebra the GPU implements.
+
+Citations name the page and the section/equation followed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+__all__ = ["recurrent", "decode", "brute_force", "chunked", "max_threads", "load"]
+
+_lib = None
+
+
+def load():
+    """Load (building if needed) the C oracle library."""
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gdn_oracle_recurrent.argtypes = [dp] * 8 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+        lib.gdn_oracle_recurrent.restype = ctypes.c_int
+        lib.gdn_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(load().gdn_oracle_max_threads())
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def recurrent(q, k, v, g, beta, s0=None, scale: float = 1.0, threads: int = 0):
+    """Token-by-token float64 gated delta rule (the definition).
+
+    S_t = S_{t-1}(alpha_t (I - beta_t k_t k_t^T)) + beta_t v_t k_t^T, o_t = S_t q_t
+    ("Architecture Thread I", section "Gated DeltaNet"; "Gated Attention Architectures",
+    section 3), stored transposed as h = S^T [B,Hv,dk,dv].
+
+    q, k: [B,T,Hqk,dk]; v: [B,T,Hv,dv]; g = log alpha, beta: [B,T,Hv]; s0: [B,Hv,dk,dv] or None.
+    Returns (o [B,T,Hv,dv], s_final [B,Hv,dk,dv]) in float64."""
+    q, k, v, g, beta, s0 = map(_f64, (q, k, v, g, beta, s0))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    assert k.shape == q.shape and v.shape[:2] == (B, T) and g.shape == (B, T, Hv) == beta.shape
+    if s0 is not None:
+        assert s0.shape == (B, Hv, dk, dv)
+    o = np.empty((B, T, Hv, dv), dtype=np.float64)
+    sf = np.empty((B, Hv, dk, dv), dtype=np.float64)
+    rc = load().gdn_oracle_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                                     _ptr(o), _ptr(sf), B, T, Hqk, Hv, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return o, sf
+
+
+def decode(q, k, v, g, beta, s0, scale: float = 1.0, threads: int = 0):
+    """Decode: one recurrence step per call, ``steps`` calls in a row, state carried over.
+
+    q, k: [steps,B,Hqk,dk]; v: [steps,B,Hv,dv]; g, beta: [steps,B,Hv]; s0: [B,Hv,dk,dv] or None.
+    Returns (o [steps,B,Hv,dv], s_final [B,Hv,dk,dv])."""
+    steps = q.shape[0]
+    h = None if s0 is None else _f64(s0)
+    outs = []
+    for s in range(steps):
+        o, h = recurrent(q[s][:, None], k[s][:, None], v[s][:, None], g[s][:, None],
+                         beta[s][:, None], h, scale, threads)
+        outs.append(o[:, 0])
+    if h is None:  # steps == 0
+        B, Hv, dk, dv = q.shape[1], v.shape[2], q.shape[3], v.shape[3]
+        h = np.zeros((B, Hv, dk, dv))
+    return np.stack(outs) if outs else np.zeros((0,) + v.shape[1:]), h
+
+
+def brute_force(q, k, v, g, beta, s0=None, scale: float = 1.0):
+    """The recurrence with each transition written out as a dense matrix (numpy, tiny T only).
+
+    Follows the Gated DeltaNet equation literally in math orientation S in R^{dv x dk}:
+    M_t = alpha_t (I - beta_t k_t k_t^T) (dk x dk), S_t = S_{t-1} M_t + beta_t v_t k_t^T,
+    o_t = S_t q_t ("Architecture Thread I", section "Gated DeltaNet")."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    o = np.zeros((B, T, Hv, dv))
+    sf = np.zeros((B, Hv, dk, dv))
+    for b in range(B):
+        for j in range(Hv):
+            i = j // grp
+            S = np.zeros((dv, dk)) if s0 is None else np.array(s0[b, j], dtype=np.float64).T.copy()
+            for t in range(T):
+                kt = k[b, t, i][:, None]
+                M = np.exp(g[b, t, j]) * (np.eye(dk) - beta[b, t, j] * (kt @ kt.T))
+                S = S @ M + beta[b, t, j] * (v[b, t, j][:, None] @ kt.T)
+                o[b, t, j] = S @ (scale * q[b, t, i])
+            sf[b, j] = S.T
+    return o, sf
+
+
+def chunked(q, k, v, g, beta, s0=None, chunk: int = 64, scale: float = 1.0):
+    """Chunkwise form of the same recurrence (numpy float64).
+
+    "Gated Attention Architectures", section 3, names the hardware-efficient algorithm: the
+    DeltaNet WY representation (section 2: I - beta k k^T is a generalised Householder matrix)
+    extended with per-chunk cumulative decay products gamma_j = prod_{i=chunk start}^{j} alpha_i.
+    The pages give no further algebra; the steps below are derived from the recurrence.  Per chunk
+    of C positions with entry state h0 (= S^T), log-decay cumsum gc_r = sum_{i<=r} g_i:
+
+      A     = strictly-lower( diag(beta) (K K^T * Gamma) ),  Gamma_ri = exp(gc_r - gc_i)
+      Delta = (I + A)^{-1} ( diag(beta) V - diag(beta exp(gc)) K h0 )
+      O     = diag(exp(gc)) Q h0 + ( lower-incl(Q K^T * Gamma) ) Delta
+      h1    = exp(gc_C) h0 + Ktilde^T Delta,   Ktilde_i = exp(gc_C - gc_i) k_i
+
+    The output step has the shape of GLA's chunkwise parallel form ("Gated Attention
+    Architectures", section 1) with V replaced by the state-corrected Delta.
+    The triangular solve is done with numpy.linalg.solve (a library primitive)."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    o = np.zeros((B, T, Hv, dv))
+    sf = np.zeros((B, Hv, dk, dv))
+    for b in range(B):
+        for j in range(Hv):
+            i = j // grp
+            h = np.zeros((dk, dv)) if s0 is None else np.array(s0[b, j], dtype=np.float64)
+            for c0 in range(0, T, chunk):
+                c1 = min(T, c0 + chunk)
+                K = k[b, c0:c1, i]
+                Q = scale * q[b, c0:c1, i]
+                V = v[b, c0:c1, j]
+                bt = beta[b, c0:c1, j]
+                gc = np.cumsum(g[b, c0:c1, j])
+                Gam = np.exp(gc[:, None] - gc[None, :])
+                A = np.tril(bt[:, None] * (K @ K.T) * Gam, -1)
+                rhs = bt[:, None] * V - (bt * np.exp(gc))[:, None] * (K @ h)
+                Delta = np.linalg.solve(np.eye(c1 - c0) + A, rhs)
+                o[b, c0:c1, j] = np.exp(gc)[:, None] * (Q @ h) + np.tril(Q @ K.T * Gam) @ Delta
+                Kt = np.exp(gc[-1] - gc)[:, None] * K
+                h = np.exp(gc[-1]) * h + Kt.T @ Delta
+            sf[b, j] = h
+    return o, sf

@@ -1,0 +1,26 @@
+"""Compile the float64 CPU oracle (oracle/gdn_oracle.c) into oracle/libgdn_oracle.so with gcc.
+
+Test infrastructure: the oracle is a checker, not part of the product path."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gdn_oracle.c")
+LIB = os.path.join(HERE, "libgdn_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())
