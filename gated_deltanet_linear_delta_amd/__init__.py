@@ -1,0 +1,178 @@
+"""Gated delta rule (Gated DeltaNet core) on AMD MI355X: Python binding of libgdn.so.
+
+The binding only marshals arguments: every step of the computation runs in the HIP kernels of
+``libgdn.so`` (built in-tree by ``gated_deltanet_linear_delta_amd/build.py``).  torch tensors
+provide device memory and the HIP stream; nothing is computed with torch.  If the library is
+missing, every call raises -- there is no fallback path.
+
+Entry points (same names as the C ABI in include/gdn.h):
+
+* :func:`gdn_chunk_fwd` -- prefill, chunkwise, optional initial / final state.
+* :func:`gdn_recurrent_step` -- decode, one token per sequence, state updated in place.
+* :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_kernel_name`,
+  :func:`gdn_status_string`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GDN_F32", "GDN_BF16", "GdnError", "library_path", "load_library", "gdn_chunk_fwd",
+    "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
+    "gdn_status_string", "EXPORTED_SYMBOLS",
+]
+
+GDN_F32 = 0
+GDN_BF16 = 1
+EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
+                    "gdn_chunk_fwd_kernel_name", "gdn_status_string")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({gdn_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libgdn.so")
+
+
+def load_library():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                           "or `python gated_deltanet_linear_delta_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp, sz, vp]
+    lib.gdn_chunk_fwd.restype = i
+    lib.gdn_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp] + [i] * 5 + [i, f, vp]
+    lib.gdn_recurrent_step.restype = i
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
+    lib.gdn_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_kernel_name.argtypes = [i] * 7 + [i]
+    lib.gdn_chunk_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [i]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status: int) -> str:
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+def gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
+
+
+def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
+    r = load_library().gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk, dtype)
+    return None if r is None else r.decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dense(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=64,
+                  scale=1.0, o=None, final_state=None, workspace=None, stream=None):
+    """Prefill.  q, k [B,T,Hqk,dk]; v [B,T,Hv,dv] (bf16 or f32, all alike); g, beta [B,T,Hv]
+    float32; initial_state [B,Hv,dk,dv] float32 or None.  Returns (o [B,T,Hv,dv], final_state or
+    None).  ``final_state`` may be passed (even as ``initial_state`` itself, for an in-place
+    update); ``o`` may be passed preallocated."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("o", o, (B, T, Hv, dv), q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(q)
+    need = int(lib.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), dt,
+                           float(scale), _ptr(workspace), wbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_recurrent_step(q, k, v, g, beta, state, scale=1.0, o=None, stream=None):
+    """Decode step.  q, k [B,Hqk,dk]; v [B,Hv,dv]; g, beta [B,Hv] float32; state [B,Hv,dk,dv]
+    float32, updated in place.  Returns o [B,Hv,dv]."""
+    torch = _torch()
+    lib = load_library()
+    B, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev = q.device
+    _check_dense("q", q, (B, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, Hv), torch.float32, dev)
+    _check_dense("state", state, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("o", o, (B, Hv, dv), q.dtype, dev)
+    st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                _ptr(o), B, Hqk, Hv, dk, dv, _dtype_code(q), float(scale),
+                                _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_recurrent_step")
+    return o

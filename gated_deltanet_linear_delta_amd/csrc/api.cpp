@@ -1,0 +1,168 @@
+// C ABI of libgdn.so: argument validation and dispatch to the gfx950 kernels.
+// Every check runs before any work is enqueued; see include/gdn.h for the contract.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+bool dtype_ok(gdn_dtype_t t) { return t == GDN_F32 || t == GDN_BF16; }
+size_t dtype_bytes(gdn_dtype_t t) { return t == GDN_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+gdn_status_t device_ok()
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return GDN_ERR_NO_DEVICE;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status_t s)
+{
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid sizes (negative or zero size, or Hv not a multiple of Hqk)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head dim, chunk size or dtype";
+    case GDN_ERR_ALIGN: return "a pointer is misaligned (tensors need 16 bytes, g and beta 4)";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_ALIAS: return "an output overlaps an input it may not overlap";
+    case GDN_ERR_NO_DEVICE: return "no HIP device visible";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int, gdn_dtype_t) { return 0; }
+
+static gdn_status_t check_chunk_sizes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                      gdn_dtype_t dtype)
+{
+    if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
+    if (Hv % Hqk != 0) return GDN_ERR_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || !chunk_ok(chunk) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+static gdn::ChunkArgs make_chunk_args(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const float* s0, float* sf, void* o, int B,
+                                      int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                      gdn_dtype_t dtype, float scale)
+{
+    gdn::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = s0; a.sf = sf; a.o = o;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    return a;
+}
+
+const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                      gdn_dtype_t dtype)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return nullptr;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    return gdn::chunk_mfma_supported(a) ? "mfma" : "simt";
+}
+
+gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* initial_state, float* final_state,
+                           void* o, int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                           gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream)
+{
+    gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s != GDN_OK) return s;
+    if (workspace_bytes < gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
+        return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, o, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = (size_t)B * T;
+    const size_t sbytes = (size_t)B * Hv * dk * dv * sizeof(float);
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rs0 = range(initial_state, initial_state ? sbytes : 0);
+    const Range rsf = range(final_state, final_state ? sbytes : 0);
+    const Range ro = range(o, work ? ntok * Hv * dv * es : 0);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rs0};
+    for (const Range& r : inputs)
+        if (overlap(ro, r) || overlap(rsf, r)) {
+            // the final state may be the initial state exactly (in-place update)
+            if (&r == &inputs[5] && final_state == initial_state && !overlap(ro, r)) continue;
+            return GDN_ERR_ALIAS;
+        }
+    if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    s = device_ok();
+    if (s != GDN_OK) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        if (!final_state) return GDN_OK;
+        return gdn::launch_state_copy(initial_state, final_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, o, B, T, Hqk,
+                                       Hv, dk, dv, chunk, dtype, scale);
+    hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, st)
+                                                : gdn::launch_chunk_simt(a, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state, void* o, int B, int Hqk, int Hv,
+                                int dk, int dv, gdn_dtype_t dtype, float scale, void* stream)
+{
+    if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
+    if (Hv % Hqk != 0) return GDN_ERR_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const Range rq = range(q, (size_t)B * Hqk * dk * es), rk = range(k, (size_t)B * Hqk * dk * es);
+    const Range rv = range(v, (size_t)B * Hv * dv * es), rg = range(g, (size_t)B * Hv * sizeof(float));
+    const Range rb = range(beta, (size_t)B * Hv * sizeof(float));
+    const Range rs = range(state, (size_t)B * Hv * dk * dv * sizeof(float));
+    const Range ro = range(o, (size_t)B * Hv * dv * es);
+    const Range inputs[] = {rq, rk, rv, rg, rb};
+    for (const Range& r : inputs)
+        if (overlap(ro, r) || overlap(rs, r)) return GDN_ERR_ALIAS;
+    if (overlap(ro, rs)) return GDN_ERR_ALIAS;
+    gdn_status_t s = device_ok();
+    if (s != GDN_OK) return s;
+    gdn::StepArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.B = B; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    return gdn::launch_recurrent_step(a, (hipStream_t)stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Chunkwise gated delta rule on the float32 vector units of gfx950 (any supported dtype, head
+// dims 32/64/128, chunk 16/32/64).  This is the float32 path (float32 inputs need float32
+// products) and the path for shapes the matrix-core kernel does not take.
+//
+// The chunk algebra is the WY/UT form named in "Gated Attention Architectures", section 3 (the
+// DeltaNet WY representation of section 2 extended with per-chunk cumulative decay products).
+// Per chunk of C positions with entry state h0 (= S^T, [dk, dv]) and the per-chunk log-decay
+// cumsum gc_r = g_1 + ... + g_r:
+//     A      = strictly-lower( beta_r exp(gc_r - gc_i) (k_r . k_i) )            [C, C]
+//     R      = diag(beta) V - diag(beta exp(gc)) K h0                              [C, dv]
+//     Delta  = (I + A)^{-1} R         (forward substitution)
+//     O      = diag(exp(gc)) Q h0 + lower-incl( exp(gc_r - gc_i) (q_r . k_i) ) Delta
+//     h1     = exp(gc_C) h0 + sum_i exp(gc_C - gc_i) k_i Delta_i^T
+// Positions past T in the last chunk enter with k = q = v = 0, g = 0, beta = 0, which leaves
+// every result unchanged.  Only differences gc_r - gc_i with r >= i are exponentiated.
+//
+// Work layout: one 256-thread workgroup per (batch, value head, 32-column tile of dv).  Value
+// columns of the state evolve independently, so column tiles are independent chains.  Everything
+// for one chunk lives in LDS in float32.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int SIMT_NT = 256;
+constexpr int SIMT_CMAX = 64;
+
+template <int DK, int BV>
+struct SimtLds {
+    static constexpr int KP = DK + 1;  // padded row pitch for K and Q
+    static constexpr int CP = SIMT_CMAX + 1;
+    static constexpr size_t k_off = 0;
+    static constexpr size_t q_off = k_off + (size_t)SIMT_CMAX * KP;
+    static constexpr size_t v_off = q_off + (size_t)SIMT_CMAX * KP;
+    static constexpr size_t h_off = v_off + (size_t)SIMT_CMAX * BV;
+    static constexpr size_t a_off = h_off + (size_t)DK * BV;
+    static constexpr size_t aq_off = a_off + (size_t)SIMT_CMAX * CP;
+    static constexpr size_t r_off = aq_off + (size_t)SIMT_CMAX * CP;
+    static constexpr size_t gc_off = r_off + (size_t)SIMT_CMAX * BV;
+    static constexpr size_t b_off = gc_off + SIMT_CMAX;
+    static constexpr size_t eg_off = b_off + SIMT_CMAX;
+    static constexpr size_t ed_off = eg_off + SIMT_CMAX;
+    static constexpr size_t floats = ed_off + SIMT_CMAX;
+    static constexpr size_t bytes = floats * sizeof(float);
+};
+
+}  // namespace
+
+template <typename T, int DK, int DV, int BV>
+__global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* s0, float* sf,  // may be the same buffer (in-place state update)
+    T* __restrict__ o, int T_len, int Hqk, int Hv, int grp, int C,
+    float scale)
+{
+    using L = SimtLds<DK, BV>;
+    extern __shared__ float lds[];
+    float* Ks = lds + L::k_off;
+    float* Qs = lds + L::q_off;
+    float* Vs = lds + L::v_off;
+    float* hs = lds + L::h_off;
+    float* As = lds + L::a_off;
+    float* Aq = lds + L::aq_off;
+    float* Rs = lds + L::r_off;
+    float* gcs = lds + L::gc_off;
+    float* bs = lds + L::b_off;
+    float* egs = lds + L::eg_off;   // exp(gc_r)
+    float* eds = lds + L::ed_off;   // exp(gc_C - gc_r)
+
+    const int head = blockIdx.x;    // b * Hv + j
+    const int b = head / Hv;
+    const int j = head - b * Hv;
+    const int i = j / grp;
+    const int c0 = blockIdx.y * BV; // first value column of this tile
+    const int tid = threadIdx.x;
+
+    // Entry state tile h[m][c] = state[b, j, m, c0 + c].
+    const size_t sbase = (size_t)head * DK * DV + c0;
+    for (int e = tid; e < DK * BV; e += SIMT_NT) {
+        const int m = e / BV, c = e % BV;
+        hs[e] = s0 ? s0[sbase + (size_t)m * DV + c] : 0.f;
+    }
+
+    for (int t0 = 0; t0 < T_len; t0 += C) {
+        const int n = min(C, T_len - t0);
+        __syncthreads();  // previous chunk finished with every LDS buffer
+        for (int e = tid; e < C * DK; e += SIMT_NT) {
+            const int r = e / DK, m = e % DK;
+            float kv = 0.f, qv = 0.f;
+            if (r < n) {
+                const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+                kv = to_f32(k[off]);
+                qv = to_f32(q[off]) * scale;
+            }
+            Ks[r * L::KP + m] = kv;
+            Qs[r * L::KP + m] = qv;
+        }
+        for (int e = tid; e < C * BV; e += SIMT_NT) {
+            const int r = e / BV, c = e % BV;
+            Vs[e] = r < n ? to_f32(v[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
+        }
+        if (tid < C) {
+            const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+            gcs[tid] = tid < n ? g[off] : 0.f;
+            bs[tid] = tid < n ? beta[off] : 0.f;
+        }
+        __syncthreads();
+        if (tid == 0) {  // per-chunk log-decay cumsum (C <= 64 terms)
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        }
+        __syncthreads();
+        if (tid < C) {
+            egs[tid] = expf(gcs[tid]);
+            eds[tid] = expf(gcs[C - 1] - gcs[tid]);
+        }
+        // A (strictly lower, beta-scaled) and the output mask matrix (lower incl. diagonal).
+        for (int e = tid; e < C * C; e += SIMT_NT) {
+            const int r = e / C, c = e % C;
+            float a = 0.f, aq = 0.f;
+            if (c <= r) {
+                float kk = 0.f, qk = 0.f;
+                for (int m = 0; m < DK; ++m) {
+                    kk = fmaf(Ks[r * L::KP + m], Ks[c * L::KP + m], kk);
+                    qk = fmaf(Qs[r * L::KP + m], Ks[c * L::KP + m], qk);
+                }
+                const float gam = expf(gcs[r] - gcs[c]);
+                aq = gam * qk;
+                if (c < r) a = bs[r] * gam * kk;
+            }
+            As[r * L::CP + c] = a;
+            Aq[r * L::CP + c] = aq;
+        }
+        __syncthreads();
+        // R = beta V - beta exp(gc) (K h0); keep exp(gc) (Q h0) for the output.
+        constexpr int PER = (SIMT_CMAX * BV + SIMT_NT - 1) / SIMT_NT;
+        float qh[PER];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * SIMT_NT;
+            qh[p] = 0.f;
+            if (e < C * BV) {
+                const int r = e / BV, c = e % BV;
+                float x = 0.f, y = 0.f;
+                for (int m = 0; m < DK; ++m) {
+                    const float hm = hs[m * BV + c];
+                    x = fmaf(Ks[r * L::KP + m], hm, x);
+                    y = fmaf(Qs[r * L::KP + m], hm, y);
+                }
+                Rs[e] = bs[r] * (Vs[e] - egs[r] * x);
+                qh[p] = egs[r] * y;
+            }
+        }
+        __syncthreads();
+        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column.
+        if (tid < BV) {
+            for (int r = 1; r < C; ++r) {
+                float acc = Rs[r * BV + tid];
+                for (int c = 0; c < r; ++c) acc = fmaf(-As[r * L::CP + c], Rs[c * BV + tid], acc);
+                Rs[r * BV + tid] = acc;
+            }
+        }
+        __syncthreads();
+        // O = exp(gc) Q h0 + Aq Delta
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = tid + p * SIMT_NT;
+            if (e < C * BV) {
+                const int r = e / BV, c = e % BV;
+                float acc = qh[p];
+                for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
+                if (r < n) o[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
+            }
+        }
+        // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T
+        const float ec = egs[C - 1];
+        for (int e = tid; e < DK * BV; e += SIMT_NT) {
+            const int m = e / BV, c = e % BV;
+            float acc = ec * hs[e];
+            for (int r = 0; r < C; ++r) acc = fmaf(eds[r] * Ks[r * L::KP + m], Rs[r * BV + c], acc);
+            hs[e] = acc;
+        }
+    }
+    __syncthreads();
+    if (sf) {
+        for (int e = tid; e < DK * BV; e += SIMT_NT) {
+            const int m = e / BV, c = e % BV;
+            sf[sbase + (size_t)m * DV + c] = hs[e];
+        }
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_simt_t(const ChunkArgs& a, hipStream_t st)
+{
+    constexpr int BV = DV < 32 ? DV : 32;
+    using L = SimtLds<DK, BV>;
+    auto kern = chunk_simt_kernel<T, DK, DV, BV>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)L::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BV), dim3(SIMT_NT), L::bytes, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, a.s0, a.sf,
+                       (T*)a.o, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_simt_dt(const ChunkArgs& a, hipStream_t st)
+{
+#define GDN_SIMT_CASE(DK_, DV_) \
+    if (a.dk == DK_ && a.dv == DV_) return launch_simt_t<T, DK_, DV_>(a, st);
+    GDN_SIMT_CASE(32, 32) GDN_SIMT_CASE(32, 64) GDN_SIMT_CASE(32, 128)
+    GDN_SIMT_CASE(64, 32) GDN_SIMT_CASE(64, 64) GDN_SIMT_CASE(64, 128)
+    GDN_SIMT_CASE(128, 32) GDN_SIMT_CASE(128, 64) GDN_SIMT_CASE(128, 128)
+#undef GDN_SIMT_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_simt(const ChunkArgs& a, hipStream_t st)
+{
+    if (a.chunk > SIMT_CMAX) return hipErrorInvalidValue;
+    return a.dtype_bf16 ? launch_simt_dt<bf16>(a, st) : launch_simt_dt<float>(a, st);
+}
+
+// T == 0: the final state is the initial state.
+__global__ void state_copy_kernel(const float* __restrict__ s0, float* __restrict__ sf, size_t n)
+{
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        sf[e] = s0 ? s0[e] : 0.f;
+}
+
+hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st)
+{
+    if (n == 0 || s0 == sf) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s0, sf, n);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

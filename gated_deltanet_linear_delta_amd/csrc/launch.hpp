@@ -1,0 +1,48 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.  Arguments arrive here
+// already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gdn {
+
+struct StepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* o;
+    int B, Hqk, Hv, dk, dv;
+    bool dtype_bf16;
+    float scale;
+};
+
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* s0;   // may be null (zero initial state)
+    float* sf;         // may be null (final state not wanted); may equal s0
+    void* o;
+    int B, T, Hqk, Hv, dk, dv, chunk;
+    bool dtype_bf16;
+    float scale;
+};
+
+hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
+
+// Float32-vector chunkwise kernel: any supported dtype, head dims and chunk size.
+hipError_t launch_chunk_simt(const ChunkArgs& a, hipStream_t st);
+
+// Fused matrix-core chunkwise kernel: bf16 inputs and the shapes chunk_mfma_supported accepts.
+bool chunk_mfma_supported(const ChunkArgs& a);
+hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t st);
+
+// final_state <- initial_state (or zeros when it is null), for T == 0.
+hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,134 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the gated delta rule (Gated DeltaNet core) on AMD MI355X (gfx950).
+ *
+ * The operation ("Architecture Thread I: Gated Attention, DeltaNet, and Hybrid Models", section
+ * "Gated DeltaNet", state-update equation; restated in "Gated Attention Architectures",
+ * section 3 "Gated DeltaNet", Mathematical Formulation), per batch row b and value head j:
+ *
+ *     S_t = S_{t-1} ( alpha_t (I - beta_t k_t k_t^T) ) + beta_t v_t k_t^T,      o_t = S_t q_t
+ *
+ * with S_t in R^{dv x dk}, alpha_t = exp(g_t) the decay gate and beta_t the write strength.  The
+ * readout o_t = S_t q_t is the linear-attention readout of "Gated Attention Architectures",
+ * section 1.  This library stores the state transposed, h = S^T, as [dk, dv] per head (the
+ * [d_k, d_v] memory of "Decoding Next-Generation LLM Architectures", section 3.2).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *    frees, or keeps a pointer after the call returns.  Tensors are dense, contiguous, row-major
+ *    in the layouts given.  q, k, v, o and the states must be 16-byte aligned; g and beta
+ *    4-byte aligned.
+ *  - q, k, v and o share one dtype (gdn_dtype_t).  g (= log alpha, any real value; g <= 0 is the
+ *    intended range, alpha in (0,1]), beta and the state are float32.
+ *  - Grouped heads: Hv must be a multiple of Hqk; value head j reads query/key head
+ *    floor(j / (Hv / Hqk)) (contiguous groups).
+ *  - q is multiplied by `scale` before the readout (1.0 gives o_t = S_t q_t exactly).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ *    without synchronising.  Results are valid once the stream has completed the work.
+ *  - Errors: every argument is validated before any device work is enqueued.  On an error
+ *    status nothing is enqueued and no output is touched.  GDN_ERR_LAUNCH means a kernel launch
+ *    failed; outputs are then undefined.
+ *  - The library is deterministic (no atomics: identical inputs give bit-identical outputs),
+ *    thread-safe and reentrant.  Calls that share output buffers must not overlap.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* a size is negative / zero where not allowed, or Hv % Hqk != 0 */
+    GDN_ERR_UNSUPPORTED = 3, /* head dim, chunk size or dtype outside the compiled variants */
+    GDN_ERR_ALIGN = 4,       /* a tensor is not 16-byte aligned (g, beta: 4-byte) */
+    GDN_ERR_WORKSPACE = 5,   /* workspace smaller than gdn_chunk_fwd_workspace_bytes() */
+    GDN_ERR_ALIAS = 6,       /* an output overlaps an input it may not overlap */
+    GDN_ERR_NO_DEVICE = 7,   /* no HIP device is visible */
+    GDN_ERR_LAUNCH = 8       /* a kernel launch failed (hipGetLastError) */
+} gdn_status_t;
+
+typedef enum {
+    GDN_F32 = 0,   /* q, k, v, o are float32 */
+    GDN_BF16 = 1   /* q, k, v, o are bfloat16; arithmetic accumulates in float32 */
+} gdn_dtype_t;
+
+/*
+ * gdn_chunk_fwd_workspace_bytes -- device scratch (bytes) that gdn_chunk_fwd needs for these
+ * sizes.  Returns 0 when no scratch is needed (the current kernels need none).  Pure host
+ * function; needs no device.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                     gdn_dtype_t dtype);
+
+/*
+ * gdn_chunk_fwd -- prefill: run the gated delta rule over T tokens for B sequences.
+ *
+ * Computed chunkwise ("Gated Attention Architectures", section 3: the DeltaNet WY representation
+ * extended with per-chunk cumulative decay products gamma_j = prod of alpha_i from the chunk
+ * start to position j).  Per chunk of `chunk` positions the kernels take the per-chunk
+ * log-decay cumsum, form the strictly lower matrix A = tril(diag(beta)(K K^T * Gamma), -1) with
+ * Gamma_ri = exp(gc_r - gc_i), apply (I + A)^{-1} (the UT/WY transform), carry the state across
+ * chunks in float32, and form O = (Q * exp(gc)) h + (Q K^T * Gamma) Delta.  The result equals the
+ * token-by-token recurrence up to rounding.
+ *
+ *   q, k           [B, T, Hqk, dk]   dtype
+ *   v              [B, T, Hv,  dv]   dtype
+ *   g, beta        [B, T, Hv]        float32   (g = log alpha_t)
+ *   initial_state  [B, Hv, dk, dv]   float32, or NULL for a zero initial state
+ *   final_state    [B, Hv, dk, dv]   float32 output, or NULL to skip; may equal initial_state
+ *                                    (updated in place) but may not partially overlap it
+ *   o              [B, T, Hv, dv]    dtype output; must not overlap any other argument
+ *   chunk          16, 32 or 64.  T need not be a multiple of chunk (the last chunk is partial).
+ *   dk, dv         32, 64 or 128 each.
+ *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes, or NULL
+ *                  when that is 0.
+ *   stream         hipStream_t (as void*), NULL for the default stream.
+ * B == 0 is a no-op.  T == 0 writes final_state (a copy of initial_state, or zeros) and no o.
+ */
+gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* initial_state, float* final_state,
+                           void* o, int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                           gdn_dtype_t dtype, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_recurrent_step -- decode: one token per sequence, state updated in place.
+ *
+ * One pass over the state per head (decoding is memory-bound: "The Transformer Isn't Alone
+ * Anymore", section "The hidden consequence: long context"; per-step cost O(d^2):
+ * "Gated Attention Architectures", summary comparison table).  Using the erase/write form of
+ * the update ("Architecture Thread I", DeltaNet section) with h = S^T:
+ *     u = h^T k,  delta = beta (v - alpha u),  h <- alpha h + k delta^T,  o = h^T (scale q)
+ *
+ *   q, k    [B, Hqk, dk]    dtype
+ *   v       [B, Hv, dv]     dtype
+ *   g, beta [B, Hv]         float32
+ *   state   [B, Hv, dk, dv] float32, read and overwritten in place
+ *   o       [B, Hv, dv]     dtype output; must not overlap any other argument
+ *   dk, dv  32, 64 or 128 each.
+ * B == 0 is a no-op.
+ */
+gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state, void* o, int B, int Hqk, int Hv,
+                                int dk, int dv, gdn_dtype_t dtype, float scale, void* stream);
+
+/*
+ * gdn_chunk_fwd_kernel_name -- which kernel family gdn_chunk_fwd would run for these sizes
+ * ("mfma" for the fused matrix-core kernel, "simt" for the float32-vector kernel), or NULL when
+ * the sizes are unsupported.  Pure host function.
+ */
+const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                      gdn_dtype_t dtype);
+
+/* gdn_status_string -- static, human-readable text for a status code (never NULL). */
+const char* gdn_status_string(gdn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every function include/gdn.h declares, and
+rejects every bad argument before touching the device (validation precedes any HIP call, so the
+fake pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_linear_delta_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, ALIAS, NODEV, LAUNCH = range(9)
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    lib = gdn.load_library()
+    names = header_functions()
+    assert set(names) == set(gdn.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nothing of the oracle leaked into the product library
+    with pytest.raises(AttributeError):
+        getattr(lib, "gdn_oracle_recurrent")
+
+
+def test_status_strings_and_queries():
+    for s in range(9):
+        assert gdn.gdn_status_string(s)
+    assert gdn.gdn_status_string(1234) == "unknown status"
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 32, 32, 16, gdn.GDN_F32) == "simt"
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 3, 32, 32, 16, gdn.GDN_F32) is None
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 48, 32, 16, gdn.GDN_F32) is None
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+BASE = 0x7F0000000000
+STRIDE = 1 << 36
+
+
+def fake(n):
+    return ctypes.c_void_p(BASE + n * STRIDE)
+
+
+def chunk_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), o=fake(7),
+             B=2, T=100, Hqk=2, Hv=4, dk=64, dv=32, chunk=32, dtype=gdn.GDN_BF16, scale=1.0,
+             ws=None, wsb=0, stream=None)
+    a.update(over)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["o"],
+                             a["B"], a["T"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["chunk"], a["dtype"],
+                             a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def step_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), state=fake(5), o=fake(7),
+             B=3, Hqk=2, Hv=4, dk=128, dv=64, dtype=gdn.GDN_F32, scale=1.0, stream=None)
+    a.update(over)
+    return lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"], a["B"],
+                                  a["Hqk"], a["Hv"], a["dk"], a["dv"], a["dtype"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(g=None), NULL),
+    (dict(beta=None), NULL), (dict(o=None), NULL),
+    (dict(B=-1), SHAPE), (dict(T=-5), SHAPE), (dict(Hqk=0), SHAPE), (dict(Hv=6, Hqk=4), SHAPE),
+    (dict(dk=0), SHAPE), (dict(chunk=0), SHAPE),
+    (dict(dk=96), UNSUP), (dict(dv=256), UNSUP), (dict(chunk=128), UNSUP), (dict(chunk=8), UNSUP),
+    (dict(dtype=7), UNSUP),
+    (dict(q=ctypes.c_void_p(BASE + 8)), ALIGN), (dict(s0=ctypes.c_void_p(BASE + 5 * STRIDE + 4)), ALIGN),
+    (dict(beta=ctypes.c_void_p(BASE + 4 * STRIDE + 1)), ALIGN),
+    (dict(o=fake(2)), ALIAS), (dict(o=ctypes.c_void_p(BASE + 64)), ALIAS),
+    (dict(sf=fake(7)), ALIAS), (dict(sf=fake(0)), ALIAS),
+    (dict(sf=ctypes.c_void_p(BASE + 5 * STRIDE + 256)), ALIAS),  # partial overlap with s0
+    (dict(o=fake(5)), ALIAS),
+])
+def test_chunk_fwd_rejects(over, status):
+    assert chunk_call(**over) == status
+
+
+def test_chunk_fwd_empty_batch_is_noop():
+    assert chunk_call(B=0, q=None, k=None, v=None, g=None, beta=None, o=None, s0=None, sf=None) == OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(state=None), NULL), (dict(o=None), NULL), (dict(q=None), NULL),
+    (dict(B=-2), SHAPE), (dict(Hv=3), SHAPE), (dict(dk=16), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(v=ctypes.c_void_p(BASE + 2 * STRIDE + 2)), ALIGN), (dict(g=ctypes.c_void_p(BASE + 3 * STRIDE + 2)), ALIGN),
+    (dict(o=fake(5)), ALIAS), (dict(state=fake(1)), ALIAS), (dict(o=fake(3)), ALIAS),
+])
+def test_recurrent_step_rejects(over, status):
+    assert step_call(**over) == status
+
+
+def test_recurrent_step_empty_batch_is_noop():
+    assert step_call(B=0) == OK
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_valid_calls_report_no_device():
+    assert chunk_call() == NODEV
+    assert chunk_call(sf=fake(5)) == NODEV  # in-place final state is allowed
+    assert chunk_call(T=0, o=None) == NODEV
+    assert step_call() == NODEV
+    assert step_call(g=ctypes.c_void_p(BASE + 3 * STRIDE + 4)) == NODEV  # 4-byte aligned gates are fine
+
+
+@pytest.mark.skipif(_has_gpu(), reason="needs a host without a GPU")
+def test_workspace_check_precedes_device():
+    assert chunk_call(wsb=0, ws=None) == NODEV

@@ -1,0 +1,197 @@
+"""Parity of the HIP library against the float64 oracle, on the same seeded inputs.
+
+Small shapes span several chunks and a ragged tail and are compared element by element over
+whole tensors; the five workload configurations are run in full on the GPU in the launch
+configuration the benchmark times, and compared on whole tensors (tiny and Qwen3-Next-shaped
+prefill) or on sampled (batch, value-head) chains that the oracle recomputes one by one."""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+from gpu_util import DEV, check, dev, f64, host, sample_chains, say
+
+gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(d, chunk, scale=1.0, want_state=True):
+    t = dev(d)
+    o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"],
+                              output_final_state=want_state, chunk=chunk, scale=scale)
+    torch.cuda.synchronize()
+    return host(o), (None if sf is None else host(sf))
+
+
+def oracle_prefill(d, scale=1.0):
+    return oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"], scale=scale)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128), (32, 128)])
+@pytest.mark.parametrize("Hqk,Hv", [(1, 1), (2, 4)])
+def test_decode_small(dtype, dk, dv, Hqk, Hv):
+    say(f"decode small dtype={dtype} dk={dk} dv={dv} Hqk={Hqk} Hv={Hv}")
+    cfg = gi.Config("s", B=3, T=1, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, chunk=64, dtype=dtype, mu=3.0,
+                    s0_std=0.05, seed=dk * 7 + dv + Hv, steps=5)
+    d = gi.generate_decode(cfg)
+    o_ref, s_ref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+    t = dev(d)
+    state = t["s0"].clone()
+    outs = []
+    for s in range(cfg.steps):
+        outs.append(gdn.gdn_recurrent_step(t["q"][s], t["k"][s], t["v"][s], t["g"][s], t["beta"][s], state))
+    torch.cuda.synchronize()
+    o = np.stack([host(x) for x in outs])
+    check(f"decode {dtype} {dk}x{dv}", dtype, o, o_ref, host(state), s_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv,C,T", [
+    (32, 32, 16, 128), (32, 32, 16, 1), (32, 64, 32, 77), (64, 64, 64, 130), (64, 32, 16, 49),
+    (128, 128, 64, 200), (128, 128, 32, 96), (128, 64, 64, 65), (32, 128, 64, 63), (128, 128, 16, 40),
+])
+def test_chunk_small(dtype, dk, dv, C, T):
+    say(f"chunk small dtype={dtype} dk={dk} dv={dv} C={C} T={T}")
+    d = gi.generate(B=2, T=T, Hqk=2, Hv=4, dk=dk, dv=dv, dtype=dtype, mu=3.0, s0_std=0.05,
+                    seed=T * 31 + dk + dv + C)
+    o_ref, s_ref = oracle_prefill(d)
+    o, s = run_prefill(d, C)
+    check(f"chunk {dtype} dk={dk} dv={dv} C={C} T={T}", dtype, o, o_ref, s, s_ref)
+
+
+def test_tiny_f32_config():
+    cfg = gi.CONFIGS["tiny_f32"]
+    say(f"config {cfg}")
+    d = gi.generate(cfg)
+    o_ref, s_ref = oracle_prefill(d)
+    o, s = run_prefill(d, cfg.chunk)
+    check("tiny_f32", "f32", o, o_ref, s, s_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_scale_and_no_final_state(dtype):
+    say(f"chunk scale dtype={dtype}")
+    d = gi.generate(B=1, T=70, Hqk=1, Hv=2, dk=64, dv=64, dtype=dtype, mu=2.0, s0_std=0.1, seed=5)
+    o_ref, _ = oracle_prefill(d, scale=0.125)
+    o, s = run_prefill(d, 32, scale=0.125, want_state=False)
+    assert s is None
+    check(f"scale {dtype}", dtype, o, o_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_in_place_state_and_resume(dtype):
+    """final_state == initial_state (in place); two calls over halves equal one call."""
+    say(f"chunk in-place/resume dtype={dtype}")
+    d = gi.generate(B=2, T=150, Hqk=2, Hv=2, dk=128, dv=128, dtype=dtype, mu=3.0, s0_std=0.05, seed=9)
+    o_ref, s_ref = oracle_prefill(d)
+    t = dev(d)
+    state = t["s0"].clone()
+    o1, _ = gdn.gdn_chunk_fwd(t["q"][:, :64].contiguous(), t["k"][:, :64].contiguous(), t["v"][:, :64].contiguous(),
+                              t["g"][:, :64].contiguous(), t["beta"][:, :64].contiguous(), state,
+                              final_state=state, chunk=64)
+    o2, _ = gdn.gdn_chunk_fwd(t["q"][:, 64:].contiguous(), t["k"][:, 64:].contiguous(), t["v"][:, 64:].contiguous(),
+                              t["g"][:, 64:].contiguous(), t["beta"][:, 64:].contiguous(), state,
+                              final_state=state, chunk=64)
+    torch.cuda.synchronize()
+    o = np.concatenate([host(o1), host(o2)], axis=1)
+    check(f"resume {dtype}", dtype, o, o_ref, host(state), s_ref)
+
+
+def test_chunk_empty_sequence_and_batch():
+    say("chunk T=0 / B=0")
+    d = gi.generate(B=2, T=0, Hqk=1, Hv=1, dk=32, dv=32, dtype="f32", mu=3.0, s0_std=0.1, seed=3)
+    t = dev(d)
+    o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=16)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 1, 32)
+    np.testing.assert_array_equal(host(sf), d["s0"])
+    o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], None, chunk=16)
+    torch.cuda.synchronize()
+    assert not host(sf).any()
+    d = gi.generate(B=0, T=5, Hqk=1, Hv=1, dk=32, dv=32, dtype="bf16", mu=3.0, s0_std=0.0, seed=3)
+    t = dev(d)
+    o, sf = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], None, chunk=16)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 5, 1, 32) and sf.shape == (0, 1, 32, 32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps_equal_prefill(dtype):
+    """T single-token decode steps reach the prefill's outputs and state (both vs the oracle,
+    and against each other)."""
+    say(f"decode == prefill dtype={dtype}")
+    d = gi.generate(B=2, T=40, Hqk=1, Hv=2, dk=128, dv=128, dtype=dtype, mu=3.0, s0_std=0.05, seed=21)
+    o_p, s_p = run_prefill(d, 16)
+    t = dev(d)
+    state = t["s0"].clone()
+    outs = []
+    for s in range(40):
+        outs.append(gdn.gdn_recurrent_step(t["q"][:, s].contiguous(), t["k"][:, s].contiguous(),
+                                           t["v"][:, s].contiguous(), t["g"][:, s].contiguous(),
+                                           t["beta"][:, s].contiguous(), state))
+    torch.cuda.synchronize()
+    o_d = np.stack([host(x) for x in outs], axis=1)
+    check(f"decode-vs-prefill {dtype}", dtype, o_d, o_p, host(state), s_p)
+
+
+def test_deterministic():
+    say("determinism")
+    d = gi.generate(B=1, T=300, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=4)
+    t = dev(d)
+    r1 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    r2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+def test_qwen3next_prefill_full():
+    cfg = gi.CONFIGS["qwen3next_prefill"]
+    say(f"config {cfg}")
+    d = gi.generate(cfg)
+    o, s = run_prefill(d, cfg.chunk)
+    o_ref, s_ref = oracle_prefill(d)
+    check("qwen3next_prefill", "bf16", o, o_ref, s, s_ref)
+
+
+@pytest.mark.parametrize("name,chains", [
+    ("batched_prefill", [(0, 0), (3, 17), (7, 31), (5, 8)]),
+    ("qwen36_long_prefill", [(0, 0), (0, 1), (0, 23), (0, 47)]),
+])
+def test_large_prefill_sampled(name, chains):
+    cfg = gi.CONFIGS[name]
+    say(f"config {cfg}, sampled chains {chains}")
+    d = gi.generate(cfg)
+    o, s = run_prefill(d, cfg.chunk)
+    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
+    o_ref, s_ref = oracle_prefill(sd)
+    o_s = np.stack([o[b, :, j] for b, j in chains])[:, :, None]
+    s_s = np.stack([s[b, j] for b, j in chains])[:, None]
+    check(name, "bf16", o_s, o_ref, s_s, s_ref)
+
+
+def test_decode_config_sampled():
+    cfg = gi.CONFIGS["decode"]
+    say(f"config {cfg}")
+    d = gi.generate_decode(cfg)
+    t = dev(d)
+    state = t["s0"].clone()
+    o = torch.empty((cfg.steps, cfg.B, cfg.Hv, cfg.dv), dtype=torch.bfloat16, device=DEV)
+    for s in range(cfg.steps):
+        gdn.gdn_recurrent_step(t["q"][s], t["k"][s], t["v"][s], t["g"][s], t["beta"][s], state, o=o[s])
+    torch.cuda.synchronize()
+    chains = [(0, 0), (17, 5), (100, 31), (255, 16), (128, 1), (64, 30), (3, 9), (200, 22)]
+    grp = cfg.Hv // cfg.Hqk
+    pick = lambda a, hd: np.stack([a[:, b, hd(j)] for b, j in chains], axis=1)
+    qs = pick(d["q"], lambda j: j // grp)[:, :, None]
+    ks = pick(d["k"], lambda j: j // grp)[:, :, None]
+    vs = pick(d["v"], lambda j: j)[:, :, None]
+    gs = pick(d["g"], lambda j: j)[:, :, None]
+    bs = pick(d["beta"], lambda j: j)[:, :, None]
+    s0 = np.stack([d["s0"][b, j] for b, j in chains])[:, None]
+    o_ref, s_ref = oracle.decode(f64(qs), f64(ks), f64(vs), gs, bs, s0)
+    oh = host(o)
+    o_s = np.stack([oh[:, b, j] for b, j in chains], axis=1)[:, :, None]
+    sh = state[[b for b, _ in chains], [j for _, j in chains]]
+    check("decode config", "bf16", o_s, o_ref, host(sh)[:, None], s_ref)
