@@ -1,0 +1,267 @@
+"""Benchmark of the gated delta rule on one MI355X.
+
+A step is one gdn_chunk_fwd (chunkwise prefill) over one batch of the Qwen3-Next-shaped GDN
+workload: B=1, T=4096, 16 query/key heads, 32 value heads, head dim 128, chunk 64, bf16 inputs,
+float32 state.  `value` is prefill tokens/s with the inputs resident in HBM; rotating input sets
+(larger than the 256 MB Infinity Cache) keep every step's reads cold.
+
+The same JSON line carries
+  roofline      -- the prefill kernel's achieved algorithmic bytes/s against 8 TB/s (its binding
+                   roofline: 167 flop/B is below the bf16-MFMA/HBM ridge), the kernel's average
+                   launch duration from HIP events on its own stream, its bf16-MFMA fraction, and
+                   the HBM traffic measured with rocprofv3 counters when a matching record exists;
+  cpu_baseline  -- the float64 oracle timed on the host cores on the same workload;
+  decode        -- the 64-step fused decode workload (B=256, Hv=32, d=128, fp32 state 512 MiB):
+                   steps/s and achieved HBM bandwidth;
+  prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3.6-27B-shaped (T=65536, Hv=48)
+                   prefill workloads, tokens/s and roofline fractions.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5166e15  # flop/s, MI355X dense bf16 matrix cores
+CSRC = os.path.join(ROOT, "gated_deltanet_linear_delta_amd", "csrc")
+
+
+def prefill_alg_bytes(B, T, Hqk, Hv, dk, dv, es, with_s0, with_sf):
+    """Algorithmic HBM bytes of one prefill: q, k once per query/key head, v and o once, g and
+    beta in float32, initial and final state in float32."""
+    n = B * T
+    b = n * Hqk * dk * es * 2 + n * Hv * dv * es * 2 + n * Hv * 4 * 2
+    st = B * Hv * dk * dv * 4
+    return b + (st if with_s0 else 0) + (st if with_sf else 0)
+
+
+def prefill_alg_flops(B, T, Hqk, Hv, dk, dv, C):
+    """Algorithmic flops of the chunkwise method per token and value head (masked halves
+    excluded): 6 dk dv (W h, Q h, K^T Delta) + C dk (W) + 2 C dv (U, Aqk Delta)
+    + 2 C dk / G (K K^T, Q K^T shared by the G value heads of a group) + C^2 / 3 (the solve)."""
+    G = Hv // Hqk
+    per = 6 * dk * dv + C * dk + 2 * C * dv + 2 * C * dk / G + C * C / 3
+    return per * B * T * Hv
+
+
+def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
+    """Per step: the float32 state read and written once, q and k per query/key head, v and o per
+    value head, g and beta in float32."""
+    return B * Hv * dk * dv * 4 * 2 + B * Hqk * dk * es * 2 + B * Hv * dv * es * 2 + B * Hv * 4 * 2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the prefill kernel from the committed rocprofv3 counter record,
+    if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_chunk_fwd_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def time_launches(fn, n_sets, steps, warmup, torch):
+    """Warm up, then time exactly `steps` launches: one (start, end) HIP event pair per launch on
+    the current stream (the one the library launches on), sync-bracketed wall clock around all."""
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(st)
+        fn(i % n_sets)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) * 1e-3 for a, b in evs]
+    return wall, sum(kern) / len(kern)
+
+
+def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20):
+    dev = "cuda:0"
+    base = gi.generate_torch(cfg, dev)
+    es = 2 if cfg.dtype == "bf16" else 4
+    per_set = prefill_alg_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, es, cfg.s0_std > 0, True)
+    n_sets = max(1, min(8, -(-min_bytes // per_set)))
+    sets = [base]
+    for s in range(1, n_sets):
+        sets.append({n: (None if t is None else t.clone()) for n, t in base.items()})
+    outs = [torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=base["q"].dtype, device=dev) for _ in range(n_sets)]
+    sfs = [torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+
+    def fn(i):
+        x = sets[i]
+        gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
+                          o=outs[i], final_state=sfs[i])
+
+    wall, kern = time_launches(fn, n_sets, steps, warmup, torch)
+    flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
+    del sets, outs, sfs
+    torch.cuda.empty_cache()
+    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets,
+                kernel=gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv,
+                                                     cfg.chunk, gdn.GDN_BF16 if es == 2 else gdn.GDN_F32))
+
+
+def bench_decode(cfg, torch, gdn, gi, repeats=3):
+    dev = "cuda:0"
+    x = gi.generate_torch(cfg, dev, decode_steps=cfg.steps)
+    state = torch.empty_like(x["s0"])
+    o = torch.empty((cfg.steps, cfg.B, cfg.Hv, cfg.dv), dtype=x["q"].dtype, device=dev)
+    st = torch.cuda.current_stream()
+    best = None
+    kern_all = []
+    for r in range(repeats + 1):  # first round is warm-up
+        state.copy_(x["s0"])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cfg.steps)]
+        t0 = time.perf_counter()
+        for s in range(cfg.steps):
+            evs[s][0].record(st)
+            gdn.gdn_recurrent_step(x["q"][s], x["k"][s], x["v"][s], x["g"][s], x["beta"][s], state, o=o[s])
+            evs[s][1].record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if r == 0:
+            continue
+        kern_all += [a.elapsed_time(b) * 1e-3 for a, b in evs]
+        best = wall if best is None else min(best, wall)
+    es = 2 if cfg.dtype == "bf16" else 4
+    per_step = decode_alg_bytes(cfg.B, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, es)
+    kern = sum(kern_all) / len(kern_all)
+    del x, state, o
+    torch.cuda.empty_cache()
+    return dict(wall64=best, kern=kern, bytes=per_step)
+
+
+def cpu_baseline(cfg, gi, min_seconds=10.0, max_repeats=30):
+    """The float64 oracle on the same workload (whole batch), repeated until about min_seconds."""
+    import numpy as np
+    import oracle
+    d = gi.generate(cfg)
+    f = lambda a: gi.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+    q, k, v = f(d["q"]), f(d["k"]), f(d["v"])
+    threads = len(os.sched_getaffinity(0))
+    reps, t_total = 0, 0.0
+    while reps < max_repeats and t_total < min_seconds:
+        t0 = time.perf_counter()
+        oracle.recurrent(q, k, v, d["g"], d["beta"], d["s0"], threads=threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    tokens = cfg.B * cfg.T * reps
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {cfg.name} batch (B={cfg.B}, T={cfg.T}, Hv={cfg.Hv}) x {reps} runs, "
+                      f"{t_total:.1f} s, float64 token-by-token recurrence, OpenMP over {cfg.B * cfg.Hv} chains"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3next_prefill")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the gated delta rule shards by (batch, head) with no "
+              "exchange, so only --gpus 1 is run here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4, "copies": 3}))
+        return
+    import gdn_inputs as gi
+    import gated_deltanet_linear_delta_amd as gdn
+
+    gdn.load_library()
+    cfg = gi.CONFIGS[args.workload]
+    print(f"bench: prefill {cfg}", file=sys.stderr, flush=True)
+    r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi)
+    tokens = cfg.B * cfg.T
+    ms = r["wall"] / args.steps * 1e3
+    achieved = r["bytes"] / r["kern"]
+    traffic = measured_traffic(cfg.name)
+    line = {
+        "metric": "GDN prefill tokens/sec + % MFMA peak; decode steps/sec + HBM GB/s, 1 MI355X",
+        "value": tokens * args.steps / r["wall"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hqk": cfg.Hqk, "Hv": cfg.Hv,
+                   "dk": cfg.dk, "dv": cfg.dv, "chunk": cfg.chunk, "state": "float32",
+                   "initial_state": cfg.s0_std > 0, "input_sets": r["n_sets"]},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": traffic,
+                     "kernel": f"chunk_fwd ({r['kernel']})", "kernel_ms": r["kern"] * 1e3,
+                     "alg_bytes": r["bytes"], "alg_flops": r["flops"],
+                     "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, gi)
+    if not args.quick:
+        dcfg = gi.CONFIGS["decode"]
+        print(f"bench: decode {dcfg}", file=sys.stderr, flush=True)
+        dr = bench_decode(dcfg, torch, gdn, gi)
+        bw = dr["bytes"] / dr["kern"]
+        line["decode"] = {"workload": dcfg.name, "B": dcfg.B, "Hv": dcfg.Hv, "d": dcfg.dk, "steps": dcfg.steps,
+                          "steps_per_s": dcfg.steps / dr["wall64"], "ms_64_steps": dr["wall64"] * 1e3,
+                          "kernel_us": dr["kern"] * 1e6, "alg_bytes_per_step": dr["bytes"],
+                          "hbm_GBps": bw / 1e9, "hbm_frac": bw / HBM_PEAK,
+                          "tokens_per_s": dcfg.steps * dcfg.B / dr["wall64"]}
+        pc = {}
+        for name in ("batched_prefill", "qwen36_long_prefill"):
+            c = gi.CONFIGS[name]
+            print(f"bench: prefill {c}", file=sys.stderr, flush=True)
+            rr = bench_prefill(c, 5, 2, torch, gdn, gi)
+            pc[name] = {"tokens_per_s": c.B * c.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
+                        "mfma_frac": rr["flops"] / rr["kern"] / MFMA_BF16_PEAK,
+                        "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
+        line["prefill_configs"] = pc
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
