@@ -1,7 +1,7 @@
 // Fused chunkwise gated delta rule on the gfx950 matrix cores (bf16 inputs, float16 matrix
-// operands, float32 state and accumulation).  One workgroup of four waves carries one (batch,
-// value head, column tile) chain through every chunk of the sequence; nothing but the inputs, O
-// and the states touches HBM.
+// operands, float32 state and accumulation).  One workgroup carries one (batch, value head,
+// column tile) chain through every chunk of the sequence; nothing but the inputs, O and the
+// states touches HBM.
 //
 // Chunk algebra (the WY/UT form named in "Gated Attention Architectures", section 3: the DeltaNet
 // WY representation of section 2 extended with per-chunk cumulative decay products).  Rows are
@@ -17,20 +17,30 @@
 // the last chunk enter as zeros with g = beta = 0, which changes no result.
 //
 // gfx950 mapping
+// * Two kinds of waves in one workgroup, in a two-stage software pipeline.  Four "prep" waves
+//   build everything of chunk n+1 that does not depend on the state (the cumsum, K K^T, Q K^T,
+//   the decay masks and T = (I + A)^{-1}) and stage the inputs in LDS, while four "chain" waves
+//   carry the state through chunk n.  Each chain wave owns BV/4 state columns (value columns
+//   evolve independently), so the state never leaves its registers.  Four workgroup barriers per
+//   chunk; buffers are double-buffered only where a prep write would meet a chain read.
 // * Matrix products use v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16, D 16x16 float32).  A lane
 //   holds D rows 4*(lane/16)+i of column lane%16.  Two D tiles stacked along rows therefore give
 //   a lane the rows {4g..4g+3, 16+4g..16+4g+3}: used as the B operand of a product over those
 //   rows, they need only that the A operand is read with the same permutation of k ("perm-K").
-//   The state h (MFMA accumulators) feeds K h and Q h, and Delta feeds (Aqk Delta) and
-//   (K^T Delta) straight from registers; only A operands come from LDS.
-// * Each wave owns BV/4 state columns (value columns are independent chains), so the state never
-//   leaves the wave's registers between chunks.
-// * T = (I + A)^{-1}: the four 16x16 diagonal blocks are inverted by forward substitution in
-//   float32 (one wave per block), then merged 16 -> 32 -> 64 with matrix products:
+//   The state h feeds K h and Q h, and Delta feeds (Aqk Delta) and (K^T Delta) from registers.
+// * K^T operands and V in accumulator layout are read straight from the row-major K and V tiles
+//   with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group the
+//   sixteen 8-byte reads form a 16x4 matrix D and lane i receives D[i/4 + 4j][i%4], j = 0..3.
+// * T: the four 16x16 diagonal blocks are inverted by forward substitution in float32 (one prep
+//   wave per block), then merged 16 -> 32 -> 64 with matrix products:
 //   T_21 = -T_22 A_21 T_11 (16x16x16), then T_hi,lo = -T_hi (A_hi,lo T_lo) (16x16x32).
-// * The next chunk's q, k, v, g, beta are loaded into registers while the current chunk computes.
+// * Operands are float16: the same MFMA rate as bf16 on gfx950 with a 3-bit longer significand.
+//   q and k arrive as bf16 and convert exactly (up to float16 subnormals, far below what matters
+//   next to unit-norm rows); every other operand is rounded once from float32.
+// * Row pitches are padded so that the 8- and 16-byte fragment reads of 8 consecutive rows
+//   cover all 64 LDS banks once.
 // * Workgroups of one query/key head (its value heads and column tiles read the same q, k) are
-//   placed on the same XCD so that the second read of q and k hits that XCD's L2.
+//   placed on the same XCD so that repeated reads of q and k hit that XCD's L2.
 #include <stdlib.h>
 
 #include "device_common.hpp"
@@ -40,37 +50,36 @@ namespace gdn {
 
 namespace {
 
-// Matrix-core operands are float16: the same MFMA rate as bf16 on gfx950 with a 3-bit longer
-// significand.  q and k arrive as bf16 and convert to float16 exactly (up to float16 subnormals,
-// far below what matters next to unit-norm rows); everything else is rounded once from float32.
 typedef _Float16 op_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 opx8;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 opx4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
 
-constexpr int CH = 64;          // chunk length
-constexpr int NW = 4;           // waves per workgroup
-constexpr int NTHR = NW * 64;
-constexpr int CP = CH + 8;      // element pitch of [*, 64] matrices (T, Aqk, K^T)
-constexpr int AFP = CH + 4;     // float pitch of the float32 A matrix
+constexpr int CH = 64;            // chunk length
+constexpr int NPW = 4;            // prep waves
+constexpr int NCW = 4;            // chain waves
+constexpr int NTHR = (NPW + NCW) * 64;
+constexpr int CP = CH + 8;        // element pitch of [64][64] fp16 matrices (T, Aqk)
+constexpr int AFP = CH + 4;       // float pitch of the float32 A matrix
 
 template <int DK, int BV>
 struct MLds {
-    static constexpr int KP = DK + 8;    // element pitch of K and Q rows
-    static constexpr int VP = BV + 8;    // bf16 pitch of V and O rows
-    static constexpr size_t ks = 0;                                     // K   [64][KP] f16
-    static constexpr size_t qs = ks + (size_t)CH * KP * 2;              // Q   [64][KP] f16
-    static constexpr size_t kt = qs + (size_t)CH * KP * 2;              // K^T [DK][CP] f16
-    static constexpr size_t vs = kt + (size_t)DK * CP * 2;              // V   [64][VP] bf16
-    static constexpr size_t os = vs + (size_t)CH * VP * 2;              // O   [64][VP] bf16
-    static constexpr size_t tm = os + (size_t)CH * VP * 2;              // T   [64][CP] f16
-    static constexpr size_t aq = tm + (size_t)CH * CP * 2;              // Aqk [64][CP] f16
-    static constexpr size_t af = aq + (size_t)CH * CP * 2;              // A   [64][AFP] f32
-    static constexpr size_t vec = af + (size_t)CH * AFP * 4;            // 8 x [64] f32
-    static constexpr size_t bytes = vec + (size_t)8 * CH * 4;
+    static constexpr int KP = DK + 8;            // element pitch of K and Q rows
+    static constexpr int VP = BV + 16;           // element pitch of V rows
+    static constexpr int NCOL = BV / NCW;        // state columns per chain wave
+    static constexpr size_t kq_bytes = (size_t)CH * KP * 2;
+    static constexpr size_t ks = 0;                                 // K   [2][64][KP] f16
+    static constexpr size_t qs = ks + 2 * kq_bytes;                 // Q   [2][64][KP] f16
+    static constexpr size_t vs = qs + 2 * kq_bytes;                 // V   [64][VP] bf16
+    static constexpr size_t tm = vs + (size_t)CH * VP * 2;          // T   [64][CP] f16
+    static constexpr size_t aq = tm + (size_t)CH * CP * 2;          // Aqk [64][CP] f16
+    static constexpr size_t af = aq + (size_t)CH * CP * 2;          // A^T [64][AFP] f32
+    static constexpr size_t vec = af + (size_t)CH * AFP * 4;        // [2][8][64] f32
+    static constexpr size_t bytes = vec + (size_t)2 * 8 * CH * 4;
 };
 
-// vec slots
-constexpr int V_G = 0;     // raw g, then gc (inclusive cumsum)
+// per-chunk vectors (slot of 8 x 64 floats)
+constexpr int V_G = 0;     // gc (inclusive cumsum of g within the chunk)
 constexpr int V_B = 1;     // beta
 constexpr int V_EG = 2;    // exp(gc)
 constexpr int V_BEG = 3;   // beta exp(gc)
@@ -86,20 +95,42 @@ __device__ __forceinline__ floatx4 mfma16(opx4 a, opx4 b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// A-operand fragment of a 32-wide k block, perm-K order: row `row`, elements
-// [kb + 4g .. kb + 4g + 3] then [kb + 16 + 4g .. kb + 16 + 4g + 3] of a row-major matrix.
-__device__ __forceinline__ opx8 frag_perm(const op_t* m, int pitch, int row, int kb, int g)
+// Column order of every float16 matrix in LDS (K, Q, T, Aqk): within each 32-column block the
+// 4-column groups are stored in the order 0, 4, 1, 5, 2, 6, 3, 7, so that lane group g's perm-K
+// set {4g..4g+3, 16+4g..16+4g+3} is one contiguous 16-byte run.  LDS costs about the same per
+// instruction for 8 and 16 bytes, so this halves the fragment reads.
+__device__ __forceinline__ int pcol(int c)
 {
-    const op_t* p = m + row * pitch + kb + 4 * g;
-    const opx4 lo = *reinterpret_cast<const opx4*>(p);
-    const opx4 hi = *reinterpret_cast<const opx4*>(p + 16);
-    return opx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const int q = (c >> 2) & 7;
+    const int p = q < 4 ? 2 * q : 2 * (q - 4) + 1;
+    return (c & ~31) + 4 * p + (c & 3);
 }
 
-// Standard-order fragment: elements [kb + 8g .. kb + 8g + 7] of row `row`.
-__device__ __forceinline__ opx8 frag_std(const op_t* m, int pitch, int row, int kb, int g)
+// Fragment of a column-permuted matrix: physical elements [kb + 8g .. kb + 8g + 7] of row `row`,
+// which are the logical perm-K elements of lane group g (also a valid standard-order fragment
+// when both operands of a product are read this way, as for K K^T and Q K^T).
+__device__ __forceinline__ opx8 frag(const op_t* m, int pitch, int row, int kb, int g)
 {
     return *reinterpret_cast<const opx8*>(m + row * pitch + kb + 8 * g);
+}
+
+// Transposing LDS read (see the header comment): returns four 16-bit values.
+__device__ __forceinline__ shortx4 ld_tr(const void* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4*)(const_cast<void*>(p)));
+}
+
+// K^T A operand (perm-K over chunk positions) for the 16 dk rows of tile mt: lane (row ml,
+// group g) gets K[kb + 4g + j][16mt + ml] and K[kb + 16 + 4g + j][16mt + ml], j = 0..3, from the
+// column-permuted K (logical columns 16mt + 4q .. +3 sit at physical 32(mt/2) + 4(2q + mt%2)).
+__device__ __forceinline__ opx8 frag_kt(const op_t* k, int pitch, int mt, int kb, int lane)
+{
+    const int m = lane & 15, g = lane >> 4;
+    const op_t* p = k + (kb + 4 * g + (m >> 2)) * pitch + 32 * (mt >> 1) + 4 * (2 * (m & 3) + (mt & 1));
+    const opx4 lo = __builtin_bit_cast(opx4, ld_tr(p));
+    const opx4 hi = __builtin_bit_cast(opx4, ld_tr(p + 16 * pitch));
+    return opx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // Two stacked D tiles (rows 0-15 in `a`, 16-31 in `b`) as a perm-K B operand.
@@ -119,7 +150,7 @@ __device__ __forceinline__ floatx4 ld4s(const float* p) { return *reinterpret_ca
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
 // global loads and stores (__syncthreads would also drain those, exposing a full HBM round trip
-// of the next chunk's prefetch at every barrier).  Waves exchange data only through LDS here.
+// of the prefetch at every barrier).  Waves exchange data only through LDS here.
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -136,26 +167,22 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
 {
     using L = MLds<DK, BV>;
     constexpr int NTILE = DV / BV;
-    constexpr int NCOL = BV / NW;       // state columns per wave
-    constexpr int NTN = NCOL / 16;      // 16-column tiles per wave
+    constexpr int NCOL = L::NCOL;       // state columns per chain wave
+    constexpr int NTN = NCOL / 16;      // 16-column tiles per chain wave
     constexpr int MT = DK / 16;         // 16-row tiles of the state
     constexpr int KB = DK / 32;         // 32-wide k blocks over dk
-    constexpr int SEGK = CH * DK / 8;   // 16-byte segments of a K (or Q) chunk
-    constexpr int SEGV = CH * BV / 8;   // 16-byte segments of a V chunk tile
-    constexpr int PK = SEGK / NTHR;
-    constexpr int PV = SEGV / NTHR;
-    static_assert(NTN >= 1 && SEGK % NTHR == 0 && SEGV % NTHR == 0, "tile shape");
+    constexpr int PK = CH * DK / 8 / (NPW * 64);   // 16-byte K (or Q) segments per prep lane
+    constexpr int PV = CH * BV / 8 / (NPW * 64);   // 16-byte V segments per prep lane
+    static_assert(NTN >= 1 && PK >= 1 && PV >= 1, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    op_t* Ks = reinterpret_cast<op_t*>(smem + L::ks);
-    op_t* Qs = reinterpret_cast<op_t*>(smem + L::qs);
-    op_t* KT = reinterpret_cast<op_t*>(smem + L::kt);
     bf16* Vs = reinterpret_cast<bf16*>(smem + L::vs);
-    bf16* Os = reinterpret_cast<bf16*>(smem + L::os);
     op_t* Tm = reinterpret_cast<op_t*>(smem + L::tm);
     op_t* Aq = reinterpret_cast<op_t*>(smem + L::aq);
     float* Af = reinterpret_cast<float*>(smem + L::af);
-    float* vec = reinterpret_cast<float*>(smem + L::vec);
+    auto Kslot = [&](int s) { return reinterpret_cast<op_t*>(smem + L::ks + (size_t)s * L::kq_bytes); };
+    auto Qslot = [&](int s) { return reinterpret_cast<op_t*>(smem + L::qs + (size_t)s * L::kq_bytes); };
+    auto vslot = [&](int s) { return reinterpret_cast<float*>(smem + L::vec) + s * 8 * CH; };
 
     // ---- which chain this workgroup carries
     int lid = blockIdx.x;
@@ -174,7 +201,12 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const int lane = tid & 63;
     const int ln = lane & 15;      // MFMA column / row-in-tile index
     const int lg = lane >> 4;      // MFMA lane group
+    const bool is_prep = w < NPW;
+    const int pw = w;              // prep wave index (prep waves)
+    const int cw = w - NPW;        // chain wave index (chain waves)
+    const int ptid = tid;          // prep thread index 0..255 (prep waves)
 
+    const int NT = (T_len + CH - 1) / CH;
     const size_t qk_row = (size_t)Hqk * DK;   // elements between consecutive tokens of q, k
     const size_t v_row = (size_t)Hv * DV;
     const bf16* qb = q + ((size_t)b * T_len * Hqk + i) * DK;
@@ -184,369 +216,475 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const float* gb = g + (size_t)b * T_len * Hv + j;
     const float* bb = beta + (size_t)b * T_len * Hv + j;
 
-    // ---- zero the parts of T and Aqk that no chunk writes (upper blocks)
-    for (int e = tid; e < CH * CP; e += NTHR) {
-        Tm[e] = (op_t)0.f;
-        Aq[e] = (op_t)0.f;
-    }
-
-    // ---- entry state in MFMA accumulator layout: hacc[nt][mt][x] = h[16mt + 4lg + x][col]
-    floatx4 hacc[NTN][MT];
-#pragma unroll
-    for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) hacc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (s0) {
-        const float* sp = s0 + ((size_t)b * Hv + j) * DK * DV + c0 + w * NCOL + ln;
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) hacc[nt][mt][x] = sp[(size_t)(16 * mt + 4 * lg + x) * DV + nt * 16];
-    }
-
-    // ---- global -> register staging of one chunk.  Loads are unconditional (rows past T are
-    // clamped to the last valid row) and rows past T are zeroed only when written to LDS, so no
-    // load destination is written early and the prefetch never waits on earlier memory traffic.
+    // =====================================================================================
+    // prep-wave state: prefetch registers and the parts of T it keeps between phases
     bf16x8 rk[PK], rq[PK], rv[PV];
     float rg = 0.f, rb = 0.f;
-    int n_pref = 0;
-    auto load_chunk = [&](int t0) {
-        const int n = min(CH, T_len - t0);
-        n_pref = n;
+    float tcol[16];
+    opx4 tb = {};
+    floatx4 t10 = {0.f, 0.f, 0.f, 0.f};
+
+    // loads of chunk c's q, k, g, beta (rows past T clamped; zeroed when staged)
+    auto load_kq = [&](int c) {
+        const int t0 = c * CH, n = min(CH, T_len - t0);
 #pragma unroll
         for (int p = 0; p < PK; ++p) {
-            const int s = tid + p * NTHR;
+            const int s = ptid + p * NPW * 64;
             const int r = min(s / (DK / 8), n - 1), c8 = (s % (DK / 8)) * 8;
             const size_t off = (size_t)(t0 + r) * qk_row + c8;
             rk[p] = *reinterpret_cast<const bf16x8*>(kb_ + off);
             rq[p] = *reinterpret_cast<const bf16x8*>(qb + off);
         }
-#pragma unroll
-        for (int p = 0; p < PV; ++p) {
-            const int s = tid + p * NTHR;
-            const int r = min(s / (BV / 8), n - 1), c8 = (s % (BV / 8)) * 8;
-            rv[p] = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + r) * v_row + c8);
-        }
-        if (w == 0) {
+        if (pw == 0) {
             const size_t off = (size_t)(t0 + min(lane, n - 1)) * Hv;
             rg = gb[off];
             rb = bb[off];
         }
     };
-    auto store_chunk = [&]() {
-        const int n = n_pref;
-#pragma unroll
-        for (int p = 0; p < PK; ++p) {
-            const int s = tid + p * NTHR;
-            const int r = s / (DK / 8), c8 = (s % (DK / 8)) * 8;
-            const bool live = r < n;
-            *reinterpret_cast<opx8*>(Ks + r * L::KP + c8) = live ? to_op(rk[p]) : opx8{};
-            *reinterpret_cast<opx8*>(Qs + r * L::KP + c8) = live ? to_op(rq[p]) : opx8{};
-        }
+    auto load_v = [&](int c) {
+        const int t0 = c * CH, n = min(CH, T_len - t0);
 #pragma unroll
         for (int p = 0; p < PV; ++p) {
-            const int s = tid + p * NTHR;
-            const int r = s / (BV / 8), c8 = (s % (BV / 8)) * 8;
-            *reinterpret_cast<bf16x8*>(Vs + r * L::VP + c8) = r < n ? rv[p] : bf16x8{};
-        }
-        if (w == 0) {
-            vec[V_G * CH + lane] = lane < n ? rg : 0.f;
-            vec[V_B * CH + lane] = lane < n ? rb : 0.f;
+            const int s = ptid + p * NPW * 64;
+            const int r = min(s / (BV / 8), n - 1), c8 = (s % (BV / 8)) * 8;
+            rv[p] = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + r) * v_row + c8);
         }
     };
-
-    load_chunk(0);
-    store_chunk();
-
-    for (int t0 = 0; t0 < T_len; t0 += CH) {
-        const int n = min(CH, T_len - t0);
-        const bool has_next = t0 + CH < T_len;
-        lds_barrier();                                   // chunk t0 staged in LDS
-        if (has_next) load_chunk(t0 + CH);                 // in flight during this chunk
-
-        // ---- (1) per-chunk log-decay cumsum and per-row factors (wave 0); K^T (all waves)
-        if (w == 0) {
-            float x = vec[V_G * CH + lane];
+    // stage chunk c's q, k (float16) into slot c&1, and its per-row vectors (wave 0 scans g)
+    auto stage_kq = [&](int c) {
+        const int n = min(CH, T_len - c * CH);
+        op_t* Ks = Kslot(c & 1);
+        op_t* Qs = Qslot(c & 1);
+#pragma unroll
+        for (int p = 0; p < PK; ++p) {
+            const int s = ptid + p * NPW * 64;
+            const int r = s / (DK / 8), c8 = (s % (DK / 8)) * 8;
+            const bool live = r < n;
+            const opx8 kv = live ? to_op(rk[p]) : opx8{};
+            const opx8 qv = live ? to_op(rq[p]) : opx8{};
+            op_t* kr = Ks + r * L::KP;
+            op_t* qr = Qs + r * L::KP;
+            *reinterpret_cast<opx4*>(kr + pcol(c8)) = opx4{kv[0], kv[1], kv[2], kv[3]};
+            *reinterpret_cast<opx4*>(kr + pcol(c8 + 4)) = opx4{kv[4], kv[5], kv[6], kv[7]};
+            *reinterpret_cast<opx4*>(qr + pcol(c8)) = opx4{qv[0], qv[1], qv[2], qv[3]};
+            *reinterpret_cast<opx4*>(qr + pcol(c8 + 4)) = opx4{qv[4], qv[5], qv[6], qv[7]};
+        }
+        if (pw == 0) {
+            float x = lane < n ? rg : 0.f;
+            const float bt = lane < n ? rb : 0.f;
 #pragma unroll
             for (int s = 1; s < 64; s <<= 1) {
                 const float y = __shfl_up(x, s, 64);
                 if (lane >= s) x += y;
             }
             const float last = __shfl(x, 63, 64);
-            const float bt = vec[V_B * CH + lane];
             const float eg = __expf(x);
-            vec[V_G * CH + lane] = x;
-            vec[V_EG * CH + lane] = eg;
-            vec[V_BEG * CH + lane] = bt * eg;
-            vec[V_ED * CH + lane] = __expf(last - x);
+            float* vs = vslot(c & 1);
+            vs[V_G * CH + lane] = x;
+            vs[V_B * CH + lane] = bt;
+            vs[V_EG * CH + lane] = eg;
+            vs[V_BEG * CH + lane] = bt * eg;
+            vs[V_ED * CH + lane] = __expf(last - x);
         }
-        // K^T[m][c] = K[c][m]: each thread assembles 8 consecutive c of one row m
-        for (int s = tid; s < DK * (CH / 8); s += NTHR) {
-            const int m = s % DK, c8 = (s / DK) * 8;
-            opx8 t;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = Ks[(c8 + e) * L::KP + m];
-            *reinterpret_cast<opx8*>(KT + m * CP + c8) = t;
-        }
-        lds_barrier();
-
-        // ---- (2) K K^T and Q K^T on the 10 lower 16x16 tiles each; masks and decays applied
-        {
-            // tile lists per wave: (is_qk, ti, tj)
-            const int gcl = ln;                      // column within tile
-            auto do_tile = [&](bool qk, int ti, int tj) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb2 = 0; kb2 < DK; kb2 += 32) {
-                    const opx8 a = frag_std(qk ? Qs : Ks, L::KP, 16 * ti + ln, kb2, lg);
-                    const opx8 bm = frag_std(Ks, L::KP, 16 * tj + ln, kb2, lg);
-                    acc = mfma32(a, bm, acc);
-                }
-                const int c = 16 * tj + gcl;
-                const float gcc = vec[V_G * CH + c];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 16 * ti + 4 * lg + x;
-                    const float gam = c <= r ? __expf(vec[V_G * CH + r] - gcc) : 0.f;
-                    if (qk) {
-                        Aq[r * CP + c] = (op_t)(gam * acc[x]);
-                    } else {
-                        Af[r * AFP + c] = c < r ? vec[V_B * CH + r] * gam * acc[x] : 0.f;
-                    }
-                }
-            };
-            if (w == 0) {
-                for (int tj = 0; tj < 4; ++tj) do_tile(false, 3, tj);
-                do_tile(true, 0, 0);
-            } else if (w == 1) {
-                for (int tj = 0; tj < 3; ++tj) do_tile(false, 2, tj);
-                for (int tj = 0; tj < 2; ++tj) do_tile(true, 1, tj);
-            } else if (w == 2) {
-                do_tile(false, 0, 0);
-                for (int tj = 0; tj < 2; ++tj) do_tile(false, 1, tj);
-                for (int tj = 0; tj < 3; ++tj) do_tile(true, 2, tj);
-            } else {
-                for (int tj = 0; tj < 4; ++tj) do_tile(true, 3, tj);
-            }
-        }
-        lds_barrier();
-
-        // ---- (3) T = (I + A)^{-1}
-        // (3a) diagonal block w: column ln of (I + A_ww)^{-1} by forward substitution (float32)
-        float tcol[16];
-        {
-            const float* Ab = Af + (16 * w) * AFP + 16 * w;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-                for (int x = 0; x < r; ++x) s = fmaf(-Ab[r * AFP + x], tcol[x], s);
-                tcol[r] = s;
-            }
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                float val = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) val = (r == 4 * lg + x) ? tcol[r] : val;
-                Tm[(16 * w + 4 * lg + x) * CP + 16 * w + ln] = (op_t)val;
-            }
-        }
-        // this lane's B-operand view of its block: rows 4lg..4lg+3 of column ln
-        opx4 tb;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            float val = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) val = (r == 4 * lg + x) ? tcol[r] : val;
-            tb[x] = (op_t)val;
-        }
-        lds_barrier();
-        // (3b) T_{w+1,w} = -T_{w+1,w+1} A_{w+1,w} T_ww for w in {0, 2}
-        floatx4 t10 = {0.f, 0.f, 0.f, 0.f};
-        if (w == 0 || w == 2) {
-            const floatx4 af = ld4s(Af + (16 * (w + 1) + ln) * AFP + 16 * w + 4 * lg);
-            const opx4 aa = {(op_t)af[0], (op_t)af[1], (op_t)af[2], (op_t)af[3]};
-            const floatx4 p = mfma16(aa, tb, floatx4{0.f, 0.f, 0.f, 0.f});
-            const opx4 pb = {(op_t)p[0], (op_t)p[1], (op_t)p[2], (op_t)p[3]};
-            const opx4 td = *reinterpret_cast<const opx4*>(Tm + (16 * (w + 1) + ln) * CP + 16 * (w + 1) + 4 * lg);
-            t10 = mfma16(td, pb, floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                t10[x] = -t10[x];
-                Tm[(16 * (w + 1) + 4 * lg + x) * CP + 16 * w + ln] = (op_t)t10[x];
-            }
-        }
-        lds_barrier();
-        // (3c) T[32:64, 0:32] = -T_hi (A[32:64, 0:32] T_lo); wave w in {0,1} takes column tile w
-        if (w < 2) {
-            // T_lo[:, 16w + ln] as a perm-K B operand: rows {4lg..+3} then {16 + 4lg..+3}
-            opx8 tlo;
-            if (w == 0) {
-                tlo = opx8{tb[0], tb[1], tb[2], tb[3], (op_t)t10[0], (op_t)t10[1], (op_t)t10[2], (op_t)t10[3]};
-            } else {
-                tlo = opx8{(op_t)0.f, (op_t)0.f, (op_t)0.f, (op_t)0.f, tb[0], tb[1], tb[2], tb[3]};
-            }
-            floatx4 q1[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const float* ar = Af + (32 + 16 * a + ln) * AFP;
-                const floatx4 lo = ld4s(ar + 4 * lg);
-                const floatx4 hi = ld4s(ar + 16 + 4 * lg);
-                const opx8 aa = {(op_t)lo[0], (op_t)lo[1], (op_t)lo[2], (op_t)lo[3],
-                                 (op_t)hi[0], (op_t)hi[1], (op_t)hi[2], (op_t)hi[3]};
-                q1[a] = mfma32(aa, tlo, floatx4{0.f, 0.f, 0.f, 0.f});
-            }
-            const opx8 q1b = pack_perm(q1[0], q1[1]);
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const opx8 th = frag_perm(Tm, CP, 32 + 16 * a + ln, 32, lg);
-                floatx4 r = mfma32(th, q1b, floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int x = 0; x < 4; ++x) Tm[(32 + 16 * a + 4 * lg + x) * CP + 16 * w + ln] = (op_t)(-r[x]);
-            }
-        }
-        lds_barrier();
-
-        // ---- (4) the chain: X = K h, Y = Q h, R, Delta = T R, O, h update
-        const float ec = __expf(vec[V_G * CH + 63]);
-        {
-            opx8 hb[NTN][KB];
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = pack_perm(hacc[nt][2 * kk], hacc[nt][2 * kk + 1]);
-
-            floatx4 X[NTN][4], Y[NTN][4];
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    X[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                    Y[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) {
-                    const opx8 ak = frag_perm(Ks, L::KP, 16 * mt + ln, 32 * kk, lg);
-                    const opx8 aqf = frag_perm(Qs, L::KP, 16 * mt + ln, 32 * kk, lg);
-#pragma unroll
-                    for (int nt = 0; nt < NTN; ++nt) {
-                        X[nt][mt] = mfma32(ak, hb[nt][kk], X[nt][mt]);
-                        Y[nt][mt] = mfma32(aqf, hb[nt][kk], Y[nt][mt]);
-                    }
-                }
-            // R = beta V - beta exp(gc) X  (rows 16mt + 4lg + x)
-            opx8 rbf[NTN][2];
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt) {
-                const int col = w * NCOL + nt * 16 + ln;
-                floatx4 rr[4];
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const int r0 = 16 * mt + 4 * lg;
-                    const floatx4 bt = ld4s(vec + V_B * CH + r0);
-                    const floatx4 beg = ld4s(vec + V_BEG * CH + r0);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        rr[mt][x] = bt[x] * (float)Vs[(r0 + x) * L::VP + col] - beg[x] * X[nt][mt][x];
-                }
-                rbf[nt][0] = pack_perm(rr[0], rr[1]);
-                rbf[nt][1] = pack_perm(rr[2], rr[3]);
-            }
-            // Delta = T R (T lower triangular: row tile mt needs k blocks <= mt/2)
-            floatx4 D[NTN][4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) D[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int cb = 0; cb <= mt / 2; ++cb) {
-                    const opx8 at = frag_perm(Tm, CP, 16 * mt + ln, 32 * cb, lg);
-#pragma unroll
-                    for (int nt = 0; nt < NTN; ++nt) D[nt][mt] = mfma32(at, rbf[nt][cb], D[nt][mt]);
-                }
-            }
-            opx8 db[NTN][2], dtb[NTN][2];
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    db[nt][cb] = pack_perm(D[nt][2 * cb], D[nt][2 * cb + 1]);
-                    const floatx4 e0 = ld4s(vec + V_ED * CH + 32 * cb + 4 * lg);
-                    const floatx4 e1 = ld4s(vec + V_ED * CH + 32 * cb + 16 + 4 * lg);
-                    floatx4 d0 = D[nt][2 * cb], d1 = D[nt][2 * cb + 1];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        d0[x] *= e0[x];
-                        d1[x] *= e1[x];
-                    }
-                    dtb[nt][cb] = pack_perm(d0, d1);
-                }
-            // O = scale (exp(gc) Y + Aqk Delta), staged in LDS as bf16 rows
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const floatx4 eg = ld4s(vec + V_EG * CH + 16 * mt + 4 * lg);
-                floatx4 oacc[NTN];
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) oacc[nt][x] = eg[x] * Y[nt][mt][x];
-#pragma unroll
-                for (int cb = 0; cb <= mt / 2; ++cb) {
-                    const opx8 aa = frag_perm(Aq, CP, 16 * mt + ln, 32 * cb, lg);
-#pragma unroll
-                    for (int nt = 0; nt < NTN; ++nt) oacc[nt] = mfma32(aa, db[nt][cb], oacc[nt]);
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) {
-                    const int col = w * NCOL + nt * 16 + ln;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        Os[(16 * mt + 4 * lg + x) * L::VP + col] = (bf16)(scale * oacc[nt][x]);
-                }
-            }
-            // h <- exp(gc_63) h + K^T (exp(gc_63 - gc) Delta)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const opx8 akt = frag_perm(KT, CP, 16 * mt + ln, 32 * cb, lg);
-#pragma unroll
-                    for (int nt = 0; nt < NTN; ++nt) hacc[nt][mt] = mfma32(akt, dtb[nt][cb], hacc[nt][mt]);
-                }
-            }
-        }
-        lds_barrier();                                   // O staged; chunk buffers free
-        // ---- (5) next chunk -> LDS, O rows -> global (16-byte stores).  The store loop has a
-        // fixed trip count so the compiler can count outstanding memory operations exactly and
-        // the next chunk's prefetch never waits for these stores to land.
-        if (has_next) store_chunk();
+    };
+    auto stage_v = [&](int c) {
+        const int n = min(CH, T_len - c * CH);
 #pragma unroll
         for (int p = 0; p < PV; ++p) {
-            const int s = tid + p * NTHR;
+            const int s = ptid + p * NPW * 64;
             const int r = s / (BV / 8), c8 = (s % (BV / 8)) * 8;
-            const bf16x8 val = *reinterpret_cast<const bf16x8*>(Os + r * L::VP + c8);
-            if (r < n) *reinterpret_cast<bf16x8*>(ob + (size_t)(t0 + r) * v_row + c8) = val;
+            *reinterpret_cast<bf16x8*>(Vs + r * L::VP + c8) = r < n ? rv[p] : bf16x8{};
         }
-    }
-
-    // ---- final state
-    if (sf) {
-        const size_t sb = ((size_t)b * Hv + j) * DK * DV + c0;
+    };
+    // NTL 16x16 tiles (ti[t], tj[t]) of K K^T (qk = false, into A^T) or Q K^T (qk = true, into
+    // Aqk) of chunk c, with the decay mask and beta applied.  The k-block loop is outermost so the
+    // tiles' MFMAs interleave instead of waiting on each other.
+    auto gram_tiles = [&](int c, bool qk, const auto& ti, const auto& tj) {
+        constexpr int NTL = sizeof(ti) / sizeof(ti[0]);
+        const op_t* Ks = Kslot(c & 1);
+        const op_t* Xs = qk ? Qslot(c & 1) : Ks;
+        const float* vs = vslot(c & 1);
+        opx8 af[NTL][KB], bf[NTL][KB];
 #pragma unroll
-        for (int nt = 0; nt < NTN; ++nt) {
-            const int col = w * NCOL + nt * 16 + ln;
+        for (int t = 0; t < NTL; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int kk = 0; kk < KB; ++kk) {
+                af[t][kk] = frag(Xs, L::KP, 16 * ti[t] + ln, 32 * kk, lg);
+                bf[t][kk] = frag(Ks, L::KP, 16 * tj[t] + ln, 32 * kk, lg);
+            }
+        floatx4 acc[NTL];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) sf[sb + (size_t)(16 * mt + 4 * lg + x) * DV + col] = hacc[nt][mt][x];
+        for (int t = 0; t < NTL; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) acc[t] = mfma32(af[t][kk], bf[t][kk], acc[t]);
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            const int cc = 16 * tj[t] + ln;
+            const int r0 = 16 * ti[t] + 4 * lg;
+            const float gcc = vs[V_G * CH + cc];
+            const floatx4 gr = ld4s(vs + V_G * CH + r0);
+            const floatx4 br = ld4s(vs + V_B * CH + r0);
+            floatx4 out;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float gam = cc <= r0 + x ? __expf(gr[x] - gcc) : 0.f;
+                out[x] = qk ? gam * acc[t][x] : (cc < r0 + x ? br[x] * gam * acc[t][x] : 0.f);
+            }
+            if (qk) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) Aq[(r0 + x) * CP + pcol(cc)] = (op_t)out[x];
+            } else {
+                *reinterpret_cast<floatx4*>(Af + cc * AFP + r0) = out;   // A^T[cc][r0..r0+3]
+            }
+        }
+    };
+    if (is_prep) {
+        // ================================================================= prep waves
+        // zero the parts of T and Aqk that no chunk writes (upper blocks)
+        for (int e = ptid; e < CH * CP; e += NPW * 64) {
+            Tm[e] = (op_t)0.f;
+            Aq[e] = (op_t)0.f;
+        }
+        load_kq(0);
+        load_v(0);
+        stage_kq(0);
+        if (NT > 1) load_kq(1);
+        lds_barrier();
+        // iteration n: build chunk n + 1 while the chain waves carry chunk n
+        for (int n = -1; n < NT; ++n) {
+            const bool on = n + 1 < NT;
+            const int c = n + 1;
+            // interval 1: K K^T tiles of chunk c -> A (10 lower tiles: 3, 3, 2, 2 per wave)
+            if (on) {
+                if (pw == 0) gram_tiles(c, false, (const int[3]){3, 3, 3}, (const int[3]){0, 1, 2});
+                else if (pw == 1) gram_tiles(c, false, (const int[3]){3, 2, 2}, (const int[3]){3, 0, 1});
+                else if (pw == 2) gram_tiles(c, false, (const int[2]){2, 1}, (const int[2]){2, 0});
+                else gram_tiles(c, false, (const int[2]){1, 0}, (const int[2]){1, 0});
+            }
+            lds_barrier();
+            // interval 2: diagonal block pw of T, (I + A_ww)^{-1} column ln by right-looking
+            // forward substitution in float32 (after row x is final, every later row takes its
+            // update at once, so the dependent chain is 15 steps long); stage V of chunk c,
+            // prefetch V of chunk c + 1
+            if (on) {
+                const float* At = Af + (16 * pw) * AFP + 16 * pw;   // At[x * AFP + r] = A_ww[r][x]
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tcol[r] = (r == ln) ? 1.f : 0.f;
+#pragma unroll
+                for (int x = 0; x < 15; ++x) {
+                    floatx4 col[4];
+#pragma unroll
+                    for (int q4 = (x + 1) / 4; q4 < 4; ++q4) col[q4] = ld4s(At + x * AFP + 4 * q4);
+#pragma unroll
+                    for (int r = x + 1; r < 16; ++r) tcol[r] = fmaf(-col[r / 4][r % 4], tcol[x], tcol[r]);
+                }
+                // lanes of group 0 write the column; each lane reads back its rows 4lg..4lg+3
+                // (same wave, so the LDS writes are seen in order)
+                op_t* tc = Tm + (16 * pw) * CP + pcol(16 * pw + ln);
+                if (lg == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) tc[r * CP] = (op_t)tcol[r];
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x) tb[x] = tc[(4 * lg + x) * CP];
+                stage_v(c);
+                if (c + 1 < NT) load_v(c + 1);
+            }
+            lds_barrier();
+            // interval 3: T_{w+1,w} = -T_{w+1,w+1} A_{w+1,w} T_ww for w in {0, 2};
+            // Q K^T tiles of chunk c -> Aqk (10 lower tiles including the diagonal)
+            if (on) {
+                if (pw == 0 || pw == 2) {
+                    const float* at = Af + (16 * pw + 4 * lg) * AFP + 16 * (pw + 1) + ln;
+                    const opx4 aa = {(op_t)at[0], (op_t)at[AFP], (op_t)at[2 * AFP], (op_t)at[3 * AFP]};
+                    const floatx4 p = mfma16(aa, tb, floatx4{0.f, 0.f, 0.f, 0.f});
+                    const opx4 pb = {(op_t)p[0], (op_t)p[1], (op_t)p[2], (op_t)p[3]};
+                    const opx4 td = *reinterpret_cast<const opx4*>(Tm + (16 * (pw + 1) + ln) * CP + pcol(16 * (pw + 1) + 4 * lg));
+                    t10 = mfma16(td, pb, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        t10[x] = -t10[x];
+                        Tm[(16 * (pw + 1) + 4 * lg + x) * CP + pcol(16 * pw + ln)] = (op_t)t10[x];
+                    }
+                }
+                if (pw == 0) gram_tiles(c, true, (const int[3]){3, 3, 3}, (const int[3]){0, 1, 2});
+                else if (pw == 1) gram_tiles(c, true, (const int[3]){3, 2, 2}, (const int[3]){3, 0, 1});
+                else if (pw == 2) gram_tiles(c, true, (const int[2]){2, 1}, (const int[2]){2, 0});
+                else gram_tiles(c, true, (const int[2]){1, 0}, (const int[2]){1, 0});
+            }
+            lds_barrier();
+            // interval 4: T[32:64, 0:32] = -T_hi (A[32:64, 0:32] T_lo), waves 0, 1 (column tile pw);
+            // stage q, k of chunk n + 2 into slot n&1 (the chain waves finished with it in
+            // interval 3) and prefetch chunk n + 3
+            if (on && pw < 2) {
+                opx8 tlo;
+                if (pw == 0) {
+                    tlo = opx8{tb[0], tb[1], tb[2], tb[3], (op_t)t10[0], (op_t)t10[1], (op_t)t10[2], (op_t)t10[3]};
+                } else {
+                    tlo = opx8{(op_t)0.f, (op_t)0.f, (op_t)0.f, (op_t)0.f, tb[0], tb[1], tb[2], tb[3]};
+                }
+                floatx4 q1[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const float* ac = Af + (4 * lg) * AFP + 32 + 16 * a + ln;
+                    const opx8 aa = {(op_t)ac[0], (op_t)ac[AFP], (op_t)ac[2 * AFP], (op_t)ac[3 * AFP],
+                                     (op_t)ac[16 * AFP], (op_t)ac[17 * AFP], (op_t)ac[18 * AFP], (op_t)ac[19 * AFP]};
+                    q1[a] = mfma32(aa, tlo, floatx4{0.f, 0.f, 0.f, 0.f});
+                }
+                const opx8 q1b = pack_perm(q1[0], q1[1]);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const opx8 th = frag(Tm, CP, 32 + 16 * a + ln, 32, lg);
+                    const floatx4 r = mfma32(th, q1b, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) Tm[(32 + 16 * a + 4 * lg + x) * CP + pcol(16 * pw + ln)] = (op_t)(-r[x]);
+                }
+            }
+            if (n + 2 < NT) {
+                stage_kq(n + 2);
+                if (n + 3 < NT) load_kq(n + 3);
+            }
+            lds_barrier();
+        }
+    } else {
+        // ================================================================= chain waves
+        // the state columns in MFMA accumulator layout,
+        // hacc[nt][mt][x] = h[16mt + 4lg + x][cw*NCOL + 16nt + ln]
+        floatx4 hacc[NTN][MT];
+        opx8 hb[NTN][KB];
+        opx8 db[NTN][2], dtb[NTN][2];
+        // With one 16-column tile per wave the Q fragments for interval 2 are loaded in interval 1
+        // and the K^T fragments for interval 3 in interval 2; with two tiles the registers do not
+        // allow it and each product loads its fragments when its interval starts.
+        constexpr bool PRE = NTN == 1;
+        opx8 aqf[KB][4];
+        opx8 akt[2][MT];
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) hacc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (s0) {
+            const float* sp = s0 + ((size_t)b * Hv + j) * DK * DV + c0 + cw * NCOL + ln;
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) hacc[nt][mt][x] = sp[(size_t)(16 * mt + 4 * lg + x) * DV + nt * 16];
+        }
+        lds_barrier();
+        // iteration n: carry chunk n (the prep waves build chunk n + 1 meanwhile); the same
+        // four barriers per iteration as the prep waves
+        for (int n = -1; n < NT; ++n) {
+            const bool on = n >= 0;
+            const op_t* Ks = Kslot(n & 1);
+            const op_t* Qs = Qslot(n & 1);
+            const float* vs = vslot(n & 1);
+            // interval 1: X = K h, R = beta V - beta exp(gc) X, Delta = T R; then the Q fragments
+            // for interval 2 are loaded (Q of chunk n stays in LDS until interval 4).  Every
+            // product's A fragments are loaded before its MFMAs, behind a scheduling barrier, so
+            // the LDS latency is paid once per product rather than once per MFMA.
+            if (on) {
+                // K fragments: all up front with one tile per wave; with two tiles (twice the MFMAs
+                // per k block) one k block ahead, which keeps the registers within budget
+                constexpr int AHEAD = PRE ? KB : 1;
+                opx8 ak[KB][4];
+#pragma unroll
+                for (int kk = 0; kk < AHEAD; ++kk)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, L::KP, 16 * mt + ln, 32 * kk, lg);
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = pack_perm(hacc[nt][2 * kk], hacc[nt][2 * kk + 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                floatx4 X[NTN][4];
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) X[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    if (kk + AHEAD < KB) {
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            ak[kk + AHEAD][mt] = frag(Ks, L::KP, 16 * mt + ln, 32 * (kk + AHEAD), lg);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) X[nt][mt] = mfma32(ak[kk][mt], hb[nt][kk], X[nt][mt]);
+                }
+                // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
+                bf16x4 vv[NTN][4];
+                floatx4 bt[4], beg[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                    for (int nt = 0; nt < NTN; ++nt)
+                        vv[nt][mt] = __builtin_bit_cast(bf16x4, ld_tr(Vs + (16 * mt + 4 * lg + (ln >> 2)) * L::VP +
+                                                                       cw * NCOL + 16 * nt + 4 * (ln & 3)));
+                    bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
+                    beg[mt] = ld4s(vs + V_BEG * CH + 16 * mt + 4 * lg);
+                }
+                opx8 at[4][2];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
+                opx8 rbf[NTN][2];
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt) {
+                    floatx4 rr[4];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) rr[mt][x] = bt[mt][x] * (float)vv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
+                    rbf[nt][0] = pack_perm(rr[0], rr[1]);
+                    rbf[nt][1] = pack_perm(rr[2], rr[3]);
+                }
+                // Delta = T R (T lower triangular: row tile mt needs k blocks cb <= mt/2)
+                floatx4 D[NTN][4];
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) D[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int mt = 2 * cb; mt < 4; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) D[nt][mt] = mfma32(at[mt][cb], rbf[nt][cb], D[nt][mt]);
+                floatx4 ed[2][2];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    ed[cb][0] = ld4s(vs + V_ED * CH + 32 * cb + 4 * lg);
+                    ed[cb][1] = ld4s(vs + V_ED * CH + 32 * cb + 16 + 4 * lg);
+                }
+                if constexpr (PRE) {
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt) aqf[kk][mt] = frag(Qs, L::KP, 16 * mt + ln, 32 * kk, lg);
+                }
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int nt = 0; nt < NTN; ++nt) {
+                        db[nt][cb] = pack_perm(D[nt][2 * cb], D[nt][2 * cb + 1]);
+                        floatx4 d0 = D[nt][2 * cb], d1 = D[nt][2 * cb + 1];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            d0[x] *= ed[cb][0][x];
+                            d1[x] *= ed[cb][1][x];
+                        }
+                        dtb[nt][cb] = pack_perm(d0, d1);
+                    }
+            }
+            lds_barrier();
+            // interval 2: Y = Q h, O = scale (exp(gc) Y + Aqk Delta) -> HBM; then the K^T
+            // fragments for interval 3
+            if (on) {
+                const int t0 = n * CH, nv = min(CH, T_len - t0);
+                if constexpr (!PRE) {
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt) aqf[kk][mt] = frag(Qs, L::KP, 16 * mt + ln, 32 * kk, lg);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                opx8 aa[4][2];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int cb = 0; cb <= ct / 2; ++cb) aa[ct][cb] = frag(Aq, CP, 16 * ct + ln, 32 * cb, lg);
+                float eg[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) eg[ct] = vs[V_EG * CH + 16 * ct + ln];
+                // O is formed transposed, O^T = (h^T Q^T) diag(exp(gc)) + Delta^T Aqk^T: the same
+                // fragments with the operand roles swapped, and the accumulator layout then gives
+                // each lane four consecutive value columns of one token (one 8-byte store).
+                floatx4 OT[NTN][4];
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) OT[nt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(hb[nt][kk], aqf[kk][ct], OT[nt][ct]);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) OT[nt][ct][x] *= eg[ct];
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int ct = 2 * cb; ct < 4; ++ct)
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(db[nt][cb], aa[ct][cb], OT[nt][ct]);
+                if constexpr (PRE) {
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) akt[cb][mt] = frag_kt(Ks, L::KP, mt, 32 * cb, lane);
+                }
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int tok = 16 * ct + ln;
+                    if (tok < nv) {
+                        bf16* op = ob + (size_t)(t0 + tok) * v_row + cw * NCOL + 4 * lg;
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) {
+                            const bf16x4 ov = {(bf16)(scale * OT[nt][ct][0]), (bf16)(scale * OT[nt][ct][1]),
+                                               (bf16)(scale * OT[nt][ct][2]), (bf16)(scale * OT[nt][ct][3])};
+                            *reinterpret_cast<bf16x4*>(op + 16 * nt) = ov;
+                        }
+                    }
+                }
+            }
+            lds_barrier();
+            // interval 3: h <- exp(gc_63) h + K^T (exp(gc_63 - gc) Delta)
+            if (on) {
+                if constexpr (!PRE) {
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) akt[cb][mt] = frag_kt(Ks, L::KP, mt, 32 * cb, lane);
+                }
+                const float ec = __expf(vs[V_G * CH + 63]);
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NTN; ++nt) hacc[nt][mt] = mfma32(akt[cb][mt], dtb[nt][cb], hacc[nt][mt]);
+            }
+            lds_barrier();
+            // interval 4: nothing for the chain waves (the prep waves finish T and restage q, k)
+            lds_barrier();
+        }
+        // ---- final state
+        if (sf) {
+            float* sp = sf + ((size_t)b * Hv + j) * DK * DV + c0 + cw * NCOL + ln;
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) sp[(size_t)(16 * mt + 4 * lg + x) * DV + nt * 16] = hacc[nt][mt][x];
         }
     }
 }
@@ -570,6 +708,7 @@ template <int DK, int DV, int BV>
 hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st)
 {
     using L = MLds<DK, BV>;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
     auto kern = chunk_mfma_kernel<DK, DV, BV>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
