@@ -113,19 +113,22 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20):
         sets.append({n: (None if t is None else t.clone()) for n, t in base.items()})
     outs = [torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=base["q"].dtype, device=dev) for _ in range(n_sets)]
     sfs = [torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev) for _ in range(n_sets)]
+    dt = gdn.GDN_BF16 if es == 2 else gdn.GDN_F32
+    need = gdn.gdn_chunk_fwd_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk, dt)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
 
     def fn(i):
         x = sets[i]
         gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
-                          o=outs[i], final_state=sfs[i])
+                          o=outs[i], final_state=sfs[i], workspace=ws)
 
     wall, kern = time_launches(fn, n_sets, steps, warmup, torch)
     flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
-    del sets, outs, sfs
+    del sets, outs, sfs, ws
     torch.cuda.empty_cache()
-    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets,
+    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets, workspace=need,
                 kernel=gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv,
-                                                     cfg.chunk, gdn.GDN_BF16 if es == 2 else gdn.GDN_F32))
+                                                     cfg.chunk, dt))
 
 
 def bench_decode(cfg, torch, gdn, gi, repeats=3):
@@ -235,6 +238,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK,
                      "traffic": traffic,
                      "kernel": f"chunk_fwd ({r['kernel']})", "kernel_ms": r["kern"] * 1e3,
+                     "workspace_bytes": r["workspace"],
                      "alg_bytes": r["bytes"], "alg_flops": r["flops"],
                      "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK},
     }

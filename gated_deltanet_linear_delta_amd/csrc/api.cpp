@@ -49,8 +49,6 @@ const char* gdn_status_string(gdn_status_t s)
     return "unknown status";
 }
 
-size_t gdn_chunk_fwd_workspace_bytes(int, int, int, int, int, int, int, gdn_dtype_t) { return 0; }
-
 static gdn_status_t check_chunk_sizes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                       gdn_dtype_t dtype)
 {
@@ -73,13 +71,23 @@ static gdn::ChunkArgs make_chunk_args(const void* q, const void* k, const void* 
     return a;
 }
 
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                     gdn_dtype_t dtype)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return 0;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    return gdn::chunk_mfma_workspace_bytes(a);
+}
+
 const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                       gdn_dtype_t dtype)
 {
     if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return nullptr;
     gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
-    return gdn::chunk_mfma_supported(a) ? "mfma" : "simt";
+    if (!gdn::chunk_mfma_supported(a)) return "simt";
+    return gdn::chunk_mfma_split(a) ? "mfma_split" : "mfma";
 }
 
 gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -90,11 +98,12 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
 {
     gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
     if (s != GDN_OK) return s;
-    if (workspace_bytes < gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
-        return GDN_ERR_WORKSPACE;
+    const size_t need = gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
     if (B == 0) return GDN_OK;
     const bool work = T > 0;
     if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
     const void* ptrs[] = {q, k, v, initial_state, final_state, o, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
@@ -116,6 +125,10 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
             return GDN_ERR_ALIAS;
         }
     if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    const Range rw = range(workspace, need);
+    const Range all[] = {rq, rk, rv, rg, rb, rs0, rsf, ro};
+    for (const Range& r : all)
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
     s = device_ok();
     if (s != GDN_OK) return s;
 
@@ -127,7 +140,7 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
     }
     gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, o, B, T, Hqk,
                                        Hv, dk, dv, chunk, dtype, scale);
-    hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, st)
+    hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st)
                                                 : gdn::launch_chunk_simt(a, st);
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

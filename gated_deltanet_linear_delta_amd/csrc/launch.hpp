@@ -38,9 +38,13 @@ hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
 // Float32-vector chunkwise kernel: any supported dtype, head dims and chunk size.
 hipError_t launch_chunk_simt(const ChunkArgs& a, hipStream_t st);
 
-// Fused matrix-core chunkwise kernel: bf16 inputs and the shapes chunk_mfma_supported accepts.
+// Matrix-core chunkwise path: bf16 inputs and the shapes chunk_mfma_supported accepts.  Either
+// one fused kernel, or (chunk_mfma_split) a parallel per-chunk prep kernel that fills a
+// workspace of chunk_mfma_workspace_bytes followed by the state-pass kernel.
 bool chunk_mfma_supported(const ChunkArgs& a);
-hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t st);
+bool chunk_mfma_split(const ChunkArgs& a);
+size_t chunk_mfma_workspace_bytes(const ChunkArgs& a);
+hipError_t launch_chunk_mfma(const ChunkArgs& a, void* workspace, hipStream_t st);
 
 // final_state <- initial_state (or zeros when it is null), for T == 0.
 hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st);

@@ -58,8 +58,12 @@ typedef enum {
 
 /*
  * gdn_chunk_fwd_workspace_bytes -- device scratch (bytes) that gdn_chunk_fwd needs for these
- * sizes.  Returns 0 when no scratch is needed (the current kernels need none).  Pure host
- * function; needs no device.
+ * sizes; 0 when the path chosen for them needs none.  The split matrix-core path (few, long
+ * sequences: see gdn_chunk_fwd_kernel_name) needs 13,824 bytes per (batch row, value head,
+ * 64-token chunk) for the per-chunk T = (I + A)^{-1}, the masked Q K^T and the gate vectors it
+ * builds before the state pass.  The result depends only on the arguments (and on the
+ * GDN_MFMA_PATH / GDN_DISABLE_MFMA environment variables, which select the path).  Pure host
+ * function; needs no device; 0 for invalid sizes.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                      gdn_dtype_t dtype);
@@ -84,8 +88,10 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int 
  *   o              [B, T, Hv, dv]    dtype output; must not overlap any other argument
  *   chunk          16, 32 or 64.  T need not be a multiple of chunk (the last chunk is partial).
  *   dk, dv         32, 64 or 128 each.
- *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes, or NULL
- *                  when that is 0.
+ *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes(...) bytes (16-byte
+ *                  aligned, owned by the caller, contents need not be initialised and are
+ *                  undefined afterwards; must not overlap any other argument), or NULL when
+ *                  that is 0.  Calls sharing a workspace must not overlap in time.
  *   stream         hipStream_t (as void*), NULL for the default stream.
  * B == 0 is a no-op.  T == 0 writes final_state (a copy of initial_state, or zeros) and no o.
  */
@@ -117,9 +123,11 @@ gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, con
                                 int dk, int dv, gdn_dtype_t dtype, float scale, void* stream);
 
 /*
- * gdn_chunk_fwd_kernel_name -- which kernel family gdn_chunk_fwd would run for these sizes
- * ("mfma" for the fused matrix-core kernel, "simt" for the float32-vector kernel), or NULL when
- * the sizes are unsupported.  Pure host function.
+ * gdn_chunk_fwd_kernel_name -- which kernel family gdn_chunk_fwd would run for these sizes:
+ * "mfma" (one fused matrix-core kernel, chosen when B * Hv >= 192), "mfma_split" (a parallel
+ * per-chunk prep kernel, then the matrix-core state pass; fewer chains), "simt" (float32
+ * vector kernel: float32 inputs, chunk != 64 or head dim 32), or NULL when the sizes are
+ * unsupported.  Pure host function.
  */
 const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                       gdn_dtype_t dtype);

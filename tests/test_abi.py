@@ -34,7 +34,15 @@ def test_status_strings_and_queries():
     for s in range(9):
         assert gdn.gdn_status_string(s)
     assert gdn.gdn_status_string(1234) == "unknown status"
-    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
+    # split matrix-core path (few chains): 13,824 bytes per (batch row, value head, chunk)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 32 * 64 * 13824
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4097, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 32 * 65 * 13824
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
+    # fused path (many chains) and the float32 path need none
+    assert gdn.gdn_chunk_fwd_workspace_bytes(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == 0
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 33, 128, 128, 64, gdn.GDN_BF16) == 0
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 32, 32, 16, gdn.GDN_F32) == "simt"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 3, 32, 32, 16, gdn.GDN_F32) is None
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 48, 32, 16, gdn.GDN_F32) is None
@@ -125,3 +133,29 @@ def test_valid_calls_report_no_device():
 @pytest.mark.skipif(_has_gpu(), reason="needs a host without a GPU")
 def test_workspace_check_precedes_device():
     assert chunk_call(wsb=0, ws=None) == NODEV
+
+
+# the split matrix-core path (bf16, chunk 64, few chains) needs a workspace
+SPLIT = dict(dk=128, dv=128, chunk=64, T=100)
+SPLIT_WS = 2 * 4 * 2 * 13824
+
+
+def test_split_workspace_size():
+    assert gdn.gdn_chunk_fwd_kernel_name(2, 100, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
+    assert gdn.gdn_chunk_fwd_workspace_bytes(2, 100, 2, 4, 128, 128, 64, gdn.GDN_BF16) == SPLIT_WS
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ws=fake(8), wsb=SPLIT_WS - 1), WS), (dict(ws=None, wsb=0), WS),
+    (dict(ws=None, wsb=SPLIT_WS), NULL),
+    (dict(ws=ctypes.c_void_p(BASE + 8 * STRIDE + 8), wsb=SPLIT_WS), ALIGN),
+    (dict(ws=fake(0), wsb=SPLIT_WS), ALIAS), (dict(ws=fake(7), wsb=SPLIT_WS), ALIAS),
+    (dict(ws=ctypes.c_void_p(BASE + 6 * STRIDE - 4096), wsb=SPLIT_WS), ALIAS),  # runs into sf
+])
+def test_split_workspace_rejects(over, status):
+    assert chunk_call(**SPLIT, **over) == status
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_split_valid_call_reports_no_device():
+    assert chunk_call(**SPLIT, ws=fake(8), wsb=SPLIT_WS) == NODEV

@@ -198,7 +198,8 @@ def test_decode_config_sampled():
 
 
 def test_kernel_family_dispatch():
-    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
+    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 32, gdn.GDN_BF16) == "simt"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == "simt"
 
@@ -211,6 +212,7 @@ def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
     chunk and a nonzero initial state."""
     if dv == 64 and bv == "128":
         pytest.skip("a 128-wide tile needs dv = 128")
+    monkeypatch.setenv("GDN_MFMA_PATH", "fused")
     monkeypatch.setenv("GDN_MFMA_BV", bv)
     say(f"mfma bv={bv} dk={dk} dv={dv} T={T} Hqk={Hqk} Hv={Hv}")
     assert gdn.gdn_chunk_fwd_kernel_name(2, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16) == "mfma"
@@ -221,11 +223,33 @@ def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
     check(f"mfma bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
 
 
+@pytest.mark.parametrize("bv", ["16", "32", "64", "128"])
+@pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
+                                            (64, 64, 1, 1, 1), (128, 128, 700, 1, 1)])
+def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
+    """The split matrix-core path (per-chunk prep kernel into the workspace, then the state pass)
+    at every column-tile width, with grouped heads, a ragged last chunk, a nonzero initial state
+    and a scale."""
+    if int(bv) > dv:
+        pytest.skip("tile wider than dv")
+    monkeypatch.setenv("GDN_MFMA_PATH", "split")
+    monkeypatch.setenv("GDN_SPLIT_BV", bv)
+    say(f"split bv={bv} dk={dk} dv={dv} T={T} Hqk={Hqk} Hv={Hv}")
+    assert gdn.gdn_chunk_fwd_kernel_name(2, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16) == "mfma_split"
+    d = gi.generate(B=2, T=T, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, dtype="bf16", mu=3.0, s0_std=0.05, seed=T + dk + 1)
+    sc = 0.5 if T == 129 else 1.0
+    o_ref, s_ref = oracle_prefill(d, scale=sc)
+    o, s = run_prefill(d, 64, scale=sc)
+    check(f"split bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
+
+
+@pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("mu", [3.0, 8.0])
-def test_mfma_identical_keys_dense_solve(mu):
+def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch):
     """All keys of a head equal: the strictly-lower A of every chunk is dense, so every block of
     the (I + A)^{-1} merge carries weight."""
-    say(f"mfma identical keys mu={mu}")
+    monkeypatch.setenv("GDN_MFMA_PATH", path)
+    say(f"mfma identical keys mu={mu} path={path}")
     d = gi.generate(B=1, T=256, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=mu, s0_std=0.05, seed=31)
     d["k"][:] = d["k"][:, :1]
     o_ref, s_ref = oracle_prefill(d)
@@ -233,10 +257,13 @@ def test_mfma_identical_keys_dense_solve(mu):
     check(f"identical keys mu={mu}", "bf16", o, o_ref, s, s_ref)
 
 
-def test_mfma_matches_simt(monkeypatch):
+@pytest.mark.parametrize("path", ["fused", "split"])
+def test_mfma_matches_simt(path, monkeypatch):
     """Two independent GPU implementations of the chunk algebra agree (and both match the oracle)."""
-    say("mfma vs simt")
+    say(f"mfma ({path}) vs simt")
     d = gi.generate(B=2, T=500, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=41)
+    monkeypatch.setenv("GDN_MFMA_PATH", path)
+    assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == ("mfma" if path == "fused" else "mfma_split")
     o_m, s_m = run_prefill(d, 64)
     monkeypatch.setenv("GDN_DISABLE_MFMA", "1")
     assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "simt"
