@@ -59,6 +59,29 @@
 
 namespace gdn {
 
+// Per-phase cycle stamps of workgroup 0 (lane 0 of each wave, chunks 2..33), compiled in only
+// with -DGDN_PHASE_TRACE for performance analysis; gdn_phase_trace_read copies them out.
+#ifdef GDN_PHASE_TRACE
+__device__ long long gdn_phase_ts[16][32][8];
+#define GDN_TRACE(n, k)                                                                   \
+    do {                                                                                  \
+        if (blockIdx.x == 0 && (threadIdx.x & 63) == 0 && (n) >= 2 && (n) < 34)            \
+            gdn_phase_ts[threadIdx.x >> 6][(n) - 2][k] = __builtin_readcyclecounter();    \
+    } while (0)
+// the prep kernel's stamps go to the otherwise unused row 15
+#define GDN_TRACE_PREP(k)                                                                 \
+    do {                                                                                  \
+        if (blockIdx.x == 0 && threadIdx.x == 0) gdn_phase_ts[15][0][k] = __builtin_readcyclecounter(); \
+    } while (0)
+#else
+#define GDN_TRACE(n, k) \
+    do {                \
+    } while (0)
+#define GDN_TRACE_PREP(k) \
+    do {                  \
+    } while (0)
+#endif
+
 namespace {
 
 typedef _Float16 op_t;
@@ -89,23 +112,24 @@ struct MLds {
     static constexpr size_t bytes = vec + (size_t)2 * 8 * CH * 4;
 };
 
-// per-chunk vectors (rows of 64 floats)
-constexpr int V_G = 0;     // gc (inclusive cumsum of g within the chunk)
-constexpr int V_B = 1;     // beta
-constexpr int V_EG = 2;    // scale exp(gc)
-constexpr int V_BEG = 3;   // beta exp(gc)
-constexpr int V_ED = 4;    // exp(gc_63 - gc)
-constexpr int V_EC = 5;    // exp(gc_63) (every element)
-constexpr int NVEC = 6;
+// per-chunk vectors (rows of 64 floats); the first four feed the state step, the fifth the output
+constexpr int V_B = 0;     // beta
+constexpr int V_BEG = 1;   // beta exp(gc)
+constexpr int V_ED = 2;    // exp(gc_63 - gc)
+constexpr int V_EC = 3;    // exp(gc_63) (every element)
+constexpr int V_EG = 4;    // scale exp(gc)
+constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk; fused prep only)
 
-// Workspace of the split path, per (batch, value head, chunk): T and Aqk as float16 in the
-// column-permuted order (below), only the 16x32 blocks a product reads (rows 0-31: columns
-// 0-31; rows 32-63: columns 0-63), then the NVEC gate vectors.
+// Workspace of the split path, per (batch, value head, chunk), in two parts: what the state step
+// reads (T, then the rows V_B..V_EC) and what the output step reads (Aqk, then the row V_EG).
+// T and Aqk are float16 in the column-permuted order (below), only the 16x32 blocks a product
+// reads (rows 0-31: columns 0-31; rows 32-63: columns 0-63).
 constexpr int WS_T = 0;
-constexpr int WS_AQ = 3072 * 2;
-constexpr int WS_VEC = 2 * 3072 * 2;
-constexpr int WS_CHUNK = WS_VEC + NVEC * CH * 4;   // 13824 bytes
-static_assert(WS_CHUNK % 16 == 0, "workspace chunk");
+constexpr int WS_CV = WS_T + 3072 * 2;
+constexpr int WS_AQ = WS_CV + 4 * CH * 4;
+constexpr int WS_EG = WS_AQ + 3072 * 2;
+constexpr int WS_CHUNK = WS_EG + CH * 4;   // 13568 bytes
+static_assert(WS_CHUNK % 16 == 0 && WS_AQ % 16 == 0, "workspace chunk");
 
 __device__ __forceinline__ int blk_off(int r, int pc) { return r < 32 ? r * 32 + pc : 1024 + (r - 32) * 64 + pc; }
 
@@ -182,6 +206,27 @@ __device__ __forceinline__ opx8 to_op(bf16x4 a, bf16x4 b)
                 (op_t)(float)b[0], (op_t)(float)b[1], (op_t)(float)b[2], (op_t)(float)b[3]};
 }
 
+// bf16 -> float16 for one pair-run: x = logical columns c .. c+7, y = c+16 .. c+23 of a
+// 32-column block (c = 8a) give the physical runs {c..c+3, c+16..c+19} and {c+4..c+7,
+// c+20..c+23}.  Each 32-bit pair is widened to two float32 (shift / mask) and narrowed with one
+// packed convert, three instructions per pair; exact for the unit-norm q, k rows (up to float16
+// subnormals).
+__device__ __forceinline__ unsigned int bf16x2_to_h2(unsigned int w)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const float lo = __builtin_bit_cast(float, w << 16);
+    const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+    return __builtin_bit_cast(unsigned int, h2{(_Float16)lo, (_Float16)hi});
+}
+
+__device__ __forceinline__ void bf16_pair_to_op(bf16x8 x, bf16x8 y, opx8& run0, opx8& run1)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = __builtin_bit_cast(u32x4, x), b = __builtin_bit_cast(u32x4, y);
+    run0 = __builtin_bit_cast(opx8, u32x4{bf16x2_to_h2(a[0]), bf16x2_to_h2(a[1]), bf16x2_to_h2(b[0]), bf16x2_to_h2(b[1])});
+    run1 = __builtin_bit_cast(opx8, u32x4{bf16x2_to_h2(a[2]), bf16x2_to_h2(a[3]), bf16x2_to_h2(b[2]), bf16x2_to_h2(b[3])});
+}
+
 __device__ __forceinline__ floatx4 ld4s(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
@@ -211,222 +256,255 @@ __device__ __forceinline__ float wave_cumsum(float x, int lane)
 }
 
 // =======================================================================================
-// One chunk of the state pass for one chain wave (column group cw): reads the staged chunk from
-// LDS (K, Q column-permuted float16 [64][DK+8]; V bf16 [64][BV+16]; T, Aqk column-permuted
-// float16 [64][CP]; the gate vectors), stores its O rows (ob points at the chunk's first token,
-// column tile start) and advances the state columns it owns.  `sync` runs between the three
-// phases: a workgroup barrier in the fused kernel (where other waves write LDS meanwhile), a
-// scheduling fence in the split path.
+// The per-chunk state step of one chain wave, in three phases.  The wave owns NTN 16-column
+// tiles of the state; `Vc` and `ob` point at its first column (V tile in LDS, O row of the
+// chunk's first token).  Inputs are the staged chunk in LDS: K, Q column-permuted float16
+// [64][DK+8]; V bf16 with pitch VP; T, Aqk column-permuted float16 [64][CP]; the gate vectors.
+//
+// phase 3: h <- h + K^T (exp(gc_63 - gc) Delta) (h already carries its decay from phase 1).
+// K^T fragments, 16 dk rows x 32 chunk positions each.
+template <int DK>
+__device__ __forceinline__ void load_kt(const op_t* Ks, int cb, int lane, opx8 (&akt)[DK / 16])
+{
+#pragma unroll
+    for (int mt = 0; mt < DK / 16; ++mt) akt[mt] = frag_kt(Ks, DK + 8, mt, 32 * cb, lane);
+}
+
+template <int DK, int NTN>
+__device__ __forceinline__ void apply_kt(floatx4 (&hacc)[NTN][DK / 16], const opx8 (&akt)[DK / 16],
+                                         const opx8 (&dtb)[NTN][2], int cb)
+{
+#pragma unroll
+    for (int mt = 0; mt < DK / 16; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt) hacc[nt][mt] = mfma32(akt[mt], dtb[nt][cb], hacc[nt][mt]);
+}
+
+// phase 1: hb = h (float16, perm-K), X = K h, R = beta V - beta exp(gc) X, Delta = T R,
+//          db = Delta and dtb = exp(gc_63 - gc) Delta (float16, perm-K); then h <- exp(gc_63) h
+//          (the decay part of the update; phase 3 adds K^T dtb).
+// Every product's A fragments are loaded before its MFMAs, behind a scheduling barrier, so the
+// LDS latency is paid once per product rather than once per MFMA; with one tile per wave the V
+// tile and the gate vectors are fetched up front too.
+template <int DK, int NTN, int VP, bool KT = false>
+__device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const op_t* Ks,
+                                            const bf16* Vc, const op_t* Tm, const float* vs, int lane,
+                                            opx8 (&hb)[NTN][DK / 32], opx8 (&db)[NTN][2],
+                                            opx8 (&dtb)[NTN][2], opx8 (*akt)[DK / 16] = nullptr)
+{
+    constexpr int KP = DK + 8;
+    constexpr int KB = DK / 32;
+    constexpr int MT = DK / 16;
+    constexpr bool EARLY = NTN == 1;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    // K fragments: all up front with one tile per wave; with two tiles (twice the MFMAs per k
+    // block) one k block ahead, which keeps the registers within budget
+    constexpr int AHEAD = NTN == 1 ? KB : 1;
+    opx8 ak[KB][4];
+#pragma unroll
+    for (int kk = 0; kk < AHEAD; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, KP, 16 * mt + ln, 32 * kk, lg);
+    opx8 at[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
+    // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
+    bf16x4 vv[NTN][4];
+    floatx4 bt[4], beg[4], ed[2][2];
+    auto fetch_rows = [&] {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt)
+                vv[nt][mt] = __builtin_bit_cast(bf16x4, ld_tr(Vc + (16 * mt + 4 * lg + (ln >> 2)) * VP + 16 * nt + 4 * (ln & 3)));
+            bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
+            beg[mt] = ld4s(vs + V_BEG * CH + 16 * mt + 4 * lg);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            ed[cb][0] = ld4s(vs + V_ED * CH + 32 * cb + 4 * lg);
+            ed[cb][1] = ld4s(vs + V_ED * CH + 32 * cb + 16 + 4 * lg);
+        }
+    };
+    if constexpr (EARLY) fetch_rows();
+    const float ec = vs[V_EC * CH];
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = pack_perm(hacc[nt][2 * kk], hacc[nt][2 * kk + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4 X[NTN][4];
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+        if (kk + AHEAD < KB) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) ak[kk + AHEAD][mt] = frag(Ks, KP, 16 * mt + ln, 32 * (kk + AHEAD), lg);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) X[nt][mt] = mfma32(ak[kk][mt], hb[nt][kk], X[nt][mt]);
+    }
+    // KT: the K^T fragments of phase 3, into the registers the K fragments free, their LDS
+    // latency hidden behind the rest of this phase
+    if constexpr (KT) {
+        load_kt<DK>(Ks, 0, lane, akt[0]);
+        load_kt<DK>(Ks, 1, lane, akt[1]);
+    }
+    // the decay of the state (its packed copy hb is already taken), while the MFMAs run
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
+    if constexpr (!EARLY) fetch_rows();
+    opx8 rbf[NTN][2];
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt) {
+        floatx4 rr[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) rr[mt][x] = bt[mt][x] * (float)vv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
+        rbf[nt][0] = pack_perm(rr[0], rr[1]);
+        rbf[nt][1] = pack_perm(rr[2], rr[3]);
+    }
+    // Delta = T R (T lower triangular: row tile mt needs k blocks cb <= mt/2)
+    floatx4 D[NTN][4];
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) D[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int mt = 2 * cb; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) D[nt][mt] = mfma32(at[mt][cb], rbf[nt][cb], D[nt][mt]);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt) {
+            db[nt][cb] = pack_perm(D[nt][2 * cb], D[nt][2 * cb + 1]);
+            floatx4 d0 = D[nt][2 * cb], d1 = D[nt][2 * cb + 1];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                d0[x] *= ed[cb][0][x];
+                d1[x] *= ed[cb][1][x];
+            }
+            dtb[nt][cb] = pack_perm(d0, d1);
+        }
+}
+
+// phase 2: O = exp(gc) (Q h) + Aqk Delta (the scale is folded into both) -> HBM.  O is formed
+// transposed, O^T = (h^T Q^T) diag(exp(gc)) + Delta^T Aqk^T: the same fragments with the operand
+// roles swapped, and the accumulator layout then gives each lane four consecutive value columns
+// of one token (one 8-byte store).
+template <int DK, int NTN>
+__device__ __forceinline__ void chain_out(const opx8 (&hb)[NTN][DK / 32], const opx8 (&db)[NTN][2],
+                                          const op_t* Qs, const op_t* Aq, const float* egv, bf16* ob,
+                                          size_t v_row, int nv, int lane)
+{
+    constexpr int KP = DK + 8;
+    constexpr int KB = DK / 32;
+    constexpr int AHEAD = NTN == 1 ? KB : 1;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
+    opx8 aqf[KB][4];
+#pragma unroll
+    for (int kk = 0; kk < AHEAD; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) aqf[kk][ct] = frag(Qs, KP, 16 * ct + ln, 32 * kk, lg);
+    opx8 aa[4][2];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int cb = 0; cb <= ct / 2; ++cb) aa[ct][cb] = frag(Aq, CP, 16 * ct + ln, 32 * cb, lg);
+    float eg[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) eg[ct] = egv[16 * ct + ln];
+    floatx4 OT[NTN][4];
+#pragma unroll
+    for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) OT[nt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+        if (kk + AHEAD < KB) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) aqf[kk + AHEAD][ct] = frag(Qs, KP, 16 * ct + ln, 32 * (kk + AHEAD), lg);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(hb[nt][kk], aqf[kk][ct], OT[nt][ct]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) OT[nt][ct][x] *= eg[ct];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int ct = 2 * cb; ct < 4; ++ct)
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(db[nt][cb], aa[ct][cb], OT[nt][ct]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const int tok = 16 * ct + ln;
+        if (tok < nv) {
+            bf16* op = ob + (size_t)tok * v_row + 4 * lg;
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) {
+                const bf16x4 ov = {(bf16)OT[nt][ct][0], (bf16)OT[nt][ct][1], (bf16)OT[nt][ct][2],
+                                   (bf16)OT[nt][ct][3]};
+                *reinterpret_cast<bf16x4*>(op + 16 * nt) = ov;
+            }
+        }
+    }
+}
+
+// phase 3 with its own fragment loads
+template <int DK, int NTN>
+__device__ __forceinline__ void chain_update(floatx4 (&hacc)[NTN][DK / 16], const op_t* Ks,
+                                             const opx8 (&dtb)[NTN][2], int lane)
+{
+    // one tile: every K^T fragment up front; two tiles: the second k block during the first's MFMAs
+    opx8 akt[2][DK / 16];
+    load_kt<DK>(Ks, 0, lane, akt[0]);
+    if constexpr (NTN == 1) load_kt<DK>(Ks, 1, lane, akt[1]);
+    apply_kt<DK, NTN>(hacc, akt[0], dtb, 0);
+    if constexpr (NTN != 1) load_kt<DK>(Ks, 1, lane, akt[1]);
+    apply_kt<DK, NTN>(hacc, akt[1], dtb, 1);
+}
+
+// The three phases in one wave (column group cw of NW), with `sync` between them: a workgroup
+// barrier in the fused kernel (where other waves write LDS meanwhile), a scheduling fence in the
+// state pass.
 template <int DK, int BV, int NW, typename Sync>
 __device__ __forceinline__ void chain_chunk(floatx4 (&hacc)[BV / NW / 16][DK / 16], const op_t* Ks,
                                             const op_t* Qs, const bf16* Vs, const op_t* Tm,
                                             const op_t* Aq, const float* vs, bf16* ob, size_t v_row,
                                             int nv, int cw, int lane, Sync&& sync)
 {
-    constexpr int KP = DK + 8;
-    constexpr int VP = BV + 16;
-    constexpr int NCOL = BV / NW;       // state columns of this wave
-    constexpr int NTN = NCOL / 16;      // 16-column tiles
-    constexpr int MT = DK / 16;         // 16-row tiles of the state
-    constexpr int KB = DK / 32;         // 32-wide k blocks over dk
-    // With one 16-column tile per wave the Q fragments for phase 2 are loaded in phase 1 and the
-    // K^T fragments for phase 3 in phase 2; with two tiles the registers do not allow it and each
-    // product loads its fragments when its phase starts.
-    constexpr bool PRE = NTN == 1;
-    const int ln = lane & 15;
-    const int lg = lane >> 4;
-    opx8 hb[NTN][KB];
-    opx8 db[NTN][2], dtb[NTN][2];
-    opx8 aqf[KB][4];
-    opx8 akt[2][MT];
-
-    // phase 1: X = K h, R = beta V - beta exp(gc) X, Delta = T R.  Every product's A fragments
-    // are loaded before its MFMAs, behind a scheduling barrier, so the LDS latency is paid once
-    // per product rather than once per MFMA.
-    {
-        // K fragments: all up front with one tile per wave; with two tiles (twice the MFMAs per
-        // k block) one k block ahead, which keeps the registers within budget
-        constexpr int AHEAD = PRE ? KB : 1;
-        opx8 ak[KB][4];
-#pragma unroll
-        for (int kk = 0; kk < AHEAD; ++kk)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, KP, 16 * mt + ln, 32 * kk, lg);
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = pack_perm(hacc[nt][2 * kk], hacc[nt][2 * kk + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 X[NTN][4];
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) X[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-            if (kk + AHEAD < KB) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) ak[kk + AHEAD][mt] = frag(Ks, KP, 16 * mt + ln, 32 * (kk + AHEAD), lg);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) X[nt][mt] = mfma32(ak[kk][mt], hb[nt][kk], X[nt][mt]);
-        }
-        // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
-        bf16x4 vv[NTN][4];
-        floatx4 bt[4], beg[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-                vv[nt][mt] = __builtin_bit_cast(bf16x4, ld_tr(Vs + (16 * mt + 4 * lg + (ln >> 2)) * VP +
-                                                               cw * NCOL + 16 * nt + 4 * (ln & 3)));
-            bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
-            beg[mt] = ld4s(vs + V_BEG * CH + 16 * mt + 4 * lg);
-        }
-        opx8 at[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
-        opx8 rbf[NTN][2];
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt) {
-            floatx4 rr[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) rr[mt][x] = bt[mt][x] * (float)vv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
-            rbf[nt][0] = pack_perm(rr[0], rr[1]);
-            rbf[nt][1] = pack_perm(rr[2], rr[3]);
-        }
-        // Delta = T R (T lower triangular: row tile mt needs k blocks cb <= mt/2)
-        floatx4 D[NTN][4];
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) D[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int mt = 2 * cb; mt < 4; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) D[nt][mt] = mfma32(at[mt][cb], rbf[nt][cb], D[nt][mt]);
-        floatx4 ed[2][2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            ed[cb][0] = ld4s(vs + V_ED * CH + 32 * cb + 4 * lg);
-            ed[cb][1] = ld4s(vs + V_ED * CH + 32 * cb + 16 + 4 * lg);
-        }
-        if constexpr (PRE) {
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) aqf[kk][mt] = frag(Qs, KP, 16 * mt + ln, 32 * kk, lg);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt) {
-                db[nt][cb] = pack_perm(D[nt][2 * cb], D[nt][2 * cb + 1]);
-                floatx4 d0 = D[nt][2 * cb], d1 = D[nt][2 * cb + 1];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    d0[x] *= ed[cb][0][x];
-                    d1[x] *= ed[cb][1][x];
-                }
-                dtb[nt][cb] = pack_perm(d0, d1);
-            }
-    }
+    constexpr int NCOL = BV / NW;
+    constexpr int NTN = NCOL / 16;
+    opx8 hb[NTN][DK / 32], db[NTN][2], dtb[NTN][2];
+    chain_delta<DK, NTN, BV + 16>(hacc, Ks, Vs + cw * NCOL, Tm, vs, lane, hb, db, dtb);
     sync();
-    // phase 2: Y = Q h, O = exp(gc) Y + Aqk Delta (scale folded into both) -> HBM; then the K^T
-    // fragments for phase 3
-    {
-        if constexpr (!PRE) {
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) aqf[kk][mt] = frag(Qs, KP, 16 * mt + ln, 32 * kk, lg);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        opx8 aa[4][2];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int cb = 0; cb <= ct / 2; ++cb) aa[ct][cb] = frag(Aq, CP, 16 * ct + ln, 32 * cb, lg);
-        float eg[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) eg[ct] = vs[V_EG * CH + 16 * ct + ln];
-        // O is formed transposed, O^T = (h^T Q^T) diag(exp(gc)) + Delta^T Aqk^T: the same
-        // fragments with the operand roles swapped, and the accumulator layout then gives each
-        // lane four consecutive value columns of one token (one 8-byte store).
-        floatx4 OT[NTN][4];
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) OT[nt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(hb[nt][kk], aqf[kk][ct], OT[nt][ct]);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) OT[nt][ct][x] *= eg[ct];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int ct = 2 * cb; ct < 4; ++ct)
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) OT[nt][ct] = mfma32(db[nt][cb], aa[ct][cb], OT[nt][ct]);
-        if constexpr (PRE) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) akt[cb][mt] = frag_kt(Ks, KP, mt, 32 * cb, lane);
-        }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const int tok = 16 * ct + ln;
-            if (tok < nv) {
-                bf16* op = ob + (size_t)tok * v_row + cw * NCOL + 4 * lg;
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) {
-                    const bf16x4 ov = {(bf16)OT[nt][ct][0], (bf16)OT[nt][ct][1], (bf16)OT[nt][ct][2],
-                                       (bf16)OT[nt][ct][3]};
-                    *reinterpret_cast<bf16x4*>(op + 16 * nt) = ov;
-                }
-            }
-        }
-    }
+    chain_out<DK, NTN>(hb, db, Qs, Aq, vs + V_EG * CH, ob + cw * NCOL, v_row, nv, lane);
     sync();
-    // phase 3: h <- exp(gc_63) h + K^T (exp(gc_63 - gc) Delta)
-    {
-        if constexpr (!PRE) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) akt[cb][mt] = frag_kt(Ks, KP, mt, 32 * cb, lane);
-        }
-        const float ec = vs[V_EC * CH];
-#pragma unroll
-        for (int nt = 0; nt < NTN; ++nt)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) hacc[nt][mt] = mfma32(akt[cb][mt], dtb[nt][cb], hacc[nt][mt]);
-    }
+    chain_update<DK, NTN>(hacc, Ks, dtb, lane);
 }
 
 // Entry state of one chain wave's columns (zeros when s0 is null), and its final state.
@@ -776,18 +854,15 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
         const size_t head = (size_t)b * Hv + j;
         load_state<DK, DV, NTN>(hacc, s0, head, c0 + cw * NCOL, lane);
         lds_barrier();
+        // iteration -1: the prep waves build chunk 0
+        for (int x = 0; x < 4; ++x) lds_barrier();
         // iteration n: carry chunk n (the prep waves build chunk n + 1 meanwhile); the same
         // four barriers per iteration as the prep waves
-        for (int n = -1; n < NT; ++n) {
-            if (n >= 0) {
-                const int t0 = n * CH;
-                chain_chunk<DK, BV, NCW>(hacc, Kslot(n & 1), Qslot(n & 1), Vs, Tm, Aq, vslot(n & 1),
-                                         ob + (size_t)t0 * v_row, v_row, min(CH, T_len - t0), cw, lane,
-                                         [] { lds_barrier(); });
-            } else {
-                lds_barrier();
-                lds_barrier();
-            }
+        for (int n = 0; n < NT; ++n) {
+            const int t0 = n * CH;
+            chain_chunk<DK, BV, NCW>(hacc, Kslot(n & 1), Qslot(n & 1), Vs, Tm, Aq, vslot(n & 1),
+                                     ob + (size_t)t0 * v_row, v_row, min(CH, T_len - t0), cw, lane,
+                                     [] { lds_barrier(); });
             lds_barrier();
             // interval 4: nothing for the chain waves (the prep waves finish T and restage q, k)
             lds_barrier();
@@ -797,11 +872,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
 }
 
 // =======================================================================================
-// Split path, kernel 1: everything of one chunk that does not depend on the state, for one
-// value head, by one wave: the gate cumsum and vectors, A (K K^T with beta and the decay mask),
-// T = (I + A)^{-1}, and Aqk (Q K^T with the decay mask and the scale).  Workgroups are ordered
-// (batch, query/key head, chunk, value head of the group), so the group's value heads read the
-// same q, k rows back to back.
+// Split path, kernel 1: everything of one chunk that does not depend on the state, by one wave
+// per (batch, query/key head, chunk).  The raw K K^T and K Q^T products are formed once (q, k
+// are shared by the query/key head's group of value heads); then for each value head of the
+// group in turn: the gate cumsum and vectors, A (beta and the decay mask), T = (I + A)^{-1}, and
+// Aqk (the decay mask and the scale), all into the workspace.
 template <int DK>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
@@ -815,22 +890,20 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
     __shared__ __attribute__((aligned(16))) float pb[CH];         // beta
 
     int lid = blockIdx.x;
-    const int jj = lid % grp;
-    lid /= grp;
     const int c = lid % NT;
     lid /= NT;
     const int i = lid % Hqk;
     const int b = lid / Hqk;
-    const int j = i * grp + jj;
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
     const int t0 = c * CH, n = min(CH, T_len - t0);
     const size_t qk_row = (size_t)Hqk * DK;
     const bf16* kp = k + ((size_t)b * T_len + t0) * qk_row + (size_t)i * DK;
     const bf16* qp = q + ((size_t)b * T_len + t0) * qk_row + (size_t)i * DK;
-    unsigned char* wc = ws + (((size_t)b * Hv + j) * NT + c) * WS_CHUNK;
 
-    // Gram fragments straight from HBM (standard k order on both sides); rows past T are clamped
-    // and masked below
+    // gates of the group's first value head, then the Gram fragments straight from HBM (standard
+    // k order on both sides); rows past T are clamped and masked below
+    const size_t grow = ((size_t)b * T_len + t0 + min(lane, n - 1)) * Hv + (size_t)i * grp;
+    float gl = g[grow], bl = beta[grow];
     bf16x8 kf[4][KB], qf[4][KB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -840,44 +913,55 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             kf[mt][kk] = *reinterpret_cast<const bf16x8*>(kp + off);
             qf[mt][kk] = *reinterpret_cast<const bf16x8*>(qp + off);
         }
-    // gates: cumsum and the per-row vectors
-    {
-        const size_t go = ((size_t)b * T_len + t0 + min(lane, n - 1)) * Hv + j;
-        const float gl = g[go], bl = beta[go];
-        const float x = wave_cumsum(lane < n ? gl : 0.f, lane);
-        const float bt = lane < n ? bl : 0.f;
-        const float last = __shfl(x, 63, 64);
-        const float eg = __expf(x);
-        pg[lane] = x;
-        pb[lane] = bt;
-        float* wv = reinterpret_cast<float*>(wc + WS_VEC);
-        wv[V_G * CH + lane] = x;
-        wv[V_B * CH + lane] = bt;
-        wv[V_EG * CH + lane] = scale * eg;
-        wv[V_BEG * CH + lane] = bt * eg;
-        wv[V_ED * CH + lane] = __expf(last - x);
-        wv[V_EC * CH + lane] = __expf(last);
-    }
+    GDN_TRACE_PREP(0);
     // zero T's two stored strictly-upper 16x16 blocks (rows 0-15 x physical columns 0-31 and
-    // rows 32-47 x 32-63; the diagonal blocks written next overwrite their half)
+    // rows 32-47 x 32-63; the diagonal blocks written later overwrite their half)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int r = 32 * p + (lane >> 2), c8 = 32 * p + 8 * (lane & 3);
         *reinterpret_cast<opx8*>(Tm + r * CP + c8) = opx8{};
     }
-    wave_lds_fence();
-
+    // raw lower tiles (TI, TJ): K K^T rows TI x columns TJ, and K Q^T rows TJ of K x columns TI
+    // of Q (Aqk transposed, so that a lane later holds four consecutive columns of one row)
     constexpr int TI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
     constexpr int TJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    // A = strictly-lower( beta_r exp(gc_r - gc_i) (k_r . k_i) ), stored transposed in float32
-    {
-        floatx4 acc[10];
+    floatx4 gk[10], gq[10];
 #pragma unroll
-        for (int t = 0; t < 10; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 10; ++t) gk[t] = gq[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
+    for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-            for (int t = 0; t < 10; ++t) acc[t] = mfma_bf(kf[TI[t]][kk], kf[TJ[t]][kk], acc[t]);
+        for (int t = 0; t < 10; ++t) {
+            gk[t] = mfma_bf(kf[TI[t]][kk], kf[TJ[t]][kk], gk[t]);
+            gq[t] = mfma_bf(kf[TJ[t]][kk], qf[TI[t]][kk], gq[t]);
+        }
+    GDN_TRACE_PREP(1);
+
+    for (int jj = 0; jj < grp; ++jj) {
+        const int j = i * grp + jj;
+        unsigned char* wc = ws + (((size_t)b * Hv + j) * NT + c) * WS_CHUNK;
+        // gates: cumsum and the per-row vectors; the next head's gates load meanwhile
+        const float x = wave_cumsum(lane < n ? gl : 0.f, lane);
+        const float bt = lane < n ? bl : 0.f;
+        if (jj + 1 < grp) {
+            gl = g[grow + jj + 1];
+            bl = beta[grow + jj + 1];
+        }
+        const float last = __shfl(x, 63, 64);
+        const float eg = __expf(x);
+        wave_lds_fence();   // the previous head is done with pg, pb
+        pg[lane] = x;
+        pb[lane] = bt;
+        {
+            float* wv = reinterpret_cast<float*>(wc + WS_CV);
+            wv[V_B * CH + lane] = bt;
+            wv[V_BEG * CH + lane] = bt * eg;
+            wv[V_ED * CH + lane] = __expf(last - x);
+            wv[V_EC * CH + lane] = __expf(last);
+            reinterpret_cast<float*>(wc + WS_EG)[lane] = scale * eg;
+        }
+        wave_lds_fence();
+        // A = strictly-lower( beta_r exp(gc_r - gc_i) (k_r . k_i) ), stored transposed in float32
 #pragma unroll
         for (int t = 0; t < 10; ++t) {
             const int cc = 16 * TJ[t] + ln;
@@ -887,161 +971,199 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             const floatx4 br = ld4s(pb + r0);
             floatx4 out;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) out[x] = cc < r0 + x ? br[x] * __expf(gr[x] - gcc) * acc[t][x] : 0.f;
+            for (int e = 0; e < 4; ++e) out[e] = cc < r0 + e ? br[e] * __expf(gr[e] - gcc) * gk[t][e] : 0.f;
             *reinterpret_cast<floatx4*>(Af + cc * AFP + r0) = out;   // A^T[cc][r0..r0+3]
         }
-    }
-    // Aqk = lower-incl( scale exp(gc_r - gc_i) (q_r . k_i) ), formed as K Q^T so that a lane
-    // holds four consecutive columns of one row (one 8-byte store); rows past T are zero
-    {
-        op_t* wa = reinterpret_cast<op_t*>(wc + WS_AQ);
+        // Aqk = lower-incl( scale exp(gc_r - gc_i) (q_r . k_i) ); rows past T are zero
+        {
+            op_t* wa = reinterpret_cast<op_t*>(wc + WS_AQ);
 #pragma unroll
-        for (int t = 0; t < 10; ++t) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < 10; ++t) {
+                const int r = 16 * TI[t] + ln;
+                const int i0 = 16 * TJ[t] + 4 * lg;
+                const float gr = pg[r];
+                const floatx4 gi = ld4s(pg + i0);
+                opx4 out;
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk) acc = mfma_bf(kf[TJ[t]][kk], qf[TI[t]][kk], acc);
-            const int r = 16 * TI[t] + ln;
-            const int i0 = 16 * TJ[t] + 4 * lg;
-            const float gr = pg[r];
-            const floatx4 gi = ld4s(pg + i0);
-            opx4 out;
+                for (int e = 0; e < 4; ++e)
+                    out[e] = (op_t)((i0 + e <= r && r < n) ? scale * __expf(gr - gi[e]) * gq[t][e] : 0.f);
+                *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = out;
+            }
+            // the stored strictly-upper blocks (0, 1) and (2, 3)
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                out[x] = (op_t)((i0 + x <= r && r < n) ? scale * __expf(gr - gi[x]) * acc[x] : 0.f);
-            *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = out;
+            for (int p = 0; p < 2; ++p) {
+                const int r = 32 * p + ln, i0 = 32 * p + 16 + 4 * lg;
+                *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = opx4{};
+            }
         }
-        // the stored strictly-upper blocks (0, 1) and (2, 3)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int r = 32 * p + ln, i0 = 32 * p + 16 + 4 * lg;
-            *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = opx4{};
-        }
-    }
-    wave_lds_fence();
-    // diagonal blocks of T: lane group lg inverts block lg, lane ln forms its column ln by
-    // right-looking forward substitution in float32
-    {
-        const float* At = Af + (16 * lg) * AFP + 16 * lg;   // At[x * AFP + r] = A_ww[r][x]
-        float tcol[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tcol[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-        for (int x = 0; x < 15; ++x) {
-            floatx4 col[4];
-#pragma unroll
-            for (int q4 = (x + 1) / 4; q4 < 4; ++q4) col[q4] = ld4s(At + x * AFP + 4 * q4);
-#pragma unroll
-            for (int r = x + 1; r < 16; ++r) tcol[r] = fmaf(-col[r / 4][r % 4], tcol[x], tcol[r]);
-        }
-        op_t* tc = Tm + (16 * lg) * CP + pcol(16 * lg + ln);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tc[r * CP] = (op_t)tcol[r];
-    }
-    wave_lds_fence();
-    // T_{w+1,w} = -T_{w+1,w+1} A_{w+1,w} T_ww, w = 0 and 2
-    {
-        floatx4 t10[2];
+        GDN_TRACE_PREP(2);
+        wave_lds_fence();
+        // the A operands of the merges (independent of T), fetched before the solve
+        opx4 a10[2];
 #pragma unroll
         for (int wi = 0; wi < 2; ++wi) {
-            const int w = 2 * wi;
-            const float* at = Af + (16 * w + 4 * lg) * AFP + 16 * (w + 1) + ln;
-            const opx4 aa = {(op_t)at[0], (op_t)at[AFP], (op_t)at[2 * AFP], (op_t)at[3 * AFP]};
-            const op_t* tw = Tm + (16 * w + 4 * lg) * CP + pcol(16 * w + ln);
-            const opx4 tb = {tw[0], tw[CP], tw[2 * CP], tw[3 * CP]};
-            const floatx4 p = mfma16(aa, tb, floatx4{0.f, 0.f, 0.f, 0.f});
-            const opx4 pb = {(op_t)p[0], (op_t)p[1], (op_t)p[2], (op_t)p[3]};
-            const opx4 td = *reinterpret_cast<const opx4*>(Tm + (16 * (w + 1) + ln) * CP + pcol(16 * (w + 1) + 4 * lg));
-            t10[wi] = mfma16(td, pb, floatx4{0.f, 0.f, 0.f, 0.f});
+            const float* at = Af + (32 * wi + 4 * lg) * AFP + 16 * (2 * wi + 1) + ln;
+            a10[wi] = opx4{(op_t)at[0], (op_t)at[AFP], (op_t)at[2 * AFP], (op_t)at[3 * AFP]};
         }
-#pragma unroll
-        for (int wi = 0; wi < 2; ++wi) {
-            const int w = 2 * wi;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) Tm[(16 * (w + 1) + 4 * lg + x) * CP + pcol(16 * w + ln)] = (op_t)(-t10[wi][x]);
-        }
-    }
-    wave_lds_fence();
-    // T[32:64, 0:32] = -T_hi (A[32:64, 0:32] T_lo)
-    {
-        opx8 tlo[2], aa[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) tlo[p] = frag_kt(Tm, CP, p, 0, lane);
+        opx8 a2[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
             const float* ac = Af + (4 * lg) * AFP + 32 + 16 * a + ln;
-            aa[a] = opx8{(op_t)ac[0], (op_t)ac[AFP], (op_t)ac[2 * AFP], (op_t)ac[3 * AFP],
+            a2[a] = opx8{(op_t)ac[0], (op_t)ac[AFP], (op_t)ac[2 * AFP], (op_t)ac[3 * AFP],
                          (op_t)ac[16 * AFP], (op_t)ac[17 * AFP], (op_t)ac[18 * AFP], (op_t)ac[19 * AFP]};
         }
-        floatx4 q1[2][2];
+        // diagonal blocks of T: lane group lg inverts block lg, lane ln forms its column ln by
+        // right-looking forward substitution in float32; each step's column of A is fetched two
+        // steps ahead
+        {
+            const float* At = Af + (16 * lg) * AFP + 16 * lg;   // At[x * AFP + r] = A_ww[r][x]
+            float tcol[16];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int r = 0; r < 16; ++r) tcol[r] = (r == ln) ? 1.f : 0.f;
+            floatx4 col[15][4];
+            auto fetch = [&](int x) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) q1[a][p] = mfma32(aa[a], tlo[p], floatx4{0.f, 0.f, 0.f, 0.f});
-        floatx4 r[2][2];
+                for (int q4 = (x + 1) / 4; q4 < 4; ++q4) col[x][q4] = ld4s(At + x * AFP + 4 * q4);
+            };
+            fetch(0);
+            fetch(1);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const opx8 qb = pack_perm(q1[0][p], q1[1][p]);
+            for (int x = 0; x < 15; ++x) {
+                if (x + 2 < 15) fetch(x + 2);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) r[a][p] = mfma32(frag(Tm, CP, 32 + 16 * a + ln, 32, lg), qb, floatx4{0.f, 0.f, 0.f, 0.f});
+                for (int r = x + 1; r < 16; ++r) tcol[r] = fmaf(-col[x][r / 4][r % 4], tcol[x], tcol[r]);
+            }
+            op_t* tc = Tm + (16 * lg) * CP + pcol(16 * lg + ln);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tc[r * CP] = (op_t)tcol[r];
         }
+        GDN_TRACE_PREP(3);
+        wave_lds_fence();
+        // T_{w+1,w} = -T_{w+1,w+1} A_{w+1,w} T_ww, w = 0 and 2
+        {
+            floatx4 t10[2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+            for (int wi = 0; wi < 2; ++wi) {
+                const int w = 2 * wi;
+                const op_t* tw = Tm + (16 * w + 4 * lg) * CP + pcol(16 * w + ln);
+                const opx4 tb = {tw[0], tw[CP], tw[2 * CP], tw[3 * CP]};
+                const opx4 td = *reinterpret_cast<const opx4*>(Tm + (16 * (w + 1) + ln) * CP + pcol(16 * (w + 1) + 4 * lg));
+                const floatx4 p = mfma16(a10[wi], tb, floatx4{0.f, 0.f, 0.f, 0.f});
+                const opx4 pb2 = {(op_t)p[0], (op_t)p[1], (op_t)p[2], (op_t)p[3]};
+                t10[wi] = mfma16(td, pb2, floatx4{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int wi = 0; wi < 2; ++wi) {
+                const int w = 2 * wi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Tm[(16 * (w + 1) + 4 * lg + e) * CP + pcol(16 * w + ln)] = (op_t)(-t10[wi][e]);
+            }
+        }
+        wave_lds_fence();
+        // T[32:64, 0:32] = -T_hi (A[32:64, 0:32] T_lo)
+        {
+            opx8 tlo[2], th[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) tlo[p] = frag_kt(Tm, CP, p, 0, lane);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) th[a] = frag(Tm, CP, 32 + 16 * a + ln, 32, lg);
+            floatx4 q1[2][2];
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) Tm[(32 + 16 * a + 4 * lg + x) * CP + pcol(16 * p + ln)] = (op_t)(-r[a][p][x]);
-    }
-    wave_lds_fence();
-    // T -> workspace (the stored blocks, 16 bytes per lane per step, consecutive)
-    {
-        op_t* wt = reinterpret_cast<op_t*>(wc + WS_T);
+                for (int p = 0; p < 2; ++p) q1[a][p] = mfma32(a2[a], tlo[p], floatx4{0.f, 0.f, 0.f, 0.f});
+            floatx4 r[2][2];
 #pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            const int s = lane + 64 * p;
-            const int r = s < 128 ? s >> 2 : 32 + ((s - 128) >> 3);
-            const int c8 = s < 128 ? 8 * (s & 3) : 8 * ((s - 128) & 7);
-            *reinterpret_cast<opx8*>(wt + 8 * s) = *reinterpret_cast<const opx8*>(Tm + r * CP + c8);
+            for (int p = 0; p < 2; ++p) {
+                const opx8 qb = pack_perm(q1[0][p], q1[1][p]);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) r[a][p] = mfma32(th[a], qb, floatx4{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Tm[(32 + 16 * a + 4 * lg + e) * CP + pcol(16 * p + ln)] = (op_t)(-r[a][p][e]);
         }
+        GDN_TRACE_PREP(4);
+        wave_lds_fence();
+        // T -> workspace (the stored blocks, 16 bytes per lane per step, consecutive)
+        {
+            op_t* wt = reinterpret_cast<op_t*>(wc + WS_T);
+#pragma unroll
+            for (int p = 0; p < 6; ++p) {
+                const int s = lane + 64 * p;
+                const int r = s < 128 ? s >> 2 : 32 + ((s - 128) >> 3);
+                const int c8 = s < 128 ? 8 * (s & 3) : 8 * ((s - 128) & 7);
+                *reinterpret_cast<opx8*>(wt + 8 * s) = *reinterpret_cast<const opx8*>(Tm + r * CP + c8);
+            }
+        }
+        GDN_TRACE_PREP(5);
     }
 }
 
 // Split path, kernel 2: the state pass.  One workgroup per (batch, value head, column tile of
-// BV = 16 NW NTN columns): NW chain waves run chain_chunk on chunk n while NLW loader waves stage
-// chunk n + 1 (q, k converted to column-permuted float16; V; T, Aqk and the gate vectors copied
-// from the workspace) into the other half of a double-buffered LDS, and prefetch chunk n + 2 into
-// registers.  One workgroup barrier per chunk.
-template <int DK, int BV>
+// BV = 16 NW NTN columns), with NW chain waves and NLW loader waves, one barrier per chunk.
+// LDS holds two double-buffered sets: the state-step tiles (K, V, T and the state vectors of a
+// chunk) and the output-step tiles (Q, Aqk and scale exp(gc)).  In iteration n the chain waves
+// carry chunk n while the loaders stage chunk n + 1's state-step tiles (q, k converted to
+// column-permuted float16; the rest copied from the workspace) and prefetch chunk n + 2.
+// * Narrow tiles (NW <= 2): the output step leaves the chain.  Each chain wave hands its packed
+//   h and Delta to an output wave of its own through LDS; in iteration n the output waves form
+//   O of chunk n - 1 while the loaders stage the output-step tiles of chunk n (one iteration
+//   ahead of their use), so every hand-over crosses exactly one barrier.
+// * Wide tiles (NW = 4): each chain wave runs all three phases, and the loaders stage both sets
+//   of chunk n + 1.
+template <int DK, int BV, int NW>
 struct SLds {
     static constexpr int KP = DK + 8;
     static constexpr int VP = BV + 16;
+    static constexpr bool OW = NW <= 2;
+    static constexpr int NTN = BV / NW / 16;
+    // state-step slot
     static constexpr size_t k = 0;                                   // K   [64][KP] f16
-    static constexpr size_t q = k + (size_t)CH * KP * 2;             // Q   [64][KP] f16
-    static constexpr size_t v = q + (size_t)CH * KP * 2;             // V   [64][VP] bf16
+    static constexpr size_t v = k + (size_t)CH * KP * 2;             // V   [64][VP] bf16
     static constexpr size_t t = v + (size_t)CH * VP * 2;             // T   [64][CP] f16
-    static constexpr size_t a = t + (size_t)CH * CP * 2;             // Aqk [64][CP] f16
-    static constexpr size_t e = a + (size_t)CH * CP * 2;             // [NVEC][64] f32
-    static constexpr size_t slot = e + (size_t)NVEC * CH * 4;
-    static constexpr size_t bytes = 2 * slot;
+    static constexpr size_t cv = t + (size_t)CH * CP * 2;            // rows V_B..V_EC, f32
+    static constexpr size_t cslot = cv + (size_t)4 * CH * 4;
+    // output-step slot
+    static constexpr size_t q = 0;                                   // Q   [64][KP] f16
+    static constexpr size_t a = q + (size_t)CH * KP * 2;             // Aqk [64][CP] f16
+    static constexpr size_t eg = a + (size_t)CH * CP * 2;            // scale exp(gc), f32
+    static constexpr size_t oslot = eg + (size_t)CH * 4;
+    static constexpr size_t obase = 2 * cslot;
+    // chain -> output hand-over, [2][NW]: hb (NTN x DK/32 fragments) then db (NTN x 2), each
+    // fragment 64 lanes x 16 bytes
+    static constexpr size_t hx_frags = (size_t)NTN * (DK / 32 + 2);
+    static constexpr size_t hx = obase + 2 * oslot;
+    static constexpr size_t bytes = hx + (OW ? 2 * NW * hx_frags * 1024 : 0);
 };
 
 template <int DK, int DV, int NW, int NTN>
-__global__ __launch_bounds__((NLW + NW) * 64, 1) void chunk_state_kernel(
+__global__ __launch_bounds__((NLW + (NW <= 2 ? 2 : 1) * NW) * 64, 1) void chunk_state_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const unsigned char* __restrict__ ws, const float* s0, float* sf, bf16* __restrict__ o,
     int T_len, int Hqk, int Hv, int grp, int xcd_remap)
 {
     constexpr int BV = 16 * NW * NTN;
-    using L = SLds<DK, BV>;
+    using L = SLds<DK, BV, NW>;
+    constexpr bool OW = L::OW;
     constexpr int NTILE = DV / BV;
     constexpr int MT = DK / 16;
+    constexpr int KB = DK / 32;
+    constexpr int NCOL = 16 * NTN;                      // columns per chain wave
     constexpr int NLT = NLW * 64;                       // loader threads
-    constexpr int RK = DK / 8;                          // 16-byte runs per K row
-    constexpr int PK = CH * RK / NLT;                   // K (and Q) runs per loader lane
+    constexpr int RP = DK / 16;                         // 32-byte pair-runs per K row
+    constexpr int PK = CH * RP / NLT;                   // K (and Q) pair-runs per loader lane
     constexpr int RV = BV / 8;                          // 16-byte runs per V row
     constexpr int PV = (CH * RV + NLT - 1) / NLT;       // V runs per loader lane
-    constexpr int NWS = WS_CHUNK / 16;                  // 16-byte runs of a workspace chunk
-    constexpr int PW = (NWS + NLT - 1) / NLT;
-    static_assert(PK >= 1 && CH * RK % NLT == 0, "tile shape");
+    constexpr int MRUNS = 384;                          // workspace runs of T (and of Aqk)
+    constexpr int CRUNS = WS_AQ / 16;                   // runs of the state-step part
+    constexpr int ORUNS = (WS_CHUNK - WS_AQ) / 16;      // runs of the output-step part
+    constexpr int PC = (CRUNS + NLT - 1) / NLT;
+    constexpr int PO = (ORUNS + NLT - 1) / NLT;
+    static_assert(PK >= 1 && CH * RP % NLT == 0, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const ChainId id = chain_id(NTILE, Hqk, grp, xcd_remap);
@@ -1051,9 +1173,13 @@ __global__ __launch_bounds__((NLW + NW) * 64, 1) void chunk_state_kernel(
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int NT = (T_len + CH - 1) / CH;
-    const size_t qk_row = (size_t)Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
     const size_t head = (size_t)b * Hv + j;
+    auto cslot = [&](int c) { return smem + (size_t)(c & 1) * L::cslot; };
+    auto oslot = [&](int c) { return smem + L::obase + (size_t)(c & 1) * L::oslot; };
+    auto hxp = [&](int c, int cw) {
+        return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
+    };
 
     if (w < NLW) {
         // ================================================================= loader waves
@@ -1061,108 +1187,208 @@ __global__ __launch_bounds__((NLW + NW) * 64, 1) void chunk_state_kernel(
         const bf16* kb_ = k + ((size_t)b * T_len * Hqk + i) * DK;
         const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
         const unsigned char* wh = ws + head * NT * WS_CHUNK;
-        bf16x4 rk[PK][2], rq[PK][2];
+        bf16x8 rk[PK][2], rq[PK][2];
         bf16x8 rv[PV];
-        floatx4 rw[PW];
-        // K, Q run s of a chunk: row s / RK, physical 16-byte run m = s % RK of the column-
-        // permuted row, i.e. logical columns 32(m/4) + 4(m%4) .. +3 and the same + 16
-        auto load = [&](int c) {
+        floatx4 rc[PC], ro[PO];
+        // K, Q pair-run s of a chunk: row s / RP, 32-column block pr / 2 (pr = s % RP), half
+        // a = pr % 2.  Two 16-byte loads (logical columns 32 blk + 8a .. +7 and the same + 16)
+        // hold exactly the physical runs 4 blk + 2a and + 1 of the column-permuted row, which sit
+        // side by side: 32 contiguous bytes in LDS.  Rows past T are loaded clamped to the last
+        // row and staged as they are: their beta is 0, so T keeps them out of Delta (identity
+        // rows) and they add nothing anywhere.
+        const int qk_row = Hqk * DK;
+        const int vrow = Hv * DV;
+        int kq_r[PK], kq_c[PK];
+#pragma unroll
+        for (int p = 0; p < PK; ++p) {
+            const int s = tid + p * NLT, pr = s % RP;
+            kq_r[p] = s / RP;
+            kq_c[p] = 32 * (pr >> 1) + 8 * (pr & 1);
+        }
+        auto load_chain = [&](int c) {
             const int t0 = c * CH, n = min(CH, T_len - t0);
+            const bf16* kc = kb_ + (size_t)t0 * qk_row;
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
-                const int s = tid + p * NLT;
-                const int r = min(s / RK, n - 1), m = s % RK;
-                const size_t off = (size_t)(t0 + r) * qk_row + 32 * (m >> 2) + 4 * (m & 3);
-                rk[p][0] = *reinterpret_cast<const bf16x4*>(kb_ + off);
-                rk[p][1] = *reinterpret_cast<const bf16x4*>(kb_ + off + 16);
-                rq[p][0] = *reinterpret_cast<const bf16x4*>(qb + off);
-                rq[p][1] = *reinterpret_cast<const bf16x4*>(qb + off + 16);
+                const int off = min(kq_r[p], n - 1) * qk_row + kq_c[p];
+                rk[p][0] = *reinterpret_cast<const bf16x8*>(kc + off);
+                rk[p][1] = *reinterpret_cast<const bf16x8*>(kc + off + 16);
             }
+            const bf16* vc = vb + (size_t)t0 * vrow;
 #pragma unroll
             for (int p = 0; p < PV; ++p) {
                 const int s = min(tid + p * NLT, CH * RV - 1);
-                const int r = min(s / RV, n - 1), c8 = (s % RV) * 8;
-                rv[p] = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + r) * v_row + c8);
+                rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
             }
             const unsigned char* wcn = wh + (size_t)c * WS_CHUNK;
 #pragma unroll
-            for (int p = 0; p < PW; ++p) {
-                const int s = min(tid + p * NLT, NWS - 1);
-                rw[p] = *reinterpret_cast<const floatx4*>(wcn + 16 * s);
-            }
+            for (int p = 0; p < PC; ++p) rc[p] = *reinterpret_cast<const floatx4*>(wcn + 16 * min(tid + p * NLT, CRUNS - 1));
         };
-        auto stage = [&](int c) {
-            const int n = min(CH, T_len - c * CH);
-            unsigned char* sb = smem + (size_t)(c & 1) * L::slot;
-            op_t* Ks = reinterpret_cast<op_t*>(sb + L::k);
-            op_t* Qs = reinterpret_cast<op_t*>(sb + L::q);
-            bf16* Vs = reinterpret_cast<bf16*>(sb + L::v);
+        auto load_out = [&](int c) {
+            const int t0 = c * CH, n = min(CH, T_len - t0);
+            const bf16* qc = qb + (size_t)t0 * qk_row;
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
-                const int s = tid + p * NLT;
-                const int r = s / RK, m = s % RK;
-                const bool live = r < n;
-                *reinterpret_cast<opx8*>(Ks + r * L::KP + 8 * m) = live ? to_op(rk[p][0], rk[p][1]) : opx8{};
-                *reinterpret_cast<opx8*>(Qs + r * L::KP + 8 * m) = live ? to_op(rq[p][0], rq[p][1]) : opx8{};
+                const int off = min(kq_r[p], n - 1) * qk_row + kq_c[p];
+                rq[p][0] = *reinterpret_cast<const bf16x8*>(qc + off);
+                rq[p][1] = *reinterpret_cast<const bf16x8*>(qc + off + 16);
+            }
+            const unsigned char* wcn = wh + (size_t)c * WS_CHUNK + WS_AQ;
+#pragma unroll
+            for (int p = 0; p < PO; ++p) ro[p] = *reinterpret_cast<const floatx4*>(wcn + 16 * min(tid + p * NLT, ORUNS - 1));
+        };
+        // workspace T / Aqk run u -> (row, physical column) of the [64][CP] LDS matrix
+        auto mrow = [](int u) { return u < 128 ? u >> 2 : 32 + ((u - 128) >> 3); };
+        auto mcol = [](int u) { return u < 128 ? 8 * (u & 3) : 8 * ((u - 128) & 7); };
+        auto stage_chain = [&](int c) {
+            unsigned char* sb = cslot(c);
+            op_t* Ks = reinterpret_cast<op_t*>(sb + L::k);
+            bf16* Vs = reinterpret_cast<bf16*>(sb + L::v);
+            op_t* Ts = reinterpret_cast<op_t*>(sb + L::t);
+#pragma unroll
+            for (int p = 0; p < PK; ++p) {
+                opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((tid + p * NLT) % RP));
+                bf16_pair_to_op(rk[p][0], rk[p][1], dst[0], dst[1]);
             }
 #pragma unroll
             for (int p = 0; p < PV; ++p) {
                 const int s = tid + p * NLT;
-                if (s < CH * RV) {
-                    const int r = s / RV, c8 = (s % RV) * 8;
-                    *reinterpret_cast<bf16x8*>(Vs + r * L::VP + c8) = r < n ? rv[p] : bf16x8{};
-                }
+                if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
             }
 #pragma unroll
-            for (int p = 0; p < PW; ++p) {
-                const int s = tid + p * NLT;
-                if (s < NWS) {
-                    // workspace run s -> T (s < 384), Aqk (< 768) or the vectors
-                    unsigned char* dst;
-                    if (s < 768) {
-                        const int u = s < 384 ? s : s - 384;
-                        const int r = u < 128 ? u >> 2 : 32 + ((u - 128) >> 3);
-                        const int c8 = u < 128 ? 8 * (u & 3) : 8 * ((u - 128) & 7);
-                        dst = sb + (s < 384 ? L::t : L::a) + (size_t)(r * CP + c8) * 2;
-                    } else {
-                        dst = sb + L::e + (size_t)(s - 768) * 16;
-                    }
-                    *reinterpret_cast<floatx4*>(dst) = rw[p];
-                }
+            for (int p = 0; p < PC; ++p) {
+                const int u = tid + p * NLT;
+                if (u < MRUNS)
+                    *reinterpret_cast<floatx4*>(Ts + mrow(u) * CP + mcol(u)) = rc[p];
+                else if (u < CRUNS)
+                    *reinterpret_cast<floatx4*>(sb + L::cv + (size_t)(u - MRUNS) * 16) = rc[p];
             }
         };
-        load(0);
-        stage(0);
-        if (NT > 1) load(1);
+        auto stage_out = [&](int c) {
+            unsigned char* sb = oslot(c);
+            op_t* Qs = reinterpret_cast<op_t*>(sb + L::q);
+            op_t* As = reinterpret_cast<op_t*>(sb + L::a);
+#pragma unroll
+            for (int p = 0; p < PK; ++p) {
+                opx8* dst = reinterpret_cast<opx8*>(Qs + kq_r[p] * L::KP + 16 * ((tid + p * NLT) % RP));
+                bf16_pair_to_op(rq[p][0], rq[p][1], dst[0], dst[1]);
+            }
+#pragma unroll
+            for (int p = 0; p < PO; ++p) {
+                const int u = tid + p * NLT;
+                if (u < MRUNS)
+                    *reinterpret_cast<floatx4*>(As + mrow(u) * CP + mcol(u)) = ro[p];
+                else if (u < ORUNS)
+                    *reinterpret_cast<floatx4*>(sb + L::eg + (size_t)(u - MRUNS) * 16) = ro[p];
+            }
+        };
+        load_chain(0);
+        load_out(0);
+        stage_chain(0);
+        if constexpr (!OW) stage_out(0);
+        if (NT > 1) {
+            load_chain(1);
+            if constexpr (!OW) load_out(1);
+        }
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
-            if (n + 1 < NT) {
-                stage(n + 1);
-                if (n + 2 < NT) load(n + 2);
+            GDN_TRACE(n, 0);
+            if (n + 1 < NT) stage_chain(n + 1);
+            if constexpr (OW) stage_out(n);   // used in iteration n + 1
+            else if (n + 1 < NT) stage_out(n + 1);
+            GDN_TRACE(n, 1);
+            if (n + 2 < NT) load_chain(n + 2);
+            if constexpr (OW) {
+                if (n + 1 < NT) load_out(n + 1);
+            } else {
+                if (n + 2 < NT) load_out(n + 2);
             }
+            GDN_TRACE(n, 2);
             lds_barrier();
         }
-    } else {
+    } else if (w < NLW + NW) {
         // ================================================================= chain waves
         const int cw = w - NLW;
         floatx4 hacc[NTN][MT];
-        load_state<DK, DV, NTN>(hacc, s0, head, c0 + cw * 16 * NTN, lane);
+        load_state<DK, DV, NTN>(hacc, s0, head, c0 + cw * NCOL, lane);
         bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0;
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
-            const unsigned char* sb = smem + (size_t)(n & 1) * L::slot;
-            const int t0 = n * CH;
-            chain_chunk<DK, BV, NW>(hacc, reinterpret_cast<const op_t*>(sb + L::k),
-                                    reinterpret_cast<const op_t*>(sb + L::q),
-                                    reinterpret_cast<const bf16*>(sb + L::v),
-                                    reinterpret_cast<const op_t*>(sb + L::t),
-                                    reinterpret_cast<const op_t*>(sb + L::a),
-                                    reinterpret_cast<const float*>(sb + L::e), ob + (size_t)t0 * v_row,
-                                    v_row, min(CH, T_len - t0), cw, lane,
-                                    [] { __builtin_amdgcn_sched_barrier(0); });
+            GDN_TRACE(n, 0);
+            const unsigned char* sb = cslot(n);
+            const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
+            const float* vs = reinterpret_cast<const float*>(sb + L::cv);
+            if constexpr (OW) {
+                opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
+                opx8 akt[2][MT];
+                chain_delta<DK, NTN, L::VP, NTN == 1>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * NCOL,
+                                                      reinterpret_cast<const op_t*>(sb + L::t), vs, lane, hb, db,
+                                                      dtb, akt);
+                opx8* hx = hxp(n, cw);
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt) {
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) hx[(nt * (KB + 2) + kk) * 64 + lane] = hb[nt][kk];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) hx[(nt * (KB + 2) + KB + cb) * 64 + lane] = db[nt][cb];
+                }
+                GDN_TRACE(n, 1);
+                if constexpr (NTN == 1) {
+                    apply_kt<DK, NTN>(hacc, akt[0], dtb, 0);
+                    apply_kt<DK, NTN>(hacc, akt[1], dtb, 1);
+                } else {
+                    chain_update<DK, NTN>(hacc, Ks, dtb, lane);
+                }
+                GDN_TRACE(n, 2);
+            } else {
+                const unsigned char* so = oslot(n);
+                const int t0 = n * CH;
+                opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
+                chain_delta<DK, NTN, L::VP>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * NCOL,
+                                            reinterpret_cast<const op_t*>(sb + L::t), vs, lane, hb, db, dtb);
+                __builtin_amdgcn_sched_barrier(0);
+                chain_out<DK, NTN>(hb, db, reinterpret_cast<const op_t*>(so + L::q),
+                                   reinterpret_cast<const op_t*>(so + L::a),
+                                   reinterpret_cast<const float*>(so + L::eg), ob + (size_t)t0 * v_row + cw * NCOL,
+                                   v_row, min(CH, T_len - t0), lane);
+                __builtin_amdgcn_sched_barrier(0);
+                chain_update<DK, NTN>(hacc, Ks, dtb, lane);
+            }
             lds_barrier();
         }
-        store_state<DK, DV, NTN>(hacc, sf, head, c0 + cw * 16 * NTN, lane);
+        store_state<DK, DV, NTN>(hacc, sf, head, c0 + cw * NCOL, lane);
+    } else {
+        // ================================================================= output waves
+        if constexpr (OW) {
+            const int ow = w - NLW - NW;
+            bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0 + ow * NCOL;
+            // O of chunk m from the hand-over of its chain wave and the staged Q, Aqk, exp(gc)
+            auto out = [&](int m) {
+                const unsigned char* so = oslot(m);
+                const opx8* hx = hxp(m, ow);
+                opx8 hb[NTN][KB], db[NTN][2];
+#pragma unroll
+                for (int nt = 0; nt < NTN; ++nt) {
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = hx[(nt * (KB + 2) + kk) * 64 + lane];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) db[nt][cb] = hx[(nt * (KB + 2) + KB + cb) * 64 + lane];
+                }
+                const int t0 = m * CH;
+                chain_out<DK, NTN>(hb, db, reinterpret_cast<const op_t*>(so + L::q),
+                                   reinterpret_cast<const op_t*>(so + L::a),
+                                   reinterpret_cast<const float*>(so + L::eg), ob + (size_t)t0 * v_row, v_row,
+                                   min(CH, T_len - t0), lane);
+            };
+            lds_barrier();
+            for (int n = 0; n < NT; ++n) {
+                GDN_TRACE(n, 0);
+                if (n >= 1) out(n - 1);
+                GDN_TRACE(n, 1);
+                lds_barrier();
+            }
+            out(NT - 1);
+        }
     }
 }
 
@@ -1230,7 +1456,8 @@ template <int DK, int DV, int NW, int NTN>
 hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
     constexpr int BV = 16 * NW * NTN;
-    using L = SLds<DK, BV>;
+    using L = SLds<DK, BV, NW>;
+    constexpr int nthr = (NLW + (L::OW ? 2 : 1) * NW) * 64;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
     auto kern = chunk_state_kernel<DK, DV, NW, NTN>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
@@ -1239,7 +1466,7 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
     const long nblk = (long)a.B * a.Hv * (DV / BV);
     const long per_xcd = nblk / 8;
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((NLW + NW) * 64), L::bytes, st, (const bf16*)a.q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(nthr), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, a.s0, a.sf,
                        (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap);
     return hipGetLastError();
@@ -1250,7 +1477,7 @@ hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
     const int grp = a.Hv / a.Hqk;
     const int NT = (a.T + CH - 1) / CH;
-    const long nprep = (long)a.B * a.Hv * NT;
+    const long nprep = (long)a.B * a.Hqk * NT;
     hipLaunchKernelGGL(chunk_prep_kernel<DK>, dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, a.T, a.Hqk, a.Hv, grp, NT, a.scale);
     hipError_t e = hipGetLastError();
@@ -1301,3 +1528,11 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, void* ws, hipStream_t st)
 }
 
 }  // namespace gdn
+
+#ifdef GDN_PHASE_TRACE
+extern "C" int gdn_phase_trace_read(long long* host)
+{
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::gdn_phase_ts), sizeof(gdn::gdn_phase_ts), 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif
