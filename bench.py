@@ -6,9 +6,10 @@ float32 state.  `value` is prefill tokens/s with the inputs resident in HBM; rot
 (larger than the 256 MB Infinity Cache) keep every step's reads cold.
 
 The same JSON line carries
-  roofline      -- the prefill kernel's achieved algorithmic bytes/s against 8 TB/s (its binding
-                   roofline: 167 flop/B is below the bf16-MFMA/HBM ridge), the kernel's average
-                   launch duration from HIP events on its own stream, its bf16-MFMA fraction, and
+  roofline      -- the prefill call's achieved algorithmic bytes/s against 8 TB/s (its binding
+                   roofline: 167 flop/B is below the bf16-MFMA/HBM ridge), the call's average
+                   duration from HIP events on its own stream (for the split path: the per-chunk
+                   prep kernel and the state-pass kernel together), its bf16-MFMA fraction, and
                    the HBM traffic measured with rocprofv3 counters when a matching record exists;
   cpu_baseline  -- the float64 oracle timed on the host cores on the same workload;
   decode        -- the 64-step fused decode workload (B=256, Hv=32, d=128, fp32 state 512 MiB):
@@ -58,6 +59,13 @@ def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
     """Per step: the float32 state read and written once, q and k per query/key head, v and o per
     value head, g and beta in float32."""
     return B * Hv * dk * dv * 4 * 2 + B * Hqk * dk * es * 2 + B * Hv * dv * es * 2 + B * Hv * 4 * 2
+
+
+# What one gdn_chunk_fwd launches, per kernel family; the roofline is taken over the whole call
+# (HIP events around it on its stream), i.e. over both kernels of the split path.
+KERNELS = {"mfma": "chunk_mfma_kernel",
+           "mfma_split": "chunk_prep_kernel + chunk_state_kernel",
+           "simt": "chunk_simt_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -237,7 +245,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK,
                      "traffic": traffic,
-                     "kernel": f"chunk_fwd ({r['kernel']})", "kernel_ms": r["kern"] * 1e3,
+                     "kernel": f"chunk_fwd ({KERNELS.get(r['kernel'], r['kernel'])})",
+                     "kernel_ms": r["kern"] * 1e3,
                      "workspace_bytes": r["workspace"],
                      "alg_bytes": r["bytes"], "alg_flops": r["flops"],
                      "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK},

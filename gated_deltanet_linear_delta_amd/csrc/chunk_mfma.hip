@@ -295,26 +295,29 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
     constexpr int KP = DK + 8;
     constexpr int KB = DK / 32;
     constexpr int MT = DK / 16;
-    constexpr bool EARLY = NTN == 1;
     const int ln = lane & 15;
     const int lg = lane >> 4;
-    // K fragments: all up front with one tile per wave; with two tiles (twice the MFMAs per k
-    // block) one k block ahead, which keeps the registers within budget
-    constexpr int AHEAD = NTN == 1 ? KB : 1;
+    // LDS reads complete in issue order and a wave can wait on at most 15 of them at a time, so
+    // they are issued in the order of use, behind scheduling fences: K blocks 0 and 1 and T
+    // first, then one more K block per k step of X = K h, then V and the row vectors.  With two
+    // tiles per wave (twice the MFMAs per k block) K runs one block ahead and V and the vectors
+    // follow X, which keeps the registers within budget.
     opx8 ak[KB][4];
-#pragma unroll
-    for (int kk = 0; kk < AHEAD; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, KP, 16 * mt + ln, 32 * kk, lg);
     opx8 at[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
-    // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
     bf16x4 vv[NTN][4];
     floatx4 bt[4], beg[4], ed[2][2];
-    auto fetch_rows = [&] {
+    auto load_k = [&](int kk) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, KP, 16 * mt + ln, 32 * kk, lg);
+    };
+    auto load_t = [&] {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
+    };
+    // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
+    auto load_rows = [&] {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -323,19 +326,25 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
             bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
             beg[mt] = ld4s(vs + V_BEG * CH + 16 * mt + 4 * lg);
         }
+    };
+    auto load_ed = [&] {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             ed[cb][0] = ld4s(vs + V_ED * CH + 32 * cb + 4 * lg);
             ed[cb][1] = ld4s(vs + V_ED * CH + 32 * cb + 16 + 4 * lg);
         }
     };
-    if constexpr (EARLY) fetch_rows();
+    constexpr bool EARLY = NTN == 1;
+    constexpr int AHEAD = EARLY ? 2 : 1;
+#pragma unroll
+    for (int kk = 0; kk < AHEAD; ++kk) load_k(kk);
+    if constexpr (EARLY) load_t();
+    __builtin_amdgcn_sched_barrier(0);
     const float ec = vs[V_EC * CH];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = pack_perm(hacc[nt][2 * kk], hacc[nt][2 * kk + 1]);
-    __builtin_amdgcn_sched_barrier(0);
     floatx4 X[NTN][4];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt)
@@ -343,14 +352,22 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
         for (int mt = 0; mt < 4; ++mt) X[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-        if (kk + AHEAD < KB) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) ak[kk + AHEAD][mt] = frag(Ks, KP, 16 * mt + ln, 32 * (kk + AHEAD), lg);
+        if (kk + AHEAD < KB) load_k(kk + AHEAD);
+        if constexpr (EARLY) {
+            if (kk + AHEAD == KB) load_rows();
+            if (kk + AHEAD == KB + 1) load_ed();
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTN; ++nt) X[nt][mt] = mfma32(ak[kk][mt], hb[nt][kk], X[nt][mt]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!EARLY) {
+        load_t();
+        load_rows();
+        load_ed();
     }
     // KT: the K^T fragments of phase 3, into the registers the K fragments free, their LDS
     // latency hidden behind the rest of this phase
@@ -365,7 +382,6 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
-    if constexpr (!EARLY) fetch_rows();
     opx8 rbf[NTN][2];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt) {
@@ -1484,7 +1500,9 @@ hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
     if (e != hipSuccess) return e;
     switch (choose_split_bv(a)) {
     case 16: return launch_state_t<DK, DV, 1, 1>(a, ws, st);
-    case 32: return launch_state_t<DK, DV, 2, 1>(a, ws, st);
+    case 32:
+        if (env_int("GDN_SPLIT_NW", 2) == 1) return launch_state_t<DK, DV, 1, 2>(a, ws, st);
+        return launch_state_t<DK, DV, 2, 1>(a, ws, st);
     case 64: return launch_state_t<DK, DV, 4, 1>(a, ws, st);
     default:
         if constexpr (DV >= 128) return launch_state_t<DK, DV, 4, 2>(a, ws, st);
