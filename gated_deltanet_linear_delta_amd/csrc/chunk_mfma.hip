@@ -122,16 +122,30 @@ constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk; fused 
 
 // Workspace of the split path, per (batch, value head, chunk), in two parts: what the state step
 // reads (T, then the rows V_B..V_EC) and what the output step reads (Aqk, then the row V_EG).
-// T and Aqk are float16 in the column-permuted order (below), only the 16x32 blocks a product
-// reads (rows 0-31: columns 0-31; rows 32-63: columns 0-63).
+// T and Aqk are float16 in MFMA fragment order: the six 16x32 operand blocks a product reads
+// ((row tile, k block) = (0,0), (1,0), (2,0), (2,1), (3,0), (3,1)), each as 64 lanes x 16 bytes
+// holding what frag() would read from the column-permuted matrix, so a wave loads a fragment
+// with one coalesced 16-byte load.
 constexpr int WS_T = 0;
 constexpr int WS_CV = WS_T + 3072 * 2;
 constexpr int WS_AQ = WS_CV + 4 * CH * 4;
 constexpr int WS_EG = WS_AQ + 3072 * 2;
 constexpr int WS_CHUNK = WS_EG + CH * 4;   // 13568 bytes
 static_assert(WS_CHUNK % 16 == 0 && WS_AQ % 16 == 0, "workspace chunk");
+// After the [B, Hv, NT] chunks: per (batch, query/key head, chunk) the q rows of the chunk as
+// float16 B operands of the output product O^T = h^T Q^T, fragment (dk block kk, token tile ct)
+// at (kk * 4 + ct) * 1 KB: lane (n, g) holds q[16ct + n][32kk + 4g .. +3] and [32kk + 16 + 4g .. +3].
+template <int DK>
+constexpr size_t ws_q_bytes() { return (size_t)CH * DK * 2; }
 
-__device__ __forceinline__ int blk_off(int r, int pc) { return r < 32 ? r * 32 + pc : 1024 + (r - 32) * 64 + pc; }
+// fragment block of (row tile mt, k block cb), cb <= mt / 2
+__device__ __forceinline__ constexpr int tblk(int mt, int cb) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + cb; }
+// element offset of (row r, physical column pc) of T or Aqk in the fragment-ordered layout
+__device__ __forceinline__ int frag_off(int r, int pc)
+{
+    const int lane = (r & 15) + 16 * ((pc & 31) >> 3);
+    return (tblk(r >> 4, pc >> 5) * 64 + lane) * 8 + (pc & 7);
+}
 
 __device__ __forceinline__ floatx4 mfma32(opx8 a, opx8 b, floatx4 c)
 {
@@ -286,9 +300,9 @@ __device__ __forceinline__ void apply_kt(floatx4 (&hacc)[NTN][DK / 16], const op
 // Every product's A fragments are loaded before its MFMAs, behind a scheduling barrier, so the
 // LDS latency is paid once per product rather than once per MFMA; with one tile per wave the V
 // tile and the gate vectors are fetched up front too.
-template <int DK, int NTN, int VP, bool KT = false>
+template <int DK, int NTN, int VP, bool KT = false, typename TF>
 __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const op_t* Ks,
-                                            const bf16* Vc, const op_t* Tm, const float* vs, int lane,
+                                            const bf16* Vc, TF&& tfrag, const float* vs, int lane,
                                             opx8 (&hb)[NTN][DK / 32], opx8 (&db)[NTN][2],
                                             opx8 (&dtb)[NTN][2], opx8 (*akt)[DK / 16] = nullptr)
 {
@@ -310,11 +324,12 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ak[kk][mt] = frag(Ks, KP, 16 * mt + ln, 32 * kk, lg);
     };
+    // T fragments (row tile mt, k block cb) from the caller: LDS reads or registers
     auto load_t = [&] {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = frag(Tm, CP, 16 * mt + ln, 32 * cb, lg);
+            for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = tfrag(mt, cb);
     };
     // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
     auto load_rows = [&] {
@@ -516,7 +531,10 @@ __device__ __forceinline__ void chain_chunk(floatx4 (&hacc)[BV / NW / 16][DK / 1
     constexpr int NCOL = BV / NW;
     constexpr int NTN = NCOL / 16;
     opx8 hb[NTN][DK / 32], db[NTN][2], dtb[NTN][2];
-    chain_delta<DK, NTN, BV + 16>(hacc, Ks, Vs + cw * NCOL, Tm, vs, lane, hb, db, dtb);
+    const int ln = lane & 15, lg = lane >> 4;
+    chain_delta<DK, NTN, BV + 16>(hacc, Ks, Vs + cw * NCOL,
+                                  [&](int mt, int cb) { return frag(Tm, CP, 16 * mt + ln, 32 * cb, lg); }, vs,
+                                  lane, hb, db, dtb);
     sync();
     chain_out<DK, NTN>(hb, db, Qs, Aq, vs + V_EG * CH, ob + cw * NCOL, v_row, nv, lane);
     sync();
@@ -894,13 +912,18 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
 // group in turn: the gate cumsum and vectors, A (beta and the decay mask), T = (I + A)^{-1}, and
 // Aqk (the decay mask and the scale), all into the workspace.
 template <int DK>
-__global__ __launch_bounds__(64) void chunk_prep_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, unsigned char* __restrict__ ws, int T_len, int Hqk, int Hv,
-    int grp, int NT, float scale)
+    const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
+    int T_len, int Hqk, int Hv, int grp, int NT, float scale)
 {
     constexpr int KB = DK / 32;
-    __shared__ __attribute__((aligned(16))) float Af[CH * AFP];   // A^T, float32
+    // A in two parts: the diagonal 16x16 blocks transposed in float32 for the solve
+    // (Ad[w][x][r] = A_ww[r][x]), the off-diagonal blocks the merges read transposed in float16
+    // (Ah[i][r - 16] = A[r][i], i < 48 <= r + 16); about 20 KB of LDS per wave in all
+    constexpr int ADP = 20, AHP = 56;
+    __shared__ __attribute__((aligned(16))) float Ad[4 * 16 * ADP];
+    __shared__ __attribute__((aligned(16))) op_t Ah[48 * AHP];
     __shared__ __attribute__((aligned(16))) op_t Tm[CH * CP];     // T, column-permuted float16
     __shared__ __attribute__((aligned(16))) float pg[CH];         // gc
     __shared__ __attribute__((aligned(16))) float pb[CH];         // beta
@@ -952,6 +975,25 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             gq[t] = mfma_bf(kf[TJ[t]][kk], qf[TI[t]][kk], gq[t]);
         }
     GDN_TRACE_PREP(1);
+    // q as output-product operands: multiplying by identity columns moves q^T into accumulator
+    // layout exactly (D[m][n] = q[16ct + n][32kk + off + m]); two such tiles stacked (off = 0, 16)
+    // are the perm-K B operand.  Stored once for the head group.
+    {
+        opx8* wq = reinterpret_cast<opx8*>(wsq + (((size_t)b * Hqk + i) * NT + c) * ws_q_bytes<DK>());
+        bf16x8 eye[2];
+#pragma unroll
+        for (int off = 0; off < 2; ++off)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) eye[off][e] = (bf16)((8 * lg + e == ln + 16 * off) ? 1.f : 0.f);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const floatx4 lo = mfma_bf(eye[0], qf[ct][kk], floatx4{0.f, 0.f, 0.f, 0.f});
+                const floatx4 hi = mfma_bf(eye[1], qf[ct][kk], floatx4{0.f, 0.f, 0.f, 0.f});
+                wq[(kk * 4 + ct) * 64 + lane] = pack_perm(lo, hi);
+            }
+    }
 
     for (int jj = 0; jj < grp; ++jj) {
         const int j = i * grp + jj;
@@ -977,18 +1019,33 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             reinterpret_cast<float*>(wc + WS_EG)[lane] = scale * eg;
         }
         wave_lds_fence();
-        // A = strictly-lower( beta_r exp(gc_r - gc_i) (k_r . k_i) ), stored transposed in float32
+        // the gate values this lane's tiles need, fetched together: gc and beta of rows
+        // 16t + 4lg .. +3 and gc of row 16t + ln, t = 0..3
+        floatx4 g4[4], b4[4];
+        float g1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            g4[t] = ld4s(pg + 16 * t + 4 * lg);
+            b4[t] = ld4s(pb + 16 * t + 4 * lg);
+            g1[t] = pg[16 * t + ln];
+        }
+        // A = strictly-lower( beta_r exp(gc_r - gc_i) (k_r . k_i) ): diagonal blocks in float32,
+        // the rest in float16, both transposed
 #pragma unroll
         for (int t = 0; t < 10; ++t) {
             const int cc = 16 * TJ[t] + ln;
             const int r0 = 16 * TI[t] + 4 * lg;
-            const float gcc = pg[cc];
-            const floatx4 gr = ld4s(pg + r0);
-            const floatx4 br = ld4s(pb + r0);
+            const float gcc = g1[TJ[t]];
+            const floatx4 gr = g4[TI[t]];
+            const floatx4 br = b4[TI[t]];
             floatx4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[e] = cc < r0 + e ? br[e] * __expf(gr[e] - gcc) * gk[t][e] : 0.f;
-            *reinterpret_cast<floatx4*>(Af + cc * AFP + r0) = out;   // A^T[cc][r0..r0+3]
+            if (TI[t] == TJ[t])
+                *reinterpret_cast<floatx4*>(Ad + (16 * TI[t] + ln) * ADP + 4 * lg) = out;
+            else
+                *reinterpret_cast<opx4*>(Ah + cc * AHP + r0 - 16) =
+                    opx4{(op_t)out[0], (op_t)out[1], (op_t)out[2], (op_t)out[3]};
         }
         // Aqk = lower-incl( scale exp(gc_r - gc_i) (q_r . k_i) ); rows past T are zero
         {
@@ -997,19 +1054,19 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             for (int t = 0; t < 10; ++t) {
                 const int r = 16 * TI[t] + ln;
                 const int i0 = 16 * TJ[t] + 4 * lg;
-                const float gr = pg[r];
-                const floatx4 gi = ld4s(pg + i0);
+                const float gr = g1[TI[t]];
+                const floatx4 gi = g4[TJ[t]];
                 opx4 out;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     out[e] = (op_t)((i0 + e <= r && r < n) ? scale * __expf(gr - gi[e]) * gq[t][e] : 0.f);
-                *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = out;
+                *reinterpret_cast<opx4*>(wa + frag_off(r, pcol(i0))) = out;
             }
             // the stored strictly-upper blocks (0, 1) and (2, 3)
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const int r = 32 * p + ln, i0 = 32 * p + 16 + 4 * lg;
-                *reinterpret_cast<opx4*>(wa + blk_off(r, pcol(i0))) = opx4{};
+                *reinterpret_cast<opx4*>(wa + frag_off(r, pcol(i0))) = opx4{};
             }
         }
         GDN_TRACE_PREP(2);
@@ -1018,28 +1075,27 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
         opx4 a10[2];
 #pragma unroll
         for (int wi = 0; wi < 2; ++wi) {
-            const float* at = Af + (32 * wi + 4 * lg) * AFP + 16 * (2 * wi + 1) + ln;
-            a10[wi] = opx4{(op_t)at[0], (op_t)at[AFP], (op_t)at[2 * AFP], (op_t)at[3 * AFP]};
+            const op_t* at = Ah + (32 * wi + 4 * lg) * AHP + 32 * wi + ln;   // A[16(w+1)+ln][16w+4lg+j]
+            a10[wi] = opx4{at[0], at[AHP], at[2 * AHP], at[3 * AHP]};
         }
         opx8 a2[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-            const float* ac = Af + (4 * lg) * AFP + 32 + 16 * a + ln;
-            a2[a] = opx8{(op_t)ac[0], (op_t)ac[AFP], (op_t)ac[2 * AFP], (op_t)ac[3 * AFP],
-                         (op_t)ac[16 * AFP], (op_t)ac[17 * AFP], (op_t)ac[18 * AFP], (op_t)ac[19 * AFP]};
+            const op_t* ac = Ah + (4 * lg) * AHP + 16 + 16 * a + ln;   // A[32+16a+ln][k], perm-K
+            a2[a] = opx8{ac[0], ac[AHP], ac[2 * AHP], ac[3 * AHP], ac[16 * AHP], ac[17 * AHP], ac[18 * AHP], ac[19 * AHP]};
         }
         // diagonal blocks of T: lane group lg inverts block lg, lane ln forms its column ln by
         // right-looking forward substitution in float32; each step's column of A is fetched two
         // steps ahead
         {
-            const float* At = Af + (16 * lg) * AFP + 16 * lg;   // At[x * AFP + r] = A_ww[r][x]
+            const float* At = Ad + (16 * lg) * ADP;   // At[x * ADP + r] = A_ww[r][x]
             float tcol[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) tcol[r] = (r == ln) ? 1.f : 0.f;
-            floatx4 col[15][4];
+            floatx4 col[3][4];   // rotating: step x uses slot x % 3
             auto fetch = [&](int x) {
 #pragma unroll
-                for (int q4 = (x + 1) / 4; q4 < 4; ++q4) col[x][q4] = ld4s(At + x * AFP + 4 * q4);
+                for (int q4 = (x + 1) / 4; q4 < 4; ++q4) col[x % 3][q4] = ld4s(At + x * ADP + 4 * q4);
             };
             fetch(0);
             fetch(1);
@@ -1047,7 +1103,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
             for (int x = 0; x < 15; ++x) {
                 if (x + 2 < 15) fetch(x + 2);
 #pragma unroll
-                for (int r = x + 1; r < 16; ++r) tcol[r] = fmaf(-col[x][r / 4][r % 4], tcol[x], tcol[r]);
+                for (int r = x + 1; r < 16; ++r) tcol[r] = fmaf(-col[x % 3][r / 4][r % 4], tcol[x], tcol[r]);
             }
             op_t* tc = Tm + (16 * lg) * CP + pcol(16 * lg + ln);
 #pragma unroll
@@ -1104,82 +1160,65 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
         }
         GDN_TRACE_PREP(4);
         wave_lds_fence();
-        // T -> workspace (the stored blocks, 16 bytes per lane per step, consecutive)
+        // T -> workspace, in fragment order (one coalesced 16-byte store per block)
         {
-            op_t* wt = reinterpret_cast<op_t*>(wc + WS_T);
+            opx8* wt = reinterpret_cast<opx8*>(wc + WS_T);
+            constexpr int BM[6] = {0, 1, 2, 2, 3, 3}, BC[6] = {0, 0, 0, 1, 0, 1};
 #pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                const int s = lane + 64 * p;
-                const int r = s < 128 ? s >> 2 : 32 + ((s - 128) >> 3);
-                const int c8 = s < 128 ? 8 * (s & 3) : 8 * ((s - 128) & 7);
-                *reinterpret_cast<opx8*>(wt + 8 * s) = *reinterpret_cast<const opx8*>(Tm + r * CP + c8);
-            }
+            for (int bk = 0; bk < 6; ++bk) wt[bk * 64 + lane] = frag(Tm, CP, 16 * BM[bk] + ln, 32 * BC[bk], lg);
         }
         GDN_TRACE_PREP(5);
     }
 }
 
 // Split path, kernel 2: the state pass.  One workgroup per (batch, value head, column tile of
-// BV = 16 NW NTN columns), with NW chain waves and NLW loader waves, one barrier per chunk.
-// LDS holds two double-buffered sets: the state-step tiles (K, V, T and the state vectors of a
-// chunk) and the output-step tiles (Q, Aqk and scale exp(gc)).  In iteration n the chain waves
-// carry chunk n while the loaders stage chunk n + 1's state-step tiles (q, k converted to
-// column-permuted float16; the rest copied from the workspace) and prefetch chunk n + 2.
-// * Narrow tiles (NW <= 2): the output step leaves the chain.  Each chain wave hands its packed
-//   h and Delta to an output wave of its own through LDS; in iteration n the output waves form
-//   O of chunk n - 1 while the loaders stage the output-step tiles of chunk n (one iteration
-//   ahead of their use), so every hand-over crosses exactly one barrier.
-// * Wide tiles (NW = 4): each chain wave runs all three phases, and the loaders stage both sets
-//   of chunk n + 1.
+// BV = 16 NW columns) with SLW loader waves, NW chain waves (16 state columns each) and NW
+// output waves, one barrier per chunk.
+// * Loaders stage chunk n + 1's K (q, k converted to column-permuted float16), V and state-step
+//   vectors into double-buffered LDS while the chain waves carry chunk n, and prefetch chunk
+//   n + 2 into registers.  That is all that goes through LDS besides the hand-over below: LDS
+//   bandwidth is what a chunk's latency is most sensitive to.
+// * A chain wave reads T straight from the workspace in fragment order (16-byte coalesced loads,
+//   one chunk ahead, double-buffered in registers over a two-chunk loop), runs the Delta and
+//   update phases, and hands its packed h and Delta to its output wave through LDS.
+// * An output wave forms O of chunk n - 1 in iteration n from that hand-over and Q, Aqk and
+//   scale exp(gc) read from the workspace in fragment order.  Its inputs for the next chunk load
+//   once it is done with the current one.
+constexpr int SLW = 2;   // loader waves of the state pass
+
 template <int DK, int BV, int NW>
 struct SLds {
     static constexpr int KP = DK + 8;
     static constexpr int VP = BV + 16;
-    static constexpr bool OW = NW <= 2;
-    static constexpr int NTN = BV / NW / 16;
-    // state-step slot
     static constexpr size_t k = 0;                                   // K   [64][KP] f16
     static constexpr size_t v = k + (size_t)CH * KP * 2;             // V   [64][VP] bf16
-    static constexpr size_t t = v + (size_t)CH * VP * 2;             // T   [64][CP] f16
-    static constexpr size_t cv = t + (size_t)CH * CP * 2;            // rows V_B..V_EC, f32
+    static constexpr size_t cv = v + (size_t)CH * VP * 2;            // rows V_B..V_EC, f32
     static constexpr size_t cslot = cv + (size_t)4 * CH * 4;
-    // output-step slot
-    static constexpr size_t q = 0;                                   // Q   [64][KP] f16
-    static constexpr size_t a = q + (size_t)CH * KP * 2;             // Aqk [64][CP] f16
-    static constexpr size_t eg = a + (size_t)CH * CP * 2;            // scale exp(gc), f32
-    static constexpr size_t oslot = eg + (size_t)CH * 4;
-    static constexpr size_t obase = 2 * cslot;
-    // chain -> output hand-over, [2][NW]: hb (NTN x DK/32 fragments) then db (NTN x 2), each
-    // fragment 64 lanes x 16 bytes
-    static constexpr size_t hx_frags = (size_t)NTN * (DK / 32 + 2);
-    static constexpr size_t hx = obase + 2 * oslot;
-    static constexpr size_t bytes = hx + (OW ? 2 * NW * hx_frags * 1024 : 0);
+    // chain -> output hand-over, [2][NW]: hb (DK/32 fragments) then db (2), each fragment 64
+    // lanes x 16 bytes
+    static constexpr size_t hx_frags = DK / 32 + 2;
+    static constexpr size_t hx = 2 * cslot;
+    static constexpr size_t bytes = hx + 2 * NW * hx_frags * 1024;
 };
 
-template <int DK, int DV, int NW, int NTN>
-__global__ __launch_bounds__((NLW + (NW <= 2 ? 2 : 1) * NW) * 64, 1) void chunk_state_kernel(
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const unsigned char* __restrict__ ws, const float* s0, float* sf, bf16* __restrict__ o,
-    int T_len, int Hqk, int Hv, int grp, int xcd_remap)
+    const unsigned char* __restrict__ ws, const unsigned char* __restrict__ wsq, const float* s0,
+    float* sf, bf16* __restrict__ o, int T_len, int Hqk, int Hv, int grp, int xcd_remap)
 {
-    constexpr int BV = 16 * NW * NTN;
+    constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
-    constexpr bool OW = L::OW;
     constexpr int NTILE = DV / BV;
     constexpr int MT = DK / 16;
     constexpr int KB = DK / 32;
-    constexpr int NCOL = 16 * NTN;                      // columns per chain wave
-    constexpr int NLT = NLW * 64;                       // loader threads
+    constexpr int NLT = SLW * 64;                       // loader threads
     constexpr int RP = DK / 16;                         // 32-byte pair-runs per K row
-    constexpr int PK = CH * RP / NLT;                   // K (and Q) pair-runs per loader lane
+    constexpr int PK = CH * RP / NLT;                   // pair-runs per loader lane
     constexpr int RV = BV / 8;                          // 16-byte runs per V row
     constexpr int PV = (CH * RV + NLT - 1) / NLT;       // V runs per loader lane
-    constexpr int MRUNS = 384;                          // workspace runs of T (and of Aqk)
-    constexpr int CRUNS = WS_AQ / 16;                   // runs of the state-step part
-    constexpr int ORUNS = (WS_CHUNK - WS_AQ) / 16;      // runs of the output-step part
-    constexpr int PC = (CRUNS + NLT - 1) / NLT;
-    constexpr int PO = (ORUNS + NLT - 1) / NLT;
-    static_assert(PK >= 1 && CH * RP % NLT == 0, "tile shape");
+    constexpr int CVR = 4 * CH * 4 / 16;                // 16-byte runs of the state vectors
+    static_assert(PK >= 1 && CH * RP % NLT == 0 && CVR <= NLT, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const ChainId id = chain_id(NTILE, Hqk, grp, xcd_remap);
@@ -1188,32 +1227,32 @@ __global__ __launch_bounds__((NLW + (NW <= 2 ? 2 : 1) * NW) * 64, 1) void chunk_
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
+    const int ln = lane & 15;
+    const int lg = lane >> 4;
     const int NT = (T_len + CH - 1) / CH;
+    const int qk_row = Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
     const size_t head = (size_t)b * Hv + j;
+    const unsigned char* wh = ws + head * NT * WS_CHUNK;
     auto cslot = [&](int c) { return smem + (size_t)(c & 1) * L::cslot; };
-    auto oslot = [&](int c) { return smem + L::obase + (size_t)(c & 1) * L::oslot; };
     auto hxp = [&](int c, int cw) {
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
     };
 
-    if (w < NLW) {
+    if (w < SLW) {
         // ================================================================= loader waves
-        const bf16* qb = q + ((size_t)b * T_len * Hqk + i) * DK;
         const bf16* kb_ = k + ((size_t)b * T_len * Hqk + i) * DK;
         const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
-        const unsigned char* wh = ws + head * NT * WS_CHUNK;
-        bf16x8 rk[PK][2], rq[PK][2];
+        const int vrow = Hv * DV;
+        bf16x8 rk[PK][2];
         bf16x8 rv[PV];
-        floatx4 rc[PC], ro[PO];
-        // K, Q pair-run s of a chunk: row s / RP, 32-column block pr / 2 (pr = s % RP), half
+        floatx4 rc = {};
+        // K pair-run s of a chunk: row s / RP, 32-column block pr / 2 (pr = s % RP), half
         // a = pr % 2.  Two 16-byte loads (logical columns 32 blk + 8a .. +7 and the same + 16)
         // hold exactly the physical runs 4 blk + 2a and + 1 of the column-permuted row, which sit
         // side by side: 32 contiguous bytes in LDS.  Rows past T are loaded clamped to the last
         // row and staged as they are: their beta is 0, so T keeps them out of Delta (identity
         // rows) and they add nothing anywhere.
-        const int qk_row = Hqk * DK;
-        const int vrow = Hv * DV;
         int kq_r[PK], kq_c[PK];
 #pragma unroll
         for (int p = 0; p < PK; ++p) {
@@ -1236,31 +1275,12 @@ __global__ __launch_bounds__((NLW + (NW <= 2 ? 2 : 1) * NW) * 64, 1) void chunk_
                 const int s = min(tid + p * NLT, CH * RV - 1);
                 rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
             }
-            const unsigned char* wcn = wh + (size_t)c * WS_CHUNK;
-#pragma unroll
-            for (int p = 0; p < PC; ++p) rc[p] = *reinterpret_cast<const floatx4*>(wcn + 16 * min(tid + p * NLT, CRUNS - 1));
+            if (tid < CVR) rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * tid);
         };
-        auto load_out = [&](int c) {
-            const int t0 = c * CH, n = min(CH, T_len - t0);
-            const bf16* qc = qb + (size_t)t0 * qk_row;
-#pragma unroll
-            for (int p = 0; p < PK; ++p) {
-                const int off = min(kq_r[p], n - 1) * qk_row + kq_c[p];
-                rq[p][0] = *reinterpret_cast<const bf16x8*>(qc + off);
-                rq[p][1] = *reinterpret_cast<const bf16x8*>(qc + off + 16);
-            }
-            const unsigned char* wcn = wh + (size_t)c * WS_CHUNK + WS_AQ;
-#pragma unroll
-            for (int p = 0; p < PO; ++p) ro[p] = *reinterpret_cast<const floatx4*>(wcn + 16 * min(tid + p * NLT, ORUNS - 1));
-        };
-        // workspace T / Aqk run u -> (row, physical column) of the [64][CP] LDS matrix
-        auto mrow = [](int u) { return u < 128 ? u >> 2 : 32 + ((u - 128) >> 3); };
-        auto mcol = [](int u) { return u < 128 ? 8 * (u & 3) : 8 * ((u - 128) & 7); };
         auto stage_chain = [&](int c) {
             unsigned char* sb = cslot(c);
             op_t* Ks = reinterpret_cast<op_t*>(sb + L::k);
             bf16* Vs = reinterpret_cast<bf16*>(sb + L::v);
-            op_t* Ts = reinterpret_cast<op_t*>(sb + L::t);
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
                 opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((tid + p * NLT) % RP));
@@ -1271,140 +1291,131 @@ __global__ __launch_bounds__((NLW + (NW <= 2 ? 2 : 1) * NW) * 64, 1) void chunk_
                 const int s = tid + p * NLT;
                 if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
             }
-#pragma unroll
-            for (int p = 0; p < PC; ++p) {
-                const int u = tid + p * NLT;
-                if (u < MRUNS)
-                    *reinterpret_cast<floatx4*>(Ts + mrow(u) * CP + mcol(u)) = rc[p];
-                else if (u < CRUNS)
-                    *reinterpret_cast<floatx4*>(sb + L::cv + (size_t)(u - MRUNS) * 16) = rc[p];
-            }
-        };
-        auto stage_out = [&](int c) {
-            unsigned char* sb = oslot(c);
-            op_t* Qs = reinterpret_cast<op_t*>(sb + L::q);
-            op_t* As = reinterpret_cast<op_t*>(sb + L::a);
-#pragma unroll
-            for (int p = 0; p < PK; ++p) {
-                opx8* dst = reinterpret_cast<opx8*>(Qs + kq_r[p] * L::KP + 16 * ((tid + p * NLT) % RP));
-                bf16_pair_to_op(rq[p][0], rq[p][1], dst[0], dst[1]);
-            }
-#pragma unroll
-            for (int p = 0; p < PO; ++p) {
-                const int u = tid + p * NLT;
-                if (u < MRUNS)
-                    *reinterpret_cast<floatx4*>(As + mrow(u) * CP + mcol(u)) = ro[p];
-                else if (u < ORUNS)
-                    *reinterpret_cast<floatx4*>(sb + L::eg + (size_t)(u - MRUNS) * 16) = ro[p];
-            }
+            if (tid < CVR) *reinterpret_cast<floatx4*>(sb + L::cv + 16 * tid) = rc;
         };
         load_chain(0);
-        load_out(0);
         stage_chain(0);
-        if constexpr (!OW) stage_out(0);
-        if (NT > 1) {
-            load_chain(1);
-            if constexpr (!OW) load_out(1);
-        }
+        if (NT > 1) load_chain(1);
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
             GDN_TRACE(n, 0);
             if (n + 1 < NT) stage_chain(n + 1);
-            if constexpr (OW) stage_out(n);   // used in iteration n + 1
-            else if (n + 1 < NT) stage_out(n + 1);
             GDN_TRACE(n, 1);
             if (n + 2 < NT) load_chain(n + 2);
-            if constexpr (OW) {
-                if (n + 1 < NT) load_out(n + 1);
-            } else {
-                if (n + 2 < NT) load_out(n + 2);
-            }
             GDN_TRACE(n, 2);
             lds_barrier();
         }
-    } else if (w < NLW + NW) {
+    } else if (w < SLW + NW) {
         // ================================================================= chain waves
-        const int cw = w - NLW;
-        floatx4 hacc[NTN][MT];
-        load_state<DK, DV, NTN>(hacc, s0, head, c0 + cw * NCOL, lane);
-        bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0;
+        const int cw = w - SLW;
+        floatx4 hacc[1][MT];
+        load_state<DK, DV, 1>(hacc, s0, head, c0 + cw * 16, lane);
+        // T fragments of chunk c (fragment order in the workspace)
+        auto load_tf = [&](int c, opx8 (&t)[6]) {
+            const opx8* src = reinterpret_cast<const opx8*>(wh + (size_t)c * WS_CHUNK + WS_T);
+#pragma unroll
+            for (int bk = 0; bk < 6; ++bk) t[bk] = src[bk * 64 + lane];
+        };
+        auto step = [&](int n, const opx8 (&tc)[6], opx8 (&tn)[6]) {
+            GDN_TRACE(n, 0);
+            if (n + 1 < NT) load_tf(n + 1, tn);
+            const unsigned char* sb = cslot(n);
+            const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
+            opx8 hb[1][KB], db[1][2], dtb[1][2];
+            opx8 akt[2][MT];
+            chain_delta<DK, 1, L::VP, true>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * 16,
+                                            [&](int mt, int cb) { return tc[tblk(mt, cb)]; },
+                                            reinterpret_cast<const float*>(sb + L::cv), lane, hb, db, dtb, akt);
+            opx8* hx = hxp(n, cw);
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) hx[kk * 64 + lane] = hb[0][kk];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) hx[(KB + cb) * 64 + lane] = db[0][cb];
+            GDN_TRACE(n, 1);
+            apply_kt<DK, 1>(hacc, akt[0], dtb, 0);
+            apply_kt<DK, 1>(hacc, akt[1], dtb, 1);
+            GDN_TRACE(n, 2);
+            lds_barrier();
+        };
+        opx8 tA[6], tB[6];
+        load_tf(0, tA);
+        lds_barrier();
+        int n = 0;
+        for (; n + 1 < NT; n += 2) {
+            step(n, tA, tB);
+            step(n + 1, tB, tA);
+        }
+        if (n < NT) step(n, tA, tB);
+        store_state<DK, DV, 1>(hacc, sf, head, c0 + cw * 16, lane);
+    } else {
+        // ================================================================= output waves
+        const int ow = w - SLW - NW;
+        bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0 + ow * 16;
+        const unsigned char* wqh = wsq + ((size_t)b * Hqk + i) * NT * ws_q_bytes<DK>();
+        // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc)
+        opx8 qf[KB][4];
+        opx8 af[6];
+        float egr[4];
+        auto load_in = [&](int c) {
+            const opx8* qs = reinterpret_cast<const opx8*>(wqh + (size_t)c * ws_q_bytes<DK>());
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) qf[kk][ct] = qs[(kk * 4 + ct) * 64 + lane];
+            const unsigned char* wc = wh + (size_t)c * WS_CHUNK;
+            const opx8* a = reinterpret_cast<const opx8*>(wc + WS_AQ);
+#pragma unroll
+            for (int bk = 0; bk < 6; ++bk) af[bk] = a[bk * 64 + lane];
+            const float* e = reinterpret_cast<const float*>(wc + WS_EG);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) egr[ct] = e[16 * ct + ln];
+        };
+        // O^T = (h^T Q^T) diag(scale exp(gc)) + Delta^T (scale Aqk)^T for chunk m (see chain_out)
+        auto out = [&](int m) {
+            const opx8* hx = hxp(m, ow);
+            opx8 hb[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) hb[kk] = hx[kk * 64 + lane];
+            opx8 db[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) db[cb] = hx[(KB + cb) * 64 + lane];
+            floatx4 OT[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) OT[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) OT[ct] = mfma32(hb[kk], qf[kk][ct], OT[ct]);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) OT[ct][x] *= egr[ct];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int ct = 2 * cb; ct < 4; ++ct) OT[ct] = mfma32(db[cb], af[tblk(ct, cb)], OT[ct]);
+            const int t0 = m * CH, nv = min(CH, T_len - t0);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const int tok = 16 * ct + ln;
+                if (tok < nv) {
+                    const bf16x4 ov = {(bf16)OT[ct][0], (bf16)OT[ct][1], (bf16)OT[ct][2], (bf16)OT[ct][3]};
+                    *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 4 * lg) = ov;
+                }
+            }
+        };
+        load_in(0);
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
             GDN_TRACE(n, 0);
-            const unsigned char* sb = cslot(n);
-            const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
-            const float* vs = reinterpret_cast<const float*>(sb + L::cv);
-            if constexpr (OW) {
-                opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
-                opx8 akt[2][MT];
-                chain_delta<DK, NTN, L::VP, NTN == 1>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * NCOL,
-                                                      reinterpret_cast<const op_t*>(sb + L::t), vs, lane, hb, db,
-                                                      dtb, akt);
-                opx8* hx = hxp(n, cw);
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) {
-#pragma unroll
-                    for (int kk = 0; kk < KB; ++kk) hx[(nt * (KB + 2) + kk) * 64 + lane] = hb[nt][kk];
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) hx[(nt * (KB + 2) + KB + cb) * 64 + lane] = db[nt][cb];
-                }
-                GDN_TRACE(n, 1);
-                if constexpr (NTN == 1) {
-                    apply_kt<DK, NTN>(hacc, akt[0], dtb, 0);
-                    apply_kt<DK, NTN>(hacc, akt[1], dtb, 1);
-                } else {
-                    chain_update<DK, NTN>(hacc, Ks, dtb, lane);
-                }
-                GDN_TRACE(n, 2);
-            } else {
-                const unsigned char* so = oslot(n);
-                const int t0 = n * CH;
-                opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
-                chain_delta<DK, NTN, L::VP>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * NCOL,
-                                            reinterpret_cast<const op_t*>(sb + L::t), vs, lane, hb, db, dtb);
-                __builtin_amdgcn_sched_barrier(0);
-                chain_out<DK, NTN>(hb, db, reinterpret_cast<const op_t*>(so + L::q),
-                                   reinterpret_cast<const op_t*>(so + L::a),
-                                   reinterpret_cast<const float*>(so + L::eg), ob + (size_t)t0 * v_row + cw * NCOL,
-                                   v_row, min(CH, T_len - t0), lane);
-                __builtin_amdgcn_sched_barrier(0);
-                chain_update<DK, NTN>(hacc, Ks, dtb, lane);
+            if (n >= 1) {
+                out(n - 1);
+                load_in(n);
             }
+            GDN_TRACE(n, 1);
             lds_barrier();
         }
-        store_state<DK, DV, NTN>(hacc, sf, head, c0 + cw * NCOL, lane);
-    } else {
-        // ================================================================= output waves
-        if constexpr (OW) {
-            const int ow = w - NLW - NW;
-            bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0 + ow * NCOL;
-            // O of chunk m from the hand-over of its chain wave and the staged Q, Aqk, exp(gc)
-            auto out = [&](int m) {
-                const unsigned char* so = oslot(m);
-                const opx8* hx = hxp(m, ow);
-                opx8 hb[NTN][KB], db[NTN][2];
-#pragma unroll
-                for (int nt = 0; nt < NTN; ++nt) {
-#pragma unroll
-                    for (int kk = 0; kk < KB; ++kk) hb[nt][kk] = hx[(nt * (KB + 2) + kk) * 64 + lane];
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) db[nt][cb] = hx[(nt * (KB + 2) + KB + cb) * 64 + lane];
-                }
-                const int t0 = m * CH;
-                chain_out<DK, NTN>(hb, db, reinterpret_cast<const op_t*>(so + L::q),
-                                   reinterpret_cast<const op_t*>(so + L::a),
-                                   reinterpret_cast<const float*>(so + L::eg), ob + (size_t)t0 * v_row, v_row,
-                                   min(CH, T_len - t0), lane);
-            };
-            lds_barrier();
-            for (int n = 0; n < NT; ++n) {
-                GDN_TRACE(n, 0);
-                if (n >= 1) out(n - 1);
-                GDN_TRACE(n, 1);
-                lds_barrier();
-            }
-            out(NT - 1);
-        }
+        out(NT - 1);
     }
 }
 
@@ -1427,17 +1438,15 @@ int choose_bv(const ChunkArgs& a)
     return chains >= 192 ? 128 : 64;
 }
 
-// Column-tile width of the state pass: the narrowest tile that keeps the workgroup count within
-// one per compute unit (each workgroup holds about 120-150 KB of LDS), so short-chain workloads
-// spread over the chip; wide tiles when the chains alone fill it.
+// Column-tile width of the state pass, 16 (one chain wave) or 32 (two): 16 while that still
+// gives at most one workgroup per compute unit, so short-chain workloads spread over the chip
+// (measured: two 16-column workgroups sharing a CU run slower than one 32-column one).
 int choose_split_bv(const ChunkArgs& a)
 {
     const int bv = env_int("GDN_SPLIT_BV", 0);
-    if ((bv == 16 || bv == 32 || bv == 64 || bv == 128) && a.dv % bv == 0) return bv;
+    if (bv == 16 || bv == 32) return bv;
     const long chains = (long)a.B * a.Hv;
-    for (int w = 16; w < a.dv; w *= 2)
-        if (chains * (a.dv / w) <= 256) return w;
-    return a.dv;
+    return chains * (a.dv / 16) <= 256 ? 16 : 32;
 }
 
 bool use_split(const ChunkArgs& a)
@@ -1468,22 +1477,23 @@ hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int DK, int DV, int NW, int NTN>
+template <int DK, int DV, int NW>
 hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
-    constexpr int BV = 16 * NW * NTN;
+    constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
-    constexpr int nthr = (NLW + (L::OW ? 2 : 1) * NW) * 64;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_state_kernel<DK, DV, NW, NTN>;
+    auto kern = chunk_state_kernel<DK, DV, NW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
     const long nblk = (long)a.B * a.Hv * (DV / BV);
     const long per_xcd = nblk / 8;
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(nthr), L::bytes, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, a.s0, a.sf,
+    const int NT = (a.T + CH - 1) / CH;
+    const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((SLW + 2 * NW) * 64), L::bytes, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0, a.sf,
                        (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap);
     return hipGetLastError();
 }
@@ -1494,20 +1504,14 @@ hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
     const int grp = a.Hv / a.Hqk;
     const int NT = (a.T + CH - 1) / CH;
     const long nprep = (long)a.B * a.Hqk * NT;
+    unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL(chunk_prep_kernel<DK>, dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
-                       (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, a.T, a.Hqk, a.Hv, grp, NT, a.scale);
+                       (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, wsq, a.T, a.Hqk, a.Hv, grp, NT,
+                       a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    switch (choose_split_bv(a)) {
-    case 16: return launch_state_t<DK, DV, 1, 1>(a, ws, st);
-    case 32:
-        if (env_int("GDN_SPLIT_NW", 2) == 1) return launch_state_t<DK, DV, 1, 2>(a, ws, st);
-        return launch_state_t<DK, DV, 2, 1>(a, ws, st);
-    case 64: return launch_state_t<DK, DV, 4, 1>(a, ws, st);
-    default:
-        if constexpr (DV >= 128) return launch_state_t<DK, DV, 4, 2>(a, ws, st);
-        return hipErrorInvalidValue;
-    }
+    if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1>(a, ws, st);
+    return launch_state_t<DK, DV, 2>(a, ws, st);
 }
 
 }  // namespace
@@ -1524,7 +1528,7 @@ size_t chunk_mfma_workspace_bytes(const ChunkArgs& a)
 {
     if (!chunk_mfma_split(a)) return 0;
     const size_t NT = ((size_t)a.T + CH - 1) / CH;
-    return (size_t)a.B * a.Hv * NT * WS_CHUNK;
+    return (size_t)a.B * NT * (a.Hv * (size_t)WS_CHUNK + a.Hqk * (size_t)CH * a.dk * 2);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, void* ws, hipStream_t st)

@@ -59,11 +59,12 @@ typedef enum {
 /*
  * gdn_chunk_fwd_workspace_bytes -- device scratch (bytes) that gdn_chunk_fwd needs for these
  * sizes; 0 when the path chosen for them needs none.  The split matrix-core path (few, long
- * sequences: see gdn_chunk_fwd_kernel_name) needs 13,568 bytes per (batch row, value head,
- * 64-token chunk) for the per-chunk T = (I + A)^{-1}, the masked Q K^T and the gate vectors it
- * builds before the state pass.  The result depends only on the arguments (and on the
- * GDN_MFMA_PATH / GDN_DISABLE_MFMA environment variables, which select the path).  Pure host
- * function; needs no device; 0 for invalid sizes.
+ * sequences: see gdn_chunk_fwd_kernel_name) needs, per 64-token chunk of each batch row,
+ * 13,568 bytes per value head (T = (I + A)^{-1}, the masked Q K^T and the gate vectors) plus
+ * 128 * dk bytes per query/key head (q as matrix-core operands), all built before the state
+ * pass.  The result depends only on the arguments (and on the GDN_MFMA_PATH / GDN_DISABLE_MFMA
+ * environment variables, which select the path).  Pure host function; needs no device; 0 for
+ * invalid sizes.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                      gdn_dtype_t dtype);

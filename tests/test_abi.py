@@ -34,9 +34,11 @@ def test_status_strings_and_queries():
     for s in range(9):
         assert gdn.gdn_status_string(s)
     assert gdn.gdn_status_string(1234) == "unknown status"
-    # split matrix-core path (few chains): 13,568 bytes per (batch row, value head, chunk)
-    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 32 * 64 * 13568
-    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4097, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 32 * 65 * 13568
+    # split matrix-core path (few chains): 13,568 bytes per (batch row, value head, chunk) plus
+    # 64 * dk * 2 bytes per (batch row, query/key head, chunk)
+    per_chunk = 32 * 13568 + 16 * 64 * 128 * 2
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 64 * per_chunk
+    assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4097, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 65 * per_chunk
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
     # fused path (many chains) and the float32 path need none
     assert gdn.gdn_chunk_fwd_workspace_bytes(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
@@ -137,7 +139,7 @@ def test_workspace_check_precedes_device():
 
 # the split matrix-core path (bf16, chunk 64, few chains) needs a workspace
 SPLIT = dict(dk=128, dv=128, chunk=64, T=100)
-SPLIT_WS = 2 * 4 * 2 * 13568
+SPLIT_WS = 2 * 2 * (4 * 13568 + 2 * 64 * 128 * 2)
 
 
 def test_split_workspace_size():

@@ -223,9 +223,9 @@ def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
     check(f"mfma bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
 
 
-@pytest.mark.parametrize("bv", ["16", "32", "64", "128"])
+@pytest.mark.parametrize("bv", ["16", "32"])
 @pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
-                                            (64, 64, 1, 1, 1), (128, 128, 700, 1, 1)])
+                                            (64, 64, 1, 1, 1), (128, 128, 700, 1, 1), (128, 128, 127, 1, 3)])
 def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
     """The split matrix-core path (per-chunk prep kernel into the workspace, then the state pass)
     at every column-tile width, with grouped heads, a ragged last chunk, a nonzero initial state
