@@ -1172,8 +1172,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
 }
 
 // Split path, kernel 2: the state pass.  One workgroup per (batch, value head, column tile of
-// BV = 16 NW columns) with SLW loader waves, NW chain waves (16 state columns each) and NW
-// output waves, one barrier per chunk.
+// BV = 16 NW columns) with SLW loader waves, NW chain waves (16 state columns each) and one
+// output wave, one barrier per chunk.
 // * Loaders stage chunk n + 1's K (q, k converted to column-permuted float16), V and state-step
 //   vectors into double-buffered LDS while the chain waves carry chunk n, and prefetch chunk
 //   n + 2 into registers.  That is all that goes through LDS besides the hand-over below: LDS
@@ -1181,9 +1181,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
 // * A chain wave reads T straight from the workspace in fragment order (16-byte coalesced loads,
 //   one chunk ahead, double-buffered in registers over a two-chunk loop), runs the Delta and
 //   update phases, and hands its packed h and Delta to its output wave through LDS.
-// * An output wave forms O of chunk n - 1 in iteration n from that hand-over and Q, Aqk and
-//   scale exp(gc) read from the workspace in fragment order.  Its inputs for the next chunk load
-//   once it is done with the current one.
+// * The output wave forms O of chunk n - 1 for every column group in iteration n from those
+//   hand-overs and Q, Aqk and scale exp(gc) read from the workspace in fragment order (one copy
+//   for the whole tile: vector-memory issue per compute unit is a limit here), double-buffered
+//   two chunks ahead.
 constexpr int SLW = 2;   // loader waves of the state pass
 
 template <int DK, int BV, int NW>
@@ -1202,7 +1203,7 @@ struct SLds {
 };
 
 template <int DK, int DV, int NW>
-__global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
+__global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const unsigned char* __restrict__ ws, const unsigned char* __restrict__ wsq, const float* s0,
     float* sf, bf16* __restrict__ o, int T_len, int Hqk, int Hv, int grp, int xcd_remap)
@@ -1229,6 +1230,12 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
     const int lane = tid & 63;
     const int ln = lane & 15;
     const int lg = lane >> 4;
+    // Roles by wave index, so that consecutive waves (which land on consecutive SIMDs) give each
+    // chain wave and the output wave a SIMD of its own and the two loaders share one: wave 0
+    // and wave NW + 2 load, waves 1..NW carry the chains, wave NW + 1 forms O.
+    const int li = w == 0 ? 0 : w - (NW + 1);   // loader index (loader waves only)
+    const bool is_loader = w == 0 || w == NW + 2;
+    const bool is_chain = w >= 1 && w <= NW;
     const int NT = (T_len + CH - 1) / CH;
     const int qk_row = Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
@@ -1239,8 +1246,9 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
     };
 
-    if (w < SLW) {
+    if (is_loader) {
         // ================================================================= loader waves
+        const int ltid = li * 64 + lane;   // loader thread index
         const bf16* kb_ = k + ((size_t)b * T_len * Hqk + i) * DK;
         const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
         const int vrow = Hv * DV;
@@ -1256,7 +1264,7 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
         int kq_r[PK], kq_c[PK];
 #pragma unroll
         for (int p = 0; p < PK; ++p) {
-            const int s = tid + p * NLT, pr = s % RP;
+            const int s = ltid + p * NLT, pr = s % RP;
             kq_r[p] = s / RP;
             kq_c[p] = 32 * (pr >> 1) + 8 * (pr & 1);
         }
@@ -1272,10 +1280,10 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
             const bf16* vc = vb + (size_t)t0 * vrow;
 #pragma unroll
             for (int p = 0; p < PV; ++p) {
-                const int s = min(tid + p * NLT, CH * RV - 1);
+                const int s = min(ltid + p * NLT, CH * RV - 1);
                 rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
             }
-            if (tid < CVR) rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * tid);
+            if (ltid < CVR) rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * ltid);
         };
         auto stage_chain = [&](int c) {
             unsigned char* sb = cslot(c);
@@ -1283,31 +1291,34 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
             bf16* Vs = reinterpret_cast<bf16*>(sb + L::v);
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
-                opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((tid + p * NLT) % RP));
+                opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((ltid + p * NLT) % RP));
                 bf16_pair_to_op(rk[p][0], rk[p][1], dst[0], dst[1]);
             }
 #pragma unroll
             for (int p = 0; p < PV; ++p) {
-                const int s = tid + p * NLT;
+                const int s = ltid + p * NLT;
                 if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
             }
-            if (tid < CVR) *reinterpret_cast<floatx4*>(sb + L::cv + 16 * tid) = rc;
+            if (ltid < CVR) *reinterpret_cast<floatx4*>(sb + L::cv + 16 * ltid) = rc;
         };
+        // Prefetches are issued unconditionally (chunk index clamped to the last chunk; the
+        // extra loads at the end are harmless) so that every path through the loop has the same
+        // memory operations in flight and each wait covers exactly the loads it needs.
         load_chain(0);
         stage_chain(0);
-        if (NT > 1) load_chain(1);
+        load_chain(min(1, NT - 1));
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
             GDN_TRACE(n, 0);
             if (n + 1 < NT) stage_chain(n + 1);
             GDN_TRACE(n, 1);
-            if (n + 2 < NT) load_chain(n + 2);
+            load_chain(min(n + 2, NT - 1));
             GDN_TRACE(n, 2);
             lds_barrier();
         }
-    } else if (w < SLW + NW) {
+    } else if (is_chain) {
         // ================================================================= chain waves
-        const int cw = w - SLW;
+        const int cw = w - 1;
         floatx4 hacc[1][MT];
         load_state<DK, DV, 1>(hacc, s0, head, c0 + cw * 16, lane);
         // T fragments of chunk c (fragment order in the workspace)
@@ -1318,7 +1329,7 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
         };
         auto step = [&](int n, const opx8 (&tc)[6], opx8 (&tn)[6]) {
             GDN_TRACE(n, 0);
-            if (n + 1 < NT) load_tf(n + 1, tn);
+            load_tf(min(n + 1, NT - 1), tn);   // unconditional: see the loaders
             const unsigned char* sb = cslot(n);
             const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
             opx8 hb[1][KB], db[1][2], dtb[1][2];
@@ -1348,30 +1359,35 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
         if (n < NT) step(n, tA, tB);
         store_state<DK, DV, 1>(hacc, sf, head, c0 + cw * 16, lane);
     } else {
-        // ================================================================= output waves
-        const int ow = w - SLW - NW;
-        bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0 + ow * 16;
+        // ================================================================= output wave
+        bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0;
         const unsigned char* wqh = wsq + ((size_t)b * Hqk + i) * NT * ws_q_bytes<DK>();
-        // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc)
-        opx8 qf[KB][4];
-        opx8 af[6];
-        float egr[4];
-        auto load_in = [&](int c) {
+        // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc);
+        // double-buffered, loaded two chunks ahead of their use
+        struct OutIn {
+            opx8 qf[KB][4];
+            opx8 af[6];
+            float eg[4];
+        };
+        auto load_in = [&](int c, OutIn& in) {
             const opx8* qs = reinterpret_cast<const opx8*>(wqh + (size_t)c * ws_q_bytes<DK>());
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) qf[kk][ct] = qs[(kk * 4 + ct) * 64 + lane];
+                for (int ct = 0; ct < 4; ++ct) in.qf[kk][ct] = qs[(kk * 4 + ct) * 64 + lane];
             const unsigned char* wc = wh + (size_t)c * WS_CHUNK;
             const opx8* a = reinterpret_cast<const opx8*>(wc + WS_AQ);
 #pragma unroll
-            for (int bk = 0; bk < 6; ++bk) af[bk] = a[bk * 64 + lane];
+            for (int bk = 0; bk < 6; ++bk) in.af[bk] = a[bk * 64 + lane];
             const float* e = reinterpret_cast<const float*>(wc + WS_EG);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) egr[ct] = e[16 * ct + ln];
+            for (int ct = 0; ct < 4; ++ct) in.eg[ct] = e[16 * ct + ln];
         };
-        // O^T = (h^T Q^T) diag(scale exp(gc)) + Delta^T (scale Aqk)^T for chunk m (see chain_out)
-        auto out = [&](int m) {
+        // O^T = (h^T Q^T) diag(scale exp(gc)) + Delta^T (scale Aqk)^T for chunk m (see
+        // chain_out), column group by column group
+        auto out = [&](int m, const OutIn& in) {
+#pragma unroll
+            for (int ow = 0; ow < NW; ++ow) {
             const opx8* hx = hxp(m, ow);
             opx8 hb[KB];
 #pragma unroll
@@ -1385,37 +1401,51 @@ __global__ __launch_bounds__((SLW + 2 * NW) * 64) __attribute__((amdgpu_waves_pe
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) OT[ct] = mfma32(hb[kk], qf[kk][ct], OT[ct]);
+                for (int ct = 0; ct < 4; ++ct) OT[ct] = mfma32(hb[kk], in.qf[kk][ct], OT[ct]);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) OT[ct][x] *= egr[ct];
+                for (int x = 0; x < 4; ++x) OT[ct][x] *= in.eg[ct];
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                for (int ct = 2 * cb; ct < 4; ++ct) OT[ct] = mfma32(db[cb], af[tblk(ct, cb)], OT[ct]);
+                for (int ct = 2 * cb; ct < 4; ++ct) OT[ct] = mfma32(db[cb], in.af[tblk(ct, cb)], OT[ct]);
             const int t0 = m * CH, nv = min(CH, T_len - t0);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const int tok = 16 * ct + ln;
                 if (tok < nv) {
                     const bf16x4 ov = {(bf16)OT[ct][0], (bf16)OT[ct][1], (bf16)OT[ct][2], (bf16)OT[ct][3]};
-                    *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 4 * lg) = ov;
+                    *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 16 * ow + 4 * lg) = ov;
                 }
             }
+            }
         };
-        load_in(0);
-        lds_barrier();
-        for (int n = 0; n < NT; ++n) {
+        // iteration n forms O of chunk n - 1 from buffer (n - 1) % 2, then loads chunk n + 1 into it
+        auto step = [&](int n, OutIn& cur) {
             GDN_TRACE(n, 0);
             if (n >= 1) {
-                out(n - 1);
-                load_in(n);
+                out(n - 1, cur);
+                GDN_TRACE(n, 1);
+                load_in(min(n + 1, NT - 1), cur);   // unconditional: see the loaders
             }
-            GDN_TRACE(n, 1);
+            GDN_TRACE(n, 2);
             lds_barrier();
+        };
+        OutIn bufA, bufB;
+        load_in(0, bufA);
+        load_in(min(1, NT - 1), bufB);
+        lds_barrier();
+        int n = 0;
+        for (; n + 1 < NT; n += 2) {
+            step(n, bufB);       // n even: O of chunk n - 1 (odd) is in bufB
+            step(n + 1, bufA);   // O of chunk n (even) is in bufA
         }
-        out(NT - 1);
+        if (n < NT) step(n, bufB);
+        if ((NT - 1) % 2 == 0)
+            out(NT - 1, bufA);
+        else
+            out(NT - 1, bufB);
     }
 }
 
@@ -1492,7 +1522,7 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
     const int NT = (a.T + CH - 1) / CH;
     const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((SLW + 2 * NW) * 64), L::bytes, st, (const bf16*)a.q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((SLW + NW + 1) * 64), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0, a.sf,
                        (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap);
     return hipGetLastError();
