@@ -15,7 +15,9 @@ The same JSON line carries
   decode        -- the 64-step fused decode workload (B=256, Hv=32, d=128, fp32 state 512 MiB):
                    steps/s and achieved HBM bandwidth;
   prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3.6-27B-shaped (T=65536, Hv=48)
-                   prefill workloads, tokens/s and roofline fractions.
+                   prefill workloads, tokens/s and roofline fractions;
+  layer_ops     -- the layer steps either side of the recurrence at the headline shape (short
+                   conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
 """
@@ -170,6 +172,54 @@ def bench_decode(cfg, torch, gdn, gi, repeats=3):
     return dict(wall64=best, kern=kern, bytes=per_step)
 
 
+def bench_layer_ops(cfg, torch, gdn, W=4, steps=20, warmup=3, min_bytes=640 << 20):
+    """The layer steps either side of the recurrence at the workload's shape: the q/k/v prologue
+    (short conv width W, SiLU, q/k L2 norm, conv state in and out) and the gated RMSNorm of the
+    output.  Both are memory-bound: algorithmic bytes = each input read once + each output written
+    once; rotating input sets larger than the Infinity Cache keep the reads cold."""
+    dev = "cuda:0"
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    es = 2 if cfg.dtype == "bf16" else 4
+    B, T, Hqk, Hv, dk, dv = cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv
+    C = 2 * Hqk * dk + Hv * dv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 17)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    wq, wk, wv = rnd(Hqk * dk, W) / W ** 0.5, rnd(Hqk * dk, W) / W ** 0.5, rnd(Hv * dv, W) / W ** 0.5
+    pro_bytes = 2 * B * T * C * es + C * W * 4 + 2 * B * C * (W - 1) * 4
+    n_sets = max(1, min(8, -(-min_bytes // pro_bytes)))
+    sets = [dict(q=rnd(B, T, Hqk, dk).to(dt), k=rnd(B, T, Hqk, dk).to(dt), v=rnd(B, T, Hv, dv).to(dt),
+                 st=rnd(B, C, W - 1), so=torch.empty(B, C, W - 1, device=dev),
+                 oq=torch.empty(B, T, Hqk, dk, dtype=dt, device=dev), ok=torch.empty(B, T, Hqk, dk, dtype=dt, device=dev),
+                 ov=torch.empty(B, T, Hv, dv, dtype=dt, device=dev)) for _ in range(n_sets)]
+
+    def pro(i):
+        x = sets[i]
+        gdn.gdn_qkv_prologue(x["q"], x["k"], x["v"], wq, wk, wv, x["st"], conv_state_out=x["so"],
+                             q=x["oq"], k=x["ok"], v=x["ov"])
+
+    _, kp = time_launches(pro, n_sets, steps, warmup, torch)
+    del sets
+    rms_bytes = 3 * B * T * Hv * dv * es + dv * 4
+    n_sets = max(1, min(8, -(-min_bytes // rms_bytes)))
+    w = 1.0 + 0.1 * rnd(dv)
+    sets = [dict(o=rnd(B, T, Hv, dv).to(dt), z=rnd(B, T, Hv, dv).to(dt), y=torch.empty(B, T, Hv, dv, dtype=dt, device=dev))
+            for _ in range(n_sets)]
+
+    def rms(i):
+        x = sets[i]
+        gdn.gdn_gated_rmsnorm(x["o"], x["z"], w, y=x["y"])
+
+    _, kr = time_launches(rms, n_sets, steps, warmup, torch)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "conv_width": W,
+            "qkv_prologue": {"kernel_us": kp * 1e6, "alg_bytes": pro_bytes, "hbm_GBps": pro_bytes / kp / 1e9,
+                             "hbm_frac": pro_bytes / kp / HBM_PEAK},
+            "gated_rmsnorm": {"kernel_us": kr * 1e6, "alg_bytes": rms_bytes, "hbm_GBps": rms_bytes / kr / 1e9,
+                              "hbm_frac": rms_bytes / kr / HBM_PEAK}}
+
+
 def cpu_baseline(cfg, gi, min_seconds=10.0, max_repeats=30):
     """The float64 oracle on the same workload (whole batch), repeated until about min_seconds."""
     import numpy as np
@@ -273,6 +323,8 @@ def main():
                         "mfma_frac": rr["flops"] / rr["kern"] / MFMA_BF16_PEAK,
                         "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
         line["prefill_configs"] = pc
+        print("bench: layer steps (prologue, gated RMSNorm)", file=sys.stderr, flush=True)
+        line["layer_ops"] = bench_layer_ops(cfg, torch, gdn)
     print(json.dumps(line), flush=True)
 
 

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/gdn.h):
 
 * :func:`gdn_chunk_fwd` -- prefill, chunkwise, optional initial / final state.
 * :func:`gdn_recurrent_step` -- decode, one token per sequence, state updated in place.
+* :func:`gdn_qkv_prologue` -- short causal conv, SiLU and q/k L2 norm after the projections.
+* :func:`gdn_gated_rmsnorm` -- RMSNorm of the output times SiLU of the gate.
 * :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_kernel_name`,
   :func:`gdn_status_string`.
 """
@@ -20,13 +22,14 @@ import os
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "library_path", "load_library", "gdn_chunk_fwd",
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
-    "gdn_status_string", "EXPORTED_SYMBOLS",
+    "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
 GDN_BF16 = 1
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
-                    "gdn_chunk_fwd_kernel_name", "gdn_status_string")
+                    "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
+                    "gdn_gated_rmsnorm")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -63,6 +66,10 @@ def load_library():
     lib.gdn_chunk_fwd_kernel_name.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [i]
     lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_qkv_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp] + [i] * 7 + [i, f, vp]
+    lib.gdn_qkv_prologue.restype = i
+    lib.gdn_gated_rmsnorm.argtypes = [vp, vp, fp, i, vp, i, i, i, i, i, f, vp]
+    lib.gdn_gated_rmsnorm.restype = i
     _lib = lib
     return lib
 
@@ -176,3 +183,62 @@ def gdn_recurrent_step(q, k, v, g, beta, state, scale=1.0, o=None, stream=None):
     if st != 0:
         raise GdnError(st, "gdn_recurrent_step")
     return o
+
+
+def gdn_qkv_prologue(q_in, k_in, v_in, conv_q, conv_k, conv_v, conv_state_in=None,
+                     output_conv_state=False, eps=1e-6, q=None, k=None, v=None, conv_state_out=None,
+                     stream=None):
+    """Short causal conv, SiLU and q/k L2 norm.  q_in, k_in [B,T,Hqk,dk]; v_in [B,T,Hv,dv] (bf16
+    or f32, all alike); conv_q, conv_k [Hqk*dk, W], conv_v [Hv*dv, W] float32; conv_state_in
+    [B, 2*Hqk*dk + Hv*dv, W-1] float32 or None.  Returns (q, k, v, conv_state_out or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q_in.shape
+    Hv, dv = v_in.shape[2], v_in.shape[3]
+    W = conv_q.shape[1]
+    dev = q_in.device
+    _check_dense("q_in", q_in, (B, T, Hqk, dk), q_in.dtype, dev)
+    _check_dense("k_in", k_in, (B, T, Hqk, dk), q_in.dtype, dev)
+    _check_dense("v_in", v_in, (B, T, Hv, dv), q_in.dtype, dev)
+    _check_dense("conv_q", conv_q, (Hqk * dk, W), torch.float32, dev)
+    _check_dense("conv_k", conv_k, (Hqk * dk, W), torch.float32, dev)
+    _check_dense("conv_v", conv_v, (Hv * dv, W), torch.float32, dev)
+    cs = (B, 2 * Hqk * dk + Hv * dv, W - 1)
+    if conv_state_in is not None:
+        _check_dense("conv_state_in", conv_state_in, cs, torch.float32, dev)
+    if conv_state_out is None and output_conv_state:
+        conv_state_out = torch.empty(cs, dtype=torch.float32, device=dev)
+    if conv_state_out is not None:
+        _check_dense("conv_state_out", conv_state_out, cs, torch.float32, dev)
+    q = torch.empty_like(q_in) if q is None else q
+    k = torch.empty_like(k_in) if k is None else k
+    v = torch.empty_like(v_in) if v is None else v
+    _check_dense("q", q, (B, T, Hqk, dk), q_in.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q_in.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q_in.dtype, dev)
+    st = lib.gdn_qkv_prologue(_ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v),
+                              _ptr(conv_state_in), _ptr(conv_state_out), _ptr(q), _ptr(k), _ptr(v), B, T, Hqk,
+                              Hv, dk, dv, W, _dtype_code(q_in), float(eps), _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_qkv_prologue")
+    return q, k, v, conv_state_out
+
+
+def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, y=None, stream=None):
+    """y = RMSNorm(o) * weight * silu(z) per value head.  o, z [B,T,Hv,dv] (bf16 or f32);
+    weight [dv] (shared by the heads) or [Hv, dv] float32.  ``y`` may be ``o`` or ``z``."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hv, dv = o.shape
+    dev = o.device
+    _check_dense("o", o, (B, T, Hv, dv), o.dtype, dev)
+    _check_dense("z", z, (B, T, Hv, dv), o.dtype, dev)
+    per_head = 1 if weight.dim() == 2 else 0
+    _check_dense("weight", weight, (Hv, dv) if per_head else (dv,), torch.float32, dev)
+    y = torch.empty_like(o) if y is None else y
+    _check_dense("y", y, (B, T, Hv, dv), o.dtype, dev)
+    st = lib.gdn_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(weight), per_head, _ptr(y), B, T, Hv, dv,
+                               _dtype_code(o), float(eps), _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_gated_rmsnorm")
+    return y

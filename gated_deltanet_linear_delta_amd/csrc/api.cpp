@@ -178,4 +178,78 @@ gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, con
     return gdn::launch_recurrent_step(a, (hipStream_t)stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+gdn_status_t gdn_qkv_prologue(const void* q_in, const void* k_in, const void* v_in, const float* conv_q,
+                              const float* conv_k, const float* conv_v, const float* conv_state_in,
+                              float* conv_state_out, void* q, void* k, void* v, int B, int T, int Hqk, int Hv,
+                              int dk, int dv, int width, gdn_dtype_t dtype, float eps, void* stream)
+{
+    if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || width <= 0) return GDN_ERR_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || width > 4 || !dtype_ok(dtype) || !(eps >= 0.f))
+        return GDN_ERR_UNSUPPORTED;
+    const bool work = T > 0;
+    const bool state_out = conv_state_out && width > 1;
+    if (B == 0 || (!work && !state_out)) return GDN_OK;
+    if (work && (!q_in || !k_in || !v_in || !conv_q || !conv_k || !conv_v || !q || !k || !v)) return GDN_ERR_NULL;
+    const void* tens[] = {q_in, k_in, v_in, q, k, v};
+    for (const void* p : tens)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const void* f4[] = {conv_q, conv_k, conv_v, conv_state_in, conv_state_out};
+    for (const void* p : f4)
+        if (p && !aligned4(p)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = (size_t)B * T;
+    const size_t cq = (size_t)Hqk * dk, cv = (size_t)Hv * dv;
+    const size_t sbytes = (size_t)B * (2 * cq + cv) * (width - 1) * sizeof(float);
+    const Range ins[] = {range(q_in, work ? ntok * cq * es : 0), range(k_in, work ? ntok * cq * es : 0),
+                         range(v_in, work ? ntok * cv * es : 0), range(conv_q, work ? cq * width * 4 : 0),
+                         range(conv_k, work ? cq * width * 4 : 0), range(conv_v, work ? cv * width * 4 : 0),
+                         range(conv_state_in, conv_state_in ? sbytes : 0)};
+    const Range outs[] = {range(q, work ? ntok * cq * es : 0), range(k, work ? ntok * cq * es : 0),
+                          range(v, work ? ntok * cv * es : 0), range(conv_state_out, state_out ? sbytes : 0)};
+    for (const Range& o : outs) {
+        for (const Range& r : ins)
+            if (overlap(o, r)) return GDN_ERR_ALIAS;
+        for (const Range& o2 : outs)
+            if (&o2 != &o && overlap(o, o2)) return GDN_ERR_ALIAS;
+    }
+    gdn_status_t s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work)
+        return gdn::launch_state_copy(conv_state_in, conv_state_out, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    gdn::PrologueArgs a;
+    a.q_in = q_in; a.k_in = k_in; a.v_in = v_in; a.wq = conv_q; a.wk = conv_k; a.wv = conv_v;
+    a.st_in = width > 1 ? conv_state_in : nullptr;
+    a.st_out = state_out ? conv_state_out : nullptr;
+    a.q = q; a.k = k; a.v = v;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.W = width;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.eps = eps;
+    return gdn::launch_qkv_prologue(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* weight, int weight_per_head, void* y,
+                               int B, int T, int Hv, int dv, gdn_dtype_t dtype, float eps, void* stream)
+{
+    if (B < 0 || T < 0 || Hv <= 0 || dv <= 0 || (weight_per_head != 0 && weight_per_head != 1)) return GDN_ERR_SHAPE;
+    if (!head_dim_ok(dv) || !dtype_ok(dtype) || !(eps >= 0.f)) return GDN_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0) return GDN_OK;
+    if (!o || !z || !weight || !y) return GDN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(z) || !aligned16(y) || !aligned4(weight)) return GDN_ERR_ALIGN;
+    const size_t bytes = (size_t)B * T * Hv * dv * dtype_bytes(dtype);
+    const Range ro = range(o, bytes), rz = range(z, bytes), ry = range(y, bytes);
+    const Range rw = range(weight, (weight_per_head ? (size_t)Hv : 1) * dv * sizeof(float));
+    // y may be o or z exactly (each element is read before it is written, by the same lane)
+    if ((overlap(ry, ro) && y != o) || (overlap(ry, rz) && y != z) || overlap(ry, rw)) return GDN_ERR_ALIAS;
+    gdn_status_t s = device_ok();
+    if (s != GDN_OK) return s;
+    gdn::RmsNormArgs a;
+    a.o = o; a.z = z; a.w = weight; a.w_head_stride = weight_per_head ? dv : 0; a.y = y;
+    a.B = B; a.T = T; a.Hv = Hv; a.dv = dv;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.eps = eps;
+    return gdn::launch_gated_rmsnorm(a, (hipStream_t)stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 }  // extern "C"

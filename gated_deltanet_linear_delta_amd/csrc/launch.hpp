@@ -49,4 +49,36 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, void* workspace, hipStream_t st
 // final_state <- initial_state (or zeros when it is null), for T == 0.
 hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st);
 
+// Layer steps around the recurrence (layer_ops.hip).
+struct PrologueArgs {
+    const void* q_in;
+    const void* k_in;
+    const void* v_in;
+    const float* wq;       // [Hqk*dk, W]
+    const float* wk;       // [Hqk*dk, W]
+    const float* wv;       // [Hv*dv, W]
+    const float* st_in;    // [B, 2*Hqk*dk + Hv*dv, W-1] or null (zeros)
+    float* st_out;         // same shape or null
+    void* q;
+    void* k;
+    void* v;
+    int B, T, Hqk, Hv, dk, dv, W;
+    bool dtype_bf16;
+    float eps;
+};
+
+struct RmsNormArgs {
+    const void* o;
+    const void* z;
+    const float* w;        // [dv] shared by the heads (w_head_stride 0) or [Hv, dv] (stride dv)
+    int w_head_stride;
+    void* y;
+    int B, T, Hv, dv;
+    bool dtype_bf16;
+    float eps;
+};
+
+hipError_t launch_qkv_prologue(const PrologueArgs& a, hipStream_t st);
+hipError_t launch_gated_rmsnorm(const RmsNormArgs& a, hipStream_t st);
+
 }  // namespace gdn

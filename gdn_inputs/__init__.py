@@ -18,6 +18,12 @@ section "The architecture hidden inside Qwen"):
   patterns (numpy has no bfloat16).
 
 Draw order from numpy.random.Generator(PCG64(seed)): q, k, v, beta-logits, alpha-logits, S0.
+
+The layer steps either side of the recurrence (:func:`generate_layer`) take the projections'
+outputs before the short convolution: q_in, k_in, v_in ~ N(0, 1); conv taps ~ N(0, 1) / sqrt(W)
+float32 [channels, W]; an optional conv state ~ N(0, 1) float32 [B, channels, W - 1]; the
+recurrence output o ~ N(0, 0.25) and the gate projection z ~ N(0, 1); the RMSNorm weight
+1 + 0.1 N(0, 1) float32.  Draw order: q_in, k_in, v_in, conv_q, conv_k, conv_v, state, o, z, w.
 """
 from __future__ import annotations
 
@@ -26,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "bf16_bits", "bf16_bits_to_f32", "generate", "generate_decode",
-    "to_torch", "generate_torch",
+    "to_torch", "generate_torch", "generate_layer",
 ]
 
 
@@ -170,3 +176,24 @@ def generate_torch(cfg: Config, device, seed: int | None = None, decode_steps: i
         s0 = cfg.s0_std * nrm((cfg.B, cfg.Hv, cfg.dk, cfg.dv))
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), g=g.contiguous(),
                 beta=beta.contiguous(), s0=s0)
+
+
+def generate_layer(B, T, Hqk, Hv, dk, dv, W=4, dtype="bf16", seed=2001, state=True, w_per_head=False) -> dict:
+    """Inputs of the layer steps: q_in, k_in [B,T,Hqk,dk], v_in [B,T,Hv,dv] (dtype), conv_q,
+    conv_k [Hqk*dk, W], conv_v [Hv*dv, W] float32, conv_state [B, 2*Hqk*dk + Hv*dv, W-1] float32
+    or None; o, z [B,T,Hv,dv] (dtype); weight [dv] or [Hv, dv] float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = np.float32
+    q_in = rng.standard_normal((B, T, Hqk, dk), dtype=f)
+    k_in = rng.standard_normal((B, T, Hqk, dk), dtype=f)
+    v_in = rng.standard_normal((B, T, Hv, dv), dtype=f)
+    sc = f(1.0 / np.sqrt(W))
+    conv_q = (rng.standard_normal((Hqk * dk, W), dtype=f) * sc).astype(f)
+    conv_k = (rng.standard_normal((Hqk * dk, W), dtype=f) * sc).astype(f)
+    conv_v = (rng.standard_normal((Hv * dv, W), dtype=f) * sc).astype(f)
+    st = rng.standard_normal((B, 2 * Hqk * dk + Hv * dv, W - 1), dtype=f) if state else None
+    o = (rng.standard_normal((B, T, Hv, dv), dtype=f) * f(0.5)).astype(f)
+    z = rng.standard_normal((B, T, Hv, dv), dtype=f)
+    w = (1.0 + 0.1 * rng.standard_normal((Hv, dv) if w_per_head else (dv,))).astype(f)
+    return dict(q_in=_store(q_in, dtype), k_in=_store(k_in, dtype), v_in=_store(v_in, dtype), conv_q=conv_q,
+                conv_k=conv_k, conv_v=conv_v, conv_state=st, o=_store(o, dtype), z=_store(z, dtype), weight=w)

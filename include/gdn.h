@@ -136,6 +136,54 @@ const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int
 /* gdn_status_string -- static, human-readable text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t status);
 
+/*
+ * gdn_qkv_prologue -- the steps between the q, k, v projections and the recurrence, in one
+ * launch: a short causal depthwise convolution over time, SiLU, and for q and k an L2
+ * normalisation over each head's channels ("Architecture Thread I: Gated Attention, DeltaNet,
+ * and Hybrid Models", section "Modern Architecture Improvements": query/key take Linear ->
+ * Short Conv -> SiLU -> L2 Norm, value Linear -> Short Conv -> SiLU).  Per channel c of token t:
+ *     a = sum_{j=0}^{W-1} w[c][j] x[t - (W-1) + j]        (x before token 0: the conv state)
+ *     y = silu(a) = a / (1 + exp(-a));   q, k:  y <- y / sqrt(sum over the head's channels y^2 + eps)
+ *
+ *   q_in, k_in [B, T, Hqk, dk] dtype     v_in [B, T, Hv, dv] dtype   (the projections' outputs)
+ *   conv_q, conv_k [Hqk*dk, W] float32   conv_v [Hv*dv, W] float32   (channel-major taps, tap
+ *                                         W-1 multiplies the current token; no bias)
+ *   conv_state_in  [B, 2*Hqk*dk + Hv*dv, W-1] float32 or NULL (zeros): per channel (q's, then
+ *                  k's, then v's) the W-1 inputs before token 0, oldest first
+ *   conv_state_out same shape or NULL: the last W-1 inputs (of this call, after the state), for
+ *                  a continuation; may not overlap conv_state_in (use two buffers in turn)
+ *   q, k, v        outputs, shapes and dtype of the inputs; may not overlap any input or each
+ *                  other
+ *   W = width, 1..4.  dk, dv 32, 64 or 128.  eps >= 0.
+ * All pointers are caller-owned device memory; tensors 16-byte aligned, float arrays 4-byte.
+ * B == 0 is a no-op; T == 0 only writes conv_state_out (= conv_state_in, or zeros).
+ * Errors as gdn_chunk_fwd (nothing is enqueued on an error).
+ */
+gdn_status_t gdn_qkv_prologue(const void* q_in, const void* k_in, const void* v_in, const float* conv_q,
+                              const float* conv_k, const float* conv_v, const float* conv_state_in,
+                              float* conv_state_out, void* q, void* k, void* v, int B, int T, int Hqk,
+                              int Hv, int dk, int dv, int width, gdn_dtype_t dtype, float eps,
+                              void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- the step after the recurrence: RMSNorm over each value head's channels
+ * ("Architecture Thread I", section "Modern Architecture Improvements", output normalisation),
+ * times SiLU of the gate projection z (the gated RMSNorm of "The Transformer Isn't Alone
+ * Anymore", Qwen3-Next reconstruction; the output gate of the Gated DeltaNet block in "Gated
+ * Attention Architectures"):
+ *     y = o / sqrt(mean over the head's dv channels of o^2 + eps) * w * silu(z)
+ *
+ *   o, z   [B, T, Hv, dv] dtype        y  [B, T, Hv, dv] dtype, may be o or z itself (in place)
+ *          but may not overlap them otherwise, nor the weight
+ *   weight [dv] float32 shared by the heads (weight_per_head 0) or [Hv, dv] (1).  A
+ *          zero-centred weight (stored as 1 + delta) is passed as its value 1 + delta.
+ *   dv 32, 64 or 128.  eps >= 0.
+ * B == 0 or T == 0 is a no-op.  Errors as gdn_chunk_fwd.
+ */
+gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* weight, int weight_per_head,
+                               void* y, int B, int T, int Hv, int dv, gdn_dtype_t dtype, float eps,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

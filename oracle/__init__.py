@@ -10,6 +10,8 @@ may import this package.  Nothing here is shared with the HIP library, and nothi
   (numpy), for tiny inputs; an independent code path used to pin :func:`recurrent`.
 * :func:`chunked` -- the chunkwise (WY / UT-transform) refactoring of the same recurrence in
   numpy float64, used to pin the chunk algebra the GPU implements.
+* :func:`qkv_prologue`, :func:`gated_rmsnorm` (module ``layer_ops``) -- the layer steps either
+  side of the recurrence: short causal conv, SiLU and q/k L2 norm; gated RMSNorm of the output.
 
 Citations name the page and the section/equation followed.
 """
@@ -22,7 +24,10 @@ import numpy as np
 
 from . import build as _build
 
-__all__ = ["recurrent", "decode", "brute_force", "chunked", "max_threads", "load"]
+from .layer_ops import gated_rmsnorm, qkv_prologue, silu
+
+__all__ = ["recurrent", "decode", "brute_force", "chunked", "max_threads", "load", "qkv_prologue",
+           "gated_rmsnorm", "silu"]
 
 _lib = None
 

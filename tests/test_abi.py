@@ -161,3 +161,72 @@ def test_split_workspace_rejects(over, status):
 @pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
 def test_split_valid_call_reports_no_device():
     assert chunk_call(**SPLIT, ws=fake(8), wsb=SPLIT_WS) == NODEV
+
+
+# ---------------------------------------------------------------- layer steps around the recurrence
+
+
+def prologue_call(**over):
+    lib = gdn.load_library()
+    a = dict(q_in=fake(0), k_in=fake(1), v_in=fake(2), wq=fake(3), wk=fake(4), wv=fake(5), si=fake(6),
+             so=fake(7), q=fake(8), k=fake(9), v=fake(10), B=2, T=70, Hqk=2, Hv=4, dk=128, dv=64, W=4,
+             dtype=gdn.GDN_BF16, eps=1e-6, stream=None)
+    a.update(over)
+    return lib.gdn_qkv_prologue(a["q_in"], a["k_in"], a["v_in"], a["wq"], a["wk"], a["wv"], a["si"], a["so"],
+                                a["q"], a["k"], a["v"], a["B"], a["T"], a["Hqk"], a["Hv"], a["dk"], a["dv"],
+                                a["W"], a["dtype"], a["eps"], a["stream"])
+
+
+def rmsnorm_call(**over):
+    lib = gdn.load_library()
+    a = dict(o=fake(0), z=fake(1), w=fake(2), per_head=0, y=fake(3), B=2, T=70, Hv=4, dv=128,
+             dtype=gdn.GDN_BF16, eps=1e-6, stream=None)
+    a.update(over)
+    return lib.gdn_gated_rmsnorm(a["o"], a["z"], a["w"], a["per_head"], a["y"], a["B"], a["T"], a["Hv"],
+                                 a["dv"], a["dtype"], a["eps"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q_in=None), NULL), (dict(wv=None), NULL), (dict(k=None), NULL),
+    (dict(B=-1), SHAPE), (dict(T=-1), SHAPE), (dict(W=0), SHAPE), (dict(Hv=0), SHAPE),
+    (dict(W=5), UNSUP), (dict(dk=48), UNSUP), (dict(dv=256), UNSUP), (dict(dtype=3), UNSUP),
+    (dict(eps=-1.0), UNSUP), (dict(eps=float("nan")), UNSUP),
+    (dict(q=ctypes.c_void_p(BASE + 8 * STRIDE + 8)), ALIGN), (dict(wk=ctypes.c_void_p(BASE + 4 * STRIDE + 2)), ALIGN),
+    (dict(q=fake(0)), ALIAS), (dict(v=fake(5)), ALIAS), (dict(so=fake(6)), ALIAS),
+    (dict(k=ctypes.c_void_p(BASE + 8 * STRIDE + 4096)), ALIAS),   # k runs into q
+    (dict(so=fake(10)), ALIAS),
+])
+def test_qkv_prologue_rejects(over, status):
+    assert prologue_call(**over) == status
+
+
+def test_qkv_prologue_noops():
+    assert prologue_call(B=0, q_in=None, q=None) == OK
+    assert prologue_call(T=0, so=None, q_in=None, q=None) == OK       # nothing to write
+    assert prologue_call(T=0, W=1, q_in=None) == OK                   # a width-1 conv has no state
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(o=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL),
+    (dict(B=-1), SHAPE), (dict(per_head=2), SHAPE), (dict(Hv=0), SHAPE),
+    (dict(dv=96), UNSUP), (dict(dtype=9), UNSUP), (dict(eps=-0.5), UNSUP),
+    (dict(z=ctypes.c_void_p(BASE + STRIDE + 4)), ALIGN), (dict(w=ctypes.c_void_p(BASE + 2 * STRIDE + 1)), ALIGN),
+    (dict(y=ctypes.c_void_p(BASE + 256)), ALIAS), (dict(y=fake(2)), ALIAS),
+])
+def test_gated_rmsnorm_rejects(over, status):
+    assert rmsnorm_call(**over) == status
+
+
+def test_gated_rmsnorm_noops():
+    assert rmsnorm_call(T=0, o=None) == OK
+    assert rmsnorm_call(B=0, o=None) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_layer_steps_valid_calls_report_no_device():
+    assert prologue_call() == NODEV
+    assert prologue_call(si=None, so=None) == NODEV
+    assert prologue_call(T=0) == NODEV                                  # writes the state out
+    assert rmsnorm_call() == NODEV
+    assert rmsnorm_call(y=fake(0)) == NODEV                             # in place over o
+    assert rmsnorm_call(y=fake(1), per_head=1) == NODEV                 # in place over z

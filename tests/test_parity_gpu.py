@@ -269,3 +269,101 @@ def test_mfma_matches_simt(path, monkeypatch):
     assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "simt"
     o_s, s_s = run_prefill(d, 64)
     check("mfma-vs-simt", "bf16", o_m, o_s, s_m, s_s)
+
+
+# ---------------------------------------------------------------- layer steps around the recurrence
+
+def _close(name, x, ref, dtype):
+    """bf16 outputs: every element within 2^-8 of the oracle relative to its size (one bf16
+    rounding is at most 2^-9), plus 1e-5 of the largest; float32: 1e-5 relative plus 1e-6."""
+    rel, floor = (2.0 ** -8, 1e-5) if dtype == "bf16" else (1e-5, 1e-6)
+    err = np.abs(x - ref)
+    bound = rel * np.abs(ref) + floor * max(float(np.abs(ref).max()) if ref.size else 0.0, 1.0)
+    worst = float((err / bound).max()) if ref.size else 0.0
+    say(f"{name}: max err/bound {worst:.3f}")
+    assert worst <= 1.0, f"{name}: error exceeds the bound by {worst:.3f}x"
+
+
+def run_layer_prologue(d, state_in=True, want_state=True):
+    t = dev(d)
+    q, k, v, so = gdn.gdn_qkv_prologue(t["q_in"], t["k_in"], t["v_in"], t["conv_q"], t["conv_k"], t["conv_v"],
+                                       t["conv_state"] if state_in else None, output_conv_state=want_state)
+    torch.cuda.synchronize()
+    return host(q), host(k), host(v), (None if so is None else host(so))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,Hqk,Hv,dk,dv,W", [
+    (2, 70, 2, 4, 128, 128, 4), (1, 1, 1, 1, 64, 32, 4), (2, 2, 1, 2, 32, 64, 4), (1, 33, 2, 2, 128, 64, 3),
+    (3, 64, 1, 3, 64, 128, 2), (1, 96, 2, 4, 32, 32, 1), (2, 31, 4, 8, 128, 128, 4),
+])
+@pytest.mark.parametrize("state_in", [True, False])
+def test_qkv_prologue_small(dtype, B, T, Hqk, Hv, dk, dv, W, state_in):
+    say(f"prologue {dtype} B={B} T={T} Hqk={Hqk} Hv={Hv} dk={dk} dv={dv} W={W} state_in={state_in}")
+    d = gi.generate_layer(B, T, Hqk, Hv, dk, dv, W=W, dtype=dtype, seed=T * 13 + dk + W, state=True)
+    ref = oracle.qkv_prologue(f64(d["q_in"]), f64(d["k_in"]), f64(d["v_in"]), d["conv_q"], d["conv_k"], d["conv_v"],
+                              d["conv_state"] if state_in else None)
+    q, k, v, so = run_layer_prologue(d, state_in=state_in)
+    for nm, x, r in (("q", q, ref[0]), ("k", k, ref[1]), ("v", v, ref[2])):
+        _close(f"prologue {nm}", x, r, dtype)
+    if W > 1:
+        assert np.array_equal(so, ref[3]), "conv state out differs"
+
+
+def test_qkv_prologue_continuation():
+    """Two calls over the halves with the state carried give the one-call result exactly."""
+    d = gi.generate_layer(2, 100, 2, 4, 128, 64, W=4, dtype="bf16", seed=77)
+    t = dev(d)
+    full = gdn.gdn_qkv_prologue(t["q_in"], t["k_in"], t["v_in"], t["conv_q"], t["conv_k"], t["conv_v"],
+                                t["conv_state"], output_conv_state=True)
+    a = gdn.gdn_qkv_prologue(t["q_in"][:, :37].contiguous(), t["k_in"][:, :37].contiguous(),
+                             t["v_in"][:, :37].contiguous(), t["conv_q"], t["conv_k"], t["conv_v"],
+                             t["conv_state"], output_conv_state=True)
+    b = gdn.gdn_qkv_prologue(t["q_in"][:, 37:].contiguous(), t["k_in"][:, 37:].contiguous(),
+                             t["v_in"][:, 37:].contiguous(), t["conv_q"], t["conv_k"], t["conv_v"], a[3],
+                             output_conv_state=True)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(torch.cat([a[i], b[i]], dim=1), full[i])
+    assert torch.equal(b[3], full[3])
+
+
+def test_qkv_prologue_empty_sequence_copies_state():
+    d = gi.generate_layer(2, 0, 2, 4, 64, 64, W=4, dtype="bf16", seed=5)
+    t = dev(d)
+    *_, so = gdn.gdn_qkv_prologue(t["q_in"], t["k_in"], t["v_in"], t["conv_q"], t["conv_k"], t["conv_v"],
+                                  t["conv_state"], output_conv_state=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(so), d["conv_state"].astype(np.float64))
+
+
+def test_qkv_prologue_qwen3next_full():
+    """The prologue at the Qwen3-Next shape (T 4096, 16 q/k and 32 value heads of 128), width 4."""
+    c = gi.CONFIGS["qwen3next_prefill"]
+    say("prologue qwen3next full")
+    d = gi.generate_layer(c.B, c.T, c.Hqk, c.Hv, c.dk, c.dv, W=4, dtype="bf16", seed=2002)
+    ref = oracle.qkv_prologue(f64(d["q_in"]), f64(d["k_in"]), f64(d["v_in"]), d["conv_q"], d["conv_k"], d["conv_v"],
+                              d["conv_state"])
+    q, k, v, so = run_layer_prologue(d)
+    for nm, x, r in (("q", q, ref[0]), ("k", k, ref[1]), ("v", v, ref[2])):
+        _close(f"prologue qwen3next {nm}", x, r, "bf16")
+    assert np.array_equal(so, ref[3])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,Hv,dv", [(2, 70, 4, 128), (1, 1, 1, 32), (3, 33, 2, 64), (1, 4096, 32, 128)])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_gated_rmsnorm(dtype, B, T, Hv, dv, per_head):
+    say(f"gated rmsnorm {dtype} B={B} T={T} Hv={Hv} dv={dv} per_head={per_head}")
+    d = gi.generate_layer(B, T, 1, Hv, 32, dv, W=1, dtype=dtype, seed=T + dv + Hv, state=False, w_per_head=per_head)
+    ref = oracle.gated_rmsnorm(f64(d["o"]), f64(d["z"]), d["weight"])
+    t = dev(d)
+    y = gdn.gdn_gated_rmsnorm(t["o"], t["z"], t["weight"])
+    torch.cuda.synchronize()
+    _close("gated rmsnorm", host(y), ref, dtype)
+    # in place over o, then over z
+    o2, z2 = t["o"].clone(), t["z"].clone()
+    gdn.gdn_gated_rmsnorm(o2, t["z"], t["weight"], y=o2)
+    gdn.gdn_gated_rmsnorm(t["o"], z2, t["weight"], y=z2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, y) and torch.equal(z2, y)
