@@ -11,8 +11,9 @@ Entry points (same names as the C ABI in include/gdn.h):
 * :func:`gdn_recurrent_step` -- decode, one token per sequence, state updated in place.
 * :func:`gdn_qkv_prologue` -- short causal conv, SiLU and q/k L2 norm after the projections.
 * :func:`gdn_gated_rmsnorm` -- RMSNorm of the output times SiLU of the gate.
-* :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_kernel_name`,
-  :func:`gdn_status_string`.
+* :func:`gdn_chunk_fwd_gated` -- prefill followed by the gated RMSNorm (fused where it can be).
+* :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_gated_workspace_bytes`,
+  :func:`gdn_chunk_fwd_kernel_name`, :func:`gdn_status_string`.
 """
 from __future__ import annotations
 
@@ -22,14 +23,15 @@ import os
 __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "library_path", "load_library", "gdn_chunk_fwd",
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
-    "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "EXPORTED_SYMBOLS",
+    "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
+    "gdn_chunk_fwd_gated_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
 GDN_BF16 = 1
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
-                    "gdn_gated_rmsnorm")
+                    "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -70,6 +72,10 @@ def load_library():
     lib.gdn_qkv_prologue.restype = i
     lib.gdn_gated_rmsnorm.argtypes = [vp, vp, fp, i, vp, i, i, i, i, i, f, vp]
     lib.gdn_gated_rmsnorm.restype = i
+    lib.gdn_chunk_fwd_gated.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, fp, i, f, vp] + [i] * 7 + [i, f, vp, sz, vp]
+    lib.gdn_chunk_fwd_gated.restype = i
+    lib.gdn_chunk_fwd_gated_workspace_bytes.argtypes = [i] * 7 + [i]
+    lib.gdn_chunk_fwd_gated_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -80,6 +86,10 @@ def gdn_status_string(status: int) -> str:
 
 def gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
     return int(load_library().gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
+
+
+def gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
 
 
 def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
@@ -242,3 +252,45 @@ def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, y=None, stream=None):
     if st != 0:
         raise GdnError(st, "gdn_gated_rmsnorm")
     return y
+
+
+def gdn_chunk_fwd_gated(q, k, v, g, beta, z, norm_weight, initial_state=None, output_final_state=True,
+                        chunk=64, scale=1.0, eps=1e-6, y=None, final_state=None, workspace=None,
+                        stream=None):
+    """Prefill, then y = RMSNorm(o) * norm_weight * silu(z) per value head.  Arguments as
+    :func:`gdn_chunk_fwd`, plus z [B,T,Hv,dv] (dtype of q) and norm_weight [dv] or [Hv, dv]
+    float32.  Returns (y, final_state or None); ``y`` may be ``z``."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    _check_dense("z", z, (B, T, Hv, dv), q.dtype, dev)
+    per_head = 1 if norm_weight.dim() == 2 else 0
+    _check_dense("norm_weight", norm_weight, (Hv, dv) if per_head else (dv,), torch.float32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("y", y, (B, T, Hv, dv), q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(q)
+    need = int(lib.gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                 _ptr(final_state), _ptr(z), _ptr(norm_weight), per_head, float(eps), _ptr(y),
+                                 B, T, Hqk, Hv, dk, dv, int(chunk), dt, float(scale), _ptr(workspace), wbytes,
+                                 _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd_gated")
+    return y, final_state

@@ -145,6 +145,94 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t gdn_chunk_fwd_gated_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                           gdn_dtype_t dtype)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return 0;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    const size_t base = gdn::chunk_mfma_workspace_bytes(a);
+    if (gdn::chunk_mfma_gated_fused(a)) return base;
+    // otherwise O goes through the workspace, after the recurrence's own part
+    const size_t obytes = (size_t)B * T * Hv * dv * dtype_bytes(dtype);
+    return obytes ? align256(base) + obytes : base;
+}
+
+gdn_status_t gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state, float* final_state,
+                                 const void* z, const float* norm_weight, int weight_per_head, float eps,
+                                 void* y, int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                 gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s != GDN_OK) return s;
+    if (weight_per_head != 0 && weight_per_head != 1) return GDN_ERR_SHAPE;
+    if (!(eps >= 0.f)) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !g || !beta || !z || !norm_weight || !y)) return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, z, y, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta) || !aligned4(norm_weight)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = work ? (size_t)B * T : 0;
+    const size_t sbytes = (size_t)B * Hv * dk * dv * sizeof(float);
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rz = range(z, ntok * Hv * dv * es);
+    const Range rw = range(norm_weight, work ? (weight_per_head ? (size_t)Hv : 1) * dv * sizeof(float) : 0);
+    const Range rs0 = range(initial_state, initial_state ? sbytes : 0);
+    const Range rsf = range(final_state, final_state ? sbytes : 0);
+    const Range ry = range(y, ntok * Hv * dv * es);
+    // y may be z exactly (each element of z is read before the same lane writes it); the final
+    // state may be the initial state exactly
+    const Range fixed[] = {rq, rk, rv, rg, rb, rw};
+    for (const Range& r : fixed)
+        if (overlap(ry, r) || overlap(rsf, r)) return GDN_ERR_ALIAS;
+    if ((overlap(ry, rz) && y != z) || overlap(ry, rs0) || overlap(ry, rsf)) return GDN_ERR_ALIAS;
+    if (overlap(rsf, rz) || (overlap(rsf, rs0) && final_state != initial_state)) return GDN_ERR_ALIAS;
+    const Range rws = range(workspace, need);
+    const Range all[] = {rq, rk, rv, rg, rb, rz, rw, rs0, rsf, ry};
+    for (const Range& r : all)
+        if (overlap(rws, r)) return GDN_ERR_ALIAS;
+    s = device_ok();
+    if (s != GDN_OK) return s;
+
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        if (!final_state) return GDN_OK;
+        return gdn::launch_state_copy(initial_state, final_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, nullptr, B, T, Hqk,
+                                       Hv, dk, dv, chunk, dtype, scale);
+    const int wstride = weight_per_head ? dv : 0;
+    hipError_t e;
+    if (gdn::chunk_mfma_gated_fused(a)) {
+        a.z = z; a.norm_w = norm_weight; a.norm_w_stride = wstride; a.eps = eps; a.y = y;
+        e = gdn::launch_chunk_mfma(a, workspace, st);
+    } else {
+        void* o = (unsigned char*)workspace + align256(gdn::chunk_mfma_workspace_bytes(a));
+        a.o = o;
+        e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st) : gdn::launch_chunk_simt(a, st);
+        if (e == hipSuccess) {
+            gdn::RmsNormArgs r;
+            r.o = o; r.z = z; r.w = norm_weight; r.w_head_stride = wstride; r.y = y;
+            r.B = B; r.T = T; r.Hv = Hv; r.dv = dv; r.dtype_bf16 = dtype == GDN_BF16; r.eps = eps;
+            e = gdn::launch_gated_rmsnorm(r, st);
+        }
+    }
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, float* state, void* o, int B, int Hqk, int Hv,
                                 int dk, int dv, gdn_dtype_t dtype, float scale, void* stream)

@@ -55,6 +55,7 @@
 #include <string.h>
 
 #include "device_common.hpp"
+#include "gated_norm.hpp"
 #include "launch.hpp"
 
 namespace gdn {
@@ -97,7 +98,7 @@ constexpr int NLW = 4;            // loader waves of the state-pass kernel
 constexpr int CP = CH + 8;        // element pitch of [64][64] fp16 matrices (T, Aqk)
 constexpr int AFP = CH + 4;       // float pitch of the float32 A matrix
 
-template <int DK, int BV>
+template <int DK, int BV, bool GATED = false>
 struct MLds {
     static constexpr int KP = DK + 8;            // element pitch of K and Q rows
     static constexpr int VP = BV + 16;           // element pitch of V rows
@@ -109,7 +110,10 @@ struct MLds {
     static constexpr size_t aq = tm + (size_t)CH * CP * 2;          // Aqk [64][CP] f16
     static constexpr size_t af = aq + (size_t)CH * CP * 2;          // A^T [64][AFP] f32
     static constexpr size_t vec = af + (size_t)CH * AFP * 4;        // [2][8][64] f32
-    static constexpr size_t bytes = vec + (size_t)2 * 8 * CH * 4;
+    static constexpr int OP = BV + 8;            // element pitch of the staged output rows
+    static constexpr size_t os = vec + (size_t)2 * 8 * CH * 4;      // O   [64][OP] bf16 (gated only)
+    static constexpr size_t bytes = os + (GATED ? (size_t)CH * OP * 2 : 0);
+    static_assert(os % 16 == 0, "16-byte aligned rows");
 };
 
 // per-chunk vectors (rows of 64 floats); the first four feed the state step, the fifth the output
@@ -601,15 +605,22 @@ __device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd
 }  // namespace
 
 // =======================================================================================
-// Fused kernel
-template <int DK, int DV, int BV>
+// Fused kernel.  GATED (whole value heads per workgroup, BV == DV): the output is the layer's
+// gated RMSNorm y = O / sqrt(mean(O^2) + eps) * w * silu(z) instead of O.  The chain waves stage
+// O of a chunk in LDS in the output phase and, in the interval the prep waves spend finishing T,
+// normalise 16 whole token rows each and write y; O itself never reaches HBM.
+template <int DK, int DV, int BV, bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
-    bf16* __restrict__ o, int T_len, int Hqk, int Hv, int grp, float scale, int xcd_remap)
+    bf16* o,                     // O, or y when gated (y may be z exactly)
+    const bf16* z, const float* __restrict__ nw, int nw_stride, float eps,
+    int T_len, int Hqk, int Hv, int grp, float scale, int xcd_remap)
 {
-    using L = MLds<DK, BV>;
+    using L = MLds<DK, BV, GATED>;
+    static_assert(!GATED || BV == DV, "the gated epilogue needs whole value heads");
+    static_assert(CH == 16 * NCW, "16 output rows per chain wave in the gated epilogue");
     constexpr int NTILE = DV / BV;
     constexpr int NCOL = BV / NCW;      // state columns per chain wave
     constexpr int NTN = NCOL / 16;      // 16-column tiles per chain wave
@@ -887,6 +898,21 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
         floatx4 hacc[NTN][MT];
         const size_t head = (size_t)b * Hv + j;
         load_state<DK, DV, NTN>(hacc, s0, head, c0 + cw * NCOL, lane);
+        // gated epilogue: a row of O is DV / 8 lanes of 8 consecutive columns; a pass covers
+        // 64 / (DV / 8) rows and a chain wave owns rows 16 cw .. 16 cw + 15
+        constexpr int ECB = DV / 8;
+        constexpr int ERP = 64 / ECB;
+        constexpr int EPASS = 16 / ERP;
+        const int ecb = lane % ECB, esub = lane / ECB;
+        bf16* Os = reinterpret_cast<bf16*>(smem + L::os);
+        const bf16* zb = z + ((size_t)b * T_len * Hv + j) * DV + 8 * ecb;
+        bf16* yb = o + ((size_t)b * T_len * Hv + j) * DV + 8 * ecb;
+        bf16x8 zr[EPASS];
+        float wc[8];
+        if constexpr (GATED) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wc[e] = nw[(size_t)j * nw_stride + 8 * ecb + e];
+        }
         lds_barrier();
         // iteration -1: the prep waves build chunk 0
         for (int x = 0; x < 4; ++x) lds_barrier();
@@ -894,12 +920,46 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
         // four barriers per iteration as the prep waves
         for (int n = 0; n < NT; ++n) {
             const int t0 = n * CH;
-            chain_chunk<DK, BV, NCW>(hacc, Kslot(n & 1), Qslot(n & 1), Vs, Tm, Aq, vslot(n & 1),
-                                     ob + (size_t)t0 * v_row, v_row, min(CH, T_len - t0), cw, lane,
-                                     [] { lds_barrier(); });
-            lds_barrier();
-            // interval 4: nothing for the chain waves (the prep waves finish T and restage q, k)
-            lds_barrier();
+            const int nv = min(CH, T_len - t0);
+            if constexpr (GATED) {
+                chain_chunk<DK, BV, NCW>(hacc, Kslot(n & 1), Qslot(n & 1), Vs, Tm, Aq, vslot(n & 1),
+                                         Os, (size_t)L::OP, CH, cw, lane, [] { lds_barrier(); });
+                // this chunk's gate rows, loaded now to arrive during the barrier wait (rows past
+                // the sequence clamped to its last row and not stored)
+#pragma unroll
+                for (int p = 0; p < EPASS; ++p) {
+                    const int tok = 16 * cw + ERP * p + esub;
+                    zr[p] = *reinterpret_cast<const bf16x8*>(zb + (size_t)(t0 + min(tok, nv - 1)) * v_row);
+                }
+                lds_barrier();
+                // interval 4: y of chunk n from the staged O rows (written by all chain waves
+                // before the last two barriers)
+#pragma unroll
+                for (int p = 0; p < EPASS; ++p) {
+                    const int tok = 16 * cw + ERP * p + esub;
+                    const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(Os + tok * L::OP + 8 * ecb);
+                    float ov[8], zv[8], yv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ov[e] = (float)o8[e];
+                        zv[e] = (float)zr[p][e];
+                    }
+                    gated_norm_lane<8>(ov, zv, wc, ECB, 1.f / (float)DV, eps, yv);
+                    if (tok < nv) {
+                        bf16x8 y8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) y8[e] = (bf16)yv[e];
+                        *reinterpret_cast<bf16x8*>(yb + (size_t)(t0 + tok) * v_row) = y8;
+                    }
+                }
+                lds_barrier();
+            } else {
+                chain_chunk<DK, BV, NCW>(hacc, Kslot(n & 1), Qslot(n & 1), Vs, Tm, Aq, vslot(n & 1),
+                                         ob + (size_t)t0 * v_row, v_row, nv, cw, lane, [] { lds_barrier(); });
+                lds_barrier();
+                // interval 4: nothing for the chain waves (the prep waves finish T and restage q, k)
+                lds_barrier();
+            }
         }
         store_state<DK, DV, NTN>(hacc, sf, head, c0 + cw * NCOL, lane);
     }
@@ -1488,12 +1548,12 @@ bool use_split(const ChunkArgs& a)
     return (long)a.B * a.Hv < 192;
 }
 
-template <int DK, int DV, int BV>
+template <int DK, int DV, int BV, bool GATED>
 hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
 {
-    using L = MLds<DK, BV>;
+    using L = MLds<DK, BV, GATED>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_mfma_kernel<DK, DV, BV>;
+    auto kern = chunk_mfma_kernel<DK, DV, BV, GATED>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
@@ -1502,7 +1562,8 @@ hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
     const long per_xcd = nblk / 8;
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(NTHR), L::bytes, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.s0, a.sf, (bf16*)a.o, a.T,
+                       (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.s0, a.sf,
+                       (bf16*)(GATED ? a.y : a.o), (const bf16*)a.z, a.norm_w, a.norm_w_stride, a.eps, a.T,
                        a.Hqk, a.Hv, grp, a.scale, remap);
     return hipGetLastError();
 }
@@ -1554,6 +1615,11 @@ bool chunk_mfma_supported(const ChunkArgs& a)
 
 bool chunk_mfma_split(const ChunkArgs& a) { return chunk_mfma_supported(a) && use_split(a); }
 
+bool chunk_mfma_gated_fused(const ChunkArgs& a)
+{
+    return chunk_mfma_supported(a) && !use_split(a) && choose_bv(a) == a.dv;
+}
+
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a)
 {
     if (!chunk_mfma_split(a)) return 0;
@@ -1571,8 +1637,17 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, void* ws, hipStream_t st)
         return hipErrorInvalidValue;
     }
     const int bv = choose_bv(a);
+    if (a.z) {
+        // the gated epilogue needs whole value heads per workgroup (chunk_mfma_gated_fused)
+        if (bv != a.dv) return hipErrorInvalidValue;
+        if (a.dk == 128 && a.dv == 128) return launch_fused_t<128, 128, 128, true>(a, st);
+        if (a.dk == 128 && a.dv == 64) return launch_fused_t<128, 64, 64, true>(a, st);
+        if (a.dk == 64 && a.dv == 128) return launch_fused_t<64, 128, 128, true>(a, st);
+        if (a.dk == 64 && a.dv == 64) return launch_fused_t<64, 64, 64, true>(a, st);
+        return hipErrorInvalidValue;
+    }
 #define GDN_MFMA_CASE(DK_, DV_, BV_) \
-    if (a.dk == DK_ && a.dv == DV_ && bv == BV_) return launch_fused_t<DK_, DV_, BV_>(a, st);
+    if (a.dk == DK_ && a.dv == DV_ && bv == BV_) return launch_fused_t<DK_, DV_, BV_, false>(a, st);
     GDN_MFMA_CASE(128, 128, 128) GDN_MFMA_CASE(128, 128, 64) GDN_MFMA_CASE(128, 64, 64)
     GDN_MFMA_CASE(64, 128, 128) GDN_MFMA_CASE(64, 128, 64) GDN_MFMA_CASE(64, 64, 64)
 #undef GDN_MFMA_CASE

@@ -31,6 +31,13 @@ struct ChunkArgs {
     int B, T, Hqk, Hv, dk, dv, chunk;
     bool dtype_bf16;
     float scale;
+    // gated output (fused epilogue of the matrix-core kernel, chunk_mfma_gated_fused): z set
+    // means y = RMSNorm(O) * norm_w * silu(z) is written to y and O is not written
+    const void* z = nullptr;
+    const float* norm_w = nullptr;   // [dv] (stride 0) or [Hv, dv] (stride dv)
+    int norm_w_stride = 0;
+    float eps = 0.f;
+    void* y = nullptr;
 };
 
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
@@ -43,6 +50,8 @@ hipError_t launch_chunk_simt(const ChunkArgs& a, hipStream_t st);
 // workspace of chunk_mfma_workspace_bytes followed by the state-pass kernel.
 bool chunk_mfma_supported(const ChunkArgs& a);
 bool chunk_mfma_split(const ChunkArgs& a);
+// The gated RMSNorm can run inside the fused kernel (whole value heads per workgroup).
+bool chunk_mfma_gated_fused(const ChunkArgs& a);
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, void* workspace, hipStream_t st);
 

@@ -23,16 +23,15 @@
 #include <stdint.h>
 
 #include "device_common.hpp"
+#include "gated_norm.hpp"
 #include "launch.hpp"
 
 namespace gdn {
 
 namespace {
 
-constexpr int PTT = 32;   // tokens per wave, prologue
-constexpr int RTT = 16;   // tokens per wave, gated RMSNorm
-
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+constexpr int PTT = 16;   // tokens per wave, prologue
+constexpr int RTT = 8;    // tokens per wave, gated RMSNorm
 
 // 16 bytes of a row as N floats (N = 8 for bf16, 4 for float32)
 template <typename T>
@@ -65,13 +64,6 @@ struct Vec<float> {
     }
     static __device__ __forceinline__ raw put(const float (&x)[N]) { return raw{x[0], x[1], x[2], x[3]}; }
 };
-
-// sum over the `group` lanes of this lane's head (group a power of two <= 64, aligned)
-__device__ __forceinline__ float group_sum(float x, int group)
-{
-    for (int s = 1; s < group; s <<= 1) x += __shfl_xor(x, s, 64);
-    return x;
-}
 
 template <typename T, int W>
 __global__ __launch_bounds__(256) void qkv_prologue_kernel(const T* __restrict__ q_in, const T* __restrict__ k_in,
@@ -215,16 +207,10 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const T* o, const T*
     const float inv_d = 1.f / (float)dv;
 #pragma unroll
     for (int s = 0; s < RTT; ++s) {
-        float ov[N], zv[N];
+        float ov[N], zv[N], yv[N];
         V::get(ro[s], ov);
         V::get(rz[s], zv);
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < N; ++e) ss = fmaf(ov[e], ov[e], ss);
-        const float r = rsqrtf(group_sum(ss, group) * inv_d + eps);
-        float yv[N];
-#pragma unroll
-        for (int e = 0; e < N; ++e) yv[e] = ov[e] * r * wc[e] * silu(zv[e]);
+        gated_norm_lane<N>(ov, zv, wc, group, inv_d, eps, yv);
         if (act && s < nt) *reinterpret_cast<typename V::raw*>(y + base + (size_t)s * cn) = V::put(yv);
     }
 }

@@ -138,6 +138,16 @@ def generate_decode(cfg: Config, *, B=None, steps=None, seed=None) -> dict:
     return d
 
 
+def generate_gate(B, T, Hv, dv, dtype="bf16", seed=3001, w_per_head=False) -> dict:
+    """Inputs of the output gate alone (same recipe as generate_layer's z and weight):
+    z [B,T,Hv,dv] (dtype) ~ N(0, 1); weight [dv] or [Hv, dv] float32 = 1 + 0.1 N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = np.float32
+    z = rng.standard_normal((B, T, Hv, dv), dtype=f)
+    w = (1.0 + 0.1 * rng.standard_normal((Hv, dv) if w_per_head else (dv,))).astype(f)
+    return dict(z=_store(z, dtype), weight=w)
+
+
 def to_torch(x: np.ndarray | None, dtype: str, device):
     """numpy array (float32, or uint16 bf16 bits) -> torch tensor on ``device``."""
     import torch

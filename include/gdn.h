@@ -184,6 +184,43 @@ gdn_status_t gdn_gated_rmsnorm(const void* o, const void* z, const float* weight
                                void* y, int B, int T, int Hv, int dv, gdn_dtype_t dtype, float eps,
                                void* stream);
 
+/*
+ * gdn_chunk_fwd_gated_workspace_bytes -- device scratch (bytes) that gdn_chunk_fwd_gated needs:
+ * gdn_chunk_fwd's own, plus, where the gated RMSNorm cannot run inside the recurrence's kernel,
+ * room for O (B*T*Hv*dv elements of dtype, after the first part rounded up to 256 bytes).  Pure
+ * host function; 0 for invalid sizes.
+ */
+size_t gdn_chunk_fwd_gated_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                           gdn_dtype_t dtype);
+
+/*
+ * gdn_chunk_fwd_gated -- prefill followed by the layer's output normalisation: gdn_chunk_fwd's
+ * O, then the gated RMSNorm of gdn_gated_rmsnorm,
+ *     y = O / sqrt(mean over the head's dv channels of O^2 + eps) * w * silu(z),
+ * with O rounded to dtype before the norm, as when the two calls run one after the other (same
+ * sources as those two).  Where the fused matrix-core kernel holds whole value heads (bf16,
+ * chunk 64, dk and dv 64 or 128, enough chains that gdn_chunk_fwd_kernel_name says "mfma" and
+ * the column tile is dv) the norm runs inside it and O never reaches device memory; otherwise O
+ * goes through the workspace and a second kernel.  Both ways give the same bits.
+ *
+ *   q, k, v, g, beta, initial_state, final_state, sizes, chunk, dtype, scale: as gdn_chunk_fwd
+ *   z              [B, T, Hv, dv] dtype, the gate projection
+ *   norm_weight    [dv] float32 shared by the heads (weight_per_head 0) or [Hv, dv] (1)
+ *   eps            >= 0
+ *   y              [B, T, Hv, dv] dtype output; may be z itself (in place) but may not overlap
+ *                  z otherwise, nor any other argument
+ *   workspace      at least gdn_chunk_fwd_gated_workspace_bytes(...) bytes, as gdn_chunk_fwd
+ * B == 0 is a no-op.  T == 0 writes final_state only.  Errors as gdn_chunk_fwd; a
+ * weight_per_head other than 0 or 1 is GDN_ERR_SHAPE, a negative or NaN eps
+ * GDN_ERR_UNSUPPORTED.
+ */
+gdn_status_t gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state, float* final_state,
+                                 const void* z, const float* norm_weight, int weight_per_head, float eps,
+                                 void* y, int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                 gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

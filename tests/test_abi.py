@@ -230,3 +230,65 @@ def test_layer_steps_valid_calls_report_no_device():
     assert rmsnorm_call() == NODEV
     assert rmsnorm_call(y=fake(0)) == NODEV                             # in place over o
     assert rmsnorm_call(y=fake(1), per_head=1) == NODEV                 # in place over z
+
+
+# ------------------------------------------------------- prefill followed by the gated RMSNorm
+
+GATED_WS = 2 * 100 * 4 * 32 * 2   # float32-vector path: no recurrence workspace, then O in bf16
+
+
+def gated_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), z=fake(7),
+             w=fake(8), per_head=0, eps=1e-6, y=fake(9), B=2, T=100, Hqk=2, Hv=4, dk=64, dv=32, chunk=32,
+             dtype=gdn.GDN_BF16, scale=1.0, ws=fake(10), wsb=GATED_WS, stream=None)
+    a.update(over)
+    return lib.gdn_chunk_fwd_gated(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["z"], a["w"],
+                                   a["per_head"], a["eps"], a["y"], a["B"], a["T"], a["Hqk"], a["Hv"], a["dk"],
+                                   a["dv"], a["chunk"], a["dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_gated_workspace_size():
+    ws = gdn.gdn_chunk_fwd_gated_workspace_bytes
+    # fused matrix-core path with whole value heads per workgroup: the norm runs inside, no O
+    assert ws(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
+    assert ws(8, 100, 16, 32, 128, 64, 64, gdn.GDN_BF16) == 0
+    # split path: its own workspace, rounded up to 256 bytes, then O
+    per_chunk = 32 * 13568 + 16 * 64 * 128 * 2
+    base = 65 * per_chunk
+    assert ws(1, 4097, 16, 32, 128, 128, 64, gdn.GDN_BF16) == (base + 255) // 256 * 256 + 4097 * 32 * 128 * 2
+    # float32 path: O only
+    assert ws(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == 4096 * 32 * 128 * 4
+    assert ws(2, 100, 2, 4, 64, 32, 32, gdn.GDN_BF16) == GATED_WS
+    assert ws(1, 0, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
+    assert ws(1, 4096, 16, 33, 128, 128, 64, gdn.GDN_BF16) == 0      # invalid sizes
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(z=None), NULL), (dict(w=None), NULL), (dict(y=None), NULL), (dict(q=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(B=-1), SHAPE), (dict(per_head=2), SHAPE), (dict(Hv=3), SHAPE),
+    (dict(dv=96), UNSUP), (dict(chunk=128), UNSUP), (dict(eps=-1.0), UNSUP), (dict(eps=float("nan")), UNSUP),
+    (dict(wsb=GATED_WS - 1), WS),
+    (dict(z=ctypes.c_void_p(BASE + 7 * STRIDE + 8)), ALIGN), (dict(y=ctypes.c_void_p(BASE + 9 * STRIDE + 4)), ALIGN),
+    (dict(w=ctypes.c_void_p(BASE + 8 * STRIDE + 2)), ALIGN),
+    (dict(y=fake(2)), ALIAS), (dict(y=fake(8)), ALIAS), (dict(y=fake(5)), ALIAS), (dict(y=fake(6)), ALIAS),
+    (dict(y=ctypes.c_void_p(BASE + 7 * STRIDE + 512)), ALIAS),     # partly over z
+    (dict(sf=fake(7)), ALIAS), (dict(sf=ctypes.c_void_p(BASE + 5 * STRIDE + 256)), ALIAS),
+    (dict(ws=fake(9)), ALIAS), (dict(ws=ctypes.c_void_p(BASE + 8 * STRIDE - 1024)), ALIAS),   # runs into w
+])
+def test_chunk_fwd_gated_rejects(over, status):
+    assert gated_call(**over) == status
+
+
+def test_chunk_fwd_gated_noops():
+    assert gated_call(B=0, q=None, z=None, y=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_chunk_fwd_gated_valid_calls_report_no_device():
+    assert gated_call() == NODEV
+    assert gated_call(y=fake(7)) == NODEV                         # in place over z
+    assert gated_call(sf=fake(5)) == NODEV                        # in-place final state
+    assert gated_call(T=0, q=None, z=None, y=None, ws=None, wsb=0) == NODEV
+    assert gated_call(per_head=1, s0=None, sf=None) == NODEV

@@ -9,7 +9,7 @@ import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import DEV, check, dev, f64, host, sample_chains, say
+from gpu_util import DEV, TOL, check, dev, f64, host, rel_l2, sample_chains, say
 
 gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
 torch = pytest.importorskip("torch")
@@ -367,3 +367,135 @@ def test_gated_rmsnorm(dtype, B, T, Hv, dv, per_head):
     gdn.gdn_gated_rmsnorm(t["o"], z2, t["weight"], y=z2)
     torch.cuda.synchronize()
     assert torch.equal(o2, y) and torch.equal(z2, y)
+
+
+# ------------------------------------------------------- prefill followed by the gated RMSNorm
+
+def _gate_inputs(d, dtype, seed, per_head=False):
+    B, T, Hv, dv = d["v"].shape
+    return gi.generate_gate(B, T, Hv, dv, dtype=dtype, seed=seed, w_per_head=per_head)
+
+
+def run_gated(d, gz, chunk=64, y=None):
+    t, tz = dev(d), dev(gz)
+    y, sf = gdn.gdn_chunk_fwd_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], tz["z"], tz["weight"], t["s0"],
+                                    chunk=chunk, y=y)
+    torch.cuda.synchronize()
+    return y, sf, t, tz
+
+
+def check_gated(name, dtype, y, y_ref, s, s_ref):
+    """y = RMSNorm(O) w silu(z): the norm is scale-invariant per (token, head) row, so the error
+    of y relative to its size is that of O's row; the whole-tensor relative L2 bar of O applies.
+    Per element the bf16 path rounds O and then y (2 x 2^-9 relative) on top of O's own error,
+    so a row's error is bounded by 2^-6 of the row's largest |y| (float32: rel-L2 only)."""
+    tol = TOL[dtype]
+    r = rel_l2(y, y_ref)
+    s_r = rel_l2(s, s_ref)
+    msg = f"{name}: rel_l2(y)={r:.3e} rel_l2(S)={s_r:.3e}"
+    ok = r <= tol["rel"] and s_r <= tol["rel"]
+    if dtype == "bf16":
+        rowmax = np.abs(y_ref).max(axis=-1, keepdims=True)
+        worst = float((np.abs(y - y_ref) / (2.0 ** -6 * rowmax + 1e-6)).max())
+        msg += f" max row-relative err/bound {worst:.3f}"
+        ok &= worst <= 1.0
+    say(msg)
+    assert ok, msg
+
+
+@pytest.mark.parametrize("route", ["fused", "split", "simt"])
+@pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
+                                           (64, 64, 200, 2, 4), (128, 128, 1, 1, 2)])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_chunk_gated_small(route, dk, dv, T, Hqk, Hv, per_head, monkeypatch):
+    """Every route of gdn_chunk_fwd_gated against the oracle's recurrence followed by the
+    oracle's gated RMSNorm, and bit for bit against gdn_chunk_fwd then gdn_gated_rmsnorm."""
+    if route == "fused":
+        monkeypatch.setenv("GDN_MFMA_PATH", "fused")
+        monkeypatch.setenv("GDN_MFMA_BV", str(dv))
+    elif route == "split":
+        monkeypatch.setenv("GDN_MFMA_PATH", "split")
+    else:
+        monkeypatch.setenv("GDN_DISABLE_MFMA", "1")
+    B = 2
+    ws = gdn.gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16)
+    say(f"gated {route} dk={dk} dv={dv} T={T} Hqk={Hqk} Hv={Hv} per_head={per_head} workspace={ws}")
+    assert (ws == 0) == (route == "fused")
+    d = gi.generate(B=B, T=T, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, dtype="bf16", mu=3.0, s0_std=0.02, seed=T + dk + Hv)
+    gz = _gate_inputs(d, "bf16", seed=T + 7, per_head=per_head)
+    y, sf, t, tz = run_gated(d, gz)
+    o_ref, s_ref = oracle_prefill(d)
+    y_ref = oracle.gated_rmsnorm(o_ref, f64(gz["z"]), gz["weight"])
+    check_gated(f"gated {route}", "bf16", host(y), y_ref, host(sf), s_ref)
+    o, sf2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    y2 = gdn.gdn_gated_rmsnorm(o, tz["z"], tz["weight"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(sf, sf2)
+
+
+def test_chunk_gated_f32_and_in_place():
+    """float32 inputs (vector path; O through the workspace) and y written over z."""
+    d = gi.generate(B=2, T=100, Hqk=2, Hv=4, dk=32, dv=64, dtype="f32", mu=3.0, s0_std=0.02, seed=5)
+    gz = _gate_inputs(d, "f32", seed=6)
+    y, sf, t, tz = run_gated(d, gz, chunk=32)
+    o_ref, s_ref = oracle_prefill(d)
+    y_ref = oracle.gated_rmsnorm(o_ref, f64(gz["z"]), gz["weight"])
+    check_gated("gated f32", "f32", host(y), y_ref, host(sf), s_ref)
+    z2 = tz["z"].clone()
+    gdn.gdn_chunk_fwd_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], z2, tz["weight"], t["s0"], chunk=32, y=z2)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, y)
+
+
+@pytest.mark.parametrize("route", ["fused", "split"])
+def test_chunk_gated_bf16_in_place_and_empty(route, monkeypatch):
+    monkeypatch.setenv("GDN_MFMA_PATH", route)
+    monkeypatch.setenv("GDN_MFMA_BV", "128")
+    d = gi.generate(B=1, T=150, Hqk=1, Hv=2, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=8)
+    gz = _gate_inputs(d, "bf16", seed=9)
+    y, sf, t, tz = run_gated(d, gz)
+    z2 = tz["z"].clone()
+    gdn.gdn_chunk_fwd_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], z2, tz["weight"], t["s0"], y=z2)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, y)
+    # T == 0: only the final state is written (a copy of the initial state)
+    e = {n: (x[:, :0].contiguous() if n not in ("s0",) and x is not None else x) for n, x in t.items()}
+    ye, se = gdn.gdn_chunk_fwd_gated(e["q"], e["k"], e["v"], e["g"], e["beta"], tz["z"][:, :0].contiguous(),
+                                     tz["weight"], e["s0"])
+    torch.cuda.synchronize()
+    assert ye.numel() == 0 and torch.equal(se, t["s0"])
+
+
+def test_chunk_gated_batched_full():
+    """The many-chain workload at full size on the fused route: bit for bit equal to the two
+    calls one after the other, and sampled chains against the oracle."""
+    cfg = gi.CONFIGS["batched_prefill"]
+    assert gdn.gdn_chunk_fwd_gated_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, 64, gdn.GDN_BF16) == 0
+    say(f"gated batched full {cfg}")
+    d = gi.generate(cfg)
+    gz = _gate_inputs(d, "bf16", seed=cfg.seed + 5)
+    y, sf, t, tz = run_gated(d, gz)
+    o, sf2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    y2 = gdn.gdn_gated_rmsnorm(o, tz["z"], tz["weight"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(sf, sf2)
+    del o, y2, sf2
+    chains = [(0, 0), (6, 13), (7, 31)]
+    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
+    o_ref, s_ref = oracle_prefill(sd)
+    z_s = np.stack([f64(gz["z"][b, :, j]) for b, j in chains])[:, :, None]
+    y_ref = oracle.gated_rmsnorm(o_ref, z_s, gz["weight"])
+    yh = np.stack([host(y[b, :, j]) for b, j in chains])[:, :, None]
+    sh = np.stack([host(sf[b, j]) for b, j in chains])[:, None]
+    check_gated("gated batched sampled", "bf16", yh, y_ref, sh, s_ref)
+
+
+def test_chunk_gated_qwen3next_full():
+    cfg = gi.CONFIGS["qwen3next_prefill"]
+    say(f"gated qwen3next full {cfg}")
+    d = gi.generate(cfg)
+    gz = _gate_inputs(d, "bf16", seed=cfg.seed + 5, per_head=True)
+    y, sf, t, tz = run_gated(d, gz)
+    o_ref, s_ref = oracle_prefill(d)
+    y_ref = oracle.gated_rmsnorm(o_ref, f64(gz["z"]), gz["weight"])
+    check_gated("gated qwen3next", "bf16", host(y), y_ref, host(sf), s_ref)
