@@ -17,7 +17,9 @@ The same JSON line carries
   prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3.6-27B-shaped (T=65536, Hv=48)
                    prefill workloads, tokens/s and roofline fractions;
   layer_ops     -- the layer steps either side of the recurrence at the headline shape (short
-                   conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth.
+                   conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth;
+  gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
+                   call) on the headline and the batched workloads.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
 """
@@ -112,11 +114,19 @@ def time_launches(fn, n_sets, steps, warmup, torch):
     return wall, sum(kern) / len(kern)
 
 
-def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20):
+def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated=False):
+    """gdn_chunk_fwd (or, gated, gdn_chunk_fwd_gated: the output's gated RMSNorm in the same call,
+    whose algorithmic bytes add the gate z read once and the norm weight)."""
     dev = "cuda:0"
     base = gi.generate_torch(cfg, dev)
     es = 2 if cfg.dtype == "bf16" else 4
     per_set = prefill_alg_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, es, cfg.s0_std > 0, True)
+    if gated:
+        per_set += cfg.B * cfg.T * cfg.Hv * cfg.dv * es + cfg.dv * 4
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed + 29)
+        base["z"] = torch.randn((cfg.B, cfg.T, cfg.Hv, cfg.dv), generator=g, device=dev).to(base["q"].dtype)
+        nw = 1.0 + 0.1 * torch.randn(cfg.dv, generator=g, device=dev)
     n_sets = max(1, min(8, -(-min_bytes // per_set)))
     sets = [base]
     for s in range(1, n_sets):
@@ -124,13 +134,18 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20):
     outs = [torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=base["q"].dtype, device=dev) for _ in range(n_sets)]
     sfs = [torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev) for _ in range(n_sets)]
     dt = gdn.GDN_BF16 if es == 2 else gdn.GDN_F32
-    need = gdn.gdn_chunk_fwd_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk, dt)
+    wsf = gdn.gdn_chunk_fwd_gated_workspace_bytes if gated else gdn.gdn_chunk_fwd_workspace_bytes
+    need = wsf(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk, dt)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
 
     def fn(i):
         x = sets[i]
-        gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
-                          o=outs[i], final_state=sfs[i], workspace=ws)
+        if gated:
+            gdn.gdn_chunk_fwd_gated(x["q"], x["k"], x["v"], x["g"], x["beta"], x["z"], nw, x["s0"],
+                                    chunk=cfg.chunk, y=outs[i], final_state=sfs[i], workspace=ws)
+        else:
+            gdn.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
+                              o=outs[i], final_state=sfs[i], workspace=ws)
 
     wall, kern = time_launches(fn, n_sets, steps, warmup, torch)
     flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
@@ -325,6 +340,18 @@ def main():
         line["prefill_configs"] = pc
         print("bench: layer steps (prologue, gated RMSNorm)", file=sys.stderr, flush=True)
         line["layer_ops"] = bench_layer_ops(cfg, torch, gdn)
+        gp = {}
+        for name in (cfg.name, "batched_prefill"):
+            c = gi.CONFIGS[name]
+            print(f"bench: gated prefill {c}", file=sys.stderr, flush=True)
+            rr = bench_prefill(c, 5, 2, torch, gdn, gi, gated=True)
+            fused = gdn.gdn_chunk_fwd_gated_workspace_bytes(c.B, c.T, c.Hqk, c.Hv, c.dk, c.dv, c.chunk,
+                                                            gdn.GDN_BF16 if c.dtype == "bf16" else gdn.GDN_F32) == 0
+            gp[name] = {"tokens_per_s": c.B * c.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
+                        "alg_bytes": rr["bytes"], "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK,
+                        "route": "norm fused into the prefill kernel" if fused
+                        else "O through the workspace, then the norm kernel"}
+        line["gated_prefill"] = gp
     print(json.dumps(line), flush=True)
 
 

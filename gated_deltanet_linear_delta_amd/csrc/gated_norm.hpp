@@ -11,12 +11,30 @@
 
 namespace gdn {
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// SiLU(x) = x sigmoid(x), with the hardware reciprocal (1 ulp) in place of a full division
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-// sum over the `group` lanes of this lane's head (group a power of two <= 64, aligned)
+// a lane's value moved across the wave by a DPP pattern (no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the `group` lanes of this lane's head (group a power of two <= 64, aligned).  Within a
+// row of 16 lanes the partners come by DPP: lanes 1 and 2 apart inside a quad, then the mirror
+// images inside a half row and a row (after the quad steps every lane of a quad holds the quad's
+// sum, so pairing mirror images pairs whole quads, then whole half rows); beyond a row by lane
+// exchange.  Each step adds two equal-rank partial sums, so every lane of the group ends with
+// the same bits.
 __device__ __forceinline__ float group_sum(float x, int group)
 {
-    for (int s = 1; s < group; s <<= 1) x += __shfl_xor(x, s, 64);
+    if (group >= 2) x += dpp_move<0xB1>(x);    // quad_perm [1,0,3,2]
+    if (group >= 4) x += dpp_move<0x4E>(x);    // quad_perm [2,3,0,1]
+    if (group >= 8) x += dpp_move<0x141>(x);   // row_half_mirror
+    if (group >= 16) x += dpp_move<0x140>(x);  // row_mirror
+    if (group >= 32) x += __shfl_xor(x, 16, 64);
+    if (group >= 64) x += __shfl_xor(x, 32, 64);
     return x;
 }
 
