@@ -6,6 +6,10 @@ may import this package.  Nothing here is shared with the HIP library, and nothi
 * :func:`recurrent` -- the definition, token by token, in C (``gdn_oracle.c``), float64, OpenMP
   over independent (batch, value-head) chains.  This is the oracle every GPU result is compared to.
 * :func:`decode` -- the same recurrence applied once per call over a sequence of decode steps.
+* :func:`recurrent_bwd` -- its reverse-mode adjoint, token by token, in C, float64: the gradients
+  of a loss through o and the final state with respect to q, k, v, g, beta and S0.
+* :func:`chunked_bwd` -- the gradients through the chunkwise form, in numpy float64: the chunk
+  algebra of the backward pass the GPU implements, pinned against :func:`recurrent_bwd`.
 * :func:`brute_force` -- the recurrence with every transition matrix written out densely
   (numpy), for tiny inputs; an independent code path used to pin :func:`recurrent`.
 * :func:`chunked` -- the chunkwise (WY / UT-transform) refactoring of the same recurrence in
@@ -26,8 +30,8 @@ from . import build as _build
 
 from .layer_ops import gated_rmsnorm, qkv_prologue, silu
 
-__all__ = ["recurrent", "decode", "brute_force", "chunked", "max_threads", "load", "qkv_prologue",
-           "gated_rmsnorm", "silu"]
+__all__ = ["recurrent", "recurrent_bwd", "decode", "brute_force", "chunked", "chunked_bwd", "max_threads",
+           "load", "qkv_prologue", "gated_rmsnorm", "silu"]
 
 _lib = None
 
@@ -42,6 +46,8 @@ def load():
         lib.gdn_oracle_recurrent.argtypes = [dp] * 8 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
         lib.gdn_oracle_recurrent.restype = ctypes.c_int
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
+        lib.gdn_oracle_recurrent_bwd.argtypes = [dp] * 14 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+        lib.gdn_oracle_recurrent_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -82,6 +88,33 @@ def recurrent(q, k, v, g, beta, s0=None, scale: float = 1.0, threads: int = 0):
     if rc != 0:
         raise ValueError("oracle rejected the sizes")
     return o, sf
+
+
+def recurrent_bwd(q, k, v, g, beta, s0, do, dsf=None, scale: float = 1.0, threads: int = 0):
+    """Gradients of L = <do, o> + <dsf, s_final> through :func:`recurrent` (reverse-mode adjoint
+    of each step of the recurrence, in C, float64).
+
+    Returns dict(dq, dk [B,T,Hqk,dk], dv [B,T,Hv,dv], dg, dbeta [B,T,Hv], ds0 [B,Hv,dk,dv]); the
+    gradient of a query/key head sums the contributions of the value heads of its group."""
+    q, k, v, g, beta, s0, do, dsf = map(_f64, (q, k, v, g, beta, s0, do, dsf))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    assert do.shape == (B, T, Hv, dv)
+    dq_v = np.empty((B, T, Hv, dk))
+    dk_v = np.empty((B, T, Hv, dk))
+    dvv = np.empty((B, T, Hv, dv))
+    dg = np.empty((B, T, Hv))
+    dbeta = np.empty((B, T, Hv))
+    ds0 = np.empty((B, Hv, dk, dv))
+    rc = load().gdn_oracle_recurrent_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(do),
+                                         _ptr(dsf), _ptr(dq_v), _ptr(dk_v), _ptr(dvv), _ptr(dg), _ptr(dbeta),
+                                         _ptr(ds0), B, T, Hqk, Hv, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    grp = Hv // Hqk
+    dq = dq_v.reshape(B, T, Hqk, grp, dk).sum(axis=3)
+    dkk = dk_v.reshape(B, T, Hqk, grp, dk).sum(axis=3)
+    return dict(dq=dq, dk=dkk, dv=dvv, dg=dg, dbeta=dbeta, ds0=ds0)
 
 
 def decode(q, k, v, g, beta, s0, scale: float = 1.0, threads: int = 0):
@@ -170,3 +203,120 @@ def chunked(q, k, v, g, beta, s0=None, chunk: int = 64, scale: float = 1.0):
                 h = np.exp(gc[-1]) * h + Kt.T @ Delta
             sf[b, j] = h
     return o, sf
+
+
+def chunked_bwd(q, k, v, g, beta, s0, do, dsf=None, chunk: int = 64, scale: float = 1.0):
+    """Gradients of L = <do, o> + <dsf, s_final> through the chunkwise form (numpy float64).
+
+    Per chunk, with the forward quantities of :func:`chunked` (A, T = (I + A)^{-1},
+    W = T diag(beta e^gc) K, U = T diag(beta) V, Delta = U - W h, M = lower-incl(Q K^T * Gamma),
+    O = diag(e^gc) Q h + M Delta, h' = e^gL h + (diag(e^(gL - gc)) K)^T Delta, gL the last gc),
+    and the gradient dh' of the chunk's exit state, the steps of the forward are differentiated in
+    reverse order (derived from those equations; the pages give none of it):
+
+      dDelta = diag(e^(gL-gc)) K dh' + M^T dO
+      dh     = e^gL dh' + Q^T diag(e^gc) dO - W^T dDelta      (the entry state's gradient)
+      dW = -dDelta h^T,  dU = dDelta,  dT = dU (diag(beta) V)^T + dW (diag(beta e^gc) K)^T
+      dA = -T^T dT T^T  (strictly lower part),  and the gates' and keys' terms of each product
+
+    and dg is the reverse cumulative sum of dgc inside the chunk.  The forward state entering
+    every chunk is kept from a first pass.  q, k gradients sum over the value heads of a group.
+    The inverse of the unit lower-triangular I + A is numpy.linalg.inv (a library primitive)."""
+    q, k, v, g, beta, s0, do, dsf = map(_f64, (q, k, v, g, beta, s0, do, dsf))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    out = dict(dq=np.zeros((B, T, Hqk, dk)), dk=np.zeros((B, T, Hqk, dk)), dv=np.zeros((B, T, Hv, dv)),
+               dg=np.zeros((B, T, Hv)), dbeta=np.zeros((B, T, Hv)), ds0=np.zeros((B, Hv, dk, dv)))
+    starts = list(range(0, T, chunk))
+    for b in range(B):
+        for j in range(Hv):
+            i = j // grp
+            h = np.zeros((dk, dv)) if s0 is None else np.array(s0[b, j], dtype=np.float64)
+
+            def parts(c0, h):
+                c1 = min(T, c0 + chunk)
+                n = c1 - c0
+                K, Q, V = k[b, c0:c1, i], scale * q[b, c0:c1, i], v[b, c0:c1, j]
+                bt = beta[b, c0:c1, j]
+                gc = np.cumsum(g[b, c0:c1, j])
+                eg, gL = np.exp(gc), gc[-1]
+                ed = np.exp(gL - gc)
+                Gam = np.exp(np.tril(gc[:, None] - gc[None, :]))
+                KK = K @ K.T
+                A = np.tril(bt[:, None] * KK * Gam, -1)
+                Tm = np.linalg.inv(np.eye(n) + A)
+                KB = (bt * eg)[:, None] * K
+                W = Tm @ KB
+                U = Tm @ (bt[:, None] * V)
+                D = U - W @ h
+                M = np.tril((Q @ K.T) * Gam)
+                return dict(c1=c1, n=n, K=K, Q=Q, V=V, bt=bt, gc=gc, eg=eg, gL=gL, ed=ed, Gam=Gam, KK=KK, A=A,
+                            Tm=Tm, KB=KB, W=W, U=U, D=D, M=M)
+
+            hs = []
+            for c0 in starts:
+                hs.append(h)
+                f = parts(c0, h)
+                h = np.exp(f["gL"]) * h + (f["ed"][:, None] * f["K"]).T @ f["D"]
+            dh = np.zeros((dk, dv)) if dsf is None else np.array(dsf[b, j], dtype=np.float64)
+            for ci in range(len(starts) - 1, -1, -1):
+                c0 = starts[ci]
+                h = hs[ci]
+                f = parts(c0, h)
+                c1, K, Q, V, bt, gc, eg, gL, ed, Gam = (f[x] for x in ("c1", "K", "Q", "V", "bt", "gc", "eg", "gL", "ed", "Gam"))
+                KK, A, Tm, KB, W, D, M = (f[x] for x in ("KK", "A", "Tm", "KB", "W", "D", "M"))
+                dO = do[b, c0:c1, j]
+                dK = np.zeros_like(K)
+                dQ = np.zeros_like(Q)
+                dgc = np.zeros_like(gc)
+                dbt = np.zeros_like(bt)
+                # h' = e^gL h + (diag(ed) K)^T D
+                dD = (ed[:, None] * K) @ dh + M.T @ dO
+                X = D @ dh.T                                  # d(diag(ed) K)
+                dK += ed[:, None] * X
+                t_ed = ed * np.sum(K * X, axis=1)             # d(ed_r) * ed_r
+                dgc -= t_ed
+                dgL = np.exp(gL) * np.sum(dh * h) + np.sum(t_ed)
+                # O = diag(eg) Q h + M D
+                Oi = eg[:, None] * (Q @ h)
+                dgc += np.sum(dO * Oi, axis=1)
+                dQ += eg[:, None] * (dO @ h.T)
+                dM = np.tril(dO @ D.T)
+                E = dM * Gam
+                dQ += E @ K
+                dK += E.T @ Q
+                PM = dM * M
+                dgc += PM.sum(axis=1) - PM.sum(axis=0)
+                # state gradient for the previous chunk
+                dh_prev = np.exp(gL) * dh + Q.T @ (eg[:, None] * dO) - W.T @ dD
+                # D = U - W h
+                dW = -dD @ h.T
+                dU = dD
+                # U = T diag(bt) V, W = T KB
+                TdU = Tm.T @ dU
+                out["dv"][b, c0:c1, j] = bt[:, None] * TdU
+                dbt += np.sum(V * TdU, axis=1)
+                dKB = Tm.T @ dW
+                dK += (bt * eg)[:, None] * dKB
+                kb = np.sum(K * dKB, axis=1)
+                dbt += eg * kb
+                dgc += bt * eg * kb
+                dT = dU @ (bt[:, None] * V).T + dW @ KB.T
+                # T = (I + A)^{-1}
+                dA = np.tril(-Tm.T @ dT @ Tm.T, -1)
+                # A = strictly-lower(diag(bt) (KK * Gam))
+                G = KK * Gam
+                dbt += np.sum(np.tril(dA * G, -1), axis=1)
+                PA = np.tril(dA * A, -1)
+                dgc += PA.sum(axis=1) - PA.sum(axis=0)
+                Dk = np.tril(dA * bt[:, None] * Gam, -1)
+                dK += Dk @ K + Dk.T @ K
+                dgc[-1] += dgL
+                out["dq"][b, c0:c1, i] += scale * dQ
+                out["dk"][b, c0:c1, i] += dK
+                out["dbeta"][b, c0:c1, j] = dbt
+                out["dg"][b, c0:c1, j] = np.cumsum(dgc[::-1])[::-1]
+                dh = dh_prev
+            out["ds0"][b, j] = dh
+    return out

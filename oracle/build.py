@@ -1,4 +1,5 @@
-"""Compile the float64 CPU oracle (oracle/gdn_oracle.c) into oracle/libgdn_oracle.so with gcc.
+"""Compile the float64 CPU oracle (oracle/gdn_oracle.c, oracle/gdn_oracle_bwd.c) into
+oracle/libgdn_oracle.so with gcc.
 
 Test infrastructure: the oracle is a checker, not part of the product path."""
 from __future__ import annotations
@@ -8,15 +9,16 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gdn_oracle.c")
+SRC_BWD = os.path.join(HERE, "gdn_oracle_bwd.c")
 LIB = os.path.join(HERE, "libgdn_oracle.so")
 
 
 def build(force: bool = True) -> str:
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(os.path.getmtime(SRC), os.path.getmtime(SRC_BWD)):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
-           SRC, "-o", tmp, "-lm"]
+           SRC, SRC_BWD, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

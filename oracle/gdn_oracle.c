@@ -97,3 +97,4 @@ int gdn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
