@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/gdn.h):
 * :func:`gdn_qkv_prologue` -- short causal conv, SiLU and q/k L2 norm after the projections.
 * :func:`gdn_gated_rmsnorm` -- RMSNorm of the output times SiLU of the gate.
 * :func:`gdn_chunk_fwd_gated` -- prefill followed by the gated RMSNorm (fused where it can be).
+* :func:`gdn_chunk_bwd` -- backward pass of the prefill (gradients of q, k, v, g, beta, S0).
 * :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_gated_workspace_bytes`,
   :func:`gdn_chunk_fwd_kernel_name`, :func:`gdn_status_string`.
 """
@@ -24,14 +25,15 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "library_path", "load_library", "gdn_chunk_fwd",
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
     "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
-    "gdn_chunk_fwd_gated_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
 GDN_BF16 = 1
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
-                    "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes")
+                    "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
+                    "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -76,6 +78,10 @@ def load_library():
     lib.gdn_chunk_fwd_gated.restype = i
     lib.gdn_chunk_fwd_gated_workspace_bytes.argtypes = [i] * 7 + [i]
     lib.gdn_chunk_fwd_gated_workspace_bytes.restype = sz
+    lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp] + [i] * 6 + [i, f, vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = i
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 6 + [i]
+    lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -90,6 +96,10 @@ def gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF1
 
 def gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
     return int(load_library().gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
+
+
+def gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype))
 
 
 def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
@@ -294,3 +304,41 @@ def gdn_chunk_fwd_gated(q, k, v, g, beta, z, norm_weight, initial_state=None, ou
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd_gated")
     return y, final_state
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, grad_o, initial_state=None, grad_final_state=None, scale=1.0,
+                  want_grad_initial_state=True, workspace=None, stream=None):
+    """Backward pass of :func:`gdn_chunk_fwd`.  Inputs as that call plus grad_o [B,T,Hv,dv]
+    (dtype of q) and grad_final_state [B,Hv,dk,dv] float32 or None.  Returns a dict of dq, dk
+    [B,T,Hqk,dk], dv [B,T,Hv,dv] (dtype of q), dg, dbeta [B,T,Hv] float32 and ds0
+    [B,Hv,dk,dv] float32 (None when not wanted)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    _check_dense("grad_o", grad_o, (B, T, Hv, dv), q.dtype, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    if grad_final_state is not None:
+        _check_dense("grad_final_state", grad_final_state, (B, Hv, dk, dv), torch.float32, dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+               ds0=torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev) if want_grad_initial_state else None)
+    dt = _dtype_code(q)
+    need = int(lib.gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(grad_o),
+                           _ptr(grad_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["ds0"]), B, T, Hqk, Hv, dk, dv, dt,
+                           float(scale), _ptr(workspace), wbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_bwd")
+    return out

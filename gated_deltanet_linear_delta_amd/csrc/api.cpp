@@ -233,6 +233,69 @@ gdn_status_t gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, co
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, gdn_dtype_t dtype)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, 32, dtype) != GDN_OK) return 0;
+    return gdn::chunk_bwd_workspace_bytes(B, T, Hv, dk, dv);
+}
+
+gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const float* initial_state, const void* grad_o, const float* grad_final_state,
+                           void* grad_q, void* grad_k, void* grad_v, float* grad_g, float* grad_beta,
+                           float* grad_initial_state, int B, int T, int Hqk, int Hv, int dk, int dv,
+                           gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, 32, dtype);
+    if (s != GDN_OK) return s;
+    const size_t need = gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !g || !beta || !grad_o || !grad_q || !grad_k || !grad_v || !grad_g || !grad_beta))
+        return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* p16[] = {q, k, v, initial_state, grad_o, grad_final_state, grad_q, grad_k, grad_v,
+                         grad_initial_state, workspace};
+    for (const void* p : p16)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const void* p4[] = {g, beta, grad_g, grad_beta};
+    for (const void* p : p4)
+        if (p && !aligned4(p)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = work ? (size_t)B * T : 0;
+    const size_t sbytes = (size_t)B * Hv * dk * dv * sizeof(float);
+    const Range ins[] = {range(q, ntok * Hqk * dk * es), range(k, ntok * Hqk * dk * es),
+                         range(v, ntok * Hv * dv * es), range(g, ntok * Hv * 4), range(beta, ntok * Hv * 4),
+                         range(initial_state, initial_state ? sbytes : 0), range(grad_o, ntok * Hv * dv * es),
+                         range(grad_final_state, grad_final_state ? sbytes : 0)};
+    const Range outs[] = {range(grad_q, ntok * Hqk * dk * es), range(grad_k, ntok * Hqk * dk * es),
+                          range(grad_v, ntok * Hv * dv * es), range(grad_g, ntok * Hv * 4),
+                          range(grad_beta, ntok * Hv * 4),
+                          range(grad_initial_state, grad_initial_state ? sbytes : 0), range(workspace, need)};
+    for (const Range& o : outs) {
+        for (const Range& r : ins)
+            if (overlap(o, r)) return GDN_ERR_ALIAS;
+        for (const Range& o2 : outs)
+            if (&o2 != &o && overlap(o, o2)) return GDN_ERR_ALIAS;
+    }
+    s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        if (!grad_initial_state) return GDN_OK;
+        return gdn::launch_state_copy(grad_final_state, grad_initial_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    gdn::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = initial_state; a.dout = grad_o;
+    a.dsf = grad_final_state; a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dg = grad_g; a.dbeta = grad_beta;
+    a.ds0 = grad_initial_state; a.ws = (float*)workspace;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk_ = dk; a.dv_ = dv;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    return gdn::launch_chunk_bwd(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, float* state, void* o, int B, int Hqk, int Hv,
                                 int dk, int dv, gdn_dtype_t dtype, float scale, void* stream)

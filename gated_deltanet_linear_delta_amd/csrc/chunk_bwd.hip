@@ -1,0 +1,671 @@
+// Backward pass of the chunkwise gated delta rule on the float32 vector units of gfx950: the
+// gradients of a loss through O and the final state with respect to q, k, v, g, beta and the
+// initial state ("Gated Attention Architectures", section 3, names hardware-efficient chunkwise
+// training for Gated DeltaNet; the algebra below is the reverse of the forward chunk steps,
+// derived from them).
+//
+// Forward chunk (positions r of one chunk, entry state h = S^T [dk, dv], gc the in-chunk
+// log-decay cumsum, gL its last value, Gamma_rs = exp(gc_r - gc_s)):
+//   A = strictly-lower(diag(beta)(K K^T * Gamma)),  T = (I + A)^{-1}
+//   W = T diag(beta e^gc) K,  U = T diag(beta) V,  Delta = U - W h
+//   M = lower-incl((scale Q) K^T * Gamma),  O = diag(e^gc)(scale Q) h + M Delta
+//   h' = e^gL h + (diag(e^(gL - gc)) K)^T Delta
+// Backward, given dO and the gradient dh' of the chunk's exit state:
+//   dDelta = diag(e^(gL-gc)) K dh' + M^T dO
+//   dh     = e^gL dh' + (scale Q)^T diag(e^gc) dO - W^T dDelta      (the entry state's gradient)
+//   dW = -dDelta h^T,  dV = diag(beta) T^T dDelta,  dT = dDelta (diag(beta) V)^T + dW (diag(beta e^gc) K)^T,
+//   dA = strictly-lower(-T^T dT T^T),  and the gates' and keys' terms of every product;
+//   dg = reverse cumulative sum of dgc inside the chunk.
+//
+// Three launches (chunks of 32 positions, value columns in tiles of 32):
+// 1. the float32 forward kernel run again, storing the state entering every chunk (workspace H);
+// 2. bwd_dh_kernel: the reverse state pass, one workgroup per (batch, value head, column tile),
+//    storing each chunk's exit-state gradient (workspace dH) and the initial state's gradient;
+// 3. bwd_chunk_kernel: one workgroup per (batch, query/key head, chunk), over the value heads of
+//    the group and the column tiles in turn, with dq and dk accumulated in registers, so every
+//    gradient is written once (no atomics, deterministic).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int BW_NT = 256;   // threads per workgroup
+constexpr int BW_C = 32;     // chunk length of the backward pass
+constexpr int BW_BV = 32;    // value columns per tile
+constexpr int BW_CP = BW_C + 1;
+constexpr int BW_VP = BW_BV + 1;
+
+// ------------------------------------------------------------------- reverse state pass
+
+template <int DK>
+struct DhLds {
+    static constexpr int KP = DK + 1;
+    static constexpr size_t k = 0;
+    static constexpr size_t q = k + (size_t)BW_C * KP;
+    static constexpr size_t dO = q + (size_t)BW_C * KP;
+    static constexpr size_t dh = dO + (size_t)BW_C * BW_VP;
+    static constexpr size_t a = dh + (size_t)DK * BW_BV;
+    static constexpr size_t m = a + (size_t)BW_C * BW_CP;
+    static constexpr size_t y = m + (size_t)BW_C * BW_CP;
+    static constexpr size_t gc = y + (size_t)BW_C * BW_VP;
+    static constexpr size_t eg = gc + BW_C;
+    static constexpr size_t ed = eg + BW_C;
+    static constexpr size_t bt = ed + BW_C;
+    static constexpr size_t floats = bt + BW_C;
+    static constexpr size_t bytes = floats * sizeof(float);
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const float* __restrict__ g, const float* __restrict__ beta,
+                                                       const T* __restrict__ dout, const float* __restrict__ dsf,
+                                                       float* __restrict__ dH, float* __restrict__ ds0, int T_len,
+                                                       int Hqk, int Hv, int grp, float scale)
+{
+    using L = DhLds<DK>;
+    constexpr int KP = L::KP;
+    extern __shared__ float lds[];
+    float* Ks = lds + L::k;
+    float* Qs = lds + L::q;
+    float* dOs = lds + L::dO;
+    float* dhs = lds + L::dh;
+    float* As = lds + L::a;
+    float* Ms = lds + L::m;
+    float* Ys = lds + L::y;
+    float* gcs = lds + L::gc;
+    float* egs = lds + L::eg;
+    float* eds = lds + L::ed;
+    float* bs = lds + L::bt;
+
+    const int head = blockIdx.x;   // b * Hv + j
+    const int b = head / Hv, j = head - b * Hv, i = j / grp;
+    const int c0 = blockIdx.y * BW_BV;
+    const int tid = threadIdx.x;
+    const int NT = (T_len + BW_C - 1) / BW_C;
+    const size_t sbase = (size_t)head * DK * DV + c0;
+
+    for (int e = tid; e < DK * BW_BV; e += BW_NT)
+        dhs[e] = dsf ? dsf[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] : 0.f;
+    for (int ci = NT - 1; ci >= 0; --ci) {
+        const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
+        __syncthreads();
+        // the exit-state gradient of this chunk, for the per-chunk kernel
+        float* dp = dH + ((size_t)head * NT + ci) * DK * DV + c0;
+        for (int e = tid; e < DK * BW_BV; e += BW_NT) dp[(size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
+        for (int e = tid; e < BW_C * DK; e += BW_NT) {
+            const int r = e / DK, m = e % DK;
+            float kv = 0.f, qv = 0.f;
+            if (r < n) {
+                const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+                kv = to_f32(k[off]);
+                qv = to_f32(q[off]) * scale;
+            }
+            Ks[r * KP + m] = kv;
+            Qs[r * KP + m] = qv;
+        }
+        for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+            const int r = e / BW_BV, c = e % BW_BV;
+            dOs[r * BW_VP + c] = r < n ? to_f32(dout[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
+        }
+        if (tid < BW_C) {
+            const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+            gcs[tid] = tid < n ? g[off] : 0.f;
+            bs[tid] = tid < n ? beta[off] : 0.f;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+#pragma unroll 4
+            for (int r = 0; r < BW_C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        }
+        __syncthreads();
+        if (tid < BW_C) {
+            egs[tid] = expf(gcs[tid]);
+            eds[tid] = expf(gcs[BW_C - 1] - gcs[tid]);
+        }
+        // A (strictly lower) and M (lower including the diagonal)
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            float a = 0.f, mm = 0.f;
+            if (s <= r) {
+                float kk = 0.f, qk = 0.f;
+#pragma unroll 4
+                for (int m = 0; m < DK; ++m) {
+                    kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
+                    qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
+                }
+                const float gam = expf(gcs[r] - gcs[s]);
+                mm = gam * qk;
+                if (s < r) a = bs[r] * gam * kk;
+            }
+            As[r * BW_CP + s] = a;
+            Ms[r * BW_CP + s] = mm;
+        }
+        __syncthreads();
+        // dDelta = diag(ed) K dh' + M^T dO
+        for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+            const int r = e / BW_BV, c = e % BW_BV;
+            float x = 0.f, y = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) x = fmaf(Ks[r * KP + m], dhs[m * BW_BV + c], x);
+#pragma unroll 4
+            for (int s = r; s < BW_C; ++s) y = fmaf(Ms[s * BW_CP + r], dOs[s * BW_VP + c], y);
+            Ys[r * BW_VP + c] = fmaf(eds[r], x, y);
+        }
+        __syncthreads();
+        // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution, one thread per column
+        if (tid < BW_BV) {
+            for (int r = BW_C - 2; r >= 0; --r) {
+                float acc = Ys[r * BW_VP + tid];
+#pragma unroll 4
+                for (int s = r + 1; s < BW_C; ++s) acc = fmaf(-As[s * BW_CP + r], Ys[s * BW_VP + tid], acc);
+                Ys[r * BW_VP + tid] = acc;
+            }
+        }
+        __syncthreads();
+        // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y
+        const float eL = egs[BW_C - 1];
+        for (int e = tid; e < DK * BW_BV; e += BW_NT) {
+            const int m = e / BW_BV, c = e % BW_BV;
+            float acc = eL * dhs[e];
+#pragma unroll 4
+            for (int r = 0; r < BW_C; ++r) {
+                const float w = egs[r] * (Qs[r * KP + m] * dOs[r * BW_VP + c] - bs[r] * Ks[r * KP + m] * Ys[r * BW_VP + c]);
+                acc += w;
+            }
+            dhs[e] = acc;
+        }
+    }
+    __syncthreads();
+    if (ds0) {
+        for (int e = tid; e < DK * BW_BV; e += BW_NT) ds0[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
+    }
+}
+
+// ------------------------------------------------------------------- per-chunk gradients
+
+template <int DK>
+struct BwLds {
+    static constexpr int KP = DK + 1;
+    static constexpr int HP = BW_BV + 1;
+    static constexpr size_t k = 0;                                   // K [C][KP]
+    static constexpr size_t q = k + (size_t)BW_C * KP;               // scale Q
+    static constexpr size_t w = q + (size_t)BW_C * KP;               // W
+    static constexpr size_t tm = w + (size_t)BW_C * KP;              // T [C][CP]
+    static constexpr size_t gm = tm + (size_t)BW_C * BW_CP;          // K K^T * Gamma, strictly lower
+    static constexpr size_t mm = gm + (size_t)BW_C * BW_CP;          // M
+    static constexpr size_t dt = mm + (size_t)BW_C * BW_CP;          // dT, later dA
+    static constexpr size_t dm = dt + (size_t)BW_C * BW_CP;          // dM, later E, Z, Dk
+    static constexpr size_t h = dm + (size_t)BW_C * BW_CP;           // h tile [DK][HP], later dW [C][KP]
+    static constexpr size_t dh = h + (size_t)DK * HP;                // dh' tile, later X / K dKB
+    static constexpr size_t v = dh + (size_t)DK * HP;                // V tile [C][VP]
+    static constexpr size_t dO = v + (size_t)BW_C * BW_VP;
+    static constexpr size_t dl = dO + (size_t)BW_C * BW_VP;          // Delta
+    static constexpr size_t dd = dl + (size_t)BW_C * BW_VP;          // dDelta
+    static constexpr size_t p1 = dd + (size_t)BW_C * BW_VP;          // row-sum scratch
+    static constexpr size_t p2 = p1 + (size_t)BW_C * BW_VP;
+    static constexpr size_t gc = p2 + (size_t)BW_C * BW_VP;
+    static constexpr size_t eg = gc + BW_C;
+    static constexpr size_t ed = eg + BW_C;
+    static constexpr size_t bt = ed + BW_C;
+    static constexpr size_t dgc = bt + BW_C;
+    static constexpr size_t dbt = dgc + BW_C;
+    static constexpr size_t red = dbt + BW_C;                         // [NT + 1]
+    static constexpr size_t floats = red + BW_NT + 1;
+    static constexpr size_t bytes = floats * sizeof(float);
+    static_assert((size_t)BW_C * KP <= (size_t)DK * HP, "dW / X fit the tile buffers");
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_chunk_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ H,
+    const float* __restrict__ dH, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+    float* __restrict__ dg, float* __restrict__ dbeta, int T_len, int Hqk, int Hv, int grp, float scale)
+{
+    using L = BwLds<DK>;
+    constexpr int KP = L::KP, HP = L::HP;
+    // accumulators of the [C, DK] gradients: thread tid owns column am = tid % DK of rows
+    // ar0, ar0 + RS, ... (RS = BW_NT / DK rows per pass, PE passes)
+    constexpr int RS = BW_NT / DK;
+    constexpr int PE = BW_C / RS;
+    static_assert(BW_NT % DK == 0 && BW_C % RS == 0, "accumulator layout");
+    extern __shared__ float lds[];
+    float* Ks = lds + L::k;
+    float* Qs = lds + L::q;
+    float* Ws = lds + L::w;
+    float* Tm = lds + L::tm;
+    float* Gs = lds + L::gm;
+    float* Ms = lds + L::mm;
+    float* dTs = lds + L::dt;
+    float* dMs = lds + L::dm;
+    float* hs = lds + L::h;
+    float* dhs = lds + L::dh;
+    float* Vs = lds + L::v;
+    float* dOs = lds + L::dO;
+    float* Ds = lds + L::dl;
+    float* dDs = lds + L::dd;
+    float* P1 = lds + L::p1;
+    float* P2 = lds + L::p2;
+    float* gcs = lds + L::gc;
+    float* egs = lds + L::eg;
+    float* eds = lds + L::ed;
+    float* bs = lds + L::bt;
+    float* dgcs = lds + L::dgc;
+    float* dbts = lds + L::dbt;
+    float* red = lds + L::red;
+
+    const int NT = (T_len + BW_C - 1) / BW_C;
+    const int ci = blockIdx.x % NT;
+    const int bi = blockIdx.x / NT;
+    const int i = bi % Hqk, b = bi / Hqk;
+    const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
+    const int tid = threadIdx.x;
+    const int am = tid % DK, ar0 = tid / DK;
+
+    for (int e = tid; e < BW_C * DK; e += BW_NT) {
+        const int r = e / DK, m = e % DK;
+        float kv = 0.f, qv = 0.f;
+        if (r < n) {
+            const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+            kv = to_f32(k[off]);
+            qv = to_f32(q[off]) * scale;
+        }
+        Ks[r * KP + m] = kv;
+        Qs[r * KP + m] = qv;
+    }
+    float aQ[PE], aK[PE];
+#pragma unroll
+    for (int p = 0; p < PE; ++p) aQ[p] = aK[p] = 0.f;
+
+#pragma unroll 1
+    for (int jj = 0; jj < grp; ++jj) {
+        const int j = i * grp + jj;
+        const size_t head = (size_t)b * Hv + j;
+        __syncthreads();   // the previous head is done with every buffer
+        if (tid < BW_C) {
+            const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+            gcs[tid] = tid < n ? g[off] : 0.f;
+            bs[tid] = tid < n ? beta[off] : 0.f;
+            dgcs[tid] = 0.f;
+            dbts[tid] = 0.f;
+        }
+        for (int e = tid; e < BW_C * BW_CP; e += BW_NT) {
+            dTs[e] = 0.f;
+            dMs[e] = 0.f;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+#pragma unroll 4
+            for (int r = 0; r < BW_C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        }
+        __syncthreads();
+        if (tid < BW_C) {
+            egs[tid] = expf(gcs[tid]);
+            eds[tid] = expf(gcs[BW_C - 1] - gcs[tid]);
+        }
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            float gg = 0.f, mm = 0.f;
+            if (s <= r) {
+                float kk = 0.f, qk = 0.f;
+#pragma unroll 4
+                for (int m = 0; m < DK; ++m) {
+                    kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
+                    qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
+                }
+                const float gam = expf(gcs[r] - gcs[s]);
+                mm = gam * qk;
+                if (s < r) gg = gam * kk;
+            }
+            Gs[r * BW_CP + s] = gg;
+            Ms[r * BW_CP + s] = mm;
+        }
+        __syncthreads();
+        // T = (I + diag(beta) G)^{-1}: column s by forward substitution, one thread per column
+        if (tid < BW_C) {
+            const int s = tid;
+#pragma unroll 4
+            for (int r = 0; r < BW_C; ++r) {
+                float x = r == s ? 1.f : 0.f;
+                if (r > s) {
+                    float acc = 0.f;
+#pragma unroll 4
+                    for (int u = s; u < r; ++u) acc = fmaf(Gs[r * BW_CP + u], Tm[u * BW_CP + s], acc);
+                    x = -bs[r] * acc;
+                }
+                Tm[r * BW_CP + s] = x;
+            }
+        }
+        __syncthreads();
+        // W = T diag(beta e^gc) K
+        for (int e = tid; e < BW_C * DK; e += BW_NT) {
+            const int r = e / DK, m = e % DK;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int u = 0; u <= r; ++u) acc = fmaf(Tm[r * BW_CP + u] * bs[u] * egs[u], Ks[u * KP + m], acc);
+            Ws[r * KP + m] = acc;
+        }
+        float aW[PE], aX[PE];
+#pragma unroll
+        for (int p = 0; p < PE; ++p) aW[p] = aX[p] = 0.f;
+        float dgl = 0.f;
+
+#pragma unroll 1
+        for (int c0 = 0; c0 < DV; c0 += BW_BV) {
+            __syncthreads();   // W written; the previous tile's row sums done
+            const float* hp = H + ((head * NT + ci) * DK) * DV + c0;
+            const float* dhp = dH + ((head * NT + ci) * DK) * DV + c0;
+            for (int e = tid; e < DK * BW_BV; e += BW_NT) {
+                const int m = e / BW_BV, c = e % BW_BV;
+                hs[m * HP + c] = hp[(size_t)m * DV + c];
+                dhs[m * HP + c] = dhp[(size_t)m * DV + c];
+            }
+            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+                const int r = e / BW_BV, c = e % BW_BV;
+                const size_t off = (((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c;
+                Vs[r * BW_VP + c] = r < n ? to_f32(v[off]) : 0.f;
+                dOs[r * BW_VP + c] = r < n ? to_f32(dout[off]) : 0.f;
+            }
+            __syncthreads();
+            // Delta = T (beta V) - W h;  dDelta = diag(ed) K dh' + M^T dO
+            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+                const int r = e / BW_BV, c = e % BW_BV;
+                float u = 0.f, wh = 0.f, kd = 0.f, md = 0.f;
+#pragma unroll 4
+                for (int s = 0; s <= r; ++s) u = fmaf(Tm[r * BW_CP + s] * bs[s], Vs[s * BW_VP + c], u);
+#pragma unroll 4
+                for (int m = 0; m < DK; ++m) {
+                    wh = fmaf(Ws[r * KP + m], hs[m * HP + c], wh);
+                    kd = fmaf(Ks[r * KP + m], dhs[m * HP + c], kd);
+                }
+#pragma unroll 4
+                for (int s = r; s < BW_C; ++s) md = fmaf(Ms[s * BW_CP + r], dOs[s * BW_VP + c], md);
+                Ds[r * BW_VP + c] = u - wh;
+                dDs[r * BW_VP + c] = fmaf(eds[r], kd, md);
+            }
+            for (int e = tid; e < DK * BW_BV; e += BW_NT) {
+                const int m = e / BW_BV, c = e % BW_BV;
+                dgl = fmaf(dhs[m * HP + c], hs[m * HP + c], dgl);
+            }
+            __syncthreads();
+            // dV = diag(beta) T^T dDelta (complete for this tile); row-sum terms of dbeta and dgc
+            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+                const int r = e / BW_BV, c = e % BW_BV;
+                float tdu = 0.f, qh = 0.f;
+#pragma unroll 4
+                for (int s = r; s < BW_C; ++s) tdu = fmaf(Tm[s * BW_CP + r], dDs[s * BW_VP + c], tdu);
+#pragma unroll 4
+                for (int m = 0; m < DK; ++m) qh = fmaf(Qs[r * KP + m], hs[m * HP + c], qh);
+                if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu);
+                P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu;
+                P2[r * BW_VP + c] = dOs[r * BW_VP + c] * qh;
+            }
+            // dT += dDelta (diag(beta) V)^T;  dM += dO Delta^T (lower incl)
+            for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+                const int r = e / BW_C, s = e % BW_C;
+                float x = 0.f, y = 0.f;
+#pragma unroll 4
+                for (int c = 0; c < BW_BV; ++c) {
+                    x = fmaf(dDs[r * BW_VP + c], Vs[s * BW_VP + c], x);
+                    y = fmaf(dOs[r * BW_VP + c], Ds[s * BW_VP + c], y);
+                }
+                dTs[r * BW_CP + s] += bs[s] * x;
+                if (s <= r) dMs[r * BW_CP + s] += y;
+            }
+            // dW -= dDelta h^T;  X += Delta dh'^T;  dQ += diag(e^gc) dO h^T
+#pragma unroll
+            for (int p = 0; p < PE; ++p) {
+                const int r = ar0 + p * RS, m = am;
+                float sw = 0.f, sx = 0.f, sq = 0.f;
+#pragma unroll 2
+                for (int c = 0; c < BW_BV; ++c) {
+                    sw = fmaf(dDs[r * BW_VP + c], hs[m * HP + c], sw);
+                    sx = fmaf(Ds[r * BW_VP + c], dhs[m * HP + c], sx);
+                    sq = fmaf(dOs[r * BW_VP + c], hs[m * HP + c], sq);
+                }
+                aW[p] -= sw;
+                aX[p] += sx;
+                aQ[p] = fmaf(egs[r], sq, aQ[p]);
+            }
+            __syncthreads();
+            if (tid < BW_C) {
+                float s1 = 0.f, s2 = 0.f;
+#pragma unroll 4
+                for (int c = 0; c < BW_BV; ++c) {
+                    s1 += P1[tid * BW_VP + c];
+                    s2 += P2[tid * BW_VP + c];
+                }
+                dbts[tid] += s1;
+                dgcs[tid] = fmaf(egs[tid], s2, dgcs[tid]);
+            }
+        }
+
+        // ---- the terms that need every column: dW, X, dM, dT are complete now
+        red[tid] = dgl;
+        __syncthreads();
+        float* dWs = hs;    // [C][KP]
+        float* Xs = dhs;    // [C][KP]
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int r = ar0 + p * RS, m = am;
+            dWs[r * KP + m] = aW[p];
+            Xs[r * KP + m] = aX[p];
+        }
+        if (tid == 0) {
+            float s = 0.f;
+#pragma unroll 4
+            for (int x = 0; x < BW_NT; ++x) s += red[x];
+            red[BW_NT] = egs[BW_C - 1] * s;   // e^gL <dh', h>
+        }
+        __syncthreads();
+        // h' = e^gL h + (diag(ed) K)^T Delta:  dK += diag(ed) X, dgc -= ed (K . X), dgL += sum of those
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int r = ar0 + p * RS, m = am;
+            aK[p] = fmaf(eds[r], Xs[r * KP + m], aK[p]);
+        }
+        if (tid < BW_C) {
+            const int r = tid;
+            float kx = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) kx = fmaf(Ks[r * KP + m], Xs[r * KP + m], kx);
+            const float ted = eds[r] * kx;
+            dgcs[r] -= ted;
+            P1[r] = ted;
+            // M = lower-incl(Q K^T * Gamma): dgc_r += sum_s dM_rs M_rs - sum_u dM_ur M_ur
+            float rs = 0.f, cs = 0.f;
+#pragma unroll 4
+            for (int s = 0; s <= r; ++s) rs = fmaf(dMs[r * BW_CP + s], Ms[r * BW_CP + s], rs);
+#pragma unroll 4
+            for (int u = r; u < BW_C; ++u) cs = fmaf(dMs[u * BW_CP + r], Ms[u * BW_CP + r], cs);
+            dgcs[r] += rs - cs;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float s = red[BW_NT];
+#pragma unroll 4
+            for (int r = 0; r < BW_C; ++r) s += P1[r];
+            red[BW_NT] = s;   // dgL
+        }
+        // E = dM * Gamma (lower incl)
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            dMs[r * BW_CP + s] = s <= r ? dMs[r * BW_CP + s] * expf(gcs[r] - gcs[s]) : 0.f;
+        }
+        __syncthreads();
+        // dQ += E K;  dK += E^T (scale Q);  dKB = T^T dW -> dK += diag(beta e^gc) dKB
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int r = ar0 + p * RS, m = am;
+            float eq = 0.f, ek = 0.f, kb = 0.f;
+#pragma unroll 2
+            for (int s = 0; s <= r; ++s) eq = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], eq);
+#pragma unroll 2
+            for (int u = r; u < BW_C; ++u) {
+                ek = fmaf(dMs[u * BW_CP + r], Qs[u * KP + m], ek);
+                kb = fmaf(Tm[u * BW_CP + r], dWs[u * KP + m], kb);
+            }
+            aQ[p] += eq;
+            aK[p] += ek + bs[r] * egs[r] * kb;
+            Xs[r * KP + m] = Ks[r * KP + m] * kb;   // for the row sums of K . dKB
+        }
+        // dT += dW (diag(beta e^gc) K)^T
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            float x = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) x = fmaf(dWs[r * KP + m], Ks[s * KP + m], x);
+            dTs[r * BW_CP + s] += bs[s] * egs[s] * x;
+        }
+        __syncthreads();
+        if (tid < BW_C) {
+            const int r = tid;
+            float kb = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) kb += Xs[r * KP + m];
+            dbts[r] = fmaf(egs[r], kb, dbts[r]);
+            dgcs[r] = fmaf(bs[r] * egs[r], kb, dgcs[r]);
+        }
+        // Z = dT T^T (into the dM buffer)
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            float z = 0.f;
+#pragma unroll 4
+            for (int u = 0; u <= s; ++u) z = fmaf(dTs[r * BW_CP + u], Tm[s * BW_CP + u], z);
+            dMs[r * BW_CP + s] = z;
+        }
+        __syncthreads();
+        // dA = strictly-lower(-T^T Z) (into the dT buffer)
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            float a = 0.f;
+            if (s < r) {
+#pragma unroll 4
+                for (int u = r; u < BW_C; ++u) a = fmaf(Tm[u * BW_CP + r], dMs[u * BW_CP + s], a);
+                a = -a;
+            }
+            dTs[r * BW_CP + s] = a;
+        }
+        __syncthreads();
+        // A = diag(beta) G:  dbeta_r += sum_s dA_rs G_rs;  dgc via Gamma;  Dk = dA beta_r Gamma
+        if (tid < BW_C) {
+            const int r = tid;
+            float rs = 0.f, cs = 0.f;
+#pragma unroll 4
+            for (int s = 0; s < r; ++s) rs = fmaf(dTs[r * BW_CP + s], Gs[r * BW_CP + s], rs);
+#pragma unroll 4
+            for (int u = r + 1; u < BW_C; ++u) cs = fmaf(dTs[u * BW_CP + r] * bs[u], Gs[u * BW_CP + r], cs);
+            dbts[r] += rs;
+            dgcs[r] += bs[r] * rs - cs;
+        }
+        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+            const int r = e / BW_C, s = e % BW_C;
+            dMs[r * BW_CP + s] = s < r ? dTs[r * BW_CP + s] * bs[r] * expf(gcs[r] - gcs[s]) : 0.f;
+        }
+        __syncthreads();
+        // dK += Dk K + Dk^T K
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int r = ar0 + p * RS, m = am;
+            float x = 0.f;
+#pragma unroll 2
+            for (int s = 0; s < r; ++s) x = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], x);
+#pragma unroll 2
+            for (int u = r + 1; u < BW_C; ++u) x = fmaf(dMs[u * BW_CP + r], Ks[u * KP + m], x);
+            aK[p] += x;
+        }
+        // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL)
+        if (tid == 0) {
+            float acc = red[BW_NT];
+            for (int r = BW_C - 1; r >= 0; --r) {
+                acc += dgcs[r];
+                if (r < n) {
+                    const size_t off = ((size_t)b * T_len + t0 + r) * Hv + j;
+                    dg[off] = acc;
+                    dbeta[off] = dbts[r];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PE; ++p) {
+        const int r = ar0 + p * RS, m = am;
+        if (r < n) {
+            const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+            dq[off] = from_f32<T>(scale * aQ[p]);
+            dk[off] = from_f32<T>(aK[p]);
+        }
+    }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
+{
+    const int NT = (a.T + BW_C - 1) / BW_C;
+    float* Hs = a.ws;
+    float* dHs = a.ws + (size_t)a.B * a.Hv * NT * DK * DV;
+    // 1. states entering every chunk (the float32 forward kernel, no output)
+    ChunkArgs f;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta; f.s0 = a.s0; f.sf = nullptr; f.o = nullptr;
+    f.B = a.B; f.T = a.T; f.Hqk = a.Hqk; f.Hv = a.Hv; f.dk = DK; f.dv = DV; f.chunk = BW_C;
+    f.dtype_bf16 = a.dtype_bf16; f.scale = a.scale; f.hst = Hs;
+    hipError_t e = launch_chunk_simt(f, st);
+    if (e != hipSuccess) return e;
+    const int grp = a.Hv / a.Hqk;
+    // 2. reverse state pass
+    {
+        using L = DhLds<DK>;
+        auto kern = bwd_dh_kernel<T, DK, DV>;
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BW_BV), dim3(BW_NT), L::bytes, st, (const T*)a.q,
+                           (const T*)a.k, a.g, a.beta, (const T*)a.dout, a.dsf, dHs, a.ds0, a.T, a.Hqk, a.Hv, grp,
+                           a.scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // 3. per-chunk gradients
+    {
+        using L = BwLds<DK>;
+        static_assert(L::bytes <= 160 * 1024, "LDS budget");
+        auto kern = bwd_chunk_kernel<T, DK, DV>;
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hqk * NT)), dim3(BW_NT), L::bytes, st,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, (const T*)a.dout, Hs, dHs,
+                           (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dg, a.dbeta, a.T, a.Hqk, a.Hv, grp, a.scale);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <typename T>
+hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st)
+{
+#define GDN_BWD_CASE(DK_, DV_) \
+    if (a.dk_ == DK_ && a.dv_ == DV_) return launch_bwd_t<T, DK_, DV_>(a, st);
+    GDN_BWD_CASE(32, 32) GDN_BWD_CASE(32, 64) GDN_BWD_CASE(32, 128)
+    GDN_BWD_CASE(64, 32) GDN_BWD_CASE(64, 64) GDN_BWD_CASE(64, 128)
+    GDN_BWD_CASE(128, 32) GDN_BWD_CASE(128, 64) GDN_BWD_CASE(128, 128)
+#undef GDN_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv)
+{
+    const size_t NT = ((size_t)T + BW_C - 1) / BW_C;
+    return 2 * (size_t)B * Hv * NT * dk * dv * sizeof(float);
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st)
+{
+    return a.dtype_bf16 ? launch_bwd_dt<bf16>(a, st) : launch_bwd_dt<float>(a, st);
+}
+
+}  // namespace gdn

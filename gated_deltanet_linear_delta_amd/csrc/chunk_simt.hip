@@ -53,8 +53,9 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
-    T* __restrict__ o, int T_len, int Hqk, int Hv, int grp, int C,
-    float scale)
+    T* __restrict__ o,           // may be null (states only)
+    float* __restrict__ hst,     // null, or [B, Hv, NT, DK, DV]: the state entering every chunk
+    int T_len, int Hqk, int Hv, int grp, int C, float scale)
 {
     using L = SimtLds<DK, BV>;
     extern __shared__ float lds[];
@@ -87,6 +88,11 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     for (int t0 = 0; t0 < T_len; t0 += C) {
         const int n = min(C, T_len - t0);
         __syncthreads();  // previous chunk finished with every LDS buffer
+        if (hst) {
+            const int NT = (T_len + C - 1) / C;
+            float* hp = hst + ((size_t)head * NT + t0 / C) * DK * DV + c0;
+            for (int e = tid; e < DK * BV; e += SIMT_NT) hp[(size_t)(e / BV) * DV + e % BV] = hs[e];
+        }
         for (int e = tid; e < C * DK; e += SIMT_NT) {
             const int r = e / DK, m = e % DK;
             float kv = 0.f, qv = 0.f;
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
                 const int r = e / BV, c = e % BV;
                 float acc = qh[p];
                 for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
-                if (r < n) o[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
+                if (o && r < n) o[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
             }
         }
         // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T
@@ -204,7 +210,7 @@ static hipError_t launch_simt_t(const ChunkArgs& a, hipStream_t st)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BV), dim3(SIMT_NT), L::bytes, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, a.s0, a.sf,
-                       (T*)a.o, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale);
+                       (T*)a.o, a.hst, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale);
     return hipGetLastError();
 }
 

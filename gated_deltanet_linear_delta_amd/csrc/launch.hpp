@@ -38,6 +38,9 @@ struct ChunkArgs {
     int norm_w_stride = 0;
     float eps = 0.f;
     void* y = nullptr;
+    // float32-vector path only: when set, the state entering every chunk is stored here
+    // ([B, Hv, NT, dk, dv], NT = ceil(T / chunk)); o may then be null
+    float* hst = nullptr;
 };
 
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
@@ -57,6 +60,31 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, void* workspace, hipStream_t st
 
 // final_state <- initial_state (or zeros when it is null), for T == 0.
 hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st);
+
+// Backward pass (chunk_bwd.hip): gradients through O and the final state.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* s0;     // may be null (zero initial state)
+    const void* dout;    // dL/dO, dtype of q
+    const float* dsf;    // dL/d(final state) or null (zero)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;
+    float* dbeta;
+    float* ds0;          // may be null (not wanted)
+    float* ws;           // chunk_bwd_workspace_bytes
+    int B, T, Hqk, Hv, dk_, dv_;
+    bool dtype_bf16;
+    float scale;
+};
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv);
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 
 // Layer steps around the recurrence (layer_ops.hip).
 struct PrologueArgs {

@@ -221,6 +221,41 @@ gdn_status_t gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, co
                                  gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/*
+ * gdn_chunk_bwd_workspace_bytes -- device scratch (bytes) that gdn_chunk_bwd needs: the state
+ * entering every 32-token chunk and the gradient of the state leaving it, float32,
+ * 2 * B * Hv * ceil(T / 32) * dk * dv * 4 bytes.  Pure host function; 0 for invalid sizes.
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, gdn_dtype_t dtype);
+
+/*
+ * gdn_chunk_bwd -- backward pass of gdn_chunk_fwd: the gradients of a loss L through O and the
+ * final state, with respect to q, k, v, g, beta and the initial state.  Computed chunkwise by
+ * reversing the forward chunk steps ("Gated Attention Architectures", section 3, names chunkwise
+ * hardware-efficient training for Gated DeltaNet): the states entering every chunk are
+ * recomputed, a reverse pass carries dL/dh from the last chunk to the first, and every chunk's
+ * gradients then follow in parallel.  The result equals the gradient of the token-by-token
+ * recurrence up to rounding; it does not depend on the forward call's chunk size.
+ *
+ *   q, k, v, g, beta, initial_state, sizes, dtype, scale: as gdn_chunk_fwd (inputs)
+ *   grad_o            [B, T, Hv, dv] dtype: dL/dO
+ *   grad_final_state  [B, Hv, dk, dv] float32 dL/d(final state), or NULL for zero
+ *   grad_q, grad_k    [B, T, Hqk, dk] dtype outputs (a query/key head's gradient sums over the
+ *                     value heads of its group)
+ *   grad_v            [B, T, Hv, dv] dtype output
+ *   grad_g, grad_beta [B, T, Hv] float32 outputs (g = log alpha)
+ *   grad_initial_state [B, Hv, dk, dv] float32 output, or NULL to skip
+ *   workspace         at least gdn_chunk_bwd_workspace_bytes(...) bytes, 16-byte aligned
+ * Outputs may not overlap any input, each other or the workspace.  Every output element is
+ * written exactly once (no atomics): the result is deterministic.  B == 0 is a no-op; T == 0
+ * writes grad_initial_state only (= grad_final_state, or zeros).  Errors as gdn_chunk_fwd.
+ */
+gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const float* initial_state, const void* grad_o, const float* grad_final_state,
+                           void* grad_q, void* grad_k, void* grad_v, float* grad_g, float* grad_beta,
+                           float* grad_initial_state, int B, int T, int Hqk, int Hv, int dk, int dv,
+                           gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

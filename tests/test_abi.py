@@ -292,3 +292,54 @@ def test_chunk_fwd_gated_valid_calls_report_no_device():
     assert gated_call(sf=fake(5)) == NODEV                        # in-place final state
     assert gated_call(T=0, q=None, z=None, y=None, ws=None, wsb=0) == NODEV
     assert gated_call(per_head=1, s0=None, sf=None) == NODEV
+
+
+# ------------------------------------------------------------------------------ backward
+
+BWD_WS = 2 * 2 * 4 * 4 * 64 * 32 * 4     # 2 x B * Hv * ceil(100 / 32) * dk * dv * 4
+
+
+def bwd_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), do=fake(6), dsf=fake(7),
+             dq=fake(8), dk=fake(9), dv=fake(10), dg=fake(11), dbeta=fake(12), ds0=fake(13), B=2, T=100, Hqk=2,
+             Hv=4, dk_=64, dv_=32, dtype=gdn.GDN_BF16, scale=1.0, ws=fake(14), wsb=BWD_WS, stream=None)
+    a.update(over)
+    return lib.gdn_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["do"], a["dsf"], a["dq"], a["dk"],
+                             a["dv"], a["dg"], a["dbeta"], a["ds0"], a["B"], a["T"], a["Hqk"], a["Hv"], a["dk_"],
+                             a["dv_"], a["dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_bwd_workspace_size():
+    assert gdn.gdn_chunk_bwd_workspace_bytes(2, 100, 2, 4, 64, 32, gdn.GDN_BF16) == BWD_WS
+    assert gdn.gdn_chunk_bwd_workspace_bytes(1, 4096, 16, 32, 128, 128, gdn.GDN_BF16) == 2 * 32 * 128 * 128 * 128 * 4
+    assert gdn.gdn_chunk_bwd_workspace_bytes(1, 0, 16, 32, 128, 128, gdn.GDN_BF16) == 0
+    assert gdn.gdn_chunk_bwd_workspace_bytes(1, 64, 16, 33, 128, 128, gdn.GDN_BF16) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), NULL), (dict(do=None), NULL), (dict(dq=None), NULL), (dict(dg=None), NULL),
+    (dict(dbeta=None), NULL), (dict(ws=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hv=3), SHAPE), (dict(T=-2), SHAPE),
+    (dict(dk_=48), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(wsb=BWD_WS - 1), WS),
+    (dict(do=ctypes.c_void_p(BASE + 6 * STRIDE + 8)), ALIGN), (dict(dq=ctypes.c_void_p(BASE + 8 * STRIDE + 4)), ALIGN),
+    (dict(dg=ctypes.c_void_p(BASE + 11 * STRIDE + 2)), ALIGN), (dict(ws=ctypes.c_void_p(BASE + 14 * STRIDE + 8)), ALIGN),
+    (dict(dq=fake(0)), ALIAS), (dict(dv=fake(6)), ALIAS), (dict(ds0=fake(5)), ALIAS), (dict(ds0=fake(7)), ALIAS),
+    (dict(dk=fake(8)), ALIAS), (dict(ws=fake(13)), ALIAS),
+    (dict(dbeta=ctypes.c_void_p(BASE + 11 * STRIDE + 64)), ALIAS),        # runs into dg
+])
+def test_chunk_bwd_rejects(over, status):
+    assert bwd_call(**over) == status
+
+
+def test_chunk_bwd_noops():
+    assert bwd_call(B=0, q=None, do=None, dq=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_chunk_bwd_valid_calls_report_no_device():
+    assert bwd_call() == NODEV
+    assert bwd_call(s0=None, dsf=None, ds0=None) == NODEV
+    assert bwd_call(T=0, q=None, do=None, dq=None, dg=None, ws=None, wsb=0) == NODEV
+    assert bwd_call(dtype=gdn.GDN_F32) == NODEV
