@@ -19,7 +19,9 @@ The same JSON line carries
   layer_ops     -- the layer steps either side of the recurrence at the headline shape (short
                    conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth;
   gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
-                   call) on the headline and the batched workloads.
+                   call) on the headline and the batched workloads;
+  backward      -- gdn_chunk_bwd (gradients of q, k, v, g, beta, S0) at the headline shape:
+                   tokens/s and the fraction of the float32 vector peak it reaches.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
 """
@@ -56,6 +58,18 @@ def prefill_alg_flops(B, T, Hqk, Hv, dk, dv, C):
     + 2 C dk / G (K K^T, Q K^T shared by the G value heads of a group) + C^2 / 3 (the solve)."""
     G = Hv // Hqk
     per = 6 * dk * dv + C * dk + 2 * C * dv + 2 * C * dk / G + C * C / 3
+    return per * B * T * Hv
+
+
+FP32_VALU_PEAK = 157.3e12   # flop/s, MI355X float32 vector units
+
+
+def backward_alg_flops(B, T, Hqk, Hv, dk, dv, C=32):
+    """Flops of the chunkwise backward as computed (chunks of C = 32; the states are recomputed,
+    not kept from the forward), per token and value head: the state recompute
+    4 dk dv + C (dk + dv); the reverse state pass 6 dk dv + 2 C (dk + dv); the per-chunk
+    gradients 12 dk dv + 6 C dv + 9 C dk + 7 C^2 / 3 (T, and dT's two triangular products)."""
+    per = 22 * dk * dv + 9 * C * dv + 12 * C * dk + 7 * C * C / 3
     return per * B * T * Hv
 
 
@@ -235,6 +249,32 @@ def bench_layer_ops(cfg, torch, gdn, W=4, steps=20, warmup=3, min_bytes=640 << 2
                               "hbm_frac": rms_bytes / kr / HBM_PEAK}}
 
 
+def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
+    """gdn_chunk_bwd at the workload's shape: dL/dO ~ N(0,1), dL/dS_final ~ 0.1 N(0,1)."""
+    import gdn_inputs as gi
+    dev = "cuda:0"
+    x = gi.generate_torch(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 41)
+    do = torch.randn((cfg.B, cfg.T, cfg.Hv, cfg.dv), generator=gen, device=dev).to(x["q"].dtype)
+    dsf = 0.1 * torch.randn((cfg.B, cfg.Hv, cfg.dk, cfg.dv), generator=gen, device=dev)
+    dt = gdn.GDN_BF16 if cfg.dtype == "bf16" else gdn.GDN_F32
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, dt),
+                     dtype=torch.uint8, device=dev)
+
+    def fn(i):
+        gdn.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["s0"], dsf, workspace=ws)
+
+    _, kern = time_launches(fn, 1, steps, warmup, torch)
+    flops = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv)
+    del x, do, dsf, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "tokens_per_s": cfg.B * cfg.T / kern, "kernel_ms": kern * 1e3,
+            "alg_flops": flops, "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12,
+            "peak_TFLOPs": FP32_VALU_PEAK / 1e12, "frac": flops / kern / FP32_VALU_PEAK,
+            "kernels": "chunk_simt_kernel (states) + bwd_dh_kernel + bwd_chunk_kernel"}
+
+
 def cpu_baseline(cfg, gi, min_seconds=10.0, max_repeats=30):
     """The float64 oracle on the same workload (whole batch), repeated until about min_seconds."""
     import numpy as np
@@ -352,6 +392,8 @@ def main():
                         "route": "norm fused into the prefill kernel" if fused
                         else "O through the workspace, then the norm kernel"}
         line["gated_prefill"] = gp
+        print(f"bench: backward {cfg}", file=sys.stderr, flush=True)
+        line["backward"] = bench_backward(cfg, torch, gdn)
     print(json.dumps(line), flush=True)
 
 
