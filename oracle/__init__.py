@@ -14,6 +14,9 @@ may import this package.  Nothing here is shared with the HIP library, and nothi
   (numpy), for tiny inputs; an independent code path used to pin :func:`recurrent`.
 * :func:`chunked` -- the chunkwise (WY / UT-transform) refactoring of the same recurrence in
   numpy float64, used to pin the chunk algebra the GPU implements.
+* :func:`kda_recurrent` (C), :func:`kda_brute_force`, :func:`kda_chunked` (numpy) -- Kimi Delta
+  Attention, the delta rule with one decay per key channel ("Gated Attention Architectures",
+  section 8): the definition, its dense transition matrices, and its chunkwise form.
 * :func:`qkv_prologue`, :func:`gated_rmsnorm` (module ``layer_ops``) -- the layer steps either
   side of the recurrence: short causal conv, SiLU and q/k L2 norm; gated RMSNorm of the output.
 
@@ -30,7 +33,7 @@ from . import build as _build
 
 from .layer_ops import gated_rmsnorm, qkv_prologue, silu
 
-__all__ = ["recurrent", "recurrent_bwd", "decode", "brute_force", "chunked", "chunked_bwd", "max_threads",
+__all__ = ["kda_recurrent", "kda_brute_force", "kda_chunked", "recurrent", "recurrent_bwd", "decode", "brute_force", "chunked", "chunked_bwd", "max_threads",
            "load", "qkv_prologue", "gated_rmsnorm", "silu"]
 
 _lib = None
@@ -48,6 +51,8 @@ def load():
         lib.gdn_oracle_max_threads.restype = ctypes.c_int
         lib.gdn_oracle_recurrent_bwd.argtypes = [dp] * 14 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
         lib.gdn_oracle_recurrent_bwd.restype = ctypes.c_int
+        lib.gdn_oracle_kda_recurrent.argtypes = [dp] * 8 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+        lib.gdn_oracle_kda_recurrent.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -320,3 +325,89 @@ def chunked_bwd(q, k, v, g, beta, s0, do, dsf=None, chunk: int = 64, scale: floa
                 dh = dh_prev
             out["ds0"][b, j] = dh
     return out
+
+
+def kda_recurrent(q, k, v, g, beta, s0=None, scale: float = 1.0, threads: int = 0):
+    """Kimi Delta Attention, token by token (C, float64): S_t = (I - beta_t k_t k_t^T) D_t S_{t-1}
+    + beta_t v_t k_t^T, o_t = S_t^T q_t with D_t = diag(exp(g_t)) over the key channels
+    ("Gated Attention Architectures", section 8, Mathematical Formulation); S stored [dk, dv].
+
+    q, k: [B,T,Hqk,dk]; v: [B,T,Hv,dv]; g = log alpha: [B,T,Hv,dk]; beta: [B,T,Hv];
+    s0: [B,Hv,dk,dv] or None.  Returns (o [B,T,Hv,dv], s_final [B,Hv,dk,dv])."""
+    q, k, v, g, beta, s0 = map(_f64, (q, k, v, g, beta, s0))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    assert g.shape == (B, T, Hv, dk) and beta.shape == (B, T, Hv)
+    o = np.empty((B, T, Hv, dv))
+    sf = np.empty((B, Hv, dk, dv))
+    rc = load().gdn_oracle_kda_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(o),
+                                         _ptr(sf), B, T, Hqk, Hv, dk, dv, float(scale), int(threads))
+    if rc != 0:
+        raise ValueError("oracle rejected the sizes")
+    return o, sf
+
+
+def kda_brute_force(q, k, v, g, beta, s0=None, scale: float = 1.0):
+    """The KDA equation with its transition written out densely (numpy, tiny T only):
+    S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T, S in R^{dk x dv}."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    o = np.zeros((B, T, Hv, dv))
+    sf = np.zeros((B, Hv, dk, dv))
+    for b in range(B):
+        for j in range(Hv):
+            i = j // grp
+            S = np.zeros((dk, dv)) if s0 is None else np.array(s0[b, j], dtype=np.float64)
+            for t in range(T):
+                kt = k[b, t, i][:, None]
+                P = np.eye(dk) - beta[b, t, j] * (kt @ kt.T)
+                S = P @ np.diag(np.exp(g[b, t, j])) @ S + beta[b, t, j] * (kt @ v[b, t, j][None, :])
+                o[b, t, j] = S.T @ (scale * q[b, t, i])
+            sf[b, j] = S
+    return o, sf
+
+
+def kda_chunked(q, k, v, g, beta, s0=None, chunk: int = 32, scale: float = 1.0):
+    """Chunkwise form of KDA (numpy float64), derived from the recurrence: with gc the in-chunk
+    cumulative log decay per key channel (gc_r = g_1 + ... + g_r, a vector) and
+    E_ri = exp(gc_r - gc_i) for i <= r (elementwise over channels, never above 1):
+
+      A     = strictly-lower( beta_r sum_c k_rc k_ic E_ric )
+      Delta = (I + A)^{-1} ( diag(beta) V - diag(beta) (e^gc * K) h0 )
+      O     = (e^gc * scale Q) h0 + lower-incl( sum_c q_rc k_ic E_ric ) Delta
+      h1    = diag(e^gL) h0 + ((e^(gL - gc) * K))^T Delta,   gL the chunk's last gc
+
+    ("Gated Attention Architectures", section 8, names a chunkwise WY-based algorithm for KDA;
+    the pairwise decays are formed from differences so nothing overflows.)  The solve is
+    numpy.linalg.solve."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    grp = Hv // Hqk
+    o = np.zeros((B, T, Hv, dv))
+    sf = np.zeros((B, Hv, dk, dv))
+    for b in range(B):
+        for j in range(Hv):
+            i = j // grp
+            h = np.zeros((dk, dv)) if s0 is None else np.array(s0[b, j], dtype=np.float64)
+            for c0 in range(0, T, chunk):
+                c1 = min(T, c0 + chunk)
+                n = c1 - c0
+                K = k[b, c0:c1, i]
+                Q = scale * q[b, c0:c1, i]
+                V = v[b, c0:c1, j]
+                bt = beta[b, c0:c1, j]
+                gc = np.cumsum(g[b, c0:c1, j], axis=0)                 # [n, dk]
+                diff = gc[:, None, :] - gc[None, :, :]                  # [n, n, dk]
+                E = np.exp(np.where(np.tril(np.ones((n, n)))[:, :, None] > 0, diff, -np.inf))
+                A = np.tril(bt[:, None] * np.einsum("rc,ic,ric->ri", K, K, E), -1)
+                Aqk = np.tril(np.einsum("rc,ic,ric->ri", Q, K, E))
+                rhs = bt[:, None] * V - bt[:, None] * ((np.exp(gc) * K) @ h)
+                Delta = np.linalg.solve(np.eye(n) + A, rhs)
+                o[b, c0:c1, j] = (np.exp(gc) * Q) @ h + Aqk @ Delta
+                gL = gc[-1]
+                h = np.exp(gL)[:, None] * h + (np.exp(gL[None, :] - gc) * K).T @ Delta
+            sf[b, j] = h
+    return o, sf
