@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/gdn.h):
 * :func:`gdn_gated_rmsnorm` -- RMSNorm of the output times SiLU of the gate.
 * :func:`gdn_chunk_fwd_gated` -- prefill followed by the gated RMSNorm (fused where it can be).
 * :func:`gdn_chunk_bwd` -- backward pass of the prefill (gradients of q, k, v, g, beta, S0).
+* :func:`gdn_kda_chunk_fwd` -- Kimi Delta Attention prefill (one decay per key channel).
 * :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_gated_workspace_bytes`,
   :func:`gdn_chunk_fwd_kernel_name`, :func:`gdn_status_string`.
 """
@@ -25,7 +26,8 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GdnError", "library_path", "load_library", "gdn_chunk_fwd",
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
     "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
-    "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
+    "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
@@ -33,7 +35,7 @@ GDN_BF16 = 1
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
                     "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
-                    "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes")
+                    "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -82,6 +84,8 @@ def load_library():
     lib.gdn_chunk_bwd.restype = i
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 6 + [i]
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn_kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp]
+    lib.gdn_kda_chunk_fwd.restype = i
     _lib = lib
     return lib
 
@@ -342,3 +346,35 @@ def gdn_chunk_bwd(q, k, v, g, beta, grad_o, initial_state=None, grad_final_state
     if st != 0:
         raise GdnError(st, "gdn_chunk_bwd")
     return out
+
+
+def gdn_kda_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=32, scale=1.0,
+                      o=None, final_state=None, stream=None):
+    """Kimi Delta Attention prefill.  q, k [B,T,Hqk,dk]; v [B,T,Hv,dv] (bf16 or f32, all alike);
+    g [B,T,Hv,dk] float32 (log decay per key channel); beta [B,T,Hv] float32; initial_state
+    [B,Hv,dk,dv] float32 or None.  Returns (o [B,T,Hv,dv], final_state or None)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv, dk), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("o", o, (B, T, Hv, dv), q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    st = lib.gdn_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                               _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), _dtype_code(q),
+                               float(scale), _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_kda_chunk_fwd")
+    return o, final_state

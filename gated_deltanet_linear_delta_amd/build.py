@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip", "kda.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 instructions are kept out of the generated code (plain float code only).

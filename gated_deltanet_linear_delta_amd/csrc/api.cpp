@@ -296,6 +296,53 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
     return gdn::launch_chunk_bwd(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
+                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* stream)
+{
+    if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
+    if (Hv % Hqk != 0) return GDN_ERR_SHAPE;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || (chunk != 16 && chunk != 32) || !dtype_ok(dtype))
+        return GDN_ERR_UNSUPPORTED;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = work ? (size_t)B * T : 0;
+    const size_t sbytes = (size_t)B * Hv * dk * dv * sizeof(float);
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * dk * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rs0 = range(initial_state, initial_state ? sbytes : 0);
+    const Range rsf = range(final_state, final_state ? sbytes : 0);
+    const Range ro = range(o, ntok * Hv * dv * es);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rs0};
+    for (const Range& r : inputs)
+        if (overlap(ro, r) || overlap(rsf, r)) {
+            if (&r == &inputs[5] && final_state == initial_state && !overlap(ro, r)) continue;
+            return GDN_ERR_ALIAS;
+        }
+    if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    gdn_status_t s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        if (!final_state) return GDN_OK;
+        return gdn::launch_state_copy(initial_state, final_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    gdn::KdaArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.s0 = initial_state; a.sf = final_state; a.o = o;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.dtype_bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    return gdn::launch_kda_chunk(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, float* state, void* o, int B, int Hqk, int Hv,
                                 int dk, int dv, gdn_dtype_t dtype, float scale, void* stream)

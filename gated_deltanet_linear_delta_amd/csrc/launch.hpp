@@ -86,6 +86,23 @@ struct BwdArgs {
 size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv);
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 
+// Kimi Delta Attention prefill (kda.hip): g is [B, T, Hv, dk] (one log decay per key channel).
+struct KdaArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* s0;   // may be null
+    float* sf;         // may be null; may equal s0
+    void* o;
+    int B, T, Hqk, Hv, dk, dv, chunk;
+    bool dtype_bf16;
+    float scale;
+};
+
+hipError_t launch_kda_chunk(const KdaArgs& a, hipStream_t st);
+
 // Layer steps around the recurrence (layer_ops.hip).
 struct PrologueArgs {
     const void* q_in;

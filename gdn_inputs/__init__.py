@@ -64,6 +64,10 @@ CONFIGS = {
                                   dv=128, chunk=64, dtype="bf16", mu=4.0, s0_std=0.0, seed=1004),
     "decode": Config("decode", B=256, T=1, Hqk=16, Hv=32, dk=128, dv=128, chunk=64,
                      dtype="bf16", mu=3.0, s0_std=0.02, seed=1005, steps=64),
+    # Kimi Delta Attention (per-key-channel decay; inputs from generate_kda): the Qwen3-Next
+    # layer's size with as many query/key heads as value heads
+    "kda_prefill": Config("kda_prefill", B=1, T=4096, Hqk=32, Hv=32, dk=128, dv=128, chunk=32,
+                          dtype="bf16", mu=3.0, s0_std=0.0, seed=1006),
 }
 
 
@@ -146,6 +150,18 @@ def generate_gate(B, T, Hv, dv, dtype="bf16", seed=3001, w_per_head=False) -> di
     z = rng.standard_normal((B, T, Hv, dv), dtype=f)
     w = (1.0 + 0.1 * rng.standard_normal((Hv, dv) if w_per_head else (dv,))).astype(f)
     return dict(z=_store(z, dtype), weight=w)
+
+
+def generate_kda(B, T, Hqk, Hv, dk, dv, dtype="bf16", mu=3.0, s0_std=0.0, seed=4001) -> dict:
+    """Kimi Delta Attention inputs: q, k, v, beta and S0 as :func:`generate` (same draws and
+    order), then g = log alpha per key channel [B,T,Hv,dk] = logsigmoid(N(mu + m_c, 1)) with a
+    per-(head, channel) offset m_c ~ N(0, 1) drawn once, so channels decay at different rates."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d = _draw(rng, (), B, T, Hqk, Hv, dk, dv, dtype, mu, s0_std)
+    off = rng.standard_normal((Hv, dk))
+    x = rng.standard_normal((B, T, Hv, dk)) + mu + off[None, None]
+    d["g"] = (-np.logaddexp(0.0, -x)).astype(np.float32)
+    return d
 
 
 def to_torch(x: np.ndarray | None, dtype: str, device):

@@ -256,6 +256,29 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            float* grad_initial_state, int B, int T, int Hqk, int Hv, int dk, int dv,
                            gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gdn_kda_chunk_fwd -- Kimi Delta Attention prefill: the delta rule with one decay per key
+ * channel ("Gated Attention Architectures", section 8, Mathematical Formulation),
+ *     S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t v_t k_t^T,   o_t = S_t^T (scale q_t),
+ *     D_t = diag(exp(g_t)) over the dk key channels,
+ * with S in R^{dk x dv} stored [B, Hv, dk, dv] (the layout of gdn_chunk_fwd's state).  With the
+ * same decay on every channel of a head this is gdn_chunk_fwd's recurrence.  Computed
+ * chunkwise: per chunk the pairwise decays exp(gc_r - gc_i) (per channel, from differences of
+ * the in-chunk cumulative log decay) weight the K K^T and Q K^T products, (I + A)^{-1} is applied
+ * by forward substitution, and the state is carried across chunks in float32.
+ *
+ *   q, k           [B, T, Hqk, dk]  dtype
+ *   v              [B, T, Hv, dv]   dtype
+ *   g              [B, T, Hv, dk]   float32, log alpha per key channel (<= 0 for a decay)
+ *   beta           [B, T, Hv]       float32
+ *   initial_state, final_state, o, scale, stream: as gdn_chunk_fwd
+ *   chunk          16 or 32.  dk, dv 32, 64 or 128.
+ * No workspace.  B == 0 is a no-op; T == 0 writes final_state only.  Errors as gdn_chunk_fwd.
+ */
+gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
+                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

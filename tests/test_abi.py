@@ -343,3 +343,39 @@ def test_chunk_bwd_valid_calls_report_no_device():
     assert bwd_call(s0=None, dsf=None, ds0=None) == NODEV
     assert bwd_call(T=0, q=None, do=None, dq=None, dg=None, ws=None, wsb=0) == NODEV
     assert bwd_call(dtype=gdn.GDN_F32) == NODEV
+
+
+# ------------------------------------------------------------------- Kimi Delta Attention
+
+def kda_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), o=fake(7),
+             B=2, T=100, Hqk=2, Hv=4, dk_=64, dv_=32, chunk=32, dtype=gdn.GDN_BF16, scale=1.0, stream=None)
+    a.update(over)
+    return lib.gdn_kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["o"], a["B"],
+                                 a["T"], a["Hqk"], a["Hv"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], a["scale"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), NULL), (dict(g=None), NULL), (dict(o=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hv=3), SHAPE), (dict(chunk=0), SHAPE),
+    (dict(chunk=64), UNSUP), (dict(chunk=8), UNSUP), (dict(dk_=96), UNSUP), (dict(dtype=4), UNSUP),
+    (dict(q=ctypes.c_void_p(BASE + 8)), ALIGN), (dict(g=ctypes.c_void_p(BASE + 3 * STRIDE + 2)), ALIGN),
+    (dict(o=fake(3)), ALIAS), (dict(o=ctypes.c_void_p(BASE + 3 * STRIDE + 4096)), ALIAS),   # runs into g
+    (dict(sf=fake(7)), ALIAS), (dict(sf=ctypes.c_void_p(BASE + 5 * STRIDE + 256)), ALIAS),
+])
+def test_kda_rejects(over, status):
+    assert kda_call(**over) == status
+
+
+def test_kda_noops():
+    assert kda_call(B=0, q=None, o=None) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_kda_valid_calls_report_no_device():
+    assert kda_call() == NODEV
+    assert kda_call(sf=fake(5)) == NODEV
+    assert kda_call(T=0, q=None, o=None) == NODEV
+    assert kda_call(chunk=16, dtype=gdn.GDN_F32) == NODEV
