@@ -21,7 +21,9 @@ The same JSON line carries
   gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
                    call) on the headline and the batched workloads;
   backward      -- gdn_chunk_bwd (gradients of q, k, v, g, beta, S0) at the headline shape:
-                   tokens/s and the fraction of the float32 vector peak it reaches.
+                   tokens/s and the fraction of the float32 vector peak it reaches;
+  kda           -- gdn_kda_chunk_fwd (Kimi Delta Attention, per-key-channel decay) on the KDA
+                   workload (B1 T4096, 32/32 heads, d128): tokens/s and float32-vector fraction.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
 """
@@ -70,6 +72,15 @@ def backward_alg_flops(B, T, Hqk, Hv, dk, dv, C=32):
     4 dk dv + C (dk + dv); the reverse state pass 6 dk dv + 2 C (dk + dv); the per-chunk
     gradients 12 dk dv + 6 C dv + 9 C dk + 7 C^2 / 3 (T, and dT's two triangular products)."""
     per = 22 * dk * dv + 9 * C * dv + 12 * C * dk + 7 * C * C / 3
+    return per * B * T * Hv
+
+
+def kda_alg_flops(B, T, Hqk, Hv, dk, dv, C=32):
+    """Flops of the chunkwise KDA forward per token and value head: the state products
+    (e^gc K) h0, (e^gc Q) h0 and the state update, 6 dk dv; the decay-weighted K K^T and Q K^T
+    over the lower triangle, 2 C dk multiply-adds plus C dk exponentials (each counted once);
+    the solve and the output product, 2 C dv."""
+    per = 6 * dk * dv + 3 * C * dk + 2 * C * dv
     return per * B * T * Hv
 
 
@@ -275,6 +286,35 @@ def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
             "kernels": "chunk_simt_kernel (states) + bwd_dh_kernel + bwd_chunk_kernel"}
 
 
+def bench_kda(cfg, torch, gdn, steps=10, warmup=2):
+    """gdn_kda_chunk_fwd on the KDA workload (inputs drawn on the device with the recipe of
+    gdn_inputs.generate_kda: per-channel log gates logsigmoid(N(mu + offset, 1)))."""
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, T, Hqk, Hv, dk, dv = cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev)
+    q = torch.nn.functional.normalize(rnd(B, T, Hqk, dk), dim=-1).to(dt)
+    k = torch.nn.functional.normalize(rnd(B, T, Hqk, dk), dim=-1).to(dt)
+    v = rnd(B, T, Hv, dv).to(dt)
+    beta = torch.sigmoid(rnd(B, T, Hv))
+    g = torch.nn.functional.logsigmoid(rnd(B, T, Hv, dk) + cfg.mu + rnd(1, 1, Hv, dk))
+    o = torch.empty((B, T, Hv, dv), dtype=dt, device=dev)
+    sf = torch.empty((B, Hv, dk, dv), device=dev)
+
+    def fn(i):
+        gdn.gdn_kda_chunk_fwd(q, k, v, g, beta, None, chunk=cfg.chunk, o=o, final_state=sf)
+
+    _, kern = time_launches(fn, 1, steps, warmup, torch)
+    flops = kda_alg_flops(B, T, Hqk, Hv, dk, dv, cfg.chunk)
+    del q, k, v, beta, g, o, sf
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "tokens_per_s": B * T / kern, "kernel_ms": kern * 1e3, "alg_flops": flops,
+            "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12, "peak_TFLOPs": FP32_VALU_PEAK / 1e12,
+            "frac": flops / kern / FP32_VALU_PEAK, "kernel": "kda_chunk_kernel"}
+
+
 def cpu_baseline(cfg, gi, min_seconds=10.0, max_repeats=30):
     """The float64 oracle on the same workload (whole batch), repeated until about min_seconds."""
     import numpy as np
@@ -394,6 +434,9 @@ def main():
         line["gated_prefill"] = gp
         print(f"bench: backward {cfg}", file=sys.stderr, flush=True)
         line["backward"] = bench_backward(cfg, torch, gdn)
+        kcfg = gi.CONFIGS["kda_prefill"]
+        print(f"bench: kda {kcfg}", file=sys.stderr, flush=True)
+        line["kda"] = bench_kda(kcfg, torch, gdn)
     print(json.dumps(line), flush=True)
 
 

@@ -31,7 +31,8 @@ namespace gdn {
 
 namespace {
 
-constexpr int BW_NT = 256;   // threads per workgroup
+constexpr int BW_NT = 256;   // threads per workgroup of the per-chunk kernel
+constexpr int DH_NT = 1024;  // threads per workgroup of the reverse state pass
 constexpr int BW_C = 32;     // chunk length of the backward pass
 constexpr int BW_BV = 32;    // value columns per tile
 constexpr int BW_CP = BW_C + 1;
@@ -58,7 +59,7 @@ struct DhLds {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                        const float* __restrict__ g, const float* __restrict__ beta,
                                                        const T* __restrict__ dout, const float* __restrict__ dsf,
                                                        float* __restrict__ dH, float* __restrict__ ds0, int T_len,
@@ -86,15 +87,15 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
     const int NT = (T_len + BW_C - 1) / BW_C;
     const size_t sbase = (size_t)head * DK * DV + c0;
 
-    for (int e = tid; e < DK * BW_BV; e += BW_NT)
+    for (int e = tid; e < DK * BW_BV; e += DH_NT)
         dhs[e] = dsf ? dsf[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] : 0.f;
     for (int ci = NT - 1; ci >= 0; --ci) {
         const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
         __syncthreads();
         // the exit-state gradient of this chunk, for the per-chunk kernel
         float* dp = dH + ((size_t)head * NT + ci) * DK * DV + c0;
-        for (int e = tid; e < DK * BW_BV; e += BW_NT) dp[(size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
-        for (int e = tid; e < BW_C * DK; e += BW_NT) {
+        for (int e = tid; e < DK * BW_BV; e += DH_NT) dp[(size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
+        for (int e = tid; e < BW_C * DK; e += DH_NT) {
             const int r = e / DK, m = e % DK;
             float kv = 0.f, qv = 0.f;
             if (r < n) {
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
             Ks[r * KP + m] = kv;
             Qs[r * KP + m] = qv;
         }
-        for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+        for (int e = tid; e < BW_C * BW_BV; e += DH_NT) {
             const int r = e / BW_BV, c = e % BW_BV;
             dOs[r * BW_VP + c] = r < n ? to_f32(dout[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
         }
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
             eds[tid] = expf(gcs[BW_C - 1] - gcs[tid]);
         }
         // A (strictly lower) and M (lower including the diagonal)
-        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+        for (int e = tid; e < BW_C * BW_C; e += DH_NT) {
             const int r = e / BW_C, s = e % BW_C;
             float a = 0.f, mm = 0.f;
             if (s <= r) {
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
         }
         __syncthreads();
         // dDelta = diag(ed) K dh' + M^T dO
-        for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
+        for (int e = tid; e < BW_C * BW_BV; e += DH_NT) {
             const int r = e / BW_BV, c = e % BW_BV;
             float x = 0.f, y = 0.f;
 #pragma unroll 4
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
         __syncthreads();
         // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y
         const float eL = egs[BW_C - 1];
-        for (int e = tid; e < DK * BW_BV; e += BW_NT) {
+        for (int e = tid; e < DK * BW_BV; e += DH_NT) {
             const int m = e / BW_BV, c = e % BW_BV;
             float acc = eL * dhs[e];
 #pragma unroll 4
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_dh_kernel(const T* __restrict__ q, 
     }
     __syncthreads();
     if (ds0) {
-        for (int e = tid; e < DK * BW_BV; e += BW_NT) ds0[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
+        for (int e = tid; e < DK * BW_BV; e += DH_NT) ds0[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
     }
 }
 
@@ -622,7 +623,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
         auto kern = bwd_dh_kernel<T, DK, DV>;
         e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BW_BV), dim3(BW_NT), L::bytes, st, (const T*)a.q,
+        hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BW_BV), dim3(DH_NT), L::bytes, st, (const T*)a.q,
                            (const T*)a.k, a.g, a.beta, (const T*)a.dout, a.dsf, dHs, a.ds0, a.T, a.Hqk, a.Hv, grp,
                            a.scale);
         e = hipGetLastError();

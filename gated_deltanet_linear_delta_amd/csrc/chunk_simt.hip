@@ -14,7 +14,7 @@
 // Positions past T in the last chunk enter with k = q = v = 0, g = 0, beta = 0, which leaves
 // every result unchanged.  Only differences gc_r - gc_i with r >= i are exponentiated.
 //
-// Work layout: one 256-thread workgroup per (batch, value head, 32-column tile of dv).  Value
+// Work layout: one 512-thread workgroup per (batch, value head, 32-column tile of dv).  Value
 // columns of the state evolve independently, so column tiles are independent chains.  Everything
 // for one chunk lives in LDS in float32.
 #include "device_common.hpp"
@@ -24,7 +24,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int SIMT_NT = 256;
+constexpr int SIMT_NT = 512;
 constexpr int SIMT_CMAX = 64;
 
 template <int DK, int BV>

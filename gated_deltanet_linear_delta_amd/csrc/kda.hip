@@ -15,7 +15,7 @@
 // The pairwise decays are exponentials of differences (never above 1), so no factor overflows
 // however strong a channel's decay is within a chunk.
 //
-// Work layout: one 256-thread workgroup per (batch, value head, 32-column tile of dv); chunks
+// Work layout: one 1024-thread workgroup per (batch, value head, 32-column tile of dv); chunks
 // of 16 or 32 positions; everything for one chunk in LDS in float32.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -24,7 +24,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int KDA_NT = 256;
+constexpr int KDA_NT = 1024;
 constexpr int KDA_CMAX = 32;
 constexpr int KDA_BV = 32;
 
