@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/gdn.h):
 * :func:`gdn_chunk_fwd_gated` -- prefill followed by the gated RMSNorm (fused where it can be).
 * :func:`gdn_chunk_bwd` -- backward pass of the prefill (gradients of q, k, v, g, beta, S0).
 * :func:`gdn_kda_chunk_fwd` -- Kimi Delta Attention prefill (one decay per key channel).
+* :func:`gdn_chunk_fwd_varlen` -- prefill of packed sequences of different lengths.
 * :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_gated_workspace_bytes`,
   :func:`gdn_chunk_fwd_kernel_name`, :func:`gdn_status_string`.
 """
@@ -27,7 +28,7 @@ __all__ = [
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
     "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
     "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
-    "EXPORTED_SYMBOLS",
+    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
@@ -35,7 +36,8 @@ GDN_BF16 = 1
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
                     "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
-                    "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd")
+                    "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
+                    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -86,6 +88,10 @@ def load_library():
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     lib.gdn_kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp]
     lib.gdn_kda_chunk_fwd.restype = i
+    lib.gdn_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp] + [i] * 8 + [i, f, vp, sz, vp]
+    lib.gdn_chunk_fwd_varlen.restype = i
+    lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 7 + [i]
+    lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -104,6 +110,10 @@ def gdn_chunk_fwd_gated_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=G
 
 def gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype=GDN_BF16) -> int:
     return int(load_library().gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype))
+
+
+def gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk, dtype))
 
 
 def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
@@ -377,4 +387,44 @@ def gdn_kda_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=T
                                float(scale), _stream(stream, dev))
     if st != 0:
         raise GdnError(st, "gdn_kda_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen, initial_state=None, output_final_state=True,
+                         chunk=64, scale=1.0, o=None, final_state=None, workspace=None, stream=None):
+    """Prefill of packed sequences.  q, k [total_T, Hqk, dk]; v [total_T, Hv, dv]; g, beta
+    [total_T, Hv] float32; cu_seqlens int32 [N+1] on the device (offsets, non-decreasing from 0 to
+    total_T); max_seqlen the longest sequence (an int the caller knows); initial_state
+    [N, Hv, dk, dv] float32 or None.  Returns (o [total_T, Hv, dv], final_state or None)."""
+    torch = _torch()
+    lib = load_library()
+    total, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    _check_dense("q", q, (total, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (total, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (total, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (total, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (total, Hv), torch.float32, dev)
+    _check_dense("cu_seqlens", cu_seqlens, (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (N, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((total, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("o", o, (total, Hv, dv), q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (N, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(q)
+    need = int(lib.gdn_chunk_fwd_varlen_workspace_bytes(N, int(max_seqlen), Hqk, Hv, dk, dv, int(chunk), dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                  _ptr(final_state), _ptr(o), _ptr(cu_seqlens), N, int(max_seqlen), total, Hqk, Hv,
+                                  dk, dv, int(chunk), dt, float(scale), _ptr(workspace), wbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd_varlen")
     return o, final_state

@@ -343,6 +343,71 @@ gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, cons
     return gdn::launch_kda_chunk(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
+size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int max_seqlen, int Hqk, int Hv, int dk, int dv, int chunk,
+                                            gdn_dtype_t dtype)
+{
+    return gdn_chunk_fwd_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk, dtype);
+}
+
+gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                  const float* initial_state, float* final_state, void* o, const int* cu_seqlens,
+                                  int N, int max_seqlen, int total_T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                  gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream)
+{
+    if (total_T < 0) return GDN_ERR_SHAPE;
+    gdn_status_t s = check_chunk_sizes(N, max_seqlen, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s != GDN_OK) return s;
+    const size_t need = gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (N == 0) return GDN_OK;
+    const bool work = total_T > 0 && max_seqlen > 0;
+    if (!cu_seqlens) return GDN_ERR_NULL;
+    if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, o, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta) || !aligned4(cu_seqlens)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = work ? (size_t)total_T : 0;
+    const size_t sbytes = (size_t)N * Hv * dk * dv * sizeof(float);
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rcu = range(cu_seqlens, (size_t)(N + 1) * sizeof(int));
+    const Range rs0 = range(initial_state, initial_state ? sbytes : 0);
+    const Range rsf = range(final_state, final_state ? sbytes : 0);
+    const Range ro = range(o, ntok * Hv * dv * es);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rcu, rs0};
+    for (const Range& r : inputs)
+        if (overlap(ro, r) || overlap(rsf, r)) {
+            if (&r == &inputs[6] && final_state == initial_state && !overlap(ro, r)) continue;
+            return GDN_ERR_ALIAS;
+        }
+    if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    const Range rw = range(workspace, need);
+    const Range all[] = {rq, rk, rv, rg, rb, rcu, rs0, rsf, ro};
+    for (const Range& r : all)
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
+    s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        // every sequence is empty: final states are the initial ones
+        if (!final_state) return GDN_OK;
+        return gdn::launch_state_copy(initial_state, final_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, o, N, max_seqlen, Hqk, Hv,
+                                       dk, dv, chunk, dtype, scale);
+    a.cu = cu_seqlens;
+    a.total = total_T;
+    hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st)
+                                                : gdn::launch_chunk_simt(a, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, float* state, void* o, int B, int Hqk, int Hv,
                                 int dk, int dv, gdn_dtype_t dtype, float scale, void* stream)

@@ -581,11 +581,39 @@ __device__ __forceinline__ void store_state(const floatx4 (&hacc)[NTN][DK / 16],
             for (int x = 0; x < 4; ++x) sp[(size_t)(16 * mt + 4 * lg + x) * DV + nt * 16] = hacc[nt][mt][x];
 }
 
+// Final state = initial state (zeros when s0 is null) for `ncols` columns from `col`: an empty
+// packed sequence.  Plain element copies, one wave.
+template <int DK, int DV>
+__device__ __forceinline__ void copy_state_cols(const float* s0, float* sf, size_t head, int col, int ncols, int lane)
+{
+    if (!sf) return;
+    for (int e = lane; e < DK * ncols; e += 64) {
+        const size_t off = head * DK * DV + (size_t)(e / ncols) * DV + col + e % ncols;
+        sf[off] = s0 ? s0[off] : 0.f;
+    }
+}
+
 // (batch, query/key head, value head, column tile) of a workgroup; XCD-major placement when
 // asked (workgroup ids are dealt to the 8 XCDs round-robin).
 struct ChainId {
     int b, i, j, tile;
 };
+
+// First token and length of batch row b: uniform rows of T_len tokens, or (cu set) packed
+// sequences with offsets cu[0..N] into total tokens, each at most T_len long.  Offsets are
+// clamped into [0, total] and lengths into [0, T_len], so no access leaves the tensors whatever
+// cu holds.
+struct SeqSpan {
+    size_t tok0;
+    int len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const int* cu, int b, int T_len, int total)
+{
+    if (!cu) return SeqSpan{(size_t)b * T_len, T_len};
+    const int s = min(max(cu[b], 0), total);
+    const int e = min(max(cu[b + 1], s), total);
+    return SeqSpan{(size_t)s, min(e - s, T_len)};
+}
 
 __device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd_remap)
 {
@@ -609,14 +637,14 @@ __device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd
 // gated RMSNorm y = O / sqrt(mean(O^2) + eps) * w * silu(z) instead of O.  The chain waves stage
 // O of a chunk in LDS in the output phase and, in the interval the prep waves spend finishing T,
 // normalise 16 whole token rows each and write y; O itself never reaches HBM.
-template <int DK, int DV, int BV, bool GATED>
+template <int DK, int DV, int BV, bool GATED, bool VARLEN>
 __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
     bf16* o,                     // O, or y when gated (y may be z exactly)
     const bf16* z, const float* __restrict__ nw, int nw_stride, float eps,
-    int T_len, int Hqk, int Hv, int grp, float scale, int xcd_remap)
+    int T_max, int Hqk, int Hv, int grp, float scale, int xcd_remap, const int* cu, int total)
 {
     using L = MLds<DK, BV, GATED>;
     static_assert(!GATED || BV == DV, "the gated epilogue needs whole value heads");
@@ -653,15 +681,23 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const int cw = w - NPW;        // chain wave index (chain waves)
     const int ptid = tid;          // prep thread index 0..255 (prep waves)
 
+    const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
+    const int T_len = sq.len;
+    if (VARLEN && T_len == 0) {
+        // an empty sequence: the final state is the initial one (every wave leaves here, before
+        // any barrier)
+        if (!is_prep) copy_state_cols<DK, DV>(s0, sf, (size_t)b * Hv + j, c0 + cw * NCOL, NCOL, lane);
+        return;
+    }
     const int NT = (T_len + CH - 1) / CH;
     const size_t qk_row = (size_t)Hqk * DK;   // elements between consecutive tokens of q, k
     const size_t v_row = (size_t)Hv * DV;
-    const bf16* qb = q + ((size_t)b * T_len * Hqk + i) * DK;
-    const bf16* kb_ = k + ((size_t)b * T_len * Hqk + i) * DK;
-    const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
-    bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0;
-    const float* gb = g + (size_t)b * T_len * Hv + j;
-    const float* bb = beta + (size_t)b * T_len * Hv + j;
+    const bf16* qb = q + (sq.tok0 * Hqk + i) * DK;
+    const bf16* kb_ = k + (sq.tok0 * Hqk + i) * DK;
+    const bf16* vb = v + (sq.tok0 * Hv + j) * DV + c0;
+    bf16* ob = o + (sq.tok0 * Hv + j) * DV + c0;
+    const float* gb = g + sq.tok0 * Hv + j;
+    const float* bb = beta + sq.tok0 * Hv + j;
 
     // =====================================================================================
     // prep-wave state: prefetch registers and the parts of T it keeps between phases
@@ -905,8 +941,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
         constexpr int EPASS = 16 / ERP;
         const int ecb = lane % ECB, esub = lane / ECB;
         bf16* Os = reinterpret_cast<bf16*>(smem + L::os);
-        const bf16* zb = z + ((size_t)b * T_len * Hv + j) * DV + 8 * ecb;
-        bf16* yb = o + ((size_t)b * T_len * Hv + j) * DV + 8 * ecb;
+        const bf16* zb = z + (sq.tok0 * Hv + j) * DV + 8 * ecb;
+        bf16* yb = o + (sq.tok0 * Hv + j) * DV + 8 * ecb;
         bf16x8 zr[EPASS];
         float wc[8];
         if constexpr (GATED) {
@@ -971,11 +1007,11 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
 // are shared by the query/key head's group of value heads); then for each value head of the
 // group in turn: the gate cumsum and vectors, A (beta and the decay mask), T = (I + A)^{-1}, and
 // Aqk (the decay mask and the scale), all into the workspace.
-template <int DK>
+template <int DK, bool VARLEN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
-    int T_len, int Hqk, int Hv, int grp, int NT, float scale)
+    int T_max, int Hqk, int Hv, int grp, int NT, float scale, const int* cu, int total)
 {
     constexpr int KB = DK / 32;
     // A in two parts: the diagonal 16x16 blocks transposed in float32 for the solve
@@ -994,14 +1030,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
     const int i = lid % Hqk;
     const int b = lid / Hqk;
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
-    const int t0 = c * CH, n = min(CH, T_len - t0);
+    const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
+    const int t0 = c * CH;
+    if (VARLEN && t0 >= sq.len) return;   // past this sequence's last chunk
+    const int n = min(CH, sq.len - t0);
     const size_t qk_row = (size_t)Hqk * DK;
-    const bf16* kp = k + ((size_t)b * T_len + t0) * qk_row + (size_t)i * DK;
-    const bf16* qp = q + ((size_t)b * T_len + t0) * qk_row + (size_t)i * DK;
+    const bf16* kp = k + (sq.tok0 + t0) * qk_row + (size_t)i * DK;
+    const bf16* qp = q + (sq.tok0 + t0) * qk_row + (size_t)i * DK;
 
     // gates of the group's first value head, then the Gram fragments straight from HBM (standard
     // k order on both sides); rows past T are clamped and masked below
-    const size_t grow = ((size_t)b * T_len + t0 + min(lane, n - 1)) * Hv + (size_t)i * grp;
+    const size_t grow = (sq.tok0 + t0 + min(lane, n - 1)) * Hv + (size_t)i * grp;
     float gl = g[grow], bl = beta[grow];
     bf16x8 kf[4][KB], qf[4][KB];
 #pragma unroll
@@ -1262,11 +1301,11 @@ struct SLds {
     static constexpr size_t bytes = hx + 2 * NW * hx_frags * 1024;
 };
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool VARLEN>
 __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const unsigned char* __restrict__ ws, const unsigned char* __restrict__ wsq, const float* s0,
-    float* sf, bf16* __restrict__ o, int T_len, int Hqk, int Hv, int grp, int xcd_remap)
+    float* sf, bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, int xcd_remap, const int* cu, int total)
 {
     constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
@@ -1296,11 +1335,20 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     const int li = w == 0 ? 0 : w - (NW + 1);   // loader index (loader waves only)
     const bool is_loader = w == 0 || w == NW + 2;
     const bool is_chain = w >= 1 && w <= NW;
-    const int NT = (T_len + CH - 1) / CH;
+    const size_t head = (size_t)b * Hv + j;
+    const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
+    const int T_len = sq.len;
+    if (VARLEN && T_len == 0) {
+        // an empty sequence: the final state is the initial one (every wave leaves here, before
+        // any barrier)
+        if (is_chain) copy_state_cols<DK, DV>(s0, sf, head, c0 + (w - 1) * 16, 16, lane);
+        return;
+    }
+    const int NT = (T_len + CH - 1) / CH;       // this sequence's chunks
+    const int NTS = (T_max + CH - 1) / CH;      // chunks per row of the workspace
     const int qk_row = Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
-    const size_t head = (size_t)b * Hv + j;
-    const unsigned char* wh = ws + head * NT * WS_CHUNK;
+    const unsigned char* wh = ws + head * NTS * WS_CHUNK;
     auto cslot = [&](int c) { return smem + (size_t)(c & 1) * L::cslot; };
     auto hxp = [&](int c, int cw) {
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
@@ -1309,8 +1357,8 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     if (is_loader) {
         // ================================================================= loader waves
         const int ltid = li * 64 + lane;   // loader thread index
-        const bf16* kb_ = k + ((size_t)b * T_len * Hqk + i) * DK;
-        const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
+        const bf16* kb_ = k + (sq.tok0 * Hqk + i) * DK;
+        const bf16* vb = v + (sq.tok0 * Hv + j) * DV + c0;
         const int vrow = Hv * DV;
         bf16x8 rk[PK][2];
         bf16x8 rv[PV];
@@ -1420,8 +1468,8 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
         store_state<DK, DV, 1>(hacc, sf, head, c0 + cw * 16, lane);
     } else {
         // ================================================================= output wave
-        bf16* ob = o + ((size_t)b * T_len * Hv + j) * DV + c0;
-        const unsigned char* wqh = wsq + ((size_t)b * Hqk + i) * NT * ws_q_bytes<DK>();
+        bf16* ob = o + (sq.tok0 * Hv + j) * DV + c0;
+        const unsigned char* wqh = wsq + ((size_t)b * Hqk + i) * NTS * ws_q_bytes<DK>();
         // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc);
         // double-buffered, loaded two chunks ahead of their use
         struct OutIn {
@@ -1548,12 +1596,13 @@ bool use_split(const ChunkArgs& a)
     return (long)a.B * a.Hv < 192;
 }
 
-template <int DK, int DV, int BV, bool GATED>
+template <int DK, int DV, int BV, bool GATED, bool VARLEN = false>
 hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
 {
+    if (!VARLEN && a.cu) return launch_fused_t<DK, DV, BV, GATED, true>(a, st);
     using L = MLds<DK, BV, GATED>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_mfma_kernel<DK, DV, BV, GATED>;
+    auto kern = chunk_mfma_kernel<DK, DV, BV, GATED, VARLEN>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
@@ -1564,17 +1613,17 @@ hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(NTHR), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.s0, a.sf,
                        (bf16*)(GATED ? a.y : a.o), (const bf16*)a.z, a.norm_w, a.norm_w_stride, a.eps, a.T,
-                       a.Hqk, a.Hv, grp, a.scale, remap);
+                       a.Hqk, a.Hv, grp, a.scale, remap, a.cu, a.total);
     return hipGetLastError();
 }
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool VARLEN>
 hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
     constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_state_kernel<DK, DV, NW>;
+    auto kern = chunk_state_kernel<DK, DV, NW, VARLEN>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
@@ -1585,24 +1634,25 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
     const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((SLW + NW + 1) * 64), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0, a.sf,
-                       (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap);
+                       (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap, a.cu, a.total);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool VARLEN = false>
 hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
+    if (!VARLEN && a.cu) return launch_split_t<DK, DV, true>(a, ws, st);
     const int grp = a.Hv / a.Hqk;
     const int NT = (a.T + CH - 1) / CH;
     const long nprep = (long)a.B * a.Hqk * NT;
     unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
-    hipLaunchKernelGGL(chunk_prep_kernel<DK>, dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
+    hipLaunchKernelGGL((chunk_prep_kernel<DK, VARLEN>), dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, wsq, a.T, a.Hqk, a.Hv, grp, NT,
-                       a.scale);
+                       a.scale, a.cu, a.total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1>(a, ws, st);
-    return launch_state_t<DK, DV, 2>(a, ws, st);
+    if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1, VARLEN>(a, ws, st);
+    return launch_state_t<DK, DV, 2, VARLEN>(a, ws, st);
 }
 
 }  // namespace

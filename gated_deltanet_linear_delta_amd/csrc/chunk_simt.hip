@@ -55,7 +55,8 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
     T* __restrict__ o,           // may be null (states only)
     float* __restrict__ hst,     // null, or [B, Hv, NT, DK, DV]: the state entering every chunk
-    int T_len, int Hqk, int Hv, int grp, int C, float scale)
+    int T_max, int Hqk, int Hv, int grp, int C, float scale,
+    const int* cu, int total)    // packed sequences (cu[0..B] offsets), or null for rows of T_max
 {
     using L = SimtLds<DK, BV>;
     extern __shared__ float lds[];
@@ -77,6 +78,15 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     const int i = j / grp;
     const int c0 = blockIdx.y * BV; // first value column of this tile
     const int tid = threadIdx.x;
+    // first token and length of this batch row (offsets clamped into [0, total], lengths into
+    // [0, T_max], so no access leaves the tensors whatever cu holds)
+    size_t tok0 = (size_t)b * T_max;
+    int T_len = T_max;
+    if (cu) {
+        const int s = min(max(cu[b], 0), total), e = min(max(cu[b + 1], s), total);
+        tok0 = (size_t)s;
+        T_len = min(e - s, T_max);
+    }
 
     // Entry state tile h[m][c] = state[b, j, m, c0 + c].
     const size_t sbase = (size_t)head * DK * DV + c0;
@@ -89,7 +99,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
         const int n = min(C, T_len - t0);
         __syncthreads();  // previous chunk finished with every LDS buffer
         if (hst) {
-            const int NT = (T_len + C - 1) / C;
+            const int NT = (T_max + C - 1) / C;
             float* hp = hst + ((size_t)head * NT + t0 / C) * DK * DV + c0;
             for (int e = tid; e < DK * BV; e += SIMT_NT) hp[(size_t)(e / BV) * DV + e % BV] = hs[e];
         }
@@ -97,7 +107,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
             const int r = e / DK, m = e % DK;
             float kv = 0.f, qv = 0.f;
             if (r < n) {
-                const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+                const size_t off = ((tok0 + t0 + r) * Hqk + i) * DK + m;
                 kv = to_f32(k[off]);
                 qv = to_f32(q[off]) * scale;
             }
@@ -106,10 +116,10 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
         }
         for (int e = tid; e < C * BV; e += SIMT_NT) {
             const int r = e / BV, c = e % BV;
-            Vs[e] = r < n ? to_f32(v[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
+            Vs[e] = r < n ? to_f32(v[((tok0 + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
         }
         if (tid < C) {
-            const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+            const size_t off = (tok0 + t0 + tid) * Hv + j;
             gcs[tid] = tid < n ? g[off] : 0.f;
             bs[tid] = tid < n ? beta[off] : 0.f;
         }
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
                 const int r = e / BV, c = e % BV;
                 float acc = qh[p];
                 for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
-                if (o && r < n) o[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
+                if (o && r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
             }
         }
         // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T
@@ -210,7 +220,7 @@ static hipError_t launch_simt_t(const ChunkArgs& a, hipStream_t st)
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BV), dim3(SIMT_NT), L::bytes, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, a.s0, a.sf,
-                       (T*)a.o, a.hst, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale);
+                       (T*)a.o, a.hst, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -41,6 +41,10 @@ struct ChunkArgs {
     // float32-vector path only: when set, the state entering every chunk is stored here
     // ([B, Hv, NT, dk, dv], NT = ceil(T / chunk)); o may then be null
     float* hst = nullptr;
+    // packed sequences: when cu is set, B is the number of sequences, cu[0..B] (device) their
+    // token offsets into `total` tokens (tensors [total, H, d]), and T the longest length
+    const int* cu = nullptr;
+    int total = 0;
 };
 
 hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);

@@ -279,6 +279,43 @@ gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, cons
                                const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
                                int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* stream);
 
+/*
+ * gdn_chunk_fwd_varlen_workspace_bytes -- device scratch (bytes) gdn_chunk_fwd_varlen needs: that
+ * of gdn_chunk_fwd for N rows of max_seqlen tokens (0 when the path chosen needs none).  Pure
+ * host function; 0 for invalid sizes.
+ */
+size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int max_seqlen, int Hqk, int Hv, int dk, int dv, int chunk,
+                                            gdn_dtype_t dtype);
+
+/*
+ * gdn_chunk_fwd_varlen -- prefill of N packed sequences of different lengths in one call: the
+ * recurrence of gdn_chunk_fwd run independently over each sequence (its own initial and final
+ * state; no state flows from one sequence into the next), with the tokens of all sequences
+ * concatenated along one axis.  Chunks start at each sequence's first token.
+ *
+ *   q, k           [total_T, Hqk, dk] dtype      v, o [total_T, Hv, dv] dtype
+ *   g, beta        [total_T, Hv] float32
+ *   cu_seqlens     [N + 1] int32, DEVICE memory: sequence n is tokens cu[n] .. cu[n+1]-1.  It must
+ *                  hold 0 = cu[0] <= cu[1] <= ... <= cu[N] = total_T with every length at most
+ *                  max_seqlen; the kernels clamp offsets into [0, total_T] and lengths into
+ *                  [0, max_seqlen], so no access leaves the tensors, but other values give
+ *                  unspecified results.  Empty sequences are allowed (final state = initial).
+ *   initial_state, final_state [N, Hv, dk, dv] float32, as gdn_chunk_fwd (NULL allowed; in place
+ *                  allowed)
+ *   N              number of sequences; max_seqlen the longest (the work grid is sized by it)
+ *   chunk, dtype, scale, sizes, workspace (gdn_chunk_fwd_varlen_workspace_bytes), stream: as
+ *                  gdn_chunk_fwd; the kernel family is chosen as gdn_chunk_fwd_kernel_name(N,
+ *                  max_seqlen, ...) names it
+ * N == 0 is a no-op; total_T == 0 or max_seqlen == 0 writes final_state only.  Errors as
+ * gdn_chunk_fwd (cu_seqlens NULL: GDN_ERR_NULL; not 4-byte aligned: GDN_ERR_ALIGN; outputs
+ * overlapping it: GDN_ERR_ALIAS).
+ */
+gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                  const float* initial_state, float* final_state, void* o, const int* cu_seqlens,
+                                  int N, int max_seqlen, int total_T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                  gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -379,3 +379,46 @@ def test_kda_valid_calls_report_no_device():
     assert kda_call(sf=fake(5)) == NODEV
     assert kda_call(T=0, q=None, o=None) == NODEV
     assert kda_call(chunk=16, dtype=gdn.GDN_F32) == NODEV
+
+
+# ------------------------------------------------------------------------- packed sequences
+
+def varlen_call(**over):
+    lib = gdn.load_library()
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), o=fake(7),
+             cu=fake(8), N=3, maxT=100, total=250, Hqk=2, Hv=4, dk_=64, dv_=32, chunk=32, dtype=gdn.GDN_BF16,
+             scale=1.0, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return lib.gdn_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["o"], a["cu"],
+                                    a["N"], a["maxT"], a["total"], a["Hqk"], a["Hv"], a["dk_"], a["dv_"], a["chunk"],
+                                    a["dtype"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_varlen_workspace_size():
+    # the split path's workspace for N rows of max_seqlen tokens
+    assert gdn.gdn_chunk_fwd_varlen_workspace_bytes(3, 100, 2, 4, 128, 128, 64, gdn.GDN_BF16) == \
+        gdn.gdn_chunk_fwd_workspace_bytes(3, 100, 2, 4, 128, 128, 64, gdn.GDN_BF16) > 0
+    assert gdn.gdn_chunk_fwd_varlen_workspace_bytes(3, 100, 2, 4, 64, 32, 32, gdn.GDN_BF16) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cu=None), NULL), (dict(q=None), NULL), (dict(o=None), NULL),
+    (dict(N=-1), SHAPE), (dict(maxT=-1), SHAPE), (dict(total=-1), SHAPE), (dict(Hv=3), SHAPE),
+    (dict(dk_=48), UNSUP), (dict(chunk=128), UNSUP),
+    (dict(cu=ctypes.c_void_p(BASE + 8 * STRIDE + 2)), ALIGN), (dict(o=ctypes.c_void_p(BASE + 7 * STRIDE + 4)), ALIGN),
+    (dict(o=fake(8)), ALIAS), (dict(sf=fake(8)), ALIAS), (dict(o=fake(0)), ALIAS),
+    (dict(dk_=128, dv_=128, chunk=64, ws=None, wsb=0), WS),
+])
+def test_varlen_rejects(over, status):
+    assert varlen_call(**over) == status
+
+
+def test_varlen_noops():
+    assert varlen_call(N=0, cu=None, q=None) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_varlen_valid_calls_report_no_device():
+    assert varlen_call() == NODEV
+    assert varlen_call(total=0, q=None, o=None) == NODEV
+    assert varlen_call(sf=fake(5)) == NODEV
