@@ -164,6 +164,12 @@ def generate_kda(B, T, Hqk, Hv, dk, dv, dtype="bf16", mu=3.0, s0_std=0.0, seed=4
     return d
 
 
+def varlen_lengths(n=64, lo=64, hi=2048, seed=5001) -> np.ndarray:
+    """Sequence lengths of a packed batch: n draws uniform in [lo, hi] (int32, seeded)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi + 1, n).astype(np.int32)
+
+
 def to_torch(x: np.ndarray | None, dtype: str, device):
     """numpy array (float32, or uint16 bf16 bits) -> torch tensor on ``device``."""
     import torch
