@@ -28,7 +28,7 @@ __all__ = [
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
     "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
     "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
-    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_worksp
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
                     "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
                     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
-                    "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes")
+                    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -86,7 +86,9 @@ def load_library():
     lib.gdn_chunk_bwd.restype = i
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 6 + [i]
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
-    lib.gdn_kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp]
+    lib.gdn_kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp, sz, vp]
+    lib.gdn_kda_chunk_fwd_workspace_bytes.argtypes = [i] * 7 + [i]
+    lib.gdn_kda_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_kda_chunk_fwd.restype = i
     lib.gdn_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp] + [i] * 8 + [i, f, vp, sz, vp]
     lib.gdn_chunk_fwd_varlen.restype = i
@@ -114,6 +116,10 @@ def gdn_chunk_bwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, dtype=GDN_BF16) -> int:
 
 def gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
     return int(load_library().gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk, dtype))
+
+
+def gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
 
 
 def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
@@ -358,11 +364,13 @@ def gdn_chunk_bwd(q, k, v, g, beta, grad_o, initial_state=None, grad_final_state
     return out
 
 
-def gdn_kda_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=32, scale=1.0,
-                      o=None, final_state=None, stream=None):
+def gdn_kda_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=None, scale=1.0,
+                      o=None, final_state=None, workspace=None, stream=None):
     """Kimi Delta Attention prefill.  q, k [B,T,Hqk,dk]; v [B,T,Hv,dv] (bf16 or f32, all alike);
     g [B,T,Hv,dk] float32 (log decay per key channel); beta [B,T,Hv] float32; initial_state
-    [B,Hv,dk,dv] float32 or None.  Returns (o [B,T,Hv,dv], final_state or None)."""
+    [B,Hv,dk,dv] float32 or None.  chunk 64 runs the matrix-core kernels (bf16, head dims 64 or
+    128), 16 or 32 the float32 vector kernel; None picks 64 where it applies, else 32.  Returns
+    (o [B,T,Hv,dv], final_state or None)."""
     torch = _torch()
     lib = load_library()
     B, T, Hqk, dk = q.shape
@@ -382,9 +390,16 @@ def gdn_kda_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=T
         final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(q)
+    if chunk is None:
+        chunk = 64 if (dt == GDN_BF16 and dk in (64, 128) and dv in (64, 128)) else 32
+    need = int(lib.gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, int(chunk), dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.gdn_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                               _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), _dtype_code(q),
-                               float(scale), _stream(stream, dev))
+                               _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), dt,
+                               float(scale), _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise GdnError(st, "gdn_kda_chunk_fwd")
     return o, final_state

@@ -296,18 +296,38 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
     return gdn::launch_chunk_bwd(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                               const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
-                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* stream)
+static gdn_status_t check_kda_sizes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype)
 {
     if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || chunk <= 0) return GDN_ERR_SHAPE;
     if (Hv % Hqk != 0) return GDN_ERR_SHAPE;
-    if (!head_dim_ok(dk) || !head_dim_ok(dv) || (chunk != 16 && chunk != 32) || !dtype_ok(dtype))
+    if (!head_dim_ok(dk) || !head_dim_ok(dv) || !dtype_ok(dtype)) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    // chunk 64: the matrix-core kernels (bf16, head dims 64 or 128)
+    if (chunk == 64 && (dtype != GDN_BF16 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)))
         return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype)
+{
+    if (check_kda_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK || chunk != 64) return 0;
+    return gdn::kda_mfma_workspace_bytes(B, T, Hv, dk);
+}
+
+gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
+                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    gdn_status_t s0s = check_kda_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s0s != GDN_OK) return s0s;
+    const size_t need = gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
     if (B == 0) return GDN_OK;
     const bool work = T > 0;
     if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-    const void* ptrs[] = {q, k, v, initial_state, final_state, o};
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, o, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
     if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
@@ -327,6 +347,10 @@ gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, cons
             return GDN_ERR_ALIAS;
         }
     if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    const Range rw = range(workspace, need);
+    const Range allk[] = {rq, rk, rv, rg, rb, rs0, rsf, ro};
+    for (const Range& r : allk)
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
     gdn_status_t s = device_ok();
     if (s != GDN_OK) return s;
     hipStream_t st = (hipStream_t)stream;
@@ -340,7 +364,8 @@ gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, cons
     a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.chunk = chunk;
     a.dtype_bf16 = dtype == GDN_BF16;
     a.scale = scale;
-    return gdn::launch_kda_chunk(a, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    const hipError_t e = chunk == 64 ? gdn::launch_kda_mfma(a, workspace, st) : gdn::launch_kda_chunk(a, st);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int max_seqlen, int Hqk, int Hv, int dk, int dv, int chunk,

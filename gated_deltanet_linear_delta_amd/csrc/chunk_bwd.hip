@@ -160,7 +160,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, 
         if (tid < BW_BV) {
             for (int r = BW_C - 2; r >= 0; --r) {
                 float acc = Ys[r * BW_VP + tid];
-#pragma unroll 4
+#pragma unroll 8
                 for (int s = r + 1; s < BW_C; ++s) acc = fmaf(-As[s * BW_CP + r], Ys[s * BW_VP + tid], acc);
                 Ys[r * BW_VP + tid] = acc;
             }
@@ -329,16 +329,11 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         // T = (I + diag(beta) G)^{-1}: column s by forward substitution, one thread per column
         if (tid < BW_C) {
             const int s = tid;
-#pragma unroll 4
             for (int r = 0; r < BW_C; ++r) {
-                float x = r == s ? 1.f : 0.f;
-                if (r > s) {
-                    float acc = 0.f;
-#pragma unroll 4
-                    for (int u = s; u < r; ++u) acc = fmaf(Gs[r * BW_CP + u], Tm[u * BW_CP + s], acc);
-                    x = -bs[r] * acc;
-                }
-                Tm[r * BW_CP + s] = x;
+                float acc = 0.f;
+#pragma unroll 8
+                for (int u = 0; u < r; ++u) acc = fmaf(Gs[r * BW_CP + u], Tm[u * BW_CP + s], acc);
+                Tm[r * BW_CP + s] = r == s ? 1.f : (r > s ? -bs[r] * acc : 0.f);
             }
         }
         __syncthreads();

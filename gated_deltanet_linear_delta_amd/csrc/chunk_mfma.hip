@@ -304,11 +304,14 @@ __device__ __forceinline__ void apply_kt(floatx4 (&hacc)[NTN][DK / 16], const op
 // Every product's A fragments are loaded before its MFMAs, behind a scheduling barrier, so the
 // LDS latency is paid once per product rather than once per MFMA; with one tile per wave the V
 // tile and the gate vectors are fetched up front too.
-template <int DK, int NTN, int VP, bool KT = false, typename TF>
+// CHDEC: the state decays by a factor per dk row (ech[m], one decay per key channel) instead of
+// the scalar exp(gc_63).
+template <int DK, int NTN, int VP, bool KT = false, bool CHDEC = false, typename TF>
 __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const op_t* Ks,
                                             const bf16* Vc, TF&& tfrag, const float* vs, int lane,
                                             opx8 (&hb)[NTN][DK / 32], opx8 (&db)[NTN][2],
-                                            opx8 (&dtb)[NTN][2], opx8 (*akt)[DK / 16] = nullptr)
+                                            opx8 (&dtb)[NTN][2], opx8 (*akt)[DK / 16] = nullptr,
+                                            const float* ech = nullptr)
 {
     constexpr int KP = DK + 8;
     constexpr int KB = DK / 32;
@@ -395,12 +398,23 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
         load_kt<DK>(Ks, 1, lane, akt[1]);
     }
     // the decay of the state (its packed copy hb is already taken), while the MFMAs run
+    if constexpr (CHDEC) {
 #pragma unroll
-    for (int nt = 0; nt < NTN; ++nt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const floatx4 e4 = ld4s(ech + 16 * mt + 4 * lg);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
+                for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= e4[x];
+        }
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) hacc[nt][mt][x] *= ec;
+    }
     opx8 rbf[NTN][2];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt) {
@@ -1701,6 +1715,341 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, void* ws, hipStream_t st)
     GDN_MFMA_CASE(128, 128, 128) GDN_MFMA_CASE(128, 128, 64) GDN_MFMA_CASE(128, 64, 64)
     GDN_MFMA_CASE(64, 128, 128) GDN_MFMA_CASE(64, 128, 64) GDN_MFMA_CASE(64, 64, 64)
 #undef GDN_MFMA_CASE
+    return hipErrorInvalidValue;
+}
+
+// =======================================================================================
+// Kimi Delta Attention on the matrix cores ("Gated Attention Architectures", section 8): the
+// delta rule with one decay per key channel.  With gc[r][m] the in-chunk cumulative log decay
+// of key channel m and gL = gc[63], every in-chunk operand is a product with a factor at most 1:
+//     Kh = e^gc * K,  Kt = e^(gL - gc) * K,  Qh = scale e^gc * Q,
+//     A  = strictly-lower(beta_r sum_m k_rm k_im e^(gc_rm - gc_im)),  T = (I + A)^{-1},
+//     Aq = lower-incl(scale sum_m q_rm k_im e^(gc_rm - gc_im))
+// and the state step is the Gated DeltaNet one with those operands:
+//     Delta = T (beta V - beta Kh h),  O = Qh h + Aq Delta,  h <- diag(e^gL) h + Kt^T Delta.
+// kda_prep_kernel forms the chunk's operands in parallel over (batch, value head, chunk) on the
+// vector units (the pairwise decays are exponentials of differences, float32) and writes them as
+// float16; kda_state_kernel carries the chains on the matrix cores with the chain-wave steps of
+// the Gated DeltaNet kernels.
+namespace {
+
+constexpr int KQ_NT = 1024;   // threads of the prep kernel
+
+// per (batch, value head, chunk) workspace block: Kh, Kt, Qh [64][DK] f16; T, Aq [64][64] f16;
+// beta [64] f32; e^gL [DK] f32
+template <int DK>
+struct KdaWs {
+    static constexpr size_t kh = 0;
+    static constexpr size_t kt = kh + (size_t)CH * DK * 2;
+    static constexpr size_t qh = kt + (size_t)CH * DK * 2;
+    static constexpr size_t tm = qh + (size_t)CH * DK * 2;
+    static constexpr size_t aq = tm + (size_t)CH * CH * 2;
+    static constexpr size_t bt = aq + (size_t)CH * CH * 2;
+    static constexpr size_t el = bt + (size_t)CH * 4;
+    static constexpr size_t bytes = el + (size_t)DK * 4;
+};
+
+template <typename T, int DK>
+__global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const float* __restrict__ g, const float* __restrict__ beta,
+                                                         unsigned char* __restrict__ ws, int T_len, int Hqk, int Hv,
+                                                         int grp, int NT, float scale)
+{
+    using W = KdaWs<DK>;
+    constexpr int KP = DK + 1, AP = CH + 1;
+    extern __shared__ float lds[];
+    float* Ks = lds;
+    float* Qs = Ks + CH * KP;
+    float* Gs = Qs + CH * KP;
+    float* As = Gs + CH * KP;
+    float* Aqs = As + CH * AP;
+    float* Ts = Aqs + CH * AP;
+    float* bs = Ts + CH * AP;
+
+    const int c = blockIdx.x % NT;
+    const int head = blockIdx.x / NT;   // b * Hv + j
+    const int b = head / Hv, j = head - b * Hv, i = j / grp;
+    const int tid = threadIdx.x;
+    const int t0 = c * CH, n = min(CH, T_len - t0);
+#pragma unroll
+    for (int e = tid; e < CH * DK; e += KQ_NT) {
+        const int r = e / DK, m = e % DK;
+        float kv = 0.f, qv = 0.f, gv = 0.f;
+        if (r < n) {
+            const size_t tok = (size_t)b * T_len + t0 + r;
+            kv = to_f32(k[(tok * Hqk + i) * DK + m]);
+            qv = to_f32(q[(tok * Hqk + i) * DK + m]) * scale;
+            gv = g[(tok * Hv + j) * DK + m];
+        }
+        Ks[r * KP + m] = kv;
+        Qs[r * KP + m] = qv;
+        Gs[r * KP + m] = gv;
+    }
+    if (tid < CH) bs[tid] = tid < n ? beta[((size_t)b * T_len + t0 + tid) * Hv + j] : 0.f;
+    __syncthreads();
+    for (int m = tid; m < DK; m += KQ_NT) {
+        float acc = 0.f;
+        for (int r = 0; r < CH; ++r) {
+            acc += Gs[r * KP + m];
+            Gs[r * KP + m] = acc;
+        }
+    }
+    __syncthreads();
+    // A (beta-scaled, strictly lower) and Aq (lower including the diagonal): the upper parts are
+    // zeros, the CH (CH + 1) / 2 lower pairs are dealt out evenly (pair p is row r, column s with
+    // p = r (r + 1) / 2 + s)
+    for (int e = tid; e < CH * CH; e += KQ_NT) {
+        const int r = e / CH, s = e % CH;
+        if (s > r) {
+            As[r * AP + s] = 0.f;
+            Aqs[r * AP + s] = 0.f;
+        }
+    }
+    for (int p = tid; p < CH * (CH + 1) / 2; p += KQ_NT) {
+        int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        r += (r + 1) * (r + 2) / 2 <= p;   // round-off guard: r (r + 1) / 2 <= p < (r + 1) (r + 2) / 2
+        r -= r * (r + 1) / 2 > p;
+        const int s = p - r * (r + 1) / 2;
+        float kk = 0.f, qk = 0.f;
+#pragma unroll 4
+        for (int m = 0; m < DK; ++m) {
+            const float w = __expf(Gs[r * KP + m] - Gs[s * KP + m]) * Ks[s * KP + m];
+            kk = fmaf(Ks[r * KP + m], w, kk);
+            qk = fmaf(Qs[r * KP + m], w, qk);
+        }
+        As[r * AP + s] = s < r ? bs[r] * kk : 0.f;
+        Aqs[r * AP + s] = qk;
+    }
+    __syncthreads();
+    // T = (I + A)^{-1}, column s by forward substitution, one thread per column.  The sum runs
+    // over u < r for every lane (T[u][s] = 0 above the diagonal is already stored), so the lanes
+    // keep one trip count and the unrolled reads issue together.
+    if (tid < CH) {
+        const int s = tid;
+        for (int r = 0; r < CH; ++r) {
+            float acc = 0.f;
+#pragma unroll 8
+            for (int u = 0; u < r; ++u) acc = fmaf(As[r * AP + u], Ts[u * AP + s], acc);
+            Ts[r * AP + s] = r == s ? 1.f : (r > s ? -acc : 0.f);
+        }
+    }
+    __syncthreads();
+    unsigned char* wb = ws + ((size_t)head * NT + c) * W::bytes;
+    op_t* kh = reinterpret_cast<op_t*>(wb + W::kh);
+    op_t* kt = reinterpret_cast<op_t*>(wb + W::kt);
+    op_t* qh = reinterpret_cast<op_t*>(wb + W::qh);
+    for (int e = tid; e < CH * DK; e += KQ_NT) {
+        const int r = e / DK, m = e % DK;
+        const float gr = Gs[r * KP + m], gl = Gs[(CH - 1) * KP + m];
+        kh[e] = (op_t)(__expf(gr) * Ks[r * KP + m]);
+        kt[e] = (op_t)(__expf(gl - gr) * Ks[r * KP + m]);
+        qh[e] = (op_t)(__expf(gr) * Qs[r * KP + m]);
+    }
+    op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
+    op_t* aw = reinterpret_cast<op_t*>(wb + W::aq);
+    for (int e = tid; e < CH * CH; e += KQ_NT) {
+        const int r = e / CH, s = e % CH;
+        tw[e] = (op_t)Ts[r * AP + s];
+        aw[e] = (op_t)Aqs[r * AP + s];
+    }
+    float* bw = reinterpret_cast<float*>(wb + W::bt);
+    float* ew = reinterpret_cast<float*>(wb + W::el);
+    if (tid < CH) bw[tid] = bs[tid];
+    for (int m = tid; m < DK; m += KQ_NT) ew[m] = __expf(Gs[(CH - 1) * KP + m]);
+}
+
+template <int DK>
+constexpr size_t kda_prep_lds_bytes()
+{
+    return ((size_t)3 * CH * (DK + 1) + (size_t)3 * CH * (CH + 1) + CH) * sizeof(float);
+}
+
+// LDS of the state kernel: two slots, each Kh, Kt, Qh [64][DK+8] f16 (column-permuted), T, Aq
+// [64][CP] f16 (column-permuted), V [64][32] bf16, the row vectors [8][64] f32, e^gL [DK] f32
+template <int DK>
+struct KsLds {
+    static constexpr int KP = DK + 8;
+    static constexpr int VP = 32;
+    static constexpr size_t kh = 0;
+    static constexpr size_t kt = kh + (size_t)CH * KP * 2;
+    static constexpr size_t qh = kt + (size_t)CH * KP * 2;
+    static constexpr size_t tm = qh + (size_t)CH * KP * 2;
+    static constexpr size_t aq = tm + (size_t)CH * CP * 2;
+    static constexpr size_t v = aq + (size_t)CH * CP * 2;
+    static constexpr size_t vec = v + (size_t)CH * VP * 2;
+    static constexpr size_t ech = vec + (size_t)8 * CH * 4;
+    static constexpr size_t slot = ech + (size_t)DK * 4;
+    static constexpr size_t bytes = 2 * slot;
+    static_assert(slot % 16 == 0 && kt % 16 == 0 && tm % 16 == 0 && v % 16 == 0 && vec % 16 == 0, "alignment");
+};
+
+// one workgroup of 4 waves per (batch, value head, 16-column tile): wave 0 carries the chain of
+// chunk n from slot n & 1 while waves 1..3 stage chunk n + 1 into the other slot; one barrier
+// per chunk
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_state_kernel(const bf16* __restrict__ v,
+                                                        const unsigned char* __restrict__ ws, const float* s0,
+                                                        float* sf, bf16* __restrict__ o, int T_len, int Hv, int NT)
+{
+    using L = KsLds<DK>;
+    using W = KdaWs<DK>;
+    constexpr int NTILE = DV / 16;
+    constexpr int KP = L::KP;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tile = blockIdx.x % NTILE;
+    const size_t head = blockIdx.x / NTILE;   // b * Hv + j
+    const int b = (int)(head / Hv), j = (int)(head - (size_t)b * Hv);
+    const int c0 = tile * 16;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t v_row = (size_t)Hv * DV;
+    const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
+
+    // loaders (waves 1..3): chunk c into slot c & 1
+    auto stage = [&](int c) {
+        unsigned char* sb = smem + (size_t)(c & 1) * L::slot;
+        const unsigned char* wb = ws + (head * NT + c) * W::bytes;
+        const int lt = threadIdx.x - 64;   // 0..191
+        // Kh, Kt, Qh: 3 x 64 rows x DK/8 runs of 8; T, Aq: 2 x 64 rows x 8 runs.  Every global
+        // load is issued before the first LDS store, so their latencies overlap.
+        constexpr int RK = DK / 8;
+        constexpr int NK = (3 * CH * RK + 191) / 192, NM = (2 * CH * 8 + 191) / 192;
+        opx8 xk[NK], xm[NM];
+#pragma unroll
+        for (int p = 0; p < NK; ++p) {
+            const int e = min(lt + p * 192, 3 * CH * RK - 1);
+            const int mtx = e / (CH * RK), rr = (e / RK) % CH, c8 = (e % RK) * 8;
+            xk[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::kh : mtx == 1 ? W::kt : W::qh) +
+                                                    ((size_t)rr * DK + c8) * 2);
+        }
+#pragma unroll
+        for (int p = 0; p < NM; ++p) {
+            const int e = min(lt + p * 192, 2 * CH * 8 - 1);
+            const int mtx = e / (CH * 8), rr = (e / 8) % CH, c8 = (e % 8) * 8;
+            xm[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::tm : W::aq) + ((size_t)rr * CH + c8) * 2);
+        }
+#pragma unroll
+        for (int p = 0; p < NK; ++p) {
+            const int e = lt + p * 192;
+            if (e < 3 * CH * RK) {
+                const int mtx = e / (CH * RK), rr = (e / RK) % CH, c8 = (e % RK) * 8;
+                op_t* dst = reinterpret_cast<op_t*>(sb + (mtx == 0 ? L::kh : mtx == 1 ? L::kt : L::qh)) + rr * KP;
+                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{xk[p][0], xk[p][1], xk[p][2], xk[p][3]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{xk[p][4], xk[p][5], xk[p][6], xk[p][7]};
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NM; ++p) {
+            const int e = lt + p * 192;
+            if (e < 2 * CH * 8) {
+                const int mtx = e / (CH * 8), rr = (e / 8) % CH, c8 = (e % 8) * 8;
+                op_t* dst = reinterpret_cast<op_t*>(sb + (mtx == 0 ? L::tm : L::aq)) + rr * CP;
+                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{xm[p][0], xm[p][1], xm[p][2], xm[p][3]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{xm[p][4], xm[p][5], xm[p][6], xm[p][7]};
+            }
+        }
+        // V: 64 rows x 2 runs of 8 bf16 (rows past T zero)
+        const int t0 = c * CH, n = min(CH, T_len - t0);
+        if (lt < 2 * CH) {
+            const int rr = lt / 2, c8 = (lt % 2) * 8;
+            bf16x8 x = {};
+            if (rr < n) x = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + rr) * v_row + c8);
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sb + L::v) + rr * L::VP + c8) = x;
+        }
+        // row vectors: beta (V_B, V_BEG: e^gc is inside Kh), ones (V_ED, V_EG), e^gL per channel
+        float* vs = reinterpret_cast<float*>(sb + L::vec);
+        const float* bw = reinterpret_cast<const float*>(wb + W::bt);
+        if (lt < CH) {
+            const float bt = bw[lt];
+            vs[V_B * CH + lt] = bt;
+            vs[V_BEG * CH + lt] = bt;
+            vs[V_ED * CH + lt] = 1.f;
+            vs[V_EC * CH + lt] = 1.f;
+            vs[V_EG * CH + lt] = 1.f;
+        }
+        float* ech = reinterpret_cast<float*>(sb + L::ech);
+        const float* ew = reinterpret_cast<const float*>(wb + W::el);
+        for (int m = lt; m < DK; m += 192) ech[m] = ew[m];
+    };
+
+    floatx4 hacc[1][DK / 16];
+    if (w == 0) {
+        load_state<DK, DV, 1>(hacc, s0, head, c0, lane);
+    } else {
+        stage(0);
+    }
+    __syncthreads();
+    for (int n = 0; n < NT; ++n) {
+        if (w == 0) {
+            const unsigned char* sb = smem + (size_t)(n & 1) * L::slot;
+            const op_t* Kh = reinterpret_cast<const op_t*>(sb + L::kh);
+            const op_t* Kt = reinterpret_cast<const op_t*>(sb + L::kt);
+            const op_t* Qh = reinterpret_cast<const op_t*>(sb + L::qh);
+            const op_t* Tm = reinterpret_cast<const op_t*>(sb + L::tm);
+            const op_t* Aq = reinterpret_cast<const op_t*>(sb + L::aq);
+            const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v);
+            const float* vs = reinterpret_cast<const float*>(sb + L::vec);
+            const float* ech = reinterpret_cast<const float*>(sb + L::ech);
+            const int ln = lane & 15, lg = lane >> 4;
+            const int t0 = n * CH;
+            opx8 hb[1][DK / 32], db[1][2], dtb[1][2];
+            chain_delta<DK, 1, L::VP, false, true>(hacc, Kh, Vs,
+                                                   [&](int mt, int cb) { return frag(Tm, CP, 16 * mt + ln, 32 * cb, lg); },
+                                                   vs, lane, hb, db, dtb, nullptr, ech);
+            chain_out<DK, 1>(hb, db, Qh, Aq, vs + V_EG * CH, o + ((size_t)b * T_len * Hv + j) * DV + c0 + (size_t)t0 * v_row,
+                             v_row, min(CH, T_len - t0), lane);
+            chain_update<DK, 1>(hacc, Kt, dtb, lane);
+        } else if (n + 1 < NT) {
+            stage(n + 1);
+        }
+        __syncthreads();
+    }
+    if (w == 0) store_state<DK, DV, 1>(hacc, sf, head, c0, lane);
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_kda_mfma_t(const KdaArgs& a, void* ws, hipStream_t st)
+{
+    const int NT = (a.T + CH - 1) / CH;
+    const int grp = a.Hv / a.Hqk;
+    auto prep = kda_prep_kernel<T, DK>;
+    constexpr size_t pl = kda_prep_lds_bytes<DK>();
+    static_assert(pl <= 160 * 1024, "LDS budget");
+    hipError_t e = hipFuncSetAttribute((const void*)prep, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep, dim3((unsigned)((long)a.B * a.Hv * NT)), dim3(KQ_NT), pl, st, (const T*)a.q,
+                       (const T*)a.k, a.g, a.beta, (unsigned char*)ws, a.T, a.Hqk, a.Hv, grp, NT, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    using L = KsLds<DK>;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    auto kern = kda_state_kernel<DK, DV>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hv * (DV / 16))), dim3(256), L::bytes, st,
+                       (const bf16*)a.v, (const unsigned char*)ws, a.s0, a.sf, (bf16*)a.o, a.T, a.Hv, NT);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool kda_mfma_supported(const KdaArgs& a)
+{
+    return a.dtype_bf16 && a.chunk == CH && (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128);
+}
+
+size_t kda_mfma_workspace_bytes(int B, int T, int Hv, int dk)
+{
+    const size_t NT = ((size_t)T + CH - 1) / CH;
+    const size_t per = dk == 128 ? KdaWs<128>::bytes : KdaWs<64>::bytes;
+    return (size_t)B * Hv * NT * per;
+}
+
+hipError_t launch_kda_mfma(const KdaArgs& a, void* ws, hipStream_t st)
+{
+    if (a.dk == 128 && a.dv == 128) return launch_kda_mfma_t<bf16, 128, 128>(a, ws, st);
+    if (a.dk == 128 && a.dv == 64) return launch_kda_mfma_t<bf16, 128, 64>(a, ws, st);
+    if (a.dk == 64 && a.dv == 128) return launch_kda_mfma_t<bf16, 64, 128>(a, ws, st);
+    if (a.dk == 64 && a.dv == 64) return launch_kda_mfma_t<bf16, 64, 64>(a, ws, st);
     return hipErrorInvalidValue;
 }
 

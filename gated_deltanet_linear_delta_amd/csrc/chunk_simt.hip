@@ -175,6 +175,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
         if (tid < BV) {
             for (int r = 1; r < C; ++r) {
                 float acc = Rs[r * BV + tid];
+#pragma unroll 8
                 for (int c = 0; c < r; ++c) acc = fmaf(-As[r * L::CP + c], Rs[c * BV + tid], acc);
                 Rs[r * BV + tid] = acc;
             }

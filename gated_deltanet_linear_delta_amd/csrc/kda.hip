@@ -147,6 +147,7 @@ __global__ __launch_bounds__(KDA_NT) void kda_chunk_kernel(
         if (tid < BV) {
             for (int r = 1; r < C; ++r) {
                 float acc = Rs[r * BV + tid];
+#pragma unroll 8
                 for (int s = 0; s < r; ++s) acc = fmaf(-As[r * CP + s], Rs[s * BV + tid], acc);
                 Rs[r * BV + tid] = acc;
             }

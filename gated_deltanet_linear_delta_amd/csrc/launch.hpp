@@ -106,6 +106,11 @@ struct KdaArgs {
 };
 
 hipError_t launch_kda_chunk(const KdaArgs& a, hipStream_t st);
+// Matrix-core KDA (chunk_mfma.hip): bf16, chunk 64, dk and dv 64 or 128; a per-chunk prep kernel
+// fills a workspace of kda_mfma_workspace_bytes, then the state pass.
+bool kda_mfma_supported(const KdaArgs& a);
+size_t kda_mfma_workspace_bytes(int B, int T, int Hv, int dk);
+hipError_t launch_kda_mfma(const KdaArgs& a, void* ws, hipStream_t st);
 
 // Layer steps around the recurrence (layer_ops.hip).
 struct PrologueArgs {

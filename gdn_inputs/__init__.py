@@ -66,7 +66,7 @@ CONFIGS = {
                      dtype="bf16", mu=3.0, s0_std=0.02, seed=1005, steps=64),
     # Kimi Delta Attention (per-key-channel decay; inputs from generate_kda): the Qwen3-Next
     # layer's size with as many query/key heads as value heads
-    "kda_prefill": Config("kda_prefill", B=1, T=4096, Hqk=32, Hv=32, dk=128, dv=128, chunk=32,
+    "kda_prefill": Config("kda_prefill", B=1, T=4096, Hqk=32, Hv=32, dk=128, dv=128, chunk=64,
                           dtype="bf16", mu=3.0, s0_std=0.0, seed=1006),
 }
 

@@ -257,6 +257,15 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_kda_chunk_fwd_workspace_bytes -- device scratch (bytes) gdn_kda_chunk_fwd needs: 0 for
+ * chunks of 16 or 32; for chunk 64 (the matrix-core kernels) one block per (batch, value head,
+ * chunk) of the chunk's decay-weighted operands in float16 (e^gc K, e^(gL-gc) K, e^gc q, T, the
+ * masked Q K^T) and its beta and e^gL vectors: 3*64*dk*2 + 2*64*64*2 + 64*4 + dk*4 bytes.  Pure
+ * host function; 0 for invalid sizes.
+ */
+size_t gdn_kda_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype);
+
+/*
  * gdn_kda_chunk_fwd -- Kimi Delta Attention prefill: the delta rule with one decay per key
  * channel ("Gated Attention Architectures", section 8, Mathematical Formulation),
  *     S_t = (I - beta_t k_t k_t^T) D_t S_{t-1} + beta_t v_t k_t^T,   o_t = S_t^T (scale q_t),
@@ -272,12 +281,17 @@ gdn_status_t gdn_chunk_bwd(const void* q, const void* k, const void* v, const fl
  *   g              [B, T, Hv, dk]   float32, log alpha per key channel (<= 0 for a decay)
  *   beta           [B, T, Hv]       float32
  *   initial_state, final_state, o, scale, stream: as gdn_chunk_fwd
- *   chunk          16 or 32.  dk, dv 32, 64 or 128.
- * No workspace.  B == 0 is a no-op; T == 0 writes final_state only.  Errors as gdn_chunk_fwd.
+ *   chunk          16 or 32 (float32 vector kernel, any supported dtype and head dims 32, 64,
+ *                  128), or 64 (matrix-core kernels: bf16, dk and dv 64 or 128; every in-chunk
+ *                  operand carries a decay factor at most 1, so float16 operands hold them)
+ *   workspace      at least gdn_kda_chunk_fwd_workspace_bytes(...) bytes (16-byte aligned,
+ *                  caller-owned, not overlapping any other argument), or NULL when that is 0
+ * B == 0 is a no-op; T == 0 writes final_state only.  Errors as gdn_chunk_fwd.
  */
 gdn_status_t gdn_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                                const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
-                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* stream);
+                               int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * gdn_chunk_fwd_varlen_workspace_bytes -- device scratch (bytes) gdn_chunk_fwd_varlen needs: that

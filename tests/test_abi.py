@@ -350,17 +350,30 @@ def test_chunk_bwd_valid_calls_report_no_device():
 def kda_call(**over):
     lib = gdn.load_library()
     a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), o=fake(7),
-             B=2, T=100, Hqk=2, Hv=4, dk_=64, dv_=32, chunk=32, dtype=gdn.GDN_BF16, scale=1.0, stream=None)
+             B=2, T=100, Hqk=2, Hv=4, dk_=64, dv_=32, chunk=32, dtype=gdn.GDN_BF16, scale=1.0, ws=None, wsb=0,
+             stream=None)
     a.update(over)
     return lib.gdn_kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["o"], a["B"],
                                  a["T"], a["Hqk"], a["Hv"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], a["scale"],
-                                 a["stream"])
+                                 a["ws"], a["wsb"], a["stream"])
+
+
+KDA_WS = 2 * 4 * 2 * (3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4 + 64 * 4)   # B Hv ceil(100/64), dk 64
+
+
+def test_kda_workspace_size():
+    assert gdn.gdn_kda_chunk_fwd_workspace_bytes(2, 100, 2, 4, 64, 32, 32, gdn.GDN_BF16) == 0
+    assert gdn.gdn_kda_chunk_fwd_workspace_bytes(2, 100, 2, 4, 64, 64, 64, gdn.GDN_BF16) == KDA_WS
+    assert gdn.gdn_kda_chunk_fwd_workspace_bytes(2, 100, 2, 4, 64, 64, 64, gdn.GDN_F32) == 0    # unsupported
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), NULL), (dict(g=None), NULL), (dict(o=None), NULL),
     (dict(B=-1), SHAPE), (dict(Hv=3), SHAPE), (dict(chunk=0), SHAPE),
-    (dict(chunk=64), UNSUP), (dict(chunk=8), UNSUP), (dict(dk_=96), UNSUP), (dict(dtype=4), UNSUP),
+    (dict(chunk=128), UNSUP), (dict(chunk=8), UNSUP), (dict(dk_=96), UNSUP), (dict(dtype=4), UNSUP),
+    (dict(chunk=64), UNSUP), (dict(chunk=64, dv_=64, dtype=gdn.GDN_F32), UNSUP),
+    (dict(chunk=64, dv_=64), WS), (dict(chunk=64, dv_=64, wsb=KDA_WS), NULL),
+    (dict(chunk=64, dv_=64, ws=fake(2), wsb=KDA_WS), ALIAS),
     (dict(q=ctypes.c_void_p(BASE + 8)), ALIGN), (dict(g=ctypes.c_void_p(BASE + 3 * STRIDE + 2)), ALIGN),
     (dict(o=fake(3)), ALIAS), (dict(o=ctypes.c_void_p(BASE + 3 * STRIDE + 4096)), ALIAS),   # runs into g
     (dict(sf=fake(7)), ALIAS), (dict(sf=ctypes.c_void_p(BASE + 5 * STRIDE + 256)), ALIAS),
@@ -379,6 +392,7 @@ def test_kda_valid_calls_report_no_device():
     assert kda_call(sf=fake(5)) == NODEV
     assert kda_call(T=0, q=None, o=None) == NODEV
     assert kda_call(chunk=16, dtype=gdn.GDN_F32) == NODEV
+    assert kda_call(chunk=64, dv_=64, ws=fake(9), wsb=KDA_WS) == NODEV
 
 
 # ------------------------------------------------------------------------- packed sequences

@@ -1,8 +1,9 @@
 """Parity of the HIP Kimi Delta Attention prefill (gdn_kda_chunk_fwd) against the float64 KDA
-oracle (oracle.kda_recurrent) on the same seeded inputs, element by element over whole tensors:
-several chunks with a ragged tail, chunks 16 and 32, grouped heads, scale, strong per-channel
-decays, in-place state, empty inputs; the equal-decay case against the Gated DeltaNet kernels;
-the Qwen3-Next-shaped KDA workload at full size on sampled chains."""
+oracle (oracle.kda_recurrent) on the same seeded inputs, element by element over whole tensors,
+for both routes (float32 vector kernel, chunks 16 and 32; matrix-core kernels, chunk 64):
+several chunks with a ragged tail, grouped heads, scale, strong per-channel decays, in-place
+state, empty inputs; the routes against each other and the equal-decay case against the Gated
+DeltaNet kernels; the Qwen3-Next-shaped KDA workload at full size on sampled chains."""
 import numpy as np
 import pytest
 
@@ -96,3 +97,67 @@ def test_kda_prefill_sampled():
     o_s = np.stack([o[b, :, j] for b, j in chains])[:, :, None]
     s_s = np.stack([s[b, j] for b, j in chains])[:, None]
     check("kda_prefill sampled", "bf16", o_s, o_ref, s_s, s_ref)
+
+
+# ------------------------------------------------------------- matrix-core route (chunk 64)
+
+@pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 200, 2, 4), (64, 128, 65, 1, 2), (128, 64, 64, 2, 2),
+                                           (64, 64, 130, 1, 3), (128, 128, 1, 1, 1)])
+def test_kda_mfma_small(dk, dv, T, Hqk, Hv):
+    say(f"kda mfma dk={dk} dv={dv} T={T} Hqk={Hqk} Hv={Hv}")
+    d = gi.generate_kda(B=2, T=T, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, dtype="bf16", mu=2.0, s0_std=0.05, seed=T + dk + Hv + 7)
+    o, s = run_kda(d, 64)
+    o_ref, s_ref = oracle_kda(d)
+    check("kda mfma", "bf16", o, o_ref, s, s_ref)
+
+
+def test_kda_mfma_strong_decay_scale_and_resume():
+    for mu in (-3.0, 8.0):
+        d = gi.generate_kda(B=1, T=150, Hqk=2, Hv=2, dk=128, dv=128, dtype="bf16", mu=mu, s0_std=0.05, seed=31)
+        o, s = run_kda(d, 64, scale=0.3)
+        o_ref, s_ref = oracle_kda(d, scale=0.3)
+        check(f"kda mfma mu={mu}", "bf16", o, o_ref, s, s_ref)
+    # continuation with the state updated in place
+    d = gi.generate_kda(B=1, T=160, Hqk=1, Hv=2, dk=64, dv=64, dtype="bf16", mu=2.0, s0_std=0.05, seed=32)
+    t = dev(d)
+    st = t["s0"].clone()
+    parts = []
+    for a, b in ((0, 70), (70, 160)):
+        x = {n: (y[:, a:b].contiguous() if n != "s0" else y) for n, y in t.items()}
+        oo, _ = gdn.gdn_kda_chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], st, final_state=st, chunk=64)
+        parts.append(host(oo))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_kda(d)
+    check("kda mfma resume in place", "bf16", np.concatenate(parts, axis=1), o_ref, host(st), s_ref)
+
+
+def test_kda_mfma_matches_vector_kernel_and_gdn():
+    """The matrix-core and vector routes agree; with one decay per head copied to every channel
+    the matrix-core KDA also agrees with the Gated DeltaNet matrix-core kernel."""
+    d = gi.generate_kda(B=2, T=257, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=33)
+    o64, s64 = run_kda(d, 64)
+    o32, s32 = run_kda(d, 32)
+    check("kda mfma vs vector", "bf16", o64, o32, s64, s32)
+    g = gi.generate(B=2, T=257, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=34)
+    dd = dict(g)
+    dd["g"] = np.ascontiguousarray(np.repeat(g["g"][..., None], 128, axis=-1))
+    ok, sk = run_kda(dd, 64)
+    t = dev(g)
+    og, sg = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    torch.cuda.synchronize()
+    check("kda mfma == gdn (equal decays)", "bf16", ok, host(og), sk, host(sg))
+
+
+def test_kda_mfma_prefill_sampled():
+    cfg = gi.CONFIGS["kda_prefill"]
+    say(f"kda mfma full {cfg}")
+    d = gi.generate_kda(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, dtype=cfg.dtype, mu=cfg.mu,
+                        s0_std=cfg.s0_std, seed=cfg.seed)
+    o, s = run_kda(d, 64)
+    chains = [(0, 0), (0, 9), (0, 31)]
+    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
+    sd["g"] = np.stack([d["g"][b, :, j] for b, j in chains])[:, :, None]
+    o_ref, s_ref = oracle_kda(sd)
+    o_s = np.stack([o[b, :, j] for b, j in chains])[:, :, None]
+    s_s = np.stack([s[b, j] for b, j in chains])[:, None]
+    check("kda_prefill mfma sampled", "bf16", o_s, o_ref, s_s, s_ref)
