@@ -27,6 +27,7 @@ The same JSON line carries
   varlen        -- gdn_chunk_fwd_varlen on 64 packed sequences of 64..2048 tokens.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
+                       [--leg layer_ops|backward|kda|varlen]
 """
 from __future__ import annotations
 
@@ -313,7 +314,8 @@ def bench_kda(cfg, torch, gdn, steps=10, warmup=2):
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "tokens_per_s": B * T / kern, "kernel_ms": kern * 1e3, "alg_flops": flops,
             "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12, "peak_TFLOPs": FP32_VALU_PEAK / 1e12,
-            "frac": flops / kern / FP32_VALU_PEAK, "kernel": "kda_chunk_kernel"}
+            "frac": flops / kern / FP32_VALU_PEAK,
+            "kernels": "kda_prep_kernel + kda_state_kernel" if cfg.chunk == 64 else "kda_chunk_kernel"}
 
 
 def bench_varlen(torch, gdn, gi, steps=10, warmup=2):
@@ -378,6 +380,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen"),
+                    help="run only this secondary leg and print its result (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the gated delta rule shards by (batch, head) with no "
@@ -398,6 +402,13 @@ def main():
 
     gdn.load_library()
     cfg = gi.CONFIGS[args.workload]
+    if args.leg:
+        legs = {"layer_ops": lambda: bench_layer_ops(cfg, torch, gdn),
+                "backward": lambda: bench_backward(cfg, torch, gdn),
+                "kda": lambda: bench_kda(gi.CONFIGS["kda_prefill"], torch, gdn),
+                "varlen": lambda: bench_varlen(torch, gdn, gi)}
+        print(json.dumps({"leg": args.leg, **legs[args.leg]()}), flush=True)
+        return
     print(f"bench: prefill {cfg}", file=sys.stderr, flush=True)
     r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi)
     tokens = cfg.B * cfg.T
