@@ -17,6 +17,9 @@ may import this package.  Nothing here is shared with the HIP library, and nothi
 * :func:`kda_recurrent` (C), :func:`kda_brute_force`, :func:`kda_chunked` (numpy) -- Kimi Delta
   Attention, the delta rule with one decay per key channel ("Gated Attention Architectures",
   section 8): the definition, its dense transition matrices, and its chunkwise form.
+* :func:`transport` -- the affine state map (M, N) of a stretch of tokens, from the definition:
+  the state reached from a zero entry state, and the states reached from unit entry states with
+  the writes removed.
 * :func:`qkv_prologue`, :func:`gated_rmsnorm` (module ``layer_ops``) -- the layer steps either
   side of the recurrence: short causal conv, SiLU and q/k L2 norm; gated RMSNorm of the output.
 
@@ -33,7 +36,7 @@ from . import build as _build
 
 from .layer_ops import gated_rmsnorm, qkv_prologue, silu
 
-__all__ = ["kda_recurrent", "kda_brute_force", "kda_chunked", "recurrent", "recurrent_bwd", "decode", "brute_force", "chunked", "chunked_bwd", "max_threads",
+__all__ = ["transport", "kda_recurrent", "kda_brute_force", "kda_chunked", "recurrent", "recurrent_bwd", "decode", "brute_force", "chunked", "chunked_bwd", "max_threads",
            "load", "qkv_prologue", "gated_rmsnorm", "silu"]
 
 _lib = None
@@ -93,6 +96,28 @@ def recurrent(q, k, v, g, beta, s0=None, scale: float = 1.0, threads: int = 0):
     if rc != 0:
         raise ValueError("oracle rejected the sizes")
     return o, sf
+
+
+def transport(k, v, g, beta, threads: int = 0):
+    """The affine state map of T tokens per (batch, value head): after them the stored state is
+    M h0 + N for any entry state h0.
+
+    Every step of the recurrence, h <- alpha (I - beta k k^T) h + beta k v^T in the stored
+    orientation h = S^T ("Gated Attention Architectures", section 3, Mathematical Formulation),
+    is affine in h, so the whole stretch is too.  N is the state reached from h0 = 0.  The linear
+    part acts on each value column of h alike, so M [dk, dk] is the state reached from h0 = I with
+    every write removed (v = 0), one unit entry column per key channel.  Both are runs of
+    :func:`recurrent` (q does not enter the state; k stands in for it).
+
+    k: [B,T,Hqk,dk]; v: [B,T,Hv,dv]; g, beta: [B,T,Hv].  Returns (M [B,Hv,dk,dk],
+    N [B,Hv,dk,dv]) float64."""
+    k, v = _f64(k), _f64(v)
+    B, T, Hqk, dk = k.shape
+    Hv = v.shape[2]
+    _, N = recurrent(k, k, v, g, beta, None, threads=threads)
+    unit = np.ascontiguousarray(np.broadcast_to(np.eye(dk), (B, Hv, dk, dk)))
+    _, M = recurrent(k, k, np.zeros((B, T, Hv, dk)), g, beta, unit, threads=threads)
+    return M, N
 
 
 def recurrent_bwd(q, k, v, g, beta, s0, do, dsf=None, scale: float = 1.0, threads: int = 0):
