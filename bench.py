@@ -24,10 +24,12 @@ The same JSON line carries
                    tokens/s and the fraction of the float32 vector peak it reaches;
   kda           -- gdn_kda_chunk_fwd (Kimi Delta Attention, per-key-channel decay) on the KDA
                    workload (B1 T4096, 32/32 heads, d128): tokens/s and float32-vector fraction;
-  varlen        -- gdn_chunk_fwd_varlen on 64 packed sequences of 64..2048 tokens.
+  varlen        -- gdn_chunk_fwd_varlen on 64 packed sequences of 64..2048 tokens;
+  scan          -- gdn_chunk_fwd_scan (the affine chunk scan) against gdn_chunk_fwd on the 64K-token
+                   workload and on one GPU's share of it under an 8-way head split.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
-                       [--leg layer_ops|backward|kda|varlen]
+                       [--leg layer_ops|backward|kda|varlen|scan]
 """
 from __future__ import annotations
 
@@ -181,6 +183,51 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated
     return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets, workspace=need,
                 kernel=gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv,
                                                      cfg.chunk, dt))
+
+
+def bench_scan(torch, gdn, gi, steps=5, warmup=2):
+    """gdn_chunk_fwd_scan (each chain cut into segments: per-segment state maps, their
+    composition, then every segment from its entry state) against the unsegmented gdn_chunk_fwd,
+    on one GPU's share of the 64K-token workload under an 8-way head split (6 value heads) and
+    on the whole 64K-token workload (48 value heads)."""
+    dev = "cuda:0"
+    out = {}
+    for name, seg_list in (("qwen36_long_prefill_tp8", (2, 3, 4, 6, 8, 12)), ("qwen36_long_prefill", (2, 3, 4))):
+        cfg = gi.CONFIGS[name]
+        x = gi.generate_torch(cfg, dev)
+        o = torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=x["q"].dtype, device=dev)
+        sf = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
+        need = max(gdn.gdn_chunk_fwd_scan_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk,
+                                                          gdn.GDN_BF16, p) for p in seg_list)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        es = 2
+        alg_bytes = prefill_alg_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, es, cfg.s0_std > 0, True)
+        flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
+
+        def plain(i):
+            gdn.gdn_chunk_fwd_scan(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
+                                   segments=1, o=o, final_state=sf, workspace=ws)
+
+        _, kp = time_launches(plain, 1, steps, warmup, torch)
+        auto = gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk, gdn.GDN_BF16)
+        r = {"unsegmented_ms": kp * 1e3, "unsegmented_tokens_per_s": cfg.B * cfg.T / kp,
+             "gdn_chunk_fwd_route": auto}
+        best = None
+        for p in seg_list:
+            def scan(i, p=p):
+                gdn.gdn_chunk_fwd_scan(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], chunk=cfg.chunk,
+                                       segments=p, o=o, final_state=sf, workspace=ws)
+            _, ks = time_launches(scan, 1, steps, warmup, torch)
+            r[f"segments_{p}_ms"] = ks * 1e3
+            if best is None or ks < best[1]:
+                best = (p, ks)
+        p, ks = best
+        r.update({"best_segments": p, "best_ms": ks * 1e3, "best_tokens_per_s": cfg.B * cfg.T / ks,
+                  "speedup": kp / ks, "mfma_frac": flops / ks / MFMA_BF16_PEAK, "hbm_frac": alg_bytes / ks / HBM_PEAK})
+        out[name] = r
+        del x, o, sf, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(cfg, torch, gdn, gi, repeats=3):
@@ -380,7 +427,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen"),
+    ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen", "scan"),
                     help="run only this secondary leg and print its result (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -406,7 +453,8 @@ def main():
         legs = {"layer_ops": lambda: bench_layer_ops(cfg, torch, gdn),
                 "backward": lambda: bench_backward(cfg, torch, gdn),
                 "kda": lambda: bench_kda(gi.CONFIGS["kda_prefill"], torch, gdn),
-                "varlen": lambda: bench_varlen(torch, gdn, gi)}
+                "varlen": lambda: bench_varlen(torch, gdn, gi),
+                "scan": lambda: bench_scan(torch, gdn, gi)}
         print(json.dumps({"leg": args.leg, **legs[args.leg]()}), flush=True)
         return
     print(f"bench: prefill {cfg}", file=sys.stderr, flush=True)
@@ -483,6 +531,8 @@ def main():
         line["kda"] = bench_kda(kcfg, torch, gdn)
         print("bench: packed variable-length prefill", file=sys.stderr, flush=True)
         line["varlen"] = bench_varlen(torch, gdn, gi)
+        print("bench: affine chunk scan on the 64K-token workloads", file=sys.stderr, flush=True)
+        line["scan"] = bench_scan(torch, gdn, gi)
     print(json.dumps(line), flush=True)
 
 

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI in include/gdn.h):
 * :func:`gdn_chunk_bwd` -- backward pass of the prefill (gradients of q, k, v, g, beta, S0).
 * :func:`gdn_kda_chunk_fwd` -- Kimi Delta Attention prefill (one decay per key channel).
 * :func:`gdn_chunk_fwd_varlen` -- prefill of packed sequences of different lengths.
+* :func:`gdn_chunk_fwd_scan` -- prefill with every chain cut into segments (affine chunk scan).
+* :func:`gdn_chunk_transport` -- the affine state map (M, N) of a stretch of tokens.
 * :func:`gdn_chunk_fwd_workspace_bytes`, :func:`gdn_chunk_fwd_gated_workspace_bytes`,
   :func:`gdn_chunk_fwd_kernel_name`, :func:`gdn_status_string`.
 """
@@ -28,7 +30,9 @@ __all__ = [
     "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_kernel_name",
     "gdn_status_string", "gdn_qkv_prologue", "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated",
     "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
-    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
+    "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments", "gdn_chunk_transport",
+    "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
 
 GDN_F32 = 0
@@ -37,7 +41,9 @@ EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_worksp
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
                     "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
                     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
-                    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes")
+                    "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
+                    "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments",
+                    "gdn_chunk_transport", "gdn_chunk_transport_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -94,6 +100,16 @@ def load_library():
     lib.gdn_chunk_fwd_varlen.restype = i
     lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 7 + [i]
     lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_scan.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, i, vp, sz, vp]
+    lib.gdn_chunk_fwd_scan.restype = i
+    lib.gdn_chunk_fwd_scan_workspace_bytes.argtypes = [i] * 7 + [i, i]
+    lib.gdn_chunk_fwd_scan_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_scan_segments.argtypes = [i] * 7 + [i, i]
+    lib.gdn_chunk_fwd_scan_segments.restype = i
+    lib.gdn_chunk_transport.argtypes = [vp, vp, vp, fp, fp, fp, fp] + [i] * 7 + [i, vp, sz, vp]
+    lib.gdn_chunk_transport.restype = i
+    lib.gdn_chunk_transport_workspace_bytes.argtypes = [i] * 7 + [i]
+    lib.gdn_chunk_transport_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -120,6 +136,18 @@ def gdn_chunk_fwd_varlen_workspace_bytes(N, max_seqlen, Hqk, Hv, dk, dv, chunk=6
 
 def gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
     return int(load_library().gdn_kda_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
+
+
+def gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16, segments=1) -> int:
+    return int(load_library().gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype, segments))
+
+
+def gdn_chunk_fwd_scan_segments(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16, segments=1) -> int:
+    return int(load_library().gdn_chunk_fwd_scan_segments(B, T, Hqk, Hv, dk, dv, chunk, dtype, segments))
+
+
+def gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16) -> int:
+    return int(load_library().gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype))
 
 
 def gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, chunk=64, dtype=GDN_BF16):
@@ -443,3 +471,74 @@ def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen, initial_state
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd_varlen")
     return o, final_state
+
+
+def gdn_chunk_fwd_scan(q, k, v, g, beta, initial_state=None, output_final_state=True, chunk=64, scale=1.0,
+                       segments=4, o=None, final_state=None, workspace=None, stream=None):
+    """Prefill with each (batch, value head) chain cut into ``segments`` segments (the affine
+    chunk scan).  Arguments and results as :func:`gdn_chunk_fwd` (bf16, chunk 64, head dims 64 or
+    128)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    _check_dense("o", o, (B, T, Hv, dv), q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(q)
+    need = int(lib.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dt, int(segments)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_fwd_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), dt, float(scale),
+                                int(segments), _ptr(workspace), wbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd_scan")
+    return o, final_state
+
+
+def gdn_chunk_transport(k, v, g, beta, q=None, chunk=64, m_out=None, n_out=None, workspace=None, stream=None):
+    """The affine state map of the given tokens per (batch, value head): after them the stored
+    state is M h + N for entry state h.  k [B,T,Hqk,dk], v [B,T,Hv,dv] bf16; g, beta [B,T,Hv]
+    float32; q optional (the map does not depend on it).  Returns (M [B,Hv,dk,dk], N [B,Hv,dk,dv])
+    float32."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = k.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = k.device
+    if q is not None:
+        _check_dense("q", q, (B, T, Hqk, dk), k.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), k.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), k.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    if m_out is None:
+        m_out = torch.empty((B, Hv, dk, dk), dtype=torch.float32, device=dev)
+    if n_out is None:
+        n_out = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    _check_dense("m_out", m_out, (B, Hv, dk, dk), torch.float32, dev)
+    _check_dense("n_out", n_out, (B, Hv, dk, dv), torch.float32, dev)
+    dt = _dtype_code(k)
+    need = int(lib.gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gdn_chunk_transport(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(m_out), _ptr(n_out), B, T,
+                                 Hqk, Hv, dk, dv, int(chunk), dt, _ptr(workspace), wbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_transport")
+    return m_out, n_out

@@ -77,6 +77,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int 
     if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return 0;
     gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    const int seg = gdn::chunk_auto_segments(a);
+    if (seg > 1) return gdn::chunk_scan_workspace_bytes(a, seg);
     return gdn::chunk_mfma_workspace_bytes(a);
 }
 
@@ -87,6 +89,7 @@ const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int
     gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
     if (!gdn::chunk_mfma_supported(a)) return "simt";
+    if (gdn::chunk_auto_segments(a) > 1) return "mfma_scan";
     return gdn::chunk_mfma_split(a) ? "mfma_split" : "mfma";
 }
 
@@ -140,7 +143,9 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
     }
     gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, o, B, T, Hqk,
                                        Hv, dk, dv, chunk, dtype, scale);
-    hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st)
+    const int seg = gdn::chunk_auto_segments(a);
+    hipError_t e = seg > 1 ? gdn::launch_chunk_scan(a, seg, workspace, st)
+                 : gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st)
                                                 : gdn::launch_chunk_simt(a, st);
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
@@ -431,6 +436,142 @@ gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
     hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, workspace, st)
                                                 : gdn::launch_chunk_simt(a, st);
     return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+// ------------------------------------------------------------------ affine chunk scan
+static bool scan_supported(const gdn::ChunkArgs& a)
+{
+    return gdn::chunk_mfma_supported(a);
+}
+
+size_t gdn_chunk_fwd_scan_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                          gdn_dtype_t dtype, int segments)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK || segments < 1) return 0;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    if (!scan_supported(a) || B == 0 || T == 0) return 0;
+    return gdn::chunk_scan_workspace_bytes(a, segments);
+}
+
+int gdn_chunk_fwd_scan_segments(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype,
+                                int segments)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK || segments < 1) return 0;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    if (!scan_supported(a)) return 0;
+    if (T == 0) return 1;
+    return gdn::chunk_scan_segments(a, segments);
+}
+
+gdn_status_t gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
+                                int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, int segments,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s != GDN_OK) return s;
+    if (segments < 1) return GDN_ERR_SHAPE;
+    gdn::ChunkArgs a = make_chunk_args(q, k, v, g, beta, initial_state, final_state, o, B, T, Hqk, Hv, dk, dv,
+                                       chunk, dtype, scale);
+    if (!scan_supported(a)) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype, segments);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, initial_state, final_state, o, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = (size_t)B * T;
+    const size_t sbytes = (size_t)B * Hv * dk * dv * sizeof(float);
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rs0 = range(initial_state, initial_state ? sbytes : 0);
+    const Range rsf = range(final_state, final_state ? sbytes : 0);
+    const Range ro = range(o, work ? ntok * Hv * dv * es : 0);
+    const Range inputs[] = {rq, rk, rv, rg, rb, rs0};
+    for (const Range& r : inputs)
+        if (overlap(ro, r) || overlap(rsf, r)) {
+            // in place: the segments read the initial state (combine kernel, first segment)
+            // before the last segment writes the final state, on one stream
+            if (&r == &inputs[5] && final_state == initial_state && !overlap(ro, r)) continue;
+            return GDN_ERR_ALIAS;
+        }
+    if (overlap(ro, rsf)) return GDN_ERR_ALIAS;
+    const Range rw = range(workspace, need);
+    const Range all[] = {rq, rk, rv, rg, rb, rs0, rsf, ro};
+    for (const Range& r : all)
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
+    s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work) {
+        if (!final_state) return GDN_OK;
+        return gdn::launch_state_copy(initial_state, final_state, sbytes / sizeof(float), st) == hipSuccess
+                   ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+    return gdn::launch_chunk_scan(a, segments, workspace, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+size_t gdn_chunk_transport_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                           gdn_dtype_t dtype)
+{
+    if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return 0;
+    gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
+    if (!scan_supported(a) || B == 0 || T == 0) return 0;
+    return gdn::chunk_transport_workspace_bytes(a);
+}
+
+gdn_status_t gdn_chunk_transport(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 float* m_out, float* n_out, int B, int T, int Hqk, int Hv, int dk, int dv,
+                                 int chunk, gdn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    gdn_status_t s = check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (s != GDN_OK) return s;
+    gdn::ChunkArgs a = make_chunk_args(q ? q : k, k, v, g, beta, nullptr, nullptr, nullptr, B, T, Hqk, Hv, dk,
+                                       dv, chunk, dtype, 1.f);
+    if (!scan_supported(a)) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, dk, dv, chunk, dtype);
+    if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    if (B == 0) return GDN_OK;
+    const bool work = T > 0;
+    if (!m_out || !n_out) return GDN_ERR_NULL;
+    if (work && (!k || !v || !g || !beta)) return GDN_ERR_NULL;
+    if (need && !workspace) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, m_out, n_out, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    if (!aligned4(g) || !aligned4(beta)) return GDN_ERR_ALIGN;
+    const size_t es = dtype_bytes(dtype);
+    const size_t ntok = work ? (size_t)B * T : 0;
+    const Range rq = range(q, ntok * Hqk * dk * es), rk = range(k, ntok * Hqk * dk * es);
+    const Range rv = range(v, ntok * Hv * dv * es), rg = range(g, ntok * Hv * sizeof(float));
+    const Range rb = range(beta, ntok * Hv * sizeof(float));
+    const Range rm = range(m_out, (size_t)B * Hv * dk * dk * sizeof(float));
+    const Range rn = range(n_out, (size_t)B * Hv * dk * dv * sizeof(float));
+    const Range rw = range(workspace, need);
+    const Range others[] = {rq, rk, rv, rg, rb, rw};
+    for (const Range& r : others)
+        if (overlap(rm, r) || overlap(rn, r)) return GDN_ERR_ALIAS;
+    if (overlap(rm, rn)) return GDN_ERR_ALIAS;
+    const Range ins[] = {rq, rk, rv, rg, rb};
+    for (const Range& r : ins)
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
+    s = device_ok();
+    if (s != GDN_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!work)
+        return gdn::launch_identity_map(m_out, n_out, (size_t)B * Hv, dk, dv, st) == hipSuccess ? GDN_OK
+                                                                                              : GDN_ERR_LAUNCH;
+    return gdn::launch_chunk_transport(a, m_out, n_out, workspace, st) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,

@@ -1300,6 +1300,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
 //   two chunks ahead.
 constexpr int SLW = 2;   // loader waves of the state pass
 
+// Segments of a chain (the affine chunk scan).  Over a chunk the state map is affine,
+// h_out = M h_in + N with M = e^gL I - K~^T W and N = K~^T U (the WY form of the chunk,
+// "Gated Attention Architectures", sections 2 and 3), and such maps compose, so a chain can be
+// cut into segments of `len` chunks (grid y = segment):
+// * transport (XPORT): each segment is run from h = [0 | I] over the value columns and dk more
+//   columns whose V is zero; the value columns end as the segment's N, the extra ones as its M
+//   (written to nout [chain][seg][dk][dv] and mout [chain][seg][dk][dk]), with no output;
+// * prefill: each segment starts from hin [chain][seg][dk][dv] (the entry states the combine
+//   kernel forms from the transports) and writes its O; the last segment writes the final
+//   state.  hin null: one segment from s0.
+struct SegArgs {
+    int len;            // chunks per segment
+    const float* hin;   // prefill: entry state of every segment, or null
+    float* mout;        // transport outputs
+    float* nout;
+};
+
 template <int DK, int BV, int NW>
 struct SLds {
     static constexpr int KP = DK + 8;
@@ -1315,15 +1332,17 @@ struct SLds {
     static constexpr size_t bytes = hx + 2 * NW * hx_frags * 1024;
 };
 
-template <int DK, int DV, int NW, bool VARLEN>
+template <int DK, int DV, int NW, bool VARLEN, bool XPORT = false>
 __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const unsigned char* __restrict__ ws, const unsigned char* __restrict__ wsq, const float* s0,
-    float* sf, bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, int xcd_remap, const int* cu, int total)
+    float* sf, bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, int xcd_remap, const int* cu, int total,
+    SegArgs sg)
 {
     constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
-    constexpr int NTILE = DV / BV;
+    constexpr int NTILE = (XPORT ? DV + DK : DV) / BV;   // transport: dk more columns (M)
+    static_assert(DV % BV == 0 && DK % BV == 0, "a tile lies in the value or the M columns");
     constexpr int MT = DK / 16;
     constexpr int KB = DK / 32;
     constexpr int NLT = SLW * 64;                       // loader threads
@@ -1350,19 +1369,29 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     const bool is_loader = w == 0 || w == NW + 2;
     const bool is_chain = w >= 1 && w <= NW;
     const size_t head = (size_t)b * Hv + j;
-    const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
-    const int T_len = sq.len;
-    if (VARLEN && T_len == 0) {
+    SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
+    if (VARLEN && sq.len == 0) {
         // an empty sequence: the final state is the initial one (every wave leaves here, before
         // any barrier)
         if (is_chain) copy_state_cols<DK, DV>(s0, sf, head, c0 + (w - 1) * 16, 16, lane);
         return;
     }
-    const int NT = (T_len + CH - 1) / CH;       // this sequence's chunks
+    // this workgroup's segment: chunks cb .. cb + NT - 1 of the row, a shorter sequence that
+    // starts cb chunks in (the launcher gives every segment at least one chunk)
+    const int seg = VARLEN ? 0 : (int)blockIdx.y;
+    const int cb = seg * sg.len;
+    if (!VARLEN) {
+        const int rem = sq.len - cb * CH;
+        sq.tok0 += (size_t)cb * CH;
+        sq.len = (rem + CH - 1) / CH > sg.len ? sg.len * CH : rem;
+    }
+    const int T_len = sq.len;
+    const int NT = (T_len + CH - 1) / CH;       // this segment's chunks
     const int NTS = (T_max + CH - 1) / CH;      // chunks per row of the workspace
     const int qk_row = Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
-    const unsigned char* wh = ws + head * NTS * WS_CHUNK;
+    const unsigned char* wh = ws + (head * NTS + cb) * WS_CHUNK;
+    const bool mcols = XPORT && c0 >= DV;       // transport columns of M: V is zero
     auto cslot = [&](int c) { return smem + (size_t)(c & 1) * L::cslot; };
     auto hxp = [&](int c, int cw) {
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
@@ -1372,7 +1401,7 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
         // ================================================================= loader waves
         const int ltid = li * 64 + lane;   // loader thread index
         const bf16* kb_ = k + (sq.tok0 * Hqk + i) * DK;
-        const bf16* vb = v + (sq.tok0 * Hv + j) * DV + c0;
+        const bf16* vb = v + (sq.tok0 * Hv + j) * DV + (mcols ? 0 : c0);
         const int vrow = Hv * DV;
         bf16x8 rk[PK][2];
         bf16x8 rv[PV];
@@ -1400,10 +1429,12 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
                 rk[p][1] = *reinterpret_cast<const bf16x8*>(kc + off + 16);
             }
             const bf16* vc = vb + (size_t)t0 * vrow;
+            if (!mcols) {
 #pragma unroll
-            for (int p = 0; p < PV; ++p) {
-                const int s = min(ltid + p * NLT, CH * RV - 1);
-                rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
+                for (int p = 0; p < PV; ++p) {
+                    const int s = min(ltid + p * NLT, CH * RV - 1);
+                    rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
+                }
             }
             if (ltid < CVR) rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * ltid);
         };
@@ -1416,13 +1447,22 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
                 opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((ltid + p * NLT) % RP));
                 bf16_pair_to_op(rk[p][0], rk[p][1], dst[0], dst[1]);
             }
+            if (!mcols) {
 #pragma unroll
-            for (int p = 0; p < PV; ++p) {
-                const int s = ltid + p * NLT;
-                if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
+                for (int p = 0; p < PV; ++p) {
+                    const int s = ltid + p * NLT;
+                    if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
+                }
             }
             if (ltid < CVR) *reinterpret_cast<floatx4*>(sb + L::cv + 16 * ltid) = rc;
         };
+        if (mcols) {
+            // the M columns' V is zero in both slots for the whole segment
+            for (int s = ltid; s < CH * L::VP / 8; s += NLT)
+#pragma unroll
+                for (int slot = 0; slot < 2; ++slot)
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(cslot(slot) + L::v) + 8 * s) = bf16x8{};
+        }
         // Prefetches are issued unconditionally (chunk index clamped to the last chunk; the
         // extra loads at the end are harmless) so that every path through the loop has the same
         // memory operations in flight and each wait covers exactly the loads it needs.
@@ -1441,16 +1481,54 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     } else if (is_chain) {
         // ================================================================= chain waves
         const int cw = w - 1;
+        const int col = c0 + cw * 16;
         floatx4 hacc[1][MT];
-        load_state<DK, DV, 1>(hacc, s0, head, c0 + cw * 16, lane);
+        if constexpr (XPORT) {
+            // h = [0 | I]: zeros in the value columns, the identity in the M columns
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) hacc[0][mt][x] = 16 * mt + 4 * lg + x == col - DV + ln ? 1.f : 0.f;
+        } else if (sg.hin) {
+            load_state<DK, DV, 1>(hacc, sg.hin + (head * gridDim.y + seg) * DK * DV, 0, col, lane);
+        } else {
+            load_state<DK, DV, 1>(hacc, s0, head, col, lane);
+        }
         // T fragments of chunk c (fragment order in the workspace)
         auto load_tf = [&](int c, opx8 (&t)[6]) {
             const opx8* src = reinterpret_cast<const opx8*>(wh + (size_t)c * WS_CHUNK + WS_T);
 #pragma unroll
             for (int bk = 0; bk < 6; ++bk) t[bk] = src[bk * 64 + lane];
         };
+        // Transport M columns: V is zero there, so the chunk step is linear in h and may run on
+        // h scaled by a power of two per column (exact in float32).  Scaling each column's largest
+        // entry into [0.5, 1) before the step keeps the float16 operands made from h, R and Delta
+        // in float16's normal range however far M has decayed.
+        auto col_scale = [&]() {
+            float mx = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) mx = fmaxf(mx, fabsf(hacc[0][mt][x]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));   // the four lanes of one column
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            int e = 0;
+            frexpf(mx, &e);
+            return mx > 0.f ? ldexpf(1.f, -max(e, -120)) : 1.f;
+        };
+        auto rescale = [&](float f) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) hacc[0][mt][x] *= f;
+        };
         auto step = [&](int n, const opx8 (&tc)[6], opx8 (&tn)[6]) {
             GDN_TRACE(n, 0);
+            float sc = 1.f;
+            if (mcols) {
+                sc = col_scale();
+                rescale(sc);
+            }
             load_tf(min(n + 1, NT - 1), tn);   // unconditional: see the loaders
             const unsigned char* sb = cslot(n);
             const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
@@ -1467,6 +1545,7 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
             GDN_TRACE(n, 1);
             apply_kt<DK, 1>(hacc, akt[0], dtb, 0);
             apply_kt<DK, 1>(hacc, akt[1], dtb, 1);
+            if (mcols) rescale(1.f / sc);
             GDN_TRACE(n, 2);
             lds_barrier();
         };
@@ -1479,11 +1558,21 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
             step(n + 1, tB, tA);
         }
         if (n < NT) step(n, tA, tB);
-        store_state<DK, DV, 1>(hacc, sf, head, c0 + cw * 16, lane);
+        if constexpr (XPORT) {
+            if (col < DV)
+                store_state<DK, DV, 1>(hacc, sg.nout + (head * gridDim.y + seg) * DK * DV, 0, col, lane);
+            else
+                store_state<DK, DK, 1>(hacc, sg.mout + (head * gridDim.y + seg) * DK * DK, 0, col - DV, lane);
+        } else if (seg == (int)gridDim.y - 1) {
+            store_state<DK, DV, 1>(hacc, sf, head, col, lane);
+        }
+    } else if (XPORT) {
+        // no output: the same barriers as the other roles
+        for (int n = 0; n <= NT; ++n) lds_barrier();
     } else {
         // ================================================================= output wave
         bf16* ob = o + (sq.tok0 * Hv + j) * DV + c0;
-        const unsigned char* wqh = wsq + ((size_t)b * Hqk + i) * NTS * ws_q_bytes<DK>();
+        const unsigned char* wqh = wsq + (((size_t)b * Hqk + i) * NTS + cb) * ws_q_bytes<DK>();
         // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc);
         // double-buffered, loaded two chunks ahead of their use
         struct OutIn {
@@ -1631,31 +1720,33 @@ hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int DK, int DV, int NW, bool VARLEN>
-hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st)
+// The state pass over `nseg` segments of sg.len chunks (grid y); nseg = 1, sg.len = NT for a
+// whole chain from s0.
+template <int DK, int DV, int NW, bool VARLEN, bool XPORT = false>
+hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st, SegArgs sg, int nseg)
 {
     constexpr int BV = 16 * NW;
+    constexpr int NTILE = (XPORT ? DV + DK : DV) / BV;
     using L = SLds<DK, BV, NW>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_state_kernel<DK, DV, NW, VARLEN>;
+    auto kern = chunk_state_kernel<DK, DV, NW, VARLEN, XPORT>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
-    const long nblk = (long)a.B * a.Hv * (DV / BV);
+    const long nblk = (long)a.B * a.Hv * NTILE;
     const long per_xcd = nblk / 8;
-    const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
+    const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * NTILE) == 0) ? 1 : 0;
     const int NT = (a.T + CH - 1) / CH;
     const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((SLW + NW + 1) * 64), L::bytes, st, (const bf16*)a.q,
-                       (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0, a.sf,
-                       (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap, a.cu, a.total);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk, (unsigned)nseg), dim3((SLW + NW + 1) * 64), L::bytes, st,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0,
+                       a.sf, (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap, a.cu, a.total, sg);
     return hipGetLastError();
 }
 
-template <int DK, int DV, bool VARLEN = false>
-hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
+template <int DK, bool VARLEN>
+hipError_t launch_prep_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
-    if (!VARLEN && a.cu) return launch_split_t<DK, DV, true>(a, ws, st);
     const int grp = a.Hv / a.Hqk;
     const int NT = (a.T + CH - 1) / CH;
     const long nprep = (long)a.B * a.Hqk * NT;
@@ -1663,10 +1754,138 @@ hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
     hipLaunchKernelGGL((chunk_prep_kernel<DK, VARLEN>), dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, wsq, a.T, a.Hqk, a.Hv, grp, NT,
                        a.scale, a.cu, a.total);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+template <int DK, int DV, bool VARLEN = false>
+hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
+{
+    if (!VARLEN && a.cu) return launch_split_t<DK, DV, true>(a, ws, st);
+    hipError_t e = launch_prep_t<DK, VARLEN>(a, ws, st);
     if (e != hipSuccess) return e;
-    if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1, VARLEN>(a, ws, st);
-    return launch_state_t<DK, DV, 2, VARLEN>(a, ws, st);
+    const int NT = (a.T + CH - 1) / CH;
+    const SegArgs whole{NT, nullptr, nullptr, nullptr};
+    if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1, VARLEN>(a, ws, st, whole, 1);
+    return launch_state_t<DK, DV, 2, VARLEN>(a, ws, st, whole, 1);
+}
+
+// ---------------------------------------------------------------- affine chunk scan
+// Entry states of the segments of every chain from their transports: h_0 = S0 (zeros when
+// null), h_{s+1} = M_s h_s + N_s, float32.  One workgroup of 2 DK threads per (chain, 32-column
+// tile); each thread keeps a 4 x 4 block of the new state, M_s is staged transposed in LDS.
+template <int DK, int DV>
+__global__ __launch_bounds__(2 * DK) void seg_combine_kernel(const float* s0, const float* __restrict__ mseg,
+                                                             const float* __restrict__ nseg, float* __restrict__ hin,
+                                                             int P)
+{
+    constexpr int MP = DK + 4;   // row pitch of the transposed M (16-byte rows)
+    constexpr int NTH = 2 * DK;
+    extern __shared__ __attribute__((aligned(16))) float cmb[];
+    float* Mt = cmb;             // [DK][MP], Mt[k][m] = M[m][k]
+    float* hs = cmb + DK * MP;   // [DK][32], the current entry state's tile
+    const size_t head = blockIdx.x;
+    const int c0 = blockIdx.y * 32;
+    const int tid = threadIdx.x;
+    const int m0 = 4 * (tid >> 3), cc = 4 * (tid & 7);
+    for (int e = tid; e < DK * 8; e += NTH) {
+        const int m = e >> 3, c = 4 * (e & 7);
+        const floatx4 x = s0 ? *reinterpret_cast<const floatx4*>(s0 + (head * DK + m) * DV + c0 + c)
+                             : floatx4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<floatx4*>(hs + m * 32 + c) = x;
+        *reinterpret_cast<floatx4*>(hin + (head * P * DK + m) * DV + c0 + c) = x;
+    }
+    for (int s = 0; s + 1 < P; ++s) {
+        const float* M = mseg + (head * (P - 1) + s) * DK * DK;
+        const float* N = nseg + (head * (P - 1) + s) * DK * DV;
+        for (int e = tid; e < DK * DK / 4; e += NTH) {
+            const int m = e % DK, k4 = 4 * (e / DK);
+            const floatx4 x = *reinterpret_cast<const floatx4*>(M + (size_t)m * DK + k4);
+#pragma unroll
+            for (int y = 0; y < 4; ++y) Mt[(k4 + y) * MP + m] = x[y];
+        }
+        floatx4 acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = *reinterpret_cast<const floatx4*>(N + (size_t)(m0 + r) * DV + c0 + cc);
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < DK; ++kk) {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(Mt + kk * MP + m0);
+            const floatx4 h = *reinterpret_cast<const floatx4*>(hs + kk * 32 + cc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[r][y] = fmaf(a[r], h[y], acc[r][y]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<floatx4*>(hs + (m0 + r) * 32 + cc) = acc[r];
+            *reinterpret_cast<floatx4*>(hin + ((head * P + s + 1) * DK + m0 + r) * DV + c0 + cc) = acc[r];
+        }
+    }
+}
+
+struct ScanLayout {
+    int L, P;                       // chunks per segment, segments
+    size_t prep, mout, nout, hin, bytes;
+};
+
+ScanLayout scan_layout(const ChunkArgs& a, int segments)
+{
+    ScanLayout s{};
+    const int NT = (a.T + CH - 1) / CH;
+    s.L = (NT + segments - 1) / segments;
+    s.P = (NT + s.L - 1) / s.L;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t chains = (size_t)a.B * a.Hv;
+    s.prep = 0;
+    s.mout = up((size_t)a.B * NT * (a.Hv * (size_t)WS_CHUNK + a.Hqk * (size_t)CH * a.dk * 2));
+    s.nout = s.mout + up(chains * (s.P - 1) * a.dk * a.dk * 4);
+    s.hin = s.nout + up(chains * (s.P - 1) * a.dk * a.dv * 4);
+    s.bytes = s.hin + up(chains * s.P * a.dk * a.dv * 4);
+    return s;
+}
+
+template <int DK, int DV>
+hipError_t launch_scan_t(const ChunkArgs& a, int segments, void* ws, hipStream_t st)
+{
+    const ScanLayout sl = scan_layout(a, segments);
+    unsigned char* w = (unsigned char*)ws;
+    hipError_t e = launch_prep_t<DK, false>(a, ws, st);
+    if (e != hipSuccess) return e;
+    const long chains = (long)a.B * a.Hv;
+    float* mout = (float*)(w + sl.mout);
+    float* nout = (float*)(w + sl.nout);
+    float* hin = (float*)(w + sl.hin);
+    if (sl.P > 1) {
+        const SegArgs xs{sl.L, nullptr, mout, nout};
+        e = chains * (sl.P - 1) * ((DV + DK) / 16) <= 256
+                ? launch_state_t<DK, DV, 1, false, true>(a, ws, st, xs, sl.P - 1)
+                : launch_state_t<DK, DV, 2, false, true>(a, ws, st, xs, sl.P - 1);
+        if (e != hipSuccess) return e;
+        constexpr size_t cl = (size_t)DK * (DK + 4) * 4 + (size_t)DK * 32 * 4;
+        auto comb = seg_combine_kernel<DK, DV>;
+        e = hipFuncSetAttribute((const void*)comb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cl);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(comb, dim3((unsigned)chains, DV / 32), dim3(2 * DK), cl, st, a.s0, (const float*)mout,
+                           (const float*)nout, hin, sl.P);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const SegArgs fs{sl.L, sl.P > 1 ? hin : nullptr, nullptr, nullptr};
+    return chains * sl.P * (DV / 16) <= 256 ? launch_state_t<DK, DV, 1, false>(a, ws, st, fs, sl.P)
+                                            : launch_state_t<DK, DV, 2, false>(a, ws, st, fs, sl.P);
+}
+
+template <int DK, int DV>
+hipError_t launch_transport_t(const ChunkArgs& a, float* m_out, float* n_out, void* ws, hipStream_t st)
+{
+    hipError_t e = launch_prep_t<DK, false>(a, ws, st);
+    if (e != hipSuccess) return e;
+    const int NT = (a.T + CH - 1) / CH;
+    const SegArgs xs{NT, nullptr, m_out, n_out};
+    return (long)a.B * a.Hv * ((DV + DK) / 16) <= 256 ? launch_state_t<DK, DV, 1, false, true>(a, ws, st, xs, 1)
+                                                      : launch_state_t<DK, DV, 2, false, true>(a, ws, st, xs, 1);
 }
 
 }  // namespace
@@ -1683,6 +1902,48 @@ bool chunk_mfma_gated_fused(const ChunkArgs& a)
 {
     return chunk_mfma_supported(a) && !use_split(a) && choose_bv(a) == a.dv;
 }
+
+size_t chunk_scan_workspace_bytes(const ChunkArgs& a, int segments) { return scan_layout(a, segments).bytes; }
+
+// Segments for an unsegmented prefill call: enough that the transport pass (32-column tiles over
+// the dv + dk columns of every segment but the last) about fills the 256 compute units, used
+// only when that gives at least 3 segments of at least 8 chunks each.  With fewer the extra work
+// of the maps (about as much again as the state pass over those segments) is not repaid: on one
+// GPU's share of a 64K-token prefill under an 8-way head split (6 value heads) 6 segments took
+// 0.52 ms against 0.97 ms unsegmented, 2 segments 1.18 ms.
+int chunk_auto_segments(const ChunkArgs& a)
+{
+    if (!chunk_mfma_split(a) || a.cu || a.z || a.hst) return 1;
+    const int env = env_int("GDN_SCAN_SEGMENTS", -1);
+    if (env >= 1) return env;
+    if (env == 0) return 1;
+    const long tiles32 = (long)a.B * a.Hv * ((a.dv + a.dk) / 32);
+    const long p = 1 + 256 / tiles32;
+    const long NT = ((long)a.T + CH - 1) / CH;
+    return p >= 3 && NT >= 8 * p ? (int)p : 1;
+}
+
+int chunk_scan_segments(const ChunkArgs& a, int segments) { return scan_layout(a, segments).P; }
+
+size_t chunk_transport_workspace_bytes(const ChunkArgs& a) { return scan_layout(a, 1).mout; }
+
+#define GDN_SCAN_DISPATCH(F, ...)                                                  \
+    if (a.dk == 128 && a.dv == 128) return F<128, 128>(a, __VA_ARGS__);           \
+    if (a.dk == 128 && a.dv == 64) return F<128, 64>(a, __VA_ARGS__);             \
+    if (a.dk == 64 && a.dv == 128) return F<64, 128>(a, __VA_ARGS__);             \
+    if (a.dk == 64 && a.dv == 64) return F<64, 64>(a, __VA_ARGS__);               \
+    return hipErrorInvalidValue;
+
+hipError_t launch_chunk_scan(const ChunkArgs& a, int segments, void* ws, hipStream_t st)
+{
+    GDN_SCAN_DISPATCH(launch_scan_t, segments, ws, st)
+}
+
+hipError_t launch_chunk_transport(const ChunkArgs& a, float* m_out, float* n_out, void* ws, hipStream_t st)
+{
+    GDN_SCAN_DISPATCH(launch_transport_t, m_out, n_out, ws, st)
+}
+#undef GDN_SCAN_DISPATCH
 
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a)
 {

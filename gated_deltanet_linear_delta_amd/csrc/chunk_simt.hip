@@ -259,4 +259,28 @@ hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t s
     return hipGetLastError();
 }
 
+// The affine state map of an empty sequence: M = I [chains, dk, dk], N = 0 [chains, dk, dv].
+__global__ void identity_map_kernel(float* __restrict__ m, float* __restrict__ n, size_t chains, int dk, int dv)
+{
+    const size_t nm = chains * dk * dk, nn = chains * dk * dv;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < nm + nn; e += (size_t)gridDim.x * blockDim.x) {
+        if (e < nm) {
+            const size_t r = e % ((size_t)dk * dk);
+            m[e] = r / dk == r % dk ? 1.f : 0.f;
+        } else {
+            n[e - nm] = 0.f;
+        }
+    }
+}
+
+hipError_t launch_identity_map(float* m, float* n, size_t chains, int dk, int dv, hipStream_t st)
+{
+    const size_t total = chains * dk * (dk + dv);
+    if (total == 0) return hipSuccess;
+    size_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(identity_map_kernel, dim3((unsigned)blocks), dim3(256), 0, st, m, n, chains, dk, dv);
+    return hipGetLastError();
+}
+
 }  // namespace gdn

@@ -62,6 +62,24 @@ bool chunk_mfma_gated_fused(const ChunkArgs& a);
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, void* workspace, hipStream_t st);
 
+// Affine chunk scan on the matrix-core split path (shapes chunk_mfma_supported accepts, uniform
+// batches): each chain cut into segments whose affine state maps are formed in parallel,
+// composed, and then the segments run from their entry states.  chunk_scan_segments gives the
+// number of segments actually used for a requested count (every segment holds at least one
+// chunk).
+size_t chunk_scan_workspace_bytes(const ChunkArgs& a, int segments);
+// Segments gdn_chunk_fwd uses on its own (1: no scan), from the number of chains and chunks.
+int chunk_auto_segments(const ChunkArgs& a);
+int chunk_scan_segments(const ChunkArgs& a, int segments);
+hipError_t launch_chunk_scan(const ChunkArgs& a, int segments, void* workspace, hipStream_t st);
+// The affine map of the whole given sequence per chain: h_out = M h_in + N, M [B, Hv, dk, dk] and
+// N [B, Hv, dk, dv] float32.
+size_t chunk_transport_workspace_bytes(const ChunkArgs& a);
+hipError_t launch_chunk_transport(const ChunkArgs& a, float* m_out, float* n_out, void* workspace,
+                                  hipStream_t st);
+// M = I, N = 0 for `chains` chains (the map of an empty sequence).
+hipError_t launch_identity_map(float* m, float* n, size_t chains, int dk, int dv, hipStream_t st);
+
 // final_state <- initial_state (or zeros when it is null), for T == 0.
 hipError_t launch_state_copy(const float* s0, float* sf, size_t n, hipStream_t st);
 

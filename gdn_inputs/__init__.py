@@ -62,6 +62,10 @@ CONFIGS = {
                               chunk=64, dtype="bf16", mu=3.0, s0_std=0.02, seed=1003),
     "qwen36_long_prefill": Config("qwen36_long_prefill", B=1, T=65536, Hqk=16, Hv=48, dk=128,
                                   dv=128, chunk=64, dtype="bf16", mu=4.0, s0_std=0.0, seed=1004),
+    # one GPU's share of the Qwen3.6-27B-shaped 64K-token prefill when its heads are split eight
+    # ways (2 query/key, 6 value heads): few chains, the case the affine chunk scan is for
+    "qwen36_long_prefill_tp8": Config("qwen36_long_prefill_tp8", B=1, T=65536, Hqk=2, Hv=6, dk=128,
+                                      dv=128, chunk=64, dtype="bf16", mu=4.0, s0_std=0.0, seed=1007),
     "decode": Config("decode", B=256, T=1, Hqk=16, Hv=32, dk=128, dv=128, chunk=64,
                      dtype="bf16", mu=3.0, s0_std=0.02, seed=1005, steps=64),
     # Kimi Delta Attention (per-key-channel decay; inputs from generate_kda): the Qwen3-Next

@@ -62,9 +62,11 @@ typedef enum {
  * sequences: see gdn_chunk_fwd_kernel_name) needs, per 64-token chunk of each batch row,
  * 13,568 bytes per value head (T = (I + A)^{-1}, the masked Q K^T and the gate vectors) plus
  * 128 * dk bytes per query/key head (q as matrix-core operands), all built before the state
- * pass.  The result depends only on the arguments (and on the GDN_MFMA_PATH / GDN_DISABLE_MFMA
- * environment variables, which select the path).  Pure host function; needs no device; 0 for
- * invalid sizes.
+ * pass.  When the chains are too few to fill the GPU and long (gdn_chunk_fwd_kernel_name says
+ * "mfma_scan") it is gdn_chunk_fwd_scan_workspace_bytes for the segment count chosen.  The result
+ * depends only on the arguments (and on the GDN_MFMA_PATH / GDN_DISABLE_MFMA /
+ * GDN_SCAN_SEGMENTS environment variables, which select the path).  Pure host function; needs
+ * no device; 0 for invalid sizes.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                      gdn_dtype_t dtype);
@@ -126,9 +128,11 @@ gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, con
 /*
  * gdn_chunk_fwd_kernel_name -- which kernel family gdn_chunk_fwd would run for these sizes:
  * "mfma" (one fused matrix-core kernel, chosen when B * Hv >= 192), "mfma_split" (a parallel
- * per-chunk prep kernel, then the matrix-core state pass; fewer chains), "simt" (float32
- * vector kernel: float32 inputs, chunk != 64 or head dim 32), or NULL when the sizes are
- * unsupported.  Pure host function.
+ * per-chunk prep kernel, then the matrix-core state pass; fewer chains), "mfma_scan" (the
+ * affine chunk scan of gdn_chunk_fwd_scan: so few chains that 32-column tiles over dv + dk
+ * columns give at most 128 workgroups, cut into p = 1 + 256 / (B * Hv * (dv + dk) / 32)
+ * segments when T holds at least 8 p chunks), "simt" (float32 vector kernel: float32 inputs,
+ * chunk != 64 or head dim 32), or NULL when the sizes are unsupported.  Pure host function.
  */
 const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                       gdn_dtype_t dtype);
@@ -329,6 +333,86 @@ gdn_status_t gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
                                   int N, int max_seqlen, int total_T, int Hqk, int Hv, int dk, int dv, int chunk,
                                   gdn_dtype_t dtype, float scale, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * Affine chunk scan.  Over a chunk the state map of the gated delta rule is affine in the entry
+ * state: in the WY form of the chunk ("Gated Attention Architectures", sections 2 and 3: the
+ * DeltaNet WY representation, with the per-chunk decay products of Gated DeltaNet),
+ *     h_out = M h_in + N,   M = e^{gL} I - K~^T W  [dk, dk],   N = K~^T U  [dk, dv],
+ * with h = S^T the stored state, and such maps compose: (M2, N2) o (M1, N1) = (M2 M1, M2 N1 + N2).
+ * So a long chain can be cut into segments whose maps are formed independently (in parallel on
+ * one GPU, or one segment per GPU for context parallelism), composed into the segments' entry
+ * states, and the segments then run from those states.  Both entry points below use the
+ * matrix-core kernels: bf16 inputs, chunk 64, dk and dv 64 or 128 (else GDN_ERR_UNSUPPORTED).
+ */
+
+/*
+ * gdn_chunk_fwd_scan_workspace_bytes -- device scratch (bytes) gdn_chunk_fwd_scan needs for
+ * `segments` requested segments: the per-chunk operands of the matrix-core path (as
+ * gdn_chunk_fwd's split path), then float32 M and N of every segment but the last and the entry
+ * state of every segment, each region 256-byte aligned.  Pure host function; 0 for invalid or
+ * unsupported sizes, for B == 0 and for T == 0.
+ */
+size_t gdn_chunk_fwd_scan_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                          gdn_dtype_t dtype, int segments);
+
+/*
+ * gdn_chunk_fwd_scan_segments -- the number of segments gdn_chunk_fwd_scan uses when asked for
+ * `segments`: with NT = ceil(T / 64) chunks, segments of L = ceil(NT / segments) chunks, so
+ * ceil(NT / L) of them, each at least one chunk (1 for T == 0).  Pure host function; 0 for invalid
+ * or unsupported sizes.
+ */
+int gdn_chunk_fwd_scan_segments(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype,
+                                int segments);
+
+/*
+ * gdn_chunk_fwd_scan -- prefill with each (batch, value head) chain cut into segments: the same
+ * result as gdn_chunk_fwd up to float rounding (o, final_state and every argument as there), for
+ * workloads with too few chains to fill the GPU.  Four launches on `stream`:
+ *   1. the per-chunk operands of every chunk (all chunks in parallel);
+ *   2. the map (M, N) of every segment but the last, by running its chunks from h = [0 | I] over
+ *      the dv value columns and dk more columns whose V is zero (the value columns end as N, the
+ *      others as M);
+ *   3. the entry states, h_0 = initial_state (zeros when NULL), h_{s+1} = M_s h_s + N_s, float32;
+ *   4. every segment from its entry state, writing its O; the last writes final_state.
+ *   segments       requested count >= 1 (1: no scan, gdn_chunk_fwd's split path); see
+ *                  gdn_chunk_fwd_scan_segments for the count used
+ *   workspace      at least gdn_chunk_fwd_scan_workspace_bytes(...) bytes, 16-byte aligned,
+ *                  caller-owned, not overlapping any other argument
+ * B == 0 is a no-op; T == 0 writes final_state only.  Errors as gdn_chunk_fwd; segments < 1:
+ * GDN_ERR_SHAPE.  final_state may be initial_state exactly.
+ */
+gdn_status_t gdn_chunk_fwd_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                const float* initial_state, float* final_state, void* o, int B, int T, int Hqk,
+                                int Hv, int dk, int dv, int chunk, gdn_dtype_t dtype, float scale, int segments,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_chunk_transport_workspace_bytes -- device scratch (bytes) gdn_chunk_transport needs: the
+ * per-chunk operands of the matrix-core path.  Pure host function; 0 for invalid or unsupported
+ * sizes, for B == 0 and for T == 0.
+ */
+size_t gdn_chunk_transport_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                           gdn_dtype_t dtype);
+
+/*
+ * gdn_chunk_transport -- the affine state map of the given T tokens for every (batch, value
+ * head) chain: after these tokens the state is M h_in + N for any entry state h_in.  This is the
+ * summary one rank computes for its slice of a sequence when a sequence is split across GPUs;
+ * the ranks' maps are then composed in order (an exclusive scan) into each rank's entry state.
+ *   q              may be NULL (the map does not depend on q); otherwise as gdn_chunk_fwd
+ *   k, v, g, beta  as gdn_chunk_fwd
+ *   m_out          [B, Hv, dk, dk] float32, device, caller-owned
+ *   n_out          [B, Hv, dk, dv] float32, device, caller-owned
+ *   workspace      at least gdn_chunk_transport_workspace_bytes(...) bytes, 16-byte aligned
+ * M and N are in the stored orientation (h = S^T, [dk, dv]).  B == 0 is a no-op; T == 0 writes
+ * M = I and N = 0.  Errors as gdn_chunk_fwd; m_out or n_out overlapping each other, an input or
+ * the workspace: GDN_ERR_ALIAS.
+ */
+gdn_status_t gdn_chunk_transport(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 float* m_out, float* n_out, int B, int T, int Hqk, int Hv, int dk, int dv,
+                                 int chunk, gdn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -436,3 +436,112 @@ def test_varlen_valid_calls_report_no_device():
     assert varlen_call() == NODEV
     assert varlen_call(total=0, q=None, o=None) == NODEV
     assert varlen_call(sf=fake(5)) == NODEV
+
+
+# ------------------------------------------------------------------------- affine chunk scan
+
+SCAN_B, SCAN_T, SCAN_HQK, SCAN_HV = 1, 1000, 2, 4   # 16 chunks of 64
+
+
+def scan_call(**over):
+    lib = gdn.load_library()
+    ws_need = gdn.gdn_chunk_fwd_scan_workspace_bytes(SCAN_B, SCAN_T, SCAN_HQK, SCAN_HV, 128, 128, 64, gdn.GDN_BF16, 4)
+    a = dict(q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=fake(5), sf=fake(6), o=fake(7),
+             B=SCAN_B, T=SCAN_T, Hqk=SCAN_HQK, Hv=SCAN_HV, dk_=128, dv_=128, chunk=64, dtype=gdn.GDN_BF16, scale=1.0,
+             seg=4, ws=fake(9), wsb=ws_need, stream=None)
+    a.update(over)
+    return lib.gdn_chunk_fwd_scan(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["sf"], a["o"], a["B"],
+                                  a["T"], a["Hqk"], a["Hv"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], a["scale"],
+                                  a["seg"], a["ws"], a["wsb"], a["stream"])
+
+
+def transport_call(**over):
+    lib = gdn.load_library()
+    ws_need = gdn.gdn_chunk_transport_workspace_bytes(SCAN_B, SCAN_T, SCAN_HQK, SCAN_HV, 128, 128, 64, gdn.GDN_BF16)
+    a = dict(q=None, k=fake(1), v=fake(2), g=fake(3), beta=fake(4), m=fake(5), n=fake(6), B=SCAN_B, T=SCAN_T,
+             Hqk=SCAN_HQK, Hv=SCAN_HV, dk_=128, dv_=128, chunk=64, dtype=gdn.GDN_BF16, ws=fake(9), wsb=ws_need,
+             stream=None)
+    a.update(over)
+    return lib.gdn_chunk_transport(a["q"], a["k"], a["v"], a["g"], a["beta"], a["m"], a["n"], a["B"], a["T"], a["Hqk"],
+                                   a["Hv"], a["dk_"], a["dv_"], a["chunk"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_scan_segments_and_workspace():
+    B, T, Hqk, Hv = 1, 65536, 16, 48          # 1024 chunks
+    seg = lambda s, T=T: gdn.gdn_chunk_fwd_scan_segments(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, s)
+    assert [seg(s) for s in (1, 2, 3, 4, 7, 1024, 5000)] == [1, 2, 3, 4, 7, 1024, 1024]
+    assert seg(7, T=200) == 4                  # 4 chunks: one per segment
+    assert seg(3, T=640) == 3                  # 10 chunks: 4 + 4 + 2
+    assert seg(3, T=0) == 1 and seg(0) == 0
+    assert gdn.gdn_chunk_fwd_scan_segments(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_F32, 4) == 0
+    # operands of the split path, then M and N of all segments but the last, then the entry states
+    up = lambda x: (x + 255) // 256 * 256
+    prep = gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
+    chains = B * Hv
+    want = up(prep) + 2 * up(chains * 3 * 128 * 128 * 4) + up(chains * 4 * 128 * 128 * 4)
+    assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, 4) == want
+    assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, 1) == up(prep) + \
+        up(chains * 128 * 128 * 4)
+    assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, 0, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, 4) == 0
+    assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 32, gdn.GDN_BF16, 4) == 0
+    assert gdn.gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, 64, 128, 64, gdn.GDN_BF16) == \
+        up(gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 64, 128, 64, gdn.GDN_BF16))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(ws=None), NULL),
+    (dict(B=-1), SHAPE), (dict(T=-1), SHAPE), (dict(Hv=3), SHAPE), (dict(seg=0), SHAPE),
+    (dict(dtype=gdn.GDN_F32), UNSUP), (dict(chunk=32), UNSUP), (dict(dk_=32), UNSUP), (dict(dk_=48), UNSUP),
+    (dict(wsb=1024), WS),
+    (dict(o=ctypes.c_void_p(BASE + 7 * STRIDE + 4)), ALIGN), (dict(g=ctypes.c_void_p(BASE + 3 * STRIDE + 2)), ALIGN),
+    (dict(o=fake(0)), ALIAS), (dict(sf=fake(1)), ALIAS), (dict(ws=fake(2)), ALIAS), (dict(o=fake(6)), ALIAS),
+])
+def test_scan_rejects(over, status):
+    assert scan_call(**over) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(m=None), NULL), (dict(n=None), NULL), (dict(k=None), NULL), (dict(ws=None), NULL),
+    (dict(T=-1), SHAPE), (dict(Hv=3), SHAPE),
+    (dict(dtype=gdn.GDN_F32), UNSUP), (dict(chunk=16), UNSUP),
+    (dict(wsb=16), WS), (dict(m=ctypes.c_void_p(BASE + 5 * STRIDE + 8)), ALIGN),
+    (dict(m=fake(6)), ALIAS), (dict(n=fake(2)), ALIAS), (dict(m=fake(9)), ALIAS),
+])
+def test_transport_rejects(over, status):
+    assert transport_call(**over) == status
+
+
+def test_scan_transport_noops():
+    assert scan_call(B=0, q=None, ws=None, wsb=0) == OK
+    assert transport_call(B=0, k=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="valid calls on fake pointers are only safe where no device exists")
+def test_scan_transport_valid_calls_report_no_device():
+    assert scan_call() == NODEV
+    assert scan_call(sf=fake(5)) == NODEV                       # in place
+    assert scan_call(T=0, ws=None, wsb=0, q=None, o=None) == NODEV
+    assert transport_call() == NODEV
+    assert transport_call(q=fake(0)) == NODEV
+    assert transport_call(T=0, ws=None, wsb=0) == NODEV
+
+
+def test_chunk_fwd_routes_scarce_long_chains_to_the_scan(monkeypatch):
+    """gdn_chunk_fwd cuts chains into segments by itself when 32-column tiles over dv + dk give at
+    most 128 workgroups and every segment keeps at least 8 chunks."""
+    name = lambda B, T, Hqk, Hv: gdn.gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
+    ws = lambda B, T, Hqk, Hv: gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
+    scan_ws = lambda B, T, Hqk, Hv, p: gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64,
+                                                                            gdn.GDN_BF16, p)
+    assert name(1, 65536, 2, 6) == "mfma_scan"          # 6 chains: 48 tiles -> 6 segments
+    assert ws(1, 65536, 2, 6) == scan_ws(1, 65536, 2, 6, 6)
+    assert name(1, 65536, 16, 16) == "mfma_scan"        # 128 tiles -> 3 segments
+    assert ws(1, 65536, 16, 16) == scan_ws(1, 65536, 16, 16, 3)
+    assert name(1, 65536, 16, 48) == "mfma_split"       # 384 tiles: the chains fill the chip
+    assert name(1, 4096, 16, 32) == "mfma_split"        # 256 tiles: 2 segments would not pay
+    assert name(1, 2000, 1, 1) == "mfma_split"          # 33 segments would hold under 8 chunks
+    assert name(1, 20000, 1, 1) == "mfma_scan"
+    monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")
+    assert name(1, 65536, 2, 6) == "mfma_split"
+    assert ws(1, 65536, 2, 6) == gdn.gdn_chunk_fwd_scan_workspace_bytes(1, 65536, 2, 6, 128, 128, 64,
+                                                                        gdn.GDN_BF16, 1) - 6 * 128 * 128 * 4
