@@ -116,23 +116,28 @@ __global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, 
             bs[tid] = tid < n ? beta[off] : 0.f;
         }
         __syncthreads();
-        if (tid == 0) {
-            float acc = 0.f;
-#pragma unroll 4
-            for (int r = 0; r < BW_C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
+            float x = tid < BW_C ? gcs[tid] : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const float y = __shfl_up(x, sh, 64);
+                if (tid >= sh) x += y;
+            }
+            const float last = __shfl(x, BW_C - 1, 64);
+            if (tid < BW_C) {
+                gcs[tid] = x;
+                egs[tid] = expf(x);
+                eds[tid] = expf(last - x);
+            }
         }
         __syncthreads();
-        if (tid < BW_C) {
-            egs[tid] = expf(gcs[tid]);
-            eds[tid] = expf(gcs[BW_C - 1] - gcs[tid]);
-        }
         // A (strictly lower) and M (lower including the diagonal)
         for (int e = tid; e < BW_C * BW_C; e += DH_NT) {
             const int r = e / BW_C, s = e % BW_C;
             float a = 0.f, mm = 0.f;
             if (s <= r) {
                 float kk = 0.f, qk = 0.f;
-#pragma unroll 4
+#pragma unroll 8
                 for (int m = 0; m < DK; ++m) {
                     kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
                     qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, 
         for (int e = tid; e < BW_C * BW_BV; e += DH_NT) {
             const int r = e / BW_BV, c = e % BW_BV;
             float x = 0.f, y = 0.f;
-#pragma unroll 4
+#pragma unroll 8
             for (int m = 0; m < DK; ++m) x = fmaf(Ks[r * KP + m], dhs[m * BW_BV + c], x);
 #pragma unroll 4
             for (int s = r; s < BW_C; ++s) y = fmaf(Ms[s * BW_CP + r], dOs[s * BW_VP + c], y);
@@ -298,22 +303,27 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
             dMs[e] = 0.f;
         }
         __syncthreads();
-        if (tid == 0) {
-            float acc = 0.f;
-#pragma unroll 4
-            for (int r = 0; r < BW_C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
+            float x = tid < BW_C ? gcs[tid] : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const float y = __shfl_up(x, sh, 64);
+                if (tid >= sh) x += y;
+            }
+            const float last = __shfl(x, BW_C - 1, 64);
+            if (tid < BW_C) {
+                gcs[tid] = x;
+                egs[tid] = expf(x);
+                eds[tid] = expf(last - x);
+            }
         }
         __syncthreads();
-        if (tid < BW_C) {
-            egs[tid] = expf(gcs[tid]);
-            eds[tid] = expf(gcs[BW_C - 1] - gcs[tid]);
-        }
         for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
             const int r = e / BW_C, s = e % BW_C;
             float gg = 0.f, mm = 0.f;
             if (s <= r) {
                 float kk = 0.f, qk = 0.f;
-#pragma unroll 4
+#pragma unroll 8
                 for (int m = 0; m < DK; ++m) {
                     kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
                     qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
                 float u = 0.f, wh = 0.f, kd = 0.f, md = 0.f;
 #pragma unroll 4
                 for (int s = 0; s <= r; ++s) u = fmaf(Tm[r * BW_CP + s] * bs[s], Vs[s * BW_VP + c], u);
-#pragma unroll 4
+#pragma unroll 8
                 for (int m = 0; m < DK; ++m) {
                     wh = fmaf(Ws[r * KP + m], hs[m * HP + c], wh);
                     kd = fmaf(Ks[r * KP + m], dhs[m * HP + c], kd);
@@ -394,7 +404,7 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
                 float tdu = 0.f, qh = 0.f;
 #pragma unroll 4
                 for (int s = r; s < BW_C; ++s) tdu = fmaf(Tm[s * BW_CP + r], dDs[s * BW_VP + c], tdu);
-#pragma unroll 4
+#pragma unroll 8
                 for (int m = 0; m < DK; ++m) qh = fmaf(Qs[r * KP + m], hs[m * HP + c], qh);
                 if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu);
                 P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu;
@@ -441,7 +451,8 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         }
 
         // ---- the terms that need every column: dW, X, dM, dT are complete now
-        red[tid] = dgl;
+        dgl = xor_sum(dgl, 1);
+        if ((tid & 63) == 0) red[tid >> 6] = dgl;
         __syncthreads();
         float* dWs = hs;    // [C][KP]
         float* Xs = dhs;    // [C][KP]
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         if (tid == 0) {
             float s = 0.f;
 #pragma unroll 4
-            for (int x = 0; x < BW_NT; ++x) s += red[x];
+            for (int x = 0; x < BW_NT / 64; ++x) s += red[x];
             red[BW_NT] = egs[BW_C - 1] * s;   // e^gL <dh', h>
         }
         __syncthreads();

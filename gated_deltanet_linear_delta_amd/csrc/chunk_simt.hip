@@ -48,7 +48,8 @@ struct SimtLds {
 
 }  // namespace
 
-template <typename T, int DK, int DV, int BV>
+// OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
+template <typename T, int DK, int DV, int BV, bool OUT>
 __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
@@ -109,10 +110,10 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
             if (r < n) {
                 const size_t off = ((tok0 + t0 + r) * Hqk + i) * DK + m;
                 kv = to_f32(k[off]);
-                qv = to_f32(q[off]) * scale;
+                if (OUT) qv = to_f32(q[off]) * scale;
             }
             Ks[r * L::KP + m] = kv;
-            Qs[r * L::KP + m] = qv;
+            if (OUT) Qs[r * L::KP + m] = qv;
         }
         for (int e = tid; e < C * BV; e += SIMT_NT) {
             const int r = e / BV, c = e % BV;
@@ -124,15 +125,21 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
             bs[tid] = tid < n ? beta[off] : 0.f;
         }
         __syncthreads();
-        if (tid == 0) {  // per-chunk log-decay cumsum (C <= 64 terms)
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) { acc += gcs[r]; gcs[r] = acc; }
+        if (tid < 64) {  // per-chunk log-decay cumsum (C <= 64 terms): a scan across wave 0
+            float x = tid < C ? gcs[tid] : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < 64; sh <<= 1) {
+                const float y = __shfl_up(x, sh, 64);
+                if (tid >= sh) x += y;
+            }
+            const float last = __shfl(x, C - 1, 64);
+            if (tid < C) {
+                gcs[tid] = x;
+                egs[tid] = expf(x);
+                eds[tid] = expf(last - x);
+            }
         }
         __syncthreads();
-        if (tid < C) {
-            egs[tid] = expf(gcs[tid]);
-            eds[tid] = expf(gcs[C - 1] - gcs[tid]);
-        }
         // A (strictly lower, beta-scaled) and the output mask matrix (lower incl. diagonal).
         for (int e = tid; e < C * C; e += SIMT_NT) {
             const int r = e / C, c = e % C;
@@ -140,8 +147,9 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
             if (c <= r) {
                 float kk = 0.f, qk = 0.f;
                 for (int m = 0; m < DK; ++m) {
-                    kk = fmaf(Ks[r * L::KP + m], Ks[c * L::KP + m], kk);
-                    qk = fmaf(Qs[r * L::KP + m], Ks[c * L::KP + m], qk);
+                    const float kc = Ks[c * L::KP + m];
+                    kk = fmaf(Ks[r * L::KP + m], kc, kk);
+                    if (OUT) qk = fmaf(Qs[r * L::KP + m], kc, qk);
                 }
                 const float gam = expf(gcs[r] - gcs[c]);
                 aq = gam * qk;
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
                 for (int m = 0; m < DK; ++m) {
                     const float hm = hs[m * BV + c];
                     x = fmaf(Ks[r * L::KP + m], hm, x);
-                    y = fmaf(Qs[r * L::KP + m], hm, y);
+                    if (OUT) y = fmaf(Qs[r * L::KP + m], hm, y);
                 }
                 Rs[e] = bs[r] * (Vs[e] - egs[r] * x);
                 qh[p] = egs[r] * y;
@@ -182,22 +190,31 @@ __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
         }
         __syncthreads();
         // O = exp(gc) Q h0 + Aq Delta
+        if (OUT) {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = tid + p * SIMT_NT;
-            if (e < C * BV) {
-                const int r = e / BV, c = e % BV;
-                float acc = qh[p];
-                for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
-                if (o && r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
+            for (int p = 0; p < PER; ++p) {
+                const int e = tid + p * SIMT_NT;
+                if (e < C * BV) {
+                    const int r = e / BV, c = e % BV;
+                    float acc = qh[p];
+                    for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
+                    if (r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
+                }
             }
         }
-        // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T
+        // K~ = exp(gc_C - gc_r) k_r in place (K is not read again in this chunk)
+        for (int e = tid; e < C * DK; e += SIMT_NT) {
+            const int r = e / DK, m = e % DK;
+            Ks[r * L::KP + m] *= eds[r];
+        }
+        __syncthreads();
+        // h1 = exp(gc_C) h0 + sum_r K~_r Delta_r^T
         const float ec = egs[C - 1];
         for (int e = tid; e < DK * BV; e += SIMT_NT) {
             const int m = e / BV, c = e % BV;
             float acc = ec * hs[e];
-            for (int r = 0; r < C; ++r) acc = fmaf(eds[r] * Ks[r * L::KP + m], Rs[r * BV + c], acc);
+#pragma unroll 8
+            for (int r = 0; r < C; ++r) acc = fmaf(Ks[r * L::KP + m], Rs[r * BV + c], acc);
             hs[e] = acc;
         }
     }
@@ -215,7 +232,7 @@ static hipError_t launch_simt_t(const ChunkArgs& a, hipStream_t st)
 {
     constexpr int BV = DV < 32 ? DV : 32;
     using L = SimtLds<DK, BV>;
-    auto kern = chunk_simt_kernel<T, DK, DV, BV>;
+    auto kern = a.o ? chunk_simt_kernel<T, DK, DV, BV, true> : chunk_simt_kernel<T, DK, DV, BV, false>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)L::bytes);
     if (e != hipSuccess) return e;
