@@ -17,21 +17,23 @@
 //   dA = strictly-lower(-T^T dT T^T),  and the gates' and keys' terms of every product;
 //   dg = reverse cumulative sum of dgc inside the chunk.
 //
-// Three launches (chunks of 32 positions, value columns in tiles of 32):
-// 1. the float32 forward kernel run again, storing the state entering every chunk (workspace H);
-// 2. bwd_dh_kernel: the reverse state pass, one workgroup per (batch, value head, column tile),
-//    storing each chunk's exit-state gradient (workspace dH) and the initial state's gradient;
-// 3. bwd_chunk_kernel: one workgroup per (batch, query/key head, chunk), over the value heads of
+// Two launches (chunks of 32 positions, value columns in tiles of 32):
+// 1. bwd_pass_kernel, two independent sequential passes side by side, one workgroup per (batch,
+//    value head, column tile) each: the float32 forward chunk step run again, storing the state
+//    entering every chunk (workspace H), and the reverse state pass, storing each chunk's
+//    exit-state gradient (workspace dH) and the initial state's gradient;
+// 2. bwd_chunk_kernel: one workgroup per (batch, query/key head, chunk), over the value heads of
 //    the group and the column tiles in turn, with dq and dk accumulated in registers, so every
 //    gradient is written once (no atomics, deterministic).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "simt_chunk.hpp"
 
 namespace gdn {
 
 namespace {
 
-constexpr int BW_NT = 256;   // threads per workgroup of the per-chunk kernel
+constexpr int BW_NT = 1024;   // threads per workgroup of the per-chunk kernel
 constexpr int DH_NT = 1024;  // threads per workgroup of the reverse state pass
 constexpr int BW_C = 32;     // chunk length of the backward pass
 constexpr int BW_BV = 32;    // value columns per tile
@@ -59,15 +61,15 @@ struct DhLds {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                       const float* __restrict__ g, const float* __restrict__ beta,
-                                                       const T* __restrict__ dout, const float* __restrict__ dsf,
-                                                       float* __restrict__ dH, float* __restrict__ ds0, int T_len,
-                                                       int Hqk, int Hv, int grp, float scale)
+__device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, const T* __restrict__ q,
+                                            const T* __restrict__ k, const float* __restrict__ g,
+                                            const float* __restrict__ beta, const T* __restrict__ dout,
+                                            const float* __restrict__ dsf, float* __restrict__ dH,
+                                            float* __restrict__ ds0, int T_len, int Hqk, int Hv, int grp,
+                                            float scale)
 {
     using L = DhLds<DK>;
     constexpr int KP = L::KP;
-    extern __shared__ float lds[];
     float* Ks = lds + L::k;
     float* Qs = lds + L::q;
     float* dOs = lds + L::dO;
@@ -80,9 +82,8 @@ __global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, 
     float* eds = lds + L::ed;
     float* bs = lds + L::bt;
 
-    const int head = blockIdx.x;   // b * Hv + j
-    const int b = head / Hv, j = head - b * Hv, i = j / grp;
-    const int c0 = blockIdx.y * BW_BV;
+    const int b = head / Hv, j = head - b * Hv, i = j / grp;   // head = b * Hv + j
+    const int c0 = tile * BW_BV;
     const int tid = threadIdx.x;
     const int NT = (T_len + BW_C - 1) / BW_C;
     const size_t sbase = (size_t)head * DK * DV + c0;
@@ -190,6 +191,33 @@ __global__ __launch_bounds__(DH_NT) void bwd_dh_kernel(const T* __restrict__ q, 
     }
 }
 
+// The two sequential passes of the backward in one launch, side by side: workgroups
+// 0 .. n_chains * NTILE - 1 recompute the states entering every chunk (the float32 forward chunk
+// step, no output), the others run the reverse state pass.  The passes do not depend on each
+// other, and each has only one workgroup per (batch, value head, column tile), so together they
+// fill twice as many compute units as either alone.  1,024 threads per workgroup for both.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, const float* s0, const T* __restrict__ dout, const float* __restrict__ dsf,
+    float* __restrict__ H, float* __restrict__ dH, float* __restrict__ ds0, int T_len, int Hqk, int Hv, int grp,
+    float scale, int n_state_blocks)
+{
+    constexpr int BV = DV < BW_BV ? DV : BW_BV;
+    static_assert(BV == BW_BV || DV < BW_BV, "one column tiling for both passes");
+    constexpr int NTILE = DV / BV;
+    extern __shared__ float lds[];
+    const int bid = blockIdx.x;
+    if (bid < n_state_blocks) {
+        simt_chunk_body<T, DK, DV, BV, false, DH_NT>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
+                                                      nullptr, H, T_len, Hqk, Hv, grp, BW_C, scale, nullptr, 0);
+    } else {
+        const int x = bid - n_state_blocks;
+        bwd_dh_body<T, DK, DV>(lds, x / NTILE, x % NTILE, q, k, g, beta, dout, dsf, dH, ds0, T_len, Hqk, Hv, grp,
+                               scale);
+    }
+}
+
 // ------------------------------------------------------------------- per-chunk gradients
 
 template <int DK>
@@ -225,7 +253,7 @@ struct BwLds {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(BW_NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_chunk_kernel(
+__global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ H,
     const float* __restrict__ dH, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
@@ -615,23 +643,20 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
     const int NT = (a.T + BW_C - 1) / BW_C;
     float* Hs = a.ws;
     float* dHs = a.ws + (size_t)a.B * a.Hv * NT * DK * DV;
-    // 1. states entering every chunk (the float32 forward kernel, no output)
-    ChunkArgs f;
-    f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.beta = a.beta; f.s0 = a.s0; f.sf = nullptr; f.o = nullptr;
-    f.B = a.B; f.T = a.T; f.Hqk = a.Hqk; f.Hv = a.Hv; f.dk = DK; f.dv = DV; f.chunk = BW_C;
-    f.dtype_bf16 = a.dtype_bf16; f.scale = a.scale; f.hst = Hs;
-    hipError_t e = launch_chunk_simt(f, st);
-    if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
-    // 2. reverse state pass
+    hipError_t e;
+    // 1 + 2. the states entering every chunk and the reverse state pass, in one launch
     {
-        using L = DhLds<DK>;
-        auto kern = bwd_dh_kernel<T, DK, DV>;
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        constexpr int BV = DV < BW_BV ? DV : BW_BV;
+        constexpr size_t lb = SimtLds<DK, BV>::bytes > DhLds<DK>::bytes ? SimtLds<DK, BV>::bytes : DhLds<DK>::bytes;
+        static_assert(lb <= 160 * 1024, "LDS budget");
+        auto kern = bwd_pass_kernel<T, DK, DV>;
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lb);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BW_BV), dim3(DH_NT), L::bytes, st, (const T*)a.q,
-                           (const T*)a.k, a.g, a.beta, (const T*)a.dout, a.dsf, dHs, a.ds0, a.T, a.Hqk, a.Hv, grp,
-                           a.scale);
+        const int nblk = a.B * a.Hv * (DV / BV);
+        hipLaunchKernelGGL(kern, dim3((unsigned)(2 * nblk)), dim3(DH_NT), lb, st, (const T*)a.q, (const T*)a.k,
+                           (const T*)a.v, a.g, a.beta, a.s0, (const T*)a.dout, a.dsf, Hs, dHs, a.ds0, a.T, a.Hqk,
+                           a.Hv, grp, a.scale, nblk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
