@@ -2024,8 +2024,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
     float* Gs = Qs + CH * KP;
     float* As = Gs + CH * KP;
     float* Aqs = As + CH * AP;
-    float* Ts = Aqs + CH * AP;
-    float* bs = Ts + CH * AP;
+    float* bs = Aqs + CH * AP;
 
     const int c = blockIdx.x % NT;
     const int head = blockIdx.x / NT;   // b * Hv + j
@@ -2048,17 +2047,31 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
     }
     if (tid < CH) bs[tid] = tid < n ? beta[((size_t)b * T_len + t0 + tid) * Hv + j] : 0.f;
     __syncthreads();
-    for (int m = tid; m < DK; m += KQ_NT) {
-        float acc = 0.f;
-        for (int r = 0; r < CH; ++r) {
-            acc += Gs[r * KP + m];
-            Gs[r * KP + m] = acc;
+    // per-channel cumsum down the 64 rows: 8 lanes per channel, 8 rows each, the lanes' totals
+    // scanned across the 8-lane group
+    static_assert(DK * 8 <= KQ_NT, "eight lanes per channel");
+    if (tid < DK * 8) {
+        const int m = tid >> 3, rg = tid & 7;
+        float x[8];
+        float run = 0.f;
+#pragma unroll
+        for (int y = 0; y < 8; ++y) {
+            run += Gs[(8 * rg + y) * KP + m];
+            x[y] = run;
         }
+        float pre = run;   // inclusive scan of the group totals over rg
+#pragma unroll
+        for (int sh = 1; sh < 8; sh <<= 1) {
+            const float u = __shfl_up(pre, sh, 8);
+            if (rg >= sh) pre += u;
+        }
+        pre -= run;        // exclusive
+#pragma unroll
+        for (int y = 0; y < 8; ++y) Gs[(8 * rg + y) * KP + m] = x[y] + pre;
     }
     __syncthreads();
-    // A (beta-scaled, strictly lower) and Aq (lower including the diagonal): the upper parts are
-    // zeros, the CH (CH + 1) / 2 lower pairs are dealt out evenly (pair p is row r, column s with
-    // p = r (r + 1) / 2 + s)
+    // A (beta-scaled, strictly lower) and Aq (lower including the diagonal); the upper parts are
+    // zeros.
     for (int e = tid; e < CH * CH; e += KQ_NT) {
         const int r = e / CH, s = e % CH;
         if (s > r) {
@@ -2066,36 +2079,81 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
             Aqs[r * AP + s] = 0.f;
         }
     }
-    for (int p = tid; p < CH * (CH + 1) / 2; p += KQ_NT) {
-        int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-        r += (r + 1) * (r + 2) / 2 <= p;   // round-off guard: r (r + 1) / 2 <= p < (r + 1) (r + 2) / 2
-        r -= r * (r + 1) / 2 > p;
-        const int s = p - r * (r + 1) / 2;
-        float kk = 0.f, qk = 0.f;
-#pragma unroll 4
-        for (int m = 0; m < DK; ++m) {
-            const float w = __expf(Gs[r * KP + m] - Gs[s * KP + m]) * Ks[s * KP + m];
-            kk = fmaf(Ks[r * KP + m], w, kk);
-            qk = fmaf(Qs[r * KP + m], w, qk);
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    if (w < 6) {
+        // The six 16 x 16 blocks below the diagonal blocks, one wave each, on the matrix cores.
+        // Block row R, block column S < R: the last row p = 16 S + 15 of block S lies between
+        // every pair (r > p >= s), so each term splits into two factors of at most |k|:
+        //     k_rm k_sm e^(gc_rm - gc_sm) = (k_rm e^(gc_rm - gc_pm)) (k_sm e^(gc_pm - gc_sm)),
+        // float16 operands formed in registers (A: rows of block R, B: rows of block S; both
+        // take channel 32 kk + 8 lg + x in element x of lane group lg, so the sum pairs channels).
+        const int R = w < 3 ? w + 1 : (w < 5 ? w - 1 : 3);
+        const int S = w < 3 ? 0 : (w < 5 ? 1 : 2);
+        const int pr = 16 * S + 15;
+        const int ra = 16 * R + ln, sb = 16 * S + ln;
+        floatx4 ca = {0.f, 0.f, 0.f, 0.f}, cq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            opx8 fa, fq, fb;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const int m = 32 * kk + 8 * lg + x;
+                const float gp = Gs[pr * KP + m];
+                const float er = __expf(Gs[ra * KP + m] - gp);
+                const float es = __expf(gp - Gs[sb * KP + m]);
+                fa[x] = (op_t)(Ks[ra * KP + m] * er);
+                fq[x] = (op_t)(Qs[ra * KP + m] * er);
+                fb[x] = (op_t)(Ks[sb * KP + m] * es);
+            }
+            ca = mfma32(fa, fb, ca);
+            cq = mfma32(fq, fb, cq);
         }
-        As[r * AP + s] = s < r ? bs[r] * kk : 0.f;
-        Aqs[r * AP + s] = qk;
-    }
-    __syncthreads();
-    // T = (I + A)^{-1}, column s by forward substitution, one thread per column.  The sum runs
-    // over u < r for every lane (T[u][s] = 0 above the diagonal is already stored), so the lanes
-    // keep one trip count and the unrolled reads issue together.
-    if (tid < CH) {
-        const int s = tid;
-        for (int r = 0; r < CH; ++r) {
-            float acc = 0.f;
-#pragma unroll 8
-            for (int u = 0; u < r; ++u) acc = fmaf(As[r * AP + u], Ts[u * AP + s], acc);
-            Ts[r * AP + s] = r == s ? 1.f : (r > s ? -acc : 0.f);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * lg + x;   // accumulator row 4 lg + x, column ln
+            As[r * AP + sb] = bs[r] * ca[x];
+            Aqs[r * AP + sb] = cq[x];
+        }
+    } else {
+        // The four diagonal blocks (16 * 17 / 2 pairs each) on the vector units: pairwise decays
+        // as exponentials of differences, one pair per lane of waves 6 .. 15 (pair t of a block is
+        // row r, column s with t = r (r + 1) / 2 + s).
+        for (int pq = tid - 6 * 64; pq < 4 * 136; pq += KQ_NT - 6 * 64) {
+            const int blk = pq / 136, t = pq - blk * 136;
+            int r = (int)((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+            r += (r + 1) * (r + 2) / 2 <= t;   // round-off guard: r (r + 1) / 2 <= t < (r + 1) (r + 2) / 2
+            r -= r * (r + 1) / 2 > t;
+            const int s = 16 * blk + t - r * (r + 1) / 2;
+            r += 16 * blk;
+            float kk = 0.f, qk = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < DK; ++m) {
+                const float wv = __expf(Gs[r * KP + m] - Gs[s * KP + m]) * Ks[s * KP + m];
+                kk = fmaf(Ks[r * KP + m], wv, kk);
+                qk = fmaf(Qs[r * KP + m], wv, qk);
+            }
+            As[r * AP + s] = s < r ? bs[r] * kk : 0.f;
+            Aqs[r * AP + s] = qk;
         }
     }
     __syncthreads();
     unsigned char* wb = ws + ((size_t)head * NT + c) * W::bytes;
+    // T = (I + A)^{-1}, column s by forward substitution, one thread per column, the column in
+    // registers (fully unrolled: no LDS round trip between rows; A's row is a broadcast read),
+    // written straight to the workspace as float16.
+    if (tid < CH) {
+        const int s = tid;
+        op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
+        float t[CH];
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int u = 0; u < r; ++u) acc = fmaf(As[r * AP + u], t[u], acc);
+            t[r] = r == s ? 1.f : (r > s ? -acc : 0.f);
+            tw[r * CH + s] = (op_t)t[r];
+        }
+    }
     op_t* kh = reinterpret_cast<op_t*>(wb + W::kh);
     op_t* kt = reinterpret_cast<op_t*>(wb + W::kt);
     op_t* qh = reinterpret_cast<op_t*>(wb + W::qh);
@@ -2106,13 +2164,8 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
         kt[e] = (op_t)(__expf(gl - gr) * Ks[r * KP + m]);
         qh[e] = (op_t)(__expf(gr) * Qs[r * KP + m]);
     }
-    op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
     op_t* aw = reinterpret_cast<op_t*>(wb + W::aq);
-    for (int e = tid; e < CH * CH; e += KQ_NT) {
-        const int r = e / CH, s = e % CH;
-        tw[e] = (op_t)Ts[r * AP + s];
-        aw[e] = (op_t)Aqs[r * AP + s];
-    }
+    for (int e = tid; e < CH * CH; e += KQ_NT) aw[e] = (op_t)Aqs[(e / CH) * AP + e % CH];
     float* bw = reinterpret_cast<float*>(wb + W::bt);
     float* ew = reinterpret_cast<float*>(wb + W::el);
     if (tid < CH) bw[tid] = bs[tid];
@@ -2122,7 +2175,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
 template <int DK>
 constexpr size_t kda_prep_lds_bytes()
 {
-    return ((size_t)3 * CH * (DK + 1) + (size_t)3 * CH * (CH + 1) + CH) * sizeof(float);
+    return ((size_t)3 * CH * (DK + 1) + (size_t)2 * CH * (CH + 1) + CH) * sizeof(float);
 }
 
 // LDS of the state kernel: two slots, each Kh, Kt, Qh [64][DK+8] f16 (column-permuted), T, Aq
