@@ -2218,37 +2218,51 @@ __global__ __launch_bounds__(256) void kda_state_kernel(const bf16* __restrict__
     const size_t v_row = (size_t)Hv * DV;
     const bf16* vb = v + ((size_t)b * T_len * Hv + j) * DV + c0;
 
-    // loaders (waves 1..3): chunk c into slot c & 1
-    auto stage = [&](int c) {
-        unsigned char* sb = smem + (size_t)(c & 1) * L::slot;
+    // loaders (waves 1..3): chunk c's operands are loaded into registers one chunk period before
+    // they are stored into LDS slot c & 1, so the global-load latency overlaps a whole chunk of
+    // the chain wave's work.
+    constexpr int RK = DK / 8;
+    constexpr int NK = (3 * CH * RK + 191) / 192, NM = (2 * CH * 8 + 191) / 192, NE = (DK + 191) / 192;
+    const int lt = (int)threadIdx.x - 64;   // loader thread 0..191 (negative on the chain wave)
+    struct Stage {
+        opx8 xk[NK], xm[NM];   // Kh, Kt, Qh runs; T, Aq runs
+        bf16x8 xv;             // V run (64 rows x 2 runs of 8)
+        float bt, el[NE];      // beta; e^gL per channel
+    };
+    // Every load is issued unconditionally with its index clamped (the chunk index too), so each
+    // path has the same loads in flight.
+    auto load = [&](int c, Stage& x) {
         const unsigned char* wb = ws + (head * NT + c) * W::bytes;
-        const int lt = threadIdx.x - 64;   // 0..191
-        // Kh, Kt, Qh: 3 x 64 rows x DK/8 runs of 8; T, Aq: 2 x 64 rows x 8 runs.  Every global
-        // load is issued before the first LDS store, so their latencies overlap.
-        constexpr int RK = DK / 8;
-        constexpr int NK = (3 * CH * RK + 191) / 192, NM = (2 * CH * 8 + 191) / 192;
-        opx8 xk[NK], xm[NM];
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
             const int e = min(lt + p * 192, 3 * CH * RK - 1);
             const int mtx = e / (CH * RK), rr = (e / RK) % CH, c8 = (e % RK) * 8;
-            xk[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::kh : mtx == 1 ? W::kt : W::qh) +
-                                                    ((size_t)rr * DK + c8) * 2);
+            x.xk[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::kh : mtx == 1 ? W::kt : W::qh) +
+                                                     ((size_t)rr * DK + c8) * 2);
         }
 #pragma unroll
         for (int p = 0; p < NM; ++p) {
             const int e = min(lt + p * 192, 2 * CH * 8 - 1);
             const int mtx = e / (CH * 8), rr = (e / 8) % CH, c8 = (e % 8) * 8;
-            xm[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::tm : W::aq) + ((size_t)rr * CH + c8) * 2);
+            x.xm[p] = *reinterpret_cast<const opx8*>(wb + (mtx == 0 ? W::tm : W::aq) + ((size_t)rr * CH + c8) * 2);
         }
+        const int t0 = c * CH, n = min(CH, T_len - t0);
+        const int rv = min(lt / 2, n - 1), cv = (lt % 2) * 8;
+        x.xv = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + rv) * v_row + cv);
+        x.bt = reinterpret_cast<const float*>(wb + W::bt)[min(lt, CH - 1)];
+#pragma unroll
+        for (int p = 0; p < NE; ++p) x.el[p] = reinterpret_cast<const float*>(wb + W::el)[min(lt + p * 192, DK - 1)];
+    };
+    auto store = [&](int c, const Stage& x) {
+        unsigned char* sb = smem + (size_t)(c & 1) * L::slot;
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
             const int e = lt + p * 192;
             if (e < 3 * CH * RK) {
                 const int mtx = e / (CH * RK), rr = (e / RK) % CH, c8 = (e % RK) * 8;
                 op_t* dst = reinterpret_cast<op_t*>(sb + (mtx == 0 ? L::kh : mtx == 1 ? L::kt : L::qh)) + rr * KP;
-                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{xk[p][0], xk[p][1], xk[p][2], xk[p][3]};
-                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{xk[p][4], xk[p][5], xk[p][6], xk[p][7]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{x.xk[p][0], x.xk[p][1], x.xk[p][2], x.xk[p][3]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{x.xk[p][4], x.xk[p][5], x.xk[p][6], x.xk[p][7]};
             }
         }
 #pragma unroll
@@ -2257,39 +2271,39 @@ __global__ __launch_bounds__(256) void kda_state_kernel(const bf16* __restrict__
             if (e < 2 * CH * 8) {
                 const int mtx = e / (CH * 8), rr = (e / 8) % CH, c8 = (e % 8) * 8;
                 op_t* dst = reinterpret_cast<op_t*>(sb + (mtx == 0 ? L::tm : L::aq)) + rr * CP;
-                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{xm[p][0], xm[p][1], xm[p][2], xm[p][3]};
-                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{xm[p][4], xm[p][5], xm[p][6], xm[p][7]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8)) = opx4{x.xm[p][0], x.xm[p][1], x.xm[p][2], x.xm[p][3]};
+                *reinterpret_cast<opx4*>(dst + pcol(c8 + 4)) = opx4{x.xm[p][4], x.xm[p][5], x.xm[p][6], x.xm[p][7]};
             }
         }
-        // V: 64 rows x 2 runs of 8 bf16 (rows past T zero)
+        // V rows past T are zero
         const int t0 = c * CH, n = min(CH, T_len - t0);
         if (lt < 2 * CH) {
             const int rr = lt / 2, c8 = (lt % 2) * 8;
-            bf16x8 x = {};
-            if (rr < n) x = *reinterpret_cast<const bf16x8*>(vb + (size_t)(t0 + rr) * v_row + c8);
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sb + L::v) + rr * L::VP + c8) = x;
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sb + L::v) + rr * L::VP + c8) = rr < n ? x.xv : bf16x8{};
         }
         // row vectors: beta (V_B, V_BEG: e^gc is inside Kh), ones (V_ED, V_EG), e^gL per channel
         float* vs = reinterpret_cast<float*>(sb + L::vec);
-        const float* bw = reinterpret_cast<const float*>(wb + W::bt);
         if (lt < CH) {
-            const float bt = bw[lt];
-            vs[V_B * CH + lt] = bt;
-            vs[V_BEG * CH + lt] = bt;
+            vs[V_B * CH + lt] = x.bt;
+            vs[V_BEG * CH + lt] = x.bt;
             vs[V_ED * CH + lt] = 1.f;
             vs[V_EC * CH + lt] = 1.f;
             vs[V_EG * CH + lt] = 1.f;
         }
         float* ech = reinterpret_cast<float*>(sb + L::ech);
-        const float* ew = reinterpret_cast<const float*>(wb + W::el);
-        for (int m = lt; m < DK; m += 192) ech[m] = ew[m];
+#pragma unroll
+        for (int p = 0; p < NE; ++p)
+            if (lt + p * 192 < DK) ech[lt + p * 192] = x.el[p];
     };
 
     floatx4 hacc[1][DK / 16];
+    Stage pre;
     if (w == 0) {
         load_state<DK, DV, 1>(hacc, s0, head, c0, lane);
     } else {
-        stage(0);
+        load(0, pre);
+        store(0, pre);
+        load(min(1, NT - 1), pre);
     }
     __syncthreads();
     for (int n = 0; n < NT; ++n) {
@@ -2312,8 +2326,9 @@ __global__ __launch_bounds__(256) void kda_state_kernel(const bf16* __restrict__
             chain_out<DK, 1>(hb, db, Qh, Aq, vs + V_EG * CH, o + ((size_t)b * T_len * Hv + j) * DV + c0 + (size_t)t0 * v_row,
                              v_row, min(CH, T_len - t0), lane);
             chain_update<DK, 1>(hacc, Kt, dtb, lane);
-        } else if (n + 1 < NT) {
-            stage(n + 1);
+        } else {
+            if (n + 1 < NT) store(n + 1, pre);
+            load(min(n + 2, NT - 1), pre);
         }
         __syncthreads();
     }
