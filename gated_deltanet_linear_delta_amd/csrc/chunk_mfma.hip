@@ -2017,7 +2017,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
                                                          int grp, int NT, float scale)
 {
     using W = KdaWs<DK>;
-    constexpr int KP = DK + 1, AP = CH + 1;
+    constexpr int KP = DK + 1, AP = CH + 4;   // A, Aq rows 16-byte aligned
     extern __shared__ float lds[];
     float* Ks = lds;
     float* Qs = Ks + CH * KP;
@@ -2144,13 +2144,23 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
     if (tid < CH) {
         const int s = tid;
         op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
-        float t[CH];
+        float t[CH + 4];
+#pragma unroll
+        for (int u = 0; u < CH + 4; ++u) t[u] = 0.f;
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
-            float acc = 0.f;
+            // A's row r four entries at a time (entries at and past the diagonal are zero, and so
+            // are the t not computed yet)
+            // four partial sums, so the dependent chain is a quarter as long
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < r; ++u) acc = fmaf(As[r * AP + u], t[u], acc);
-            t[r] = r == s ? 1.f : (r > s ? -acc : 0.f);
+            for (int u = 0; u < r; u += 4) {
+                const floatx4 a4 = *reinterpret_cast<const floatx4*>(As + r * AP + u);
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[y] = fmaf(a4[y], t[u + y], acc[y]);
+            }
+            const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            t[r] = r == s ? 1.f : (r > s ? -sum : 0.f);
             tw[r * CH + s] = (op_t)t[r];
         }
     }
@@ -2175,7 +2185,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
 template <int DK>
 constexpr size_t kda_prep_lds_bytes()
 {
-    return ((size_t)3 * CH * (DK + 1) + (size_t)2 * CH * (CH + 1) + CH) * sizeof(float);
+    return ((size_t)3 * CH * (DK + 1) + (size_t)2 * CH * (CH + 4) + CH) * sizeof(float);
 }
 
 // LDS of the state kernel: two slots, each Kh, Kt, Qh [64][DK+8] f16 (column-permuted), T, Aq
