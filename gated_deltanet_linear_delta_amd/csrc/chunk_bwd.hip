@@ -132,34 +132,44 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             }
         }
         __syncthreads();
-        // A (strictly lower) and M (lower including the diagonal)
-        for (int e = tid; e < BW_C * BW_C; e += DH_NT) {
-            const int r = e / BW_C, s = e % BW_C;
-            float a = 0.f, mm = 0.f;
-            if (s <= r) {
-                float kk = 0.f, qk = 0.f;
-#pragma unroll 8
-                for (int m = 0; m < DK; ++m) {
-                    kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
-                    qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
-                }
-                const float gam = expf(gcs[r] - gcs[s]);
-                mm = gam * qk;
-                if (s < r) a = bs[r] * gam * kk;
+        // The dense products on the float32 matrix cores (mfma_f32_tile), one 16 x 16 output tile
+        // per wave at a time.
+        constexpr int CT = BW_C / 16, BT = BW_BV / 16;
+        const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
+        // A (strictly lower) and M (lower including the diagonal): tiles (R, S), S <= R
+        for (int tt = w; tt < CT * (CT + 1) / 2; tt += DH_NT / 64) {
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= tt) ++R;
+            const int S = tt - R * (R + 1) / 2;
+            auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
+            const floatx4 ga = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk);
+            const floatx4 gq = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
+                As[r * BW_CP + sc] = sc < r ? bs[r] * gam * ga[x] : 0.f;
+                Ms[r * BW_CP + sc] = gam * gq[x];
             }
-            As[r * BW_CP + s] = a;
-            Ms[r * BW_CP + s] = mm;
         }
         __syncthreads();
-        // dDelta = diag(ed) K dh' + M^T dO
-        for (int e = tid; e < BW_C * BW_BV; e += DH_NT) {
-            const int r = e / BW_BV, c = e % BW_BV;
-            float x = 0.f, y = 0.f;
-#pragma unroll 8
-            for (int m = 0; m < DK; ++m) x = fmaf(Ks[r * KP + m], dhs[m * BW_BV + c], x);
-#pragma unroll 4
-            for (int s = r; s < BW_C; ++s) y = fmaf(Ms[s * BW_CP + r], dOs[s * BW_VP + c], y);
-            Ys[r * BW_VP + c] = fmaf(eds[r], x, y);
+        // dDelta = diag(ed) K dh' + M^T dO: tiles (R, T) of the chunk's rows and the columns; M^T's
+        // column r is nonzero from row r on, so its sum starts at the tile's first row
+        if (w < CT * BT) {
+            const int tr = w / BT, tc = w % BT;
+            const floatx4 xk = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int kk) { return Ks[(16 * tr + ii) * KP + kk]; },
+                                             [&](int kk, int jj) { return dhs[kk * BW_BV + 16 * tc + jj]; });
+            const floatx4 xm = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 16 * tr, BW_C,
+                                             [&](int ii, int kk) { return Ms[kk * BW_CP + 16 * tr + ii]; },
+                                             [&](int kk, int jj) { return dOs[kk * BW_VP + 16 * tc + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * tr + 4 * lq + x;
+                Ys[r * BW_VP + 16 * tc + li] = fmaf(eds[r], xk[x], xm[x]);
+            }
         }
         __syncthreads();
         // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution, one thread per column
@@ -172,17 +182,21 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             }
         }
         __syncthreads();
-        // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y
+        // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y:
+        // tiles (M, T) of the state
         const float eL = egs[BW_C - 1];
-        for (int e = tid; e < DK * BW_BV; e += DH_NT) {
-            const int m = e / BW_BV, c = e % BW_BV;
-            float acc = eL * dhs[e];
-#pragma unroll 4
-            for (int r = 0; r < BW_C; ++r) {
-                const float w = egs[r] * (Qs[r * KP + m] * dOs[r * BW_VP + c] - bs[r] * Ks[r * KP + m] * Ys[r * BW_VP + c]);
-                acc += w;
-            }
-            dhs[e] = acc;
+        for (int tt = w; tt < (DK / 16) * BT; tt += DH_NT / 64) {
+            const int M = tt / BT, T2 = tt % BT;
+            floatx4 acc;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = eL * dhs[(16 * M + 4 * lq + x) * BW_BV + 16 * T2 + li];
+            acc = mfma_f32_tile(acc, 0, BW_C, [&](int ii, int kk) { return egs[kk] * Qs[kk * KP + 16 * M + ii]; },
+                                [&](int kk, int jj) { return dOs[kk * BW_VP + 16 * T2 + jj]; });
+            acc = mfma_f32_tile(acc, 0, BW_C,
+                                [&](int ii, int kk) { return -bs[kk] * egs[kk] * Ks[kk * KP + 16 * M + ii]; },
+                                [&](int kk, int jj) { return Ys[kk * BW_VP + 16 * T2 + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dhs[(16 * M + 4 * lq + x) * BW_BV + 16 * T2 + li] = acc[x];
         }
     }
     __syncthreads();

@@ -1913,7 +1913,7 @@ size_t chunk_scan_workspace_bytes(const ChunkArgs& a, int segments) { return sca
 // 0.52 ms against 0.97 ms unsegmented, 2 segments 1.18 ms.
 int chunk_auto_segments(const ChunkArgs& a)
 {
-    if (!chunk_mfma_split(a) || a.cu || a.z || a.hst) return 1;
+    if (!chunk_mfma_split(a) || a.cu || a.z) return 1;
     const int env = env_int("GDN_SCAN_SEGMENTS", -1);
     if (env >= 1) return env;
     if (env == 0) return 1;

@@ -28,15 +28,15 @@ namespace {
 constexpr int SIMT_NT = 512;
 
 // One 512-thread workgroup per (batch, value head, column tile): grid (B * Hv, DV / BV).
-template <typename T, int DK, int DV, int BV, bool OUT>
+template <typename T, int DK, int DV, int BV>
 __global__ __launch_bounds__(SIMT_NT) void chunk_simt_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* s0, float* sf, T* __restrict__ o,
-    float* __restrict__ hst, int T_max, int Hqk, int Hv, int grp, int C, float scale, const int* cu, int total)
+    int T_max, int Hqk, int Hv, int grp, int C, float scale, const int* cu, int total)
 {
     extern __shared__ float lds[];
-    simt_chunk_body<T, DK, DV, BV, OUT, SIMT_NT>(lds, blockIdx.x, blockIdx.y, q, k, v, g, beta, s0, sf, o, hst, T_max,
-                                                  Hqk, Hv, grp, C, scale, cu, total);
+    simt_chunk_body<T, DK, DV, BV, true, SIMT_NT>(lds, blockIdx.x, blockIdx.y, q, k, v, g, beta, s0, sf, o, nullptr,
+                                                   T_max, Hqk, Hv, grp, C, scale, cu, total);
 }
 
 }  // namespace
@@ -46,13 +46,13 @@ static hipError_t launch_simt_t(const ChunkArgs& a, hipStream_t st)
 {
     constexpr int BV = DV < 32 ? DV : 32;
     using L = SimtLds<DK, BV>;
-    auto kern = a.o ? chunk_simt_kernel<T, DK, DV, BV, true> : chunk_simt_kernel<T, DK, DV, BV, false>;
+    auto kern = chunk_simt_kernel<T, DK, DV, BV>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)L::bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.B * a.Hv, DV / BV), dim3(SIMT_NT), L::bytes, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, a.s0, a.sf,
-                       (T*)a.o, a.hst, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale, a.cu, a.total);
+                       (T*)a.o, a.T, a.Hqk, a.Hv, a.Hv / a.Hqk, a.chunk, a.scale, a.cu, a.total);
     return hipGetLastError();
 }
 

@@ -38,9 +38,6 @@ struct ChunkArgs {
     int norm_w_stride = 0;
     float eps = 0.f;
     void* y = nullptr;
-    // float32-vector path only: when set, the state entering every chunk is stored here
-    // ([B, Hv, NT, dk, dv], NT = ceil(T / chunk)); o may then be null
-    float* hst = nullptr;
     // packed sequences: when cu is set, B is the number of sequences, cu[0..B] (device) their
     // token offsets into `total` tokens (tensors [total, H, d]), and T the longest length
     const int* cu = nullptr;

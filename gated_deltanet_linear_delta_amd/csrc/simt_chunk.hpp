@@ -28,6 +28,19 @@ struct SimtLds {
     static constexpr size_t bytes = floats * sizeof(float);
 };
 
+// D += A B for one 16 x 16 tile on the float32 matrix cores (v_mfma_f32_16x16x4_f32): lane l
+// supplies A[l % 16][k + l / 16] = a(l % 16, k + l / 16) and B[k + l / 16][l % 16] =
+// b(k + l / 16, l % 16) for k = k0, k0 + 4, ... < k1 (k1 - k0 a multiple of 4) and holds
+// D[4 (l / 16) + x][l % 16] in element x.
+template <typename FA, typename FB>
+__device__ __forceinline__ floatx4 mfma_f32_tile(floatx4 acc, int k0, int k1, FA&& a, FB&& b)
+{
+    const int l = threadIdx.x & 63, i = l & 15, kq = l >> 4;
+#pragma unroll 8
+    for (int k = k0; k < k1; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(i, k + kq), b(k + kq, i), acc, 0, 0, 0);
+    return acc;
+}
+
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 template <typename T, int DK, int DV, int BV, bool OUT, int NTH>
 __device__ __forceinline__ void simt_chunk_body(
@@ -119,42 +132,47 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        // A (strictly lower, beta-scaled) and the output mask matrix (lower incl. diagonal).
-        for (int e = tid; e < C * C; e += NTH) {
-            const int r = e / C, c = e % C;
-            float a = 0.f, aq = 0.f;
-            if (c <= r) {
-                float kk = 0.f, qk = 0.f;
-                for (int m = 0; m < DK; ++m) {
-                    const float kc = Ks[c * L::KP + m];
-                    kk = fmaf(Ks[r * L::KP + m], kc, kk);
-                    if (OUT) qk = fmaf(Qs[r * L::KP + m], kc, qk);
-                }
-                const float gam = expf(gcs[r] - gcs[c]);
-                aq = gam * qk;
-                if (c < r) a = bs[r] * gam * kk;
-            }
-            As[r * L::CP + c] = a;
-            Aq[r * L::CP + c] = aq;
-        }
-        __syncthreads();
-        // R = beta V - beta exp(gc) (K h0); keep exp(gc) (Q h0) for the output.
-        constexpr int PER = (SIMT_CMAX * BV + NTH - 1) / NTH;
-        float qh[PER];
+        // The dense products run on the float32 matrix cores (mfma_f32_tile: float32 products,
+        // so float32 inputs keep float32 accuracy), one 16 x 16 output tile per wave at a time.
+        const int nw = NTH / 64, w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
+        const int CT = C / 16;          // row tiles of the chunk
+        constexpr int BT = BV / 16;     // column tiles of the value tile
+        // A (strictly lower, beta-scaled) and the output mask matrix (lower incl. diagonal):
+        // tiles (R, S) with S <= R of K K^T and Q K^T, then the decays exp(gc_r - gc_s)
+        for (int tt = w; tt < CT * (CT + 1) / 2; tt += nw) {
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= tt) ++R;
+            const int S = tt - R * (R + 1) / 2;
+            const float* Kr = Ks + 16 * R * L::KP;
+            const float* Qr = Qs + 16 * R * L::KP;
+            const float* Kc = Ks + 16 * S * L::KP;
+            auto bk = [&](int k, int jj) { return Kc[jj * L::KP + k]; };
+            const floatx4 ga = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int k) { return Kr[ii * L::KP + k]; }, bk);
+            floatx4 gq = {0.f, 0.f, 0.f, 0.f};
+            if (OUT) gq = mfma_f32_tile(gq, 0, DK, [&](int ii, int k) { return Qr[ii * L::KP + k]; }, bk);
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int e = tid + p * NTH;
-            qh[p] = 0.f;
-            if (e < C * BV) {
-                const int r = e / BV, c = e % BV;
-                float x = 0.f, y = 0.f;
-                for (int m = 0; m < DK; ++m) {
-                    const float hm = hs[m * BV + c];
-                    x = fmaf(Ks[r * L::KP + m], hm, x);
-                    if (OUT) y = fmaf(Qs[r * L::KP + m], hm, y);
-                }
-                Rs[e] = bs[r] * (Vs[e] - egs[r] * x);
-                qh[p] = egs[r] * y;
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * R + 4 * lq + x, c = 16 * S + li;
+                const float gam = c <= r ? expf(gcs[r] - gcs[c]) : 0.f;
+                As[r * L::CP + c] = c < r ? bs[r] * gam * ga[x] : 0.f;
+                if (OUT) Aq[r * L::CP + c] = gam * gq[x];
+            }
+        }
+        // R = beta V - beta exp(gc) (K h0); keep exp(gc) (Q h0) for the output: tiles (R, T) of
+        // the chunk's rows and the value columns (at most one per wave)
+        floatx4 qh = {0.f, 0.f, 0.f, 0.f};
+        const int tr = w / BT, tc = w % BT;   // this wave's (R, T) tile, when w < CT * BT
+        if (w < CT * BT) {
+            auto bh = [&](int k, int jj) { return hs[k * BV + 16 * tc + jj]; };
+            const floatx4 xk = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int k) { return Ks[(16 * tr + ii) * L::KP + k]; }, bh);
+            if (OUT) qh = mfma_f32_tile(qh, 0, DK, [&](int ii, int k) { return Qs[(16 * tr + ii) * L::KP + k]; }, bh);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
+                Rs[r * BV + c] = bs[r] * (Vs[r * BV + c] - egs[r] * xk[x]);
+                qh[x] *= egs[r];
             }
         }
         __syncthreads();
@@ -168,33 +186,28 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        // O = exp(gc) Q h0 + Aq Delta
-        if (OUT) {
+        // O = exp(gc) Q h0 + Aq Delta (Aq is zero right of the diagonal: k up to the tile's end)
+        if (OUT && w < CT * BT) {
+            const floatx4 ot = mfma_f32_tile(qh, 0, 16 * (tr + 1),
+                                             [&](int ii, int k) { return Aq[(16 * tr + ii) * L::CP + k]; },
+                                             [&](int k, int jj) { return Rs[k * BV + 16 * tc + jj]; });
 #pragma unroll
-            for (int p = 0; p < PER; ++p) {
-                const int e = tid + p * NTH;
-                if (e < C * BV) {
-                    const int r = e / BV, c = e % BV;
-                    float acc = qh[p];
-                    for (int x = 0; x <= r; ++x) acc = fmaf(Aq[r * L::CP + x], Rs[x * BV + c], acc);
-                    if (r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(acc);
-                }
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
+                if (r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(ot[x]);
             }
         }
-        // K~ = exp(gc_C - gc_r) k_r in place (K is not read again in this chunk)
-        for (int e = tid; e < C * DK; e += NTH) {
-            const int r = e / DK, m = e % DK;
-            Ks[r * L::KP + m] *= eds[r];
-        }
-        __syncthreads();
-        // h1 = exp(gc_C) h0 + sum_r K~_r Delta_r^T
+        // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T: tiles (M, T) of the state
         const float ec = egs[C - 1];
-        for (int e = tid; e < DK * BV; e += NTH) {
-            const int m = e / BV, c = e % BV;
-            float acc = ec * hs[e];
-#pragma unroll 8
-            for (int r = 0; r < C; ++r) acc = fmaf(Ks[r * L::KP + m], Rs[r * BV + c], acc);
-            hs[e] = acc;
+        for (int tt = w; tt < (DK / 16) * BT; tt += nw) {
+            const int M = tt / BT, T2 = tt % BT;
+            floatx4 acc;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc[x] = ec * hs[(16 * M + 4 * lq + x) * BV + 16 * T2 + li];
+            acc = mfma_f32_tile(acc, 0, C, [&](int ii, int k) { return eds[k] * Ks[k * L::KP + 16 * M + ii]; },
+                                [&](int k, int jj) { return Rs[k * BV + 16 * T2 + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) hs[(16 * M + 4 * lq + x) * BV + 16 * T2 + li] = acc[x];
         }
     }
     __syncthreads();
