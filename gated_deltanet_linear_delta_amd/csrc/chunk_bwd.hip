@@ -275,11 +275,12 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 {
     using L = BwLds<DK>;
     constexpr int KP = L::KP, HP = L::HP;
-    // accumulators of the [C, DK] gradients: thread tid owns column am = tid % DK of rows
-    // ar0, ar0 + RS, ... (RS = BW_NT / DK rows per pass, PE passes)
-    constexpr int RS = BW_NT / DK;
-    constexpr int PE = BW_C / RS;
-    static_assert(BW_NT % DK == 0 && BW_C % RS == 0, "accumulator layout");
+    // accumulators of the [C, DK] gradients in the layout of a 16 x 16 float32 matrix-core tile
+    // (mfma_f32_tile): wave w < NTL owns tile (w / MTL, w % MTL) of the [C, DK] matrix, and
+    // element p of lane l is row aR + p, column aM (aR = 16 (w / MTL) + 4 (l / 16),
+    // aM = 16 (w % MTL) + l % 16)
+    constexpr int MTL = DK / 16, NTL = (BW_C / 16) * MTL, PE = 4;
+    static_assert(NTL <= BW_NT / 64, "one accumulator tile per wave");
     extern __shared__ float lds[];
     float* Ks = lds + L::k;
     float* Qs = lds + L::q;
@@ -311,7 +312,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     const int i = bi % Hqk, b = bi / Hqk;
     const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
     const int tid = threadIdx.x;
-    const int am = tid % DK, ar0 = tid / DK;
+    const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
+    const bool accw = w < NTL;
+    const int aR = 16 * (w / MTL) + 4 * lq, aM = 16 * (w % MTL) + li;
 
     for (int e = tid; e < BW_C * DK; e += BW_NT) {
         const int r = e / DK, m = e % DK;
@@ -419,21 +422,29 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 dOs[r * BW_VP + c] = r < n ? to_f32(dout[off]) : 0.f;
             }
             __syncthreads();
-            // Delta = T (beta V) - W h;  dDelta = diag(ed) K dh' + M^T dO
-            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
-                const int r = e / BW_BV, c = e % BW_BV;
-                float u = 0.f, wh = 0.f, kd = 0.f, md = 0.f;
-#pragma unroll 4
-                for (int s = 0; s <= r; ++s) u = fmaf(Tm[r * BW_CP + s] * bs[s], Vs[s * BW_VP + c], u);
-#pragma unroll 8
-                for (int m = 0; m < DK; ++m) {
-                    wh = fmaf(Ws[r * KP + m], hs[m * HP + c], wh);
-                    kd = fmaf(Ks[r * KP + m], dhs[m * HP + c], kd);
+            // Delta = T (beta V) - W h;  dDelta = diag(ed) K dh' + M^T dO: the (C / 16) x (BV / 16)
+            // tiles on the float32 matrix cores, one per wave (T is lower triangular and M^T upper,
+            // so their sums stop at, or start at, the tile's own rows)
+            constexpr int VT = BW_BV / 16;
+            const int tr = w / VT, tc = w % VT;
+            if (w < (BW_C / 16) * VT) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                const floatx4 u = mfma_f32_tile(z, 0, 16 * (tr + 1),
+                                                [&](int ii, int kk) { return Tm[(16 * tr + ii) * BW_CP + kk] * bs[kk]; },
+                                                [&](int kk, int jj) { return Vs[kk * BW_VP + 16 * tc + jj]; });
+                const floatx4 wh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ws[(16 * tr + ii) * KP + kk]; },
+                                                 [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
+                const floatx4 kd = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * tr + ii) * KP + kk]; },
+                                                 [&](int kk, int jj) { return dhs[kk * HP + 16 * tc + jj]; });
+                const floatx4 md = mfma_f32_tile(z, 16 * tr, BW_C,
+                                                 [&](int ii, int kk) { return Ms[kk * BW_CP + 16 * tr + ii]; },
+                                                 [&](int kk, int jj) { return dOs[kk * BW_VP + 16 * tc + jj]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
+                    Ds[r * BW_VP + c] = u[x] - wh[x];
+                    dDs[r * BW_VP + c] = fmaf(eds[r], kd[x], md[x]);
                 }
-#pragma unroll 4
-                for (int s = r; s < BW_C; ++s) md = fmaf(Ms[s * BW_CP + r], dOs[s * BW_VP + c], md);
-                Ds[r * BW_VP + c] = u - wh;
-                dDs[r * BW_VP + c] = fmaf(eds[r], kd, md);
             }
             for (int e = tid; e < DK * BW_BV; e += BW_NT) {
                 const int m = e / BW_BV, c = e % BW_BV;
@@ -441,16 +452,20 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
             __syncthreads();
             // dV = diag(beta) T^T dDelta (complete for this tile); row-sum terms of dbeta and dgc
-            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
-                const int r = e / BW_BV, c = e % BW_BV;
-                float tdu = 0.f, qh = 0.f;
-#pragma unroll 4
-                for (int s = r; s < BW_C; ++s) tdu = fmaf(Tm[s * BW_CP + r], dDs[s * BW_VP + c], tdu);
-#pragma unroll 8
-                for (int m = 0; m < DK; ++m) qh = fmaf(Qs[r * KP + m], hs[m * HP + c], qh);
-                if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu);
-                P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu;
-                P2[r * BW_VP + c] = dOs[r * BW_VP + c] * qh;
+            if (w < (BW_C / 16) * VT) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                const floatx4 tdu = mfma_f32_tile(z, 16 * tr, BW_C,
+                                                  [&](int ii, int kk) { return Tm[kk * BW_CP + 16 * tr + ii]; },
+                                                  [&](int kk, int jj) { return dDs[kk * BW_VP + 16 * tc + jj]; });
+                const floatx4 qh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Qs[(16 * tr + ii) * KP + kk]; },
+                                                 [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
+                    if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu[x]);
+                    P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu[x];
+                    P2[r * BW_VP + c] = dOs[r * BW_VP + c] * qh[x];
+                }
             }
             // dT += dDelta (diag(beta) V)^T;  dM += dO Delta^T (lower incl)
             for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
@@ -464,20 +479,22 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 dTs[r * BW_CP + s] += bs[s] * x;
                 if (s <= r) dMs[r * BW_CP + s] += y;
             }
-            // dW -= dDelta h^T;  X += Delta dh'^T;  dQ += diag(e^gc) dO h^T
+            // dW -= dDelta h^T;  X += Delta dh'^T;  dQ += diag(e^gc) dO h^T: this wave's
+            // accumulator tile, summed over the tile's value columns on the matrix cores
+            if (accw) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                const int r0 = aR - 4 * lq, m0 = aM - li;
+                auto bh = [&](int kk, int jj) { return hs[(m0 + jj) * HP + kk]; };
+                const floatx4 sw = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dDs[(r0 + ii) * BW_VP + kk]; }, bh);
+                const floatx4 sx = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return Ds[(r0 + ii) * BW_VP + kk]; },
+                                                 [&](int kk, int jj) { return dhs[(m0 + jj) * HP + kk]; });
+                const floatx4 sq = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dOs[(r0 + ii) * BW_VP + kk]; }, bh);
 #pragma unroll
-            for (int p = 0; p < PE; ++p) {
-                const int r = ar0 + p * RS, m = am;
-                float sw = 0.f, sx = 0.f, sq = 0.f;
-#pragma unroll 2
-                for (int c = 0; c < BW_BV; ++c) {
-                    sw = fmaf(dDs[r * BW_VP + c], hs[m * HP + c], sw);
-                    sx = fmaf(Ds[r * BW_VP + c], dhs[m * HP + c], sx);
-                    sq = fmaf(dOs[r * BW_VP + c], hs[m * HP + c], sq);
+                for (int p = 0; p < PE; ++p) {
+                    aW[p] -= sw[p];
+                    aX[p] += sx[p];
+                    aQ[p] = fmaf(egs[aR + p], sq[p], aQ[p]);
                 }
-                aW[p] -= sw;
-                aX[p] += sx;
-                aQ[p] = fmaf(egs[r], sq, aQ[p]);
             }
             __syncthreads();
             if (tid < BW_C) {
@@ -499,8 +516,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         float* dWs = hs;    // [C][KP]
         float* Xs = dhs;    // [C][KP]
 #pragma unroll
-        for (int p = 0; p < PE; ++p) {
-            const int r = ar0 + p * RS, m = am;
+        for (int p = 0; p < PE; ++p) if (accw) {
+            const int r = aR + p, m = aM;
             dWs[r * KP + m] = aW[p];
             Xs[r * KP + m] = aX[p];
         }
@@ -513,8 +530,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         __syncthreads();
         // h' = e^gL h + (diag(ed) K)^T Delta:  dK += diag(ed) X, dgc -= ed (K . X), dgL += sum of those
 #pragma unroll
-        for (int p = 0; p < PE; ++p) {
-            const int r = ar0 + p * RS, m = am;
+        for (int p = 0; p < PE; ++p) if (accw) {
+            const int r = aR + p, m = aM;
             aK[p] = fmaf(eds[r], Xs[r * KP + m], aK[p]);
         }
         if (tid < BW_C) {
@@ -548,8 +565,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         __syncthreads();
         // dQ += E K;  dK += E^T (scale Q);  dKB = T^T dW -> dK += diag(beta e^gc) dKB
 #pragma unroll
-        for (int p = 0; p < PE; ++p) {
-            const int r = ar0 + p * RS, m = am;
+        for (int p = 0; p < PE; ++p) if (accw) {
+            const int r = aR + p, m = aM;
             float eq = 0.f, ek = 0.f, kb = 0.f;
 #pragma unroll 2
             for (int s = 0; s <= r; ++s) eq = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], eq);
@@ -618,8 +635,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         __syncthreads();
         // dK += Dk K + Dk^T K
 #pragma unroll
-        for (int p = 0; p < PE; ++p) {
-            const int r = ar0 + p * RS, m = am;
+        for (int p = 0; p < PE; ++p) if (accw) {
+            const int r = aR + p, m = aM;
             float x = 0.f;
 #pragma unroll 2
             for (int s = 0; s < r; ++s) x = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], x);
@@ -641,8 +658,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         }
     }
 #pragma unroll
-    for (int p = 0; p < PE; ++p) {
-        const int r = ar0 + p * RS, m = am;
+    for (int p = 0; p < PE; ++p) if (accw) {
+        const int r = aR + p, m = aM;
         if (r < n) {
             const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
             dq[off] = from_f32<T>(scale * aQ[p]);
