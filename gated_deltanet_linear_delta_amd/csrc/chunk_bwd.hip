@@ -363,22 +363,24 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
         }
         __syncthreads();
-        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
-            const int r = e / BW_C, s = e % BW_C;
-            float gg = 0.f, mm = 0.f;
-            if (s <= r) {
-                float kk = 0.f, qk = 0.f;
-#pragma unroll 8
-                for (int m = 0; m < DK; ++m) {
-                    kk = fmaf(Ks[r * KP + m], Ks[s * KP + m], kk);
-                    qk = fmaf(Qs[r * KP + m], Ks[s * KP + m], qk);
-                }
-                const float gam = expf(gcs[r] - gcs[s]);
-                mm = gam * qk;
-                if (s < r) gg = gam * kk;
+        // G = K K^T * Gamma (strictly lower) and M = Q K^T * Gamma (lower incl): tiles (R, S),
+        // S <= R, on the float32 matrix cores (entries above the diagonal are never read)
+        constexpr int CT = BW_C / 16;
+        for (int tt = w; tt < CT * (CT + 1) / 2; tt += BW_NT / 64) {
+            int R = 0;
+            while ((R + 1) * (R + 2) / 2 <= tt) ++R;
+            const int S = tt - R * (R + 1) / 2;
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
+            const floatx4 ga = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk);
+            const floatx4 gq = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
+                Gs[r * BW_CP + sc] = sc < r ? gam * ga[x] : 0.f;
+                Ms[r * BW_CP + sc] = gam * gq[x];
             }
-            Gs[r * BW_CP + s] = gg;
-            Ms[r * BW_CP + s] = mm;
         }
         __syncthreads();
         // T = (I + diag(beta) G)^{-1}: column s by forward substitution, one thread per column
@@ -392,13 +394,14 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
         }
         __syncthreads();
-        // W = T diag(beta e^gc) K
-        for (int e = tid; e < BW_C * DK; e += BW_NT) {
-            const int r = e / DK, m = e % DK;
-            float acc = 0.f;
-#pragma unroll 4
-            for (int u = 0; u <= r; ++u) acc = fmaf(Tm[r * BW_CP + u] * bs[u] * egs[u], Ks[u * KP + m], acc);
-            Ws[r * KP + m] = acc;
+        // W = T diag(beta e^gc) K: tiles (R, M) (T lower triangular: the sum stops at the tile's rows)
+        for (int tt = w; tt < CT * MTL; tt += BW_NT / 64) {
+            const int R = tt / MTL, M = tt % MTL;
+            const floatx4 acc = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16 * (R + 1),
+                                              [&](int ii, int kk) { return Tm[(16 * R + ii) * BW_CP + kk] * bs[kk] * egs[kk]; },
+                                              [&](int kk, int jj) { return Ks[kk * KP + 16 * M + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Ws[(16 * R + 4 * lq + x) * KP + 16 * M + li] = acc[x];
         }
         float aW[PE], aX[PE];
 #pragma unroll
@@ -563,29 +566,37 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dMs[r * BW_CP + s] = s <= r ? dMs[r * BW_CP + s] * expf(gcs[r] - gcs[s]) : 0.f;
         }
         __syncthreads();
-        // dQ += E K;  dK += E^T (scale Q);  dKB = T^T dW -> dK += diag(beta e^gc) dKB
+        // dQ += E K;  dK += E^T (scale Q);  dKB = T^T dW -> dK += diag(beta e^gc) dKB, on this
+        // wave's accumulator tile (E lower incl and T lower: the sums stop at, or start at, the
+        // tile's rows)
+        if (accw) {
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            const int R0 = aR - 4 * lq, M0 = aM - li;
+            const floatx4 eq = mfma_f32_tile(z, 0, R0 + 16, [&](int ii, int kk) { return dMs[(R0 + ii) * BW_CP + kk]; },
+                                             [&](int kk, int jj) { return Ks[kk * KP + M0 + jj]; });
+            const floatx4 ek = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return dMs[kk * BW_CP + R0 + ii]; },
+                                             [&](int kk, int jj) { return Qs[kk * KP + M0 + jj]; });
+            const floatx4 kb = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return Tm[kk * BW_CP + R0 + ii]; },
+                                             [&](int kk, int jj) { return dWs[kk * KP + M0 + jj]; });
 #pragma unroll
-        for (int p = 0; p < PE; ++p) if (accw) {
-            const int r = aR + p, m = aM;
-            float eq = 0.f, ek = 0.f, kb = 0.f;
-#pragma unroll 2
-            for (int s = 0; s <= r; ++s) eq = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], eq);
-#pragma unroll 2
-            for (int u = r; u < BW_C; ++u) {
-                ek = fmaf(dMs[u * BW_CP + r], Qs[u * KP + m], ek);
-                kb = fmaf(Tm[u * BW_CP + r], dWs[u * KP + m], kb);
+            for (int p = 0; p < PE; ++p) {
+                const int r = aR + p, m = aM;
+                aQ[p] += eq[p];
+                aK[p] += ek[p] + bs[r] * egs[r] * kb[p];
+                Xs[r * KP + m] = Ks[r * KP + m] * kb[p];   // for the row sums of K . dKB
             }
-            aQ[p] += eq;
-            aK[p] += ek + bs[r] * egs[r] * kb;
-            Xs[r * KP + m] = Ks[r * KP + m] * kb;   // for the row sums of K . dKB
         }
-        // dT += dW (diag(beta e^gc) K)^T
-        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
-            const int r = e / BW_C, s = e % BW_C;
-            float x = 0.f;
-#pragma unroll 4
-            for (int m = 0; m < DK; ++m) x = fmaf(dWs[r * KP + m], Ks[s * KP + m], x);
-            dTs[r * BW_CP + s] += bs[s] * egs[s] * x;
+        // dT += dW (diag(beta e^gc) K)^T: tiles (R, S) of the full [C, C]
+        for (int tt = w; tt < CT * CT; tt += BW_NT / 64) {
+            const int R = tt / CT, S = tt % CT;
+            const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+                                             [&](int ii, int kk) { return dWs[(16 * R + ii) * KP + kk]; },
+                                             [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                dTs[r * BW_CP + sc] += bs[sc] * egs[sc] * x4[x];
+            }
         }
         __syncthreads();
         if (tid < BW_C) {
@@ -633,16 +644,15 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dMs[r * BW_CP + s] = s < r ? dTs[r * BW_CP + s] * bs[r] * expf(gcs[r] - gcs[s]) : 0.f;
         }
         __syncthreads();
-        // dK += Dk K + Dk^T K
+        // dK += Dk K + Dk^T K on this wave's accumulator tile (Dk strictly lower)
+        if (accw) {
+            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            const int R0 = aR - 4 * lq, M0 = aM - li;
+            auto bk = [&](int kk, int jj) { return Ks[kk * KP + M0 + jj]; };
+            const floatx4 x1 = mfma_f32_tile(z, 0, R0 + 16, [&](int ii, int kk) { return dMs[(R0 + ii) * BW_CP + kk]; }, bk);
+            const floatx4 x2 = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return dMs[kk * BW_CP + R0 + ii]; }, bk);
 #pragma unroll
-        for (int p = 0; p < PE; ++p) if (accw) {
-            const int r = aR + p, m = aM;
-            float x = 0.f;
-#pragma unroll 2
-            for (int s = 0; s < r; ++s) x = fmaf(dMs[r * BW_CP + s], Ks[s * KP + m], x);
-#pragma unroll 2
-            for (int u = r + 1; u < BW_C; ++u) x = fmaf(dMs[u * BW_CP + r], Ks[u * KP + m], x);
-            aK[p] += x;
+            for (int p = 0; p < PE; ++p) aK[p] += x1[p] + x2[p];
         }
         // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL)
         if (tid == 0) {
