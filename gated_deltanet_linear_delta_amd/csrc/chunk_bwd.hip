@@ -33,7 +33,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int BW_NT = 1024;   // threads per workgroup of the per-chunk kernel
+constexpr int BW_NT = 512;    // threads per workgroup of the per-chunk kernel
 constexpr int DH_NT = 1024;  // threads per workgroup of the reverse state pass
 constexpr int BW_C = 32;     // chunk length of the backward pass
 constexpr int BW_BV = 32;    // value columns per tile
@@ -275,12 +275,12 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 {
     using L = BwLds<DK>;
     constexpr int KP = L::KP, HP = L::HP;
-    // accumulators of the [C, DK] gradients in the layout of a 16 x 16 float32 matrix-core tile
-    // (mfma_f32_tile): wave w < NTL owns tile (w / MTL, w % MTL) of the [C, DK] matrix, and
-    // element p of lane l is row aR + p, column aM (aR = 16 (w / MTL) + 4 (l / 16),
-    // aM = 16 (w % MTL) + l % 16)
-    constexpr int MTL = DK / 16, NTL = (BW_C / 16) * MTL, PE = 4;
-    static_assert(NTL <= BW_NT / 64, "one accumulator tile per wave");
+    // accumulators of the [C, DK] gradients in the layout of 16 x 16 float32 matrix-core tiles
+    // (mfma_f32_tile): tile u of the [C, DK] matrix is rows 16 (u / MTL) .., columns 16 (u % MTL) ..;
+    // wave w owns tiles w, w + NWV, ... (TPW per wave), and element 4 t + x of lane l for the
+    // wave's t-th tile (R0, M0) is row R0 + 4 (l / 16) + x, column M0 + l % 16
+    constexpr int MTL = DK / 16, NTL = (BW_C / 16) * MTL, NWV = BW_NT / 64;
+    constexpr int TPW = (NTL + NWV - 1) / NWV, PE = 4 * TPW;
     extern __shared__ float lds[];
     float* Ks = lds + L::k;
     float* Qs = lds + L::q;
@@ -313,8 +313,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
-    const bool accw = w < NTL;
-    const int aR = 16 * (w / MTL) + 4 * lq, aM = 16 * (w % MTL) + li;
+    auto tile_ok = [&](int t) { return w + t * NWV < NTL; };
+    auto tile_r0 = [&](int t) { return 16 * ((w + t * NWV) / MTL); };
+    auto tile_m0 = [&](int t) { return 16 * ((w + t * NWV) % MTL); };
 
     for (int e = tid; e < BW_C * DK; e += BW_NT) {
         const int r = e / DK, m = e % DK;
@@ -484,19 +485,21 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
             // dW -= dDelta h^T;  X += Delta dh'^T;  dQ += diag(e^gc) dO h^T: this wave's
             // accumulator tile, summed over the tile's value columns on the matrix cores
-            if (accw) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) if (tile_ok(t)) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                const int r0 = aR - 4 * lq, m0 = aM - li;
+                const int r0 = tile_r0(t), m0 = tile_m0(t);
                 auto bh = [&](int kk, int jj) { return hs[(m0 + jj) * HP + kk]; };
                 const floatx4 sw = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dDs[(r0 + ii) * BW_VP + kk]; }, bh);
                 const floatx4 sx = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return Ds[(r0 + ii) * BW_VP + kk]; },
                                                  [&](int kk, int jj) { return dhs[(m0 + jj) * HP + kk]; });
                 const floatx4 sq = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dOs[(r0 + ii) * BW_VP + kk]; }, bh);
 #pragma unroll
-                for (int p = 0; p < PE; ++p) {
-                    aW[p] -= sw[p];
-                    aX[p] += sx[p];
-                    aQ[p] = fmaf(egs[aR + p], sq[p], aQ[p]);
+                for (int x = 0; x < 4; ++x) {
+                    const int p = 4 * t + x;
+                    aW[p] -= sw[x];
+                    aX[p] += sx[x];
+                    aQ[p] = fmaf(egs[r0 + 4 * lq + x], sq[x], aQ[p]);
                 }
             }
             __syncthreads();
@@ -519,8 +522,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         float* dWs = hs;    // [C][KP]
         float* Xs = dhs;    // [C][KP]
 #pragma unroll
-        for (int p = 0; p < PE; ++p) if (accw) {
-            const int r = aR + p, m = aM;
+        for (int p = 0; p < PE; ++p) if (tile_ok(p / 4)) {
+            const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
             dWs[r * KP + m] = aW[p];
             Xs[r * KP + m] = aX[p];
         }
@@ -533,8 +536,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         __syncthreads();
         // h' = e^gL h + (diag(ed) K)^T Delta:  dK += diag(ed) X, dgc -= ed (K . X), dgL += sum of those
 #pragma unroll
-        for (int p = 0; p < PE; ++p) if (accw) {
-            const int r = aR + p, m = aM;
+        for (int p = 0; p < PE; ++p) if (tile_ok(p / 4)) {
+            const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
             aK[p] = fmaf(eds[r], Xs[r * KP + m], aK[p]);
         }
         if (tid < BW_C) {
@@ -569,9 +572,10 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         // dQ += E K;  dK += E^T (scale Q);  dKB = T^T dW -> dK += diag(beta e^gc) dKB, on this
         // wave's accumulator tile (E lower incl and T lower: the sums stop at, or start at, the
         // tile's rows)
-        if (accw) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) if (tile_ok(t)) {
             const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-            const int R0 = aR - 4 * lq, M0 = aM - li;
+            const int R0 = tile_r0(t), M0 = tile_m0(t);
             const floatx4 eq = mfma_f32_tile(z, 0, R0 + 16, [&](int ii, int kk) { return dMs[(R0 + ii) * BW_CP + kk]; },
                                              [&](int kk, int jj) { return Ks[kk * KP + M0 + jj]; });
             const floatx4 ek = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return dMs[kk * BW_CP + R0 + ii]; },
@@ -579,11 +583,11 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             const floatx4 kb = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return Tm[kk * BW_CP + R0 + ii]; },
                                              [&](int kk, int jj) { return dWs[kk * KP + M0 + jj]; });
 #pragma unroll
-            for (int p = 0; p < PE; ++p) {
-                const int r = aR + p, m = aM;
-                aQ[p] += eq[p];
-                aK[p] += ek[p] + bs[r] * egs[r] * kb[p];
-                Xs[r * KP + m] = Ks[r * KP + m] * kb[p];   // for the row sums of K . dKB
+            for (int x = 0; x < 4; ++x) {
+                const int p = 4 * t + x, r = R0 + 4 * lq + x, m = M0 + li;
+                aQ[p] += eq[x];
+                aK[p] += ek[x] + bs[r] * egs[r] * kb[x];
+                Xs[r * KP + m] = Ks[r * KP + m] * kb[x];   // for the row sums of K . dKB
             }
         }
         // dT += dW (diag(beta e^gc) K)^T: tiles (R, S) of the full [C, C]
@@ -645,14 +649,15 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         }
         __syncthreads();
         // dK += Dk K + Dk^T K on this wave's accumulator tile (Dk strictly lower)
-        if (accw) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) if (tile_ok(t)) {
             const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-            const int R0 = aR - 4 * lq, M0 = aM - li;
+            const int R0 = tile_r0(t), M0 = tile_m0(t);
             auto bk = [&](int kk, int jj) { return Ks[kk * KP + M0 + jj]; };
             const floatx4 x1 = mfma_f32_tile(z, 0, R0 + 16, [&](int ii, int kk) { return dMs[(R0 + ii) * BW_CP + kk]; }, bk);
             const floatx4 x2 = mfma_f32_tile(z, R0, BW_C, [&](int ii, int kk) { return dMs[kk * BW_CP + R0 + ii]; }, bk);
 #pragma unroll
-            for (int p = 0; p < PE; ++p) aK[p] += x1[p] + x2[p];
+            for (int x = 0; x < 4; ++x) aK[4 * t + x] += x1[x] + x2[x];
         }
         // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL)
         if (tid == 0) {
@@ -668,8 +673,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         }
     }
 #pragma unroll
-    for (int p = 0; p < PE; ++p) if (accw) {
-        const int r = aR + p, m = aM;
+    for (int p = 0; p < PE; ++p) if (tile_ok(p / 4)) {
+        const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
         if (r < n) {
             const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
             dq[off] = from_f32<T>(scale * aQ[p]);
