@@ -172,14 +172,21 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             }
         }
         __syncthreads();
-        // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution, one thread per column
+        // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution, one thread per column with the
+        // column in registers (fully unrolled; A is read by broadcast, four partial sums per row)
         if (tid < BW_BV) {
+            float y[BW_C];
+#pragma unroll
+            for (int r = 0; r < BW_C; ++r) y[r] = Ys[r * BW_VP + tid];
+#pragma unroll
             for (int r = BW_C - 2; r >= 0; --r) {
-                float acc = Ys[r * BW_VP + tid];
-#pragma unroll 8
-                for (int s = r + 1; s < BW_C; ++s) acc = fmaf(-As[s * BW_CP + r], Ys[s * BW_VP + tid], acc);
-                Ys[r * BW_VP + tid] = acc;
+                float acc[4] = {y[r], 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = r + 1; s < BW_C; ++s) acc[(s - r - 1) & 3] = fmaf(-As[s * BW_CP + r], y[s], acc[(s - r - 1) & 3]);
+                y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
+#pragma unroll
+            for (int r = 0; r < BW_C; ++r) Ys[r * BW_VP + tid] = y[r];
         }
         __syncthreads();
         // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y:
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
     extern __shared__ float lds[];
     const int bid = blockIdx.x;
     if (bid < n_state_blocks) {
-        simt_chunk_body<T, DK, DV, BV, false, DH_NT>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
+        simt_chunk_body<T, DK, DV, BV, false, DH_NT, BW_C>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
                                                       nullptr, H, T_len, Hqk, Hv, grp, BW_C, scale, nullptr, 0);
     } else {
         const int x = bid - n_state_blocks;

@@ -42,7 +42,8 @@ __device__ __forceinline__ floatx4 mfma_f32_tile(floatx4 acc, int k0, int k1, FA
 }
 
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
-template <typename T, int DK, int DV, int BV, bool OUT, int NTH>
+// CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
+template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX>
 __device__ __forceinline__ void simt_chunk_body(
     float* lds, int head, int tile,   // head = b * Hv + j; tile = column tile of BV
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -176,13 +177,33 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column.
+        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column: with
+        // the chunk no longer than the column registers (CMAX <= 32) the column stays in registers
+        // (fully unrolled, four partial sums per row), else it goes through LDS.
         if (tid < BV) {
-            for (int r = 1; r < C; ++r) {
-                float acc = Rs[r * BV + tid];
+            if constexpr (CMAX <= 32) {
+                float y[CMAX];
+#pragma unroll
+                for (int r = 0; r < CMAX; ++r) y[r] = r < C ? Rs[r * BV + tid] : 0.f;
+#pragma unroll
+                for (int r = 1; r < CMAX; ++r) {
+                    if (r < C) {
+                        float acc[4] = {y[r], 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < r; ++c) acc[c & 3] = fmaf(-As[r * L::CP + c], y[c], acc[c & 3]);
+                        y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < CMAX; ++r)
+                    if (r < C) Rs[r * BV + tid] = y[r];
+            } else {
+                for (int r = 1; r < C; ++r) {
+                    float acc = Rs[r * BV + tid];
 #pragma unroll 8
-                for (int c = 0; c < r; ++c) acc = fmaf(-As[r * L::CP + c], Rs[c * BV + tid], acc);
-                Rs[r * BV + tid] = acc;
+                    for (int c = 0; c < r; ++c) acc = fmaf(-As[r * L::CP + c], Rs[c * BV + tid], acc);
+                    Rs[r * BV + tid] = acc;
+                }
             }
         }
         __syncthreads();
