@@ -90,32 +90,57 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
 
     for (int e = tid; e < DK * BW_BV; e += DH_NT)
         dhs[e] = dsf ? dsf[sbase + (size_t)(e / BW_BV) * DV + e % BW_BV] : 0.f;
+    // Each chunk's inputs are loaded into registers a chunk ahead (the chunk before it, as the
+    // pass runs backwards), with unconditional loads of rows clamped into the sequence; rows past
+    // its end are zeroed when they are written to LDS.
+    constexpr int KPT = (BW_C * DK + DH_NT - 1) / DH_NT;
+    constexpr int VPT = (BW_C * BW_BV + DH_NT - 1) / DH_NT;
+    T kr[KPT], qr[KPT], dr[VPT];
+    float gr = 0.f, br = 0.f;
+    auto fetch = [&](int t0) {   // 0 <= t0 < T_len
+#pragma unroll
+        for (int p = 0; p < KPT; ++p) {
+            const int e = tid + p * DH_NT, r = e / DK, m = e % DK;
+            const size_t off = (((size_t)b * T_len + min(t0 + r, T_len - 1)) * Hqk + i) * DK + m;
+            kr[p] = k[off];
+            qr[p] = q[off];
+        }
+#pragma unroll
+        for (int p = 0; p < VPT; ++p) {
+            const int e = tid + p * DH_NT, r = e / BW_BV, c = e % BW_BV;
+            dr[p] = dout[(((size_t)b * T_len + min(t0 + r, T_len - 1)) * Hv + j) * DV + c0 + c];
+        }
+        if (tid < BW_C) {
+            const size_t off = ((size_t)b * T_len + min(t0 + tid, T_len - 1)) * Hv + j;
+            gr = g[off];
+            br = beta[off];
+        }
+    };
+    if (NT > 0) fetch((NT - 1) * BW_C);
     for (int ci = NT - 1; ci >= 0; --ci) {
         const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
         __syncthreads();
         // the exit-state gradient of this chunk, for the per-chunk kernel
         float* dp = dH + ((size_t)head * NT + ci) * DK * DV + c0;
         for (int e = tid; e < DK * BW_BV; e += DH_NT) dp[(size_t)(e / BW_BV) * DV + e % BW_BV] = dhs[e];
-        for (int e = tid; e < BW_C * DK; e += DH_NT) {
-            const int r = e / DK, m = e % DK;
-            float kv = 0.f, qv = 0.f;
-            if (r < n) {
-                const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
-                kv = to_f32(k[off]);
-                qv = to_f32(q[off]) * scale;
+#pragma unroll
+        for (int p = 0; p < KPT; ++p) {
+            const int e = tid + p * DH_NT, r = e / DK, m = e % DK;
+            if (e < BW_C * DK) {
+                Ks[r * KP + m] = r < n ? to_f32(kr[p]) : 0.f;
+                Qs[r * KP + m] = r < n ? to_f32(qr[p]) * scale : 0.f;
             }
-            Ks[r * KP + m] = kv;
-            Qs[r * KP + m] = qv;
         }
-        for (int e = tid; e < BW_C * BW_BV; e += DH_NT) {
-            const int r = e / BW_BV, c = e % BW_BV;
-            dOs[r * BW_VP + c] = r < n ? to_f32(dout[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
+#pragma unroll
+        for (int p = 0; p < VPT; ++p) {
+            const int e = tid + p * DH_NT, r = e / BW_BV, c = e % BW_BV;
+            if (e < BW_C * BW_BV) dOs[r * BW_VP + c] = r < n ? to_f32(dr[p]) : 0.f;
         }
         if (tid < BW_C) {
-            const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
-            gcs[tid] = tid < n ? g[off] : 0.f;
-            bs[tid] = tid < n ? beta[off] : 0.f;
+            gcs[tid] = tid < n ? gr : 0.f;
+            bs[tid] = tid < n ? br : 0.f;
         }
+        if (ci > 0) fetch(t0 - BW_C);
         __syncthreads();
         if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
             float x = tid < BW_C ? gcs[tid] : 0.f;
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
     extern __shared__ float lds[];
     const int bid = blockIdx.x;
     if (bid < n_state_blocks) {
-        simt_chunk_body<T, DK, DV, BV, false, DH_NT, BW_C>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
+        simt_chunk_body<T, DK, DV, BV, false, DH_NT, BW_C, true>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
                                                       nullptr, H, T_len, Hqk, Hv, grp, BW_C, scale, nullptr, 0);
     } else {
         const int x = bid - n_state_blocks;

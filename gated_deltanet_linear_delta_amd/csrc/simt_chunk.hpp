@@ -43,7 +43,8 @@ __device__ __forceinline__ floatx4 mfma_f32_tile(floatx4 acc, int k0, int k1, FA
 
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 // CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
-template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX>
+// PF: load each chunk's inputs into registers a chunk ahead (see below), else at the chunk's turn.
+template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX, bool PF = false>
 __device__ __forceinline__ void simt_chunk_body(
     float* lds, int head, int tile,   // head = b * Hv + j; tile = column tile of BV
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -89,6 +90,37 @@ __device__ __forceinline__ void simt_chunk_body(
         hs[e] = s0 ? s0[sbase + (size_t)m * DV + c] : 0.f;
     }
 
+    // With PF, each chunk's inputs are loaded into registers a chunk ahead: the loads of the next
+    // chunk are in flight while this one computes, and land in LDS at the top of its turn.  The
+    // loads are unconditional, with the row clamped into the sequence (rows past its end are
+    // zeroed when they are written to LDS).  The 1,024-thread states-only pass of the backward
+    // gains from it; the 512-thread output kernel at 64-token chunks (16 K and 16 Q registers per
+    // thread) measured slower with it than with the loads at each chunk's turn.
+    constexpr int KPT = PF ? (CMAX * DK + NTH - 1) / NTH : 1;   // K (and Q) elements per thread
+    constexpr int VPT = PF ? (CMAX * BV + NTH - 1) / NTH : 1;   // V elements per thread
+    T kr[KPT], qr[OUT ? KPT : 1], vr[VPT];
+    float gr = 0.f, br = 0.f;
+    auto fetch = [&](int t0) {   // t0 < T_len; rows at or past T_len read row T_len - 1
+#pragma unroll
+        for (int p = 0; p < KPT; ++p) {
+            const int e = tid + p * NTH, r = e / DK, m = e % DK;
+            const size_t off = ((tok0 + min(t0 + r, T_len - 1)) * Hqk + i) * DK + m;
+            kr[p] = k[off];
+            if (OUT) qr[p] = q[off];
+        }
+#pragma unroll
+        for (int p = 0; p < VPT; ++p) {
+            const int e = tid + p * NTH, r = e / BV, c = e % BV;
+            vr[p] = v[((tok0 + min(t0 + r, T_len - 1)) * Hv + j) * DV + c0 + c];
+        }
+        if (tid < C) {
+            const size_t off = (tok0 + min(t0 + tid, T_len - 1)) * Hv + j;
+            gr = g[off];
+            br = beta[off];
+        }
+    };
+    if (PF && T_len > 0) fetch(0);
+
     for (int t0 = 0; t0 < T_len; t0 += C) {
         const int n = min(C, T_len - t0);
         __syncthreads();  // previous chunk finished with every LDS buffer
@@ -97,25 +129,46 @@ __device__ __forceinline__ void simt_chunk_body(
             float* hp = hst + ((size_t)head * NT + t0 / C) * DK * DV + c0;
             for (int e = tid; e < DK * BV; e += NTH) hp[(size_t)(e / BV) * DV + e % BV] = hs[e];
         }
-        for (int e = tid; e < C * DK; e += NTH) {
-            const int r = e / DK, m = e % DK;
-            float kv = 0.f, qv = 0.f;
-            if (r < n) {
-                const size_t off = ((tok0 + t0 + r) * Hqk + i) * DK + m;
-                kv = to_f32(k[off]);
-                if (OUT) qv = to_f32(q[off]) * scale;
+        if constexpr (PF) {
+#pragma unroll
+            for (int p = 0; p < KPT; ++p) {
+                const int e = tid + p * NTH, r = e / DK, m = e % DK;
+                if (e < C * DK) {
+                    Ks[r * L::KP + m] = r < n ? to_f32(kr[p]) : 0.f;
+                    if (OUT) Qs[r * L::KP + m] = r < n ? to_f32(qr[p]) * scale : 0.f;
+                }
             }
-            Ks[r * L::KP + m] = kv;
-            if (OUT) Qs[r * L::KP + m] = qv;
-        }
-        for (int e = tid; e < C * BV; e += NTH) {
-            const int r = e / BV, c = e % BV;
-            Vs[e] = r < n ? to_f32(v[((tok0 + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
-        }
-        if (tid < C) {
-            const size_t off = (tok0 + t0 + tid) * Hv + j;
-            gcs[tid] = tid < n ? g[off] : 0.f;
-            bs[tid] = tid < n ? beta[off] : 0.f;
+#pragma unroll
+            for (int p = 0; p < VPT; ++p) {
+                const int e = tid + p * NTH;
+                if (e < C * BV) Vs[e] = e / BV < n ? to_f32(vr[p]) : 0.f;
+            }
+            if (tid < C) {
+                gcs[tid] = tid < n ? gr : 0.f;
+                bs[tid] = tid < n ? br : 0.f;
+            }
+            if (t0 + C < T_len) fetch(t0 + C);
+        } else {
+            for (int e = tid; e < C * DK; e += NTH) {
+                const int r = e / DK, m = e % DK;
+                float kv = 0.f, qv = 0.f;
+                if (r < n) {
+                    const size_t off = ((tok0 + t0 + r) * Hqk + i) * DK + m;
+                    kv = to_f32(k[off]);
+                    if (OUT) qv = to_f32(q[off]) * scale;
+                }
+                Ks[r * L::KP + m] = kv;
+                if (OUT) Qs[r * L::KP + m] = qv;
+            }
+            for (int e = tid; e < C * BV; e += NTH) {
+                const int r = e / BV, c = e % BV;
+                Vs[e] = r < n ? to_f32(v[((tok0 + t0 + r) * Hv + j) * DV + c0 + c]) : 0.f;
+            }
+            if (tid < C) {
+                const size_t off = (tok0 + t0 + tid) * Hv + j;
+                gcs[tid] = tid < n ? g[off] : 0.f;
+                bs[tid] = tid < n ? beta[off] : 0.f;
+            }
         }
         __syncthreads();
         if (tid < 64) {  // per-chunk log-decay cumsum (C <= 64 terms): a scan across wave 0
@@ -177,11 +230,11 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column: with
-        // the chunk no longer than the column registers (CMAX <= 32) the column stays in registers
-        // (fully unrolled, four partial sums per row), else it goes through LDS.
+        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column: where
+        // the register budget leaves room for the column (64 rows at 512 threads, 32 at 1,024) it
+        // stays in registers (fully unrolled, four partial sums per row), else it goes through LDS.
         if (tid < BV) {
-            if constexpr (CMAX <= 32) {
+            if constexpr (CMAX * NTH <= 32 * 1024) {
                 float y[CMAX];
 #pragma unroll
                 for (int r = 0; r < CMAX; ++r) y[r] = r < C ? Rs[r * BV + tid] : 0.f;
