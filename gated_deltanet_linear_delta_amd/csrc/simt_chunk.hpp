@@ -31,12 +31,14 @@ struct SimtLds {
 // D += A B for one 16 x 16 tile on the float32 matrix cores (v_mfma_f32_16x16x4_f32): lane l
 // supplies A[l % 16][k + l / 16] = a(l % 16, k + l / 16) and B[k + l / 16][l % 16] =
 // b(k + l / 16, l % 16) for k = k0, k0 + 4, ... < k1 (k1 - k0 a multiple of 4) and holds
-// D[4 (l / 16) + x][l % 16] in element x.
+// D[4 (l / 16) + x][l % 16] in element x.  Unrolled by 4: at 8 the backward's gradient kernel
+// kept enough hoisted LDS addresses live to spill 104 registers per lane (23 at 4) and ran 8%
+// slower.
 template <typename FA, typename FB>
 __device__ __forceinline__ floatx4 mfma_f32_tile(floatx4 acc, int k0, int k1, FA&& a, FB&& b)
 {
     const int l = threadIdx.x & 63, i = l & 15, kq = l >> 4;
-#pragma unroll 8
+#pragma unroll 4
     for (int k = k0; k < k1; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(i, k + kq), b(k + kq, i), acc, 0, 0, 0);
     return acc;
 }
