@@ -416,15 +416,43 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
         }
         __syncthreads();
-        // T = (I + diag(beta) G)^{-1}: column s by forward substitution, one thread per column
+        // T = (I + diag(beta) G)^{-1} blockwise over the two 16 x 16 diagonal blocks: each diagonal
+        // block T_DD = (I + A_DD)^{-1} by forward substitution (one thread per column, the column
+        // in registers, G read by broadcast), then T_10 = -T_11 A_10 T_00 on the matrix cores
+        static_assert(BW_C == 32, "two diagonal blocks");
         if (tid < BW_C) {
-            const int s = tid;
-            for (int r = 0; r < BW_C; ++r) {
-                float acc = 0.f;
-#pragma unroll 8
-                for (int u = 0; u < r; ++u) acc = fmaf(Gs[r * BW_CP + u], Tm[u * BW_CP + s], acc);
-                Tm[r * BW_CP + s] = r == s ? 1.f : (r > s ? -bs[r] * acc : 0.f);
+            const int s = tid, D = 16 * (s / 16), sl = s % 16;
+            float y[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < r; ++u) acc[u & 3] = fmaf(Gs[(D + r) * BW_CP + D + u], y[u], acc[u & 3]);
+                const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                y[r] = r == sl ? 1.f : (r > sl ? -bs[D + r] * sum : 0.f);
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                Tm[(D + r) * BW_CP + s] = y[r];
+                if (D) Tm[r * BW_CP + s] = 0.f;   // above the diagonal blocks
+            }
+        }
+        __syncthreads();
+        // X = A_10 T_00 (A = diag(beta) G) into the row-sum scratch, then T_10 = -T_11 X: wave 0
+        if (w == 0) {
+            const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                             [&](int ii, int kk) { return bs[16 + ii] * Gs[(16 + ii) * BW_CP + kk]; },
+                                             [&](int kk, int jj) { return Tm[kk * BW_CP + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) P1[(4 * lq + x) * BW_VP + li] = x4[x];
+        }
+        __syncthreads();
+        if (w == 0) {
+            const floatx4 t4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                             [&](int ii, int kk) { return Tm[(16 + ii) * BW_CP + 16 + kk]; },
+                                             [&](int kk, int jj) { return P1[kk * BW_VP + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Tm[(16 + 4 * lq + x) * BW_CP + li] = -t4[x];
         }
         __syncthreads();
         // W = T diag(beta e^gc) K: tiles (R, M) (T lower triangular: the sum stops at the tile's rows)
@@ -441,22 +469,57 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         for (int p = 0; p < PE; ++p) aW[p] = aX[p] = 0.f;
         float dgl = 0.f;
 
+        // Each column tile's h, dh', V and dO are loaded into registers while the tile before it
+        // computes (h and dh' as 16-byte loads; rows of V and dO past the sequence's end read its
+        // last row and are zeroed when written to LDS).
+        constexpr int H4 = DK * BW_BV / 4;                    // float4 of h (and of dh') per tile
+        constexpr int HPT = (H4 + BW_NT - 1) / BW_NT;
+        constexpr int VPT = BW_C * BW_BV / BW_NT;             // elements of V (and of dO) per thread
+        static_assert(VPT * BW_NT == BW_C * BW_BV, "V tile spread evenly");
+        floatx4 hr[HPT], dhr[HPT];
+        T vr[VPT], dor[VPT];
+        auto fetch = [&](int c0) {
+            const float* hp = H + ((head * NT + ci) * DK) * DV + c0;
+            const float* dhp = dH + ((head * NT + ci) * DK) * DV + c0;
+#pragma unroll
+            for (int p = 0; p < HPT; ++p) {
+                const int e4 = tid + p * BW_NT, m = e4 / (BW_BV / 4), c = 4 * (e4 % (BW_BV / 4));
+                if (e4 < H4) {
+                    hr[p] = ld4(hp + (size_t)m * DV + c);
+                    dhr[p] = ld4(dhp + (size_t)m * DV + c);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < VPT; ++p) {
+                const int e = tid + p * BW_NT, r = e / BW_BV, c = e % BW_BV;
+                const size_t off = (((size_t)b * T_len + t0 + min(r, n - 1)) * Hv + j) * DV + c0 + c;
+                vr[p] = v[off];
+                dor[p] = dout[off];
+            }
+        };
+        fetch(0);
+
 #pragma unroll 1
         for (int c0 = 0; c0 < DV; c0 += BW_BV) {
             __syncthreads();   // W written; the previous tile's row sums done
-            const float* hp = H + ((head * NT + ci) * DK) * DV + c0;
-            const float* dhp = dH + ((head * NT + ci) * DK) * DV + c0;
-            for (int e = tid; e < DK * BW_BV; e += BW_NT) {
-                const int m = e / BW_BV, c = e % BW_BV;
-                hs[m * HP + c] = hp[(size_t)m * DV + c];
-                dhs[m * HP + c] = dhp[(size_t)m * DV + c];
+#pragma unroll
+            for (int p = 0; p < HPT; ++p) {
+                const int e4 = tid + p * BW_NT, m = e4 / (BW_BV / 4), c = 4 * (e4 % (BW_BV / 4));
+                if (e4 < H4) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        hs[m * HP + c + x] = hr[p][x];
+                        dhs[m * HP + c + x] = dhr[p][x];
+                    }
+                }
             }
-            for (int e = tid; e < BW_C * BW_BV; e += BW_NT) {
-                const int r = e / BW_BV, c = e % BW_BV;
-                const size_t off = (((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c;
-                Vs[r * BW_VP + c] = r < n ? to_f32(v[off]) : 0.f;
-                dOs[r * BW_VP + c] = r < n ? to_f32(dout[off]) : 0.f;
+#pragma unroll
+            for (int p = 0; p < VPT; ++p) {
+                const int e = tid + p * BW_NT, r = e / BW_BV, c = e % BW_BV;
+                Vs[r * BW_VP + c] = r < n ? to_f32(vr[p]) : 0.f;
+                dOs[r * BW_VP + c] = r < n ? to_f32(dor[p]) : 0.f;
             }
+            if (c0 + BW_BV < DV) fetch(c0 + BW_BV);
             __syncthreads();
             // Delta = T (beta V) - W h;  dDelta = diag(ed) K dh' + M^T dO: the (C / 16) x (BV / 16)
             // tiles on the float32 matrix cores, one per wave (T is lower triangular and M^T upper,
@@ -503,17 +566,33 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                     P2[r * BW_VP + c] = dOs[r * BW_VP + c] * qh[x];
                 }
             }
-            // dT += dDelta (diag(beta) V)^T;  dM += dO Delta^T (lower incl)
-            for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
-                const int r = e / BW_C, s = e % BW_C;
-                float x = 0.f, y = 0.f;
-#pragma unroll 4
-                for (int c = 0; c < BW_BV; ++c) {
-                    x = fmaf(dDs[r * BW_VP + c], Vs[s * BW_VP + c], x);
-                    y = fmaf(dOs[r * BW_VP + c], Ds[s * BW_VP + c], y);
+            // dT += dDelta (diag(beta) V)^T over all (R, S) tiles, dM += dO Delta^T over the tiles
+            // with S <= R (lower incl), summed over the tile's value columns on the matrix cores:
+            // waves 0 .. CT^2 - 1 take the dT tiles, the next CT (CT + 1) / 2 the dM tiles
+            static_assert(CT * CT + CT * (CT + 1) / 2 <= BW_NT / 64, "one [C, C] tile per wave");
+            if (w < CT * CT) {
+                const int R = w / CT, S = w % CT;
+                const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, BW_BV,
+                                                 [&](int ii, int kk) { return dDs[(16 * R + ii) * BW_VP + kk]; },
+                                                 [&](int kk, int jj) { return Vs[(16 * S + jj) * BW_VP + kk]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                    dTs[r * BW_CP + sc] += bs[sc] * x4[x];
                 }
-                dTs[r * BW_CP + s] += bs[s] * x;
-                if (s <= r) dMs[r * BW_CP + s] += y;
+            } else if (w < CT * CT + CT * (CT + 1) / 2) {
+                const int tt = w - CT * CT;
+                int R = 0;
+                while ((R + 1) * (R + 2) / 2 <= tt) ++R;
+                const int S = tt - R * (R + 1) / 2;
+                const floatx4 y4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, BW_BV,
+                                                 [&](int ii, int kk) { return dOs[(16 * R + ii) * BW_VP + kk]; },
+                                                 [&](int kk, int jj) { return Ds[(16 * S + jj) * BW_VP + kk]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                    if (sc <= r) dMs[r * BW_CP + sc] += y4[x];
+                }
             }
             // dW -= dDelta h^T;  X += Delta dh'^T;  dQ += diag(e^gc) dO h^T: this wave's
             // accumulator tile, summed over the tile's value columns on the matrix cores
