@@ -34,7 +34,7 @@ namespace gdn {
 namespace {
 
 constexpr int BW_NT = 512;    // threads per workgroup of the per-chunk kernel
-constexpr int DH_NT = 1024;  // threads per workgroup of the reverse state pass
+constexpr int DH_NT = 512;   // threads per workgroup of the two sequential passes
 constexpr int BW_C = 32;     // chunk length of the backward pass
 constexpr int BW_BV = 32;    // value columns per tile
 constexpr int BW_CP = BW_C + 1;
@@ -197,22 +197,37 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             }
         }
         __syncthreads();
-        // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution, one thread per column with the
-        // column in registers (fully unrolled; A is read by broadcast, four partial sums per row)
-        if (tid < BW_BV) {
-            float y[BW_C];
+        // y = (I + A)^{-T} dDelta = T^T dDelta, back substitution over the two 16-row blocks:
+        // y_1 = (I + A_11^T)^{-1} dDelta_1, then dDelta_0 -= A_10^T y_1 on the matrix cores, then
+        // y_0 = (I + A_00^T)^{-1} dDelta_0.  Within a block one thread per column, the column in
+        // registers (fully unrolled; A read by broadcast, four partial sums per row).
+        static_assert(BW_C == 32, "two row blocks");
+        auto back_block = [&](int D) {
+            float y[16];
 #pragma unroll
-            for (int r = 0; r < BW_C; ++r) y[r] = Ys[r * BW_VP + tid];
+            for (int r = 0; r < 16; ++r) y[r] = Ys[(D + r) * BW_VP + tid];
 #pragma unroll
-            for (int r = BW_C - 2; r >= 0; --r) {
+            for (int r = 14; r >= 0; --r) {
                 float acc[4] = {y[r], 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = r + 1; s < BW_C; ++s) acc[(s - r - 1) & 3] = fmaf(-As[s * BW_CP + r], y[s], acc[(s - r - 1) & 3]);
+                for (int s2 = r + 1; s2 < 16; ++s2)
+                    acc[(s2 - r - 1) & 3] = fmaf(-As[(D + s2) * BW_CP + D + r], y[s2], acc[(s2 - r - 1) & 3]);
                 y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
 #pragma unroll
-            for (int r = 0; r < BW_C; ++r) Ys[r * BW_VP + tid] = y[r];
+            for (int r = 0; r < 16; ++r) Ys[(D + r) * BW_VP + tid] = y[r];
+        };
+        if (tid < BW_BV) back_block(16);
+        __syncthreads();
+        if (w < BW_BV / 16) {
+            const floatx4 t4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                             [&](int ii, int kk) { return As[(16 + kk) * BW_CP + ii]; },
+                                             [&](int kk, int jj) { return Ys[(16 + kk) * BW_VP + 16 * w + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Ys[(4 * lq + x) * BW_VP + 16 * w + li] -= t4[x];
         }
+        __syncthreads();
+        if (tid < BW_BV) back_block(0);
         __syncthreads();
         // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y:
         // tiles (M, T) of the state
@@ -241,7 +256,8 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
 // 0 .. n_chains * NTILE - 1 recompute the states entering every chunk (the float32 forward chunk
 // step, no output), the others run the reverse state pass.  The passes do not depend on each
 // other, and each has only one workgroup per (batch, value head, column tile), so together they
-// fill twice as many compute units as either alone.  1,024 threads per workgroup for both.
+// fill twice as many compute units as either alone.  512 threads per workgroup for both
+// (at 1,024 the 128-register cap spilled the register-column substitutions).
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,

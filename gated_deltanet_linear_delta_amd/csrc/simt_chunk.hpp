@@ -232,36 +232,39 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        // Delta = (I + A)^{-1} R, forward substitution down the rows, one thread per column: where
-        // the register budget leaves room for the column (64 rows at 512 threads, 32 at 1,024) it
-        // stays in registers (fully unrolled, four partial sums per row), else it goes through LDS.
-        if (tid < BV) {
-            if constexpr (CMAX * NTH <= 32 * 1024) {
-                float y[CMAX];
+        // Delta = (I + A)^{-1} R blockwise over 16-row blocks D = 0, 16, ...: forward substitution
+        // inside the block (one thread per column, the column in registers, fully unrolled; A read
+        // by broadcast, four partial sums per row), then the rows below it take R -= A[rows, D..]
+        // Delta[D..] on the matrix cores.
+        for (int D = 0; D < C; D += 16) {
+            if (tid < BV) {
+                float y[16];
 #pragma unroll
-                for (int r = 0; r < CMAX; ++r) y[r] = r < C ? Rs[r * BV + tid] : 0.f;
+                for (int r = 0; r < 16; ++r) y[r] = Rs[(D + r) * BV + tid];
 #pragma unroll
-                for (int r = 1; r < CMAX; ++r) {
-                    if (r < C) {
-                        float acc[4] = {y[r], 0.f, 0.f, 0.f};
+                for (int r = 1; r < 16; ++r) {
+                    float acc[4] = {y[r], 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int c = 0; c < r; ++c) acc[c & 3] = fmaf(-As[r * L::CP + c], y[c], acc[c & 3]);
-                        y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                    }
+                    for (int c = 0; c < r; ++c) acc[c & 3] = fmaf(-As[(D + r) * L::CP + D + c], y[c], acc[c & 3]);
+                    y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
                 }
 #pragma unroll
-                for (int r = 0; r < CMAX; ++r)
-                    if (r < C) Rs[r * BV + tid] = y[r];
-            } else {
-                for (int r = 1; r < C; ++r) {
-                    float acc = Rs[r * BV + tid];
-#pragma unroll 8
-                    for (int c = 0; c < r; ++c) acc = fmaf(-As[r * L::CP + c], Rs[c * BV + tid], acc);
-                    Rs[r * BV + tid] = acc;
+                for (int r = 0; r < 16; ++r) Rs[(D + r) * BV + tid] = y[r];
+            }
+            __syncthreads();
+            if (D + 16 < C) {
+                const int RT0 = D / 16 + 1;   // first row tile below the block
+                for (int tt = w; tt < (CT - RT0) * BT; tt += nw) {
+                    const int R = RT0 + tt / BT, T2 = tt % BT;
+                    const floatx4 u4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                                     [&](int ii, int k) { return As[(16 * R + ii) * L::CP + D + k]; },
+                                                     [&](int k, int jj) { return Rs[(D + k) * BV + 16 * T2 + jj]; });
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) Rs[(16 * R + 4 * lq + x) * BV + 16 * T2 + li] -= u4[x];
                 }
+                __syncthreads();
             }
         }
-        __syncthreads();
         // O = exp(gc) Q h0 + Aq Delta (Aq is zero right of the diagonal: k up to the tile's end)
         if (OUT && w < CT * BT) {
             const floatx4 ot = mfma_f32_tile(qh, 0, 16 * (tr + 1),
