@@ -167,10 +167,9 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             while ((R + 1) * (R + 2) / 2 <= tt) ++R;
             const int S = tt - R * (R + 1) / 2;
             auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
-            const floatx4 ga = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
-                                             [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk);
-            const floatx4 gq = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
-                                             [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
+            floatx4 ga = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+            mfma_f32_pair(ga, gq, 0, DK, [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk,
+                          [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
@@ -232,7 +231,28 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
         // entry-state gradient: e^gL dh' + (scale Q)^T diag(e^gc) dO - (diag(beta e^gc) K)^T y:
         // tiles (M, T) of the state
         const float eL = egs[BW_C - 1];
-        for (int tt = w; tt < (DK / 16) * BT; tt += DH_NT / 64) {
+        if constexpr (BT == 2 && DK / 16 >= DH_NT / 64) {
+            // both column tiles of one 16-row block M per wave: the Q and K operands read once
+            for (int M = w; M < DK / 16; M += DH_NT / 64) {
+                floatx4 d0, d1;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    d0[x] = eL * dhs[(16 * M + 4 * lq + x) * BW_BV + li];
+                    d1[x] = eL * dhs[(16 * M + 4 * lq + x) * BW_BV + 16 + li];
+                }
+                auto aq = [&](int ii, int kk) { return egs[kk] * Qs[kk * KP + 16 * M + ii]; };
+                auto ak = [&](int ii, int kk) { return -bs[kk] * egs[kk] * Ks[kk * KP + 16 * M + ii]; };
+                mfma_f32_pair(d0, d1, 0, BW_C, aq, [&](int kk, int jj) { return dOs[kk * BW_VP + jj]; },
+                              aq, [&](int kk, int jj) { return dOs[kk * BW_VP + 16 + jj]; });
+                mfma_f32_pair(d0, d1, 0, BW_C, ak, [&](int kk, int jj) { return Ys[kk * BW_VP + jj]; },
+                              ak, [&](int kk, int jj) { return Ys[kk * BW_VP + 16 + jj]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    dhs[(16 * M + 4 * lq + x) * BW_BV + li] = d0[x];
+                    dhs[(16 * M + 4 * lq + x) * BW_BV + 16 + li] = d1[x];
+                }
+            }
+        } else for (int tt = w; tt < (DK / 16) * BT; tt += DH_NT / 64) {
             const int M = tt / BT, T2 = tt % BT;
             floatx4 acc;
 #pragma unroll

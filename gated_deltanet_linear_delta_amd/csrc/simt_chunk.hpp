@@ -43,6 +43,21 @@ __device__ __forceinline__ floatx4 mfma_f32_tile(floatx4 acc, int k0, int k1, FA
     return acc;
 }
 
+// Two tiles in one pass over k: D0 += A0 B0 and D1 += A1 B1, with the operands in the layout of
+// mfma_f32_tile.  Where the two tiles share an operand (the same expression in both), each step
+// reads it from LDS once for both products.
+template <typename FA0, typename FB0, typename FA1, typename FB1>
+__device__ __forceinline__ void mfma_f32_pair(floatx4& d0, floatx4& d1, int k0, int k1, FA0&& a0, FB0&& b0,
+                                              FA1&& a1, FB1&& b1)
+{
+    const int l = threadIdx.x & 63, i = l & 15, kq = l >> 4;
+#pragma unroll 4
+    for (int k = k0; k < k1; k += 4) {
+        d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0(i, k + kq), b0(k + kq, i), d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1(i, k + kq), b1(k + kq, i), d1, 0, 0, 0);
+    }
+}
+
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 // CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
 // PF: load each chunk's inputs into registers a chunk ahead (see below), else at the chunk's turn.
@@ -276,9 +291,28 @@ __device__ __forceinline__ void simt_chunk_body(
                 if (r < n) o[((tok0 + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(ot[x]);
             }
         }
-        // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T: tiles (M, T) of the state
+        // h1 = exp(gc_C) h0 + sum_r exp(gc_C - gc_r) k_r Delta_r^T: tiles (M, T) of the state; with
+        // as many 16-row blocks M as waves, each wave takes both column tiles of its M (BT = 2),
+        // reading the K operand once for the two
         const float ec = egs[C - 1];
-        for (int tt = w; tt < (DK / 16) * BT; tt += nw) {
+        if constexpr (BT == 2 && DK / 16 >= NTH / 64) {
+            for (int M = w; M < DK / 16; M += nw) {
+                floatx4 d0, d1;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    d0[x] = ec * hs[(16 * M + 4 * lq + x) * BV + li];
+                    d1[x] = ec * hs[(16 * M + 4 * lq + x) * BV + 16 + li];
+                }
+                auto ak = [&](int ii, int k) { return eds[k] * Ks[k * L::KP + 16 * M + ii]; };
+                mfma_f32_pair(d0, d1, 0, C, ak, [&](int k, int jj) { return Rs[k * BV + jj]; },
+                              ak, [&](int k, int jj) { return Rs[k * BV + 16 + jj]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    hs[(16 * M + 4 * lq + x) * BV + li] = d0[x];
+                    hs[(16 * M + 4 * lq + x) * BV + 16 + li] = d1[x];
+                }
+            }
+        } else for (int tt = w; tt < (DK / 16) * BT; tt += nw) {
             const int M = tt / BT, T2 = tt % BT;
             floatx4 acc;
 #pragma unroll
