@@ -557,28 +557,34 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
             if (c0 + BW_BV < DV) fetch(c0 + BW_BV);
             __syncthreads();
-            // Delta = T (beta V) - W h;  dDelta = diag(ed) K dh' + M^T dO: the (C / 16) x (BV / 16)
-            // tiles on the float32 matrix cores, one per wave (T is lower triangular and M^T upper,
-            // so their sums stop at, or start at, the tile's own rows)
-            constexpr int VT = BW_BV / 16;
-            const int tr = w / VT, tc = w % VT;
-            if (w < (BW_C / 16) * VT) {
+            // Delta = T (beta V) - W h and dDelta = diag(ed) K dh' + M^T dO over the (C / 16) x (BV / 16)
+            // tiles on the float32 matrix cores: one wave per tile for Delta and another for dDelta
+            // (T is lower triangular and M^T upper, so their sums stop at, or start at, the tile's
+            // own rows)
+            constexpr int VT = BW_BV / 16, DT = (BW_C / 16) * VT;
+            static_assert(2 * DT <= BW_NT / 64, "a wave per tile of each");
+            if (w < 2 * DT) {
+                const int tr = (w % DT) / VT, tc = w % VT;
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                const floatx4 u = mfma_f32_tile(z, 0, 16 * (tr + 1),
-                                                [&](int ii, int kk) { return Tm[(16 * tr + ii) * BW_CP + kk] * bs[kk]; },
-                                                [&](int kk, int jj) { return Vs[kk * BW_VP + 16 * tc + jj]; });
-                const floatx4 wh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ws[(16 * tr + ii) * KP + kk]; },
-                                                 [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
-                const floatx4 kd = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * tr + ii) * KP + kk]; },
-                                                 [&](int kk, int jj) { return dhs[kk * HP + 16 * tc + jj]; });
-                const floatx4 md = mfma_f32_tile(z, 16 * tr, BW_C,
-                                                 [&](int ii, int kk) { return Ms[kk * BW_CP + 16 * tr + ii]; },
-                                                 [&](int kk, int jj) { return dOs[kk * BW_VP + 16 * tc + jj]; });
+                if (w < DT) {
+                    const floatx4 u = mfma_f32_tile(z, 0, 16 * (tr + 1),
+                                                    [&](int ii, int kk) { return Tm[(16 * tr + ii) * BW_CP + kk] * bs[kk]; },
+                                                    [&](int kk, int jj) { return Vs[kk * BW_VP + 16 * tc + jj]; });
+                    const floatx4 wh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ws[(16 * tr + ii) * KP + kk]; },
+                                                     [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
-                    Ds[r * BW_VP + c] = u[x] - wh[x];
-                    dDs[r * BW_VP + c] = fmaf(eds[r], kd[x], md[x]);
+                    for (int x = 0; x < 4; ++x) Ds[(16 * tr + 4 * lq + x) * BW_VP + 16 * tc + li] = u[x] - wh[x];
+                } else {
+                    const floatx4 kd = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * tr + ii) * KP + kk]; },
+                                                     [&](int kk, int jj) { return dhs[kk * HP + 16 * tc + jj]; });
+                    const floatx4 md = mfma_f32_tile(z, 16 * tr, BW_C,
+                                                     [&](int ii, int kk) { return Ms[kk * BW_CP + 16 * tr + ii]; },
+                                                     [&](int kk, int jj) { return dOs[kk * BW_VP + 16 * tc + jj]; });
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int r = 16 * tr + 4 * lq + x;
+                        dDs[r * BW_VP + 16 * tc + li] = fmaf(eds[r], kd[x], md[x]);
+                    }
                 }
             }
             for (int e = tid; e < DK * BW_BV; e += BW_NT) {
@@ -587,7 +593,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
             __syncthreads();
             // dV = diag(beta) T^T dDelta (complete for this tile); row-sum terms of dbeta and dgc
-            if (w < (BW_C / 16) * VT) {
+            const int tr = w / VT, tc = w % VT;
+            if (w < DT) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
                 const floatx4 tdu = mfma_f32_tile(z, 16 * tr, BW_C,
                                                   [&](int ii, int kk) { return Tm[kk * BW_CP + 16 * tr + ii]; },
