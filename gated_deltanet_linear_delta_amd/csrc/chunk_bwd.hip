@@ -17,7 +17,9 @@
 //   dA = strictly-lower(-T^T dT T^T),  and the gates' and keys' terms of every product;
 //   dg = reverse cumulative sum of dgc inside the chunk.
 //
-// Two launches (chunks of 32 positions, value columns in tiles of 32):
+// Three launches (chunks of 32 positions, value columns in tiles of 32):
+// 0. bwd_gram_kernel, one workgroup per (batch, value head, chunk): A and M of the chunk into the
+//    workspace (they depend on the chunk's inputs only);
 // 1. bwd_pass_kernel, two independent sequential passes side by side, one workgroup per (batch,
 //    value head, column tile) each: the float32 forward chunk step run again, storing the state
 //    entering every chunk (workspace H), and the reverse state pass, storing each chunk's
@@ -66,7 +68,7 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
                                             const float* __restrict__ beta, const T* __restrict__ dout,
                                             const float* __restrict__ dsf, float* __restrict__ dH,
                                             float* __restrict__ ds0, int T_len, int Hqk, int Hv, int grp,
-                                            float scale)
+                                            float scale, const float* __restrict__ Ain)
 {
     using L = DhLds<DK>;
     constexpr int KP = L::KP;
@@ -95,9 +97,15 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     // its end are zeroed when they are written to LDS.
     constexpr int KPT = (BW_C * DK + DH_NT - 1) / DH_NT;
     constexpr int VPT = (BW_C * BW_BV + DH_NT - 1) / DH_NT;
+    constexpr int APT = 2 * BW_C * BW_C / DH_NT;   // A and M elements per thread
+    static_assert(APT * DH_NT == 2 * BW_C * BW_C, "A and M spread evenly");
     T kr[KPT], qr[KPT], dr[VPT];
+    float ar[APT];
     float gr = 0.f, br = 0.f;
     auto fetch = [&](int t0) {   // 0 <= t0 < T_len
+        const float* ap = Ain + ((size_t)head * NT + t0 / BW_C) * 2 * BW_C * BW_C;
+#pragma unroll
+        for (int p = 0; p < APT; ++p) ar[p] = ap[tid + p * DH_NT];
 #pragma unroll
         for (int p = 0; p < KPT; ++p) {
             const int e = tid + p * DH_NT, r = e / DK, m = e % DK;
@@ -140,6 +148,11 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             gcs[tid] = tid < n ? gr : 0.f;
             bs[tid] = tid < n ? br : 0.f;
         }
+#pragma unroll
+        for (int p = 0; p < APT; ++p) {   // A, then M: [2][C][C]
+            const int e = tid + p * DH_NT, mat = e / (BW_C * BW_C), rc = e % (BW_C * BW_C);
+            (mat ? Ms : As)[(rc / BW_C) * BW_CP + rc % BW_C] = ar[p];
+        }
         if (ci > 0) fetch(t0 - BW_C);
         __syncthreads();
         if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
@@ -161,24 +174,6 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
         // per wave at a time.
         constexpr int CT = BW_C / 16, BT = BW_BV / 16;
         const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
-        // A (strictly lower) and M (lower including the diagonal): tiles (R, S), S <= R
-        for (int tt = w; tt < CT * (CT + 1) / 2; tt += DH_NT / 64) {
-            int R = 0;
-            while ((R + 1) * (R + 2) / 2 <= tt) ++R;
-            const int S = tt - R * (R + 1) / 2;
-            auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
-            floatx4 ga = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
-            mfma_f32_pair(ga, gq, 0, DK, [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk,
-                          [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
-                const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
-                As[r * BW_CP + sc] = sc < r ? bs[r] * gam * ga[x] : 0.f;
-                Ms[r * BW_CP + sc] = gam * gq[x];
-            }
-        }
-        __syncthreads();
         // dDelta = diag(ed) K dh' + M^T dO: tiles (R, T) of the chunk's rows and the columns; M^T's
         // column r is nonzero from row r on, so its sum starts at the tile's first row
         if (w < CT * BT) {
@@ -272,6 +267,75 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     }
 }
 
+// A and M of every (batch, value head, chunk) for the two sequential passes, which then load them
+// a chunk ahead instead of forming them inside their serial chains (both depend on the chunk's q,
+// k, g and beta only).  Aw[(b Hv + j) NT + ci] holds [2][C][C]: A = strictly-lower(diag(beta)
+// (K K^T * Gamma)), then M = lower-incl((scale Q) K^T * Gamma).  One 256-thread workgroup per
+// (batch, value head, chunk); the 16 x 16 tiles on the float32 matrix cores in the same order as
+// the passes would take them.
+constexpr int GR_NT = 256;
+
+template <typename T, int DK>
+__global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                         const float* __restrict__ g, const float* __restrict__ beta,
+                                                         float* __restrict__ Aw, int T_len, int Hqk, int Hv, int grp,
+                                                         float scale)
+{
+    constexpr int KP = DK + 1, CT = BW_C / 16;
+    __shared__ float Ks[BW_C * KP], Qs[BW_C * KP], gcs[BW_C], bs[BW_C];
+    const int NT = (T_len + BW_C - 1) / BW_C;
+    const int ci = blockIdx.x % NT, head = blockIdx.x / NT;
+    const int b = head / Hv, j = head - b * Hv, i = j / grp;
+    const int t0 = ci * BW_C, n = min(BW_C, T_len - t0);
+    const int tid = threadIdx.x;
+    for (int e = tid; e < BW_C * DK; e += GR_NT) {
+        const int r = e / DK, m = e % DK;
+        float kv = 0.f, qv = 0.f;
+        if (r < n) {
+            const size_t off = (((size_t)b * T_len + t0 + r) * Hqk + i) * DK + m;
+            kv = to_f32(k[off]);
+            qv = to_f32(q[off]) * scale;
+        }
+        Ks[r * KP + m] = kv;
+        Qs[r * KP + m] = qv;
+    }
+    if (tid < BW_C) {
+        const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+        gcs[tid] = tid < n ? g[off] : 0.f;
+        bs[tid] = tid < n ? beta[off] : 0.f;
+    }
+    __syncthreads();
+    if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
+        float x = tid < BW_C ? gcs[tid] : 0.f;
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) {
+            const float y = __shfl_up(x, sh, 64);
+            if (tid >= sh) x += y;
+        }
+        if (tid < BW_C) gcs[tid] = x;
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
+    float* Ao = Aw + ((size_t)head * NT + ci) * 2 * BW_C * BW_C;
+    float* Mo = Ao + BW_C * BW_C;
+    for (int tt = w; tt < CT * CT; tt += GR_NT / 64) {   // tiles (R, S); those above the diagonal are zero
+        const int R = tt / CT, S = tt % CT;
+        floatx4 ga = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
+        if (S <= R) {
+            auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
+            mfma_f32_pair(ga, gq, 0, DK, [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk,
+                          [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+            const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
+            Ao[r * BW_C + sc] = sc < r ? bs[r] * gam * ga[x] : 0.f;
+            Mo[r * BW_C + sc] = gam * gq[x];
+        }
+    }
+}
+
 // The two sequential passes of the backward in one launch, side by side: workgroups
 // 0 .. n_chains * NTILE - 1 recompute the states entering every chunk (the float32 forward chunk
 // step, no output), the others run the reverse state pass.  The passes do not depend on each
@@ -283,7 +347,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const float* s0, const T* __restrict__ dout, const float* __restrict__ dsf,
     float* __restrict__ H, float* __restrict__ dH, float* __restrict__ ds0, int T_len, int Hqk, int Hv, int grp,
-    float scale, int n_state_blocks)
+    float scale, int n_state_blocks, const float* __restrict__ Aw)
 {
     constexpr int BV = DV < BW_BV ? DV : BW_BV;
     static_assert(BV == BW_BV || DV < BW_BV, "one column tiling for both passes");
@@ -291,12 +355,13 @@ __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
     extern __shared__ float lds[];
     const int bid = blockIdx.x;
     if (bid < n_state_blocks) {
-        simt_chunk_body<T, DK, DV, BV, false, DH_NT, BW_C, true>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta, s0, nullptr,
-                                                      nullptr, H, T_len, Hqk, Hv, grp, BW_C, scale, nullptr, 0);
+        simt_chunk_body<T, DK, DV, BV, false, DH_NT, BW_C, true, true>(lds, bid / NTILE, bid % NTILE, q, k, v, g, beta,
+                                                                    s0, nullptr, nullptr, H, T_len, Hqk, Hv, grp, BW_C,
+                                                                    scale, nullptr, 0, Aw);
     } else {
         const int x = bid - n_state_blocks;
         bwd_dh_body<T, DK, DV>(lds, x / NTILE, x % NTILE, q, k, g, beta, dout, dsf, dH, ds0, T_len, Hqk, Hv, grp,
-                               scale);
+                               scale, Aw);
     }
 }
 
@@ -843,8 +908,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
     const int NT = (a.T + BW_C - 1) / BW_C;
     float* Hs = a.ws;
     float* dHs = a.ws + (size_t)a.B * a.Hv * NT * DK * DV;
+    float* Aw = dHs + (size_t)a.B * a.Hv * NT * DK * DV;
     const int grp = a.Hv / a.Hqk;
     hipError_t e;
+    // 0. A and M of every chunk
+    auto gram = bwd_gram_kernel<T, DK>;
+    hipLaunchKernelGGL(gram, dim3((unsigned)((long)a.B * a.Hv * NT)), dim3(GR_NT), 0, st,
+                       (const T*)a.q, (const T*)a.k, a.g, a.beta, Aw, a.T, a.Hqk, a.Hv, grp, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     // 1 + 2. the states entering every chunk and the reverse state pass, in one launch
     {
         constexpr int BV = DV < BW_BV ? DV : BW_BV;
@@ -856,7 +928,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
         const int nblk = a.B * a.Hv * (DV / BV);
         hipLaunchKernelGGL(kern, dim3((unsigned)(2 * nblk)), dim3(DH_NT), lb, st, (const T*)a.q, (const T*)a.k,
                            (const T*)a.v, a.g, a.beta, a.s0, (const T*)a.dout, a.dsf, Hs, dHs, a.ds0, a.T, a.Hqk,
-                           a.Hv, grp, a.scale, nblk);
+                           a.Hv, grp, a.scale, nblk, Aw);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -892,7 +964,7 @@ hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st)
 size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv)
 {
     const size_t NT = ((size_t)T + BW_C - 1) / BW_C;
-    return 2 * (size_t)B * Hv * NT * dk * dv * sizeof(float);
+    return 2 * (size_t)B * Hv * NT * ((size_t)dk * dv + BW_C * BW_C) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st)

@@ -61,7 +61,10 @@ __device__ __forceinline__ void mfma_f32_pair(floatx4& d0, floatx4& d1, int k0, 
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 // CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
 // PF: load each chunk's inputs into registers a chunk ahead (see below), else at the chunk's turn.
-template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX, bool PF = false>
+// AIN: A comes formed from Ain ([B Hv][chunks][2][C][C], A first; with PF and without the output)
+// instead of from the chunk's K K^T tiles.
+template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX, bool PF = false,
+          bool AIN = false>
 __device__ __forceinline__ void simt_chunk_body(
     float* lds, int head, int tile,   // head = b * Hv + j; tile = column tile of BV
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -70,8 +73,10 @@ __device__ __forceinline__ void simt_chunk_body(
     T* __restrict__ o,           // may be null (states only)
     float* __restrict__ hst,     // null, or [B, Hv, NT, DK, DV]: the state entering every chunk
     int T_max, int Hqk, int Hv, int grp, int C, float scale,
-    const int* cu, int total)    // packed sequences (cu[0..B] offsets), or null for rows of T_max
+    const int* cu, int total,    // packed sequences (cu[0..B] offsets), or null for rows of T_max
+    const float* __restrict__ Ain = nullptr)
 {
+    static_assert(!AIN || (PF && !OUT), "A from memory rides the prefetch of the states-only pass");
     using L = SimtLds<DK, BV>;
     float* Ks = lds + L::k_off;
     float* Qs = lds + L::q_off;
@@ -115,9 +120,19 @@ __device__ __forceinline__ void simt_chunk_body(
     // thread) measured slower with it than with the loads at each chunk's turn.
     constexpr int KPT = PF ? (CMAX * DK + NTH - 1) / NTH : 1;   // K (and Q) elements per thread
     constexpr int VPT = PF ? (CMAX * BV + NTH - 1) / NTH : 1;   // V elements per thread
+    constexpr int APT = AIN ? (CMAX * CMAX + NTH - 1) / NTH : 1;   // A elements per thread
     T kr[KPT], qr[OUT ? KPT : 1], vr[VPT];
+    float ar[APT];
     float gr = 0.f, br = 0.f;
     auto fetch = [&](int t0) {   // t0 < T_len; rows at or past T_len read row T_len - 1
+        if constexpr (AIN) {
+            const float* ap = Ain + ((size_t)head * ((T_max + C - 1) / C) + t0 / C) * 2 * C * C;
+#pragma unroll
+            for (int p = 0; p < APT; ++p) {
+                const int e = tid + p * NTH;
+                if (e < C * C) ar[p] = ap[e];
+            }
+        }
 #pragma unroll
         for (int p = 0; p < KPT; ++p) {
             const int e = tid + p * NTH, r = e / DK, m = e % DK;
@@ -163,6 +178,13 @@ __device__ __forceinline__ void simt_chunk_body(
             if (tid < C) {
                 gcs[tid] = tid < n ? gr : 0.f;
                 bs[tid] = tid < n ? br : 0.f;
+            }
+            if constexpr (AIN) {
+#pragma unroll
+                for (int p = 0; p < APT; ++p) {
+                    const int e = tid + p * NTH;
+                    if (e < C * C) As[(e / C) * L::CP + e % C] = ar[p];
+                }
             }
             if (t0 + C < T_len) fetch(t0 + C);
         } else {
@@ -210,7 +232,7 @@ __device__ __forceinline__ void simt_chunk_body(
         constexpr int BT = BV / 16;     // column tiles of the value tile
         // A (strictly lower, beta-scaled) and the output mask matrix (lower incl. diagonal):
         // tiles (R, S) with S <= R of K K^T and Q K^T, then the decays exp(gc_r - gc_s)
-        for (int tt = w; tt < CT * (CT + 1) / 2; tt += nw) {
+        if (!AIN) for (int tt = w; tt < CT * (CT + 1) / 2; tt += nw) {
             int R = 0;
             while ((R + 1) * (R + 2) / 2 <= tt) ++R;
             const int S = tt - R * (R + 1) / 2;
