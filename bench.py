@@ -332,7 +332,7 @@ def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
     return {"workload": cfg.name, "tokens_per_s": cfg.B * cfg.T / kern, "kernel_ms": kern * 1e3,
             "alg_flops": flops, "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12,
             "peak_TFLOPs": FP32_VALU_PEAK / 1e12, "frac": flops / kern / FP32_VALU_PEAK,
-            "kernels": "bwd_pass_kernel (state recompute beside the reverse state pass) + bwd_chunk_kernel"}
+            "kernels": "bwd_gram_kernel + bwd_pass_kernel (state recompute beside the reverse state pass) + bwd_chunk_kernel"}
 
 
 def bench_kda(cfg, torch, gdn, steps=10, warmup=2):

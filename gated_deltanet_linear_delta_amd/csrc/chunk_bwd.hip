@@ -103,7 +103,7 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     float ar[APT];
     float gr = 0.f, br = 0.f;
     auto fetch = [&](int t0) {   // 0 <= t0 < T_len
-        const float* ap = Ain + ((size_t)head * NT + t0 / BW_C) * 2 * BW_C * BW_C;
+        const float* ap = Ain + ((size_t)head * NT + t0 / BW_C) * 4 * BW_C * BW_C;
 #pragma unroll
         for (int p = 0; p < APT; ++p) ar[p] = ap[tid + p * DH_NT];
 #pragma unroll
@@ -267,12 +267,13 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     }
 }
 
-// A and M of every (batch, value head, chunk) for the two sequential passes, which then load them
-// a chunk ahead instead of forming them inside their serial chains (both depend on the chunk's q,
-// k, g and beta only).  Aw[(b Hv + j) NT + ci] holds [2][C][C]: A = strictly-lower(diag(beta)
-// (K K^T * Gamma)), then M = lower-incl((scale Q) K^T * Gamma).  One 256-thread workgroup per
-// (batch, value head, chunk); the 16 x 16 tiles on the float32 matrix cores in the same order as
-// the passes would take them.
+// The chunk matrices that depend on the chunk's q, k, g and beta only, for every (batch, value
+// head, chunk), formed here in parallel so that the sequential passes and the gradient kernel
+// load them instead of forming them inside their serial chains.  Aw[(b Hv + j) NT + ci] holds
+// [4][C][C]: A = strictly-lower(diag(beta) G), M = lower-incl((scale Q) K^T * Gamma),
+// G = strictly-lower(K K^T * Gamma), T = (I + A)^{-1}.  One 256-thread workgroup per (batch,
+// value head, chunk); the 16 x 16 tiles on the float32 matrix cores in the same order as the
+// consumers took them before.
 constexpr int GR_NT = 256;
 
 template <typename T, int DK>
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q
 {
     constexpr int KP = DK + 1, CT = BW_C / 16;
     __shared__ float Ks[BW_C * KP], Qs[BW_C * KP], gcs[BW_C], bs[BW_C];
+    __shared__ float Gs[BW_C * BW_CP], Tm[BW_C * BW_CP], Xs[16 * BW_VP];
     const int NT = (T_len + BW_C - 1) / BW_C;
     const int ci = blockIdx.x % NT, head = blockIdx.x / NT;
     const int b = head / Hv, j = head - b * Hv, i = j / grp;
@@ -316,8 +318,10 @@ __global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q
     }
     __syncthreads();
     const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
-    float* Ao = Aw + ((size_t)head * NT + ci) * 2 * BW_C * BW_C;
+    float* Ao = Aw + ((size_t)head * NT + ci) * 4 * BW_C * BW_C;
     float* Mo = Ao + BW_C * BW_C;
+    float* Go = Mo + BW_C * BW_C;
+    float* To = Go + BW_C * BW_C;
     for (int tt = w; tt < CT * CT; tt += GR_NT / 64) {   // tiles (R, S); those above the diagonal are zero
         const int R = tt / CT, S = tt % CT;
         floatx4 ga = {0.f, 0.f, 0.f, 0.f}, gq = {0.f, 0.f, 0.f, 0.f};
@@ -332,8 +336,52 @@ __global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q
             const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
             Ao[r * BW_C + sc] = sc < r ? bs[r] * gam * ga[x] : 0.f;
             Mo[r * BW_C + sc] = gam * gq[x];
+            const float gv = sc < r ? gam * ga[x] : 0.f;
+            Go[r * BW_C + sc] = gv;
+            Gs[r * BW_CP + sc] = gv;
         }
     }
+    __syncthreads();
+    // T = (I + diag(beta) G)^{-1} blockwise over the two 16 x 16 diagonal blocks: each diagonal
+    // block T_DD = (I + A_DD)^{-1} by forward substitution (one thread per column, the column in
+    // registers, G read by broadcast), then T_10 = -T_11 A_10 T_00 on the matrix cores
+    static_assert(BW_C == 32, "two diagonal blocks");
+    if (tid < BW_C) {
+        const int s = tid, D = 16 * (s / 16), sl = s % 16;
+        float y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < r; ++u) acc[u & 3] = fmaf(Gs[(D + r) * BW_CP + D + u], y[u], acc[u & 3]);
+            const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            y[r] = r == sl ? 1.f : (r > sl ? -bs[D + r] * sum : 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            Tm[(D + r) * BW_CP + s] = y[r];
+            if (D) Tm[r * BW_CP + s] = 0.f;   // above the diagonal blocks
+        }
+    }
+    __syncthreads();
+    // X = A_10 T_00 (A = diag(beta) G), then T_10 = -T_11 X: wave 0
+    if (w == 0) {
+        const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                         [&](int ii, int kk) { return bs[16 + ii] * Gs[(16 + ii) * BW_CP + kk]; },
+                                         [&](int kk, int jj) { return Tm[kk * BW_CP + jj]; });
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Xs[(4 * lq + x) * BW_VP + li] = x4[x];
+    }
+    __syncthreads();
+    if (w == 0) {
+        const floatx4 t4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                         [&](int ii, int kk) { return Tm[(16 + ii) * BW_CP + 16 + kk]; },
+                                         [&](int kk, int jj) { return Xs[kk * BW_VP + jj]; });
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Tm[(16 + 4 * lq + x) * BW_CP + li] = -t4[x];
+    }
+    __syncthreads();
+    for (int e = tid; e < BW_C * BW_C; e += GR_NT) To[e] = Tm[(e / BW_C) * BW_CP + e % BW_C];
 }
 
 // The two sequential passes of the backward in one launch, side by side: workgroups
@@ -404,7 +452,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ H,
     const float* __restrict__ dH, T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
-    float* __restrict__ dg, float* __restrict__ dbeta, int T_len, int Hqk, int Hv, int grp, float scale)
+    float* __restrict__ dg, float* __restrict__ dbeta, int T_len, int Hqk, int Hv, int grp, float scale,
+    const float* __restrict__ Aw)
 {
     using L = BwLds<DK>;
     constexpr int KP = L::KP, HP = L::HP;
@@ -481,6 +530,15 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dTs[e] = 0.f;
             dMs[e] = 0.f;
         }
+        {   // G, M and T of this chunk, formed by bwd_gram_kernel ([4][C][C]: A, M, G, T)
+            const float* gp = Aw + (head * NT + ci) * 4 * BW_C * BW_C;
+            for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
+                const int r = e / BW_C, c = e % BW_C;
+                Ms[r * BW_CP + c] = gp[BW_C * BW_C + e];
+                Gs[r * BW_CP + c] = gp[2 * BW_C * BW_C + e];
+                Tm[r * BW_CP + c] = gp[3 * BW_C * BW_C + e];
+            }
+        }
         __syncthreads();
         if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
             float x = tid < BW_C ? gcs[tid] : 0.f;
@@ -497,65 +555,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
         }
         __syncthreads();
-        // G = K K^T * Gamma (strictly lower) and M = Q K^T * Gamma (lower incl): tiles (R, S),
-        // S <= R, on the float32 matrix cores (entries above the diagonal are never read)
         constexpr int CT = BW_C / 16;
-        for (int tt = w; tt < CT * (CT + 1) / 2; tt += BW_NT / 64) {
-            int R = 0;
-            while ((R + 1) * (R + 2) / 2 <= tt) ++R;
-            const int S = tt - R * (R + 1) / 2;
-            const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-            auto bk = [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; };
-            const floatx4 ga = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * R + ii) * KP + kk]; }, bk);
-            const floatx4 gq = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Qs[(16 * R + ii) * KP + kk]; }, bk);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
-                const float gam = sc <= r ? expf(gcs[r] - gcs[sc]) : 0.f;
-                Gs[r * BW_CP + sc] = sc < r ? gam * ga[x] : 0.f;
-                Ms[r * BW_CP + sc] = gam * gq[x];
-            }
-        }
-        __syncthreads();
-        // T = (I + diag(beta) G)^{-1} blockwise over the two 16 x 16 diagonal blocks: each diagonal
-        // block T_DD = (I + A_DD)^{-1} by forward substitution (one thread per column, the column
-        // in registers, G read by broadcast), then T_10 = -T_11 A_10 T_00 on the matrix cores
-        static_assert(BW_C == 32, "two diagonal blocks");
-        if (tid < BW_C) {
-            const int s = tid, D = 16 * (s / 16), sl = s % 16;
-            float y[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int u = 0; u < r; ++u) acc[u & 3] = fmaf(Gs[(D + r) * BW_CP + D + u], y[u], acc[u & 3]);
-                const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                y[r] = r == sl ? 1.f : (r > sl ? -bs[D + r] * sum : 0.f);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                Tm[(D + r) * BW_CP + s] = y[r];
-                if (D) Tm[r * BW_CP + s] = 0.f;   // above the diagonal blocks
-            }
-        }
-        __syncthreads();
-        // X = A_10 T_00 (A = diag(beta) G) into the row-sum scratch, then T_10 = -T_11 X: wave 0
-        if (w == 0) {
-            const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
-                                             [&](int ii, int kk) { return bs[16 + ii] * Gs[(16 + ii) * BW_CP + kk]; },
-                                             [&](int kk, int jj) { return Tm[kk * BW_CP + jj]; });
-#pragma unroll
-            for (int x = 0; x < 4; ++x) P1[(4 * lq + x) * BW_VP + li] = x4[x];
-        }
-        __syncthreads();
-        if (w == 0) {
-            const floatx4 t4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
-                                             [&](int ii, int kk) { return Tm[(16 + ii) * BW_CP + 16 + kk]; },
-                                             [&](int kk, int jj) { return P1[kk * BW_VP + jj]; });
-#pragma unroll
-            for (int x = 0; x < 4; ++x) Tm[(16 + 4 * lq + x) * BW_CP + li] = -t4[x];
-        }
-        __syncthreads();
         // W = T diag(beta e^gc) K: tiles (R, M) (T lower triangular: the sum stops at the tile's rows)
         for (int tt = w; tt < CT * MTL; tt += BW_NT / 64) {
             const int R = tt / MTL, M = tt % MTL;
@@ -941,7 +941,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hqk * NT)), dim3(BW_NT), L::bytes, st,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, (const T*)a.dout, Hs, dHs,
-                           (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dg, a.dbeta, a.T, a.Hqk, a.Hv, grp, a.scale);
+                           (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dg, a.dbeta, a.T, a.Hqk, a.Hv, grp, a.scale, Aw);
         e = hipGetLastError();
     }
     return e;
@@ -964,7 +964,7 @@ hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st)
 size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv)
 {
     const size_t NT = ((size_t)T + BW_C - 1) / BW_C;
-    return 2 * (size_t)B * Hv * NT * ((size_t)dk * dv + BW_C * BW_C) * sizeof(float);
+    return 2 * (size_t)B * Hv * NT * ((size_t)dk * dv + 2 * BW_C * BW_C) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st)

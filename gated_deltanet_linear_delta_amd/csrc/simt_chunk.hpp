@@ -61,7 +61,7 @@ __device__ __forceinline__ void mfma_f32_pair(floatx4& d0, floatx4& d1, int k0, 
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 // CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
 // PF: load each chunk's inputs into registers a chunk ahead (see below), else at the chunk's turn.
-// AIN: A comes formed from Ain ([B Hv][chunks][2][C][C], A first; with PF and without the output)
+// AIN: A comes formed from Ain ([B Hv][chunks][4][C][C], A first; with PF and without the output)
 // instead of from the chunk's K K^T tiles.
 template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX, bool PF = false,
           bool AIN = false>
@@ -126,7 +126,7 @@ __device__ __forceinline__ void simt_chunk_body(
     float gr = 0.f, br = 0.f;
     auto fetch = [&](int t0) {   // t0 < T_len; rows at or past T_len read row T_len - 1
         if constexpr (AIN) {
-            const float* ap = Ain + ((size_t)head * ((T_max + C - 1) / C) + t0 / C) * 2 * C * C;
+            const float* ap = Ain + ((size_t)head * ((T_max + C - 1) / C) + t0 / C) * 4 * C * C;
 #pragma unroll
             for (int p = 0; p < APT; ++p) {
                 const int e = tid + p * NTH;
