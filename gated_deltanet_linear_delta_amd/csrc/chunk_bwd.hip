@@ -530,6 +530,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dTs[e] = 0.f;
             dMs[e] = 0.f;
         }
+        static_assert(NWV * BW_C <= BW_C * BW_VP, "per-wave row partials fit the scratch");
+        for (int e = tid; e < NWV * BW_C; e += BW_NT) P2[e] = 0.f;
         {   // G, M and T of this chunk, formed by bwd_gram_kernel ([4][C][C]: A, M, G, T)
             const float* gp = Aw + (head * NT + ci) * 4 * BW_C * BW_C;
             for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
@@ -565,9 +567,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 #pragma unroll
             for (int x = 0; x < 4; ++x) Ws[(16 * R + 4 * lq + x) * KP + 16 * M + li] = acc[x];
         }
-        float aW[PE], aX[PE];
+        float aW[PE], aX[PE], aS[PE];   // aS: dO h^T of this head over the tiles (for dgc)
 #pragma unroll
-        for (int p = 0; p < PE; ++p) aW[p] = aX[p] = 0.f;
+        for (int p = 0; p < PE; ++p) aW[p] = aX[p] = aS[p] = 0.f;
         float dgl = 0.f;
 
         // Each column tile's h, dh', V and dO are loaded into registers while the tile before it
@@ -657,21 +659,18 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 dgl = fmaf(dhs[m * HP + c], hs[m * HP + c], dgl);
             }
             __syncthreads();
-            // dV = diag(beta) T^T dDelta (complete for this tile); row-sum terms of dbeta and dgc
+            // dV = diag(beta) T^T dDelta (complete for this tile); the row-sum term of dbeta
             const int tr = w / VT, tc = w % VT;
             if (w < DT) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
                 const floatx4 tdu = mfma_f32_tile(z, 16 * tr, BW_C,
                                                   [&](int ii, int kk) { return Tm[kk * BW_CP + 16 * tr + ii]; },
                                                   [&](int kk, int jj) { return dDs[kk * BW_VP + 16 * tc + jj]; });
-                const floatx4 qh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Qs[(16 * tr + ii) * KP + kk]; },
-                                                 [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
                     if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu[x]);
                     P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu[x];
-                    P2[r * BW_VP + c] = dOs[r * BW_VP + c] * qh[x];
                 }
             }
             // dT += dDelta (diag(beta) V)^T over all (R, S) tiles, dM += dO Delta^T over the tiles
@@ -719,24 +718,32 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                     aW[p] -= sw[x];
                     aX[p] += sx[x];
                     aQ[p] = fmaf(egs[r0 + 4 * lq + x], sq[x], aQ[p]);
+                    aS[p] += sq[x];
                 }
             }
             __syncthreads();
             if (tid < BW_C) {
-                float s1 = 0.f, s2 = 0.f;
+                float s1 = 0.f;
 #pragma unroll 4
-                for (int c = 0; c < BW_BV; ++c) {
-                    s1 += P1[tid * BW_VP + c];
-                    s2 += P2[tid * BW_VP + c];
-                }
+                for (int c = 0; c < BW_BV; ++c) s1 += P1[tid * BW_VP + c];
                 dbts[tid] += s1;
-                dgcs[tid] = fmaf(egs[tid], s2, dgcs[tid]);
             }
         }
 
         // ---- the terms that need every column: dW, X, dM, dT are complete now
         dgl = xor_sum(dgl, 1);
         if ((tid & 63) == 0) red[tid >> 6] = dgl;
+        // the dgc term sum_m (scale Q)_rm (dO h^T)_rm of this head: each lane over its accumulator
+        // entries, summed across the 16 lanes of a row, one partial per (wave, row) (a wave's
+        // tiles cover distinct rows)
+#pragma unroll
+        for (int p = 0; p < PE; ++p) {
+            const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
+            float v = tile_ok(p / 4) ? Qs[r * KP + m] * aS[p] : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) v += __shfl_xor(v, sh, 64);
+            if (li == 0 && tile_ok(p / 4)) P2[w * BW_C + r] = v;
+        }
         __syncthreads();
         float* dWs = hs;    // [C][KP]
         float* Xs = dhs;    // [C][KP]
@@ -765,7 +772,10 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 #pragma unroll 4
             for (int m = 0; m < DK; ++m) kx = fmaf(Ks[r * KP + m], Xs[r * KP + m], kx);
             const float ted = eds[r] * kx;
-            dgcs[r] -= ted;
+            float s2 = 0.f;
+#pragma unroll
+            for (int x = 0; x < NWV; ++x) s2 += P2[x * BW_C + r];
+            dgcs[r] = fmaf(egs[r], s2, dgcs[r]) - ted;
             P1[r] = ted;
             // M = lower-incl(Q K^T * Gamma): dgc_r += sum_s dM_rs M_rs - sum_u dM_ur M_ur
             float rs = 0.f, cs = 0.f;
