@@ -41,6 +41,8 @@ constexpr int BW_C = 32;     // chunk length of the backward pass
 constexpr int BW_BV = 32;    // value columns per tile
 constexpr int BW_CP = BW_C + 1;
 constexpr int BW_VP = BW_BV + 1;
+// per (batch, value head, chunk) in the workspace: A, M, G, T [4][C][C], then e^gc and e^(gL - gc)
+constexpr int BW_AWS = 4 * BW_C * BW_C + 2 * BW_C;
 
 // ------------------------------------------------------------------- reverse state pass
 
@@ -79,7 +81,6 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     float* As = lds + L::a;
     float* Ms = lds + L::m;
     float* Ys = lds + L::y;
-    float* gcs = lds + L::gc;
     float* egs = lds + L::eg;
     float* eds = lds + L::ed;
     float* bs = lds + L::bt;
@@ -101,9 +102,9 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
     static_assert(APT * DH_NT == 2 * BW_C * BW_C, "A and M spread evenly");
     T kr[KPT], qr[KPT], dr[VPT];
     float ar[APT];
-    float gr = 0.f, br = 0.f;
+    float er = 0.f, br = 0.f;
     auto fetch = [&](int t0) {   // 0 <= t0 < T_len
-        const float* ap = Ain + ((size_t)head * NT + t0 / BW_C) * 4 * BW_C * BW_C;
+        const float* ap = Ain + ((size_t)head * NT + t0 / BW_C) * BW_AWS;
 #pragma unroll
         for (int p = 0; p < APT; ++p) ar[p] = ap[tid + p * DH_NT];
 #pragma unroll
@@ -118,11 +119,8 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             const int e = tid + p * DH_NT, r = e / BW_BV, c = e % BW_BV;
             dr[p] = dout[(((size_t)b * T_len + min(t0 + r, T_len - 1)) * Hv + j) * DV + c0 + c];
         }
-        if (tid < BW_C) {
-            const size_t off = ((size_t)b * T_len + min(t0 + tid, T_len - 1)) * Hv + j;
-            gr = g[off];
-            br = beta[off];
-        }
+        if (tid < BW_C) br = beta[((size_t)b * T_len + min(t0 + tid, T_len - 1)) * Hv + j];
+        if (tid < 2 * BW_C) er = ap[4 * BW_C * BW_C + tid];   // e^gc, then e^(gL - gc)
     };
     if (NT > 0) fetch((NT - 1) * BW_C);
     for (int ci = NT - 1; ci >= 0; --ci) {
@@ -144,31 +142,14 @@ __device__ __forceinline__ void bwd_dh_body(float* lds, int head, int tile, cons
             const int e = tid + p * DH_NT, r = e / BW_BV, c = e % BW_BV;
             if (e < BW_C * BW_BV) dOs[r * BW_VP + c] = r < n ? to_f32(dr[p]) : 0.f;
         }
-        if (tid < BW_C) {
-            gcs[tid] = tid < n ? gr : 0.f;
-            bs[tid] = tid < n ? br : 0.f;
-        }
+        if (tid < BW_C) bs[tid] = tid < n ? br : 0.f;
+        if (tid < 2 * BW_C) (tid < BW_C ? egs : eds)[tid % BW_C] = er;
 #pragma unroll
         for (int p = 0; p < APT; ++p) {   // A, then M: [2][C][C]
             const int e = tid + p * DH_NT, mat = e / (BW_C * BW_C), rc = e % (BW_C * BW_C);
             (mat ? Ms : As)[(rc / BW_C) * BW_CP + rc % BW_C] = ar[p];
         }
         if (ci > 0) fetch(t0 - BW_C);
-        __syncthreads();
-        if (tid < 64) {   // per-chunk log-decay cumsum: a scan across wave 0
-            float x = tid < BW_C ? gcs[tid] : 0.f;
-#pragma unroll
-            for (int sh = 1; sh < 64; sh <<= 1) {
-                const float y = __shfl_up(x, sh, 64);
-                if (tid >= sh) x += y;
-            }
-            const float last = __shfl(x, BW_C - 1, 64);
-            if (tid < BW_C) {
-                gcs[tid] = x;
-                egs[tid] = expf(x);
-                eds[tid] = expf(last - x);
-            }
-        }
         __syncthreads();
         // The dense products on the float32 matrix cores (mfma_f32_tile), one 16 x 16 output tile
         // per wave at a time.
@@ -314,11 +295,17 @@ __global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q
             const float y = __shfl_up(x, sh, 64);
             if (tid >= sh) x += y;
         }
-        if (tid < BW_C) gcs[tid] = x;
+        const float last = __shfl(x, BW_C - 1, 64);
+        if (tid < BW_C) {
+            gcs[tid] = x;
+            float* Eo = Aw + ((size_t)head * NT + ci) * BW_AWS + 4 * BW_C * BW_C;
+            Eo[tid] = expf(x);
+            Eo[BW_C + tid] = expf(last - x);
+        }
     }
     __syncthreads();
     const int w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;
-    float* Ao = Aw + ((size_t)head * NT + ci) * 4 * BW_C * BW_C;
+    float* Ao = Aw + ((size_t)head * NT + ci) * BW_AWS;
     float* Mo = Ao + BW_C * BW_C;
     float* Go = Mo + BW_C * BW_C;
     float* To = Go + BW_C * BW_C;
@@ -533,7 +520,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         static_assert(NWV * BW_C <= BW_C * BW_VP, "per-wave row partials fit the scratch");
         for (int e = tid; e < NWV * BW_C; e += BW_NT) P2[e] = 0.f;
         {   // G, M and T of this chunk, formed by bwd_gram_kernel ([4][C][C]: A, M, G, T)
-            const float* gp = Aw + (head * NT + ci) * 4 * BW_C * BW_C;
+            const float* gp = Aw + (head * NT + ci) * BW_AWS;
             for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
                 const int r = e / BW_C, c = e % BW_C;
                 Ms[r * BW_CP + c] = gp[BW_C * BW_C + e];
@@ -974,7 +961,7 @@ hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st)
 size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv)
 {
     const size_t NT = ((size_t)T + BW_C - 1) / BW_C;
-    return 2 * (size_t)B * Hv * NT * ((size_t)dk * dv + 2 * BW_C * BW_C) * sizeof(float);
+    return (2 * (size_t)B * Hv * NT * dk * dv + (size_t)B * Hv * NT * BW_AWS) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st)

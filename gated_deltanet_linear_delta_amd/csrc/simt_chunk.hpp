@@ -61,8 +61,9 @@ __device__ __forceinline__ void mfma_f32_pair(floatx4& d0, floatx4& d1, int k0, 
 // OUT false: the states only (o is null): the output-only products Q K^T and Q h0 are skipped.
 // CMAX: the longest chunk the caller passes (C <= CMAX <= SIMT_CMAX).
 // PF: load each chunk's inputs into registers a chunk ahead (see below), else at the chunk's turn.
-// AIN: A comes formed from Ain ([B Hv][chunks][4][C][C], A first; with PF and without the output)
-// instead of from the chunk's K K^T tiles.
+// AIN: A and the decay exponentials come formed from Ain (per (batch, value head, chunk): A, three
+// more [C][C] matrices, e^gc, e^(gL - gc); with PF and without the output) instead of from the
+// chunk's K K^T tiles and log-decay cumsum.
 template <typename T, int DK, int DV, int BV, bool OUT, int NTH, int CMAX = SIMT_CMAX, bool PF = false,
           bool AIN = false>
 __device__ __forceinline__ void simt_chunk_body(
@@ -115,23 +116,24 @@ __device__ __forceinline__ void simt_chunk_body(
     // With PF, each chunk's inputs are loaded into registers a chunk ahead: the loads of the next
     // chunk are in flight while this one computes, and land in LDS at the top of its turn.  The
     // loads are unconditional, with the row clamped into the sequence (rows past its end are
-    // zeroed when they are written to LDS).  The 1,024-thread states-only pass of the backward
-    // gains from it; the 512-thread output kernel at 64-token chunks (16 K and 16 Q registers per
-    // thread) measured slower with it than with the loads at each chunk's turn.
+    // zeroed when they are written to LDS).  The states-only pass of the backward (32-token
+    // chunks) gains from it; the output kernel at 64-token chunks (16 K and 16 Q registers per
+    // thread at 512 threads) measured slower with it than with the loads at each chunk's turn.
     constexpr int KPT = PF ? (CMAX * DK + NTH - 1) / NTH : 1;   // K (and Q) elements per thread
     constexpr int VPT = PF ? (CMAX * BV + NTH - 1) / NTH : 1;   // V elements per thread
     constexpr int APT = AIN ? (CMAX * CMAX + NTH - 1) / NTH : 1;   // A elements per thread
     T kr[KPT], qr[OUT ? KPT : 1], vr[VPT];
     float ar[APT];
-    float gr = 0.f, br = 0.f;
+    float gr = 0.f, br = 0.f, er = 0.f;
     auto fetch = [&](int t0) {   // t0 < T_len; rows at or past T_len read row T_len - 1
         if constexpr (AIN) {
-            const float* ap = Ain + ((size_t)head * ((T_max + C - 1) / C) + t0 / C) * 4 * C * C;
+            const float* ap = Ain + ((size_t)head * ((T_max + C - 1) / C) + t0 / C) * (4 * C * C + 2 * C);
 #pragma unroll
             for (int p = 0; p < APT; ++p) {
                 const int e = tid + p * NTH;
                 if (e < C * C) ar[p] = ap[e];
             }
+            if (tid < 2 * C) er = ap[4 * C * C + tid];   // e^gc, then e^(gL - gc)
         }
 #pragma unroll
         for (int p = 0; p < KPT; ++p) {
@@ -185,6 +187,7 @@ __device__ __forceinline__ void simt_chunk_body(
                     const int e = tid + p * NTH;
                     if (e < C * C) As[(e / C) * L::CP + e % C] = ar[p];
                 }
+                if (tid < 2 * C) (tid < C ? egs : eds)[tid % C] = er;
             }
             if (t0 + C < T_len) fetch(t0 + C);
         } else {
@@ -210,21 +213,23 @@ __device__ __forceinline__ void simt_chunk_body(
             }
         }
         __syncthreads();
-        if (tid < 64) {  // per-chunk log-decay cumsum (C <= 64 terms): a scan across wave 0
-            float x = tid < C ? gcs[tid] : 0.f;
+        if constexpr (!AIN) {
+            if (tid < 64) {  // per-chunk log-decay cumsum (C <= 64 terms): a scan across wave 0
+                float x = tid < C ? gcs[tid] : 0.f;
 #pragma unroll
-            for (int sh = 1; sh < 64; sh <<= 1) {
-                const float y = __shfl_up(x, sh, 64);
-                if (tid >= sh) x += y;
+                for (int sh = 1; sh < 64; sh <<= 1) {
+                    const float y = __shfl_up(x, sh, 64);
+                    if (tid >= sh) x += y;
+                }
+                const float last = __shfl(x, C - 1, 64);
+                if (tid < C) {
+                    gcs[tid] = x;
+                    egs[tid] = expf(x);
+                    eds[tid] = expf(last - x);
+                }
             }
-            const float last = __shfl(x, C - 1, 64);
-            if (tid < C) {
-                gcs[tid] = x;
-                egs[tid] = expf(x);
-                eds[tid] = expf(last - x);
-            }
+            __syncthreads();
         }
-        __syncthreads();
         // The dense products run on the float32 matrix cores (mfma_f32_tile: float32 products,
         // so float32 inputs keep float32 accuracy), one 16 x 16 output tile per wave at a time.
         const int nw = NTH / 64, w = tid >> 6, lane = tid & 63, li = lane & 15, lq = lane >> 4;

@@ -227,10 +227,11 @@ gdn_status_t gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, co
 
 /*
  * gdn_chunk_bwd_workspace_bytes -- device scratch (bytes) that gdn_chunk_bwd needs: the state
- * entering every 32-token chunk, the gradient of the state leaving it, and four 32 x 32 matrices
- * per chunk (K K^T and Q K^T with the decays and gates, and the inverse of the unit triangular
- * system), float32: 2 * B * Hv * ceil(T / 32) * (dk * dv + 2 * 32 * 32) * 4 bytes.  Pure host
- * function; 0 for invalid sizes.
+ * entering every 32-token chunk and the gradient of the state leaving it (2 * dk * dv floats per
+ * chunk and value head), and per chunk and value head four 32 x 32 matrices (K K^T and Q K^T with
+ * the decays and gates, and the inverse of the unit triangular system) and the chunk's 2 * 32
+ * decay exponentials, float32: B * Hv * ceil(T / 32) * (2 * dk * dv + 4 * 32 * 32 + 2 * 32) * 4
+ * bytes.  Pure host function; 0 for invalid sizes.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, gdn_dtype_t dtype);
 

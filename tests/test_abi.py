@@ -296,7 +296,7 @@ def test_chunk_fwd_gated_valid_calls_report_no_device():
 
 # ------------------------------------------------------------------------------ backward
 
-BWD_WS = 2 * 2 * 4 * 4 * (64 * 32 + 2 * 32 * 32) * 4     # 2 x B * Hv * ceil(100 / 32) * (dk * dv + 2 * 32 * 32) * 4
+BWD_WS = 2 * 4 * 4 * (2 * 64 * 32 + 4 * 32 * 32 + 2 * 32) * 4     # B * Hv * ceil(100 / 32) * (2 dk dv + 4 * 32 * 32 + 2 * 32) * 4
 
 
 def bwd_call(**over):
@@ -312,7 +312,7 @@ def bwd_call(**over):
 
 def test_bwd_workspace_size():
     assert gdn.gdn_chunk_bwd_workspace_bytes(2, 100, 2, 4, 64, 32, gdn.GDN_BF16) == BWD_WS
-    assert gdn.gdn_chunk_bwd_workspace_bytes(1, 4096, 16, 32, 128, 128, gdn.GDN_BF16) == 2 * 32 * 128 * (128 * 128 + 2 * 32 * 32) * 4
+    assert gdn.gdn_chunk_bwd_workspace_bytes(1, 4096, 16, 32, 128, 128, gdn.GDN_BF16) == 32 * 128 * (2 * 128 * 128 + 4 * 32 * 32 + 2 * 32) * 4
     assert gdn.gdn_chunk_bwd_workspace_bytes(1, 0, 16, 32, 128, 128, gdn.GDN_BF16) == 0
     assert gdn.gdn_chunk_bwd_workspace_bytes(1, 64, 16, 33, 128, 128, gdn.GDN_BF16) == 0
 
