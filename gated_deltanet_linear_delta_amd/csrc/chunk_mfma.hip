@@ -57,6 +57,7 @@
 #include "device_common.hpp"
 #include "gated_norm.hpp"
 #include "launch.hpp"
+#include "simt_chunk.hpp"
 
 namespace gdn {
 
@@ -2025,6 +2026,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
     float* As = Gs + CH * KP;
     float* Aqs = As + CH * AP;
     float* bs = Aqs + CH * AP;
+    float* Ts = bs + CH;   // T = (I + A)^{-1} in float32 [CH][AP]
 
     const int c = blockIdx.x % NT;
     const int head = blockIdx.x / NT;   // b * Hv + j
@@ -2138,54 +2140,71 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
     }
     __syncthreads();
     unsigned char* wb = ws + ((size_t)head * NT + c) * W::bytes;
-    // T = (I + A)^{-1}, column s by forward substitution, one thread per column, the column in
-    // registers (fully unrolled: no LDS round trip between rows; A's row is a broadcast read),
-    // written straight to the workspace as float16.
-    if (tid < CH) {
-        const int s = tid;
-        op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
-        float t[CH + 4];
+    // The chunk's operands for the state pass, which do not depend on T: written by waves 1.. while
+    // wave 0 runs the first block of the solve below.
+    auto write_operands = [&](int t, int nt) {
+        op_t* kh = reinterpret_cast<op_t*>(wb + W::kh);
+        op_t* kt = reinterpret_cast<op_t*>(wb + W::kt);
+        op_t* qh = reinterpret_cast<op_t*>(wb + W::qh);
+        for (int e = t; e < CH * DK; e += nt) {
+            const int r = e / DK, m = e % DK;
+            const float gr = Gs[r * KP + m], gl = Gs[(CH - 1) * KP + m];
+            kh[e] = (op_t)(__expf(gr) * Ks[r * KP + m]);
+            kt[e] = (op_t)(__expf(gl - gr) * Ks[r * KP + m]);
+            qh[e] = (op_t)(__expf(gr) * Qs[r * KP + m]);
+        }
+        op_t* aw = reinterpret_cast<op_t*>(wb + W::aq);
+        for (int e = t; e < CH * CH; e += nt) aw[e] = (op_t)Aqs[(e / CH) * AP + e % CH];
+        float* bw = reinterpret_cast<float*>(wb + W::bt);
+        float* ew = reinterpret_cast<float*>(wb + W::el);
+        if (t < CH) bw[t] = bs[t];
+        for (int m = t; m < DK; m += nt) ew[m] = __expf(Gs[(CH - 1) * KP + m]);
+    };
+    // T = (I + A)^{-1} blockwise over four 16-row blocks D: the identity's columns by forward
+    // substitution inside block D (one thread per column, 16 rows in registers, A read by
+    // broadcast, four partial sums), then the rows below take R -= A[rows, D..] T[D..] as float32
+    // matrix-core tiles.  Each thread's dependent chain is 16 rows instead of 64.
+    for (int e = tid; e < CH * CH; e += KQ_NT) Ts[(e / CH) * AP + e % CH] = e / CH == e % CH ? 1.f : 0.f;
+    __syncthreads();
+    for (int D = 0; D < CH; D += 16) {
+        if (tid < CH) {
+            float y[16];
 #pragma unroll
-        for (int u = 0; u < CH + 4; ++u) t[u] = 0.f;
+            for (int r = 0; r < 16; ++r) y[r] = Ts[(D + r) * AP + tid];
 #pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            // A's row r four entries at a time (entries at and past the diagonal are zero, and so
-            // are the t not computed yet)
-            // four partial sums, so the dependent chain is a quarter as long
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int r = 1; r < 16; ++r) {
+                float acc[4] = {y[r], 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < r; u += 4) {
-                const floatx4 a4 = *reinterpret_cast<const floatx4*>(As + r * AP + u);
-#pragma unroll
-                for (int y = 0; y < 4; ++y) acc[y] = fmaf(a4[y], t[u + y], acc[y]);
+                for (int u = 0; u < r; ++u) acc[u & 3] = fmaf(-As[(D + r) * AP + D + u], y[u], acc[u & 3]);
+                y[r] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
-            const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            t[r] = r == s ? 1.f : (r > s ? -sum : 0.f);
-            tw[r * CH + s] = (op_t)t[r];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ts[(D + r) * AP + tid] = y[r];
+        } else if (D == 0) {
+            write_operands(tid - CH, KQ_NT - CH);
+        }
+        __syncthreads();
+        if (D + 16 < CH) {
+            const int RT0 = D / 16 + 1;   // first row tile below the block
+            for (int tt = w; tt < (CH / 16 - RT0) * (CH / 16); tt += KQ_NT / 64) {
+                const int R = RT0 + tt / (CH / 16), T2 = tt % (CH / 16);
+                const floatx4 u4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16,
+                                                 [&](int ii, int kk) { return As[(16 * R + ii) * AP + D + kk]; },
+                                                 [&](int kk, int jj) { return Ts[(D + kk) * AP + 16 * T2 + jj]; });
+#pragma unroll
+                for (int x = 0; x < 4; ++x) Ts[(16 * R + 4 * lg + x) * AP + 16 * T2 + ln] -= u4[x];
+            }
+            __syncthreads();
         }
     }
-    op_t* kh = reinterpret_cast<op_t*>(wb + W::kh);
-    op_t* kt = reinterpret_cast<op_t*>(wb + W::kt);
-    op_t* qh = reinterpret_cast<op_t*>(wb + W::qh);
-    for (int e = tid; e < CH * DK; e += KQ_NT) {
-        const int r = e / DK, m = e % DK;
-        const float gr = Gs[r * KP + m], gl = Gs[(CH - 1) * KP + m];
-        kh[e] = (op_t)(__expf(gr) * Ks[r * KP + m]);
-        kt[e] = (op_t)(__expf(gl - gr) * Ks[r * KP + m]);
-        qh[e] = (op_t)(__expf(gr) * Qs[r * KP + m]);
-    }
-    op_t* aw = reinterpret_cast<op_t*>(wb + W::aq);
-    for (int e = tid; e < CH * CH; e += KQ_NT) aw[e] = (op_t)Aqs[(e / CH) * AP + e % CH];
-    float* bw = reinterpret_cast<float*>(wb + W::bt);
-    float* ew = reinterpret_cast<float*>(wb + W::el);
-    if (tid < CH) bw[tid] = bs[tid];
-    for (int m = tid; m < DK; m += KQ_NT) ew[m] = __expf(Gs[(CH - 1) * KP + m]);
+    op_t* tw = reinterpret_cast<op_t*>(wb + W::tm);
+    for (int e = tid; e < CH * CH; e += KQ_NT) tw[e] = (op_t)Ts[(e / CH) * AP + e % CH];
 }
 
 template <int DK>
 constexpr size_t kda_prep_lds_bytes()
 {
-    return ((size_t)3 * CH * (DK + 1) + (size_t)2 * CH * (CH + 4) + CH) * sizeof(float);
+    return ((size_t)3 * CH * (DK + 1) + (size_t)3 * CH * (CH + 4) + CH) * sizeof(float);
 }
 
 // LDS of the state kernel: two slots, each Kh, Kt, Qh [64][DK+8] f16 (column-permuted), T, Aq
