@@ -15,7 +15,8 @@ The same JSON line carries
   decode        -- the 64-step fused decode workload (B=256, Hv=32, d=128, fp32 state 512 MiB):
                    steps/s and achieved HBM bandwidth;
   prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3.6-27B-shaped (T=65536, Hv=48)
-                   prefill workloads, tokens/s and roofline fractions;
+                   prefill workloads, tokens/s and roofline fractions, and the headline shape
+                   with float32 inputs (the float32 chunk kernel);
   layer_ops     -- the layer steps either side of the recurrence at the headline shape (short
                    conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth;
   gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
@@ -34,6 +35,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-b
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -508,6 +510,14 @@ def main():
             rr = bench_prefill(c, 5, 2, torch, gdn, gi)
             pc[name] = {"tokens_per_s": c.B * c.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
                         "mfma_frac": rr["flops"] / rr["kern"] / MFMA_BF16_PEAK,
+                        "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
+        # the same qwen3next shape with float32 q, k, v, o: the float32 chunk kernel (float32
+        # matrix-core products), bound by its per-chunk chain; fraction of the float32 peak
+        c32 = dataclasses.replace(cfg, name=cfg.name + "_f32", dtype="f32")
+        print(f"bench: prefill {c32}", file=sys.stderr, flush=True)
+        rr = bench_prefill(c32, 5, 2, torch, gdn, gi)
+        pc[c32.name] = {"tokens_per_s": c32.B * c32.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
+                        "fp32_frac": rr["flops"] / rr["kern"] / FP32_VALU_PEAK,
                         "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
         line["prefill_configs"] = pc
         print("bench: layer steps (prologue, gated RMSNorm)", file=sys.stderr, flush=True)
