@@ -1,36 +1,39 @@
 """Benchmark of the gated delta rule on one MI355X.
 
-A step is one gdn_chunk_fwd (chunkwise prefill) over one batch of the Qwen3-Next-shaped GDN
-workload: B=1, T=4096, 16 query/key heads, 32 value heads, head dim 128, chunk 64, bf16 inputs,
-float32 state.  `value` is prefill tokens/s with the inputs resident in HBM; rotating input sets
-(larger than the 256 MB Infinity Cache) keep every step's reads cold.
+A step is one gdn_chunk_fwd (chunkwise prefill) over one batch of the Qwen3.6-27B-shaped GDN
+workload, the largest single-GPU configuration: B=1, T=65536, 16 query/key heads, 48 value heads,
+head dim 128, chunk 64, bf16 inputs, float32 state.  `value` is prefill tokens/s with the inputs
+resident in HBM (one input set of 2.2 GB, larger than the 256 MB Infinity Cache).
 
 The same JSON line carries
   roofline      -- the prefill call's achieved algorithmic bytes/s against 8 TB/s (its binding
-                   roofline: 167 flop/B is below the bf16-MFMA/HBM ridge), the call's average
-                   duration from HIP events on its own stream (for the split path: the per-chunk
-                   prep kernel and the state-pass kernel together), its bf16-MFMA fraction, and
-                   the HBM traffic measured with rocprofv3 counters when a matching record exists;
-  cpu_baseline  -- the float64 oracle timed on the host cores on the same workload;
+                   roofline: 188 flop/B is below the bf16-MFMA/HBM ridge of 315), the call's
+                   average duration from HIP events on its own stream (every kernel the call
+                   launches), its bf16-MFMA fraction (algorithmic flops / time / 2.5166 PFLOP/s),
+                   and the HBM traffic measured with rocprofv3 counters when a record taken on the
+                   current kernel sources exists;
+  cpu_baseline  -- the float64 oracle timed on the host cores on the same 48-chain batch;
   decode        -- the 64-step fused decode workload (B=256, Hv=32, d=128, fp32 state 512 MiB):
-                   steps/s and achieved HBM bandwidth;
-  prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3.6-27B-shaped (T=65536, Hv=48)
-                   prefill workloads, tokens/s and roofline fractions, and the headline shape
-                   with float32 inputs (the float32 chunk kernel);
-  layer_ops     -- the layer steps either side of the recurrence at the headline shape (short
+                   steps/s and its own HBM roofline object;
+  prefill_configs -- the batched (B=8, T=8192, S0 != 0) and Qwen3-Next-shaped (B=1, T=4096)
+                   prefill workloads, each with its own roofline object, and the Qwen3-Next shape
+                   with float32 inputs (the float32 kernel, against the float32 peak);
+  layer_ops     -- the layer steps either side of the recurrence at the Qwen3-Next shape (short
                    conv + SiLU + q/k L2 norm; gated RMSNorm): time and achieved HBM bandwidth;
   gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
-                   call) on the headline and the batched workloads;
-  backward      -- gdn_chunk_bwd (gradients of q, k, v, g, beta, S0) at the headline shape:
-                   tokens/s and the fraction of the float32 vector peak it reaches;
+                   call) on the Qwen3-Next and the batched workloads;
+  backward      -- gdn_chunk_bwd (gradients of q, k, v, g, beta, S0) at the Qwen3-Next shape:
+                   tokens/s and its fraction of the float32 peak, for the method's own work and
+                   for the work as computed (which recomputes the states);
   kda           -- gdn_kda_chunk_fwd (Kimi Delta Attention, per-key-channel decay) on the KDA
-                   workload (B1 T4096, 32/32 heads, d128): tokens/s and float32-vector fraction;
+                   workload (B1 T4096, 32/32 heads, d128, chunk 64 on the float16 matrix cores):
+                   tokens/s and its fraction of the 16-bit matrix-core peak;
   varlen        -- gdn_chunk_fwd_varlen on 64 packed sequences of 64..2048 tokens;
   scan          -- gdn_chunk_fwd_scan (the affine chunk scan) against gdn_chunk_fwd on the 64K-token
                    workload and on one GPU's share of it under an 8-way head split.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
-                       [--leg layer_ops|backward|kda|varlen|scan]
+                       [--leg layer_ops|backward|kda|varlen|scan|decode]
 """
 from __future__ import annotations
 
@@ -72,12 +75,15 @@ def prefill_alg_flops(B, T, Hqk, Hv, dk, dv, C):
 FP32_VALU_PEAK = 157.3e12   # flop/s, MI355X float32 vector units
 
 
-def backward_alg_flops(B, T, Hqk, Hv, dk, dv, C=32):
-    """Flops of the chunkwise backward as computed (chunks of C = 32; the states are recomputed,
-    not kept from the forward), per token and value head: the state recompute
-    4 dk dv + C (dk + dv); the reverse state pass 6 dk dv + 2 C (dk + dv); the per-chunk
-    gradients 12 dk dv + 6 C dv + 9 C dk + 7 C^2 / 3 (T, and dT's two triangular products)."""
-    per = 22 * dk * dv + 9 * C * dv + 12 * C * dk + 7 * C * C / 3
+def backward_alg_flops(B, T, Hqk, Hv, dk, dv, C=32, recompute=True):
+    """Flops of the chunkwise backward (chunks of C = 32), per token and value head: the reverse
+    state pass 6 dk dv + 2 C (dk + dv); the per-chunk gradients 12 dk dv + 6 C dv + 9 C dk
+    + 7 C^2 / 3 (T, and dT's two triangular products).  With `recompute`, also the forward state
+    recompute the kernels run because the states are not kept from the forward,
+    4 dk dv + C (dk + dv); without it, the method's own work."""
+    per = 18 * dk * dv + 8 * C * dv + 11 * C * dk + 7 * C * C / 3
+    if recompute:
+        per += 4 * dk * dv + C * (dk + dv)
     return per * B * T * Hv
 
 
@@ -100,7 +106,7 @@ def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
 # (HIP events around it on its stream), i.e. over both kernels of the split path.
 KERNELS = {"mfma": "chunk_mfma_kernel",
            "mfma_split": "chunk_prep_kernel + chunk_state_kernel",
-           "simt": "chunk_simt_kernel"}
+           "mfma_f32": "chunk_simt_kernel (float32 matrix-core products)"}
 
 
 def kernel_source_hash() -> str:
@@ -112,10 +118,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the prefill kernel from the committed rocprofv3 counter record,
-    if it was taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_chunk_fwd_{workload}.md")
+def prefill_roofline(r, traffic):
+    """The roofline object of one prefill workload: its binding roofline is HBM (the chunkwise
+    method's intensity, 167-188 flop/B, is below the bf16-MFMA/HBM ridge); `achieved` is the
+    algorithmic bytes of one call over the call's average duration (HIP events on its stream,
+    every kernel the call launches); the bf16-MFMA fraction of the algorithmic flops rides along."""
+    achieved = r["bytes"] / r["kern"]
+    return {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK, "traffic": traffic,
+            "kernel": f"chunk_fwd ({KERNELS.get(r['kernel'], r['kernel'])})", "kernel_ms": r["kern"] * 1e3,
+            "workspace_bytes": r["workspace"], "alg_bytes": r["bytes"], "alg_flops": r["flops"],
+            "mfma_achieved_TFLOPs": r["flops"] / r["kern"] / 1e12,
+            "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK}
+
+
+def measured_traffic(workload: str, op: str = "chunk_fwd"):
+    """HBM bytes per call from the committed rocprofv3 counter record, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -328,12 +348,15 @@ def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
         gdn.gdn_chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, x["s0"], dsf, workspace=ws)
 
     _, kern = time_launches(fn, 1, steps, warmup, torch)
-    flops = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv)
+    flops = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, recompute=False)
+    flops_rc = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, recompute=True)
     del x, do, dsf, ws
     torch.cuda.empty_cache()
+    # float32 products on the float32 matrix cores (whose peak equals the float32 vector peak)
     return {"workload": cfg.name, "tokens_per_s": cfg.B * cfg.T / kern, "kernel_ms": kern * 1e3,
-            "alg_flops": flops, "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12,
+            "alg_flops": flops, "bound": "mfma", "unit": "TFLOP/s", "achieved_TFLOPs": flops / kern / 1e12,
             "peak_TFLOPs": FP32_VALU_PEAK / 1e12, "frac": flops / kern / FP32_VALU_PEAK,
+            "flops_with_state_recompute": flops_rc, "frac_with_state_recompute": flops_rc / kern / FP32_VALU_PEAK,
             "kernels": "bwd_gram_kernel + bwd_pass_kernel (state recompute beside the reverse state pass) + bwd_chunk_kernel"}
 
 
@@ -361,10 +384,14 @@ def bench_kda(cfg, torch, gdn, steps=10, warmup=2):
     flops = kda_alg_flops(B, T, Hqk, Hv, dk, dv, cfg.chunk)
     del q, k, v, beta, g, o, sf
     torch.cuda.empty_cache()
-    return {"workload": cfg.name, "tokens_per_s": B * T / kern, "kernel_ms": kern * 1e3, "alg_flops": flops,
-            "bound": "alu", "achieved_TFLOPs": flops / kern / 1e12, "peak_TFLOPs": FP32_VALU_PEAK / 1e12,
-            "frac": flops / kern / FP32_VALU_PEAK,
-            "kernels": "kda_prep_kernel + kda_state_kernel" if cfg.chunk == 64 else "kda_chunk_kernel"}
+    # chunk 64 runs its products on the float16 matrix cores (the bf16 rate); chunks 16 and 32
+    # run the float32 vector kernel
+    mfma = cfg.chunk == 64
+    peak = MFMA_BF16_PEAK if mfma else FP32_VALU_PEAK
+    return {"workload": cfg.name, "chunk": cfg.chunk, "tokens_per_s": B * T / kern, "kernel_ms": kern * 1e3,
+            "alg_flops": flops, "bound": "mfma" if mfma else "alu", "unit": "TFLOP/s",
+            "achieved_TFLOPs": flops / kern / 1e12, "peak_TFLOPs": peak / 1e12, "frac": flops / kern / peak,
+            "kernels": "kda_prep_kernel + kda_state_kernel" if mfma else "kda_chunk_kernel"}
 
 
 def bench_varlen(torch, gdn, gi, steps=10, warmup=2):
@@ -424,12 +451,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3next_prefill")
+    ap.add_argument("--workload", default="qwen36_long_prefill")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen", "scan"),
+    ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen", "scan", "decode"),
                     help="run only this secondary leg and print its result (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -452,19 +479,20 @@ def main():
     gdn.load_library()
     cfg = gi.CONFIGS[args.workload]
     if args.leg:
-        legs = {"layer_ops": lambda: bench_layer_ops(cfg, torch, gdn),
-                "backward": lambda: bench_backward(cfg, torch, gdn),
+        # the layer steps and the backward run at the Qwen3-Next shape unless a workload is named
+        lcfg = cfg if args.workload != ap.get_default("workload") else gi.CONFIGS["qwen3next_prefill"]
+        legs = {"layer_ops": lambda: bench_layer_ops(lcfg, torch, gdn),
+                "backward": lambda: bench_backward(lcfg, torch, gdn),
                 "kda": lambda: bench_kda(gi.CONFIGS["kda_prefill"], torch, gdn),
                 "varlen": lambda: bench_varlen(torch, gdn, gi),
-                "scan": lambda: bench_scan(torch, gdn, gi)}
+                "scan": lambda: bench_scan(torch, gdn, gi),
+                "decode": lambda: bench_decode(gi.CONFIGS["decode"], torch, gdn, gi)}
         print(json.dumps({"leg": args.leg, **legs[args.leg]()}), flush=True)
         return
     print(f"bench: prefill {cfg}", file=sys.stderr, flush=True)
     r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi)
     tokens = cfg.B * cfg.T
     ms = r["wall"] / args.steps * 1e3
-    achieved = r["bytes"] / r["kern"]
-    traffic = measured_traffic(cfg.name)
     line = {
         "metric": "GDN prefill tokens/sec + % MFMA peak; decode steps/sec + HBM GB/s, 1 MI355X",
         "value": tokens * args.steps / r["wall"],
@@ -481,14 +509,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hqk": cfg.Hqk, "Hv": cfg.Hv,
                    "dk": cfg.dk, "dv": cfg.dv, "chunk": cfg.chunk, "state": "float32",
                    "initial_state": cfg.s0_std > 0, "input_sets": r["n_sets"]},
-        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                     "traffic": traffic,
-                     "kernel": f"chunk_fwd ({KERNELS.get(r['kernel'], r['kernel'])})",
-                     "kernel_ms": r["kern"] * 1e3,
-                     "workspace_bytes": r["workspace"],
-                     "alg_bytes": r["bytes"], "alg_flops": r["flops"],
-                     "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK},
+        "roofline": prefill_roofline(r, measured_traffic(cfg.name)),
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -500,30 +521,35 @@ def main():
         bw = dr["bytes"] / dr["kern"]
         line["decode"] = {"workload": dcfg.name, "B": dcfg.B, "Hv": dcfg.Hv, "d": dcfg.dk, "steps": dcfg.steps,
                           "steps_per_s": dcfg.steps / dr["wall64"], "ms_64_steps": dr["wall64"] * 1e3,
-                          "kernel_us": dr["kern"] * 1e6, "alg_bytes_per_step": dr["bytes"],
-                          "hbm_GBps": bw / 1e9, "hbm_frac": bw / HBM_PEAK,
-                          "tokens_per_s": dcfg.steps * dcfg.B / dr["wall64"]}
+                          "tokens_per_s": dcfg.steps * dcfg.B / dr["wall64"],
+                          "roofline": {"bound": "hbm", "achieved": bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                       "frac": bw / HBM_PEAK, "traffic": measured_traffic("decode", "recurrent_step"),
+                                       "kernel": "recurrent_step_kernel", "kernel_us": dr["kern"] * 1e6,
+                                       "alg_bytes": dr["bytes"]}}
         pc = {}
-        for name in ("batched_prefill", "qwen36_long_prefill"):
+        for name in ("batched_prefill", "qwen3next_prefill"):
+            if name == cfg.name:
+                continue
             c = gi.CONFIGS[name]
             print(f"bench: prefill {c}", file=sys.stderr, flush=True)
-            rr = bench_prefill(c, 5, 2, torch, gdn, gi)
+            rr = bench_prefill(c, 10, 3, torch, gdn, gi)
             pc[name] = {"tokens_per_s": c.B * c.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
-                        "mfma_frac": rr["flops"] / rr["kern"] / MFMA_BF16_PEAK,
-                        "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
-        # the same qwen3next shape with float32 q, k, v, o: the float32 chunk kernel (float32
-        # matrix-core products), bound by its per-chunk chain; fraction of the float32 peak
-        c32 = dataclasses.replace(cfg, name=cfg.name + "_f32", dtype="f32")
+                        "roofline": prefill_roofline(rr, measured_traffic(name))}
+        # the Qwen3-Next shape with float32 q, k, v, o: the float32 kernel (float32 matrix-core
+        # products), bound by its per-chunk chain; fraction of the float32 peak
+        c32 = dataclasses.replace(gi.CONFIGS["qwen3next_prefill"], name="qwen3next_prefill_f32", dtype="f32")
         print(f"bench: prefill {c32}", file=sys.stderr, flush=True)
         rr = bench_prefill(c32, 5, 2, torch, gdn, gi)
         pc[c32.name] = {"tokens_per_s": c32.B * c32.T / rr["kern"], "kernel_ms": rr["kern"] * 1e3,
-                        "fp32_frac": rr["flops"] / rr["kern"] / FP32_VALU_PEAK,
-                        "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}
+                        "roofline": {"bound": "mfma", "achieved": rr["flops"] / rr["kern"] / 1e12,
+                                     "peak": FP32_VALU_PEAK / 1e12, "unit": "TFLOP/s",
+                                     "frac": rr["flops"] / rr["kern"] / FP32_VALU_PEAK,
+                                     "hbm_frac": rr["bytes"] / rr["kern"] / HBM_PEAK, "kernel": rr["kernel"]}}
         line["prefill_configs"] = pc
         print("bench: layer steps (prologue, gated RMSNorm)", file=sys.stderr, flush=True)
-        line["layer_ops"] = bench_layer_ops(cfg, torch, gdn)
+        line["layer_ops"] = bench_layer_ops(gi.CONFIGS["qwen3next_prefill"], torch, gdn)
         gp = {}
-        for name in (cfg.name, "batched_prefill"):
+        for name in ("qwen3next_prefill", "batched_prefill"):
             c = gi.CONFIGS[name]
             print(f"bench: gated prefill {c}", file=sys.stderr, flush=True)
             rr = bench_prefill(c, 5, 2, torch, gdn, gi, gated=True)
@@ -534,8 +560,9 @@ def main():
                         "route": "norm fused into the prefill kernel" if fused
                         else "O through the workspace, then the norm kernel"}
         line["gated_prefill"] = gp
-        print(f"bench: backward {cfg}", file=sys.stderr, flush=True)
-        line["backward"] = bench_backward(cfg, torch, gdn)
+        bcfg = gi.CONFIGS["qwen3next_prefill"]
+        print(f"bench: backward {bcfg}", file=sys.stderr, flush=True)
+        line["backward"] = bench_backward(bcfg, torch, gdn)
         kcfg = gi.CONFIGS["kda_prefill"]
         print(f"bench: kda {kcfg}", file=sys.stderr, flush=True)
         line["kda"] = bench_kda(kcfg, torch, gdn)

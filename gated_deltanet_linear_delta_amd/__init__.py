@@ -22,6 +22,7 @@ Entry points (same names as the C ABI in include/gdn.h):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -32,7 +33,7 @@ __all__ = [
     "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
     "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
     "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments", "gdn_chunk_transport",
-    "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS", "test_hooks",
 ]
 
 GDN_F32 = 0
@@ -46,7 +47,8 @@ EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_worksp
                     "gdn_chunk_transport", "gdn_chunk_transport_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_lib = None
+_libs = {}
+_variant = "release"
 
 
 class GdnError(RuntimeError):
@@ -55,16 +57,32 @@ class GdnError(RuntimeError):
         super().__init__(f"{where}: status {status} ({gdn_status_string(status)})")
 
 
-def library_path() -> str:
-    return os.path.join(_HERE, "libgdn.so")
+def library_path(variant: str = "release") -> str:
+    """libgdn.so, or (variant "hooks") libgdn_hooks.so: the same kernels, with the automatic route
+    choice open to environment overrides (GDN_MFMA_PATH, GDN_MFMA_BV, GDN_SPLIT_BV,
+    GDN_DISABLE_MFMA, GDN_SCAN_SEGMENTS) so that tests can run every kernel family."""
+    return os.path.join(_HERE, "libgdn.so" if variant == "release" else "libgdn_hooks.so")
 
 
-def load_library():
-    """Load libgdn.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    path = library_path()
+@contextlib.contextmanager
+def test_hooks():
+    """Route every call made inside the block through libgdn_hooks.so (a testing aid)."""
+    global _variant
+    prev = _variant
+    load_library("hooks")
+    _variant = "hooks"
+    try:
+        yield
+    finally:
+        _variant = prev
+
+
+def load_library(variant: str | None = None):
+    """Load libgdn.so (or the test-hooks build; raises if it has not been built)."""
+    v = variant or _variant
+    if v in _libs:
+        return _libs[v]
+    path = library_path(v)
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
                            "or `python gated_deltanet_linear_delta_amd/build.py`")
@@ -110,7 +128,7 @@ def load_library():
     lib.gdn_chunk_transport.restype = i
     lib.gdn_chunk_transport_workspace_bytes.argtypes = [i] * 7 + [i]
     lib.gdn_chunk_transport_workspace_bytes.restype = sz
-    _lib = lib
+    _libs[v] = lib
     return lib
 
 

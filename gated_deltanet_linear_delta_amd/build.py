@@ -1,4 +1,8 @@
-"""Build libgdn.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc."""
+"""Build libgdn.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
+
+Also builds libgdn_hooks.so, the same library with chunk_mfma.hip compiled with GDN_TEST_HOOKS:
+that build lets environment variables override the automatic route choice so that the tests
+can run every kernel family on small shapes.  The release library reads no environment."""
 from __future__ import annotations
 
 import os
@@ -11,6 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+LIB_HOOKS = os.path.join(PKG, "libgdn_hooks.so")
 SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip", "kda.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -22,32 +27,39 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    procs = []
+    jobs = []   # (label, object, command)
     objs = []
     for src in SOURCES:
         obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        jobs.append((src, obj, [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    hooks_obj = os.path.join(OBJDIR, "chunk_mfma_hooks.o")
+    jobs.append(("chunk_mfma.hip (test hooks)", hooks_obj,
+                 [HIPCC] + FLAGS + ["-DGDN_TEST_HOOKS", "-x", "hip", "-c", os.path.join(CSRC, "chunk_mfma.hip"), "-o", hooks_obj]))
+    procs = []
+    for label, _, cmd in jobs:
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        procs.append((label, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
-    for src, p in procs:
+    for label, p in procs:
         out, _ = p.communicate()
         text = out.decode(errors="replace")
         # hipcc's host pass does not know the packed-fp32 feature flag and says so; that is harmless.
         lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
         if p.returncode != 0:
-            failed.append(src)
+            failed.append(label)
             sys.stderr.write(text)
         elif verbose and lines:
             sys.stderr.write("\n".join(lines) + "\n")
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp], check=True)
-    os.replace(tmp, LIB)
+    hooks_objs = [hooks_obj if o.endswith(os.sep + "chunk_mfma.o") else o for o in objs]
+    for out, parts in ((LIB, objs), (LIB_HOOKS, hooks_objs)):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + parts + ["-o", tmp], check=True)
+        os.replace(tmp, out)
     return LIB
 
 

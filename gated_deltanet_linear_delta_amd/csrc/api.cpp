@@ -88,7 +88,7 @@ const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int
     if (check_chunk_sizes(B, T, Hqk, Hv, dk, dv, chunk, dtype) != GDN_OK) return nullptr;
     gdn::ChunkArgs a = make_chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                        nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
-    if (!gdn::chunk_mfma_supported(a)) return "simt";
+    if (!gdn::chunk_mfma_supported(a)) return "mfma_f32";
     if (gdn::chunk_auto_segments(a) > 1) return "mfma_scan";
     return gdn::chunk_mfma_split(a) ? "mfma_split" : "mfma";
 }

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(GR_NT) void bwd_gram_kernel(const T* __restrict__ q
     }
     if (tid < BW_C) {
         const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
-        gcs[tid] = tid < n ? g[off] : 0.f;
+        gcs[tid] = tid < n ? log_decay(g[off]) : 0.f;
         bs[tid] = tid < n ? beta[off] : 0.f;
     }
     __syncthreads();
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         __syncthreads();   // the previous head is done with every buffer
         if (tid < BW_C) {
             const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
-            gcs[tid] = tid < n ? g[off] : 0.f;
+            gcs[tid] = tid < n ? log_decay(g[off]) : 0.f;
             bs[tid] = tid < n ? beta[off] : 0.f;
             dgcs[tid] = 0.f;
             dbts[tid] = 0.f;

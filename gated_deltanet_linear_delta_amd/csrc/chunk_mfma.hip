@@ -735,7 +735,7 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
         }
         if (pw == 0) {
             const size_t off = (size_t)(t0 + min(lane, n - 1)) * Hv;
-            rg = gb[off];
+            rg = log_decay(gb[off]);
             rb = bb[off];
         }
     };
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
     // gates of the group's first value head, then the Gram fragments straight from HBM (standard
     // k order on both sides); rows past T are clamped and masked below
     const size_t grow = (sq.tok0 + t0 + min(lane, n - 1)) * Hv + (size_t)i * grp;
-    float gl = g[grow], bl = beta[grow];
+    float gl = log_decay(g[grow]), bl = beta[grow];
     bf16x8 kf[4][KB], qf[4][KB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -1116,7 +1116,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
         const float x = wave_cumsum(lane < n ? gl : 0.f, lane);
         const float bt = lane < n ? bl : 0.f;
         if (jj + 1 < grp) {
-            gl = g[grow + jj + 1];
+            gl = log_decay(g[grow + jj + 1]);
             bl = beta[grow + jj + 1];
         }
         const float last = __shfl(x, 63, 64);
@@ -1663,11 +1663,20 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
 
 namespace {
 
+#ifdef GDN_TEST_HOOKS
+// Only in the test-hooks build of the library (libgdn_hooks.so, which the tests load to run every
+// kernel family on small shapes): environment overrides of the automatic route choice.  The
+// release library reads no environment; its route and workspace size follow from the arguments.
 int env_int(const char* name, int dflt)
 {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
 }
+const char* env_str(const char* name) { return getenv(name); }
+#else
+int env_int(const char*, int dflt) { return dflt; }
+const char* env_str(const char*) { return nullptr; }
+#endif
 
 int choose_bv(const ChunkArgs& a)
 {
@@ -1693,7 +1702,7 @@ int choose_split_bv(const ChunkArgs& a)
 
 bool use_split(const ChunkArgs& a)
 {
-    if (const char* e = getenv("GDN_MFMA_PATH")) {
+    if (const char* e = env_str("GDN_MFMA_PATH")) {
         if (!strcmp(e, "split")) return true;
         if (!strcmp(e, "fused")) return false;
     }
@@ -1893,7 +1902,7 @@ hipError_t launch_transport_t(const ChunkArgs& a, float* m_out, float* n_out, vo
 
 bool chunk_mfma_supported(const ChunkArgs& a)
 {
-    if (getenv("GDN_DISABLE_MFMA")) return false;
+    if (env_str("GDN_DISABLE_MFMA")) return false;
     return a.dtype_bf16 && a.chunk == CH && (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128);
 }
 
@@ -2041,7 +2050,7 @@ __global__ __launch_bounds__(KQ_NT) void kda_prep_kernel(const T* __restrict__ q
             const size_t tok = (size_t)b * T_len + t0 + r;
             kv = to_f32(k[(tok * Hqk + i) * DK + m]);
             qv = to_f32(q[(tok * Hqk + i) * DK + m]) * scale;
-            gv = g[(tok * Hv + j) * DK + m];
+            gv = log_decay(g[(tok * Hv + j) * DK + m]);
         }
         Ks[r * KP + m] = kv;
         Qs[r * KP + m] = qv;

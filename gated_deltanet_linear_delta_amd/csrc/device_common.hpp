@@ -37,6 +37,15 @@ __device__ __forceinline__ void store4f(bf16* p, floatx4 v) {
     *reinterpret_cast<bf16x4*>(p) = o;
 }
 
+// A log decay g = log alpha as the chunk kernels use it: raised to at least -100.  The chunk
+// algebra exponentiates differences of in-chunk cumulative sums of g, so g = -inf (alpha = 0,
+// which clears the state: "Gated Attention Architectures", section 3) would give -inf - -inf =
+// NaN.  exp(-100) is below every float32 normal (the smallest is about exp(-87.3)), so the floor
+// changes no product by more than float32's own rounding.  A floored token moves the cumsum by
+// about -100, where float32's spacing is 8e-6, so later differences keep that accuracy; a chunk
+// of 64 floored tokens sums to -6400, far from float32's range limits.
+__device__ __forceinline__ float log_decay(float g) { return fmaxf(g, -100.f); }
+
 // Butterfly sum over lanes whose ids differ only in bits [lo_mask .. 32]: used to reduce the
 // row-partials of one column group held by several lanes of a wave.
 __device__ __forceinline__ float xor_sum(float x, int stride_lo) {

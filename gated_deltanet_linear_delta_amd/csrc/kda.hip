@@ -82,7 +82,7 @@ __global__ __launch_bounds__(KDA_NT) void kda_chunk_kernel(
                 const size_t tok = (size_t)b * T_len + t0 + r;
                 kv = to_f32(k[(tok * Hqk + i) * DK + m]);
                 qv = to_f32(q[(tok * Hqk + i) * DK + m]) * scale;
-                gv = g[(tok * Hv + j) * DK + m];
+                gv = log_decay(g[(tok * Hv + j) * DK + m]);
             }
             Ks[r * KP + m] = kv;
             Qs[r * KP + m] = qv;

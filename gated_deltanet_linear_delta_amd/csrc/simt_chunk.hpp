@@ -149,7 +149,7 @@ __device__ __forceinline__ void simt_chunk_body(
         }
         if (tid < C) {
             const size_t off = (tok0 + min(t0 + tid, T_len - 1)) * Hv + j;
-            gr = g[off];
+            gr = log_decay(g[off]);
             br = beta[off];
         }
     };
@@ -208,7 +208,7 @@ __device__ __forceinline__ void simt_chunk_body(
             }
             if (tid < C) {
                 const size_t off = (tok0 + t0 + tid) * Hv + j;
-                gcs[tid] = tid < n ? g[off] : 0.f;
+                gcs[tid] = tid < n ? log_decay(g[off]) : 0.f;
                 bs[tid] = tid < n ? beta[off] : 0.f;
             }
         }

@@ -17,8 +17,27 @@
  *    frees, or keeps a pointer after the call returns.  Tensors are dense, contiguous, row-major
  *    in the layouts given.  q, k, v, o and the states must be 16-byte aligned; g and beta
  *    4-byte aligned.
- *  - q, k, v and o share one dtype (gdn_dtype_t).  g (= log alpha, any real value; g <= 0 is the
- *    intended range, alpha in (0,1]), beta and the state are float32.
+ *  - q, k, v and o share one dtype (gdn_dtype_t).  g = log alpha, beta and the state are float32.
+ *  - Gate range.  g <= 0 (alpha in [0, 1], the decay gate); g = -inf (alpha = 0: the state is
+ *    cleared, "Gated Attention Architectures", section 3) is accepted.  The prefill kernels raise
+ *    g to at least -100 before use: exp(-100) lies below float32's normal range, so this changes
+ *    no result beyond float32 rounding, and it keeps differences of in-chunk sums of g finite.
+ *    beta in [0, 1] (the write strength).  g > 0 (alpha > 1, a growing state) is outside the
+ *    supported range of the bf16 matrix-core routes below; the float32 routes and decode accept it
+ *    while every value stays finite in float32.
+ *  - Operand range of the bf16 matrix-core routes (gdn_chunk_fwd_kernel_name "mfma",
+ *    "mfma_split", "mfma_scan"; gdn_chunk_fwd_gated, _varlen, _scan, gdn_chunk_transport and
+ *    gdn_kda_chunk_fwd at chunk 64).  Their products take float16 operands (the same matrix-core
+ *    rate as bf16 with a 3-bit longer significand) and accumulate in float32.  The operands are
+ *    q, k, v, the state, (I + A)^{-1}, and per chunk R = beta (v - e^gc k^T h) and
+ *    Delta = (I + A)^{-1} R, so every one of them must stay below 65504 in magnitude.  With
+ *    L2-normalised q and k, g <= 0 and beta in [0, 1] (the intended use: "Architecture Thread I",
+ *    section "Modern Architecture Improvements", normalises q and k before the recurrence) that
+ *    holds while |v| and the entries of the state stay below about 2^11 (the tests run |v| and
+ *    |initial_state| up to 2^10).  Outside that range the float16 operands may overflow and the
+ *    results are unspecified (inf or NaN may appear); the float32 route has no such limit.  bf16
+ *    components of q and k below 2^-14 in magnitude become float16 subnormals (absolute error at
+ *    most 2^-25, negligible next to a unit-norm row).
  *  - Grouped heads: Hv must be a multiple of Hqk; value head j reads query/key head
  *    floor(j / (Hv / Hqk)) (contiguous groups).
  *  - q is multiplied by `scale` before the readout (1.0 gives o_t = S_t q_t exactly).
@@ -53,7 +72,7 @@ typedef enum {
 
 typedef enum {
     GDN_F32 = 0,   /* q, k, v, o are float32 */
-    GDN_BF16 = 1   /* q, k, v, o are bfloat16; arithmetic accumulates in float32 */
+    GDN_BF16 = 1   /* q, k, v, o are bfloat16; products accumulate in float32 (operand range above) */
 } gdn_dtype_t;
 
 /*
@@ -64,9 +83,7 @@ typedef enum {
  * 128 * dk bytes per query/key head (q as matrix-core operands), all built before the state
  * pass.  When the chains are too few to fill the GPU and long (gdn_chunk_fwd_kernel_name says
  * "mfma_scan") it is gdn_chunk_fwd_scan_workspace_bytes for the segment count chosen.  The result
- * depends only on the arguments (and on the GDN_MFMA_PATH / GDN_DISABLE_MFMA /
- * GDN_SCAN_SEGMENTS environment variables, which select the path).  Pure host function; needs
- * no device; 0 for invalid sizes.
+ * depends only on the arguments.  Pure host function; needs no device; 0 for invalid sizes.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                      gdn_dtype_t dtype);
@@ -131,8 +148,10 @@ gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, con
  * per-chunk prep kernel, then the matrix-core state pass; fewer chains), "mfma_scan" (the
  * affine chunk scan of gdn_chunk_fwd_scan: so few chains that 32-column tiles over dv + dk
  * columns give at most 128 workgroups, cut into p = 1 + 256 / (B * Hv * (dv + dk) / 32)
- * segments when T holds at least 8 p chunks), "simt" (float32 vector kernel: float32 inputs,
- * chunk != 64 or head dim 32), or NULL when the sizes are unsupported.  Pure host function.
+ * segments when T holds at least 8 p chunks), "mfma_f32" (the float32 kernel: the chunk algebra
+ * in float32 with its dense products on the float32 matrix cores; float32 inputs, chunk != 64 or
+ * head dim 32), or NULL when the sizes are unsupported.  The choice depends only on the
+ * arguments.  Pure host function.
  */
 const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
                                       gdn_dtype_t dtype);

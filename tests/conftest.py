@@ -26,3 +26,12 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture
+def hooks():
+    """Calls made in the test go through libgdn_hooks.so, the build of the library whose route
+    choice honours the GDN_* environment overrides (the release libgdn.so reads no environment)."""
+    import gated_deltanet_linear_delta_amd as gdn
+    with gdn.test_hooks():
+        yield gdn

@@ -70,3 +70,26 @@ def sample_chains(d, chains, Hqk, Hv):
         out[n] = np.stack([d[n][b, :, j] for b, j in chains])[:, :, None]
     out["s0"] = None if d["s0"] is None else np.stack([d["s0"][b, j] for b, j in chains])[:, None]
     return out
+
+
+class Guarded:
+    """An output tensor with guard bands: `t` is a view into a larger buffer whose GUARD elements
+    before and after it hold a fill pattern; `check()` asserts that no kernel wrote past either
+    end of `t`."""
+    GUARD = 1024
+
+    def __init__(self, shape, dtype, fill=-7.75):
+        import torch
+        n = 1
+        for x in shape:
+            n *= int(x)
+        self.n = n
+        self.fill = fill
+        self.buf = torch.full((n + 2 * self.GUARD,), fill, dtype=dtype, device=DEV)
+        self.t = self.buf[self.GUARD:self.GUARD + n].view(*shape)
+
+    def check(self, name=""):
+        import torch
+        lo, hi = self.buf[:self.GUARD], self.buf[self.GUARD + self.n:]
+        ref = torch.full_like(lo, self.fill)
+        assert torch.equal(lo, ref) and torch.equal(hi, ref), f"{name}: a kernel wrote outside its output"

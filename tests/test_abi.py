@@ -45,7 +45,7 @@ def test_status_strings_and_queries():
     assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 33, 128, 128, 64, gdn.GDN_BF16) == 0
-    assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 32, 32, 16, gdn.GDN_F32) == "simt"
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 32, 32, 16, gdn.GDN_F32) == "mfma_f32"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 3, 32, 32, 16, gdn.GDN_F32) is None
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 48, 32, 16, gdn.GDN_F32) is None
 
@@ -526,7 +526,7 @@ def test_scan_transport_valid_calls_report_no_device():
     assert transport_call(T=0, ws=None, wsb=0) == NODEV
 
 
-def test_chunk_fwd_routes_scarce_long_chains_to_the_scan(monkeypatch):
+def test_chunk_fwd_routes_scarce_long_chains_to_the_scan(monkeypatch, hooks):
     """gdn_chunk_fwd cuts chains into segments by itself when 32-column tiles over dv + dk give at
     most 128 workgroups and every segment keeps at least 8 chunks."""
     name = lambda B, T, Hqk, Hv: gdn.gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
@@ -545,3 +545,21 @@ def test_chunk_fwd_routes_scarce_long_chains_to_the_scan(monkeypatch):
     assert name(1, 65536, 2, 6) == "mfma_split"
     assert ws(1, 65536, 2, 6) == gdn.gdn_chunk_fwd_scan_workspace_bytes(1, 65536, 2, 6, 128, 128, 64,
                                                                         gdn.GDN_BF16, 1) - 6 * 128 * 128 * 4
+
+
+def test_release_library_reads_no_environment(monkeypatch):
+    """The route and the workspace size of the release library follow from the arguments alone:
+    the overrides that the test-hooks build honours change nothing in libgdn.so."""
+    args = (1, 65536, 2, 6, 128, 128, 64, gdn.GDN_BF16)
+    name, ws = gdn.gdn_chunk_fwd_kernel_name(*args), gdn.gdn_chunk_fwd_workspace_bytes(*args)
+    small = (2, 300, 2, 4, 128, 128, 64, gdn.GDN_BF16)
+    name_s = gdn.gdn_chunk_fwd_kernel_name(*small)
+    for var, val in (("GDN_SCAN_SEGMENTS", "0"), ("GDN_MFMA_PATH", "fused"), ("GDN_DISABLE_MFMA", "1"),
+                     ("GDN_SPLIT_BV", "16"), ("GDN_MFMA_BV", "64")):
+        monkeypatch.setenv(var, val)
+        assert gdn.gdn_chunk_fwd_kernel_name(*args) == name == "mfma_scan"
+        assert gdn.gdn_chunk_fwd_workspace_bytes(*args) == ws
+        assert gdn.gdn_chunk_fwd_kernel_name(*small) == name_s == "mfma_split"
+    # the test-hooks build does take them
+    with gdn.test_hooks():
+        assert gdn.gdn_chunk_fwd_kernel_name(*small) == "mfma_f32"

@@ -1,0 +1,147 @@
+"""The gate limits and the operand range, on every route, against the float64 oracle.
+
+"Gated Attention Architectures", section 3 (Gated DeltaNet, description): alpha -> 0 clears the
+memory and alpha = 1 gives back the pure delta rule; section 2: beta in (0, 1) is the writing
+strength, so beta = 0 writes nothing (the state only decays) and beta = 1 overwrites the value
+stored under the key.  Each case runs on the fused and split matrix-core kernels, the affine
+chunk scan, the float32 kernel and the decode step, with a nonzero initial state, several chunks
+and a ragged tail, and guard bands after every output.  The operand-range case runs |v| and
+|S0| near the limit the header states for the float16 operands of the matrix-core routes.  The
+last test gives the chunk-64 KDA kernels a dense strictly-lower A (identical keys, beta near 1).
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+import oracle
+from gpu_util import Guarded, check, dev, f64, host, say
+
+gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ROUTES = ("fused", "split", "scan", "f32", "decode")
+
+
+def limit_case(case, dtype, T, seed):
+    d = gi.generate(B=2, T=T, Hqk=2, Hv=4, dk=128, dv=128, dtype=dtype, mu=3.0, s0_std=0.05, seed=seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    if case == "alpha0_some":      # alpha = 0 (g = -inf) on about a quarter of the tokens
+        d["g"][rng.random(d["g"].shape) < 0.25] = -np.inf
+    elif case == "alpha0_all":     # alpha = 0 everywhere: every step keeps only its own write
+        d["g"][:] = -np.inf
+    elif case == "alpha_tiny":     # alpha = e^-60, finite but far below float32's normal range
+        d["g"][:] = -60.0
+    elif case == "alpha1":         # alpha = 1: the ungated delta rule
+        d["g"][:] = 0.0
+    elif case == "beta0":          # beta = 0: the initial state only decays
+        d["beta"][:] = 0.0
+    elif case == "beta1":          # beta = 1: full overwrite
+        d["beta"][:] = 1.0
+    elif case == "alpha1_beta1":
+        d["g"][:] = 0.0
+        d["beta"][:] = 1.0
+    else:
+        raise ValueError(case)
+    return d
+
+
+def run_route(route, d, hooks_env, monkeypatch):
+    """One prefill (or T decode steps) on the given route; O and the final state on the host."""
+    B, T, Hqk, dk = d["q"].shape
+    Hv, dv = d["v"].shape[2], d["v"].shape[3]
+    t = dev(d)
+    tdt = torch.bfloat16 if d["q"].dtype == np.uint16 else torch.float32
+    # decode writes one [B, Hv, dv] output per step: step-major there, token-major elsewhere
+    og = Guarded((T, B, Hv, dv) if route == "decode" else (B, T, Hv, dv), tdt)
+    sg = Guarded((B, Hv, dk, dv), torch.float32)
+    if route in ("fused", "split"):
+        monkeypatch.setenv("GDN_MFMA_PATH", route)
+        monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")
+        with hooks_env():
+            assert gdn.gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16) == \
+                ("mfma" if route == "fused" else "mfma_split")
+            gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64, o=og.t, final_state=sg.t)
+    elif route == "scan":
+        gdn.gdn_chunk_fwd_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], segments=3, o=og.t,
+                               final_state=sg.t)
+    elif route == "f32":
+        gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=32, o=og.t, final_state=sg.t)
+    else:
+        sg.t.copy_(t["s0"])
+        for s in range(T):
+            gdn.gdn_recurrent_step(t["q"][:, s].contiguous(), t["k"][:, s].contiguous(), t["v"][:, s].contiguous(),
+                                   t["g"][:, s].contiguous(), t["beta"][:, s].contiguous(), sg.t, o=og.t[s])
+    torch.cuda.synchronize()
+    og.check(route)
+    sg.check(route)
+    o = host(og.t)
+    return (np.ascontiguousarray(o.transpose(1, 0, 2, 3)) if route == "decode" else o), host(sg.t)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("case", ["alpha0_some", "alpha0_all", "alpha_tiny", "alpha1", "beta0", "beta1",
+                                  "alpha1_beta1"])
+def test_gate_limits(case, route, monkeypatch):
+    dtype = "f32" if route == "f32" else "bf16"
+    T = 40 if route == "decode" else 333
+    say(f"gate limit {case} route={route} dtype={dtype} T={T}")
+    d = limit_case(case, dtype, T, seed=sum(map(ord, case)) + T)
+    o, s = run_route(route, d, gdn.test_hooks, monkeypatch)
+    o_ref, s_ref = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    check(f"{case} {route}", dtype, o, o_ref, s, s_ref)
+
+
+def test_beta0_is_pure_decay_closed_form():
+    """beta = 0 everywhere: h_T = e^{G_T} S0 and o_t = e^{G_t} S0^T q_t (no write at all), on the
+    affine chunk scan, against that closed form directly (G the inclusive cumsum of g)."""
+    d = limit_case("beta0", "bf16", 200, seed=5)
+    o, s = run_route("scan", d, gdn.test_hooks, None)
+    G = np.cumsum(d["g"].astype(np.float64), axis=1)                       # [B,T,Hv]
+    q = f64(d["q"])
+    grp = d["v"].shape[2] // q.shape[2]
+    qv = np.repeat(q, grp, axis=2)                                          # [B,T,Hv,dk]
+    o_cf = np.exp(G)[..., None] * np.einsum("bhkv,bthk->bthv", d["s0"].astype(np.float64), qv)
+    s_cf = np.exp(G[:, -1])[..., None, None] * d["s0"]
+    check("beta0 closed form", "bf16", o, o_cf, s, s_cf)
+
+
+@pytest.mark.parametrize("route", ["fused", "split", "scan"])
+def test_fp16_operand_range(route, monkeypatch):
+    """|v| and |S0| near 2^10 (v ~ 256 N(0,1), S0 ~ 256 N(0,1)): the float16 operands of the
+    matrix-core routes stay in range and the bf16 tolerance holds (relative measures)."""
+    d = gi.generate(B=2, T=300, Hqk=2, Hv=4, dk=128, dv=128, dtype="f32", mu=3.0, s0_std=256.0, seed=61)
+    v = d["v"] * 256.0
+    d["v"] = gi.bf16_bits(v)
+    d["q"], d["k"] = gi.bf16_bits(d["q"]), gi.bf16_bits(d["k"])
+    say(f"operand range route={route}: max|v|={np.abs(v).max():.0f} max|S0|={np.abs(d['s0']).max():.0f}")
+    o, s = run_route(route, d, gdn.test_hooks, monkeypatch)
+    o_ref, s_ref = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    scale = float(np.abs(o_ref).max())
+    # the max-abs bound of the bf16 tolerance is for unit-scale outputs; here it scales with O
+    check(f"operand range {route}", "bf16", o / scale, o_ref / scale, s, s_ref)
+
+
+@pytest.mark.parametrize("beta", [0.9, 1.0])
+def test_kda_mfma_dense_a(beta):
+    """Chunk-64 KDA (matrix-core prep with the blockwise T = (I + A)^{-1}) with every key of a
+    head equal and beta near 1: A is dense with entries near 1, so the blocks of T below its
+    16-row diagonal blocks carry weight.  Against the KDA oracle, and against the float32 vector
+    kernel (chunk 32, float32 inputs of the same values)."""
+    d = gi.generate_kda(B=1, T=256, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=4.0, s0_std=0.05, seed=71)
+    d["k"][:] = d["k"][:, :1]
+    d["beta"][:] = beta
+    say(f"kda dense A beta={beta}")
+    t = dev(d)
+    o, sf = gdn.gdn_kda_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+    check(f"kda dense A beta={beta}", "bf16", host(o), o_ref, host(sf), s_ref)
+    t32 = {n: (x.float() if x is not None and x.dtype == torch.bfloat16 else x) for n, x in t.items()}
+    o32, s32 = gdn.gdn_kda_chunk_fwd(t32["q"], t32["k"], t32["v"], t32["g"], t32["beta"], t32["s0"], chunk=32)
+    torch.cuda.synchronize()
+    # the float32 route of the same (bf16-valued) inputs is within float32 rounding of the oracle,
+    # so this measures the matrix-core route's own error at the bf16 bound
+    check(f"kda dense A beta={beta} vs f32 route", "bf16", host(o), host(o32), host(sf), host(s32))

@@ -2,14 +2,14 @@
 
 Small shapes span several chunks and a ragged tail and are compared element by element over
 whole tensors; the five workload configurations are run in full on the GPU in the launch
-configuration the benchmark times, and compared on whole tensors (tiny and Qwen3-Next-shaped
-prefill) or on sampled (batch, value-head) chains that the oracle recomputes one by one."""
+configuration the benchmark times, and compared on whole tensors (every chain and token of
+every workload, and the 64 decode steps)."""
 import numpy as np
 import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import DEV, TOL, check, dev, f64, host, rel_l2, sample_chains, say
+from gpu_util import DEV, TOL, Guarded, check, dev, f64, host, rel_l2, sample_chains, say
 
 gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
 torch = pytest.importorskip("torch")
@@ -155,59 +155,58 @@ def test_qwen3next_prefill_full():
     check("qwen3next_prefill", "bf16", o, o_ref, s, s_ref)
 
 
-@pytest.mark.parametrize("name,chains", [
-    ("batched_prefill", [(0, 0), (3, 17), (7, 31), (5, 8)]),
-    ("qwen36_long_prefill", [(0, 0), (0, 1), (0, 23), (0, 47)]),
-])
-def test_large_prefill_sampled(name, chains):
+@pytest.mark.parametrize("name", ["batched_prefill", "qwen36_long_prefill"])
+def test_large_prefill_full(name):
+    """The batched (256 chains, S0 != 0) and the 64K-token (48 chains) workloads at full size, in
+    the launch configuration the benchmark times, against the oracle over whole tensors (every
+    chain, every token), with guard bands after O and the final state."""
     cfg = gi.CONFIGS[name]
-    say(f"config {cfg}, sampled chains {chains}")
+    say(f"config {cfg}, whole tensors")
     d = gi.generate(cfg)
-    o, s = run_prefill(d, cfg.chunk)
-    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
-    o_ref, s_ref = oracle_prefill(sd)
-    o_s = np.stack([o[b, :, j] for b, j in chains])[:, :, None]
-    s_s = np.stack([s[b, j] for b, j in chains])[:, None]
-    check(name, "bf16", o_s, o_ref, s_s, s_ref)
+    t = dev(d)
+    og = Guarded((cfg.B, cfg.T, cfg.Hv, cfg.dv), torch.bfloat16)
+    sg = Guarded((cfg.B, cfg.Hv, cfg.dk, cfg.dv), torch.float32)
+    gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=cfg.chunk, o=og.t,
+                      final_state=sg.t)
+    torch.cuda.synchronize()
+    og.check(name)
+    sg.check(name)
+    o, s = host(og.t), host(sg.t)
+    del t, og, sg
+    o_ref, s_ref = oracle_prefill(d)
+    check(name, "bf16", o, o_ref, s, s_ref)
 
 
-def test_decode_config_sampled():
+def test_decode_config_full():
+    """The decode workload (B=256, 32 value heads, 64 steps, state updated in place): every
+    output of every step and the whole final state against the oracle."""
     cfg = gi.CONFIGS["decode"]
-    say(f"config {cfg}")
+    say(f"config {cfg}, whole tensors")
     d = gi.generate_decode(cfg)
     t = dev(d)
     state = t["s0"].clone()
-    o = torch.empty((cfg.steps, cfg.B, cfg.Hv, cfg.dv), dtype=torch.bfloat16, device=DEV)
+    og = Guarded((cfg.steps, cfg.B, cfg.Hv, cfg.dv), torch.bfloat16)
     for s in range(cfg.steps):
-        gdn.gdn_recurrent_step(t["q"][s], t["k"][s], t["v"][s], t["g"][s], t["beta"][s], state, o=o[s])
+        gdn.gdn_recurrent_step(t["q"][s], t["k"][s], t["v"][s], t["g"][s], t["beta"][s], state, o=og.t[s])
     torch.cuda.synchronize()
-    chains = [(0, 0), (17, 5), (100, 31), (255, 16), (128, 1), (64, 30), (3, 9), (200, 22)]
-    grp = cfg.Hv // cfg.Hqk
-    pick = lambda a, hd: np.stack([a[:, b, hd(j)] for b, j in chains], axis=1)
-    qs = pick(d["q"], lambda j: j // grp)[:, :, None]
-    ks = pick(d["k"], lambda j: j // grp)[:, :, None]
-    vs = pick(d["v"], lambda j: j)[:, :, None]
-    gs = pick(d["g"], lambda j: j)[:, :, None]
-    bs = pick(d["beta"], lambda j: j)[:, :, None]
-    s0 = np.stack([d["s0"][b, j] for b, j in chains])[:, None]
-    o_ref, s_ref = oracle.decode(f64(qs), f64(ks), f64(vs), gs, bs, s0)
-    oh = host(o)
-    o_s = np.stack([oh[:, b, j] for b, j in chains], axis=1)[:, :, None]
-    sh = state[[b for b, _ in chains], [j for _, j in chains]]
-    check("decode config", "bf16", o_s, o_ref, host(sh)[:, None], s_ref)
+    og.check("decode")
+    oh, sh = host(og.t), host(state)
+    del t, state, og
+    o_ref, s_ref = oracle.decode(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+    check("decode config", "bf16", oh, o_ref, sh, s_ref)
 
 
 def test_kernel_family_dispatch():
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
     assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
-    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 32, gdn.GDN_BF16) == "simt"
-    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == "simt"
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 32, gdn.GDN_BF16) == "mfma_f32"
+    assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == "mfma_f32"
 
 
 @pytest.mark.parametrize("bv", ["64", "128"])
 @pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
                                             (64, 64, 1, 1, 1), (128, 128, 700, 1, 1)])
-def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
+def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch, hooks):
     """The fused matrix-core kernel at both column-tile widths, with grouped heads, a ragged last
     chunk and a nonzero initial state."""
     if dv == 64 and bv == "128":
@@ -226,7 +225,7 @@ def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
 @pytest.mark.parametrize("bv", ["16", "32"])
 @pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
                                             (64, 64, 1, 1, 1), (128, 128, 700, 1, 1), (128, 128, 127, 1, 3)])
-def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
+def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch, hooks):
     """The split matrix-core path (per-chunk prep kernel into the workspace, then the state pass)
     at every column-tile width, with grouped heads, a ragged last chunk, a nonzero initial state
     and a scale."""
@@ -245,7 +244,7 @@ def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch):
 
 @pytest.mark.parametrize("path", ["fused", "split"])
 @pytest.mark.parametrize("mu", [3.0, 8.0])
-def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch):
+def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch, hooks):
     """All keys of a head equal: the strictly-lower A of every chunk is dense, so every block of
     the (I + A)^{-1} merge carries weight."""
     monkeypatch.setenv("GDN_MFMA_PATH", path)
@@ -258,7 +257,7 @@ def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch):
 
 
 @pytest.mark.parametrize("path", ["fused", "split"])
-def test_mfma_matches_simt(path, monkeypatch):
+def test_mfma_matches_simt(path, monkeypatch, hooks):
     """Two independent GPU implementations of the chunk algebra agree (and both match the oracle)."""
     say(f"mfma ({path}) vs simt")
     d = gi.generate(B=2, T=500, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=41)
@@ -266,7 +265,7 @@ def test_mfma_matches_simt(path, monkeypatch):
     assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == ("mfma" if path == "fused" else "mfma_split")
     o_m, s_m = run_prefill(d, 64)
     monkeypatch.setenv("GDN_DISABLE_MFMA", "1")
-    assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "simt"
+    assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "mfma_f32"
     o_s, s_s = run_prefill(d, 64)
     check("mfma-vs-simt", "bf16", o_m, o_s, s_m, s_s)
 
@@ -403,11 +402,11 @@ def check_gated(name, dtype, y, y_ref, s, s_ref):
     assert ok, msg
 
 
-@pytest.mark.parametrize("route", ["fused", "split", "simt"])
+@pytest.mark.parametrize("route", ["fused", "split", "f32"])
 @pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
                                            (64, 64, 200, 2, 4), (128, 128, 1, 1, 2)])
 @pytest.mark.parametrize("per_head", [False, True])
-def test_chunk_gated_small(route, dk, dv, T, Hqk, Hv, per_head, monkeypatch):
+def test_chunk_gated_small(route, dk, dv, T, Hqk, Hv, per_head, monkeypatch, hooks):
     """Every route of gdn_chunk_fwd_gated against the oracle's recurrence followed by the
     oracle's gated RMSNorm, and bit for bit against gdn_chunk_fwd then gdn_gated_rmsnorm."""
     if route == "fused":
@@ -448,7 +447,7 @@ def test_chunk_gated_f32_and_in_place():
 
 
 @pytest.mark.parametrize("route", ["fused", "split"])
-def test_chunk_gated_bf16_in_place_and_empty(route, monkeypatch):
+def test_chunk_gated_bf16_in_place_and_empty(route, monkeypatch, hooks):
     monkeypatch.setenv("GDN_MFMA_PATH", route)
     monkeypatch.setenv("GDN_MFMA_BV", "128")
     d = gi.generate(B=1, T=150, Hqk=1, Hv=2, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=8)
@@ -468,7 +467,7 @@ def test_chunk_gated_bf16_in_place_and_empty(route, monkeypatch):
 
 def test_chunk_gated_batched_full():
     """The many-chain workload at full size on the fused route: bit for bit equal to the two
-    calls one after the other, and sampled chains against the oracle."""
+    calls one after the other, and against the oracle over whole tensors."""
     cfg = gi.CONFIGS["batched_prefill"]
     assert gdn.gdn_chunk_fwd_gated_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, 64, gdn.GDN_BF16) == 0
     say(f"gated batched full {cfg}")
@@ -480,14 +479,12 @@ def test_chunk_gated_batched_full():
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(sf, sf2)
     del o, y2, sf2
-    chains = [(0, 0), (6, 13), (7, 31)]
-    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
-    o_ref, s_ref = oracle_prefill(sd)
-    z_s = np.stack([f64(gz["z"][b, :, j]) for b, j in chains])[:, :, None]
-    y_ref = oracle.gated_rmsnorm(o_ref, z_s, gz["weight"])
-    yh = np.stack([host(y[b, :, j]) for b, j in chains])[:, :, None]
-    sh = np.stack([host(sf[b, j]) for b, j in chains])[:, None]
-    check_gated("gated batched sampled", "bf16", yh, y_ref, sh, s_ref)
+    yh, sh = host(y), host(sf)
+    del y, sf, t, tz
+    o_ref, s_ref = oracle_prefill(d)
+    y_ref = oracle.gated_rmsnorm(o_ref, f64(gz["z"]), gz["weight"])
+    del o_ref
+    check_gated("gated batched", "bf16", yh, y_ref, sh, s_ref)
 
 
 def test_chunk_gated_qwen3next_full():

@@ -2,13 +2,13 @@
 (gdn_chunk_transport) against the float64 oracle on the same seeded inputs: several segment
 counts (one chunk per segment, uneven last segments, more segments asked than chunks), ragged T,
 grouped heads, scale, an initial state, in place; maps against oracle.transport, including T = 0;
-the scan against the unsegmented call; the 64K-token workloads at full size on sampled chains."""
+the scan against the unsegmented call; the 64K-token workloads at full size over whole tensors."""
 import numpy as np
 import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import check, dev, f64, host, rel_l2, sample_chains, say
+from gpu_util import check, dev, f64, host, rel_l2, say
 
 gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
 torch = pytest.importorskip("torch")
@@ -128,23 +128,19 @@ def test_transport_empty():
 
 # ------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name,segments,chains", [
-    ("qwen36_long_prefill_tp8", 6, [(0, 0), (0, 5)]),
-    ("qwen36_long_prefill", 4, [(0, 0), (0, 47)]),
-])
-def test_scan_long_sampled(name, segments, chains):
+@pytest.mark.parametrize("name,segments", [("qwen36_long_prefill_tp8", 6), ("qwen36_long_prefill", 4)])
+def test_scan_long_full(name, segments):
+    """The scan on one GPU's share of the 64K-token workload under an 8-way head split and on the
+    whole workload, against the oracle over whole tensors."""
     cfg = gi.CONFIGS[name]
-    say(f"scan {cfg} segments={segments}, sampled chains {chains}")
+    say(f"scan {cfg} segments={segments}, whole tensors")
     d = gi.generate(cfg)
     o, s = run_scan(d, segments)
-    sd = sample_chains(d, chains, cfg.Hqk, cfg.Hv)
-    o_ref, s_ref = oracle_prefill(sd)
-    o_s = np.stack([o[b, :, j] for b, j in chains])[:, :, None]
-    s_s = np.stack([s[b, j] for b, j in chains])[:, None]
-    check(f"{name} scan", "bf16", o_s, o_ref, s_s, s_ref)
+    o_ref, s_ref = oracle_prefill(d)
+    check(f"{name} scan", "bf16", o, o_ref, s, s_ref)
 
 
-def test_chunk_fwd_picks_the_scan_for_scarce_long_chains(monkeypatch):
+def test_chunk_fwd_picks_the_scan_for_scarce_long_chains(monkeypatch, hooks):
     """B1 T17000, 2 value heads of d 64: gdn_chunk_fwd runs the scan by itself (33 segments);
     against the oracle, and against the unsegmented call forced by GDN_SCAN_SEGMENTS=0."""
     assert gdn.gdn_chunk_fwd_kernel_name(1, 17000, 1, 2, 64, 64, 64, gdn.GDN_BF16) == "mfma_scan"

@@ -46,25 +46,25 @@ def oracle_varlen(d, cu):
     return np.concatenate(os_, axis=0), np.stack(ss)
 
 
-ROUTES = {"fused": dict(GDN_MFMA_PATH="fused"), "split": dict(GDN_MFMA_PATH="split"), "simt": dict(GDN_DISABLE_MFMA="1")}
+ROUTES = {"fused": dict(GDN_MFMA_PATH="fused"), "split": dict(GDN_MFMA_PATH="split"), "f32": dict(GDN_DISABLE_MFMA="1")}
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
-def test_varlen_matches_oracle(route, dk, dv, monkeypatch):
+def test_varlen_matches_oracle(route, dk, dv, monkeypatch, hooks):
     for k_, v_ in ROUTES[route].items():
         monkeypatch.setenv(k_, v_)
     lengths = [37, 1, 0, 64, 65, 150, 129]
-    dtype = "f32" if route == "simt" else "bf16"
+    dtype = "f32" if route == "f32" else "bf16"
     say(f"varlen {route} dk={dk} dv={dv} lengths={lengths}")
     d, cu = packed(lengths, 2, 4, dk, dv, dtype, seed=dk + dv)
-    o, s = run_varlen(d, cu, max(lengths), 64 if route != "simt" else 32)
+    o, s = run_varlen(d, cu, max(lengths), 64 if route != "f32" else 32)
     o_ref, s_ref = oracle_varlen(d, cu)
     check(f"varlen {route}", dtype, o, o_ref, s, s_ref)
 
 
 @pytest.mark.parametrize("route", ["fused", "split"])
-def test_varlen_equal_lengths_equal_batched(route, monkeypatch):
+def test_varlen_equal_lengths_equal_batched(route, monkeypatch, hooks):
     """Equal lengths L: the same bits as gdn_chunk_fwd over B = N rows of L tokens."""
     monkeypatch.setenv("GDN_MFMA_PATH", route)
     N, L, Hqk, Hv, d_ = 3, 200, 2, 4, 128
@@ -95,7 +95,8 @@ def test_varlen_all_empty_and_out_of_contract_offsets():
         import os
         os.environ["GDN_MFMA_PATH"] = route
         try:
-            gdn.gdn_chunk_fwd_varlen(t["q"], t["k"], t["v"], t["g"], t["beta"], bad, 2, s3)
-            torch.cuda.synchronize()
+            with gdn.test_hooks():
+                gdn.gdn_chunk_fwd_varlen(t["q"], t["k"], t["v"], t["g"], t["beta"], bad, 2, s3)
+                torch.cuda.synchronize()
         finally:
             del os.environ["GDN_MFMA_PATH"]
