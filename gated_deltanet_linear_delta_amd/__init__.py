@@ -33,18 +33,20 @@ __all__ = [
     "gdn_chunk_fwd_gated_workspace_bytes", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
     "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
     "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments", "gdn_chunk_transport",
-    "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS", "test_hooks",
+    "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS", "test_hooks", "gdn_chunk_fwd_noalloc",
+    "GDN_NOALLOC_SCRATCH_BYTES",
 ]
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/gdn.h
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
                     "gdn_chunk_fwd_kernel_name", "gdn_status_string", "gdn_qkv_prologue",
                     "gdn_gated_rmsnorm", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_gated_workspace_bytes",
                     "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes", "gdn_kda_chunk_fwd",
                     "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
                     "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments",
-                    "gdn_chunk_transport", "gdn_chunk_transport_workspace_bytes")
+                    "gdn_chunk_transport", "gdn_chunk_transport_workspace_bytes", "gdn_chunk_fwd_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _libs = {}
@@ -128,6 +130,8 @@ def load_library(variant: str | None = None):
     lib.gdn_chunk_transport.restype = i
     lib.gdn_chunk_transport_workspace_bytes.argtypes = [i] * 7 + [i]
     lib.gdn_chunk_transport_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp] + [i] * 7 + [i, f, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i
     _libs[v] = lib
     return lib
 
@@ -243,6 +247,34 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, output_final_state=True,
                            float(scale), _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, o, final_state=None, chunk=64, scale=1.0,
+                          stream=None):
+    """Prefill through gdn_chunk_fwd_noalloc: as :func:`gdn_chunk_fwd`, with the workspace in the
+    library's fixed per-device array.  The caller passes every output (``o``, and ``final_state``
+    or None); this wrapper allocates nothing.  Returns (o, final_state)."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dev = q.device
+    _check_dense("q", q, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("k", k, (B, T, Hqk, dk), q.dtype, dev)
+    _check_dense("v", v, (B, T, Hv, dv), q.dtype, dev)
+    _check_dense("g", g, (B, T, Hv), torch.float32, dev)
+    _check_dense("beta", beta, (B, T, Hv), torch.float32, dev)
+    if initial_state is not None:
+        _check_dense("initial_state", initial_state, (B, Hv, dk, dv), torch.float32, dev)
+    _check_dense("o", o, (B, T, Hv, dv), q.dtype, dev)
+    if final_state is not None:
+        _check_dense("final_state", final_state, (B, Hv, dk, dv), torch.float32, dev)
+    st = lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                   _ptr(final_state), _ptr(o), B, T, Hqk, Hv, dk, dv, int(chunk), _dtype_code(q),
+                                   float(scale), _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 LIB_HOOKS = os.path.join(PKG, "libgdn_hooks.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip", "kda.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip", "kda.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 instructions are kept out of the generated code (plain float code only).

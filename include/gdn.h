@@ -121,6 +121,31 @@ gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            gdn_dtype_t dtype, float scale, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Size of the fixed device array gdn_chunk_fwd_noalloc uses as its workspace (64 MiB per device). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate device memory (code
+ * under HIP stream or graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results, with no workspace argument.  Where gdn_chunk_fwd needs
+ * a workspace, this call uses a fixed array of GDN_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each device it runs on (from the time its code is loaded there until the process ends); it
+ * calls no allocating routine.  The array's device address is looked up once per device, on the
+ * first call that needs it.
+ *   every argument       as gdn_chunk_fwd (caller-owned inputs and outputs; `stream`'s device,
+ *                        or the current device for the null stream, runs the work)
+ * Limit: sizes for which gdn_chunk_fwd_workspace_bytes exceeds GDN_NOALLOC_SCRATCH_BYTES return
+ * GDN_ERR_WORKSPACE before anything is enqueued (the fused and float32 routes need none, so
+ * only the split and scan routes of long sequences with few chains can hit it).  All calls on one
+ * device share that device's array and each leaves its contents behind (nothing in it needs to
+ * start at zero): calls on one device that overlap in time (other streams, other threads) race
+ * on it and must be serialised by the caller.  Other errors as gdn_chunk_fwd.
+ */
+gdn_status_t gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, const float* initial_state, float* final_state,
+                                   void* o, int B, int T, int Hqk, int Hv, int dk, int dv, int chunk,
+                                   gdn_dtype_t dtype, float scale, void* stream);
+
 /*
  * gdn_recurrent_step -- decode: one token per sequence, state updated in place.
  *
