@@ -902,7 +902,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
 {
-    const int NT = (a.T + BW_C - 1) / BW_C;
+    const int NT = (int)(((long)a.T + BW_C - 1) / BW_C);
     float* Hs = a.ws;
     float* dHs = a.ws + (size_t)a.B * a.Hv * NT * DK * DV;
     float* Aw = dHs + (size_t)a.B * a.Hv * NT * DK * DV;

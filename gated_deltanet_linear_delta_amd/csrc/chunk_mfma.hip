@@ -1746,7 +1746,7 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st, SegArgs 
     const long nblk = (long)a.B * a.Hv * NTILE;
     const long per_xcd = nblk / 8;
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * NTILE) == 0) ? 1 : 0;
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk, (unsigned)nseg), dim3((SLW + NW + 1) * 64), L::bytes, st,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0,
@@ -1758,7 +1758,7 @@ template <int DK, bool VARLEN>
 hipError_t launch_prep_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
     const int grp = a.Hv / a.Hqk;
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     const long nprep = (long)a.B * a.Hqk * NT;
     unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL((chunk_prep_kernel<DK, VARLEN>), dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
@@ -1773,7 +1773,7 @@ hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
     if (!VARLEN && a.cu) return launch_split_t<DK, DV, true>(a, ws, st);
     hipError_t e = launch_prep_t<DK, VARLEN>(a, ws, st);
     if (e != hipSuccess) return e;
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     const SegArgs whole{NT, nullptr, nullptr, nullptr};
     if (choose_split_bv(a) == 16) return launch_state_t<DK, DV, 1, VARLEN>(a, ws, st, whole, 1);
     return launch_state_t<DK, DV, 2, VARLEN>(a, ws, st, whole, 1);
@@ -1843,7 +1843,7 @@ struct ScanLayout {
 ScanLayout scan_layout(const ChunkArgs& a, int segments)
 {
     ScanLayout s{};
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     s.L = (NT + segments - 1) / segments;
     s.P = (NT + s.L - 1) / s.L;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1892,7 +1892,7 @@ hipError_t launch_transport_t(const ChunkArgs& a, float* m_out, float* n_out, vo
 {
     hipError_t e = launch_prep_t<DK, false>(a, ws, st);
     if (e != hipSuccess) return e;
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     const SegArgs xs{NT, nullptr, m_out, n_out};
     return (long)a.B * a.Hv * ((DV + DK) / 16) <= 256 ? launch_state_t<DK, DV, 1, false, true>(a, ws, st, xs, 1)
                                                       : launch_state_t<DK, DV, 2, false, true>(a, ws, st, xs, 1);
@@ -2376,7 +2376,7 @@ __global__ __launch_bounds__(256) void kda_state_kernel(const bf16* __restrict__
 template <typename T, int DK, int DV>
 hipError_t launch_kda_mfma_t(const KdaArgs& a, void* ws, hipStream_t st)
 {
-    const int NT = (a.T + CH - 1) / CH;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
     const int grp = a.Hv / a.Hqk;
     auto prep = kda_prep_kernel<T, DK>;
     constexpr size_t pl = kda_prep_lds_bytes<DK>();

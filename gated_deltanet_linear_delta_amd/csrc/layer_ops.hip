@@ -221,7 +221,7 @@ hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t st)
     constexpr int CB = 64 * Vec<T>::N;
     const long cq = (long)a.Hqk * a.dk, cv = (long)a.Hv * a.dv;
     const long nb = 2 * ((cq + CB - 1) / CB) + (cv + CB - 1) / CB;
-    const long nwaves = (long)a.B * nb * ((a.T + PTT - 1) / PTT);
+    const long nwaves = (long)a.B * nb * (((long)a.T + PTT - 1) / PTT);
     if (nwaves == 0) return hipSuccess;
     if (nwaves > INT32_MAX - 3) return hipErrorInvalidValue;
     const unsigned nblk = (unsigned)((nwaves + 3) / 4);
@@ -242,7 +242,7 @@ hipError_t launch_rmsnorm_t(const RmsNormArgs& a, hipStream_t st)
 {
     constexpr int CB = 64 * Vec<T>::N;
     const long cn = (long)a.Hv * a.dv;
-    const long nwaves = (long)a.B * ((cn + CB - 1) / CB) * ((a.T + RTT - 1) / RTT);
+    const long nwaves = (long)a.B * (((long)cn + CB - 1) / CB) * (((long)a.T + RTT - 1) / RTT);
     if (nwaves == 0) return hipSuccess;
     if (nwaves > INT32_MAX - 3) return hipErrorInvalidValue;
     const unsigned nblk = (unsigned)((nwaves + 3) / 4);
