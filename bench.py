@@ -105,6 +105,7 @@ def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
 # What one gdn_chunk_fwd launches, per kernel family; the roofline is taken over the whole call
 # (HIP events around it on its stream), i.e. over both kernels of the split path.
 KERNELS = {"mfma": "chunk_mfma_kernel",
+           "mfma_pipe": "chunk_pipe_kernel",
            "mfma_split": "chunk_prep_kernel + chunk_state_kernel",
            "mfma_f32": "chunk_simt_kernel (float32 matrix-core products)"}
 

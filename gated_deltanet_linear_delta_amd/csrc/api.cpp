@@ -90,7 +90,7 @@ const char* gdn_chunk_fwd_kernel_name(int B, int T, int Hqk, int Hv, int dk, int
                                        nullptr, B, T, Hqk, Hv, dk, dv, chunk, dtype, 1.f);
     if (!gdn::chunk_mfma_supported(a)) return "mfma_f32";
     if (gdn::chunk_auto_segments(a) > 1) return "mfma_scan";
-    return gdn::chunk_mfma_split(a) ? "mfma_split" : "mfma";
+    return gdn::chunk_mfma_split(a) ? "mfma_split" : gdn::chunk_mfma_pipe(a) ? "mfma_pipe" : "mfma";
 }
 
 gdn_status_t gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,

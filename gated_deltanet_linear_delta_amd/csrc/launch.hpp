@@ -49,11 +49,13 @@ hipError_t launch_recurrent_step(const StepArgs& a, hipStream_t st);
 // Float32-vector chunkwise kernel: any supported dtype, head dims and chunk size.
 hipError_t launch_chunk_simt(const ChunkArgs& a, hipStream_t st);
 
-// Matrix-core chunkwise path: bf16 inputs and the shapes chunk_mfma_supported accepts.  Either
-// one fused kernel, or (chunk_mfma_split) a parallel per-chunk prep kernel that fills a
-// workspace of chunk_mfma_workspace_bytes followed by the state-pass kernel.
+// Matrix-core chunkwise path: bf16 inputs and the shapes chunk_mfma_supported accepts.  One
+// fused kernel (with the state-independent part of each chunk built inside it by prep waves:
+// chunk_mfma_pipe for the pipelined one), or (chunk_mfma_split) a parallel per-chunk prep kernel
+// that fills a workspace of chunk_mfma_workspace_bytes followed by the state-pass kernel.
 bool chunk_mfma_supported(const ChunkArgs& a);
 bool chunk_mfma_split(const ChunkArgs& a);
+bool chunk_mfma_pipe(const ChunkArgs& a);
 // The gated RMSNorm can run inside the fused kernel (whole value heads per workgroup).
 bool chunk_mfma_gated_fused(const ChunkArgs& a);
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a);

@@ -40,9 +40,9 @@ def test_status_strings_and_queries():
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 64 * per_chunk
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4097, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 65 * per_chunk
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
-    # fused path (many chains) and the float32 path need none
+    # pipelined fused path (many chains) and the float32 path need none
     assert gdn.gdn_chunk_fwd_workspace_bytes(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == 0
-    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
+    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_pipe"
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == 0
     assert gdn.gdn_chunk_fwd_workspace_bytes(1, 4096, 16, 33, 128, 128, 64, gdn.GDN_BF16) == 0
     assert gdn.gdn_chunk_fwd_kernel_name(1, 128, 2, 2, 32, 32, 16, gdn.GDN_F32) == "mfma_f32"

@@ -3,7 +3,7 @@
 "Gated Attention Architectures", section 3 (Gated DeltaNet, description): alpha -> 0 clears the
 memory and alpha = 1 gives back the pure delta rule; section 2: beta in (0, 1) is the writing
 strength, so beta = 0 writes nothing (the state only decays) and beta = 1 overwrites the value
-stored under the key.  Each case runs on the fused and split matrix-core kernels, the affine
+stored under the key.  Each case runs on the fused, pipelined and split matrix-core kernels, the affine
 chunk scan, the float32 kernel and the decode step, with a nonzero initial state, several chunks
 and a ragged tail, and guard bands after every output.  The operand-range case runs |v| and
 |S0| near the limit the header states for the float16 operands of the matrix-core routes.  The
@@ -20,7 +20,7 @@ gdn = pytest.importorskip("gated_deltanet_linear_delta_amd")
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-ROUTES = ("fused", "split", "scan", "f32", "decode")
+ROUTES = ("fused", "split", "pipe", "scan", "f32", "decode")
 
 
 def limit_case(case, dtype, T, seed):
@@ -55,12 +55,12 @@ def run_route(route, d, hooks_env, monkeypatch):
     # decode writes one [B, Hv, dv] output per step: step-major there, token-major elsewhere
     og = Guarded((T, B, Hv, dv) if route == "decode" else (B, T, Hv, dv), tdt)
     sg = Guarded((B, Hv, dk, dv), torch.float32)
-    if route in ("fused", "split"):
+    if route in ("fused", "split", "pipe"):
         monkeypatch.setenv("GDN_MFMA_PATH", route)
         monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")
         with hooks_env():
             assert gdn.gdn_chunk_fwd_kernel_name(B, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16) == \
-                ("mfma" if route == "fused" else "mfma_split")
+                {"fused": "mfma", "split": "mfma_split", "pipe": "mfma_pipe"}[route]
             gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64, o=og.t, final_state=sg.t)
     elif route == "scan":
         gdn.gdn_chunk_fwd_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], segments=3, o=og.t,
@@ -107,7 +107,7 @@ def test_beta0_is_pure_decay_closed_form():
     check("beta0 closed form", "bf16", o, o_cf, s, s_cf)
 
 
-@pytest.mark.parametrize("route", ["fused", "split", "scan"])
+@pytest.mark.parametrize("route", ["fused", "split", "pipe", "scan"])
 def test_fp16_operand_range(route, monkeypatch):
     """|v| and |S0| near 2^10 (v ~ 256 N(0,1), S0 ~ 256 N(0,1)): the float16 operands of the
     matrix-core routes stay in range and the bf16 tolerance holds (relative measures)."""

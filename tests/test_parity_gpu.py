@@ -198,7 +198,7 @@ def test_decode_config_full():
 
 def test_kernel_family_dispatch():
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_split"
-    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
+    assert gdn.gdn_chunk_fwd_kernel_name(8, 8192, 16, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_pipe"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 32, gdn.GDN_BF16) == "mfma_f32"
     assert gdn.gdn_chunk_fwd_kernel_name(1, 4096, 16, 32, 128, 128, 64, gdn.GDN_F32) == "mfma_f32"
 
@@ -222,6 +222,26 @@ def test_mfma_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch, hooks):
     check(f"mfma bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
 
 
+@pytest.mark.parametrize("bv", ["16", "32", "64", "128"])
+@pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
+                                            (64, 64, 1, 1, 1), (128, 128, 700, 1, 1), (128, 128, 127, 1, 3)])
+def test_pipe_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch, hooks):
+    """The pipelined fused kernel (prep waves build chunk n + 1 while the chain waves carry chunk
+    n) at every column-tile width, with grouped heads, a ragged last chunk, a nonzero initial
+    state and a scale."""
+    if int(bv) > dv:
+        pytest.skip("tile wider than dv")
+    monkeypatch.setenv("GDN_MFMA_PATH", "pipe")
+    monkeypatch.setenv("GDN_PIPE_BV", bv)
+    say(f"pipe bv={bv} dk={dk} dv={dv} T={T} Hqk={Hqk} Hv={Hv}")
+    assert gdn.gdn_chunk_fwd_kernel_name(2, T, Hqk, Hv, dk, dv, 64, gdn.GDN_BF16) == "mfma_pipe"
+    d = gi.generate(B=2, T=T, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, dtype="bf16", mu=3.0, s0_std=0.05, seed=T + dk + 2)
+    sc = 0.5 if T == 129 else 1.0
+    o_ref, s_ref = oracle_prefill(d, scale=sc)
+    o, s = run_prefill(d, 64, scale=sc)
+    check(f"pipe bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
+
+
 @pytest.mark.parametrize("bv", ["16", "32"])
 @pytest.mark.parametrize("dk,dv,T,Hqk,Hv", [(128, 128, 333, 2, 6), (64, 128, 129, 1, 2), (128, 64, 64, 2, 2),
                                             (64, 64, 1, 1, 1), (128, 128, 700, 1, 1), (128, 128, 127, 1, 3)])
@@ -242,7 +262,7 @@ def test_split_tile_widths(bv, dk, dv, T, Hqk, Hv, monkeypatch, hooks):
     check(f"split bv={bv} dk={dk} dv={dv} T={T}", "bf16", o, o_ref, s, s_ref)
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "split", "pipe"])
 @pytest.mark.parametrize("mu", [3.0, 8.0])
 def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch, hooks):
     """All keys of a head equal: the strictly-lower A of every chunk is dense, so every block of
@@ -256,13 +276,14 @@ def test_mfma_identical_keys_dense_solve(mu, path, monkeypatch, hooks):
     check(f"identical keys mu={mu}", "bf16", o, o_ref, s, s_ref)
 
 
-@pytest.mark.parametrize("path", ["fused", "split"])
+@pytest.mark.parametrize("path", ["fused", "split", "pipe"])
 def test_mfma_matches_simt(path, monkeypatch, hooks):
     """Two independent GPU implementations of the chunk algebra agree (and both match the oracle)."""
     say(f"mfma ({path}) vs simt")
     d = gi.generate(B=2, T=500, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=41)
     monkeypatch.setenv("GDN_MFMA_PATH", path)
-    assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == ("mfma" if path == "fused" else "mfma_split")
+    assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == \
+        {"fused": "mfma", "split": "mfma_split", "pipe": "mfma_pipe"}[path]
     o_m, s_m = run_prefill(d, 64)
     monkeypatch.setenv("GDN_DISABLE_MFMA", "1")
     assert gdn.gdn_chunk_fwd_kernel_name(2, 500, 2, 4, 128, 128, 64, gdn.GDN_BF16) == "mfma_f32"
@@ -465,9 +486,11 @@ def test_chunk_gated_bf16_in_place_and_empty(route, monkeypatch, hooks):
     assert ye.numel() == 0 and torch.equal(se, t["s0"])
 
 
-def test_chunk_gated_batched_full():
-    """The many-chain workload at full size on the fused route: bit for bit equal to the two
-    calls one after the other, and against the oracle over whole tensors."""
+def test_chunk_gated_batched_full(monkeypatch, hooks):
+    """The many-chain workload at full size with the gated epilogue inside the fused kernel: bit
+    for bit equal to that kernel's plain call followed by gdn_gated_rmsnorm, and against the
+    oracle over whole tensors."""
+    monkeypatch.setenv("GDN_MFMA_PATH", "fused")
     cfg = gi.CONFIGS["batched_prefill"]
     assert gdn.gdn_chunk_fwd_gated_workspace_bytes(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, 64, gdn.GDN_BF16) == 0
     say(f"gated batched full {cfg}")

@@ -47,7 +47,7 @@ def test_noalloc_matches_chunk_fwd_twice_split_route():
 
 def test_noalloc_fused_route_and_in_place_state():
     d = gi.generate(B=8, T=300, Hqk=8, Hv=32, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=13)
-    assert gdn.gdn_chunk_fwd_kernel_name(8, 300, 8, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma"
+    assert gdn.gdn_chunk_fwd_kernel_name(8, 300, 8, 32, 128, 128, 64, gdn.GDN_BF16) == "mfma_pipe"
     o, s, o_ref, s_ref = both(d)
     assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
     t = dev(d)
