@@ -54,6 +54,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gated_norm.hpp"
 #include "launch.hpp"
@@ -123,7 +125,7 @@ constexpr int V_BEG = 1;   // beta exp(gc)
 constexpr int V_ED = 2;    // exp(gc_63 - gc)
 constexpr int V_EC = 3;    // exp(gc_63) (every element)
 constexpr int V_EG = 4;    // scale exp(gc)
-constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk; fused prep only)
+constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk)
 
 // Workspace of the split path, per (batch, value head, chunk), in two parts: what the state step
 // reads (T, then the rows V_B..V_EC) and what the output step reads (Aqk, then the row V_EG).
@@ -1636,20 +1638,22 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
 }
 
 // Split path, kernel 2: the state pass.  One workgroup per (batch, value head, column tile of
-// BV = 16 NW columns) with SLW loader waves, NW chain waves (16 state columns each) and one
-// output wave, one barrier per chunk.
+// BV = 16 NW columns) with SLW loader waves, NW chain waves (16 state columns each) and SOW
+// output waves, one barrier per chunk.  The chain waves are the critical path; every other role
+// is sized to finish inside their period.
 // * Loaders stage chunk n + 1's K (q, k converted to column-permuted float16), V and state-step
-//   vectors into double-buffered LDS while the chain waves carry chunk n, and prefetch chunk
-//   n + 2 into registers.  That is all that goes through LDS besides the hand-over below: LDS
-//   bandwidth is what a chunk's latency is most sensitive to.
+//   vectors into double-buffered LDS while the chain waves carry chunk n, from registers loaded
+//   two chunks ahead (one chunk ahead left the staging waiting on the loads).  That is all that
+//   goes through LDS besides the hand-over below: LDS bandwidth is what a chunk's latency is most
+//   sensitive to.
 // * A chain wave reads T straight from the workspace in fragment order (16-byte coalesced loads,
 //   one chunk ahead, double-buffered in registers over a two-chunk loop), runs the Delta and
-//   update phases, and hands its packed h and Delta to its output wave through LDS.
-// * The output wave forms O of chunk n - 1 for every column group in iteration n from those
-//   hand-overs and Q, Aqk and scale exp(gc) read from the workspace in fragment order (one copy
-//   for the whole tile: vector-memory issue per compute unit is a limit here), double-buffered
-//   two chunks ahead.
+//   update phases, and hands its packed h and Delta to the output waves through LDS.
+// * Each output wave forms two token tiles of O of chunk n - 1, for every column group, in
+//   iteration n from those hand-overs and Q, Aqk and scale exp(gc) read from the workspace in
+//   fragment order, double-buffered two chunks ahead.
 constexpr int SLW = 2;   // loader waves of the state pass
+constexpr int SOW = 2;   // output waves of the state pass (two token tiles of every chunk each)
 
 // Segments of a chain (the affine chunk scan).  Over a chunk the state map is affine,
 // h_out = M h_in + N with M = e^gL I - K~^T W and N = K~^T U (the WY form of the chunk,
@@ -1672,23 +1676,27 @@ template <int DK, int BV, int NW>
 struct SLds {
     static constexpr int KP = DK + 8;
     static constexpr int VP = BV + 16;
-    static constexpr size_t k = 0;                                   // K   [64][KP] f16
-    static constexpr size_t v = k + (size_t)CH * KP * 2;             // V   [64][VP] bf16
-    static constexpr size_t cv = v + (size_t)CH * VP * 2;            // rows V_B..V_EC, f32
-    static constexpr size_t cslot = cv + (size_t)4 * CH * 4;
+    // K, V and the state-step vectors in two slots: the chain waves read chunk n while the
+    // loaders stage chunk n + 1
+    static constexpr size_t kbytes = (size_t)CH * KP * 2;
+    static constexpr size_t vbytes = (size_t)CH * VP * 2;
+    static constexpr size_t cvbytes = (size_t)4 * CH * 4;
+    static constexpr size_t k = 0;                                   // K   [2][64][KP] f16
+    static constexpr size_t v = k + 2 * kbytes;                      // V   [2][64][VP] bf16
+    static constexpr size_t cv = v + 2 * vbytes;                     // rows V_B..V_EC [2][4][64] f32
     // chain -> output hand-over, [2][NW]: hb (DK/32 fragments) then db (2), each fragment 64
     // lanes x 16 bytes
     static constexpr size_t hx_frags = DK / 32 + 2;
-    static constexpr size_t hx = 2 * cslot;
+    static constexpr size_t hx = cv + 2 * cvbytes;
     static constexpr size_t bytes = hx + 2 * NW * hx_frags * 1024;
+    static_assert(v % 16 == 0 && cv % 16 == 0 && hx % 16 == 0, "16-byte aligned parts");
 };
 
 template <int DK, int DV, int NW, bool VARLEN, bool XPORT = false>
-__global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const unsigned char* __restrict__ ws, const unsigned char* __restrict__ wsq, const float* s0,
-    float* sf, bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, int xcd_remap, const int* cu, int total,
-    SegArgs sg)
+__global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const unsigned char* __restrict__ ws,
+    const unsigned char* __restrict__ wsq, const float* s0, float* sf, bf16* __restrict__ o, int T_max, int Hqk,
+    int Hv, int grp, int xcd_remap, const int* cu, int total, SegArgs sg)
 {
     constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
@@ -1701,7 +1709,7 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     constexpr int PK = CH * RP / NLT;                   // pair-runs per loader lane
     constexpr int RV = BV / 8;                          // 16-byte runs per V row
     constexpr int PV = (CH * RV + NLT - 1) / NLT;       // V runs per loader lane
-    constexpr int CVR = 4 * CH * 4 / 16;                // 16-byte runs of the state vectors
+    constexpr int CVR = 4 * CH * 4 / 16;                // 16-byte runs of the state-step vectors
     static_assert(PK >= 1 && CH * RP % NLT == 0 && CVR <= NLT, "tile shape");
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1713,18 +1721,21 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     const int lane = tid & 63;
     const int ln = lane & 15;
     const int lg = lane >> 4;
-    // Roles by wave index, so that consecutive waves (which land on consecutive SIMDs) give each
-    // chain wave and the output wave a SIMD of its own and the two loaders share one: wave 0
-    // and wave NW + 2 load, waves 1..NW carry the chains, wave NW + 1 forms O.
-    const int li = w == 0 ? 0 : w - (NW + 1);   // loader index (loader waves only)
-    const bool is_loader = w == 0 || w == NW + 2;
-    const bool is_chain = w >= 1 && w <= NW;
+    // Roles by wave index.  Wave w runs on SIMD w % 4, and the chain waves (the latency-bound
+    // critical path) get SIMDs of their own: waves 0 and 1 form O, waves 2 .. NW + 1 carry the
+    // chains, waves NW + 2 and NW + 3 load (the two output waves and the two loaders each on
+    // different SIMDs).
+    static_assert(SLW == 2 && SOW == 2 && NW <= 2, "wave roles");
+    const bool is_chain = w >= 2 && w < 2 + NW;
+    const bool is_loader = w >= 2 + NW;
+    const int li = w - (2 + NW);     // loader index (loader waves)
+    const int cw = w - 2;            // chain wave index (chain waves)
     const size_t head = (size_t)b * Hv + j;
     SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
     if (VARLEN && sq.len == 0) {
         // an empty sequence: the final state is the initial one (every wave leaves here, before
         // any barrier)
-        if (is_chain) copy_state_cols<DK, DV>(s0, sf, head, c0 + (w - 1) * 16, 16, lane);
+        if (is_chain) copy_state_cols<DK, DV>(s0, sf, head, c0 + cw * 16, 16, lane);
         return;
     }
     // this workgroup's segment: chunks cb .. cb + NT - 1 of the row, a shorter sequence that
@@ -1743,7 +1754,9 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
     const size_t v_row = (size_t)Hv * DV;
     const unsigned char* wh = ws + (head * NTS + cb) * WS_CHUNK;
     const bool mcols = XPORT && c0 >= DV;       // transport columns of M: V is zero
-    auto cslot = [&](int c) { return smem + (size_t)(c & 1) * L::cslot; };
+    auto kslot = [&](int c) { return reinterpret_cast<op_t*>(smem + L::k + (size_t)(c & 1) * L::kbytes); };
+    auto vslot = [&](int c) { return reinterpret_cast<bf16*>(smem + L::v + (size_t)(c & 1) * L::vbytes); };
+    auto cvslot = [&](int c) { return reinterpret_cast<float*>(smem + L::cv + (size_t)(c & 1) * L::cvbytes); };
     auto hxp = [&](int c, int cw) {
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
     };
@@ -1754,9 +1767,12 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
         const bf16* kb_ = k + (sq.tok0 * Hqk + i) * DK;
         const bf16* vb = v + (sq.tok0 * Hv + j) * DV + (mcols ? 0 : c0);
         const int vrow = Hv * DV;
-        bf16x8 rk[PK][2];
-        bf16x8 rv[PV];
-        floatx4 rc = {};
+        // one chunk's loads; two in flight, so each has two periods to arrive
+        struct LdBuf {
+            bf16x8 rk[PK][2];
+            bf16x8 rv[PV];
+            floatx4 rc;
+        };
         // K pair-run s of a chunk: row s / RP, 32-column block pr / 2 (pr = s % RP), half
         // a = pr % 2.  Two 16-byte loads (logical columns 32 blk + 8a .. +7 and the same + 16)
         // hold exactly the physical runs 4 blk + 2a and + 1 of the column-permuted row, which sit
@@ -1770,68 +1786,75 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
             kq_r[p] = s / RP;
             kq_c[p] = 32 * (pr >> 1) + 8 * (pr & 1);
         }
-        auto load_chain = [&](int c) {
+        auto load_chain = [&](int c, LdBuf& r) {
             const int t0 = c * CH, n = min(CH, T_len - t0);
             const bf16* kc = kb_ + (size_t)t0 * qk_row;
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
                 const int off = min(kq_r[p], n - 1) * qk_row + kq_c[p];
-                rk[p][0] = *reinterpret_cast<const bf16x8*>(kc + off);
-                rk[p][1] = *reinterpret_cast<const bf16x8*>(kc + off + 16);
+                r.rk[p][0] = *reinterpret_cast<const bf16x8*>(kc + off);
+                r.rk[p][1] = *reinterpret_cast<const bf16x8*>(kc + off + 16);
             }
             const bf16* vc = vb + (size_t)t0 * vrow;
             if (!mcols) {
 #pragma unroll
                 for (int p = 0; p < PV; ++p) {
                     const int s = min(ltid + p * NLT, CH * RV - 1);
-                    rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
+                    r.rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
                 }
             }
-            if (ltid < CVR) rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * ltid);
+            if (ltid < CVR) r.rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * ltid);
         };
-        auto stage_chain = [&](int c) {
-            unsigned char* sb = cslot(c);
-            op_t* Ks = reinterpret_cast<op_t*>(sb + L::k);
-            bf16* Vs = reinterpret_cast<bf16*>(sb + L::v);
+        auto stage_chain = [&](int c, const LdBuf& r) {
+            op_t* Ks = kslot(c);
+            bf16* Vs = vslot(c);
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
                 opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((ltid + p * NLT) % RP));
-                bf16_pair_to_op(rk[p][0], rk[p][1], dst[0], dst[1]);
+                bf16_pair_to_op(r.rk[p][0], r.rk[p][1], dst[0], dst[1]);
             }
             if (!mcols) {
 #pragma unroll
                 for (int p = 0; p < PV; ++p) {
                     const int s = ltid + p * NLT;
-                    if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = rv[p];
+                    if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = r.rv[p];
                 }
             }
-            if (ltid < CVR) *reinterpret_cast<floatx4*>(sb + L::cv + 16 * ltid) = rc;
+            if (ltid < CVR) reinterpret_cast<floatx4*>(cvslot(c))[ltid] = r.rc;
         };
         if (mcols) {
             // the M columns' V is zero in both slots for the whole segment
             for (int s = ltid; s < CH * L::VP / 8; s += NLT)
 #pragma unroll
                 for (int slot = 0; slot < 2; ++slot)
-                    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(cslot(slot) + L::v) + 8 * s) = bf16x8{};
+                    *reinterpret_cast<bf16x8*>(vslot(slot) + 8 * s) = bf16x8{};
         }
         // Prefetches are issued unconditionally (chunk index clamped to the last chunk; the
         // extra loads at the end are harmless) so that every path through the loop has the same
         // memory operations in flight and each wait covers exactly the loads it needs.
-        load_chain(0);
-        stage_chain(0);
-        load_chain(min(1, NT - 1));
+        // iteration n stages chunk n + 1 from buffer (n + 1) % 2, then loads chunk n + 3 into it
+        LdBuf bufA, bufB;
+        load_chain(0, bufA);
+        stage_chain(0, bufA);
+        load_chain(min(1, NT - 1), bufB);
+        load_chain(min(2, NT - 1), bufA);
         lds_barrier();
-        for (int n = 0; n < NT; ++n) {
+        auto step = [&](int n, LdBuf& r) {
             GDN_TRACE(n, 0);
-            if (n + 1 < NT) stage_chain(n + 1);
+            if (n + 1 < NT) stage_chain(n + 1, r);
             GDN_TRACE(n, 1);
-            load_chain(min(n + 2, NT - 1));
+            load_chain(min(n + 3, NT - 1), r);
             GDN_TRACE(n, 2);
             lds_barrier();
+        };
+        int n = 0;
+        for (; n + 1 < NT; n += 2) {
+            step(n, bufB);
+            step(n + 1, bufA);
         }
+        if (n < NT) step(n, bufB);
     } else if (is_chain) {
         // ================================================================= chain waves
-        const int cw = w - 1;
         const int col = c0 + cw * 16;
         floatx4 hacc[1][MT];
         if constexpr (XPORT) {
@@ -1846,7 +1869,7 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
             load_state<DK, DV, 1>(hacc, s0, head, col, lane);
         }
         // T fragments of chunk c (fragment order in the workspace)
-        auto load_tf = [&](int c, opx8 (&t)[6]) {
+        auto load_tf = [&](int c, opx8 (&t)[6], int lane) {
             const opx8* src = reinterpret_cast<const opx8*>(wh + (size_t)c * WS_CHUNK + WS_T);
 #pragma unroll
             for (int bk = 0; bk < 6; ++bk) t[bk] = src[bk * 64 + lane];
@@ -1875,19 +1898,18 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
         };
         auto step = [&](int n, const opx8 (&tc)[6], opx8 (&tn)[6]) {
             GDN_TRACE(n, 0);
+            const int lane = opaque(threadIdx.x & 63);
             float sc = 1.f;
             if (mcols) {
                 sc = col_scale();
                 rescale(sc);
             }
-            load_tf(min(n + 1, NT - 1), tn);   // unconditional: see the loaders
-            const unsigned char* sb = cslot(n);
-            const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
+            load_tf(min(n + 1, NT - 1), tn, lane);   // unconditional: see the loaders
+            const op_t* Ks = kslot(n);
             opx8 hb[1][KB], db[1][2], dtb[1][2];
             opx8 akt[2][MT];
-            chain_delta<DK, 1, L::VP, true>(hacc, Ks, reinterpret_cast<const bf16*>(sb + L::v) + cw * 16,
-                                            [&](int mt, int cb) { return tc[tblk(mt, cb)]; },
-                                            reinterpret_cast<const float*>(sb + L::cv), lane, hb, db, dtb, akt);
+            chain_delta<DK, 1, L::VP, true>(hacc, Ks, vslot(n) + cw * 16, [&](int mt, int cb) { return tc[tblk(mt, cb)]; },
+                                            cvslot(n), lane, hb, db, dtb, akt);
             opx8* hx = hxp(n, cw);
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) hx[kk * 64 + lane] = hb[0][kk];
@@ -1901,7 +1923,7 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
             lds_barrier();
         };
         opx8 tA[6], tB[6];
-        load_tf(0, tA);
+        load_tf(0, tA, lane);
         lds_barrier();
         int n = 0;
         for (; n + 1 < NT; n += 2) {
@@ -1921,93 +1943,109 @@ __global__ __launch_bounds__((SLW + NW + 1) * 64) __attribute__((amdgpu_waves_pe
         // no output: the same barriers as the other roles
         for (int n = 0; n <= NT; ++n) lds_barrier();
     } else {
-        // ================================================================= output wave
-        bf16* ob = o + (sq.tok0 * Hv + j) * DV + c0;
-        const unsigned char* wqh = wsq + (((size_t)b * Hqk + i) * NTS + cb) * ws_q_bytes<DK>();
-        // inputs of one chunk's output step, all in fragment order: Q, Aqk, scale exp(gc);
-        // double-buffered, loaded two chunks ahead of their use
-        struct OutIn {
-            opx8 qf[KB][4];
-            opx8 af[6];
-            float eg[4];
-        };
-        auto load_in = [&](int c, OutIn& in) {
-            const opx8* qs = reinterpret_cast<const opx8*>(wqh + (size_t)c * ws_q_bytes<DK>());
+        // ================================================================= output waves
+        // Output wave ow forms token tiles {0, 3} (ow = 0) or {1, 2} (ow = 1) of O of chunk n - 1
+        // in iteration n, for every column group: the two sets take the same number of products.
+        auto role = [&](auto owc) {
+            constexpr int OWC = decltype(owc)::value;
+            constexpr int CT0 = OWC == 0 ? 0 : 1, CT1 = OWC == 0 ? 3 : 2;
+            auto ctile = [](int t) { return t == 0 ? CT0 : CT1; };
+            bf16* ob = o + (sq.tok0 * Hv + j) * DV + c0;
+            const unsigned char* wqh = wsq + (((size_t)b * Hqk + i) * NTS + cb) * ws_q_bytes<DK>();
+            // inputs of one chunk's output step for these token tiles, all in fragment order from
+            // the workspace: Q, the Aqk blocks (ct, cb <= ct / 2) and scale exp(gc);
+            // double-buffered, loaded two chunks ahead of their use
+            struct OutIn {
+                opx8 qf[KB][2];
+                opx8 af[2][2];
+                float eg[2];
+            };
+            auto load_in = [&](int c, OutIn& in) {
+                const opx8* qs = reinterpret_cast<const opx8*>(wqh + (size_t)c * ws_q_bytes<DK>());
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
+                for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) in.qf[kk][ct] = qs[(kk * 4 + ct) * 64 + lane];
-            const unsigned char* wc = wh + (size_t)c * WS_CHUNK;
-            const opx8* a = reinterpret_cast<const opx8*>(wc + WS_AQ);
+                    for (int t = 0; t < 2; ++t) in.qf[kk][t] = qs[(kk * 4 + ctile(t)) * 64 + lane];
+                const unsigned char* wc = wh + (size_t)c * WS_CHUNK;
+                const opx8* a = reinterpret_cast<const opx8*>(wc + WS_AQ);
+                const float* e = reinterpret_cast<const float*>(wc + WS_EG);
 #pragma unroll
-            for (int bk = 0; bk < 6; ++bk) in.af[bk] = a[bk * 64 + lane];
-            const float* e = reinterpret_cast<const float*>(wc + WS_EG);
+                for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) in.eg[ct] = e[16 * ct + ln];
-        };
-        // O^T = (h^T Q^T) diag(scale exp(gc)) + Delta^T (scale Aqk)^T for chunk m (see
-        // chain_out), column group by column group
-        auto out = [&](int m, const OutIn& in) {
-#pragma unroll
-            for (int ow = 0; ow < NW; ++ow) {
-            const opx8* hx = hxp(m, ow);
-            opx8 hb[KB];
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) hb[kk] = hx[kk * 64 + lane];
-            opx8 db[2];
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) db[cb] = hx[(KB + cb) * 64 + lane];
-            floatx4 OT[4];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) OT[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) OT[ct] = mfma32(hb[kk], in.qf[kk][ct], OT[ct]);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) OT[ct][x] *= in.eg[ct];
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int ct = 2 * cb; ct < 4; ++ct) OT[ct] = mfma32(db[cb], in.af[tblk(ct, cb)], OT[ct]);
-            const int t0 = m * CH, nv = min(CH, T_len - t0);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const int tok = 16 * ct + ln;
-                if (tok < nv) {
-                    const bf16x4 ov = {(bf16)OT[ct][0], (bf16)OT[ct][1], (bf16)OT[ct][2], (bf16)OT[ct][3]};
-                    *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 16 * ow + 4 * lg) = ov;
+                    for (int cb = 0; cb <= ctile(t) / 2; ++cb) in.af[t][cb] = a[tblk(ctile(t), cb) * 64 + lane];
+                    in.eg[t] = e[16 * ctile(t) + ln];
                 }
-            }
-            }
-        };
-        // iteration n forms O of chunk n - 1 from buffer (n - 1) % 2, then loads chunk n + 1 into it
-        auto step = [&](int n, OutIn& cur) {
-            GDN_TRACE(n, 0);
-            if (n >= 1) {
-                out(n - 1, cur);
-                GDN_TRACE(n, 1);
-                load_in(min(n + 1, NT - 1), cur);   // unconditional: see the loaders
-            }
-            GDN_TRACE(n, 2);
+            };
+            // O^T = (h^T Q^T) diag(scale exp(gc)) + Delta^T (scale Aqk)^T for chunk m (see
+            // chain_out), column group by column group
+            auto out = [&](int m, const OutIn& in) {
+                const int lane = opaque(threadIdx.x & 63), ln = lane & 15, lg = lane >> 4;
+                const int t0 = m * CH, nv = min(CH, T_len - t0);
+#pragma unroll
+                for (int cgw = 0; cgw < NW; ++cgw) {
+                    const opx8* hx = hxp(m, cgw);
+                    opx8 hb[KB];
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) hb[kk] = hx[kk * 64 + lane];
+                    opx8 db[2];
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) db[cb] = hx[(KB + cb) * 64 + lane];
+                    floatx4 OT[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) OT[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) OT[t] = mfma32(hb[kk], in.qf[kk][t], OT[t]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) OT[t][x] *= in.eg[t];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int cb = 0; cb <= ctile(t) / 2; ++cb) OT[t] = mfma32(db[cb], in.af[t][cb], OT[t]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int tok = 16 * ctile(t) + ln;
+                        if (tok < nv) {
+                            const bf16x4 ov = {(bf16)OT[t][0], (bf16)OT[t][1], (bf16)OT[t][2], (bf16)OT[t][3]};
+                            *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 16 * cgw + 4 * lg) = ov;
+                        }
+                    }
+                }
+            };
+            // iteration n forms O of chunk n - 1 from buffer (n - 1) % 2, then loads chunk n + 1
+            // into it
+            auto step = [&](int n, OutIn& cur) {
+                GDN_TRACE(n, 0);
+                if (n >= 1) {
+                    out(n - 1, cur);
+                    GDN_TRACE(n, 1);
+                    load_in(min(n + 1, NT - 1), cur);   // unconditional: see the loaders
+                }
+                GDN_TRACE(n, 2);
+                lds_barrier();
+            };
+            OutIn bufA, bufB;
+            load_in(0, bufA);
+            load_in(min(1, NT - 1), bufB);
             lds_barrier();
+            int n = 0;
+            for (; n + 1 < NT; n += 2) {
+                step(n, bufB);       // n even: O of chunk n - 1 (odd) is in bufB
+                step(n + 1, bufA);   // O of chunk n (even) is in bufA
+            }
+            if (n < NT) step(n, bufB);
+            if ((NT - 1) % 2 == 0)
+                out(NT - 1, bufA);
+            else
+                out(NT - 1, bufB);
         };
-        OutIn bufA, bufB;
-        load_in(0, bufA);
-        load_in(min(1, NT - 1), bufB);
-        lds_barrier();
-        int n = 0;
-        for (; n + 1 < NT; n += 2) {
-            step(n, bufB);       // n even: O of chunk n - 1 (odd) is in bufB
-            step(n + 1, bufA);   // O of chunk n (even) is in bufA
-        }
-        if (n < NT) step(n, bufB);
-        if ((NT - 1) % 2 == 0)
-            out(NT - 1, bufA);
+        if (w == 0)
+            role(std::integral_constant<int, 0>{});
         else
-            out(NT - 1, bufB);
+            role(std::integral_constant<int, 1>{});
     }
 }
 
@@ -2141,9 +2179,9 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st, SegArgs 
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * NTILE) == 0) ? 1 : 0;
     const int NT = (int)(((long)a.T + CH - 1) / CH);
     const unsigned char* wsq = (const unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk, (unsigned)nseg), dim3((SLW + NW + 1) * 64), L::bytes, st,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0,
-                       a.sf, (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, remap, a.cu, a.total, sg);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk, (unsigned)nseg), dim3((SLW + NW + SOW) * 64), L::bytes, st,
+                       (const bf16*)a.k, (const bf16*)a.v, (const unsigned char*)ws, wsq, a.s0, a.sf, (bf16*)a.o,
+                       a.T, a.Hqk, a.Hv, grp, remap, a.cu, a.total, sg);
     return hipGetLastError();
 }
 
