@@ -25,8 +25,8 @@
  *    beta in [0, 1] (the write strength).  g > 0 (alpha > 1, a growing state) is outside the
  *    supported range of the bf16 matrix-core routes below; the float32 routes and decode accept it
  *    while every value stays finite in float32.
- *  - Operand range of the bf16 matrix-core routes (gdn_chunk_fwd_kernel_name "mfma",
- *    "mfma_split", "mfma_scan"; gdn_chunk_fwd_gated, _varlen, _scan, gdn_chunk_transport and
+ *  - Operand range of the bf16 matrix-core routes (gdn_chunk_fwd_kernel_name "mfma_pipe",
+ *    "mfma", "mfma_split", "mfma_scan"; gdn_chunk_fwd_gated, _varlen, _scan, gdn_chunk_transport and
  *    gdn_kda_chunk_fwd at chunk 64).  Their products take float16 operands (the same matrix-core
  *    rate as bf16 with a 3-bit longer significand) and accumulate in float32.  The operands are
  *    q, k, v, the state, (I + A)^{-1}, and per chunk R = beta (v - e^gc k^T h) and
@@ -169,8 +169,11 @@ gdn_status_t gdn_recurrent_step(const void* q, const void* k, const void* v, con
 
 /*
  * gdn_chunk_fwd_kernel_name -- which kernel family gdn_chunk_fwd would run for these sizes:
- * "mfma" (one fused matrix-core kernel, chosen when B * Hv >= 192), "mfma_split" (a parallel
- * per-chunk prep kernel, then the matrix-core state pass; fewer chains), "mfma_scan" (the
+ * "mfma_pipe" (one fused matrix-core kernel in which prep waves build chunk n + 1 while chain
+ * waves carry chunk n; chosen when B * Hv >= 192), "mfma" (the fused matrix-core kernel of the
+ * gated epilogue and of packed sequences with as many chains; gdn_chunk_fwd itself does not
+ * choose it), "mfma_split" (a parallel per-chunk prep kernel, then the matrix-core state pass;
+ * fewer chains), "mfma_scan" (the
  * affine chunk scan of gdn_chunk_fwd_scan: so few chains that 32-column tiles over dv + dk
  * columns give at most 128 workgroups, cut into p = 1 + 256 / (B * Hv * (dv + dk) / 32)
  * segments when T holds at least 8 p chunks), "mfma_f32" (the float32 kernel: the chunk algebra
@@ -247,9 +250,11 @@ size_t gdn_chunk_fwd_gated_workspace_bytes(int B, int T, int Hqk, int Hv, int dk
  *     y = O / sqrt(mean over the head's dv channels of O^2 + eps) * w * silu(z),
  * with O rounded to dtype before the norm, as when the two calls run one after the other (same
  * sources as those two).  Where the fused matrix-core kernel holds whole value heads (bf16,
- * chunk 64, dk and dv 64 or 128, enough chains that gdn_chunk_fwd_kernel_name says "mfma" and
- * the column tile is dv) the norm runs inside it and O never reaches device memory; otherwise O
- * goes through the workspace and a second kernel.  Both ways give the same bits.
+ * chunk 64, dk and dv 64 or 128, enough chains that gdn_chunk_fwd_kernel_name says "mfma_pipe")
+ * the norm runs inside that kernel ("mfma") and O never reaches device memory; its O matches
+ * gdn_chunk_fwd's (the pipelined kernel there) to the bf16 tolerance, not bit for bit, since the
+ * two kernels round T and Aqk in different orders.  Otherwise O goes through the workspace and a
+ * second kernel, and the result is bit for bit gdn_chunk_fwd followed by gdn_gated_rmsnorm.
  *
  *   q, k, v, g, beta, initial_state, final_state, sizes, chunk, dtype, scale: as gdn_chunk_fwd
  *   z              [B, T, Hv, dv] dtype, the gate projection
