@@ -1210,7 +1210,7 @@ template <int DK, bool VARLEN>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
-    int T_max, int Hqk, int Hv, int grp, int NT, float scale, const int* cu, int total)
+    int T_max, int Hqk, int Hv, int grp, int NT, float scale, int xcd_remap, const int* cu, int total)
 {
     constexpr int KB = DK / 32;
     // A and T (prep_store_a, prep_solve_t): about 20 KB of LDS per wave in all
@@ -1220,11 +1220,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
     __shared__ __attribute__((aligned(16))) float pg[CH];         // gc
     __shared__ __attribute__((aligned(16))) float pb[CH];         // beta
 
+    // (batch, chunk, query/key head) with the head fastest: the head group of one chunk reads
+    // the same g, beta lines and adjacent q, k rows, so those workgroups run together, and on
+    // one XCD (workgroup ids are dealt to the 8 XCDs round-robin) so that they share its L2
     int lid = blockIdx.x;
-    const int c = lid % NT;
-    lid /= NT;
+    if (xcd_remap) lid = (lid & 7) * (gridDim.x >> 3) + (lid >> 3);
     const int i = lid % Hqk;
-    const int b = lid / Hqk;
+    lid /= Hqk;
+    const int c = lid % NT;
+    const int b = lid / NT;
     const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
     const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
     const int t0 = c * CH;
@@ -2194,7 +2198,7 @@ hipError_t launch_prep_t(const ChunkArgs& a, void* ws, hipStream_t st)
     unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL((chunk_prep_kernel<DK, VARLEN>), dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, wsq, a.T, a.Hqk, a.Hv, grp, NT,
-                       a.scale, a.cu, a.total);
+                       a.scale, nprep % 8 == 0 ? 1 : 0, a.cu, a.total);
     return hipGetLastError();
 }
 
