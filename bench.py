@@ -105,6 +105,7 @@ def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
 # What one gdn_chunk_fwd launches, per kernel family; the roofline is taken over the whole call
 # (HIP events around it on its stream), i.e. over both kernels of the split path.
 KERNELS = {"mfma": "chunk_mfma_kernel",
+           "mfma (gated epilogue)": "chunk_mfma_kernel with the gated RMSNorm",
            "mfma_pipe": "chunk_pipe_kernel",
            "mfma_split": "chunk_prep_kernel + chunk_state_kernel",
            "mfma_f32": "chunk_simt_kernel (float32 matrix-core products)"}
@@ -203,9 +204,11 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated
     flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
     del sets, outs, sfs, ws
     torch.cuda.empty_cache()
-    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets, workspace=need,
-                kernel=gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv,
-                                                     cfg.chunk, dt))
+    kernel = gdn.gdn_chunk_fwd_kernel_name(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk, dt)
+    if gated:
+        # the norm inside the fused kernel when it holds whole heads (no workspace), else a second kernel
+        kernel = "mfma (gated epilogue)" if need == 0 and es == 2 else kernel + " + gated_rmsnorm"
+    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets, workspace=need, kernel=kernel)
 
 
 def bench_scan(torch, gdn, gi, steps=5, warmup=2):
@@ -455,6 +458,8 @@ def main():
     ap.add_argument("--workload", default="qwen36_long_prefill")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gated", action="store_true",
+                    help="time gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--leg", choices=("layer_ops", "backward", "kda", "varlen", "scan", "decode"),
@@ -490,8 +495,8 @@ def main():
                 "decode": lambda: bench_decode(gi.CONFIGS["decode"], torch, gdn, gi)}
         print(json.dumps({"leg": args.leg, **legs[args.leg]()}), flush=True)
         return
-    print(f"bench: prefill {cfg}", file=sys.stderr, flush=True)
-    r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi)
+    print(f"bench: prefill {cfg}{' (gated)' if args.gated else ''}", file=sys.stderr, flush=True)
+    r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi, gated=args.gated)
     tokens = cfg.B * cfg.T
     ms = r["wall"] / args.steps * 1e3
     line = {
@@ -510,8 +515,10 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hqk": cfg.Hqk, "Hv": cfg.Hv,
                    "dk": cfg.dk, "dv": cfg.dv, "chunk": cfg.chunk, "state": "float32",
                    "initial_state": cfg.s0_std > 0, "input_sets": r["n_sets"]},
-        "roofline": prefill_roofline(r, measured_traffic(cfg.name)),
+        "roofline": prefill_roofline(r, measured_traffic(cfg.name, "chunk_fwd_gated" if args.gated else "chunk_fwd")),
     }
+    if args.gated:
+        line["config"]["gated_output_norm"] = True
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, gi)
