@@ -15,14 +15,17 @@
 // the last chunk enter as zeros with g = beta = 0, which changes no result.  The scale is folded
 // into exp(gc) of the output step and into the Q K^T matrix ("Aqk") when they are built.
 //
-// Two ways to run it, both built from the same per-chunk state step (chain_chunk):
+// Three ways to run it, all built from the same per-chunk state step (chain_delta, chain_out,
+// chain_update) and, for the state-independent part, the same prep steps (prep_store_a,
+// prep_solve_t, prep_store_aqk, prep_store_t):
 //
-// * Fused (chunk_mfma_kernel): one workgroup carries one (batch, value head, column tile) chain
-//   through every chunk; nothing but the inputs, O and the states touches HBM.  Four "prep" waves
-//   build everything of chunk n+1 that does not depend on the state (the cumsum, K K^T, Q K^T,
-//   the decay masks and T) and stage the inputs in LDS, while four "chain" waves carry the state
-//   through chunk n.  Four workgroup barriers per chunk.  Suits many chains: the prep work runs
-//   beside the chain on the same compute unit.
+// * Pipelined fused (chunk_pipe_kernel): one workgroup carries one (batch, value head, column
+//   tile) chain through every chunk; nothing but the inputs, O and the states touches HBM.
+//   Three prep waves build chunk n+1 (T, Aqk, the staged K, Q, V and the gate vectors), each a
+//   whole part on its own, while the chain waves carry chunk n; one workgroup barrier per
+//   chunk.  Suits many chains: the prep work runs beside the chain on the same compute unit.
+// * Fused (chunk_mfma_kernel): the same split of work over four prep and four chain waves, with
+//   four barriers per chunk; it carries the gated output norm and packed sequences.
 // * Split (chunk_prep_kernel + chunk_state_kernel): the state-independent part of every chunk is
 //   built first, all chunks at once (one wave per chunk and value head), into a workspace: T,
 //   scaled Aqk and the gate vectors, 13.5 KB per chunk.  The state pass then only stages inputs
@@ -44,8 +47,9 @@
 //   merged 16 -> 32 -> 64 with matrix products:
 //   T_21 = -T_22 A_21 T_11 (16x16x16), then T_hi,lo = -T_hi (A_hi,lo T_lo) (16x16x32).
 // * Operands are float16: the same MFMA rate as bf16 on gfx950 with a 3-bit longer significand.
-//   q and k arrive as bf16 and convert exactly (up to float16 subnormals, far below what matters
-//   next to unit-norm rows); every other operand is rounded once from float32.  The Gram
+//   q and k arrive as bf16 and convert exactly for unit-norm rows (components below 2^-14 become
+//   float16 subnormals, an error of at most 2^-25); every other operand (v, the state, T, R,
+//   Delta) is rounded once from float32, which bounds the magnitudes the inputs may reach.  The Gram
 //   products of the split path take q and k as bf16 directly (exact products either way).
 // * Row pitches are padded so that the 8- and 16-byte fragment reads of 8 consecutive rows
 //   cover all 64 LDS banks once.

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so `-m "not gpu"` and plain
-    # runs on a CPU-only host behave; on the GPU machine they run.
+    # runs on a CPU-only host behave; on a host with the GPU they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
