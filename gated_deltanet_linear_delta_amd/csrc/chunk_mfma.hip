@@ -25,7 +25,7 @@
 //   whole part on its own, while the chain waves carry chunk n; one workgroup barrier per
 //   chunk.  Suits many chains: the prep work runs beside the chain on the same compute unit.
 // * Fused (chunk_mfma_kernel): the same split of work over four prep and four chain waves, with
-//   four barriers per chunk; it carries the gated output norm and packed sequences.
+//   four barriers per chunk; it carries the gated output norm.
 // * Split (chunk_prep_kernel + chunk_state_kernel): the state-independent part of every chunk is
 //   built first, all chunks at once (one wave per chunk and value head), into a workspace: T,
 //   scaled Aqk and the gate vectors, 13.5 KB per chunk.  The state pass then only stages inputs
@@ -1417,12 +1417,13 @@ __device__ __forceinline__ void store_rows_frag(const bf16x8 (&f)[4][KB], op_t* 
         }
 }
 
-template <int DK, int DV, int BV, int NW>
+template <int DK, int DV, int BV, int NW, bool VARLEN>
 __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
-    bf16* __restrict__ o, int T_len, int Hqk, int Hv, int grp, float scale, int xcd_remap)
+    bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, float scale, int xcd_remap, const int* cu,
+    int total)
 {
     using L = PLds<DK, BV>;
     constexpr int NTILE = DV / BV;
@@ -1438,10 +1439,18 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
     const int b = id.b, i = id.i, j = id.j, c0 = id.tile * BV;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
+    const int T_len = sq.len;
+    if (VARLEN && T_len == 0) {
+        // an empty sequence: the final state is the initial one (every wave leaves here, before
+        // any barrier)
+        if (w < NW) copy_state_cols<DK, DV>(s0, sf, (size_t)b * Hv + j, c0 + w * NCOL, NCOL, lane);
+        return;
+    }
     const int NT = (T_len + CH - 1) / CH;
     const size_t qk_row = (size_t)Hqk * DK;
     const size_t v_row = (size_t)Hv * DV;
-    const size_t tok0 = (size_t)b * T_len;
+    const size_t tok0 = sq.tok0;
     auto slot = [&](int c) { return smem + (size_t)(c & 1) * L::slot; };
 
     if (w < NW) {
@@ -2096,14 +2105,13 @@ int choose_split_bv(const ChunkArgs& a)
     return chains * (a.dv / 16) <= 256 ? 16 : 32;
 }
 
-// The pipelined fused kernel (chunk_pipe_kernel) serves uniform-length calls with enough chains
-// to fill the chip (measured: 0.62 ms against 0.81 ms for chunk_mfma_kernel on 8 x 8192 tokens x
-// 32 value heads); a gated call on this route takes the fused kernel with the gated epilogue.
-// With fewer chains the split path wins: the pipelined kernel builds T and Aqk once per column
-// tile, the split path once per value head.
+// The pipelined fused kernel (chunk_pipe_kernel) serves calls with enough chains to fill the
+// chip, uniform or packed (measured: 0.62 ms against 0.81 ms for chunk_mfma_kernel on 8 x 8192
+// tokens x 32 value heads); a gated call on this route takes the fused kernel with the gated
+// epilogue.  With fewer chains the split path wins: the pipelined kernel builds T and Aqk once
+// per column tile, the split path once per value head.
 bool use_pipe(const ChunkArgs& a)
 {
-    if (a.cu) return false;
     if (const char* e = env_str("GDN_MFMA_PATH")) return !strcmp(e, "pipe");
     return (long)a.B * a.Hv >= 192;
 }
@@ -2153,12 +2161,13 @@ hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
 
 // The state pass over `nseg` segments of sg.len chunks (grid y); nseg = 1, sg.len = NT for a
 // whole chain from s0.
-template <int DK, int DV, int BV, int NW>
+template <int DK, int DV, int BV, int NW, bool VARLEN = false>
 hipError_t launch_pipe_t(const ChunkArgs& a, hipStream_t st)
 {
+    if (!VARLEN && a.cu) return launch_pipe_t<DK, DV, BV, NW, true>(a, st);
     using L = PLds<DK, BV>;
     static_assert(L::bytes <= 160 * 1024, "LDS budget");
-    auto kern = chunk_pipe_kernel<DK, DV, BV, NW>;
+    auto kern = chunk_pipe_kernel<DK, DV, BV, NW, VARLEN>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
     if (e != hipSuccess) return e;
     const int grp = a.Hv / a.Hqk;
@@ -2167,7 +2176,7 @@ hipError_t launch_pipe_t(const ChunkArgs& a, hipStream_t st)
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((NW + 3) * 64), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.s0, a.sf, (bf16*)a.o, a.T, a.Hqk, a.Hv,
-                       grp, a.scale, remap);
+                       grp, a.scale, remap, a.cu, a.total);
     return hipGetLastError();
 }
 

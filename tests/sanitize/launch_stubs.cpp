@@ -12,7 +12,7 @@ bool chunk_mfma_supported(const ChunkArgs& a)
     return a.dtype_bf16 && a.chunk == 64 && (a.dk == 64 || a.dk == 128) && (a.dv == 64 || a.dv == 128);
 }
 bool chunk_mfma_split(const ChunkArgs& a) { return chunk_mfma_supported(a) && (long)a.B * a.Hv < 192; }
-bool chunk_mfma_pipe(const ChunkArgs& a) { return chunk_mfma_supported(a) && !a.cu && (long)a.B * a.Hv >= 192; }
+bool chunk_mfma_pipe(const ChunkArgs& a) { return chunk_mfma_supported(a) && (long)a.B * a.Hv >= 192; }
 bool chunk_mfma_gated_fused(const ChunkArgs& a) { return chunk_mfma_supported(a) && !chunk_mfma_split(a); }
 size_t chunk_mfma_workspace_bytes(const ChunkArgs& a)
 {

@@ -46,7 +46,8 @@ def oracle_varlen(d, cu):
     return np.concatenate(os_, axis=0), np.stack(ss)
 
 
-ROUTES = {"fused": dict(GDN_MFMA_PATH="fused"), "split": dict(GDN_MFMA_PATH="split"), "f32": dict(GDN_DISABLE_MFMA="1")}
+ROUTES = {"pipe": dict(GDN_MFMA_PATH="pipe"), "fused": dict(GDN_MFMA_PATH="fused"), "split": dict(GDN_MFMA_PATH="split"),
+          "f32": dict(GDN_DISABLE_MFMA="1")}
 
 
 @pytest.mark.parametrize("route", list(ROUTES))
@@ -63,7 +64,7 @@ def test_varlen_matches_oracle(route, dk, dv, monkeypatch, hooks):
     check(f"varlen {route}", dtype, o, o_ref, s, s_ref)
 
 
-@pytest.mark.parametrize("route", ["fused", "split"])
+@pytest.mark.parametrize("route", ["pipe", "fused", "split"])
 def test_varlen_equal_lengths_equal_batched(route, monkeypatch, hooks):
     """Equal lengths L: the same bits as gdn_chunk_fwd over B = N rows of L tokens."""
     monkeypatch.setenv("GDN_MFMA_PATH", route)
@@ -91,7 +92,7 @@ def test_varlen_all_empty_and_out_of_contract_offsets():
     # the kernels clamp them, so the call completes; the results are unspecified
     bad = torch.tensor([-7, 3, 1, 99], dtype=torch.int32, device="cuda:0")
     s3 = torch.zeros((3, 2, 64, 64), device="cuda:0")
-    for route in ("fused", "split"):
+    for route in ("pipe", "fused", "split"):
         import os
         os.environ["GDN_MFMA_PATH"] = route
         try:
