@@ -131,7 +131,8 @@ def prefill_roofline(r, traffic):
             "kernel": f"chunk_fwd ({KERNELS.get(r['kernel'], r['kernel'])})", "kernel_ms": r["kern"] * 1e3,
             "workspace_bytes": r["workspace"], "alg_bytes": r["bytes"], "alg_flops": r["flops"],
             "mfma_achieved_TFLOPs": r["flops"] / r["kern"] / 1e12,
-            "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK}
+            "mfma_frac": r["flops"] / r["kern"] / MFMA_BF16_PEAK,
+            "cold_kernel_ms": None if r.get("kern_cold") is None else r["kern_cold"] * 1e3}
 
 
 def measured_traffic(workload: str, op: str = "chunk_fwd"):
@@ -167,7 +168,23 @@ def time_launches(fn, n_sets, steps, warmup, torch):
     return wall, sum(kern) / len(kern)
 
 
-def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated=False):
+def time_cold(fn, steps, torch, flush_bytes=512 << 20):
+    """Average of `steps` launches, each after a 512 MiB device write that evicts the 256 MB
+    Infinity Cache (the write itself is outside the timed events)."""
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(float(i))
+        evs[i][0].record(st)
+        fn(0)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    del flush
+    return sum(a.elapsed_time(b) for a, b in evs) / steps * 1e-3
+
+
+def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated=False, cold_steps=5):
     """gdn_chunk_fwd (or, gated, gdn_chunk_fwd_gated: the output's gated RMSNorm in the same call,
     whose algorithmic bytes add the gate z read once and the norm weight)."""
     dev = "cuda:0"
@@ -201,6 +218,7 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated
                               o=outs[i], final_state=sfs[i], workspace=ws)
 
     wall, kern = time_launches(fn, n_sets, steps, warmup, torch)
+    kern_cold = time_cold(fn, cold_steps, torch) if cold_steps else None
     flops = prefill_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, cfg.chunk)
     del sets, outs, sfs, ws
     torch.cuda.empty_cache()
@@ -208,7 +226,8 @@ def bench_prefill(cfg, steps, warmup, torch, gdn, gi, min_bytes=640 << 20, gated
     if gated:
         # the norm inside the fused kernel when it holds whole heads (no workspace), else a second kernel
         kernel = "mfma (gated epilogue)" if need == 0 and es == 2 else kernel + " + gated_rmsnorm"
-    return dict(wall=wall, kern=kern, bytes=per_set, flops=flops, n_sets=n_sets, workspace=need, kernel=kernel)
+    return dict(wall=wall, kern=kern, kern_cold=kern_cold, bytes=per_set, flops=flops, n_sets=n_sets,
+                workspace=need, kernel=kernel)
 
 
 def bench_scan(torch, gdn, gi, steps=5, warmup=2):
@@ -445,7 +464,13 @@ def cpu_baseline(cfg, gi, min_seconds=10.0, max_repeats=30):
         t_total += time.perf_counter() - t0
         reps += 1
     tokens = cfg.B * cfg.T * reps
-    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": model,
             "sample": f"whole {cfg.name} batch (B={cfg.B}, T={cfg.T}, Hv={cfg.Hv}) x {reps} runs, "
                       f"{t_total:.1f} s, float64 token-by-token recurrence, OpenMP over {cfg.B * cfg.Hv} chains"}
 
