@@ -107,7 +107,8 @@ def decode_alg_bytes(B, Hqk, Hv, dk, dv, es):
 KERNELS = {"mfma": "chunk_mfma_kernel",
            "mfma (gated epilogue)": "chunk_mfma_kernel with the gated RMSNorm",
            "mfma_pipe": "chunk_pipe_kernel",
-           "mfma_split": "chunk_prep_kernel + chunk_state_kernel",
+           "mfma_split": "chunk_prep_kernel + chunk_state_kernel (rows of 256 chunks or more: in pieces, "
+                         "chunk_overlap_kernel)",
            "mfma_f32": "chunk_simt_kernel (float32 matrix-core products)"}
 
 

@@ -30,7 +30,9 @@
 //   built first, all chunks at once (one wave per chunk and value head), into a workspace: T,
 //   scaled Aqk and the gate vectors, 13.5 KB per chunk.  The state pass then only stages inputs
 //   and runs the chain, with one barrier per chunk.  Suits few, long chains, where the
-//   sequential per-chunk latency of the state pass is the whole cost.
+//   sequential per-chunk latency of the state pass is the whole cost.  Long rows whose state
+//   pass leaves compute units idle run in pieces: one launch (chunk_overlap_kernel) per piece
+//   carries its state pass on some compute units and the next piece's prep on the others.
 //
 // gfx950 mapping
 // * Each chain wave owns 16 or 32 state columns (value columns evolve independently), so the
@@ -58,6 +60,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -638,10 +642,9 @@ __device__ __forceinline__ SeqSpan seq_span(const int* cu, int b, int T_len, int
     return SeqSpan{(size_t)s, min(e - s, T_len)};
 }
 
-__device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd_remap)
+__device__ __forceinline__ ChainId chain_id_of(int lid, int nblk, int ntile, int Hqk, int grp, int xcd_remap)
 {
-    int lid = blockIdx.x;
-    if (xcd_remap) lid = (lid & 7) * (gridDim.x >> 3) + (lid >> 3);
+    if (xcd_remap) lid = (lid & 7) * (nblk >> 3) + (lid >> 3);
     ChainId c;
     c.tile = lid % ntile;
     lid /= ntile;
@@ -651,6 +654,11 @@ __device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd
     c.b = lid / Hqk;
     c.j = c.i * grp + jj;
     return c;
+}
+
+__device__ __forceinline__ ChainId chain_id(int ntile, int Hqk, int grp, int xcd_remap)
+{
+    return chain_id_of(blockIdx.x, gridDim.x, ntile, Hqk, grp, xcd_remap);
 }
 
 }  // namespace
@@ -1210,30 +1218,39 @@ __device__ __forceinline__ void prep_zero_t_upper(op_t* Tm, int lane)
 // are shared by the query/key head's group of value heads); then for each value head of the
 // group in turn: the gate cumsum and vectors, A (beta and the decay mask), T = (I + A)^{-1}, and
 // Aqk (the decay mask and the scale), all into the workspace.
+// LDS of one prep wave: A and T (prep_store_a, prep_solve_t), gc and beta; about 20 KB
+struct PrepLds {
+    static constexpr size_t ad = 0;                                  // f32 [PREP_AD]
+    static constexpr size_t ah = ad + (size_t)PREP_AD * 4;           // f16 [PREP_AH]
+    static constexpr size_t tm = ah + (size_t)PREP_AH * 2;           // T, column-permuted f16
+    static constexpr size_t pg = tm + (size_t)PREP_TM * 2;           // gc [64] f32
+    static constexpr size_t pb = pg + (size_t)CH * 4;                // beta [64] f32
+    static constexpr size_t bytes = pb + (size_t)CH * 4;
+    static_assert(ah % 16 == 0 && tm % 16 == 0 && pg % 16 == 0 && bytes % 16 == 0, "16-byte aligned parts");
+};
+
+// One unit of the prep work, run by one wave on its own: (batch row b, chunk c, query/key head i)
+// from unit index u over the chunks c_base .. c_base + NTg - 1, with the head fastest.  Its
+// results go to chunk c of the workspace (NT chunks per row).
 template <int DK, bool VARLEN>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
-    int T_max, int Hqk, int Hv, int grp, int NT, float scale, int xcd_remap, const int* cu, int total)
+__device__ __forceinline__ void prep_unit(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                          const float* __restrict__ g, const float* __restrict__ beta,
+                                          unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
+                                          int T_max, int Hqk, int Hv, int grp, int NT, float scale,
+                                          const int* cu, int total, int u, int c_base, int NTg,
+                                          unsigned char* lds)
 {
     constexpr int KB = DK / 32;
-    // A and T (prep_store_a, prep_solve_t): about 20 KB of LDS per wave in all
-    __shared__ __attribute__((aligned(16))) float Ad[PREP_AD];
-    __shared__ __attribute__((aligned(16))) op_t Ah[PREP_AH];
-    __shared__ __attribute__((aligned(16))) op_t Tm[PREP_TM];     // T, column-permuted float16
-    __shared__ __attribute__((aligned(16))) float pg[CH];         // gc
-    __shared__ __attribute__((aligned(16))) float pb[CH];         // beta
-
-    // (batch, chunk, query/key head) with the head fastest: the head group of one chunk reads
-    // the same g, beta lines and adjacent q, k rows, so those workgroups run together, and on
-    // one XCD (workgroup ids are dealt to the 8 XCDs round-robin) so that they share its L2
-    int lid = blockIdx.x;
-    if (xcd_remap) lid = (lid & 7) * (gridDim.x >> 3) + (lid >> 3);
-    const int i = lid % Hqk;
-    lid /= Hqk;
-    const int c = lid % NT;
-    const int b = lid / NT;
-    const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
+    float* Ad = reinterpret_cast<float*>(lds + PrepLds::ad);
+    op_t* Ah = reinterpret_cast<op_t*>(lds + PrepLds::ah);
+    op_t* Tm = reinterpret_cast<op_t*>(lds + PrepLds::tm);
+    float* pg = reinterpret_cast<float*>(lds + PrepLds::pg);
+    float* pb = reinterpret_cast<float*>(lds + PrepLds::pb);
+    const int i = u % Hqk;
+    u /= Hqk;
+    const int c = c_base + u % NTg;
+    const int b = u / NTg;
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
     const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
     const int t0 = c * CH;
     if (VARLEN && t0 >= sq.len) return;   // past this sequence's last chunk
@@ -1338,6 +1355,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
         prep_store_t(Tm, reinterpret_cast<opx8*>(wc + WS_T), lane);
         GDN_TRACE_PREP(5);
     }
+}
+
+// One workgroup (one wave) per unit of chunks c_base .. c_base + NTg - 1.  The units run with
+// the head fastest: the head group of one chunk reads the same g, beta lines and adjacent q, k
+// rows, so those workgroups run together, and on one XCD (workgroup ids are dealt to the 8 XCDs
+// round-robin) so that they share its L2.
+template <int DK, bool VARLEN>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const float* __restrict__ g,
+    const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
+    int T_max, int Hqk, int Hv, int grp, int NT, float scale, int xcd_remap, const int* cu, int total,
+    int c_base, int NTg)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[PrepLds::bytes];
+    int u = blockIdx.x;
+    if (xcd_remap) u = (u & 7) * (gridDim.x >> 3) + (u >> 3);
+    prep_unit<DK, VARLEN>(q, k, g, beta, ws, wsq, T_max, Hqk, Hv, grp, NT, scale, cu, total, u, c_base, NTg, lds);
 }
 
 // =======================================================================================
@@ -1687,6 +1721,7 @@ struct SegArgs {
     const float* hin;   // prefill: entry state of every segment, or null
     float* mout;        // transport outputs
     float* nout;
+    int base = 0;       // first chunk of segment 0 (a later piece of the rows)
 };
 
 template <int DK, int BV, int NW>
@@ -1709,11 +1744,13 @@ struct SLds {
     static_assert(v % 16 == 0 && cv % 16 == 0 && hx % 16 == 0, "16-byte aligned parts");
 };
 
-template <int DK, int DV, int NW, bool VARLEN, bool XPORT = false>
-__global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
+// The state pass of workgroup `blk` of `nblk` (segment `seg` of `nseg`), in the LDS at smem.
+template <int DK, int DV, int NW, bool VARLEN, bool XPORT>
+__device__ __forceinline__ void state_body(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const unsigned char* __restrict__ ws,
     const unsigned char* __restrict__ wsq, const float* s0, float* sf, bf16* __restrict__ o, int T_max, int Hqk,
-    int Hv, int grp, int xcd_remap, const int* cu, int total, SegArgs sg)
+    int Hv, int grp, int xcd_remap, const int* cu, int total, SegArgs sg, int blk, int nblk, int seg_y, int nseg,
+    unsigned char* smem)
 {
     constexpr int BV = 16 * NW;
     using L = SLds<DK, BV, NW>;
@@ -1729,8 +1766,7 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
     constexpr int CVR = 4 * CH * 4 / 16;                // 16-byte runs of the state-step vectors
     static_assert(PK >= 1 && CH * RP % NLT == 0 && CVR <= NLT, "tile shape");
 
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const ChainId id = chain_id(NTILE, Hqk, grp, xcd_remap);
+    const ChainId id = chain_id_of(blk, nblk, NTILE, Hqk, grp, xcd_remap);
     const int b = id.b, i = id.i, j = id.j;
     const int c0 = id.tile * BV;
     const int tid = threadIdx.x;
@@ -1757,8 +1793,8 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
     }
     // this workgroup's segment: chunks cb .. cb + NT - 1 of the row, a shorter sequence that
     // starts cb chunks in (the launcher gives every segment at least one chunk)
-    const int seg = VARLEN ? 0 : (int)blockIdx.y;
-    const int cb = seg * sg.len;
+    const int seg = VARLEN ? 0 : seg_y;
+    const int cb = sg.base + seg * sg.len;
     if (!VARLEN) {
         const int rem = sq.len - cb * CH;
         sq.tok0 += (size_t)cb * CH;
@@ -1881,7 +1917,7 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
 #pragma unroll
                 for (int x = 0; x < 4; ++x) hacc[0][mt][x] = 16 * mt + 4 * lg + x == col - DV + ln ? 1.f : 0.f;
         } else if (sg.hin) {
-            load_state<DK, DV, 1>(hacc, sg.hin + (head * gridDim.y + seg) * DK * DV, 0, col, lane);
+            load_state<DK, DV, 1>(hacc, sg.hin + (head * nseg + seg) * DK * DV, 0, col, lane);
         } else {
             load_state<DK, DV, 1>(hacc, s0, head, col, lane);
         }
@@ -1950,10 +1986,10 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
         if (n < NT) step(n, tA, tB);
         if constexpr (XPORT) {
             if (col < DV)
-                store_state<DK, DV, 1>(hacc, sg.nout + (head * gridDim.y + seg) * DK * DV, 0, col, lane);
+                store_state<DK, DV, 1>(hacc, sg.nout + (head * nseg + seg) * DK * DV, 0, col, lane);
             else
-                store_state<DK, DK, 1>(hacc, sg.mout + (head * gridDim.y + seg) * DK * DK, 0, col - DV, lane);
-        } else if (seg == (int)gridDim.y - 1) {
+                store_state<DK, DK, 1>(hacc, sg.mout + (head * nseg + seg) * DK * DK, 0, col - DV, lane);
+        } else if (seg == nseg - 1) {
             store_state<DK, DV, 1>(hacc, sf, head, col, lane);
         }
     } else if (XPORT) {
@@ -2066,6 +2102,45 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
     }
 }
 
+template <int DK, int DV, int NW, bool VARLEN, bool XPORT = false>
+__global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_state_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const unsigned char* __restrict__ ws,
+    const unsigned char* __restrict__ wsq, const float* s0, float* sf, bf16* __restrict__ o, int T_max, int Hqk,
+    int Hv, int grp, int xcd_remap, const int* cu, int total, SegArgs sg)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    state_body<DK, DV, NW, VARLEN, XPORT>(k, v, ws, wsq, s0, sf, o, T_max, Hqk, Hv, grp, xcd_remap, cu, total, sg,
+                                          blockIdx.x, gridDim.x, blockIdx.y, gridDim.y, smem);
+}
+
+// The state pass of one piece of the rows (chunks sg.base .. sg.base + sg.len - 1) beside the
+// prep of the next piece (chunks c_base .. c_base + NTg - 1), in one launch: workgroups
+// 0 .. nstate - 1 run the state pass, the others (on the compute units it leaves free: one
+// workgroup per compute unit, as the LDS size allows no more) run prep units, one per wave at a
+// time.  The two parts share no data, and the launch boundary orders each piece's prep before
+// its state pass.
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_per_eu(2))) void chunk_overlap_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, unsigned char* __restrict__ ws, unsigned char* __restrict__ wsq,
+    const float* s0, float* sf, bf16* __restrict__ o, int T_max, int Hqk, int Hv, int grp, float scale,
+    int xcd_remap, SegArgs sg, int nstate, int c_base, int NTg, int nunits)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if ((int)blockIdx.x < nstate) {
+        state_body<DK, DV, NW, false, false>(k, v, ws, wsq, s0, sf, o, T_max, Hqk, Hv, grp, xcd_remap, nullptr, 0,
+                                             sg, blockIdx.x, nstate, 0, 1, smem);
+        return;
+    }
+    constexpr int NWAVE = SLW + NW + SOW;
+    const int w = threadIdx.x >> 6;
+    const int NT = (T_max + CH - 1) / CH;
+    const int npw = ((int)gridDim.x - nstate) * NWAVE;   // prep waves; nunits = B Hqk NTg units
+    for (int u = ((int)blockIdx.x - nstate) * NWAVE + w; u < nunits; u += npw)
+        prep_unit<DK, false>(q, k, g, beta, ws, wsq, T_max, Hqk, Hv, grp, NT, scale, nullptr, 0, u, c_base, NTg,
+                             smem + (size_t)w * PrepLds::bytes);
+}
+
 namespace {
 
 #ifdef GDN_TEST_HOOKS
@@ -2138,6 +2213,39 @@ bool use_split(const ChunkArgs& a)
     return (long)a.B * a.Hv < 192;
 }
 
+// Pieces of the split path: the rows cut into pieces of PIECE chunks; the prep of piece p + 1
+// runs in the same launch as the state pass of piece p, on the compute units the state pass
+// leaves free (chunk_overlap_kernel), and only piece 0's prep runs alone.  Taken when the state
+// pass leaves at least 32 compute units idle and the rows hold at least two pieces; uniform
+// batches only.  Measured on the 64K-token workload (48 value heads, 192 state workgroups on the
+// 256 compute units): the prep alone took 295 us on the whole chip and the state pass 1,297 us;
+// run side by side on 64 and 192 compute units they took 866 and 1,422 us.
+int piece_len() { return std::max(16, env_int("GDN_SPLIT_PIECE", 128)); }
+
+long split_state_blocks(const ChunkArgs& a) { return (long)a.B * a.Hv * (a.dv / choose_split_bv(a)); }
+
+// The shape takes pieces on a 256-compute-unit device; the workspace then holds the state
+// handed from piece to piece (a function of the arguments only).
+bool pieces_shape(const ChunkArgs& a)
+{
+    const long NT = ((long)a.T + CH - 1) / CH;
+    return !a.cu && use_split(a) && NT >= 2L * piece_len() && split_state_blocks(a) <= 256 - 32;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = -1;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int DK, int DV, int BV, bool GATED, bool VARLEN = false>
 hipError_t launch_fused_t(const ChunkArgs& a, hipStream_t st)
 {
@@ -2202,23 +2310,76 @@ hipError_t launch_state_t(const ChunkArgs& a, void* ws, hipStream_t st, SegArgs 
     return hipGetLastError();
 }
 
+// The prep of chunks c_base .. c_base + NTg - 1 of every row (all of them by default).
 template <int DK, bool VARLEN>
-hipError_t launch_prep_t(const ChunkArgs& a, void* ws, hipStream_t st)
+hipError_t launch_prep_t(const ChunkArgs& a, void* ws, hipStream_t st, int c_base = 0, int NTg = -1)
 {
     const int grp = a.Hv / a.Hqk;
     const int NT = (int)(((long)a.T + CH - 1) / CH);
-    const long nprep = (long)a.B * a.Hqk * NT;
+    if (NTg < 0) NTg = NT;
+    const long nprep = (long)a.B * a.Hqk * NTg;
     unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
     hipLaunchKernelGGL((chunk_prep_kernel<DK, VARLEN>), dim3((unsigned)nprep), dim3(64), 0, st, (const bf16*)a.q,
                        (const bf16*)a.k, a.g, a.beta, (unsigned char*)ws, wsq, a.T, a.Hqk, a.Hv, grp, NT,
-                       a.scale, nprep % 8 == 0 ? 1 : 0, a.cu, a.total);
+                       a.scale, nprep % 8 == 0 ? 1 : 0, a.cu, a.total, c_base, NTg);
     return hipGetLastError();
+}
+
+// The split path in pieces (see pieces_shape): piece 0's prep alone, then one launch per piece of
+// its state pass beside the next piece's prep, the last piece's state pass alone.  The state
+// passes hand the state on through the workspace.
+template <int DK, int DV, int NW>
+hipError_t launch_pieces_t(const ChunkArgs& a, void* ws, hipStream_t st, int ncu)
+{
+    constexpr int BV = 16 * NW;
+    constexpr int NWAVE = SLW + NW + SOW;
+    using L = SLds<DK, BV, NW>;
+    constexpr size_t lds = L::bytes > NWAVE * PrepLds::bytes ? L::bytes : NWAVE * PrepLds::bytes;
+    static_assert(lds <= 160 * 1024, "LDS budget");
+    auto kern = chunk_overlap_kernel<DK, DV, NW>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int NT = (int)(((long)a.T + CH - 1) / CH);
+    const int len = piece_len();
+    const int P = (NT + len - 1) / len;
+    const int grp = a.Hv / a.Hqk;
+    const long nstate = (long)a.B * a.Hv * (DV / BV);
+    const int remap = (nstate % 8 == 0) && ((nstate / 8) % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
+    unsigned char* wsq = (unsigned char*)ws + (size_t)a.B * a.Hv * NT * WS_CHUNK;
+    float* hand = reinterpret_cast<float*>(wsq + (size_t)a.B * a.Hqk * NT * ws_q_bytes<DK>());
+    e = launch_prep_t<DK, false>(a, ws, st, 0, std::min(len, NT));
+    for (int p = 0; p < P && e == hipSuccess; ++p) {
+        SegArgs sg{len, nullptr, nullptr, nullptr};
+        sg.base = p * len;
+        const float* s0p = p == 0 ? a.s0 : hand;
+        float* sfp = p == P - 1 ? a.sf : hand;
+        if (p + 1 < P) {
+            const int cn = (p + 1) * len, ntg = std::min(len, NT - cn);
+            hipLaunchKernelGGL(kern, dim3((unsigned)ncu), dim3(NWAVE * 64), lds, st, (const bf16*)a.q,
+                               (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, (unsigned char*)ws, wsq, s0p, sfp,
+                               (bf16*)a.o, a.T, a.Hqk, a.Hv, grp, a.scale, remap, sg, (int)nstate, cn, ntg,
+                               a.B * a.Hqk * ntg);
+            e = hipGetLastError();
+        } else {
+            ChunkArgs ap = a;
+            ap.s0 = s0p;
+            ap.sf = sfp;
+            e = launch_state_t<DK, DV, NW, false>(ap, ws, st, sg, 1);
+        }
+    }
+    return e;
 }
 
 template <int DK, int DV, bool VARLEN = false>
 hipError_t launch_split_t(const ChunkArgs& a, void* ws, hipStream_t st)
 {
     if (!VARLEN && a.cu) return launch_split_t<DK, DV, true>(a, ws, st);
+    if (!VARLEN && pieces_shape(a)) {
+        const int ncu = device_cus();
+        if (ncu - split_state_blocks(a) >= 32)
+            return choose_split_bv(a) == 16 ? launch_pieces_t<DK, DV, 1>(a, ws, st, ncu)
+                                            : launch_pieces_t<DK, DV, 2>(a, ws, st, ncu);
+    }
     hipError_t e = launch_prep_t<DK, VARLEN>(a, ws, st);
     if (e != hipSuccess) return e;
     const int NT = (int)(((long)a.T + CH - 1) / CH);
@@ -2409,7 +2570,8 @@ size_t chunk_mfma_workspace_bytes(const ChunkArgs& a)
 {
     if (!chunk_mfma_split(a)) return 0;
     const size_t NT = ((size_t)a.T + CH - 1) / CH;
-    return (size_t)a.B * NT * (a.Hv * (size_t)WS_CHUNK + a.Hqk * (size_t)CH * a.dk * 2);
+    const size_t hand = pieces_shape(a) ? (size_t)a.B * a.Hv * a.dk * a.dv * 4 : 0;
+    return (size_t)a.B * NT * (a.Hv * (size_t)WS_CHUNK + a.Hqk * (size_t)CH * a.dk * 2) + hand;
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, void* ws, hipStream_t st)

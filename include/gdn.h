@@ -81,7 +81,10 @@ typedef enum {
  * sequences: see gdn_chunk_fwd_kernel_name) needs, per 64-token chunk of each batch row,
  * 13,568 bytes per value head (T = (I + A)^{-1}, the masked Q K^T and the gate vectors) plus
  * 128 * dk bytes per query/key head (q as matrix-core operands), all built before the state
- * pass.  When the chains are too few to fill the GPU and long (gdn_chunk_fwd_kernel_name says
+ * pass reads them; rows of at least 256 chunks whose state pass leaves at least 32 of 256
+ * compute units free are run in pieces of 128 chunks (each piece's operands built beside the
+ * previous piece's state pass), and then B * Hv * dk * dv * 4 bytes more hold the state handed
+ * from piece to piece.  When the chains are too few to fill the GPU and long (gdn_chunk_fwd_kernel_name says
  * "mfma_scan") it is gdn_chunk_fwd_scan_workspace_bytes for the segment count chosen.  The result
  * depends only on the arguments.  Pure host function; needs no device; 0 for invalid sizes.
  */

@@ -476,7 +476,11 @@ def test_scan_segments_and_workspace():
     assert gdn.gdn_chunk_fwd_scan_segments(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_F32, 4) == 0
     # operands of the split path, then M and N of all segments but the last, then the entry states
     up = lambda x: (x + 255) // 256 * 256
-    prep = gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
+    # the split path's per-chunk operands (gdn_chunk_fwd's workspace holds, on this shape, also
+    # the state its pieces hand on, which the scan does not use)
+    split_ops = lambda dk: B * (T // 64) * (Hv * 13568 + Hqk * 64 * dk * 2)
+    prep = split_ops(128)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16) == prep + B * Hv * 128 * 128 * 4
     chains = B * Hv
     want = up(prep) + 2 * up(chains * 3 * 128 * 128 * 4) + up(chains * 4 * 128 * 128 * 4)
     assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, 4) == want
@@ -484,8 +488,7 @@ def test_scan_segments_and_workspace():
         up(chains * 128 * 128 * 4)
     assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, 0, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16, 4) == 0
     assert gdn.gdn_chunk_fwd_scan_workspace_bytes(B, T, Hqk, Hv, 128, 128, 32, gdn.GDN_BF16, 4) == 0
-    assert gdn.gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, 64, 128, 64, gdn.GDN_BF16) == \
-        up(gdn.gdn_chunk_fwd_workspace_bytes(B, T, Hqk, Hv, 64, 128, 64, gdn.GDN_BF16))
+    assert gdn.gdn_chunk_transport_workspace_bytes(B, T, Hqk, Hv, 64, 128, 64, gdn.GDN_BF16) == up(split_ops(64))
 
 
 @pytest.mark.parametrize("over,status", [
@@ -543,8 +546,10 @@ def test_chunk_fwd_routes_scarce_long_chains_to_the_scan(monkeypatch, hooks):
     assert name(1, 20000, 1, 1) == "mfma_scan"
     monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")
     assert name(1, 65536, 2, 6) == "mfma_split"
+    # the split path's operands and the state its pieces hand on: as large as the one-segment
+    # scan's operands and entry states
     assert ws(1, 65536, 2, 6) == gdn.gdn_chunk_fwd_scan_workspace_bytes(1, 65536, 2, 6, 128, 128, 64,
-                                                                        gdn.GDN_BF16, 1) - 6 * 128 * 128 * 4
+                                                                        gdn.GDN_BF16, 1)
 
 
 def test_release_library_reads_no_environment(monkeypatch):

@@ -519,3 +519,31 @@ def test_chunk_gated_qwen3next_full():
     o_ref, s_ref = oracle_prefill(d)
     y_ref = oracle.gated_rmsnorm(o_ref, f64(gz["z"]), gz["weight"])
     check_gated("gated qwen3next", "bf16", host(y), y_ref, host(sf), s_ref)
+
+
+@pytest.mark.parametrize("T,Hqk,Hv,bv,s0", [
+    (2048, 2, 4, 16, True), (4160, 2, 6, 32, True), (3000, 2, 2, 32, False), (2100, 1, 3, 16, True),
+])
+def test_split_pieces_bitwise(monkeypatch, hooks, T, Hqk, Hv, bv, s0):
+    """The split path cut into pieces of 16 chunks (each piece's state pass in one launch with the
+    next piece's prep, the state handed on through the workspace; ragged last pieces) gives the
+    uncut split path's O and final state bit for bit, and the oracle's to tolerance."""
+    monkeypatch.setenv("GDN_MFMA_PATH", "split")
+    monkeypatch.setenv("GDN_SPLIT_BV", str(bv))
+    monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")   # not the affine scan, which few chains would take
+    say(f"split pieces T={T} Hqk={Hqk} Hv={Hv} bv={bv} s0={s0}")
+    d = gi.generate(B=1, T=T, Hqk=Hqk, Hv=Hv, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.05 if s0 else 0.0,
+                    seed=T + Hv + bv)
+    t = dev(d)
+    args = (1, T, Hqk, Hv, 128, 128, 64, gdn.GDN_BF16)
+    monkeypatch.setenv("GDN_SPLIT_PIECE", "100000")
+    whole_ws = gdn.gdn_chunk_fwd_workspace_bytes(*args)
+    o2, s2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    monkeypatch.setenv("GDN_SPLIT_PIECE", "16")
+    # the pieced route's workspace also holds the state handed from piece to piece
+    assert gdn.gdn_chunk_fwd_workspace_bytes(*args) == whole_ws + Hv * 128 * 128 * 4
+    o1, s1 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = oracle_prefill(d)
+    check(f"split pieces T={T} Hv={Hv}", "bf16", host(o1), o_ref, host(s1), s_ref)
