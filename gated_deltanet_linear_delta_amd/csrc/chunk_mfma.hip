@@ -317,9 +317,11 @@ __device__ __forceinline__ void apply_kt(floatx4 (&hacc)[NTN][DK / 16], const op
 // tile and the gate vectors are fetched up front too.
 // CHDEC: the state decays by a factor per dk row (ech[m], one decay per key channel) instead of
 // the scalar exp(gc_63).
-template <int DK, int NTN, int VP, bool KT = false, bool CHDEC = false, typename TF>
+// RV32: Vc holds beta V already formed, float32 and transposed (column c, row r at c * VP + r),
+// so that R takes one multiply-add per element.
+template <int DK, int NTN, int VP, bool KT = false, bool CHDEC = false, bool RV32 = false, typename TF>
 __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const op_t* Ks,
-                                            const bf16* Vc, TF&& tfrag, const float* vs, int lane,
+                                            const void* Vc, TF&& tfrag, const float* vs, int lane,
                                             opx8 (&hb)[NTN][DK / 32], opx8 (&db)[NTN][2],
                                             opx8 (&dtb)[NTN][2], opx8 (*akt)[DK / 16] = nullptr,
                                             const float* ech = nullptr)
@@ -337,6 +339,7 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
     opx8 ak[KB][4];
     opx8 at[4][2];
     bf16x4 vv[NTN][4];
+    floatx4 rv[NTN][4];
     floatx4 bt[4], beg[4], ed[2][2];
     auto load_k = [&](int kk) {
 #pragma unroll
@@ -349,14 +352,20 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
 #pragma unroll
             for (int cb = 0; cb <= mt / 2; ++cb) at[mt][cb] = tfrag(mt, cb);
     };
-    // V rows 16mt+4lg..+3 of this lane's columns via the transposing read; row vectors
+    // V rows 16mt+4lg..+3 of this lane's columns via the transposing read (or beta V as four
+    // consecutive float32 rows); row vectors
     auto load_rows = [&] {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-            for (int nt = 0; nt < NTN; ++nt)
-                vv[nt][mt] = __builtin_bit_cast(bf16x4, ld_tr(Vc + (16 * mt + 4 * lg + (ln >> 2)) * VP + 16 * nt + 4 * (ln & 3)));
-            bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
+            for (int nt = 0; nt < NTN; ++nt) {
+                if constexpr (RV32)
+                    rv[nt][mt] = ld4s(static_cast<const float*>(Vc) + (16 * nt + ln) * VP + 16 * mt + 4 * lg);
+                else
+                    vv[nt][mt] = __builtin_bit_cast(
+                        bf16x4, ld_tr(static_cast<const bf16*>(Vc) + (16 * mt + 4 * lg + (ln >> 2)) * VP + 16 * nt + 4 * (ln & 3)));
+            }
+            if constexpr (!RV32) bt[mt] = ld4s(vs + V_B * CH + 16 * mt + 4 * lg);
             beg[mt] = ld4s(vs + V_BEG * CH + 16 * mt + 4 * lg);
         }
     };
@@ -433,7 +442,12 @@ __device__ __forceinline__ void chain_delta(floatx4 (&hacc)[NTN][DK / 16], const
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) rr[mt][x] = bt[mt][x] * (float)vv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
+            for (int x = 0; x < 4; ++x) {
+                if constexpr (RV32)
+                    rr[mt][x] = rv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
+                else
+                    rr[mt][x] = bt[mt][x] * (float)vv[nt][mt][x] - beg[mt][x] * X[nt][mt][x];
+            }
         rbf[nt][0] = pack_perm(rr[0], rr[1]);
         rbf[nt][1] = pack_perm(rr[2], rr[3]);
     }
@@ -1727,14 +1741,20 @@ struct SegArgs {
 template <int DK, int BV, int NW>
 struct SLds {
     static constexpr int KP = DK + 8;
-    static constexpr int VP = BV + 16;
+    // With one chain wave (its per-chunk latency is the whole period) the loaders stage beta V,
+    // float32 and transposed (pitch RVP: conflict-free 16-byte reads), which takes two vector
+    // instructions per element off the chain; with two the loaders' extra work costs more than
+    // it saves (measured on the 64K-token workload), and V stays bf16 row-major (pitch VP).
+    static constexpr bool RV32 = NW == 1;
+    static constexpr int RVP = CH + 4;
+    static constexpr int VP = RV32 ? RVP : BV + 16;
     // K, V and the state-step vectors in two slots: the chain waves read chunk n while the
     // loaders stage chunk n + 1
     static constexpr size_t kbytes = (size_t)CH * KP * 2;
-    static constexpr size_t vbytes = (size_t)CH * VP * 2;
+    static constexpr size_t vbytes = RV32 ? (size_t)BV * RVP * 4 : (size_t)CH * VP * 2;
     static constexpr size_t cvbytes = (size_t)4 * CH * 4;
     static constexpr size_t k = 0;                                   // K   [2][64][KP] f16
-    static constexpr size_t v = k + 2 * kbytes;                      // V   [2][64][VP] bf16
+    static constexpr size_t v = k + 2 * kbytes;                      // beta V [2][BV][RVP] f32 or V [2][64][VP] bf16
     static constexpr size_t cv = v + 2 * vbytes;                     // rows V_B..V_EC [2][4][64] f32
     // chain -> output hand-over, [2][NW]: hb (DK/32 fragments) then db (2), each fragment 64
     // lanes x 16 bytes
@@ -1808,7 +1828,7 @@ __device__ __forceinline__ void state_body(
     const unsigned char* wh = ws + (head * NTS + cb) * WS_CHUNK;
     const bool mcols = XPORT && c0 >= DV;       // transport columns of M: V is zero
     auto kslot = [&](int c) { return reinterpret_cast<op_t*>(smem + L::k + (size_t)(c & 1) * L::kbytes); };
-    auto vslot = [&](int c) { return reinterpret_cast<bf16*>(smem + L::v + (size_t)(c & 1) * L::vbytes); };
+    auto vslot = [&](int c) { return smem + L::v + (size_t)(c & 1) * L::vbytes; };
     auto cvslot = [&](int c) { return reinterpret_cast<float*>(smem + L::cv + (size_t)(c & 1) * L::cvbytes); };
     auto hxp = [&](int c, int cw) {
         return reinterpret_cast<opx8*>(smem + L::hx + ((size_t)(c & 1) * NW + cw) * L::hx_frags * 1024);
@@ -1824,6 +1844,7 @@ __device__ __forceinline__ void state_body(
         struct LdBuf {
             bf16x8 rk[PK][2];
             bf16x8 rv[PV];
+            float rb[PV];   // beta of each V run's row
             floatx4 rc;
         };
         // K pair-run s of a chunk: row s / RP, 32-column block pr / 2 (pr = s % RP), half
@@ -1850,17 +1871,19 @@ __device__ __forceinline__ void state_body(
             }
             const bf16* vc = vb + (size_t)t0 * vrow;
             if (!mcols) {
+                const float* bc = reinterpret_cast<const float*>(wh + (size_t)c * WS_CHUNK + WS_CV) + V_B * CH;
 #pragma unroll
                 for (int p = 0; p < PV; ++p) {
                     const int s = min(ltid + p * NLT, CH * RV - 1);
                     r.rv[p] = *reinterpret_cast<const bf16x8*>(vc + min(s / RV, n - 1) * vrow + (s % RV) * 8);
+                    if constexpr (L::RV32) r.rb[p] = bc[s / RV];   // 0 past the last row: clamped rows add nothing
                 }
             }
             if (ltid < CVR) r.rc = *reinterpret_cast<const floatx4*>(wh + (size_t)c * WS_CHUNK + WS_CV + 16 * ltid);
         };
         auto stage_chain = [&](int c, const LdBuf& r) {
             op_t* Ks = kslot(c);
-            bf16* Vs = vslot(c);
+            unsigned char* Vs = vslot(c);
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
                 opx8* dst = reinterpret_cast<opx8*>(Ks + kq_r[p] * L::KP + 16 * ((ltid + p * NLT) % RP));
@@ -1870,17 +1893,26 @@ __device__ __forceinline__ void state_body(
 #pragma unroll
                 for (int p = 0; p < PV; ++p) {
                     const int s = ltid + p * NLT;
-                    if (s < CH * RV) *reinterpret_cast<bf16x8*>(Vs + (s / RV) * L::VP + (s % RV) * 8) = r.rv[p];
+                    if (s < CH * RV) {
+                        if constexpr (L::RV32) {
+                            // beta V, float32, transposed: the 8 columns of this run at row s / RV
+                            float* dst = reinterpret_cast<float*>(Vs) + (s % RV) * 8 * L::RVP + s / RV;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) dst[e * L::RVP] = r.rb[p] * (float)r.rv[p][e];
+                        } else {
+                            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(Vs) + (s / RV) * L::VP + (s % RV) * 8) = r.rv[p];
+                        }
+                    }
                 }
             }
             if (ltid < CVR) reinterpret_cast<floatx4*>(cvslot(c))[ltid] = r.rc;
         };
         if (mcols) {
             // the M columns' V is zero in both slots for the whole segment
-            for (int s = ltid; s < CH * L::VP / 8; s += NLT)
+            for (int s = ltid; s < (int)(L::vbytes / 16); s += NLT)
 #pragma unroll
                 for (int slot = 0; slot < 2; ++slot)
-                    *reinterpret_cast<bf16x8*>(vslot(slot) + 8 * s) = bf16x8{};
+                    reinterpret_cast<floatx4*>(vslot(slot))[s] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         // Prefetches are issued unconditionally (chunk index clamped to the last chunk; the
         // extra loads at the end are harmless) so that every path through the loop has the same
@@ -1961,7 +1993,9 @@ __device__ __forceinline__ void state_body(
             const op_t* Ks = kslot(n);
             opx8 hb[1][KB], db[1][2], dtb[1][2];
             opx8 akt[2][MT];
-            chain_delta<DK, 1, L::VP, true>(hacc, Ks, vslot(n) + cw * 16, [&](int mt, int cb) { return tc[tblk(mt, cb)]; },
+            const void* Vc = L::RV32 ? (const void*)(reinterpret_cast<const float*>(vslot(n)) + cw * 16 * L::RVP)
+                                     : (const void*)(reinterpret_cast<const bf16*>(vslot(n)) + cw * 16);
+            chain_delta<DK, 1, L::VP, true, false, L::RV32>(hacc, Ks, Vc, [&](int mt, int cb) { return tc[tblk(mt, cb)]; },
                                             cvslot(n), lane, hb, db, dtb, akt);
             opx8* hx = hxp(n, cw);
 #pragma unroll
