@@ -482,7 +482,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen36_long_prefill")
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--quick", action="store_true",
+                    help="headline workload only, warm calls only (no cold-cache timing): for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gated", action="store_true",
                     help="time gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm) instead")
@@ -522,7 +523,7 @@ def main():
         print(json.dumps({"leg": args.leg, **legs[args.leg]()}), flush=True)
         return
     print(f"bench: prefill {cfg}{' (gated)' if args.gated else ''}", file=sys.stderr, flush=True)
-    r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi, gated=args.gated)
+    r = bench_prefill(cfg, args.steps, args.warmup, torch, gdn, gi, gated=args.gated, cold_steps=0 if args.quick else 5)
     tokens = cfg.B * cfg.T
     ms = r["wall"] / args.steps * 1e3
     line = {
