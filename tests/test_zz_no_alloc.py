@@ -1,7 +1,8 @@
 """gdn_chunk_fwd_noalloc (the prefill with its workspace in the library's fixed per-device array)
 against gdn_chunk_fwd with a caller workspace, through the C ABI: the same kernels on the same
 inputs give the same bits, and both meet the oracle's tolerance.  Two calls in a row on the
-split route (the second smaller, so it runs over what the first left in the array), one on the
+split route (the second smaller, so it runs over what the first left in the array), the same on
+the split route in pieces, one on the
 fused route (no workspace), and sizes beyond the array's limit rejected with nothing written."""
 import numpy as np
 import pytest
@@ -43,6 +44,25 @@ def test_noalloc_matches_chunk_fwd_twice_split_route():
         assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
         oo, so = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
         check(f"noalloc {sh}", "bf16", host(o), oo, host(s), so)
+
+
+def test_noalloc_split_route_in_pieces():
+    """A shape whose rows are long enough for the pieced split path (256 chunks, 17 chains that
+    leave compute units free) and whose workspace, with the state handed between pieces, still
+    fits the array; then a smaller call over what it left."""
+    sh = dict(B=1, T=16384, Hqk=1, Hv=17)
+    args = (sh["B"], sh["T"], sh["Hqk"], sh["Hv"], 128, 128, 64, gdn.GDN_BF16)
+    ws = gdn.gdn_chunk_fwd_workspace_bytes(*args)
+    say(f"noalloc pieces {sh} workspace={ws}")
+    assert gdn.gdn_chunk_fwd_kernel_name(*args) == "mfma_split"
+    # operands of 256 chunks plus the handed-on state: the shape takes pieces
+    assert ws == 256 * (17 * 13568 + 64 * 128 * 2) + 17 * 128 * 128 * 4 <= gdn.GDN_NOALLOC_SCRATCH_BYTES
+    for i, (T, Hv, seed) in enumerate(((16384, 17, 21), (700, 3, 22))):
+        d = gi.generate(B=1, T=T, Hqk=1, Hv=Hv, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.02, seed=seed)
+        o, s, o_ref, s_ref = both(d)
+        assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+        oo, so = oracle.recurrent(f64(d["q"]), f64(d["k"]), f64(d["v"]), d["g"], d["beta"], d["s0"])
+        check(f"noalloc pieces call {i}", "bf16", host(o), oo, host(s), so)
 
 
 def test_noalloc_fused_route_and_in_place_state():
