@@ -34,6 +34,7 @@ __all__ = [
     "gdn_kda_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_varlen", "gdn_chunk_fwd_varlen_workspace_bytes",
     "gdn_chunk_fwd_scan", "gdn_chunk_fwd_scan_workspace_bytes", "gdn_chunk_fwd_scan_segments", "gdn_chunk_transport",
     "gdn_chunk_transport_workspace_bytes", "EXPORTED_SYMBOLS", "test_hooks", "gdn_chunk_fwd_noalloc",
+    "debug_checks", "gdn_debug_take_flags", "gdn_debug_self_test",
     "GDN_NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -61,9 +62,12 @@ class GdnError(RuntimeError):
 
 def library_path(variant: str = "release") -> str:
     """libgdn.so, or (variant "hooks") libgdn_hooks.so: the same kernels, with the automatic route
-    choice open to environment overrides (GDN_MFMA_PATH, GDN_MFMA_BV, GDN_SPLIT_BV,
-    GDN_DISABLE_MFMA, GDN_SCAN_SEGMENTS) so that tests can run every kernel family."""
-    return os.path.join(_HERE, "libgdn.so" if variant == "release" else "libgdn_hooks.so")
+    choice open to environment overrides (GDN_MFMA_PATH, GDN_MFMA_BV, GDN_SPLIT_BV, GDN_SPLIT_PIECE,
+    GDN_DISABLE_MFMA, GDN_SCAN_SEGMENTS) so that tests can run every kernel family; or (variant
+    "debug") libgdn_debug.so: the hooks build whose prefill kernels also check their indices
+    (include/gdn_debug.h)."""
+    name = {"release": "libgdn.so", "hooks": "libgdn_hooks.so", "debug": "libgdn_debug.so"}[variant]
+    return os.path.join(_HERE, name)
 
 
 @contextlib.contextmanager
@@ -77,6 +81,32 @@ def test_hooks():
         yield
     finally:
         _variant = prev
+
+
+@contextlib.contextmanager
+def debug_checks():
+    """Route every call made inside the block through libgdn_debug.so (a testing aid); read its
+    failed index checks with gdn_debug_take_flags()."""
+    global _variant
+    prev = _variant
+    load_library("debug")
+    _variant = "debug"
+    try:
+        yield
+    finally:
+        _variant = prev
+
+
+def gdn_debug_take_flags() -> int:
+    """The debug build's failed index checks since the last call (0: none), then cleared."""
+    lib = load_library("debug")
+    return int(lib.gdn_debug_take_flags())
+
+
+def gdn_debug_self_test(bit: int) -> None:
+    """Make the debug build's check at `bit` fail once (the flags' path itself under test)."""
+    if load_library("debug").gdn_debug_self_test(bit) != 0:
+        raise GdnError(7, "gdn_debug_self_test")
 
 
 def load_library(variant: str | None = None):
@@ -98,6 +128,11 @@ def load_library(variant: str | None = None):
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
     lib.gdn_chunk_fwd_kernel_name.argtypes = [i] * 7 + [i]
     lib.gdn_chunk_fwd_kernel_name.restype = ctypes.c_char_p
+    if hasattr(lib, "gdn_debug_take_flags"):
+        lib.gdn_debug_take_flags.argtypes = []
+        lib.gdn_debug_take_flags.restype = ctypes.c_uint
+        lib.gdn_debug_self_test.argtypes = [i]
+        lib.gdn_debug_self_test.restype = i
     lib.gdn_status_string.argtypes = [i]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_qkv_prologue.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp] + [i] * 7 + [i, f, vp]

@@ -2,7 +2,9 @@
 
 Also builds libgdn_hooks.so, the same library with chunk_mfma.hip compiled with GDN_TEST_HOOKS:
 that build lets environment variables override the automatic route choice so that the tests
-can run every kernel family on small shapes.  The release library reads no environment."""
+can run every kernel family on small shapes.  The release library reads no environment.  And
+libgdn_debug.so: the hooks build with GDN_DEBUG too, whose prefill kernels check their indices
+and report failed checks through gdn_debug_take_flags (include/gdn_debug.h)."""
 from __future__ import annotations
 
 import os
@@ -16,6 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 LIB_HOOKS = os.path.join(PKG, "libgdn_hooks.so")
+LIB_DEBUG = os.path.join(PKG, "libgdn_debug.so")
 SOURCES = ["api.cpp", "decode.hip", "chunk_simt.hip", "chunk_mfma.hip", "layer_ops.hip", "chunk_bwd.hip", "kda.hip",
            "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,6 +41,10 @@ def build(verbose: bool = False) -> str:
     hooks_obj = os.path.join(OBJDIR, "chunk_mfma_hooks.o")
     jobs.append(("chunk_mfma.hip (test hooks)", hooks_obj,
                  [HIPCC] + FLAGS + ["-DGDN_TEST_HOOKS", "-x", "hip", "-c", os.path.join(CSRC, "chunk_mfma.hip"), "-o", hooks_obj]))
+    debug_obj = os.path.join(OBJDIR, "chunk_mfma_debug.o")
+    jobs.append(("chunk_mfma.hip (index checks)", debug_obj,
+                 [HIPCC] + FLAGS + ["-DGDN_TEST_HOOKS", "-DGDN_DEBUG", "-x", "hip", "-c", os.path.join(CSRC, "chunk_mfma.hip"),
+                                    "-o", debug_obj]))
     procs = []
     for label, _, cmd in jobs:
         if verbose:
@@ -57,7 +64,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     hooks_objs = [hooks_obj if o.endswith(os.sep + "chunk_mfma.o") else o for o in objs]
-    for out, parts in ((LIB, objs), (LIB_HOOKS, hooks_objs)):
+    debug_objs = [debug_obj if o.endswith(os.sep + "chunk_mfma.o") else o for o in objs]
+    for out, parts in ((LIB, objs), (LIB_HOOKS, hooks_objs), (LIB_DEBUG, debug_objs)):
         tmp = out + ".tmp%d" % os.getpid()
         subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + parts + ["-o", tmp], check=True)
         os.replace(tmp, out)

@@ -94,6 +94,24 @@ __device__ long long gdn_phase_ts[16][32][8];
     } while (0)
 #endif
 
+// Index checks of the debug build (-DGDN_DEBUG, libgdn_debug.so): a failed check sets its bit in
+// gdn_debug_flags with a vector atomic OR and the kernel goes on (every checked access is also
+// clamped or guarded by the code around it), so a bad index shows up as a flag that
+// gdn_debug_take_flags returns to the host, not as a fault.  Bits: 0 prep unit, 1 state-pass
+// chain, 2 state-pass segment, 3 state-pass workspace chunk, 4 state-pass output token, 5
+// pipelined-kernel chain and tokens, 6 combined launch, 7 fused-kernel chain and tokens.
+#ifdef GDN_DEBUG
+__device__ unsigned int gdn_debug_flags;
+#define GDN_CHECK(cond, bit)                                                     \
+    do {                                                                          \
+        if (!(cond)) atomicOr(&gdn_debug_flags, 1u << (bit));                     \
+    } while (0)
+#else
+#define GDN_CHECK(cond, bit) \
+    do {                     \
+    } while (0)
+#endif
+
 namespace {
 
 typedef _Float16 op_t;
@@ -715,6 +733,8 @@ __global__ __launch_bounds__(NTHR, 1) void chunk_mfma_kernel(
     const ChainId id = chain_id(NTILE, Hqk, grp, xcd_remap);
     const int b = id.b, i = id.i, j = id.j;
     const int c0 = id.tile * BV;
+    GDN_CHECK((int)gridDim.x % (Hv * NTILE) == 0 && b < (int)gridDim.x / (Hv * NTILE) && i < Hqk && j < Hv &&
+                  j / grp == i, 7);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1265,6 +1285,7 @@ __device__ __forceinline__ void prep_unit(const bf16* __restrict__ q, const bf16
     const int c = c_base + u % NTg;
     const int b = u / NTg;
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+    GDN_CHECK(u >= 0 && c >= 0 && c < NT && NTg >= 1 && c_base + NTg <= NT && grp * Hqk == Hv, 0);
     const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
     const int t0 = c * CH;
     if (VARLEN && t0 >= sq.len) return;   // past this sequence's last chunk
@@ -1489,6 +1510,9 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
     const int lane = threadIdx.x & 63;
     const SeqSpan sq = VARLEN ? seq_span(cu, b, T_max, total) : SeqSpan{(size_t)b * T_max, T_max};
     const int T_len = sq.len;
+    GDN_CHECK((int)gridDim.x % (Hv * NTILE) == 0 && b < (int)gridDim.x / (Hv * NTILE) && i < Hqk && j < Hv &&
+                  j / grp == i && T_len >= 0 && T_len <= T_max &&
+                  sq.tok0 + T_len <= (VARLEN ? (size_t)total : (size_t)(gridDim.x / (Hv * NTILE)) * T_max), 5);
     if (VARLEN && T_len == 0) {
         // an empty sequence: the final state is the initial one (every wave leaves here, before
         // any barrier)
@@ -1789,6 +1813,9 @@ __device__ __forceinline__ void state_body(
     const ChainId id = chain_id_of(blk, nblk, NTILE, Hqk, grp, xcd_remap);
     const int b = id.b, i = id.i, j = id.j;
     const int c0 = id.tile * BV;
+    const int nrows = nblk / (Hv * NTILE);   // batch rows (sequences) of the launch
+    GDN_CHECK(blk < nblk && nblk % (Hv * NTILE) == 0 && b < nrows && i < Hqk && j < Hv && j / grp == i &&
+                  id.tile < NTILE && seg_y < nseg, 1);
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -1827,6 +1854,8 @@ __device__ __forceinline__ void state_body(
     const size_t v_row = (size_t)Hv * DV;
     const unsigned char* wh = ws + (head * NTS + cb) * WS_CHUNK;
     const bool mcols = XPORT && c0 >= DV;       // transport columns of M: V is zero
+    GDN_CHECK(NT >= 1 && cb >= 0 && cb + NT <= NTS && T_len <= (NTS - cb) * CH &&
+                  sq.tok0 + T_len <= (VARLEN ? (size_t)total : (size_t)nrows * T_max), 2);
     auto kslot = [&](int c) { return reinterpret_cast<op_t*>(smem + L::k + (size_t)(c & 1) * L::kbytes); };
     auto vslot = [&](int c) { return smem + L::v + (size_t)(c & 1) * L::vbytes; };
     auto cvslot = [&](int c) { return reinterpret_cast<float*>(smem + L::cv + (size_t)(c & 1) * L::cvbytes); };
@@ -1862,6 +1891,7 @@ __device__ __forceinline__ void state_body(
         }
         auto load_chain = [&](int c, LdBuf& r) {
             const int t0 = c * CH, n = min(CH, T_len - t0);
+            GDN_CHECK(c >= 0 && c < NT && n >= 1 && (head * NTS + cb + c) < (size_t)nrows * Hv * NTS, 3);
             const bf16* kc = kb_ + (size_t)t0 * qk_row;
 #pragma unroll
             for (int p = 0; p < PK; ++p) {
@@ -2096,6 +2126,7 @@ __device__ __forceinline__ void state_body(
                     for (int t = 0; t < 2; ++t) {
                         const int tok = 16 * ctile(t) + ln;
                         if (tok < nv) {
+                            GDN_CHECK(sq.tok0 + t0 + tok < (VARLEN ? (size_t)total : (size_t)nrows * T_max), 4);
                             const bf16x4 ov = {(bf16)OT[t][0], (bf16)OT[t][1], (bf16)OT[t][2], (bf16)OT[t][3]};
                             *reinterpret_cast<bf16x4*>(ob + (size_t)(t0 + tok) * v_row + 16 * cgw + 4 * lg) = ov;
                         }
@@ -2161,6 +2192,7 @@ __global__ __launch_bounds__((SLW + NW + SOW) * 64) __attribute__((amdgpu_waves_
     int xcd_remap, SegArgs sg, int nstate, int c_base, int NTg, int nunits)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    GDN_CHECK(nstate >= 1 && nstate < (int)gridDim.x && nunits == nunits / (Hqk * NTg) * Hqk * NTg && sg.base >= 0, 6);
     if ((int)blockIdx.x < nstate) {
         state_body<DK, DV, NW, false, false>(k, v, ws, wsq, s0, sf, o, T_max, Hqk, Hv, grp, xcd_remap, nullptr, 0,
                                              sg, blockIdx.x, nstate, 0, 1, smem);
@@ -3085,5 +3117,33 @@ extern "C" int gdn_phase_trace_read(long long* host)
 {
     return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::gdn_phase_ts), sizeof(gdn::gdn_phase_ts), 0,
                                     hipMemcpyDeviceToHost);
+}
+#endif
+
+#ifdef GDN_DEBUG
+namespace gdn {
+namespace {
+// one failed check at the given bit, and nothing else: the flags' path end to end
+__global__ void debug_fail_kernel(int bit) { GDN_CHECK(threadIdx.x != 0, bit); }
+}  // namespace
+}  // namespace gdn
+
+extern "C" int gdn_debug_self_test(int bit)
+{
+    if (bit < 0 || bit > 31) return -1;
+    hipLaunchKernelGGL(gdn::debug_fail_kernel, dim3(1), dim3(64), 0, nullptr, bit);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The index checks that failed since the last call (bits as in GDN_CHECK), then cleared; the
+// current device's copy.  Exported only by the debug build.
+extern "C" unsigned int gdn_debug_take_flags(void)
+{
+    unsigned int h = 0;
+    const unsigned int z = 0;
+    if (hipDeviceSynchronize() != hipSuccess) return 0xffffffffu;
+    if (hipMemcpyFromSymbol(&h, HIP_SYMBOL(gdn::gdn_debug_flags), sizeof(h)) != hipSuccess) return 0xffffffffu;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(gdn::gdn_debug_flags), &z, sizeof(z)) != hipSuccess) return 0xffffffffu;
+    return h;
 }
 #endif

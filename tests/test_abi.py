@@ -30,6 +30,22 @@ def test_header_symbols_exported():
         getattr(lib, "gdn_oracle_recurrent")
 
 
+def test_debug_library_exports():
+    """libgdn_debug.so exports every gdn.h function and the one call of gdn_debug.h; the release
+    library does not export the debug call."""
+    src = open(os.path.join(ROOT, "include", "gdn_debug.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    debug_names = sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+    assert debug_names == ["gdn_debug_self_test", "gdn_debug_take_flags"]
+    dbg = gdn.load_library("debug")
+    for n in header_functions() + debug_names:
+        assert hasattr(dbg, n), n
+    for n in debug_names:
+        with pytest.raises(AttributeError):
+            getattr(gdn.load_library(), n)
+    assert dbg.gdn_debug_self_test(32) == -1 and dbg.gdn_debug_self_test(-1) == -1   # no device touched
+
+
 def test_status_strings_and_queries():
     for s in range(9):
         assert gdn.gdn_status_string(s)
