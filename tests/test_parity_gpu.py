@@ -547,3 +547,34 @@ def test_split_pieces_bitwise(monkeypatch, hooks, T, Hqk, Hv, bv, s0):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     o_ref, s_ref = oracle_prefill(d)
     check(f"split pieces T={T} Hv={Hv}", "bf16", host(o1), o_ref, host(s1), s_ref)
+
+
+def test_split_pieces_in_place_state_and_gated(monkeypatch, hooks):
+    """The pieced split path with the final state written over the initial one (piece 0 reads it,
+    the last piece writes it, the pieces between hand the state on through the workspace), and
+    under gdn_chunk_fwd_gated (O through the workspace, then the norm): bit for bit the uncut
+    split path's results."""
+    monkeypatch.setenv("GDN_MFMA_PATH", "split")
+    monkeypatch.setenv("GDN_SPLIT_BV", "16")
+    monkeypatch.setenv("GDN_SCAN_SEGMENTS", "0")
+    d = gi.generate(B=2, T=2200, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=3.0, s0_std=0.05, seed=31)
+    t = dev(d)
+    rng = np.random.Generator(np.random.PCG64(32))
+    z = torch.from_numpy(rng.standard_normal((2, 2200, 4, 128)).astype(np.float32)).to("cuda:0").to(torch.bfloat16)
+    w = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(128)).astype(np.float32)).to("cuda:0")
+    res = {}
+    for piece in ("100000", "16"):
+        monkeypatch.setenv("GDN_SPLIT_PIECE", piece)
+        st = t["s0"].clone()
+        o, s = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], st, final_state=st, chunk=64)
+        assert s.data_ptr() == st.data_ptr()
+        y, sy = gdn.gdn_chunk_fwd_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], z, w, t["s0"], chunk=64)
+        torch.cuda.synchronize()
+        res[piece] = (o, st, y, sy)
+    args = (2, 2200, 2, 4, 128, 128, 64, gdn.GDN_BF16)
+    assert gdn.gdn_chunk_fwd_workspace_bytes(*args) == 2 * 35 * (4 * 13568 + 2 * 64 * 128 * 2) + 2 * 4 * 128 * 128 * 4
+    a, b = res["100000"], res["16"]
+    for x, y_ in zip(a, b):
+        assert torch.equal(x, y_)
+    o_ref, s_ref = oracle_prefill(d)
+    check("split pieces in place", "bf16", host(b[0]), o_ref, host(b[1]), s_ref)
