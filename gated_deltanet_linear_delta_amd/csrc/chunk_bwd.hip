@@ -914,8 +914,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
                        (const T*)a.q, (const T*)a.k, a.g, a.beta, Aw, a.T, a.Hqk, a.Hv, grp, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // 1 + 2. the states entering every chunk and the reverse state pass, in one launch
-    {
+    // 1 + 2. the states entering every chunk and the reverse state pass, in one launch: on the
+    // float16 matrix cores for bf16 inputs where that kernel takes the shape
+    if (bwd_pass16_supported(a)) {
+        e = launch_bwd_pass16(a, Hs, dHs, Aw, st);
+        if (e != hipSuccess) return e;
+    } else {
         constexpr int BV = DV < BW_BV ? DV : BW_BV;
         constexpr size_t lb = SimtLds<DK, BV>::bytes > DhLds<DK>::bytes ? SimtLds<DK, BV>::bytes : DhLds<DK>::bytes;
         static_assert(lb <= 160 * 1024, "LDS budget");

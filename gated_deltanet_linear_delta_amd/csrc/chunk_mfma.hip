@@ -3110,6 +3110,313 @@ hipError_t launch_kda_mfma(const KdaArgs& a, void* ws, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
+// =======================================================================================
+// The backward pass's two sequential passes on the float16 matrix cores (bf16 inputs, chunks of
+// 32 tokens, the backward's own chunking): the states entering every chunk (the forward chunk
+// step again, without its output) and the reverse state pass, which stores each chunk's
+// exit-state gradient and finally dS0 (the algebra is in chunk_bwd.hip's header).  The chunk
+// matrices come formed from the backward's gram kernel (float32 A, M, G, T and the decay
+// exponentials per (batch, value head, chunk)); T itself is applied, not a substitution with A.
+// Per chunk of the reverse pass (rows r of the chunk, dh' the exit-state gradient, 16 columns
+// per chain wave):
+//   dDelta = diag(e^(gL - gc)) K dh' + M^T dO,   dR = T^T dDelta,
+//   dh = e^gL dh' + (scale Q)^T diag(e^gc) dO - K^T diag(beta e^gc) dR.
+// One workgroup per (batch, value head, 32-column tile) and pass: two chain waves of 16 columns
+// and four loader waves that stage the next chunk (K; Q and dO, or V; T or its transpose; M^T; the
+// row vectors) into double-buffered LDS, one barrier per chunk.  The operands are float16 in
+// the layouts of the forward kernels (column-permuted rows; perm-K fragments), rows past the
+// sequence zero.
+constexpr int BC = 32;                        // chunk length of the backward
+constexpr int B16_NTH = 384;                  // two chain waves, four loader waves
+constexpr int BC_AWS = 4 * BC * BC + 2 * BC;  // floats per chunk of the gram kernel's output
+
+template <int DK>
+struct B16Lds {
+    static constexpr int KP = DK + 8;    // K and Q rows, column-permuted f16
+    static constexpr int MP = BC + 8;    // [32][MP] f16: T (or T^T) and M^T, column-permuted
+    static constexpr int VP = 32 + 16;   // the tile's V or dO rows, bf16
+    static constexpr size_t kq = (size_t)BC * KP * 2;
+    static constexpr size_t mm = (size_t)BC * MP * 2;
+    static constexpr size_t k = 0, q = k + kq, t = q + kq, m = t + mm, v = m + mm;
+    static constexpr size_t vec = v + (size_t)BC * VP * 2;   // beta, e^gc, e^(gL - gc): [3][32] f32
+    static constexpr size_t slot = vec + 3 * BC * 4;
+    static constexpr size_t bytes = 2 * slot;
+    static_assert(q % 16 == 0 && t % 16 == 0 && m % 16 == 0 && v % 16 == 0 && vec % 16 == 0 && slot % 16 == 0,
+                  "16-byte aligned parts");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                         const bf16* __restrict__ v, const float* __restrict__ beta,
+                                                         const float* s0, const bf16* __restrict__ dout,
+                                                         const float* dsf, float* __restrict__ H,
+                                                         float* __restrict__ dH, float* ds0,
+                                                         const float* __restrict__ Aw, int T_len, int Hqk, int Hv,
+                                                         int grp, float scale, int nblk)
+{
+    using L = B16Lds<DK>;
+    constexpr int NTILE = DV / 32;
+    constexpr int MT = DK / 16, KB = DK / 32;
+    constexpr int NLT = B16_NTH - 128;       // loader threads
+    constexpr int RP = DK / 16;              // 32-byte pair-runs per K row
+    constexpr int PK = (BC * RP + NLT - 1) / NLT;   // pair-runs per loader thread
+    static_assert(BC * BC == 4 * NLT, "one float4 of T and of M per loader thread");
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const bool rev = (int)blockIdx.x >= nblk;
+    const int x = rev ? (int)blockIdx.x - nblk : (int)blockIdx.x;
+    const size_t head = (size_t)(x / NTILE);   // b * Hv + j
+    const int c0 = (x % NTILE) * 32;
+    const int b = (int)(head / Hv), j = (int)(head % Hv), i = j / grp;
+    const int NT = (T_len + BC - 1) / BC;
+    const int w = threadIdx.x >> 6;
+    const size_t qk_row = (size_t)Hqk * DK, v_row = (size_t)Hv * DV;
+    const size_t tok0 = (size_t)b * T_len;
+    auto slot = [&](int n) { return smem + (size_t)(n & 1) * L::slot; };
+    auto chunk_of = [&](int n) { return rev ? NT - 1 - n : n; };
+
+    if (w >= 2) {
+        // ================================================================= loader waves
+        const int lt = (int)threadIdx.x - 128;
+        struct Buf {
+            bf16x8 rk[PK][2], rq[PK][2];
+            bf16x8 rv;
+            floatx4 rt, rm;
+            float rvec;
+        };
+        auto load = [&](int c, Buf& r) {
+            const int t0 = c * BC, n = min(BC, T_len - t0);
+#pragma unroll
+            for (int p = 0; p < PK; ++p) {
+                const int s = min(lt + p * NLT, BC * RP - 1), row = min(s / RP, n - 1), pr = s % RP;
+                const size_t off = (tok0 + t0 + row) * qk_row + (size_t)i * DK + 32 * (pr >> 1) + 8 * (pr & 1);
+                r.rk[p][0] = *reinterpret_cast<const bf16x8*>(k + off);
+                r.rk[p][1] = *reinterpret_cast<const bf16x8*>(k + off + 16);
+                if (rev) {
+                    r.rq[p][0] = *reinterpret_cast<const bf16x8*>(q + off);
+                    r.rq[p][1] = *reinterpret_cast<const bf16x8*>(q + off + 16);
+                }
+            }
+            if (lt < 128) {   // the first two loader waves: the tile's V or dO rows
+                const int row = min(lt / 4, n - 1), c8 = (lt % 4) * 8;
+                const bf16* src = rev ? dout : v;
+                r.rv = *reinterpret_cast<const bf16x8*>(src + (tok0 + t0 + row) * v_row + (size_t)j * DV + c0 + c8);
+            }
+            // T and M, four consecutive elements of a row per thread (coalesced); the reverse
+            // pass transposes them as it writes them to LDS
+            const float* aw = Aw + (head * NT + c) * BC_AWS;
+            r.rt = ld4s(aw + 3 * BC * BC + 4 * lt);
+            if (rev) r.rm = ld4s(aw + BC * BC + 4 * lt);
+            // row vectors: beta (from the input, 0 past the sequence), e^gc, e^(gL - gc)
+            if (lt < BC)
+                r.rvec = lt < n ? beta[(tok0 + t0 + lt) * Hv + j] : 0.f;
+            else if (lt < 3 * BC)
+                r.rvec = aw[4 * BC * BC + (lt - BC)];
+        };
+        auto stage = [&](int c, int n_slot, const Buf& r) {
+            unsigned char* sb = slot(n_slot);
+            const int n = min(BC, T_len - c * BC);
+            op_t* Ks = reinterpret_cast<op_t*>(sb + L::k);
+            op_t* Qs = reinterpret_cast<op_t*>(sb + L::q);
+#pragma unroll
+            for (int p = 0; p < PK; ++p) {
+                const int s = lt + p * NLT, row = s / RP, pr = s % RP;
+                if (s >= BC * RP) break;
+                opx8 r0, r1;
+                bf16_pair_to_op(r.rk[p][0], r.rk[p][1], r0, r1);
+                if (row >= n) r0 = r1 = opx8{};
+                opx8* dk_ = reinterpret_cast<opx8*>(Ks + row * L::KP + 16 * pr);
+                dk_[0] = r0;
+                dk_[1] = r1;
+                if (rev) {
+                    bf16_pair_to_op(r.rq[p][0], r.rq[p][1], r0, r1);
+                    if (row >= n) r0 = r1 = opx8{};
+                    opx8* dq_ = reinterpret_cast<opx8*>(Qs + row * L::KP + 16 * pr);
+                    dq_[0] = r0;
+                    dq_[1] = r1;
+                }
+            }
+            if (lt < 128) {
+                const int row = lt / 4, c8 = (lt % 4) * 8;
+                *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(sb + L::v) + row * L::VP + c8) =
+                    row < n ? r.rv : bf16x8{};
+            }
+            op_t* Ts = reinterpret_cast<op_t*>(sb + L::t);
+            op_t* Ms = reinterpret_cast<op_t*>(sb + L::m);
+            {
+                // elements (rr, cc .. cc + 3) of T: at (rr, cc) in the forward pass, at (cc, rr)
+                // (T^T, and M^T) in the reverse one
+                const int rr = (4 * lt) / BC, cc = (4 * lt) % BC;
+                if (rev) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Ts[(cc + e) * L::MP + pcol(rr)] = (op_t)r.rt[e];
+                        Ms[(cc + e) * L::MP + pcol(rr)] = (op_t)r.rm[e];
+                    }
+                } else {
+                    // four consecutive logical columns stay adjacent under the permutation
+                    *reinterpret_cast<opx4*>(Ts + rr * L::MP + pcol(cc)) =
+                        opx4{(op_t)r.rt[0], (op_t)r.rt[1], (op_t)r.rt[2], (op_t)r.rt[3]};
+                }
+            }
+            if (lt < 3 * BC) reinterpret_cast<float*>(sb + L::vec)[lt] = r.rvec;
+        };
+        // step n stages step n + 1 from buffer (n + 1) % 2, then loads step n + 3 into it: two
+        // chunks of loads in flight (clamped to the last step, as in the forward state pass)
+        Buf bA, bB;
+        if (NT > 0) {
+            load(chunk_of(0), bA);
+            stage(chunk_of(0), 0, bA);
+            load(chunk_of(min(1, NT - 1)), bB);
+            load(chunk_of(min(2, NT - 1)), bA);
+        }
+        lds_barrier();
+        auto step = [&](int n, Buf& r) {
+            if (n + 1 < NT) stage(chunk_of(n + 1), n + 1, r);
+            load(chunk_of(min(n + 3, NT - 1)), r);
+            lds_barrier();
+        };
+        int n = 0;
+        for (; n + 1 < NT; n += 2) {
+            step(n, bB);
+            step(n + 1, bA);
+        }
+        if (n < NT) step(n, bB);
+    } else {
+        // ================================================================= chain waves
+        const int col = c0 + 16 * w;
+        floatx4 hacc[1][MT];
+        load_state<DK, DV, 1>(hacc, rev ? dsf : s0, head, col, threadIdx.x & 63);
+        lds_barrier();
+        for (int n = 0; n < NT; ++n) {
+            const int c = chunk_of(n);
+            const int lane = opaque(threadIdx.x & 63), ln = lane & 15, lg = lane >> 4;
+            const unsigned char* sb = slot(n);
+            const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
+            const op_t* Qs = reinterpret_cast<const op_t*>(sb + L::q);
+            const op_t* Ts = reinterpret_cast<const op_t*>(sb + L::t);
+            const op_t* Ms = reinterpret_cast<const op_t*>(sb + L::m);
+            const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v) + 16 * w;
+            const float* vs = reinterpret_cast<const float*>(sb + L::vec);
+            // this chunk's state (forward) or exit-state gradient (reverse) for the gradient kernel,
+            // [B, Hv, NT, dk, dv]
+            {
+                float* sp = (rev ? dH : H) + (head * NT + c) * DK * DV + col + ln;
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sp[(size_t)(16 * m + 4 * lg + e) * DV] = hacc[0][m][e];
+            }
+            opx8 hb[KB];
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) hb[kk] = pack_perm(hacc[0][2 * kk], hacc[0][2 * kk + 1]);
+            // K h (or K dh'): the chunk's two 16-row tiles
+            floatx4 X[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) X[mt] = mfma32(frag(Ks, L::KP, 16 * mt + ln, 32 * kk, lg), hb[kk], X[mt]);
+            // V (or dO) rows 16mt + 4lg .. +3 of this lane's column; the row vectors
+            bf16x4 vr[2];
+            floatx4 bt[2], eg[2], ed[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                vr[mt] = __builtin_bit_cast(bf16x4, ld_tr(Vs + (16 * mt + 4 * lg + (ln >> 2)) * L::VP + 4 * (ln & 3)));
+                bt[mt] = ld4s(vs + 16 * mt + 4 * lg);
+                eg[mt] = ld4s(vs + BC + 16 * mt + 4 * lg);
+                ed[mt] = ld4s(vs + 2 * BC + 16 * mt + 4 * lg);
+            }
+            const float eL = vs[BC + BC - 1];
+            floatx4 Y[2];
+            if (!rev) {
+                // R = beta V - beta e^gc K h, Delta = T R, h <- e^gL h + K^T diag(e^(gL - gc)) Delta
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Y[mt][e] = bt[mt][e] * ((float)vr[mt][e] - eg[mt][e] * X[mt][e]);
+                const opx8 rb = pack_perm(Y[0], Y[1]);
+                floatx4 D[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    D[mt] = mfma32(frag(Ts, L::MP, 16 * mt + ln, 0, lg), rb, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) D[mt][e] *= ed[mt][e];
+                const opx8 db = pack_perm(D[0], D[1]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hacc[0][m][e] *= eL;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) hacc[0][m] = mfma32(frag_kt(Ks, L::KP, m, 0, lane), db, hacc[0][m]);
+            } else {
+                // dDelta = diag(e^(gL - gc)) K dh' + M^T dO, dR = T^T dDelta,
+                // dh = e^gL dh' + (scale Q)^T diag(e^gc) dO - K^T diag(beta e^gc) dR
+                const opx8 dob = to_op(vr[0], vr[1]);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const floatx4 P = mfma32(frag(Ms, L::MP, 16 * mt + ln, 0, lg), dob, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Y[mt][e] = ed[mt][e] * X[mt][e] + P[e];
+                }
+                const opx8 ddb = pack_perm(Y[0], Y[1]);
+                floatx4 R[2], G[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    R[mt] = mfma32(frag(Ts, L::MP, 16 * mt + ln, 0, lg), ddb, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        R[mt][e] *= -bt[mt][e] * eg[mt][e];
+                        G[mt][e] = scale * eg[mt][e] * (float)vr[mt][e];
+                    }
+                }
+                const opx8 gb = pack_perm(G[0], G[1]), rb = pack_perm(R[0], R[1]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hacc[0][m][e] *= eL;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    hacc[0][m] = mfma32(frag_kt(Qs, L::KP, m, 0, lane), gb, hacc[0][m]);
+                    hacc[0][m] = mfma32(frag_kt(Ks, L::KP, m, 0, lane), rb, hacc[0][m]);
+                }
+            }
+            lds_barrier();
+        }
+        if (rev) store_state<DK, DV, 1>(hacc, ds0, head, col, threadIdx.x & 63);
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_pass16_t(const BwdArgs& a, float* H, float* dH, const float* Aw, hipStream_t st)
+{
+    using L = B16Lds<DK>;
+    static_assert(L::bytes <= 160 * 1024, "LDS budget");
+    auto kern = bwd_pass16_kernel<DK, DV>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+    if (e != hipSuccess) return e;
+    const int nblk = a.B * a.Hv * (DV / 32);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * nblk)), dim3(B16_NTH), L::bytes, st, (const bf16*)a.q, (const bf16*)a.k,
+                       (const bf16*)a.v, a.beta, a.s0, (const bf16*)a.dout, a.dsf, H, dH, a.ds0, Aw, a.T, a.Hqk,
+                       a.Hv, a.Hv / a.Hqk, a.scale, nblk);
+    return hipGetLastError();
+}
+
+bool bwd_pass16_supported(const BwdArgs& a)
+{
+    return a.dtype_bf16 && (a.dk_ == 64 || a.dk_ == 128) && (a.dv_ == 32 || a.dv_ == 64 || a.dv_ == 128);
+}
+
+hipError_t launch_bwd_pass16(const BwdArgs& a, float* H, float* dH, const float* Aw, hipStream_t st)
+{
+#define GDN_B16_CASE(DK_, DV_) \
+    if (a.dk_ == DK_ && a.dv_ == DV_) return launch_bwd_pass16_t<DK_, DV_>(a, H, dH, Aw, st);
+    GDN_B16_CASE(64, 32) GDN_B16_CASE(64, 64) GDN_B16_CASE(64, 128)
+    GDN_B16_CASE(128, 32) GDN_B16_CASE(128, 64) GDN_B16_CASE(128, 128)
+#undef GDN_B16_CASE
+    return hipErrorInvalidValue;
+}
+
 }  // namespace gdn
 
 #ifdef GDN_PHASE_TRACE
