@@ -27,6 +27,8 @@
 // 2. bwd_chunk_kernel: one workgroup per (batch, query/key head, chunk), over the value heads of
 //    the group and the column tiles in turn, with dq and dk accumulated in registers, so every
 //    gradient is written once (no atomics, deterministic).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "simt_chunk.hpp"
@@ -434,7 +436,9 @@ struct BwLds {
     static_assert((size_t)BW_C * KP <= (size_t)DK * HP, "dW / X fit the tile buffers");
 };
 
-template <typename T, int DK, int DV>
+// H16: H and dH hold each chunk's matrices as float16, transposed, [dv][dk] (the layout of the
+// float16 sequential passes), instead of float32 [dk][dv].
+template <typename T, int DK, int DV, bool H16>
 __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ H,
@@ -562,21 +566,33 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         // Each column tile's h, dh', V and dO are loaded into registers while the tile before it
         // computes (h and dh' as 16-byte loads; rows of V and dO past the sequence's end read its
         // last row and are zeroed when written to LDS).
-        constexpr int H4 = DK * BW_BV / 4;                    // float4 of h (and of dh') per tile
+        constexpr int HE = H16 ? 8 : 4;                       // elements per load
+        constexpr int H4 = DK * BW_BV / HE;                   // loads of h (and of dh') per tile
         constexpr int HPT = (H4 + BW_NT - 1) / BW_NT;
         constexpr int VPT = BW_C * BW_BV / BW_NT;             // elements of V (and of dO) per thread
         static_assert(VPT * BW_NT == BW_C * BW_BV, "V tile spread evenly");
-        floatx4 hr[HPT], dhr[HPT];
+        typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 halfx8;
+        using HR = typename std::conditional<H16, halfx8, floatx4>::type;
+        HR hr[HPT], dhr[HPT];
         T vr[VPT], dor[VPT];
         auto fetch = [&](int c0) {
-            const float* hp = H + ((head * NT + ci) * DK) * DV + c0;
-            const float* dhp = dH + ((head * NT + ci) * DK) * DV + c0;
 #pragma unroll
             for (int p = 0; p < HPT; ++p) {
-                const int e4 = tid + p * BW_NT, m = e4 / (BW_BV / 4), c = 4 * (e4 % (BW_BV / 4));
+                const int e4 = tid + p * BW_NT;
                 if (e4 < H4) {
-                    hr[p] = ld4(hp + (size_t)m * DV + c);
-                    dhr[p] = ld4(dhp + (size_t)m * DV + c);
+                    if constexpr (H16) {
+                        // rows 8 (e4 / BV) .. +7 of column e4 % BV (consecutive threads take
+                        // consecutive columns, so the LDS writes below are conflict-free)
+                        const size_t off = (head * NT + ci) * DK * DV + (size_t)(c0 + e4 % BW_BV) * DK + 8 * (e4 / BW_BV);
+                        hr[p] = *reinterpret_cast<const halfx8*>(reinterpret_cast<const _Float16*>(H) + off);
+                        dhr[p] = *reinterpret_cast<const halfx8*>(reinterpret_cast<const _Float16*>(dH) + off);
+                    } else {
+                        // columns 4 (e4 % (BV / 4)) .. +3 of row e4 / (BV / 4)
+                        const size_t off = (head * NT + ci) * DK * DV + (size_t)(e4 / (BW_BV / 4)) * DV + c0 +
+                                           4 * (e4 % (BW_BV / 4));
+                        hr[p] = ld4(H + off);
+                        dhr[p] = ld4(dH + off);
+                    }
                 }
             }
 #pragma unroll
@@ -594,12 +610,16 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             __syncthreads();   // W written; the previous tile's row sums done
 #pragma unroll
             for (int p = 0; p < HPT; ++p) {
-                const int e4 = tid + p * BW_NT, m = e4 / (BW_BV / 4), c = 4 * (e4 % (BW_BV / 4));
+                const int e4 = tid + p * BW_NT;
                 if (e4 < H4) {
+                    // element x of the load at (m + x, c) (H16) or (m, c + x)
+                    const int m = H16 ? 8 * (e4 / BW_BV) : e4 / (BW_BV / 4);
+                    const int c = H16 ? e4 % BW_BV : 4 * (e4 % (BW_BV / 4));
+                    constexpr int XS = H16 ? HP : 1;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        hs[m * HP + c + x] = hr[p][x];
-                        dhs[m * HP + c + x] = dhr[p][x];
+                    for (int x = 0; x < HE; ++x) {
+                        hs[m * HP + c + x * XS] = (float)hr[p][x];
+                        dhs[m * HP + c + x * XS] = (float)dhr[p][x];
                     }
                 }
             }
@@ -916,7 +936,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
     if (e != hipSuccess) return e;
     // 1 + 2. the states entering every chunk and the reverse state pass, in one launch: on the
     // float16 matrix cores for bf16 inputs where that kernel takes the shape
-    if (bwd_pass16_supported(a)) {
+    const bool p16 = bwd_pass16_supported(a);
+    if (p16) {
         e = launch_bwd_pass16(a, Hs, dHs, Aw, st);
         if (e != hipSuccess) return e;
     } else {
@@ -937,7 +958,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
     {
         using L = BwLds<DK>;
         static_assert(L::bytes <= 160 * 1024, "LDS budget");
-        auto kern = bwd_chunk_kernel<T, DK, DV>;
+        auto kern = p16 ? bwd_chunk_kernel<T, DK, DV, true> : bwd_chunk_kernel<T, DK, DV, false>;
         e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hqk * NT)), dim3(BW_NT), L::bytes, st,

@@ -3174,8 +3174,9 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
     auto slot = [&](int n) { return smem + (size_t)(n & 1) * L::slot; };
     auto chunk_of = [&](int n) { return rev ? NT - 1 - n : n; };
 
-    if (w >= 2) {
-        // ================================================================= loader waves
+    // the loader role, compiled once per pass (REV: the reverse pass)
+    auto loaders = [&](auto rev_c) {
+        constexpr bool REV = decltype(rev_c)::value;
         const int lt = (int)threadIdx.x - 128;
         struct Buf {
             bf16x8 rk[PK][2], rq[PK][2];
@@ -3183,6 +3184,11 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             floatx4 rt, rm;
             float rvec;
         };
+        // Every loader thread of a pass issues the same loads in every step, whatever its role
+        // (the V and vector loads it does not stage read a valid address and are dropped), so
+        // that each wait before staging covers exactly the loads of the chunk being staged and
+        // none of those in flight behind it.  With loads under branches the compiler is left a
+        // smaller count of loads in flight to wait for, down to all of them.
         auto load = [&](int c, Buf& r) {
             const int t0 = c * BC, n = min(BC, T_len - t0);
 #pragma unroll
@@ -3191,26 +3197,23 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
                 const size_t off = (tok0 + t0 + row) * qk_row + (size_t)i * DK + 32 * (pr >> 1) + 8 * (pr & 1);
                 r.rk[p][0] = *reinterpret_cast<const bf16x8*>(k + off);
                 r.rk[p][1] = *reinterpret_cast<const bf16x8*>(k + off + 16);
-                if (rev) {
+                if constexpr (REV) {
                     r.rq[p][0] = *reinterpret_cast<const bf16x8*>(q + off);
                     r.rq[p][1] = *reinterpret_cast<const bf16x8*>(q + off + 16);
                 }
             }
-            if (lt < 128) {   // the first two loader waves: the tile's V or dO rows
-                const int row = min(lt / 4, n - 1), c8 = (lt % 4) * 8;
-                const bf16* src = rev ? dout : v;
-                r.rv = *reinterpret_cast<const bf16x8*>(src + (tok0 + t0 + row) * v_row + (size_t)j * DV + c0 + c8);
+            {   // the tile's V or dO rows (staged by the first two loader waves)
+                const int row = min((lt & 127) / 4, n - 1), c8 = (lt % 4) * 8;
+                r.rv = *reinterpret_cast<const bf16x8*>((REV ? dout : v) + (tok0 + t0 + row) * v_row + (size_t)j * DV + c0 + c8);
             }
             // T and M, four consecutive elements of a row per thread (coalesced); the reverse
             // pass transposes them as it writes them to LDS
             const float* aw = Aw + (head * NT + c) * BC_AWS;
             r.rt = ld4s(aw + 3 * BC * BC + 4 * lt);
-            if (rev) r.rm = ld4s(aw + BC * BC + 4 * lt);
-            // row vectors: beta (from the input, 0 past the sequence), e^gc, e^(gL - gc)
-            if (lt < BC)
-                r.rvec = lt < n ? beta[(tok0 + t0 + lt) * Hv + j] : 0.f;
-            else if (lt < 3 * BC)
-                r.rvec = aw[4 * BC * BC + (lt - BC)];
+            if constexpr (REV) r.rm = ld4s(aw + BC * BC + 4 * lt);
+            // row vectors: beta (from the input; rows past the sequence clamped here and zeroed
+            // when staged), e^gc, e^(gL - gc)
+            r.rvec = *(lt < BC ? beta + (tok0 + t0 + min(lt, n - 1)) * Hv + j : aw + 4 * BC * BC + min(lt - BC, 2 * BC - 1));
         };
         auto stage = [&](int c, int n_slot, const Buf& r) {
             unsigned char* sb = slot(n_slot);
@@ -3227,7 +3230,7 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
                 opx8* dk_ = reinterpret_cast<opx8*>(Ks + row * L::KP + 16 * pr);
                 dk_[0] = r0;
                 dk_[1] = r1;
-                if (rev) {
+                if constexpr (REV) {
                     bf16_pair_to_op(r.rq[p][0], r.rq[p][1], r0, r1);
                     if (row >= n) r0 = r1 = opx8{};
                     opx8* dq_ = reinterpret_cast<opx8*>(Qs + row * L::KP + 16 * pr);
@@ -3246,7 +3249,7 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
                 // elements (rr, cc .. cc + 3) of T: at (rr, cc) in the forward pass, at (cc, rr)
                 // (T^T, and M^T) in the reverse one
                 const int rr = (4 * lt) / BC, cc = (4 * lt) % BC;
-                if (rev) {
+                if constexpr (REV) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         Ts[(cc + e) * L::MP + pcol(rr)] = (op_t)r.rt[e];
@@ -3258,7 +3261,7 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
                         opx4{(op_t)r.rt[0], (op_t)r.rt[1], (op_t)r.rt[2], (op_t)r.rt[3]};
                 }
             }
-            if (lt < 3 * BC) reinterpret_cast<float*>(sb + L::vec)[lt] = r.rvec;
+            if (lt < 3 * BC) reinterpret_cast<float*>(sb + L::vec)[lt] = lt < BC && lt >= n ? 0.f : r.rvec;
         };
         // step n stages step n + 1 from buffer (n + 1) % 2, then loads step n + 3 into it: two
         // chunks of loads in flight (clamped to the last step, as in the forward state pass)
@@ -3281,6 +3284,14 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             step(n + 1, bA);
         }
         if (n < NT) step(n, bB);
+    };
+
+    if (w >= 2) {
+        // ================================================================= loader waves
+        if (rev)
+            loaders(std::true_type{});
+        else
+            loaders(std::false_type{});
     } else {
         // ================================================================= chain waves
         const int col = c0 + 16 * w;
@@ -3297,14 +3308,16 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             const op_t* Ms = reinterpret_cast<const op_t*>(sb + L::m);
             const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v) + 16 * w;
             const float* vs = reinterpret_cast<const float*>(sb + L::vec);
-            // this chunk's state (forward) or exit-state gradient (reverse) for the gradient kernel,
-            // [B, Hv, NT, dk, dv]
+            // this chunk's state (forward) or exit-state gradient (reverse) for the gradient kernel:
+            // float16, transposed, [B, Hv, NT, dv, dk] (a lane's four rows of a column are one
+            // 8-byte store).  These stores are the pass's largest traffic; float16 halves them, and
+            // the values are the float16 operands the pass itself multiplies with.
             {
-                float* sp = (rev ? dH : H) + (head * NT + c) * DK * DV + col + ln;
+                op_t* sp = reinterpret_cast<op_t*>(rev ? dH : H) + ((head * NT + c) * DV + col + ln) * DK + 4 * lg;
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sp[(size_t)(16 * m + 4 * lg + e) * DV] = hacc[0][m][e];
+                    *reinterpret_cast<opx4*>(sp + 16 * m) =
+                        opx4{(op_t)hacc[0][m][0], (op_t)hacc[0][m][1], (op_t)hacc[0][m][2], (op_t)hacc[0][m][3]};
             }
             opx8 hb[KB];
 #pragma unroll

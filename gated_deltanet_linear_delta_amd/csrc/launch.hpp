@@ -108,8 +108,8 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int Hv, int dk, int dv);
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 // The backward's two sequential passes on the float16 matrix cores (chunk_mfma.hip): bf16
 // inputs, dk 64 or 128, dv 32, 64 or 128.  Fill H (the state entering every 32-token chunk) and
-// dH (each chunk's exit-state gradient), [B, Hv, NT, dk, dv] float32, and ds0, from the gram
-// kernel's per-chunk matrices Aw.
+// dH (each chunk's exit-state gradient) as float16, transposed, [B, Hv, NT, dv, dk] (in the first
+// half of each float32 region), and ds0, from the gram kernel's per-chunk matrices Aw.
 bool bwd_pass16_supported(const BwdArgs& a);
 hipError_t launch_bwd_pass16(const BwdArgs& a, float* H, float* dH, const float* Aw, hipStream_t st);
 
