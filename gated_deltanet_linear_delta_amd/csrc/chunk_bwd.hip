@@ -521,8 +521,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dTs[e] = 0.f;
             dMs[e] = 0.f;
         }
-        static_assert(NWV * BW_C <= BW_C * BW_VP, "per-wave row partials fit the scratch");
-        for (int e = tid; e < NWV * BW_C; e += BW_NT) P2[e] = 0.f;
+        // per-wave row partials of three row sums (P2: sum_m Q (dO h^T), K . X, K . dKB)
+        static_assert(3 * NWV * BW_C <= BW_C * BW_VP, "per-wave row partials fit the scratch");
+        for (int e = tid; e < 3 * NWV * BW_C; e += BW_NT) P2[e] = 0.f;
         {   // G, M and T of this chunk, formed by bwd_gram_kernel ([4][C][C]: A, M, G, T)
             const float* gp = Aw + (head * NT + ci) * BW_AWS;
             for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
@@ -740,25 +741,30 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         // ---- the terms that need every column: dW, X, dM, dT are complete now
         dgl = xor_sum(dgl, 1);
         if ((tid & 63) == 0) red[tid >> 6] = dgl;
-        // the dgc term sum_m (scale Q)_rm (dO h^T)_rm of this head: each lane over its accumulator
-        // entries, summed across the 16 lanes of a row, one partial per (wave, row) (a wave's
-        // tiles cover distinct rows)
+        // the row sums sum_m (scale Q)_rm (dO h^T)_rm (a dgc term) and sum_m K_rm X_rm of this
+        // head: each lane over its accumulator entries, summed across the 16 lanes of a row, one
+        // partial per (wave, row) (a wave's tiles cover distinct rows)
 #pragma unroll
         for (int p = 0; p < PE; ++p) {
             const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
             float v = tile_ok(p / 4) ? Qs[r * KP + m] * aS[p] : 0.f;
+            float u = tile_ok(p / 4) ? Ks[r * KP + m] * aX[p] : 0.f;
 #pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) v += __shfl_xor(v, sh, 64);
-            if (li == 0 && tile_ok(p / 4)) P2[w * BW_C + r] = v;
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                v += __shfl_xor(v, sh, 64);
+                u += __shfl_xor(u, sh, 64);
+            }
+            if (li == 0 && tile_ok(p / 4)) {
+                P2[w * BW_C + r] = v;
+                P2[(NWV + w) * BW_C + r] = u;
+            }
         }
         __syncthreads();
         float* dWs = hs;    // [C][KP]
-        float* Xs = dhs;    // [C][KP]
 #pragma unroll
         for (int p = 0; p < PE; ++p) if (tile_ok(p / 4)) {
             const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
             dWs[r * KP + m] = aW[p];
-            Xs[r * KP + m] = aX[p];
         }
         if (tid == 0) {
             float s = 0.f;
@@ -770,20 +776,24 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         // h' = e^gL h + (diag(ed) K)^T Delta:  dK += diag(ed) X, dgc -= ed (K . X), dgL += sum of those
 #pragma unroll
         for (int p = 0; p < PE; ++p) if (tile_ok(p / 4)) {
-            const int r = tile_r0(p / 4) + 4 * lq + p % 4, m = tile_m0(p / 4) + li;
-            aK[p] = fmaf(eds[r], Xs[r * KP + m], aK[p]);
+            const int r = tile_r0(p / 4) + 4 * lq + p % 4;
+            aK[p] = fmaf(eds[r], aX[p], aK[p]);
         }
         if (tid < BW_C) {
             const int r = tid;
-            float kx = 0.f;
-#pragma unroll 4
-            for (int m = 0; m < DK; ++m) kx = fmaf(Ks[r * KP + m], Xs[r * KP + m], kx);
-            const float ted = eds[r] * kx;
-            float s2 = 0.f;
+            float kx = 0.f, s2 = 0.f;
 #pragma unroll
-            for (int x = 0; x < NWV; ++x) s2 += P2[x * BW_C + r];
+            for (int x = 0; x < NWV; ++x) {
+                s2 += P2[x * BW_C + r];
+                kx += P2[(NWV + x) * BW_C + r];
+            }
+            const float ted = eds[r] * kx;
             dgcs[r] = fmaf(egs[r], s2, dgcs[r]) - ted;
-            P1[r] = ted;
+            // dgL += sum_r ted_r, across the 32 lanes
+            float tsum = ted;
+#pragma unroll
+            for (int sh = 1; sh < BW_C; sh <<= 1) tsum += __shfl_xor(tsum, sh, 64);
+            if (r == 0) red[BW_NT] += tsum;   // written by this thread above
             // M = lower-incl(Q K^T * Gamma): dgc_r += sum_s dM_rs M_rs - sum_u dM_ur M_ur
             float rs = 0.f, cs = 0.f;
 #pragma unroll 4
@@ -793,12 +803,6 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             dgcs[r] += rs - cs;
         }
         __syncthreads();
-        if (tid == 0) {
-            float s = red[BW_NT];
-#pragma unroll 4
-            for (int r = 0; r < BW_C; ++r) s += P1[r];
-            red[BW_NT] = s;   // dgL
-        }
         // E = dM * Gamma (lower incl)
         for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
             const int r = e / BW_C, s = e % BW_C;
@@ -823,7 +827,11 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 const int p = 4 * t + x, r = R0 + 4 * lq + x, m = M0 + li;
                 aQ[p] += eq[x];
                 aK[p] += ek[x] + bs[r] * egs[r] * kb[x];
-                Xs[r * KP + m] = Ks[r * KP + m] * kb[x];   // for the row sums of K . dKB
+                // the row sums of K . dKB, per (wave, row) as above
+                float u = Ks[r * KP + m] * kb[x];
+#pragma unroll
+                for (int sh = 1; sh < 16; sh <<= 1) u += __shfl_xor(u, sh, 64);
+                if (li == 0) P2[(2 * NWV + w) * BW_C + r] = u;
             }
         }
         // dT += dW (diag(beta e^gc) K)^T: tiles (R, S) of the full [C, C]
@@ -842,30 +850,36 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         if (tid < BW_C) {
             const int r = tid;
             float kb = 0.f;
-#pragma unroll 4
-            for (int m = 0; m < DK; ++m) kb += Xs[r * KP + m];
+#pragma unroll
+            for (int x = 0; x < NWV; ++x) kb += P2[(2 * NWV + x) * BW_C + r];
             dbts[r] = fmaf(egs[r], kb, dbts[r]);
             dgcs[r] = fmaf(bs[r] * egs[r], kb, dgcs[r]);
         }
-        // Z = dT T^T (into the dM buffer)
-        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
-            const int r = e / BW_C, s = e % BW_C;
-            float z = 0.f;
-#pragma unroll 4
-            for (int u = 0; u <= s; ++u) z = fmaf(dTs[r * BW_CP + u], Tm[s * BW_CP + u], z);
-            dMs[r * BW_CP + s] = z;
+        // Z = dT T^T (into the dM buffer), one 16 x 16 tile (R, S) per wave on the matrix cores
+        // (T lower triangular: the sum over u stops at the tile's last column)
+        static_assert(CT * CT <= NWV, "a wave per tile of Z and of dA");
+        if (w < CT * CT) {
+            const int R = w / CT, S = w % CT;
+            const floatx4 z4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16 * (S + 1),
+                                             [&](int ii, int kk) { return dTs[(16 * R + ii) * BW_CP + kk]; },
+                                             [&](int kk, int jj) { return Tm[(16 * S + jj) * BW_CP + kk]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dMs[(16 * R + 4 * lq + x) * BW_CP + 16 * S + li] = z4[x];
         }
         __syncthreads();
-        // dA = strictly-lower(-T^T Z) (into the dT buffer)
-        for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
-            const int r = e / BW_C, s = e % BW_C;
-            float a = 0.f;
-            if (s < r) {
-#pragma unroll 4
-                for (int u = r; u < BW_C; ++u) a = fmaf(Tm[u * BW_CP + r], dMs[u * BW_CP + s], a);
-                a = -a;
+        // dA = strictly-lower(-T^T Z) (into the dT buffer), the same way (T^T upper: the sum over
+        // u starts at the tile's first row; the tile above the diagonal is zero)
+        if (w < CT * CT) {
+            const int R = w / CT, S = w % CT;
+            floatx4 a4 = {0.f, 0.f, 0.f, 0.f};
+            if (S <= R)
+                a4 = mfma_f32_tile(a4, 16 * R, BW_C, [&](int ii, int kk) { return Tm[kk * BW_CP + 16 * R + ii]; },
+                                   [&](int kk, int jj) { return dMs[kk * BW_CP + 16 * S + jj]; });
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
+                dTs[r * BW_CP + sc] = sc < r ? -a4[x] : 0.f;
             }
-            dTs[r * BW_CP + s] = a;
         }
         __syncthreads();
         // A = diag(beta) G:  dbeta_r += sum_s dA_rs G_rs;  dgc via Gamma;  Dk = dA beta_r Gamma
@@ -895,16 +909,19 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 #pragma unroll
             for (int x = 0; x < 4; ++x) aK[4 * t + x] += x1[x] + x2[x];
         }
-        // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL)
-        if (tid == 0) {
-            float acc = red[BW_NT];
-            for (int r = BW_C - 1; r >= 0; --r) {
-                acc += dgcs[r];
-                if (r < n) {
-                    const size_t off = ((size_t)b * T_len + t0 + r) * Hv + j;
-                    dg[off] = acc;
-                    dbeta[off] = dbts[r];
-                }
+        // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL): a suffix
+        // scan across wave 0, which wrote dgc, dbeta and dgL
+        if (tid < 64) {
+            float x = tid < BW_C ? dgcs[tid] : 0.f;
+#pragma unroll
+            for (int sh = 1; sh < BW_C; sh <<= 1) {
+                const float y = __shfl_down(x, sh, 64);
+                if (tid + sh < BW_C) x += y;
+            }
+            if (tid < n) {
+                const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
+                dg[off] = red[BW_NT] + x;
+                dbeta[off] = dbts[tid];
             }
         }
     }
