@@ -550,6 +550,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         }
         __syncthreads();
         constexpr int CT = BW_C / 16;
+        constexpr int VT = BW_BV / 16, DT = CT * VT;   // value-column tiles; Delta (dDelta) tiles
         // W = T diag(beta e^gc) K: tiles (R, M) (T lower triangular: the sum stops at the tile's rows)
         for (int tt = w; tt < CT * MTL; tt += BW_NT / 64) {
             const int R = tt / MTL, M = tt % MTL;
@@ -562,6 +563,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         float aW[PE], aX[PE], aS[PE];   // aS: dO h^T of this head over the tiles (for dgc)
 #pragma unroll
         for (int p = 0; p < PE; ++p) aW[p] = aX[p] = aS[p] = 0.f;
+        float dbr[4] = {0.f, 0.f, 0.f, 0.f};   // dV waves: row sums of V . (T^T dDelta), over the tiles
         float dgl = 0.f;
 
         // Each column tile's h, dh', V and dO are loaded into registers while the tile before it
@@ -636,7 +638,6 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             // tiles on the float32 matrix cores: one wave per tile for Delta and another for dDelta
             // (T is lower triangular and M^T upper, so their sums stop at, or start at, the tile's
             // own rows)
-            constexpr int VT = BW_BV / 16, DT = (BW_C / 16) * VT;
             static_assert(2 * DT <= BW_NT / 64, "a wave per tile of each");
             if (w < 2 * DT) {
                 const int tr = (w % DT) / VT, tc = w % VT;
@@ -678,7 +679,10 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 for (int x = 0; x < 4; ++x) {
                     const int r = 16 * tr + 4 * lq + x, c = 16 * tc + li;
                     if (r < n) dv[(((size_t)b * T_len + t0 + r) * Hv + j) * DV + c0 + c] = from_f32<T>(bs[r] * tdu[x]);
-                    P1[r * BW_VP + c] = Vs[r * BW_VP + c] * tdu[x];
+                    float u = Vs[r * BW_VP + c] * tdu[x];
+#pragma unroll
+                    for (int sh = 1; sh < 16; sh <<= 1) u += __shfl_xor(u, sh, 64);
+                    dbr[x] += u;
                 }
             }
             // dT += dDelta (diag(beta) V)^T over all (R, S) tiles, dM += dO Delta^T over the tiles
@@ -730,12 +734,6 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 }
             }
             __syncthreads();
-            if (tid < BW_C) {
-                float s1 = 0.f;
-#pragma unroll 4
-                for (int c = 0; c < BW_BV; ++c) s1 += P1[tid * BW_VP + c];
-                dbts[tid] += s1;
-            }
         }
 
         // ---- the terms that need every column: dW, X, dM, dT are complete now
@@ -758,6 +756,29 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 P2[w * BW_C + r] = v;
                 P2[(NWV + w) * BW_C + r] = u;
             }
+        }
+        // P1 rows: [VT][C] the dV waves' dbeta partials, then [C] the M terms of dgc,
+        // sum_{s < r} dM_rs M_rs - sum_{u > r} dM_ur M_ur (16 lanes per row; the diagonal terms
+        // cancel), then [2][C] the same of A below
+        static_assert(BW_NT == 16 * BW_C && (VT + 3) * BW_C <= BW_C * BW_VP, "row-term layout");
+        float* dbP = P1;
+        float* mP = P1 + VT * BW_C;
+        float* aP = mP + BW_C;
+        if (w < DT && li == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dbP[(w % VT) * BW_C + 16 * (w / VT) + 4 * lq + x] = dbr[x];
+        }
+        {
+            const int r = tid >> 4, sub = tid & 15;
+            float d = 0.f;
+#pragma unroll
+            for (int s2 = sub; s2 < BW_C; s2 += 16) {
+                if (s2 < r) d = fmaf(dMs[r * BW_CP + s2], Ms[r * BW_CP + s2], d);
+                if (s2 > r) d = fmaf(-dMs[s2 * BW_CP + r], Ms[s2 * BW_CP + r], d);
+            }
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) d += __shfl_xor(d, sh, 64);
+            if (sub == 0) mP[r] = d;
         }
         __syncthreads();
         float* dWs = hs;    // [C][KP]
@@ -788,19 +809,14 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 kx += P2[(NWV + x) * BW_C + r];
             }
             const float ted = eds[r] * kx;
-            dgcs[r] = fmaf(egs[r], s2, dgcs[r]) - ted;
+            dgcs[r] = fmaf(egs[r], s2, dgcs[r]) - ted + mP[r];
+#pragma unroll
+            for (int x = 0; x < VT; ++x) dbts[r] += dbP[x * BW_C + r];
             // dgL += sum_r ted_r, across the 32 lanes
             float tsum = ted;
 #pragma unroll
             for (int sh = 1; sh < BW_C; sh <<= 1) tsum += __shfl_xor(tsum, sh, 64);
             if (r == 0) red[BW_NT] += tsum;   // written by this thread above
-            // M = lower-incl(Q K^T * Gamma): dgc_r += sum_s dM_rs M_rs - sum_u dM_ur M_ur
-            float rs = 0.f, cs = 0.f;
-#pragma unroll 4
-            for (int s = 0; s <= r; ++s) rs = fmaf(dMs[r * BW_CP + s], Ms[r * BW_CP + s], rs);
-#pragma unroll 4
-            for (int u = r; u < BW_C; ++u) cs = fmaf(dMs[u * BW_CP + r], Ms[u * BW_CP + r], cs);
-            dgcs[r] += rs - cs;
         }
         __syncthreads();
         // E = dM * Gamma (lower incl)
@@ -834,16 +850,22 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                 if (li == 0) P2[(2 * NWV + w) * BW_C + r] = u;
             }
         }
-        // dT += dW (diag(beta e^gc) K)^T: tiles (R, S) of the full [C, C]
-        for (int tt = w; tt < CT * CT; tt += BW_NT / 64) {
-            const int R = tt / CT, S = tt % CT;
-            const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, DK,
+        // dT += dW (diag(beta e^gc) K)^T: tiles (R, S) of the full [C, C], each over the two halves
+        // of dk on two waves; the second half goes to the Delta buffer and Z below adds it
+        static_assert(2 * CT * CT == NWV && DK % 8 == 0, "two waves per dT tile");
+        float* dT2 = Ds;
+        {
+            const int R = (w % (CT * CT)) / CT, S = w % CT, kh = w / (CT * CT);
+            const floatx4 x4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, kh * (DK / 2), (kh + 1) * (DK / 2),
                                              [&](int ii, int kk) { return dWs[(16 * R + ii) * KP + kk]; },
                                              [&](int kk, int jj) { return Ks[(16 * S + jj) * KP + kk]; });
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * R + 4 * lq + x, sc = 16 * S + li;
-                dTs[r * BW_CP + sc] += bs[sc] * egs[sc] * x4[x];
+                if (kh == 0)
+                    dTs[r * BW_CP + sc] += bs[sc] * egs[sc] * x4[x];
+                else
+                    dT2[r * BW_VP + sc] = bs[sc] * egs[sc] * x4[x];
             }
         }
         __syncthreads();
@@ -861,7 +883,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         if (w < CT * CT) {
             const int R = w / CT, S = w % CT;
             const floatx4 z4 = mfma_f32_tile(floatx4{0.f, 0.f, 0.f, 0.f}, 0, 16 * (S + 1),
-                                             [&](int ii, int kk) { return dTs[(16 * R + ii) * BW_CP + kk]; },
+                                             [&](int ii, int kk) {
+                                                 return dTs[(16 * R + ii) * BW_CP + kk] + dT2[(16 * R + ii) * BW_VP + kk];
+                                             },
                                              [&](int kk, int jj) { return Tm[(16 * S + jj) * BW_CP + kk]; });
 #pragma unroll
             for (int x = 0; x < 4; ++x) dMs[(16 * R + 4 * lq + x) * BW_CP + 16 * S + li] = z4[x];
@@ -882,16 +906,26 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             }
         }
         __syncthreads();
-        // A = diag(beta) G:  dbeta_r += sum_s dA_rs G_rs;  dgc via Gamma;  Dk = dA beta_r Gamma
-        if (tid < BW_C) {
-            const int r = tid;
+        // A = diag(beta) G:  dbeta_r += sum_{s < r} dA_rs G_rs and dgc_r += beta_r (that sum)
+        // - sum_{u > r} dA_ur beta_u G_ur (16 lanes per row; added by the scan below);
+        // Dk = dA beta_r Gamma
+        {
+            const int r = tid >> 4, sub = tid & 15;
             float rs = 0.f, cs = 0.f;
-#pragma unroll 4
-            for (int s = 0; s < r; ++s) rs = fmaf(dTs[r * BW_CP + s], Gs[r * BW_CP + s], rs);
-#pragma unroll 4
-            for (int u = r + 1; u < BW_C; ++u) cs = fmaf(dTs[u * BW_CP + r] * bs[u], Gs[u * BW_CP + r], cs);
-            dbts[r] += rs;
-            dgcs[r] += bs[r] * rs - cs;
+#pragma unroll
+            for (int s2 = sub; s2 < BW_C; s2 += 16) {
+                if (s2 < r) rs = fmaf(dTs[r * BW_CP + s2], Gs[r * BW_CP + s2], rs);
+                if (s2 > r) cs = fmaf(dTs[s2 * BW_CP + r] * bs[s2], Gs[s2 * BW_CP + r], cs);
+            }
+#pragma unroll
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                rs += __shfl_xor(rs, sh, 64);
+                cs += __shfl_xor(cs, sh, 64);
+            }
+            if (sub == 0) {
+                aP[r] = rs;
+                aP[BW_C + r] = cs;
+            }
         }
         for (int e = tid; e < BW_C * BW_C; e += BW_NT) {
             const int r = e / BW_C, s = e % BW_C;
@@ -912,7 +946,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         // dg = reverse cumulative sum of dgc (the chunk's last gc also carries dgL): a suffix
         // scan across wave 0, which wrote dgc, dbeta and dgL
         if (tid < 64) {
-            float x = tid < BW_C ? dgcs[tid] : 0.f;
+            float x = tid < BW_C ? dgcs[tid] + bs[tid] * aP[tid] - aP[BW_C + tid] : 0.f;
 #pragma unroll
             for (int sh = 1; sh < BW_C; sh <<= 1) {
                 const float y = __shfl_down(x, sh, 64);
@@ -921,7 +955,7 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             if (tid < n) {
                 const size_t off = ((size_t)b * T_len + t0 + tid) * Hv + j;
                 dg[off] = red[BW_NT] + x;
-                dbeta[off] = dbts[tid];
+                dbeta[off] = dbts[tid] + aP[tid];
             }
         }
     }
