@@ -376,12 +376,18 @@ def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
     flops_rc = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, recompute=True)
     del x, do, dsf, ws
     torch.cuda.empty_cache()
-    # float32 products on the float32 matrix cores (whose peak equals the float32 vector peak)
+    # bf16 inputs: the two sequential passes run on the float16 matrix cores, the per-chunk
+    # matrices and gradients (most of the time) on the float32 matrix cores, whose peak equals
+    # the float32 vector peak; the fraction is given against both peaks
+    f16 = cfg.dtype == "bf16" and cfg.dk in (64, 128) and cfg.dv in (32, 64, 128)
+    passes = ("bwd_pass16_kernel (state recompute and reverse state pass, float16 matrix cores)" if f16 else
+              "bwd_pass_kernel (state recompute beside the reverse state pass, float32)")
     return {"workload": cfg.name, "tokens_per_s": cfg.B * cfg.T / kern, "kernel_ms": kern * 1e3,
             "alg_flops": flops, "bound": "mfma", "unit": "TFLOP/s", "achieved_TFLOPs": flops / kern / 1e12,
             "peak_TFLOPs": FP32_VALU_PEAK / 1e12, "frac": flops / kern / FP32_VALU_PEAK,
+            "frac_of_bf16_mfma_peak": flops / kern / MFMA_BF16_PEAK,
             "flops_with_state_recompute": flops_rc, "frac_with_state_recompute": flops_rc / kern / FP32_VALU_PEAK,
-            "kernels": "bwd_gram_kernel + bwd_pass_kernel (state recompute beside the reverse state pass) + bwd_chunk_kernel"}
+            "kernels": f"bwd_gram_kernel + {passes} + bwd_chunk_kernel (float32 matrix cores)"}
 
 
 def bench_kda(cfg, torch, gdn, steps=10, warmup=2):
