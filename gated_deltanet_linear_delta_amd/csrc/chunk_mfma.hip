@@ -3139,9 +3139,12 @@ struct B16Lds {
     static constexpr size_t mm = (size_t)BC * MP * 2;
     static constexpr size_t k = 0, q = k + kq, t = q + kq, m = t + mm, v = m + mm;
     static constexpr size_t vec = v + (size_t)BC * VP * 2;   // beta, e^gc, e^(gL - gc): [3][32] f32
-    static constexpr size_t slot = vec + 3 * BC * 4;
+    static constexpr int HSP = DK + 8;                        // the chain waves' state, [32 columns][HSP] f16
+    static constexpr size_t hst = vec + 3 * BC * 4;
+    static constexpr size_t slot = hst + (size_t)32 * HSP * 2;
     static constexpr size_t bytes = 2 * slot;
-    static_assert(q % 16 == 0 && t % 16 == 0 && m % 16 == 0 && v % 16 == 0 && vec % 16 == 0 && slot % 16 == 0,
+    static_assert(q % 16 == 0 && t % 16 == 0 && m % 16 == 0 && v % 16 == 0 && vec % 16 == 0 && hst % 16 == 0 &&
+                      slot % 16 == 0,
                   "16-byte aligned parts");
 };
 
@@ -3263,8 +3266,25 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             }
             if (lt < 3 * BC) reinterpret_cast<float*>(sb + L::vec)[lt] = lt < BC && lt >= n ? 0.f : r.rvec;
         };
-        // step n stages step n + 1 from buffer (n + 1) % 2, then loads step n + 3 into it: two
-        // chunks of loads in flight (clamped to the last step, as in the forward state pass)
+        // the state (or state gradient) the chain waves put in slot n during step n, float16,
+        // transposed, to H (dH): the tile's 32 columns of the chunk's [dv][dk] block are one
+        // contiguous run, copied in 16-byte pieces
+        auto copy_out = [&](int n) {
+            const op_t* src = reinterpret_cast<const op_t*>(slot(n) + L::hst);
+            op_t* dst = reinterpret_cast<op_t*>(REV ? dH : H) + ((head * NT + chunk_of(n)) * DV + c0) * DK;
+            constexpr int R8 = DK / 8;   // 16-byte pieces per column
+            static_assert(32 * R8 % NLT == 0, "whole copies per loader thread");
+#pragma unroll
+            for (int p = 0; p < 32 * R8 / NLT; ++p) {
+                const int e = lt + p * NLT, col = e / R8, k8 = e % R8;
+                *reinterpret_cast<opx8*>(dst + (size_t)col * DK + 8 * k8) =
+                    *reinterpret_cast<const opx8*>(src + col * L::HSP + 8 * k8);
+            }
+        };
+        // step n stages step n + 1 from buffer (n + 1) % 2, loads step n + 3 into it (two chunks
+        // of loads in flight, clamped to the last step, as in the forward state pass), then copies
+        // out the state of step n - 1 (in the first step, that of step 0 before it is written; the
+        // second step writes it again, from the same threads)
         Buf bA, bB;
         if (NT > 0) {
             load(chunk_of(0), bA);
@@ -3276,6 +3296,7 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
         auto step = [&](int n, Buf& r) {
             if (n + 1 < NT) stage(chunk_of(n + 1), n + 1, r);
             load(chunk_of(min(n + 3, NT - 1)), r);
+            copy_out(max(n - 1, 0));
             lds_barrier();
         };
         int n = 0;
@@ -3284,6 +3305,7 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             step(n + 1, bA);
         }
         if (n < NT) step(n, bB);
+        if (NT > 0) copy_out(NT - 1);
     };
 
     if (w >= 2) {
@@ -3299,7 +3321,6 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
         load_state<DK, DV, 1>(hacc, rev ? dsf : s0, head, col, threadIdx.x & 63);
         lds_barrier();
         for (int n = 0; n < NT; ++n) {
-            const int c = chunk_of(n);
             const int lane = opaque(threadIdx.x & 63), ln = lane & 15, lg = lane >> 4;
             const unsigned char* sb = slot(n);
             const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
@@ -3309,11 +3330,12 @@ __global__ __launch_bounds__(B16_NTH) void bwd_pass16_kernel(const bf16* __restr
             const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v) + 16 * w;
             const float* vs = reinterpret_cast<const float*>(sb + L::vec);
             // this chunk's state (forward) or exit-state gradient (reverse) for the gradient kernel:
-            // float16, transposed, [B, Hv, NT, dv, dk] (a lane's four rows of a column are one
-            // 8-byte store).  These stores are the pass's largest traffic; float16 halves them, and
-            // the values are the float16 operands the pass itself multiplies with.
+            // float16, transposed, [B, Hv, NT, dv, dk], into the slot, from where the loader waves
+            // copy it out in the next step with coalesced 16-byte stores.  These stores are the
+            // pass's largest traffic; float16 halves them, and the values are the float16 operands
+            // the pass itself multiplies with.
             {
-                op_t* sp = reinterpret_cast<op_t*>(rev ? dH : H) + ((head * NT + c) * DV + col + ln) * DK + 4 * lg;
+                op_t* sp = reinterpret_cast<op_t*>(slot(n) + L::hst) + (16 * w + ln) * L::HSP + 4 * lg;
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     *reinterpret_cast<opx4*>(sp + 16 * m) =
