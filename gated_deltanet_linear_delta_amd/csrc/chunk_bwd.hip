@@ -46,6 +46,14 @@ constexpr int BW_VP = BW_BV + 1;
 // per (batch, value head, chunk) in the workspace: A, M, G, T [4][C][C], then e^gc and e^(gL - gc)
 constexpr int BW_AWS = 4 * BW_C * BW_C + 2 * BW_C;
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 halfx8;
+// D += A B on the float16 matrix cores, 16 x 16 x 32 (lane l supplies A[l % 16][8 (l / 16) + e]
+// and B[8 (l / 16) + e][l % 16], e = 0..7, and holds D[4 (l / 16) + x][l % 16])
+__device__ __forceinline__ floatx4 mfma_h(halfx8 a, halfx8 b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // ------------------------------------------------------------------- reverse state pass
 
 template <int DK>
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(DH_NT) void bwd_pass_kernel(
 
 // ------------------------------------------------------------------- per-chunk gradients
 
-template <int DK>
+template <int DK, bool H16 = false>
 struct BwLds {
     static constexpr int KP = DK + 1;
     static constexpr int HP = BW_BV + 1;
@@ -432,7 +440,15 @@ struct BwLds {
     static constexpr size_t dbt = dgc + BW_C;
     static constexpr size_t red = dbt + BW_C;                         // [NT + 1]
     static constexpr size_t floats = red + BW_NT + 1;
-    static constexpr size_t bytes = floats * sizeof(float);
+    // H16: float16 copies of the column tile's operands of the accumulator products (h, dh'
+    // [DK][HP16]; Delta, dDelta, dO [C][HP16]), after the float32 part (bytes)
+    static constexpr int HP16 = BW_BV + 8;
+    static constexpr size_t h16 = (floats * sizeof(float) + 15) / 16 * 16;
+    static constexpr size_t dh16 = h16 + (size_t)DK * HP16 * 2;
+    static constexpr size_t d16 = dh16 + (size_t)DK * HP16 * 2;
+    static constexpr size_t dd16 = d16 + (size_t)BW_C * HP16 * 2;
+    static constexpr size_t do16 = dd16 + (size_t)BW_C * HP16 * 2;
+    static constexpr size_t bytes = H16 ? do16 + (size_t)BW_C * HP16 * 2 : floats * sizeof(float);
     static_assert((size_t)BW_C * KP <= (size_t)DK * HP, "dW / X fit the tile buffers");
 };
 
@@ -446,8 +462,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     float* __restrict__ dg, float* __restrict__ dbeta, int T_len, int Hqk, int Hv, int grp, float scale,
     const float* __restrict__ Aw)
 {
-    using L = BwLds<DK>;
-    constexpr int KP = L::KP, HP = L::HP;
+    using L = BwLds<DK, H16>;
+    constexpr int KP = L::KP, HP = L::HP, HP16 = L::HP16;
     // accumulators of the [C, DK] gradients in the layout of 16 x 16 float32 matrix-core tiles
     // (mfma_f32_tile): tile u of the [C, DK] matrix is rows 16 (u / MTL) .., columns 16 (u % MTL) ..;
     // wave w owns tiles w, w + NWV, ... (TPW per wave), and element 4 t + x of lane l for the
@@ -478,6 +494,11 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
     float* dgcs = lds + L::dgc;
     float* dbts = lds + L::dbt;
     float* red = lds + L::red;
+    _Float16* h16s = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(lds) + L::h16);
+    _Float16* dh16s = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(lds) + L::dh16);
+    _Float16* D16s = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(lds) + L::d16);
+    _Float16* dD16s = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(lds) + L::dd16);
+    _Float16* dO16s = reinterpret_cast<_Float16*>(reinterpret_cast<unsigned char*>(lds) + L::do16);
 
     const int NT = (T_len + BW_C - 1) / BW_C;
     const int ci = blockIdx.x % NT;
@@ -574,7 +595,6 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
         constexpr int HPT = (H4 + BW_NT - 1) / BW_NT;
         constexpr int VPT = BW_C * BW_BV / BW_NT;             // elements of V (and of dO) per thread
         static_assert(VPT * BW_NT == BW_C * BW_BV, "V tile spread evenly");
-        typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 halfx8;
         using HR = typename std::conditional<H16, halfx8, floatx4>::type;
         HR hr[HPT], dhr[HPT];
         T vr[VPT], dor[VPT];
@@ -623,6 +643,10 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                     for (int x = 0; x < HE; ++x) {
                         hs[m * HP + c + x * XS] = (float)hr[p][x];
                         dhs[m * HP + c + x * XS] = (float)dhr[p][x];
+                        if constexpr (H16) {
+                            h16s[(m + x) * HP16 + c] = hr[p][x];
+                            dh16s[(m + x) * HP16 + c] = dhr[p][x];
+                        }
                     }
                 }
             }
@@ -630,7 +654,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             for (int p = 0; p < VPT; ++p) {
                 const int e = tid + p * BW_NT, r = e / BW_BV, c = e % BW_BV;
                 Vs[r * BW_VP + c] = r < n ? to_f32(vr[p]) : 0.f;
-                dOs[r * BW_VP + c] = r < n ? to_f32(dor[p]) : 0.f;
+                const float dov = r < n ? to_f32(dor[p]) : 0.f;
+                dOs[r * BW_VP + c] = dov;
+                if constexpr (H16) dO16s[r * HP16 + c] = (_Float16)dov;
             }
             if (c0 + BW_BV < DV) fetch(c0 + BW_BV);
             __syncthreads();
@@ -649,7 +675,11 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
                     const floatx4 wh = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ws[(16 * tr + ii) * KP + kk]; },
                                                      [&](int kk, int jj) { return hs[kk * HP + 16 * tc + jj]; });
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) Ds[(16 * tr + 4 * lq + x) * BW_VP + 16 * tc + li] = u[x] - wh[x];
+                    for (int x = 0; x < 4; ++x) {
+                        const float dl = u[x] - wh[x];
+                        Ds[(16 * tr + 4 * lq + x) * BW_VP + 16 * tc + li] = dl;
+                        if constexpr (H16) D16s[(16 * tr + 4 * lq + x) * HP16 + 16 * tc + li] = (_Float16)dl;
+                    }
                 } else {
                     const floatx4 kd = mfma_f32_tile(z, 0, DK, [&](int ii, int kk) { return Ks[(16 * tr + ii) * KP + kk]; },
                                                      [&](int kk, int jj) { return dhs[kk * HP + 16 * tc + jj]; });
@@ -659,7 +689,9 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int r = 16 * tr + 4 * lq + x;
-                        dDs[r * BW_VP + 16 * tc + li] = fmaf(eds[r], kd[x], md[x]);
+                        const float dd = fmaf(eds[r], kd[x], md[x]);
+                        dDs[r * BW_VP + 16 * tc + li] = dd;
+                        if constexpr (H16) dD16s[r * HP16 + 16 * tc + li] = (_Float16)dd;
                     }
                 }
             }
@@ -719,11 +751,22 @@ __global__ __launch_bounds__(BW_NT) void bwd_chunk_kernel(
             for (int t = 0; t < TPW; ++t) if (tile_ok(t)) {
                 const floatx4 z = {0.f, 0.f, 0.f, 0.f};
                 const int r0 = tile_r0(t), m0 = tile_m0(t);
-                auto bh = [&](int kk, int jj) { return hs[(m0 + jj) * HP + kk]; };
-                const floatx4 sw = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dDs[(r0 + ii) * BW_VP + kk]; }, bh);
-                const floatx4 sx = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return Ds[(r0 + ii) * BW_VP + kk]; },
-                                                 [&](int kk, int jj) { return dhs[(m0 + jj) * HP + kk]; });
-                const floatx4 sq = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dOs[(r0 + ii) * BW_VP + kk]; }, bh);
+                floatx4 sw, sx, sq;
+                if constexpr (H16) {
+                    // one float16 16 x 16 x 32 product each (k = the tile's 32 value columns): lane l
+                    // supplies row l % 16 of A and column l % 16 of B, k = 8 (l / 16) .. + 7
+                    const halfx8 bh = *reinterpret_cast<const halfx8*>(h16s + (m0 + li) * HP16 + 8 * lq);
+                    const halfx8 bdh = *reinterpret_cast<const halfx8*>(dh16s + (m0 + li) * HP16 + 8 * lq);
+                    sw = mfma_h(*reinterpret_cast<const halfx8*>(dD16s + (r0 + li) * HP16 + 8 * lq), bh, z);
+                    sx = mfma_h(*reinterpret_cast<const halfx8*>(D16s + (r0 + li) * HP16 + 8 * lq), bdh, z);
+                    sq = mfma_h(*reinterpret_cast<const halfx8*>(dO16s + (r0 + li) * HP16 + 8 * lq), bh, z);
+                } else {
+                    auto bh = [&](int kk, int jj) { return hs[(m0 + jj) * HP + kk]; };
+                    sw = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dDs[(r0 + ii) * BW_VP + kk]; }, bh);
+                    sx = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return Ds[(r0 + ii) * BW_VP + kk]; },
+                                       [&](int kk, int jj) { return dhs[(m0 + jj) * HP + kk]; });
+                    sq = mfma_f32_tile(z, 0, BW_BV, [&](int ii, int kk) { return dOs[(r0 + ii) * BW_VP + kk]; }, bh);
+                }
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const int p = 4 * t + x;
@@ -1007,12 +1050,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st)
     }
     // 3. per-chunk gradients
     {
-        using L = BwLds<DK>;
-        static_assert(L::bytes <= 160 * 1024, "LDS budget");
+        static_assert(BwLds<DK, true>::bytes <= 160 * 1024 && BwLds<DK, false>::bytes <= 160 * 1024, "LDS budget");
+        const size_t lb = p16 ? BwLds<DK, true>::bytes : BwLds<DK, false>::bytes;
         auto kern = p16 ? bwd_chunk_kernel<T, DK, DV, true> : bwd_chunk_kernel<T, DK, DV, false>;
-        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+        e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lb);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hqk * NT)), dim3(BW_NT), L::bytes, st,
+        hipLaunchKernelGGL(kern, dim3((unsigned)((long)a.B * a.Hqk * NT)), dim3(BW_NT), lb, st,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, a.g, a.beta, (const T*)a.dout, Hs, dHs,
                            (T*)a.dq, (T*)a.dk, (T*)a.dv, a.dg, a.dbeta, a.T, a.Hqk, a.Hv, grp, a.scale, Aw);
         e = hipGetLastError();

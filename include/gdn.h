@@ -296,9 +296,10 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int Hqk, int Hv, int dk, int 
  * gradients then follow in parallel.  The result equals the gradient of the token-by-token
  * recurrence up to rounding; it does not depend on the forward call's chunk size.  For bf16
  * inputs with dk in {64, 128} and dv in {32, 64, 128} the two sequential passes (the state
- * recompute and the reverse pass) run on the float16 matrix cores: besides the forward's operand
- * range (above), grad_o, grad_final_state and every state gradient dL/dh must stay below 65504 in
- * magnitude; the per-chunk gradients stay float32.
+ * recompute and the reverse pass) and the per-chunk products dDelta h^T, Delta dh^T and dO h^T
+ * take float16 operands: besides the forward's operand range (above), grad_o, grad_final_state,
+ * every state gradient dL/dh and the per-chunk Delta and dL/dDelta must stay below 65504 in
+ * magnitude; the other per-chunk products are float32.
  *
  *   q, k, v, g, beta, initial_state, sizes, dtype, scale: as gdn_chunk_fwd (inputs)
  *   grad_o            [B, T, Hv, dv] dtype: dL/dO
