@@ -23,8 +23,11 @@ The same JSON line carries
   gated_prefill -- gdn_chunk_fwd_gated (prefill with the output's gated RMSNorm in the same
                    call) on the Qwen3-Next and the batched workloads;
   backward      -- gdn_chunk_bwd (gradients of q, k, v, g, beta, S0) at the Qwen3-Next shape:
-                   tokens/s and its fraction of the float32 peak, for the method's own work and
-                   for the work as computed (which recomputes the states);
+                   tokens/s and its roofline fraction (the time the work would take with each
+                   part at the peak of the unit that runs it: float16 matrix cores for the bf16
+                   route's passes and three gradient products, float32 for the rest, over the
+                   measured time), for the method's own work and for the work as computed
+                   (which recomputes the states);
   kda           -- gdn_kda_chunk_fwd (Kimi Delta Attention, per-key-channel decay) on the KDA
                    workload (B1 T4096, 32/32 heads, d128, chunk 64 on the float16 matrix cores):
                    tokens/s and its fraction of the 16-bit matrix-core peak;
@@ -82,6 +85,17 @@ def backward_alg_flops(B, T, Hqk, Hv, dk, dv, C=32, recompute=True):
     recompute the kernels run because the states are not kept from the forward,
     4 dk dv + C (dk + dv); without it, the method's own work."""
     per = 18 * dk * dv + 8 * C * dv + 11 * C * dk + 7 * C * C / 3
+    if recompute:
+        per += 4 * dk * dv + C * (dk + dv)
+    return per * B * T * Hv
+
+
+def backward_f16_flops(B, T, Hqk, Hv, dk, dv, C=32, recompute=True):
+    """The part of backward_alg_flops that the bf16 route runs on the float16 matrix cores: the
+    reverse state pass, 6 dk dv + 2 C (dk + dv) (and the state recompute beside it), and the
+    gradient kernel's three products that contract over a tile's value columns (dDelta h^T,
+    Delta dh'^T, dO h^T), 6 dk dv.  The rest runs on the float32 matrix cores."""
+    per = 12 * dk * dv + 2 * C * (dk + dv)
     if recompute:
         per += 4 * dk * dv + C * (dk + dv)
     return per * B * T * Hv
@@ -376,18 +390,32 @@ def bench_backward(cfg, torch, gdn, steps=10, warmup=2):
     flops_rc = backward_alg_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, recompute=True)
     del x, do, dsf, ws
     torch.cuda.empty_cache()
-    # bf16 inputs: the two sequential passes run on the float16 matrix cores, the per-chunk
-    # matrices and gradients (most of the time) on the float32 matrix cores, whose peak equals
-    # the float32 vector peak; the fraction is given against both peaks
+    # bf16 inputs: the two sequential passes and three of the gradient kernel's products run on
+    # the float16 matrix cores, the chunk matrices and the other gradient products on the float32
+    # matrix cores (whose peak equals the float32 vector peak).  The roofline is then the time the
+    # work would take with each part at its own unit's peak, over the measured time; float32
+    # inputs run everything in float32.
     f16 = cfg.dtype == "bf16" and cfg.dk in (64, 128) and cfg.dv in (32, 64, 128)
     passes = ("bwd_pass16_kernel (state recompute and reverse state pass, float16 matrix cores)" if f16 else
               "bwd_pass_kernel (state recompute beside the reverse state pass, float32)")
+    grad = ("bwd_chunk_kernel (float32 matrix cores; dDelta h^T, Delta dh^T, dO h^T on the float16 ones)" if f16 else
+            "bwd_chunk_kernel (float32 matrix cores)")
+
+    def t_min(total, recompute):
+        h = backward_f16_flops(cfg.B, cfg.T, cfg.Hqk, cfg.Hv, cfg.dk, cfg.dv, recompute=recompute) if f16 else 0.0
+        return h / MFMA_BF16_PEAK + (total - h) / FP32_VALU_PEAK, h
+
+    tm, h16 = t_min(flops, False)
+    tm_rc, _ = t_min(flops_rc, True)
     return {"workload": cfg.name, "tokens_per_s": cfg.B * cfg.T / kern, "kernel_ms": kern * 1e3,
-            "alg_flops": flops, "bound": "mfma", "unit": "TFLOP/s", "achieved_TFLOPs": flops / kern / 1e12,
-            "peak_TFLOPs": FP32_VALU_PEAK / 1e12, "frac": flops / kern / FP32_VALU_PEAK,
+            "alg_flops": flops, "alg_flops_f16_matrix_cores": h16, "bound": "mfma", "unit": "TFLOP/s",
+            "achieved_TFLOPs": flops / kern / 1e12, "peak_TFLOPs": flops / tm / 1e12, "frac": tm / kern,
+            "peak_note": "each part of the work at the peak of the unit that runs it (float16 matrix cores "
+                         "2516.6, float32 157.3 TFLOP/s): peak = work / that time",
             "frac_of_bf16_mfma_peak": flops / kern / MFMA_BF16_PEAK,
-            "flops_with_state_recompute": flops_rc, "frac_with_state_recompute": flops_rc / kern / FP32_VALU_PEAK,
-            "kernels": f"bwd_gram_kernel + {passes} + bwd_chunk_kernel (float32 matrix cores)"}
+            "frac_of_fp32_peak": flops / kern / FP32_VALU_PEAK,
+            "flops_with_state_recompute": flops_rc, "frac_with_state_recompute": tm_rc / kern,
+            "kernels": f"bwd_gram_kernel + {passes} + {grad}"}
 
 
 def bench_kda(cfg, torch, gdn, steps=10, warmup=2):
