@@ -152,6 +152,7 @@ constexpr int V_ED = 2;    // exp(gc_63 - gc)
 constexpr int V_EC = 3;    // exp(gc_63) (every element)
 constexpr int V_EG = 4;    // scale exp(gc)
 constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk)
+constexpr int NVEC = 6;
 
 // Workspace of the split path, per (batch, value head, chunk), in two parts: what the state step
 // reads (T, then the rows V_B..V_EC) and what the output step reads (Aqk, then the row V_EG).
@@ -253,6 +254,15 @@ __device__ __forceinline__ opx8 to_op(bf16x4 a, bf16x4 b)
                 (op_t)(float)b[0], (op_t)(float)b[1], (op_t)(float)b[2], (op_t)(float)b[3]};
 }
 
+// to_op, or zero where `keep` is false, without a branch (a select on the result's bits: the
+// compiler had wrapped each conditional conversion in its own branch)
+__device__ __forceinline__ opx8 to_op_or_zero(bf16x8 x, bool keep)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const unsigned int m = keep ? 0xffffffffu : 0u;
+    return __builtin_bit_cast(opx8, __builtin_bit_cast(u32x4, to_op(x)) & m);
+}
+
 // bf16 -> float16 for one pair-run: x = logical columns c .. c+7, y = c+16 .. c+23 of a
 // 32-column block (c = 8a) give the physical runs {c..c+3, c+16..c+19} and {c+4..c+7,
 // c+20..c+23}.  Each 32-bit pair is widened to two float32 (shift / mask) and narrowed with one
@@ -299,6 +309,27 @@ __device__ __forceinline__ float wave_cumsum(float x, int lane)
         const float y = __shfl_up(x, s, 64);
         if (lane >= s) x += y;
     }
+    return x;
+}
+
+// The same prefix sum with cross-lane moves only (no LDS round trip): Hillis-Steele steps of 1,
+// 2, 4 and 8 inside each row of 16 lanes, then each row adds the running total of the rows before
+// it (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3).  Lanes a move has no source
+// for add zero.  The additions group differently from wave_cumsum's, so the two may differ in the
+// last bit.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_take(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_cumsum_dpp(float x)
+{
+    x += dpp_take<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_take<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_take<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_take<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_take<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_take<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -1411,21 +1442,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
 
 // =======================================================================================
 // Pipelined fused kernel: one workgroup per (batch, value head, column tile of BV columns) with
-// NW chain waves and three prep waves, and one workgroup barrier per chunk.  While the chain
+// NW chain waves and four prep waves, and one workgroup barrier per chunk.  While the chain
 // waves carry chunk n out of LDS slot n & 1, the prep waves build chunk n + 1 in the other slot,
 // each prep wave a whole part of it on its own, so that no wave waits on another inside a chunk:
 // * T wave: the chunk's k rows from HBM straight into MFMA fragments, K K^T, A and the blocked
-//   solve for T = (I + A)^{-1} in LDS of its own, T into the slot in fragment order; the gate
-//   vectors into the slot;
-// * Aqk wave: q and k rows into fragments, K Q^T and Aqk into the slot in fragment order; Q into
-//   the slot;
-// * V wave: the chunk's V tile and K (column-permuted float16) into the slot, and the raw gates
-//   (g, beta) of the chunk after it into a small double buffer that the T and Aqk waves read in
-//   the next period.
+//   solve for T = (I + A)^{-1} in LDS of its own, T into the slot in fragment order;
+// * Aqk wave: q and k rows into fragments, K Q^T and Aqk into the slot in fragment order;
+// * V wave: the chunk's V tile and K (column-permuted float16) into the slot;
+// * Q wave: the chunk's Q (column-permuted float16) into the slot, and the gate vectors of the
+//   chunk after it (the cumsum of log alpha and the decay factors built from it) into a ring of
+//   three sets, which the T and Aqk waves read in the next period and the chain waves in the one
+//   after.  Staging Q and forming the vectors had been the T and Aqk waves' own work, and those
+//   two set the period; this wave takes them off both.
 // Each prep wave loads the next chunk's operands while it works on this one; no prep wave waits
 // on a global load it issued in the same period.  The chain waves read every operand from LDS (T
 // and Aqk with one 16-byte read per fragment) and run the delta, output and update phases back
 // to back.
+constexpr int PIPE_PW = 4;   // prep waves of the pipelined kernel
 template <int DK, int BV>
 struct PLds {
     static constexpr int KP = DK + 8;            // element pitch of K and Q rows
@@ -1435,15 +1468,13 @@ struct PLds {
     static constexpr size_t v = q + (size_t)CH * KP * 2;            // V   [64][VP] bf16
     static constexpr size_t t = v + (size_t)CH * VP * 2;            // T   6 fragment blocks f16
     static constexpr size_t aq = t + 6 * 64 * 16;                   // Aqk 6 fragment blocks f16
-    static constexpr size_t vec = aq + 6 * 64 * 16;                 // [8][64] f32
-    static constexpr size_t slot = vec + (size_t)8 * CH * 4;
+    static constexpr size_t slot = aq + 6 * 64 * 16;
     static constexpr size_t ad = 2 * slot;                          // T wave: A, T scratch
     static constexpr size_t ah = ad + (size_t)PREP_AD * 4;
     static constexpr size_t tm = ah + (size_t)PREP_AH * 2;
-    static constexpr size_t pg = tm + (size_t)PREP_TM * 2;          // Aqk wave: gc [64] f32
-    static constexpr size_t gr = pg + (size_t)CH * 4;               // raw g, beta [2][2][64] f32
-    static constexpr size_t bytes = gr + (size_t)4 * CH * 4;
-    static_assert(slot % 16 == 0 && v % 16 == 0 && tm % 16 == 0, "16-byte aligned parts");
+    static constexpr size_t vr = tm + (size_t)PREP_TM * 2;          // gate vectors [3][NVEC][64] f32
+    static constexpr size_t bytes = vr + (size_t)3 * NVEC * CH * 4;
+    static_assert(slot % 16 == 0 && v % 16 == 0 && tm % 16 == 0 && vr % 16 == 0, "16-byte aligned parts");
 };
 
 // A copy of x the compiler cannot see through: lane-derived values (addresses, masks) computed
@@ -1479,15 +1510,46 @@ __device__ __forceinline__ void store_rows_frag(const bf16x8 (&f)[4][KB], op_t* 
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
             const int r = 16 * mt + ln, c8 = 32 * kk + 8 * lg;
-            const opx8 x = r < n ? to_op(f[mt][kk]) : opx8{};
+            const opx8 x = to_op_or_zero(f[mt][kk], r < n);
             op_t* mr = m + r * KP;
             *reinterpret_cast<opx4*>(mr + pcol(c8)) = opx4{x[0], x[1], x[2], x[3]};
             *reinterpret_cast<opx4*>(mr + pcol(c8 + 4)) = opx4{x[4], x[5], x[6], x[7]};
         }
 }
 
+// A chunk's q or k rows as whole rows: lane + 64 p takes the 16 bytes at segment s % (DK / 8) of
+// row s / (DK / 8), so each load instruction covers DK / 16 whole rows (a fragment-ordered load
+// covers 64 bytes of each of 16 rows).  Rows are clamped to the chunk's last token; the store
+// below zeroes what lies past it.
+template <int DK>
+__device__ __forceinline__ void load_rows_lin(bf16x8 (&f)[DK / 8], const bf16* p, size_t row, int n, int lane)
+{
+    constexpr int SEG = DK / 8;
+#pragma unroll
+    for (int pp = 0; pp < DK / 8; ++pp) {
+        const int s = lane + 64 * pp;
+        f[pp] = *reinterpret_cast<const bf16x8*>(p + (size_t)min(s / SEG, n - 1) * row + (s % SEG) * 8);
+    }
+}
+
+// The same rows into an LDS matrix as column-permuted float16 with pitch KP, rows at or past n zero.
+template <int DK, int KP>
+__device__ __forceinline__ void store_rows_lin(const bf16x8 (&f)[DK / 8], op_t* m, int n, int lane)
+{
+    constexpr int SEG = DK / 8;
+#pragma unroll
+    for (int pp = 0; pp < DK / 8; ++pp) {
+        const int s = lane + 64 * pp;
+        const int r = s / SEG, c8 = (s % SEG) * 8;
+        const opx8 x = to_op_or_zero(f[pp], r < n);
+        op_t* mr = m + r * KP;
+        *reinterpret_cast<opx4*>(mr + pcol(c8)) = opx4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<opx4*>(mr + pcol(c8 + 4)) = opx4{x[4], x[5], x[6], x[7]};
+    }
+}
+
 template <int DK, int DV, int BV, int NW, bool VARLEN>
-__global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
+__global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* s0, float* sf,  // may be the same buffer (in-place state update)
@@ -1524,6 +1586,9 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
     const size_t v_row = (size_t)Hv * DV;
     const size_t tok0 = sq.tok0;
     auto slot = [&](int c) { return smem + (size_t)(c & 1) * L::slot; };
+    // gate vectors of chunk c: written by the Q wave in the period before chunk c is built, read
+    // by the T and Aqk waves while they build it and by the chain waves in the period after
+    auto ring = [&](int c) { return reinterpret_cast<float*>(smem + L::vr) + (c % 3) * (NVEC * CH); };
 
     if (w < NW) {
         // ================================================================= chain waves
@@ -1533,7 +1598,7 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
         const int col = c0 + w * NCOL;
         load_state<DK, DV, NTN>(hacc, s0, head, col, lane);
         bf16* ob = o + (tok0 * Hv + j) * DV + col;
-        lds_barrier();   // gates of chunk 0 staged
+        lds_barrier();   // gate vectors of chunk 0 in the ring
         lds_barrier();   // chunk 0 built
         for (int n = 0; n < NT; ++n) {
             const unsigned char* sb = slot(n);
@@ -1542,7 +1607,7 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
             const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v) + w * NCOL;
             const opx8* Tf = reinterpret_cast<const opx8*>(sb + L::t);
             const opx8* Af = reinterpret_cast<const opx8*>(sb + L::aq);
-            const float* vs = reinterpret_cast<const float*>(sb + L::vec);
+            const float* vs = ring(n);
             const int t0 = n * CH;
             opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
             GDN_TRACE(n, 0);
@@ -1561,11 +1626,12 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
     }
 
     // ===================================================================== prep waves
-    // a prologue barrier (the V wave stages chunk 0's gates), then chunk c is built before the
-    // barrier that ends period c - 1; one more barrier matches the chain waves' last
+    // a prologue barrier (the Q wave puts chunk 0's gate vectors in the ring), then chunk c is
+    // built before the barrier that ends period c - 1; one more barrier matches the chain waves'
+    // last
     const int pw = w - NW;
     const bf16* kb_ = k + (tok0 * Hqk + i) * DK;
-    const float* grw = reinterpret_cast<const float*>(smem + L::gr);   // [2][2][64]: g, beta
+    const bf16* qb = q + (tok0 * Hqk + i) * DK;
     if (pw == 0) {
         // T wave
         float* Ad = reinterpret_cast<float*>(smem + L::ad);
@@ -1581,9 +1647,7 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
         lds_barrier();
         for (int c = 0; c < NT; ++c) {
             unsigned char* sb = slot(c);
-            const int n = min(CH, T_len - c * CH);
             const int lane = opaque(threadIdx.x & 63);
-            const float gl = grw[(c & 1) * 2 * CH + lane], bl = grw[(c & 1) * 2 * CH + CH + lane];
             floatx4 gk[10];
 #pragma unroll
             for (int t = 0; t < 10; ++t) gk[t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1593,18 +1657,7 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
                 for (int t = 0; t < 10; ++t) gk[t] = mfma_bf(kf[TI[t]][kk], kf[TJ[t]][kk], gk[t]);
             GDN_TRACE(c, 0);
             if (c + 1 < NT) load(c + 1);
-            const float x = wave_cumsum(lane < n ? log_decay(gl) : 0.f, lane);
-            const float bt = lane < n ? bl : 0.f;
-            const float last = __shfl(x, 63, 64);
-            const float eg = __expf(x);
-            float* vs = reinterpret_cast<float*>(sb + L::vec);
-            vs[V_G * CH + lane] = x;
-            vs[V_B * CH + lane] = bt;
-            vs[V_BEG * CH + lane] = bt * eg;
-            vs[V_ED * CH + lane] = __expf(last - x);
-            vs[V_EC * CH + lane] = __expf(last);
-            vs[V_EG * CH + lane] = scale * eg;
-            wave_lds_fence();
+            const float* vs = ring(c);
             const int ln = lane & 15, lg = lane >> 4;
             floatx4 g4[4], b4[4];
             float g1[4];
@@ -1626,8 +1679,6 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
         }
     } else if (pw == 1) {
         // Aqk wave
-        const bf16* qb = q + (tok0 * Hqk + i) * DK;
-        float* pg = reinterpret_cast<float*>(smem + L::pg);
         bf16x8 kf[4][KB], qf[4][KB];
         auto load = [&](int c) {
             const int t0 = c * CH, n = min(CH, T_len - t0);
@@ -1640,7 +1691,6 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
             unsigned char* sb = slot(c);
             const int n = min(CH, T_len - c * CH);
             const int lane = opaque(threadIdx.x & 63);
-            const float gl = grw[(c & 1) * 2 * CH + lane];
             // K Q^T: rows TJ of K x columns TI of Q (Aqk transposed)
             floatx4 gq[10];
 #pragma unroll
@@ -1650,33 +1700,26 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
 #pragma unroll
                 for (int t = 0; t < 10; ++t) gq[t] = mfma_bf(kf[TJ[t]][kk], qf[TI[t]][kk], gq[t]);
             GDN_TRACE(c, 0);
-            store_rows_frag<KB, L::KP>(qf, reinterpret_cast<op_t*>(sb + L::q), n, lane);
             if (c + 1 < NT) load(c + 1);
             GDN_TRACE(c, 1);
-            const float x = wave_cumsum(lane < n ? log_decay(gl) : 0.f, lane);
-            pg[lane] = x;
-            wave_lds_fence();
+            const float* vs = ring(c);
             const int ln = lane & 15, lg = lane >> 4;
             floatx4 g4[4];
             float g1[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                g4[t] = ld4s(pg + 16 * t + 4 * lg);
-                g1[t] = pg[16 * t + ln];
+                g4[t] = ld4s(vs + V_G * CH + 16 * t + 4 * lg);
+                g1[t] = vs[V_G * CH + 16 * t + ln];
             }
             prep_store_aqk(gq, g4, g1, scale, n, reinterpret_cast<op_t*>(sb + L::aq), lane);
             GDN_TRACE(c, 2);
             lds_barrier();
         }
-    } else {
-        // V wave: V and K into the slot; also the raw gates, one chunk ahead
+    } else if (pw == 2) {
+        // V wave: V and K into the slot
         const bf16* vb = v + (tok0 * Hv + j) * DV + c0;
-        const float* gb = g + tok0 * Hv + j;
-        const float* bb = beta + tok0 * Hv + j;
-        float* gw = reinterpret_cast<float*>(smem + L::gr);
         bf16x8 rv[PV];
         bf16x8 kf[4][KB];
-        float rg = 0.f, rb = 0.f;
         auto load_v = [&](int c) {
             const int t0 = c * CH, n = min(CH, T_len - t0);
 #pragma unroll
@@ -1687,28 +1730,11 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
             }
             load_rows_frag<KB>(kf, kb_ + (size_t)t0 * qk_row, qk_row, n, lane);
         };
-        // g, beta of chunk c, rows past the sequence clamped (the other waves mask them)
-        auto load_g = [&](int c) {
-            const int t0 = c * CH, n = min(CH, T_len - t0);
-            const size_t off = (size_t)(t0 + min(lane, n - 1)) * Hv;
-            rg = gb[off];
-            rb = bb[off];
-        };
-        if (NT > 0) {
-            load_g(0);
-            gw[lane] = rg;
-            gw[CH + lane] = rb;
-            if (NT > 1) load_g(1);
-            load_v(0);
-        }
+        if (NT > 0) load_v(0);
         lds_barrier();
         for (int c = 0; c < NT; ++c) {
             bf16* Vs = reinterpret_cast<bf16*>(slot(c) + L::v);
             const int n = min(CH, T_len - c * CH);
-            if (c + 1 < NT) {
-                gw[((c + 1) & 1) * 2 * CH + lane] = rg;
-                gw[((c + 1) & 1) * 2 * CH + CH + lane] = rb;
-            }
 #pragma unroll
             for (int p = 0; p < PV; ++p) {
                 const int s = lane + 64 * p;
@@ -1717,9 +1743,58 @@ __global__ __launch_bounds__((NW + 3) * 64, 1) void chunk_pipe_kernel(
             }
             store_rows_frag<KB, L::KP>(kf, reinterpret_cast<op_t*>(slot(c) + L::k), n, opaque(lane));
             GDN_TRACE(c, 0);
-            if (c + 2 < NT) load_g(c + 2);
             if (c + 1 < NT) load_v(c + 1);
             GDN_TRACE(c, 1);
+            lds_barrier();
+        }
+    } else {
+        // Q wave: Q into the slot; the gate vectors of the chunk after, into the ring
+        const float* gb = g + tok0 * Hv + j;
+        const float* bb = beta + tok0 * Hv + j;
+        bf16x8 qf[DK / 8];
+        float rg = 0.f, rb = 0.f;
+        auto load_q = [&](int c) {
+            const int t0 = c * CH;
+            load_rows_lin<DK>(qf, qb + (size_t)t0 * qk_row, qk_row, min(CH, T_len - t0), lane);
+        };
+        // g, beta of chunk c, rows past the sequence clamped (masked below)
+        auto load_g = [&](int c) {
+            const int t0 = c * CH, n = min(CH, T_len - t0);
+            const size_t off = (size_t)(t0 + min(lane, n - 1)) * Hv;
+            rg = gb[off];
+            rb = bb[off];
+        };
+        // the gate vectors of chunk c from its raw g, beta (one token per lane)
+        auto put_vec = [&](int c) {
+            const int n = min(CH, T_len - c * CH);
+            const float x = wave_cumsum_dpp(lane < n ? log_decay(rg) : 0.f);
+            const float bt = lane < n ? rb : 0.f;
+            const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+            const float eg = __expf(x);
+            float* vs = ring(c);
+            vs[V_G * CH + lane] = x;
+            vs[V_B * CH + lane] = bt;
+            vs[V_BEG * CH + lane] = bt * eg;
+            vs[V_ED * CH + lane] = __expf(last - x);
+            vs[V_EC * CH + lane] = __expf(last);
+            vs[V_EG * CH + lane] = scale * eg;
+        };
+        if (NT > 0) {
+            load_g(0);
+            put_vec(0);
+            if (NT > 1) load_g(1);
+            load_q(0);
+        }
+        lds_barrier();
+        for (int c = 0; c < NT; ++c) {
+            const int n = min(CH, T_len - c * CH);
+            if (c + 1 < NT) put_vec(c + 1);
+            GDN_TRACE(c, 0);
+            store_rows_lin<DK, L::KP>(qf, reinterpret_cast<op_t*>(slot(c) + L::q), n, opaque(lane));
+            GDN_TRACE(c, 1);
+            if (c + 2 < NT) load_g(c + 2);
+            if (c + 1 < NT) load_q(c + 1);
+            GDN_TRACE(c, 2);
             lds_barrier();
         }
     }
@@ -2348,7 +2423,7 @@ hipError_t launch_pipe_t(const ChunkArgs& a, hipStream_t st)
     const long nblk = (long)a.B * a.Hv * (DV / BV);
     const long per_xcd = nblk / 8;
     const int remap = (nblk % 8 == 0) && (per_xcd % ((long)grp * (DV / BV)) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((NW + 3) * 64), L::bytes, st, (const bf16*)a.q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3((NW + PIPE_PW) * 64), L::bytes, st, (const bf16*)a.q,
                        (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.s0, a.sf, (bf16*)a.o, a.T, a.Hqk, a.Hv,
                        grp, a.scale, remap, a.cu, a.total);
     return hipGetLastError();
