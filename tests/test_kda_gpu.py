@@ -152,3 +152,31 @@ def test_kda_mfma_prefill_full():
     o, s = run_kda(d, 64)
     o_ref, s_ref = oracle_kda(d)
     check("kda_prefill mfma", "bf16", o, o_ref, s, s_ref)
+
+
+@pytest.mark.parametrize("mu", [6.0, 1.0])
+@pytest.mark.parametrize("keys", ["identical", "correlated"])
+def test_kda_mfma_dense_solve(keys, mu):
+    """All keys of a head equal (or close: a shared unit key plus 0.3 of a random one, renormalised)
+    and beta near 1: the strictly-lower A of every chunk is dense with entries near beta, so the
+    blocks of the blockwise (I + A)^{-1} off its diagonal carry large entries.  Slow channel decay
+    (mu = 6) keeps those entries near one; mu = 1 mixes slow and fast channels.  Checked against the
+    float64 oracle and against the float32 vector kernel (chunk 32)."""
+    say(f"kda mfma dense solve keys={keys} mu={mu}")
+    d = gi.generate_kda(B=1, T=256, Hqk=2, Hv=4, dk=128, dv=128, dtype="bf16", mu=mu, s0_std=0.05, seed=35)
+    k = f64(d["k"])
+    if keys == "identical":
+        k[:] = k[:, :1]
+    else:
+        rng = np.random.default_rng(36)
+        r = rng.standard_normal(k.shape)
+        r /= np.linalg.norm(r, axis=-1, keepdims=True)
+        k = k[:, :1] + 0.3 * r
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    d["k"] = gi.bf16_bits(k.astype(np.float32))
+    d["beta"][:] = 0.97
+    o, s = run_kda(d, 64)
+    o_ref, s_ref = oracle_kda(d)
+    check(f"kda mfma dense keys={keys} mu={mu}", "bf16", o, o_ref, s, s_ref)
+    o32, s32 = run_kda(d, 32)
+    check(f"kda mfma vs vector, dense keys={keys} mu={mu}", "bf16", o, o32, s, s32)
