@@ -152,7 +152,12 @@ constexpr int V_ED = 2;    // exp(gc_63 - gc)
 constexpr int V_EC = 3;    // exp(gc_63) (every element)
 constexpr int V_EG = 4;    // scale exp(gc)
 constexpr int V_G = 5;     // gc (inclusive cumsum of g within the chunk)
-constexpr int NVEC = 6;
+constexpr int V_EN = 6;    // exp(-gc) (pipelined kernel only; used where the chunk's decay allows it)
+constexpr int NVEC = 7;
+// exp(gc_r - gc_c) = exp(gc_r) exp(-gc_c) with both factors normal floats when the chunk's total
+// log-decay gc_63 is above this (exp(-60) and exp(60) are far inside float32's normal range);
+// chunks that decay faster take the per-element exponentials
+constexpr float GC_FACTOR_MIN = -60.f;
 
 // Workspace of the split path, per (batch, value head, chunk), in two parts: what the state step
 // reads (T, then the rows V_B..V_EC) and what the output step reads (Aqk, then the row V_EG).
@@ -1160,6 +1165,52 @@ __device__ __forceinline__ void prep_store_aqk(const floatx4 (&gq)[10], const fl
     }
 }
 
+// prep_store_a with the decay factorised: A[r][c] = (beta_r exp(gc_r)) exp(-gc_c) (k_r . k_c);
+// br4 = beta exp(gc) of the lane's rows, en1 = exp(-gc) of its columns
+__device__ __forceinline__ void prep_store_a_fac(const floatx4 (&gk)[10], const floatx4 (&br4)[4], const float (&en1)[4],
+                                                 float* Ad, op_t* Ah, int lane)
+{
+    const int ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+        const int cc = 16 * TJ[t] + ln;
+        const int r0 = 16 * TI[t] + 4 * lg;
+        const float ec = en1[TJ[t]];
+        const floatx4 br = br4[TI[t]];
+        floatx4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = cc < r0 + e ? br[e] * ec * gk[t][e] : 0.f;
+        if (TI[t] == TJ[t])
+            *reinterpret_cast<floatx4*>(Ad + (16 * TI[t] + ln) * ADP + 4 * lg) = out;
+        else
+            *reinterpret_cast<opx4*>(Ah + cc * AHP + r0 - 16) = opx4{(op_t)out[0], (op_t)out[1], (op_t)out[2], (op_t)out[3]};
+    }
+}
+
+// prep_store_aqk with the decay factorised: Aqk[r][i] = (scale exp(gc_r)) exp(-gc_i) (q_r . k_i);
+// eg1 = scale exp(gc) of the lane's rows r, en4 = exp(-gc) of its columns i
+__device__ __forceinline__ void prep_store_aqk_fac(const floatx4 (&gq)[10], const float (&eg1)[4], const floatx4 (&en4)[4],
+                                                   int n, op_t* wa, int lane)
+{
+    const int ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+        const int r = 16 * TI[t] + ln;
+        const int i0 = 16 * TJ[t] + 4 * lg;
+        const float er = eg1[TI[t]];
+        const floatx4 ei = en4[TJ[t]];
+        opx4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (op_t)((i0 + e <= r && r < n) ? er * ei[e] * gq[t][e] : 0.f);
+        *reinterpret_cast<opx4*>(wa + frag_off(r, pcol(i0))) = out;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int r = 32 * p + ln, i0 = 32 * p + 16 + 4 * lg;
+        *reinterpret_cast<opx4*>(wa + frag_off(r, pcol(i0))) = opx4{};
+    }
+}
+
 // T = (I + A)^{-1} into Tm (column-permuted float16; its strictly-upper blocks (0, 1) and
 // (2, 3) must hold zeros): the four diagonal blocks by forward substitution in float32, then
 // T_{w+1,w} = -T_{w+1,w+1} A_{w+1,w} T_ww (w = 0, 2) and T[32:64, 0:32] = -T_hi (A[32:64, 0:32] T_lo)
@@ -1659,16 +1710,27 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
             if (c + 1 < NT) load(c + 1);
             const float* vs = ring(c);
             const int ln = lane & 15, lg = lane >> 4;
-            floatx4 g4[4], b4[4];
-            float g1[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                g4[t] = ld4s(vs + V_G * CH + 16 * t + 4 * lg);
-                b4[t] = ld4s(vs + V_B * CH + 16 * t + 4 * lg);
-                g1[t] = vs[V_G * CH + 16 * t + ln];
-            }
             GDN_TRACE(c, 1);
-            prep_store_a(gk, g4, b4, g1, Ad, Ah, lane);
+            if (vs[V_G * CH + CH - 1] > GC_FACTOR_MIN) {
+                floatx4 br4[4];
+                float en1[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    br4[t] = ld4s(vs + V_BEG * CH + 16 * t + 4 * lg);
+                    en1[t] = vs[V_EN * CH + 16 * t + ln];
+                }
+                prep_store_a_fac(gk, br4, en1, Ad, Ah, lane);
+            } else {
+                floatx4 g4[4], b4[4];
+                float g1[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    g4[t] = ld4s(vs + V_G * CH + 16 * t + 4 * lg);
+                    b4[t] = ld4s(vs + V_B * CH + 16 * t + 4 * lg);
+                    g1[t] = vs[V_G * CH + 16 * t + ln];
+                }
+                prep_store_a(gk, g4, b4, g1, Ad, Ah, lane);
+            }
             GDN_TRACE(c, 2);
             prep_solve_t(Ad, Ah, Tm, lane);
             GDN_TRACE(c, 3);
@@ -1704,14 +1766,25 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
             GDN_TRACE(c, 1);
             const float* vs = ring(c);
             const int ln = lane & 15, lg = lane >> 4;
-            floatx4 g4[4];
-            float g1[4];
+            if (vs[V_G * CH + CH - 1] > GC_FACTOR_MIN) {
+                floatx4 en4[4];
+                float eg1[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                g4[t] = ld4s(vs + V_G * CH + 16 * t + 4 * lg);
-                g1[t] = vs[V_G * CH + 16 * t + ln];
+                for (int t = 0; t < 4; ++t) {
+                    en4[t] = ld4s(vs + V_EN * CH + 16 * t + 4 * lg);
+                    eg1[t] = vs[V_EG * CH + 16 * t + ln];
+                }
+                prep_store_aqk_fac(gq, eg1, en4, n, reinterpret_cast<op_t*>(sb + L::aq), lane);
+            } else {
+                floatx4 g4[4];
+                float g1[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    g4[t] = ld4s(vs + V_G * CH + 16 * t + 4 * lg);
+                    g1[t] = vs[V_G * CH + 16 * t + ln];
+                }
+                prep_store_aqk(gq, g4, g1, scale, n, reinterpret_cast<op_t*>(sb + L::aq), lane);
             }
-            prep_store_aqk(gq, g4, g1, scale, n, reinterpret_cast<op_t*>(sb + L::aq), lane);
             GDN_TRACE(c, 2);
             lds_barrier();
         }
@@ -1778,6 +1851,7 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
             vs[V_ED * CH + lane] = __expf(last - x);
             vs[V_EC * CH + lane] = __expf(last);
             vs[V_EG * CH + lane] = scale * eg;
+            vs[V_EN * CH + lane] = __expf(fminf(-x, -GC_FACTOR_MIN));
         };
         if (NT > 0) {
             load_g(0);
