@@ -1497,7 +1497,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ch
 // waves carry chunk n out of LDS slot n & 1, the prep waves build chunk n + 1 in the other slot,
 // each prep wave a whole part of it on its own, so that no wave waits on another inside a chunk:
 // * T wave: the chunk's k rows from HBM straight into MFMA fragments, K K^T, A and the blocked
-//   solve for T = (I + A)^{-1} in LDS of its own, T into the slot in fragment order;
+//   solve for T = (I + A)^{-1} into a column-permuted matrix of its own, double-buffered like the
+//   slots, from which the chain waves read T's fragments (no copy into the slot);
 // * Aqk wave: q and k rows into fragments, K Q^T and Aqk into the slot in fragment order;
 // * V wave: the chunk's V tile and K (column-permuted float16) into the slot;
 // * Q wave: the chunk's Q (column-permuted float16) into the slot, and the gate vectors of the
@@ -1517,15 +1518,15 @@ struct PLds {
     static constexpr size_t k = 0;                                  // K   [64][KP] f16
     static constexpr size_t q = k + (size_t)CH * KP * 2;            // Q   [64][KP] f16
     static constexpr size_t v = q + (size_t)CH * KP * 2;            // V   [64][VP] bf16
-    static constexpr size_t t = v + (size_t)CH * VP * 2;            // T   6 fragment blocks f16
-    static constexpr size_t aq = t + 6 * 64 * 16;                   // Aqk 6 fragment blocks f16
+    static constexpr size_t aq = v + (size_t)CH * VP * 2;           // Aqk 6 fragment blocks f16
     static constexpr size_t slot = aq + 6 * 64 * 16;
-    static constexpr size_t ad = 2 * slot;                          // T wave: A, T scratch
+    static constexpr size_t ad = 2 * slot;                          // T wave: A
     static constexpr size_t ah = ad + (size_t)PREP_AD * 4;
-    static constexpr size_t tm = ah + (size_t)PREP_AH * 2;
-    static constexpr size_t vr = tm + (size_t)PREP_TM * 2;          // gate vectors [3][NVEC][64] f32
+    static constexpr size_t tm = ah + (size_t)PREP_AH * 2;          // T [2][64][CP] f16, column-permuted
+    static constexpr size_t vr = tm + (size_t)2 * PREP_TM * 2;      // gate vectors [3][NVEC][64] f32
     static constexpr size_t bytes = vr + (size_t)3 * NVEC * CH * 4;
-    static_assert(slot % 16 == 0 && v % 16 == 0 && tm % 16 == 0 && vr % 16 == 0, "16-byte aligned parts");
+    static_assert(slot % 16 == 0 && v % 16 == 0 && aq % 16 == 0 && tm % 16 == 0 && vr % 16 == 0,
+                  "16-byte aligned parts");
 };
 
 // A copy of x the compiler cannot see through: lane-derived values (addresses, masks) computed
@@ -1656,13 +1657,15 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
             const op_t* Ks = reinterpret_cast<const op_t*>(sb + L::k);
             const op_t* Qs = reinterpret_cast<const op_t*>(sb + L::q);
             const bf16* Vs = reinterpret_cast<const bf16*>(sb + L::v) + w * NCOL;
-            const opx8* Tf = reinterpret_cast<const opx8*>(sb + L::t);
+            const op_t* Tn = reinterpret_cast<const op_t*>(smem + L::tm) + (n & 1) * PREP_TM;
             const opx8* Af = reinterpret_cast<const opx8*>(sb + L::aq);
+            const int ln = lane & 15, lg = lane >> 4;
             const float* vs = ring(n);
             const int t0 = n * CH;
             opx8 hb[NTN][KB], db[NTN][2], dtb[NTN][2];
             GDN_TRACE(n, 0);
-            chain_delta<DK, NTN, L::VP>(hacc, Ks, Vs, [&](int mt, int cb) { return Tf[tblk(mt, cb) * 64 + lane]; },
+            chain_delta<DK, NTN, L::VP>(hacc, Ks, Vs,
+                                        [&](int mt, int cb) { return frag(Tn, CP, 16 * mt + ln, 32 * cb, lg); },
                                         vs, lane, hb, db, dtb);
             GDN_TRACE(n, 1);
             chain_out<DK, NTN>(hb, db, Qs, [&](int ct, int cb) { return Af[tblk(ct, cb) * 64 + lane]; },
@@ -1687,8 +1690,9 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
         // T wave
         float* Ad = reinterpret_cast<float*>(smem + L::ad);
         op_t* Ah = reinterpret_cast<op_t*>(smem + L::ah);
-        op_t* Tm = reinterpret_cast<op_t*>(smem + L::tm);
-        prep_zero_t_upper(Tm, lane);
+        op_t* Tm0 = reinterpret_cast<op_t*>(smem + L::tm);
+        prep_zero_t_upper(Tm0, lane);
+        prep_zero_t_upper(Tm0 + PREP_TM, lane);
         bf16x8 kf[4][KB];
         auto load = [&](int c) {
             const int t0 = c * CH;
@@ -1697,7 +1701,6 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
         if (NT > 0) load(0);
         lds_barrier();
         for (int c = 0; c < NT; ++c) {
-            unsigned char* sb = slot(c);
             const int lane = opaque(threadIdx.x & 63);
             floatx4 gk[10];
 #pragma unroll
@@ -1732,11 +1735,9 @@ __global__ __launch_bounds__((NW + PIPE_PW) * 64, 1) void chunk_pipe_kernel(
                 prep_store_a(gk, g4, b4, g1, Ad, Ah, lane);
             }
             GDN_TRACE(c, 2);
-            prep_solve_t(Ad, Ah, Tm, lane);
+            // T into the chunk's matrix, which the chain waves read in the next period
+            prep_solve_t(Ad, Ah, Tm0 + (c & 1) * PREP_TM, lane);
             GDN_TRACE(c, 3);
-            wave_lds_fence();
-            prep_store_t(Tm, reinterpret_cast<opx8*>(sb + L::t), lane);
-            GDN_TRACE(c, 4);
             lds_barrier();
         }
     } else if (pw == 1) {
